@@ -1,0 +1,215 @@
+"""Benchmark of the four-direction GSPN line-scan forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload profile]
+
+A step is one gspn_forward4 call (normalise the logits, scan T->B, B->T,
+L->R, R->L, merge by summation) over one batch of seeded synthetic inputs
+already resident in HBM; for the proxy workload a step is the compressive
+proxy pipeline (1x1 projection down, forward4 in proxy space, 1x1 projection
+up).  Prints one JSON line.
+
+Measurements:
+  - ms per step: HIP events on the stream the library launches on, bracketing
+    the K timed steps (synchronised on both sides).
+  - roofline: the dominant kernel (the line-scan kernel) timed per launch with
+    HIP events in its own loop over the same inputs and launch configuration;
+    achieved = its algorithmic bytes per launch / its average duration.
+  - effective bandwidth of the whole step = algorithmic bytes of the forward
+    (every distinct input read once, y written once) / ms per step.
+  - cpu_baseline: the fp64 oracle on a bounded sample of the same workload,
+    on the host's cores (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from linear_spatial_propagation_gspn_amd import gspn as G  # noqa: E402
+from linear_spatial_propagation_gspn_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "ms per 4-direction GSPN forward at 1024², B=16, C=8; achieved HBM GB/s"
+
+
+def esize(wl) -> int:
+    return 4 if wl.dtype == "f32" else 2
+
+
+def algorithmic_bytes(wl) -> int:
+    """Every distinct input read once and y written once."""
+    es = esize(wl)
+    hw = wl.h * wl.w
+    if wl.c_proxy:
+        x = wl.n * wl.c * hw * es
+        y = x
+        lam = 4 * wl.n * wl.c_proxy * hw * es
+        z = 4 * wl.n * wl.cw * 3 * hw * es
+        wts = 2 * wl.c * wl.c_proxy * es
+        return x + y + lam + z + wts
+    u = wl.n * wl.c * hw * es
+    z = 4 * wl.n * wl.cw * 3 * hw * es
+    return u + 4 * u + z + u
+
+
+def scan_launch_bytes(wl, accumulate: bool) -> int:
+    """Compulsory bytes of one direction's scan launch: x, its logits and
+    lambda read once, the output written once (and read once when the launch
+    accumulates into it)."""
+    es = esize(wl)
+    c = wl.c_scan
+    u = wl.n * c * wl.h * wl.w * es
+    z = wl.n * wl.cw * 3 * wl.h * wl.w * es
+    return u + z + u + u + (u if accumulate else 0)
+
+
+def run_step(wl, inp, out):
+    if wl.c_proxy:
+        return G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
+                                     chunk_len=wl.chunk)
+    return G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out)
+
+
+def time_scan_kernel(wl, inp, reps: int):
+    """Per-launch durations of the scan kernel (HIP events on the launch stream)."""
+    if wl.c_proxy:
+        x = G.gspn_proxy_project(inp["x"], inp["w_down"])
+    else:
+        x = inp["x"]
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    per_dir = []
+    for d in range(4):
+        acc = d > 0
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        G.gspn_scan_fwd(d, x, inp["logits"][d], inp["lam"][d], wl.chunk, out=out, accumulate=acc)
+        for a, b in evs:
+            a.record(stream)
+            G.gspn_scan_fwd(d, x, inp["logits"][d], inp["lam"][d], wl.chunk, out=out, accumulate=acc)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+        per_dir.append((ms, scan_launch_bytes(wl, acc)))
+    return per_dir
+
+
+def cpu_baseline(wl, inp):
+    """The fp64 oracle on a bounded sample of the workload (whole planes),
+    scaled to ms per full forward."""
+    import oracle
+    nthreads = os.cpu_count() or 1
+    planes = wl.n * wl.c
+    if wl.c_proxy:
+        # sample: the proxy-space four-direction scan (all proxy planes) plus
+        # the two projections restricted to a pixel band
+        return None
+    budget_planes = max(1, min(planes, 16 if wl.h * wl.w >= 1 << 20 else 512))
+    idx = [(p // wl.c, p % wl.c) for p in range(budget_planes)]
+    xs = torch.stack([inp["x"][n, c] for n, c in idx])[:, None].float().cpu()
+    zs, ls = [], []
+    for d in range(4):
+        zs.append(torch.stack([inp["logits"][d][n, 0 if wl.shared_w else c] for n, c in idx])[:, None]
+                  .float().cpu())
+        ls.append(torch.stack([inp["lam"][d][n, c] for n, c in idx])[:, None].float().cpu())
+    t = time.perf_counter()
+    oracle.forward4(xs, zs, ls, chunk=wl.chunk)
+    dt = time.perf_counter() - t
+    ms_full = dt * 1e3 * planes / budget_planes
+    return {"value": round(ms_full, 3), "unit": "ms per forward (extrapolated)", "cores": nthreads,
+            "kind": "oracle",
+            "sample": "%d of %d planes (%dx%d), all 4 directions, fp64, %.2f s measured"
+                      % (budget_planes, planes, wl.h, wl.w, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="profile", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.init()
+    G.lib()
+    print("bench: workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
+    inp = make_inputs(wl, "cuda")
+    out = torch.empty_like(inp["x"]) if not wl.c_proxy else None
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run_step(wl, inp, out)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        run_step(wl, inp, out)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    print("bench: %.3f ms/step (wall %.3f ms/step)" % (ms, wall * 1e3 / args.steps),
+          file=sys.stderr, flush=True)
+
+    per_dir = time_scan_kernel(wl, inp, reps=max(3, min(args.steps, 10)))
+    k_ms = sum(m for m, _ in per_dir) / 4
+    k_bytes = sum(b for _, b in per_dir) / 4
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    alg = algorithmic_bytes(wl)
+    eff = alg / (ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, inp)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16 storage, f32 arithmetic",
+        "data": "synthetic (seeded)",
+        "config": {"workload": wl.name, "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
+                   "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
+                   "c_proxy": wl.c_proxy},
+        "effective_GBps": round(eff, 1),
+        "effective_frac": round(eff / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": alg,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "scan_kernel", "kernel_ms": round(k_ms, 4),
+                     "bytes_per_launch": int(k_bytes),
+                     "per_direction_ms": [round(m, 4) for m, _ in per_dir]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * gspn.h -- C ABI of libgspn, GSPN's 2D line-scan linear propagation on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (GSPN-2 paper notes, section "2D spatial propagation
+ * recap"; GSPN summary page, section "Approach"): for x in R^{N x C x H x W}
+ * a line scan runs in each of four directions,
+ *
+ *     h_i = w_i h_{i-1} + lambda_i (.) x_i,
+ *
+ * line by line along the scan axis, with h = 0 before the first line.  Each
+ * w_i is tridiagonal and row-stochastic: position k of line i couples to
+ * positions k-1, k, k+1 of the previous line with weights obtained from three
+ * logits by a sigmoid followed by division by their sum; at a line border
+ * the sum runs over the neighbours that exist (a missing neighbour has
+ * weight 0).  The four direction outputs are merged by an elementwise sum.
+ * Variants: channel-shared w (GSPN-2 notes, "Optimisation 2"), independent
+ * chunks along the scan axis ("Optimisation 1") and the 1x1 projections to
+ * and from a C_proxy-channel space ("Optimisation 2").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All pointers are device pointers (HIP device memory) unless stated;
+ *    every tensor is contiguous, row-major.  Pointers must be aligned to
+ *    their element size; otherwise GSPN_ERR_MISALIGNED.
+ *  - Layouts:
+ *      x, y, h, out        [N][C][H][W]
+ *      logits, w (dir d)   [N][Cw][3][S][L]   Cw = 1 (shared) or C
+ *      lam (dir d)         [N][C][S][L]
+ *    (S, L) = (H, W) for GSPN_T2B / GSPN_B2T and (W, H) for GSPN_L2R /
+ *    GSPN_R2L: the per-direction tensors are stored in the direction's scan
+ *    frame, so that each scan step reads one contiguous line (the coalesced
+ *    layout of GSPN-2 notes, "Optimisation 3").  For a horizontal direction,
+ *    element (step i, position k) is array column i, row k.  The three
+ *    logits/weights of a position are ordered (k-1, k, k+1) in array order
+ *    for every direction; the first line of a scan (and of each chunk) does
+ *    not use its logits.
+ *  - dtype: every tensor of one call has the same storage type, GSPN_F32 or
+ *    GSPN_BF16.  Arithmetic is always fp32 (bf16 values are widened exactly;
+ *    bf16 results are rounded to nearest even at each store).
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call is asynchronous on that stream; the library never synchronises,
+ *    never allocates or frees memory, and keeps no mutable global state.
+ *  - Ownership: the caller owns every buffer and must keep it alive until the
+ *    work queued on `stream` has finished.
+ *  - Errors: arguments are validated on the host before anything is queued.
+ *    A failed validation returns its code and queues nothing.  A failed
+ *    kernel launch returns GSPN_ERR_HIP.  No C++ exception crosses the ABI.
+ *    A call whose tensors are empty (a zero dimension) returns GSPN_OK and
+ *    queues nothing, without looking at its pointers.
+ *  - Aliasing: an output may not overlap any input, except that with
+ *    accumulate = 1 the output is read and written in place.
+ *  - Domain: the fp32 sigmoid saturates, so for each position at least one
+ *    existing neighbour's logit must exceed about -87 (otherwise every weight
+ *    of that row is 0/0 = NaN).  NaN/Inf inputs propagate by IEEE rules.
+ *  - Limits: a line may hold at most GSPN_MAX_LINE positions (else
+ *    GSPN_ERR_UNSUPPORTED); dimensions must be in [0, 2^31) and N*C*H*W < 2^58.
+ */
+#ifndef GSPN_H_
+#define GSPN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GSPN_ABI_VERSION 1
+#define GSPN_MAX_LINE 8192
+
+typedef enum {
+    GSPN_OK = 0,
+    GSPN_ERR_NULL_POINTER = 1,
+    GSPN_ERR_BAD_SHAPE = 2,
+    GSPN_ERR_BAD_DIRECTION = 3,
+    GSPN_ERR_BAD_DTYPE = 4,
+    GSPN_ERR_BAD_CHUNK = 5,
+    GSPN_ERR_BAD_WEIGHT_CHANNELS = 6,
+    GSPN_ERR_MISALIGNED = 7,
+    GSPN_ERR_ALIASING = 8,
+    GSPN_ERR_UNSUPPORTED = 9,
+    GSPN_ERR_HIP = 10
+} gspn_status;
+
+typedef enum { GSPN_T2B = 0, GSPN_B2T = 1, GSPN_L2R = 2, GSPN_R2L = 3 } gspn_dir;
+
+typedef enum { GSPN_F32 = 0, GSPN_BF16 = 1 } gspn_dtype;
+
+/*
+ * gspn_normalize_weights -- sigmoid + row normalisation of one direction's
+ * logits (GSPN summary page, "Approach"; GSPN-2 notes, "2D spatial
+ * propagation recap": rows sum to 1).
+ *   logits  [n][cw][3][S][L] (input), w_out same layout (output).
+ *   w_out[o] = s_o / sum_{valid o'} s_{o'}, s_o = 1/(1+exp(-logit_o)), and 0
+ *   for a neighbour outside the line.  (S, L) follow from dir, h, w.
+ */
+gspn_status gspn_normalize_weights(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
+                                   const void* logits, void* w_out, int dtype, void* stream);
+
+/*
+ * gspn_scan_fwd -- one direction of the line scan (GSPN-2 notes, "2D
+ * spatial propagation recap"), optionally cut into independent chunks of
+ * chunk_len steps counted in scan order (GSPN-2 notes, "Optimisation 1":
+ * independent (chunk, n, c) blocks).
+ *   dir           GSPN_T2B / GSPN_B2T / GSPN_L2R / GSPN_R2L.
+ *   chunk_len     0 or >= S: one chunk over the whole scan; K > 0: h is reset
+ *                 to 0 every K steps; < 0: GSPN_ERR_BAD_CHUNK.
+ *   n, c, h, w    dimensions of x and out.
+ *   cw            1 (channel-shared w, "Optimisation 2") or c; else
+ *                 GSPN_ERR_BAD_WEIGHT_CHANNELS.
+ *   x             [n][c][h][w] input.
+ *   wts           [n][cw][3][S][L]: logits if wts_are_logits = 1, else
+ *                 weights already normalised (e.g. by gspn_normalize_weights).
+ *   lam           [n][c][S][L] per-position scaling lambda.
+ *   out           [n][c][h][w]: out = h (accumulate = 0) or out += h (1).
+ */
+gspn_status gspn_scan_fwd(int dir, int64_t chunk_len, int64_t n, int64_t c, int64_t h, int64_t w,
+                          int64_t cw, const void* x, const void* wts, int wts_are_logits,
+                          const void* lam, void* out, int accumulate, int dtype, void* stream);
+
+/*
+ * gspn_merge4 -- y = h0 + h1 + h2 + h3 elementwise over numel elements (the
+ * merge of the four direction outputs by summation).  y may not overlap any
+ * h_d.  Sum order: ((h0 + h1) + h2) + h3 in fp32.
+ */
+gspn_status gspn_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
+                        int64_t numel, int dtype, void* stream);
+
+/*
+ * gspn_proxy_project -- 1x1 projection between channel spaces (GSPN-2
+ * notes, "Optimisation 2", compressive channel proxy): for every pixel,
+ * out[n][o][p] = sum_c weight[o][c] * in[n][c][p].  No bias.
+ *   in      [n][c_in][h][w], weight [c_out][c_in], out [n][c_out][h][w].
+ * Accumulation is fp32 whatever the storage type.
+ */
+gspn_status gspn_proxy_project(int64_t n, int64_t c_in, int64_t h, int64_t w, int64_t c_out,
+                               const void* in, const void* weight, void* out, int dtype,
+                               void* stream);
+
+/*
+ * gspn_forward4 -- the four-direction propagation with summed merge:
+ *   y = sum over d in (T2B, B2T, L2R, R2L) of scan_d(x, logits[d], lam[d]).
+ *   logits[d]  [n][cw][3][S_d][L_d] logits of direction d (normalised inside).
+ *   lam[d]     [n][c][S_d][L_d]; the same pointer may be given for all d.
+ *   logits and lam are host arrays of 4 device pointers, indexed by gspn_dir.
+ *   y          [n][c][h][w] output; may not overlap any input.
+ */
+gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                          int64_t chunk_len, const void* x, const void* const logits[4],
+                          const void* const lam[4], void* y, int dtype, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* gspn_status_string(int status);
+
+/* GSPN_ABI_VERSION of the built library. */
+int gspn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSPN_H_ */

@@ -1,0 +1,237 @@
+// api.cpp -- the C ABI of libgspn (declared in include/gspn.h): host-side
+// validation of every argument, then kernel launches on the caller's stream.
+// Validation never touches the device; nothing here allocates, frees or
+// synchronises.
+#include "../../include/gspn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+using gspn::kBF16;
+using gspn::kF32;
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxElems = int64_t{1} << 58;
+
+bool valid_dtype(int dt) { return dt == GSPN_F32 || dt == GSPN_BF16; }
+size_t elem_size(int dt) { return dt == GSPN_F32 ? 4 : 2; }
+bool valid_dir(int d) { return d >= GSPN_T2B && d <= GSPN_R2L; }
+bool horizontal(int d) { return d == GSPN_L2R || d == GSPN_R2L; }
+
+// Product of non-negative dims without overflow; -1 when it exceeds kMaxElems.
+int64_t checked_product(std::initializer_list<int64_t> dims) {
+    int64_t p = 1;
+    for (int64_t d : dims) {
+        if (d == 0) return 0;
+    }
+    for (int64_t d : dims) {
+        if (d > kMaxElems / p) return -1;
+        p *= d;
+    }
+    return p;
+}
+
+bool dims_ok(std::initializer_list<int64_t> dims) {
+    for (int64_t d : dims)
+        if (d < 0 || d > kMaxDim) return false;
+    return checked_product(dims) >= 0;
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+gspn_status from_hip(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR_HIP; }
+
+struct ScanCheck {
+    gspn_status st;
+    int64_t chunk;  // clamped to [1, S]
+};
+
+// Shared validation of one scan direction's arguments.
+ScanCheck check_scan(int dir, int64_t chunk_len, int64_t n, int64_t c, int64_t h, int64_t w,
+                     int64_t cw, int dtype, bool* empty) {
+    *empty = false;
+    if (!valid_dtype(dtype)) return {GSPN_ERR_BAD_DTYPE, 0};
+    if (!valid_dir(dir)) return {GSPN_ERR_BAD_DIRECTION, 0};
+    if (!dims_ok({n, c, h, w})) return {GSPN_ERR_BAD_SHAPE, 0};
+    if (chunk_len < 0) return {GSPN_ERR_BAD_CHUNK, 0};
+    if (!(cw == 1 || cw == c)) return {GSPN_ERR_BAD_WEIGHT_CHANNELS, 0};
+    if (checked_product({n, c, h, w}) == 0) {
+        *empty = true;
+        return {GSPN_OK, 0};
+    }
+    const int64_t S = horizontal(dir) ? w : h;
+    const int64_t L = horizontal(dir) ? h : w;
+    if (L > GSPN_MAX_LINE) return {GSPN_ERR_UNSUPPORTED, 0};
+    const int64_t K = (chunk_len == 0 || chunk_len >= S) ? S : chunk_len;
+    const int64_t nchunks = (S + K - 1) / K;
+    if (n * c > INT_MAX / nchunks) return {GSPN_ERR_UNSUPPORTED, 0};
+    return {GSPN_OK, K};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gspn_status_string(int status) {
+    switch (status) {
+        case GSPN_OK: return "GSPN_OK";
+        case GSPN_ERR_NULL_POINTER: return "GSPN_ERR_NULL_POINTER: a required pointer is NULL";
+        case GSPN_ERR_BAD_SHAPE: return "GSPN_ERR_BAD_SHAPE: a dimension is negative or too large";
+        case GSPN_ERR_BAD_DIRECTION: return "GSPN_ERR_BAD_DIRECTION: direction is not 0..3";
+        case GSPN_ERR_BAD_DTYPE: return "GSPN_ERR_BAD_DTYPE: dtype is not GSPN_F32 or GSPN_BF16";
+        case GSPN_ERR_BAD_CHUNK: return "GSPN_ERR_BAD_CHUNK: chunk_len is negative";
+        case GSPN_ERR_BAD_WEIGHT_CHANNELS:
+            return "GSPN_ERR_BAD_WEIGHT_CHANNELS: weight channels must be 1 or C";
+        case GSPN_ERR_MISALIGNED: return "GSPN_ERR_MISALIGNED: a pointer is not aligned to its element size";
+        case GSPN_ERR_ALIASING: return "GSPN_ERR_ALIASING: an output overlaps an input";
+        case GSPN_ERR_UNSUPPORTED:
+            return "GSPN_ERR_UNSUPPORTED: line longer than GSPN_MAX_LINE or grid too large";
+        case GSPN_ERR_HIP: return "GSPN_ERR_HIP: a HIP launch failed";
+        default: return "unknown gspn_status";
+    }
+}
+
+int gspn_abi_version(void) { return GSPN_ABI_VERSION; }
+
+gspn_status gspn_normalize_weights(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
+                                   const void* logits, void* w_out, int dtype, void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
+    if (!valid_dir(dir)) return GSPN_ERR_BAD_DIRECTION;
+    if (!dims_ok({n, cw, 3, h, w})) return GSPN_ERR_BAD_SHAPE;
+    const int64_t total = checked_product({n, cw, 3, h, w});
+    if (total == 0) return GSPN_OK;
+    if (!logits || !w_out) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    if (!aligned(logits, es) || !aligned(w_out, es)) return GSPN_ERR_MISALIGNED;
+    const int64_t bytes = total * static_cast<int64_t>(es);
+    if (overlap(logits, bytes, w_out, bytes)) return GSPN_ERR_ALIASING;
+    return from_hip(gspn::launch_normalize(dir, n, cw, h, w, logits, w_out, dtype, as_stream(stream)));
+}
+
+gspn_status gspn_scan_fwd(int dir, int64_t chunk_len, int64_t n, int64_t c, int64_t h, int64_t w,
+                          int64_t cw, const void* x, const void* wts, int wts_are_logits,
+                          const void* lam, void* out, int accumulate, int dtype, void* stream) {
+    bool empty = false;
+    const ScanCheck ck = check_scan(dir, chunk_len, n, c, h, w, cw, dtype, &empty);
+    if (ck.st != GSPN_OK || empty) return ck.st;
+    if (!x || !wts || !lam || !out) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    if (!aligned(x, es) || !aligned(wts, es) || !aligned(lam, es) || !aligned(out, es))
+        return GSPN_ERR_MISALIGNED;
+    const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
+    const int64_t wb = n * cw * 3 * h * w * static_cast<int64_t>(es);
+    if (overlap(out, xb, x, xb) || overlap(out, xb, wts, wb) || overlap(out, xb, lam, xb))
+        return GSPN_ERR_ALIASING;
+    gspn::ScanParams p;
+    p.x = x;
+    p.wts = wts;
+    p.lam = lam;
+    p.out = out;
+    p.n = n;
+    p.c = c;
+    p.cw = cw;
+    p.h = h;
+    p.w = w;
+    p.dir = dir;
+    p.chunk = ck.chunk;
+    p.wts_are_logits = wts_are_logits ? 1 : 0;
+    p.accumulate = accumulate ? 1 : 0;
+    p.dtype = dtype;
+    return from_hip(gspn::launch_scan(p, as_stream(stream)));
+}
+
+gspn_status gspn_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
+                        int64_t numel, int dtype, void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
+    if (numel < 0 || numel >= kMaxElems) return GSPN_ERR_BAD_SHAPE;
+    if (numel == 0) return GSPN_OK;
+    if (!h0 || !h1 || !h2 || !h3 || !y) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    if (!aligned(h0, es) || !aligned(h1, es) || !aligned(h2, es) || !aligned(h3, es) || !aligned(y, es))
+        return GSPN_ERR_MISALIGNED;
+    const int64_t b = numel * static_cast<int64_t>(es);
+    if (overlap(y, b, h0, b) || overlap(y, b, h1, b) || overlap(y, b, h2, b) || overlap(y, b, h3, b))
+        return GSPN_ERR_ALIASING;
+    return from_hip(gspn::launch_merge4(h0, h1, h2, h3, y, numel, dtype, as_stream(stream)));
+}
+
+gspn_status gspn_proxy_project(int64_t n, int64_t c_in, int64_t h, int64_t w, int64_t c_out,
+                               const void* in, const void* weight, void* out, int dtype,
+                               void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
+    if (!dims_ok({n, c_in, h, w}) || !dims_ok({n, c_out, h, w}) || !dims_ok({c_out, c_in}))
+        return GSPN_ERR_BAD_SHAPE;
+    const int64_t out_elems = checked_product({n, c_out, h, w});
+    if (out_elems == 0) return GSPN_OK;
+    if (c_in == 0) return GSPN_ERR_BAD_SHAPE;
+    if (!in || !weight || !out) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    if (!aligned(in, es) || !aligned(weight, es) || !aligned(out, es)) return GSPN_ERR_MISALIGNED;
+    const int64_t ob = out_elems * static_cast<int64_t>(es);
+    const int64_t ib = n * c_in * h * w * static_cast<int64_t>(es);
+    const int64_t wb = c_out * c_in * static_cast<int64_t>(es);
+    if (overlap(out, ob, in, ib) || overlap(out, ob, weight, wb)) return GSPN_ERR_ALIASING;
+    return from_hip(gspn::launch_project(n, c_in, h * w, c_out, in, weight, out, dtype, as_stream(stream)));
+}
+
+gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                          int64_t chunk_len, const void* x, const void* const logits[4],
+                          const void* const lam[4], void* y, int dtype, void* stream) {
+    int64_t chunks[4];
+    for (int d = 0; d < 4; ++d) {
+        bool empty = false;
+        const ScanCheck ck = check_scan(d, chunk_len, n, c, h, w, cw, dtype, &empty);
+        if (ck.st != GSPN_OK || empty) return ck.st;
+        chunks[d] = ck.chunk;
+    }
+    if (!x || !y || !logits || !lam) return GSPN_ERR_NULL_POINTER;
+    for (int d = 0; d < 4; ++d)
+        if (!logits[d] || !lam[d]) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    if (!aligned(x, es) || !aligned(y, es)) return GSPN_ERR_MISALIGNED;
+    for (int d = 0; d < 4; ++d)
+        if (!aligned(logits[d], es) || !aligned(lam[d], es)) return GSPN_ERR_MISALIGNED;
+    const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
+    const int64_t wb = n * cw * 3 * h * w * static_cast<int64_t>(es);
+    if (overlap(y, xb, x, xb)) return GSPN_ERR_ALIASING;
+    for (int d = 0; d < 4; ++d)
+        if (overlap(y, xb, logits[d], wb) || overlap(y, xb, lam[d], xb)) return GSPN_ERR_ALIASING;
+
+    // Four passes on one stream: the first writes y, the others add to it.
+    for (int d = 0; d < 4; ++d) {
+        gspn::ScanParams p;
+        p.x = x;
+        p.wts = logits[d];
+        p.lam = lam[d];
+        p.out = y;
+        p.n = n;
+        p.c = c;
+        p.cw = cw;
+        p.h = h;
+        p.w = w;
+        p.dir = d;
+        p.chunk = chunks[d];
+        p.wts_are_logits = 1;
+        p.accumulate = d > 0 ? 1 : 0;
+        p.dtype = dtype;
+        const hipError_t e = gspn::launch_scan(p, as_stream(stream));
+        if (e != hipSuccess) return GSPN_ERR_HIP;
+    }
+    return GSPN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// device.hpp -- small device-side helpers shared by the libgspn kernels:
+// storage-type loads/stores (fp32, bf16 widened exactly, rounded to nearest
+// even on store) and the sigmoid row normalisation of one tridiagonal row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gspn {
+
+using bf16_t = uint16_t;  // bf16 storage as raw bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// gfx950 has a native round-to-nearest-even fp32 -> bf16 conversion
+// (v_cvt_pk_bf16_f32); NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float v) {
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(v));
+}
+
+template <typename T>
+struct Store;
+
+template <>
+struct Store<float> {
+    static __device__ __forceinline__ float ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+
+template <>
+struct Store<bf16_t> {
+    static __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(*p); }
+    static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// 1 / d to within about half an ulp: the hardware reciprocal (1 ulp) refined
+// by one Newton step.
+__device__ __forceinline__ float recip(float d) {
+    float r = __builtin_amdgcn_rcpf(d);
+    float e = __builtin_fmaf(-d, r, 1.0f);
+    return __builtin_fmaf(r, e, r);
+}
+
+// Logistic sigmoid 1 / (1 + e^{-z}).  e^{-z} is evaluated as 2^{-z log2 e}
+// with the hardware exp2; it saturates to +inf for z below about -88, which
+// gives sigmoid = 0, and to 0 for large z, which gives 1.
+__device__ __forceinline__ float sigmoid(float z) {
+    const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Row normalisation of one tridiagonal row (GSPN summary page, "Approach":
+// sigmoid then division by the row sum, so the row sums to 1).  has_l /
+// has_r say whether the neighbours k-1 / k+1 exist on the line; a missing
+// neighbour gets weight exactly 0 and is left out of the sum.
+__device__ __forceinline__ void normalise_row(float z0, float z1, float z2, bool has_l, bool has_r,
+                                              float& w0, float& w1, float& w2) {
+    const float s0 = has_l ? sigmoid(z0) : 0.0f;
+    const float s1 = sigmoid(z1);
+    const float s2 = has_r ? sigmoid(z2) : 0.0f;
+    const float r = recip((s0 + s1) + s2);
+    w0 = s0 * r;
+    w1 = s1 * r;
+    w2 = s2 * r;
+}
+
+}  // namespace gspn

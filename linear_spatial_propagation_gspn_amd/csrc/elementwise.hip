@@ -1,0 +1,93 @@
+// elementwise.hip -- the standalone weight normalisation and the four-way
+// merge.  Both are pure streaming kernels (HBM-bound): grid-stride loops over
+// contiguous elements so every wavefront access is a coalesced run.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace gspn {
+namespace {
+
+// w = sigmoid row normalisation of the logit triple at every (plane, i, k)
+// (GSPN summary page, "Approach"; rows sum to 1, border rows renormalised
+// over the neighbours that exist).  Layout [planes][3][S][L].
+template <typename T>
+__global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ z, T* __restrict__ w,
+                                                        int64_t planes, int64_t S, int64_t L) {
+    const int64_t per_plane = S * L;
+    const int64_t total = planes * per_plane;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+         e += stride) {
+        const int64_t pl = e / per_plane;
+        const int64_t r = e - pl * per_plane;
+        const int64_t k = r % L;
+        const int64_t base = pl * 3 * per_plane + r;
+        float w0, w1, w2;
+        normalise_row(Store<T>::ld(z + base), Store<T>::ld(z + base + per_plane),
+                      Store<T>::ld(z + base + 2 * per_plane), k > 0, k + 1 < L, w0, w1, w2);
+        Store<T>::st(w + base, w0);
+        Store<T>::st(w + base + per_plane, w1);
+        Store<T>::st(w + base + 2 * per_plane, w2);
+    }
+}
+
+// y = ((h0 + h1) + h2) + h3
+template <typename T>
+__global__ __launch_bounds__(256) void merge4_kernel(const T* __restrict__ h0, const T* __restrict__ h1,
+                                                     const T* __restrict__ h2, const T* __restrict__ h3,
+                                                     T* __restrict__ y, int64_t numel) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < numel;
+         e += stride) {
+        const float v = ((Store<T>::ld(h0 + e) + Store<T>::ld(h1 + e)) + Store<T>::ld(h2 + e)) +
+                        Store<T>::ld(h3 + e);
+        Store<T>::st(y + e, v);
+    }
+}
+
+unsigned grid_for(int64_t total, int threads) {
+    int64_t blocks = (total + threads - 1) / threads;
+    const int64_t cap = 256 * 64;  // 64 workgroups per CU is plenty for a grid-stride loop
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return static_cast<unsigned>(blocks);
+}
+
+}  // namespace
+
+hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
+                            const void* logits, void* w_out, int dtype, hipStream_t stream) {
+    const bool horiz = (dir == 2 || dir == 3);
+    const int64_t S = horiz ? w : h;
+    const int64_t L = horiz ? h : w;
+    const int64_t planes = n * cw;
+    const unsigned grid = grid_for(planes * S * L, 256);
+    if (dtype == kF32) {
+        hipLaunchKernelGGL(normalize_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const float*>(logits), static_cast<float*>(w_out), planes, S, L);
+    } else {
+        hipLaunchKernelGGL(normalize_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const bf16_t*>(logits), static_cast<bf16_t*>(w_out), planes, S,
+                           L);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
+                         int64_t numel, int dtype, hipStream_t stream) {
+    const unsigned grid = grid_for(numel, 256);
+    if (dtype == kF32) {
+        hipLaunchKernelGGL(merge4_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const float*>(h0), static_cast<const float*>(h1),
+                           static_cast<const float*>(h2), static_cast<const float*>(h3),
+                           static_cast<float*>(y), numel);
+    } else {
+        hipLaunchKernelGGL(merge4_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const bf16_t*>(h0), static_cast<const bf16_t*>(h1),
+                           static_cast<const bf16_t*>(h2), static_cast<const bf16_t*>(h3),
+                           static_cast<bf16_t*>(y), numel);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gspn

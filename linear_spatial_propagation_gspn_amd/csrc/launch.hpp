@@ -1,0 +1,36 @@
+// launch.hpp -- host-side launchers behind the C ABI (internal to libgspn).
+// Arguments reaching these functions have been validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gspn {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+struct ScanParams {
+    const void* x;
+    const void* wts;
+    const void* lam;
+    void* out;
+    int64_t n, c, cw, h, w;
+    int dir;             // 0 T2B, 1 B2T, 2 L2R, 3 R2L
+    int64_t chunk;       // steps per chunk, already clamped to [1, S]
+    int wts_are_logits;
+    int accumulate;
+    int dtype;
+};
+
+hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
+
+hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
+                            const void* logits, void* w_out, int dtype, hipStream_t stream);
+
+hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
+                         int64_t numel, int dtype, hipStream_t stream);
+
+hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const void* in,
+                          const void* weight, void* out, int dtype, hipStream_t stream);
+
+}  // namespace gspn

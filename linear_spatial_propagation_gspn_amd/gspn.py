@@ -1,0 +1,219 @@
+"""Thin ctypes binding of libgspn (include/gspn.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in libgspn's HIP kernels.
+The functions carry the C ABI's names.  Shapes, dtypes, devices and
+contiguity are checked here so that the pointers handed to the library
+always cover the sizes it is told; everything else (and the error codes) is
+the library's.
+
+If libgspn.so is missing, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgspn.so")
+
+T2B, B2T, L2R, R2L = 0, 1, 2, 3
+DIRECTIONS = ("T2B", "B2T", "L2R", "R2L")
+GSPN_F32, GSPN_BF16 = 0, 1
+
+STATUS = {
+    0: "GSPN_OK", 1: "GSPN_ERR_NULL_POINTER", 2: "GSPN_ERR_BAD_SHAPE", 3: "GSPN_ERR_BAD_DIRECTION",
+    4: "GSPN_ERR_BAD_DTYPE", 5: "GSPN_ERR_BAD_CHUNK", 6: "GSPN_ERR_BAD_WEIGHT_CHANNELS",
+    7: "GSPN_ERR_MISALIGNED", 8: "GSPN_ERR_ALIASING", 9: "GSPN_ERR_UNSUPPORTED", 10: "GSPN_ERR_HIP",
+}
+
+# Symbols declared in include/gspn.h.
+EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy_project",
+           "gspn_forward4", "gspn_status_string", "gspn_abi_version")
+
+
+class GspnError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (call, lib().gspn_status_string(status).decode()))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgspn with argument types set.  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    "libgspn.so is not built (expected at %s); run "
+                    "`python -m linear_spatial_propagation_gspn_amd.build`" % LIB_PATH)
+            h = ctypes.CDLL(LIB_PATH)
+            i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+            h.gspn_normalize_weights.argtypes = [ci, i64, i64, i64, i64, vp, vp, ci, vp]
+            h.gspn_scan_fwd.argtypes = [ci, i64, i64, i64, i64, i64, i64, vp, vp, ci, vp, vp, ci, ci, vp]
+            h.gspn_merge4.argtypes = [vp, vp, vp, vp, vp, i64, ci, vp]
+            h.gspn_proxy_project.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, ci, vp]
+            h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), vp, ci, vp]
+            for name in ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4",
+                         "gspn_proxy_project", "gspn_forward4"):
+                getattr(h, name).restype = ci
+            h.gspn_status_string.argtypes = [ci]
+            h.gspn_status_string.restype = ctypes.c_char_p
+            h.gspn_abi_version.argtypes = []
+            h.gspn_abi_version.restype = ci
+            _lib = h
+        return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GSPN_F32
+    if t.dtype == torch.bfloat16:
+        return GSPN_BF16
+    raise TypeError("libgspn stores float32 or bfloat16, got %s" % t.dtype)
+
+
+def _check(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError("%s must live on %s (a HIP device)" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _raise(st: int, call: str) -> None:
+    if st != 0:
+        raise GspnError(st, call)
+
+
+def frame_shape(direction: int, h: int, w: int) -> tuple[int, int]:
+    """(S, L): scan steps and line length of a direction."""
+    return (w, h) if direction in (L2R, R2L) else (h, w)
+
+
+def to_scan_frame(t: torch.Tensor, direction: int) -> torch.Tensor:
+    """An [..., H, W] tensor in the scan frame of ``direction`` (contiguous
+    copy of the transpose for the horizontal directions)."""
+    return t.transpose(-1, -2).contiguous() if direction in (L2R, R2L) else t.contiguous()
+
+
+def gspn_normalize_weights(direction: int, logits: torch.Tensor, h: int, w: int,
+                           out: torch.Tensor | None = None) -> torch.Tensor:
+    """Sigmoid + row normalisation of one direction's logits [N][Cw][3][S][L]."""
+    n, cw = logits.shape[0], logits.shape[1]
+    S, L = frame_shape(direction, h, w)
+    _check(logits, "logits", (n, cw, 3, S, L), logits.dtype, logits.device)
+    if out is None:
+        out = torch.empty_like(logits)
+    _check(out, "out", logits.shape, logits.dtype, logits.device)
+    _raise(lib().gspn_normalize_weights(direction, n, cw, h, w, _ptr(logits), _ptr(out),
+                                        _dtype_code(logits), _stream(logits.device)),
+           "gspn_normalize_weights")
+    return out
+
+
+def gspn_scan_fwd(direction: int, x: torch.Tensor, wts: torch.Tensor, lam: torch.Tensor,
+                  chunk_len: int = 0, wts_are_logits: bool = True,
+                  out: torch.Tensor | None = None, accumulate: bool = False) -> torch.Tensor:
+    """One direction of the line scan.  x [N][C][H][W]; wts [N][Cw][3][S][L];
+    lam [N][C][S][L]; returns out (= h, or out += h when accumulate)."""
+    n, c, h, w = x.shape
+    S, L = frame_shape(direction, h, w)
+    dt = x.dtype
+    cw = wts.shape[1] if wts.dim() == 5 else -1
+    _check(x, "x", (n, c, h, w), dt, x.device)
+    _check(wts, "wts", (n, cw, 3, S, L), dt, x.device)
+    _check(lam, "lam", (n, c, S, L), dt, x.device)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an out tensor")
+        out = torch.empty_like(x)
+    _check(out, "out", (n, c, h, w), dt, x.device)
+    _raise(lib().gspn_scan_fwd(direction, int(chunk_len), n, c, h, w, cw, _ptr(x), _ptr(wts),
+                               1 if wts_are_logits else 0, _ptr(lam), _ptr(out),
+                               1 if accumulate else 0, _dtype_code(x), _stream(x.device)),
+           "gspn_scan_fwd")
+    return out
+
+
+def gspn_merge4(hs: Sequence[torch.Tensor], out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = h0 + h1 + h2 + h3 elementwise."""
+    h0 = hs[0]
+    _dtype_code(h0)
+    for i, t in enumerate(hs):
+        _check(t, "h%d" % i, h0.shape, h0.dtype, h0.device)
+    if out is None:
+        out = torch.empty_like(h0)
+    _check(out, "out", h0.shape, h0.dtype, h0.device)
+    _raise(lib().gspn_merge4(_ptr(hs[0]), _ptr(hs[1]), _ptr(hs[2]), _ptr(hs[3]), _ptr(out),
+                             h0.numel(), _dtype_code(h0), _stream(h0.device)), "gspn_merge4")
+    return out
+
+
+def gspn_proxy_project(inp: torch.Tensor, weight: torch.Tensor,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """1x1 projection: out[n, o] = sum_c weight[o, c] inp[n, c] per pixel."""
+    n, cin, h, w = inp.shape
+    cout = weight.shape[0]
+    _check(inp, "inp", (n, cin, h, w), inp.dtype, inp.device)
+    _check(weight, "weight", (cout, cin), inp.dtype, inp.device)
+    if out is None:
+        out = torch.empty((n, cout, h, w), dtype=inp.dtype, device=inp.device)
+    _check(out, "out", (n, cout, h, w), inp.dtype, inp.device)
+    _raise(lib().gspn_proxy_project(n, cin, h, w, cout, _ptr(inp), _ptr(weight), _ptr(out),
+                                    _dtype_code(inp), _stream(inp.device)), "gspn_proxy_project")
+    return out
+
+
+def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                  chunk_len: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Four-direction propagation with summed merge; logits[d] / lams[d] in
+    direction d's scan frame."""
+    n, c, h, w = x.shape
+    dt = x.dtype
+    cw = logits[0].shape[1]
+    _check(x, "x", (n, c, h, w), dt, x.device)
+    for d in range(4):
+        S, L = frame_shape(d, h, w)
+        _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
+        _check(lams[d], "lam[%d]" % d, (n, c, S, L), dt, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (n, c, h, w), dt, x.device)
+    zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
+    lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
+    _raise(lib().gspn_forward4(n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, _ptr(out),
+                               _dtype_code(x), _stream(x.device)), "gspn_forward4")
+    return out
+
+
+def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
+                        logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                        chunk_len: int = 0) -> torch.Tensor:
+    """Compressive-proxy forward: C -> C_proxy projection, four-direction scan in
+    proxy space, C_proxy -> C projection (three libgspn calls)."""
+    xp = gspn_proxy_project(x, w_down)
+    yp = gspn_forward4(xp, logits, lams, chunk_len)
+    return gspn_proxy_project(yp, w_up)

@@ -1,0 +1,140 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and host-side validation rejects bad arguments before anything reaches a
+device.  No call here passes validation with a non-empty tensor, so nothing
+is ever launched (there is no GPU in this suite)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_spatial_propagation_gspn_amd import gspn as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gspn.h")
+
+OK, NULLP, SHAPE, DIR, DTYPE, CHUNK, WCH, MISAL, ALIAS, UNSUP, HIP = range(11)
+
+# Fake, never-dereferenced device addresses (validation only compares them).
+A = 0x10000000
+B = 0x20000000
+C_ = 0x30000000
+D_ = 0x40000000
+E_ = 0x50000000
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gspn_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return G.lib()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(G.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.gspn_abi_version() == 1
+    for code in range(11):
+        s = lib.gspn_status_string(code).decode()
+        assert s.startswith(G.STATUS[code])
+    assert lib.gspn_status_string(99).decode() == "unknown gspn_status"
+
+
+def scan(lib, dir=0, chunk=0, n=1, c=2, h=8, w=8, cw=2, x=A, wts=B, logits=1, lam=C_, out=D_,
+         acc=0, dt=0):
+    return lib.gspn_scan_fwd(dir, chunk, n, c, h, w, cw, x, wts, logits, lam, out, acc, dt, None)
+
+
+def test_scan_validation(lib):
+    assert scan(lib, dt=2) == DTYPE
+    assert scan(lib, dir=4) == DIR
+    assert scan(lib, dir=-1) == DIR
+    assert scan(lib, n=-1) == SHAPE
+    assert scan(lib, h=1 << 31) == SHAPE
+    assert scan(lib, n=1 << 20, c=1 << 20, h=1 << 20, w=1 << 10) == SHAPE  # > 2^58 elements
+    assert scan(lib, chunk=-1) == CHUNK
+    assert scan(lib, cw=3) == WCH
+    assert scan(lib, c=1, cw=2) == WCH
+    assert scan(lib, w=8193) == UNSUP                    # vertical line longer than the limit
+    assert scan(lib, dir=2, h=8193, w=4) == UNSUP        # horizontal lines run along H
+    assert scan(lib, x=0) == NULLP
+    assert scan(lib, wts=0) == NULLP
+    assert scan(lib, lam=0) == NULLP
+    assert scan(lib, out=0) == NULLP
+    assert scan(lib, x=A + 2) == MISAL
+    assert scan(lib, dt=1, x=A + 1) == MISAL
+    assert scan(lib, out=A) == ALIAS                     # out == x
+    assert scan(lib, out=B + 64) == ALIAS                # inside the weights
+    assert scan(lib, out=C_ + 4) == ALIAS                # inside lambda
+
+
+def test_scan_empty_is_a_no_op(lib):
+    # An empty tensor returns OK without looking at pointers (all NULL here).
+    assert scan(lib, n=0, x=0, wts=0, lam=0, out=0) == OK
+    assert scan(lib, h=0, x=0, wts=0, lam=0, out=0) == OK
+    # ...but enum and chunk checks still run first.
+    assert scan(lib, n=0, dir=7) == DIR
+
+
+def test_forward4_validation(lib):
+    vp4 = ctypes.c_void_p * 4
+    zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
+    ls = vp4(C_, C_, C_, C_)
+    f = lib.gspn_forward4
+    assert f(1, 2, 8, 8, 2, 0, A, zs, ls, D_, 3, None) == DTYPE
+    assert f(1, 2, 8, 8, 3, 0, A, zs, ls, D_, 0, None) == WCH
+    assert f(1, 2, 8, 8, 2, -2, A, zs, ls, D_, 0, None) == CHUNK
+    assert f(1, 2, 8, 8, 2, 0, 0, zs, ls, D_, 0, None) == NULLP
+    assert f(1, 2, 8, 8, 2, 0, A, vp4(B, 0, B, B), ls, D_, 0, None) == NULLP
+    assert f(1, 2, 8, 8, 2, 0, A, zs, ls, A, 0, None) == ALIAS
+    assert f(1, 2, 8, 8, 2, 0, A, zs, ls, C_, 0, None) == ALIAS
+    assert f(1, 2, 8, 8, 2, 0, A, zs, vp4(C_, C_, C_, C_ + 1), D_, 0, None) == MISAL
+    assert f(0, 2, 8, 8, 2, 0, 0, None, None, 0, 0, None) == OK
+
+
+def test_normalize_merge_project_validation(lib):
+    nw = lib.gspn_normalize_weights
+    assert nw(0, 1, 1, 4, 4, A, B, 5, None) == DTYPE
+    assert nw(9, 1, 1, 4, 4, A, B, 0, None) == DIR
+    assert nw(0, -1, 1, 4, 4, A, B, 0, None) == SHAPE
+    assert nw(0, 1, 1, 4, 4, 0, B, 0, None) == NULLP
+    assert nw(0, 1, 1, 4, 4, A, A + 8, 0, None) == ALIAS
+    assert nw(0, 1, 1, 4, 4, A, B + 2, 0, None) == MISAL
+    assert nw(0, 0, 1, 4, 4, 0, 0, 0, None) == OK
+
+    m4 = lib.gspn_merge4
+    assert m4(A, B, C_, D_, E_, 10, 7, None) == DTYPE
+    assert m4(A, B, C_, D_, E_, -1, 0, None) == SHAPE
+    assert m4(A, 0, C_, D_, E_, 10, 0, None) == NULLP
+    assert m4(A, B, C_, D_, D_ + 4, 10, 0, None) == ALIAS
+    assert m4(A, B, C_, D_, E_ + 1, 10, 1, None) == MISAL
+    assert m4(0, 0, 0, 0, 0, 0, 0, None) == OK
+
+    pp = lib.gspn_proxy_project
+    assert pp(1, 8, 4, 4, 2, A, B, C_, 9, None) == DTYPE
+    assert pp(1, -8, 4, 4, 2, A, B, C_, 0, None) == SHAPE
+    assert pp(1, 0, 4, 4, 2, A, B, C_, 0, None) == SHAPE
+    assert pp(1, 8, 4, 4, 2, A, 0, C_, 0, None) == NULLP
+    assert pp(1, 8, 4, 4, 2, A, B, A + 16, 0, None) == ALIAS
+    assert pp(1, 8, 4, 4, 2, A, B, B, 0, None) == ALIAS
+    assert pp(1, 8, 4, 4, 2, A + 2, B, C_, 0, None) == MISAL
+    assert pp(1, 8, 4, 4, 0, 0, 0, 0, 0, None) == OK
+
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    x = torch.zeros(1, 2, 4, 4)
+    with pytest.raises(ValueError):
+        # CPU tensors never reach the library
+        G.gspn_scan_fwd(0, x, torch.zeros(1, 2, 3, 4, 4), torch.zeros(1, 2, 4, 4))
+    with pytest.raises(TypeError):
+        G.gspn_merge4([x.double()] * 4)
