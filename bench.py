@@ -71,35 +71,66 @@ def scan_launch_bytes(wl, accumulate: bool) -> int:
     return u + z + u + u + (u if accumulate else 0)
 
 
-def run_step(wl, inp, out):
+def scan4_launch_bytes(wl) -> int:
+    """Compulsory bytes of one four-direction launch: x once, the four
+    directions' logits and lambda once, four output maps written once."""
+    es = esize(wl)
+    u = wl.n * wl.c_scan * wl.h * wl.w * es
+    z = wl.n * wl.cw * 3 * wl.h * wl.w * es
+    return u + 4 * z + 4 * u + 4 * u
+
+
+# Mirror of the library's rule (api.cpp): with a workspace, gspn_forward4 runs
+# the four directions in one launch when one direction has fewer than 512
+# (plane, chunk) lines and no line exceeds 2048 positions.
+def uses_fused_path(wl) -> bool:
+    most = 0
+    for S in (wl.h, wl.w):
+        k = S if wl.chunk in (0,) or wl.chunk >= S else wl.chunk
+        most = max(most, wl.n * wl.c_scan * ((S + k - 1) // k))
+    return most < 512 and max(wl.h, wl.w) <= 2048
+
+
+def run_step(wl, inp, out, ws):
     if wl.c_proxy:
         return G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
                                      chunk_len=wl.chunk)
-    return G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out)
+    return G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out,
+                           workspace=ws)
 
 
-def time_scan_kernel(wl, inp, reps: int):
-    """Per-launch durations of the scan kernel (HIP events on the launch stream)."""
-    if wl.c_proxy:
-        x = G.gspn_proxy_project(inp["x"], inp["w_down"])
-    else:
-        x = inp["x"]
-    out = torch.empty_like(x)
+def _time(fn, reps: int) -> float:
+    """Average ms of fn() over reps launches, HIP events on the current stream."""
     stream = torch.cuda.current_stream()
-    per_dir = []
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def time_dominant_kernel(wl, inp, reps: int) -> dict:
+    """Per-launch duration of the scan kernel in the configuration the step uses."""
+    x = G.gspn_proxy_project(inp["x"], inp["w_down"]) if wl.c_proxy else inp["x"]
+    if uses_fused_path(wl):
+        outs = [torch.empty_like(x) for _ in range(4)]
+        ms = _time(lambda: G.gspn_scan4_fwd(x, inp["logits"], inp["lam"], wl.chunk, outs), reps)
+        return {"kernel": "scan4_kernel", "kernel_ms": ms, "bytes_per_launch": scan4_launch_bytes(wl)}
+    out = torch.empty_like(x)
+    per_dir, total_bytes = [], 0
     for d in range(4):
         acc = d > 0
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        G.gspn_scan_fwd(d, x, inp["logits"][d], inp["lam"][d], wl.chunk, out=out, accumulate=acc)
-        for a, b in evs:
-            a.record(stream)
-            G.gspn_scan_fwd(d, x, inp["logits"][d], inp["lam"][d], wl.chunk, out=out, accumulate=acc)
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
-        per_dir.append((ms, scan_launch_bytes(wl, acc)))
-    return per_dir
+        ms = _time(lambda: G.gspn_scan_fwd(d, x, inp["logits"][d], inp["lam"][d], wl.chunk, out=out,
+                                           accumulate=acc), reps)
+        per_dir.append(ms)
+        total_bytes += scan_launch_bytes(wl, acc)
+    return {"kernel": "scan_kernel", "kernel_ms": sum(per_dir) / 4, "bytes_per_launch": total_bytes // 4,
+            "per_direction_ms": [round(m, 4) for m in per_dir]}
 
 
 def cpu_baseline(wl, inp):
@@ -130,6 +161,17 @@ def cpu_baseline(wl, inp):
                       % (budget_planes, planes, wl.h, wl.w, dt)}
 
 
+def copy_check(mib: int) -> None:
+    """A plain device-to-device copy of known size: reads and writes mib MiB
+    per launch.  Used to calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms = _time(lambda: b.copy_(a), 10)
+    print(json.dumps({"copy_MiB": mib, "ms": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,22 +179,28 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="profile", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)",
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_check:
+        copy_check(args.copy_check)
+        return
     wl = WORKLOADS[args.workload]
     torch.cuda.init()
     G.lib()
     print("bench: workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
     inp = make_inputs(wl, "cuda")
     out = torch.empty_like(inp["x"]) if not wl.c_proxy else None
+    ws = G.forward4_workspace(inp["x"]) if not wl.c_proxy else None
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        run_step(wl, inp, out)
+        run_step(wl, inp, out, ws)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -162,7 +210,7 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        run_step(wl, inp, out)
+        run_step(wl, inp, out, ws)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -170,10 +218,8 @@ def main():
     print("bench: %.3f ms/step (wall %.3f ms/step)" % (ms, wall * 1e3 / args.steps),
           file=sys.stderr, flush=True)
 
-    per_dir = time_scan_kernel(wl, inp, reps=max(3, min(args.steps, 10)))
-    k_ms = sum(m for m, _ in per_dir) / 4
-    k_bytes = sum(b for _, b in per_dir) / 4
-    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    dom = time_dominant_kernel(wl, inp, reps=max(3, min(args.steps, 10)))
+    achieved = dom["bytes_per_launch"] / (dom["kernel_ms"] * 1e-3) / 1e9
     alg = algorithmic_bytes(wl)
     eff = alg / (ms * 1e-3) / 1e9
 
@@ -193,7 +239,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.dtype == "f32" else "bf16 storage, f32 arithmetic",
+        "dtype": "f32",
         "data": "synthetic (seeded)",
         "config": {"workload": wl.name, "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
@@ -201,11 +247,9 @@ def main():
         "effective_GBps": round(eff, 1),
         "effective_frac": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": alg,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "scan_kernel", "kernel_ms": round(k_ms, 4),
-                     "bytes_per_launch": int(k_bytes),
-                     "per_direction_ms": [round(m, 4) for m, _ in per_dir]},
+        "roofline": dict({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                         **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in dom.items()}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

@@ -80,7 +80,8 @@ typedef enum {
     GSPN_ERR_MISALIGNED = 7,
     GSPN_ERR_ALIASING = 8,
     GSPN_ERR_UNSUPPORTED = 9,
-    GSPN_ERR_HIP = 10
+    GSPN_ERR_HIP = 10,
+    GSPN_ERR_WORKSPACE = 11
 } gspn_status;
 
 typedef enum { GSPN_T2B = 0, GSPN_B2T = 1, GSPN_L2R = 2, GSPN_R2L = 3 } gspn_dir;
@@ -139,16 +140,49 @@ gspn_status gspn_proxy_project(int64_t n, int64_t c_in, int64_t h, int64_t w, in
                                void* stream);
 
 /*
+ * gspn_scan4_fwd -- the four directions' scans of one forward in a single
+ * launch, each writing its own output: out[d] = scan_d(x, logits[d], lam[d])
+ * for d in (T2B, B2T, L2R, R2L) (GSPN-2 notes, "2D spatial propagation
+ * recap": four line scans over the same x).  The four directions run
+ * concurrently.  Shapes as for gspn_forward4; out is a host array of 4
+ * device pointers, each [n][c][h][w], pairwise disjoint and overlapping no
+ * input.  Lines may hold at most 2048 positions (else GSPN_ERR_UNSUPPORTED).
+ */
+gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                           int64_t chunk_len, const void* x, const void* const logits[4],
+                           const void* const lam[4], void* const out[4], int dtype, void* stream);
+
+/*
+ * gspn_forward4_workspace_bytes -- bytes of the optional gspn_forward4
+ * workspace: three partial output maps, 3 * n*c*h*w elements of the storage
+ * type.  Returns -1 when the arguments are invalid (negative or overflowing
+ * dimensions, unknown dtype).
+ */
+int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int dtype);
+
+/*
  * gspn_forward4 -- the four-direction propagation with summed merge:
  *   y = sum over d in (T2B, B2T, L2R, R2L) of scan_d(x, logits[d], lam[d]).
  *   logits[d]  [n][cw][3][S_d][L_d] logits of direction d (normalised inside).
  *   lam[d]     [n][c][S_d][L_d]; the same pointer may be given for all d.
  *   logits and lam are host arrays of 4 device pointers, indexed by gspn_dir.
  *   y          [n][c][h][w] output; may not overlap any input.
+ *   workspace  optional device buffer of workspace_bytes bytes.  NULL (or 0
+ *              bytes): the directions run one after another, the first
+ *              writing y and the others adding to it.  Otherwise it must hold
+ *              gspn_forward4_workspace_bytes() bytes (else GSPN_ERR_WORKSPACE)
+ *              and overlap neither y nor any input (else GSPN_ERR_ALIASING);
+ *              when there are too few planes to fill the GPU with one
+ *              direction at a time, the library then runs all four
+ *              directions in one launch, three of them into the workspace,
+ *              and adds those into y.  Its contents afterwards are
+ *              unspecified.  Either way y is the same up to fp32 rounding
+ *              order (and, for bf16, rounding of the partial maps).
  */
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
-                          const void* const lam[4], void* y, int dtype, void* stream);
+                          const void* const lam[4], void* y, void* workspace,
+                          int64_t workspace_bytes, int dtype, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgspn.so")
-SOURCES = ["api.cpp", "scan.hip", "scan_f32_vert.hip", "scan_f32_horiz.hip", "scan_bf16_vert.hip",
+SOURCES = ["api.cpp", "scan.hip", "scan_f32_vert.hip", "scan_f32_horiz.hip", "scan_bf16_vert.hip", "scan4_f32.hip", "scan4_bf16.hip",
            "scan_bf16_horiz.hip", "elementwise.hip", "project.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -35,30 +35,33 @@ DEVICE = [
 ]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE + ["-x", "hip", "-c", path, "-o", obj]
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [HIPCC] + COMMON + DEVICE + ["-D" + d for d in defines] + ["-x", "hip", "-c", path, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libgspn.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile every source and link libgspn.so (always rebuilds).  ``out`` and
+    ``defines`` (preprocessor NAME=VALUE pairs, e.g. launch-configuration
+    overrides) allow variant builds elsewhere."""
+    build_dir = BUILD if out == LIB else os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, build_dir, tuple(defines)), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -18,6 +18,9 @@ using gspn::kF32;
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxElems = int64_t{1} << 58;
+// Most (plane, chunk) lines per direction for which gspn_forward4 runs the
+// four directions concurrently when given a workspace.
+constexpr int64_t kFuse4MaxBlocks = 512;
 
 bool valid_dtype(int dt) { return dt == GSPN_F32 || dt == GSPN_BF16; }
 size_t elem_size(int dt) { return dt == GSPN_F32 ? 4 : 2; }
@@ -101,6 +104,7 @@ const char* gspn_status_string(int status) {
         case GSPN_ERR_UNSUPPORTED:
             return "GSPN_ERR_UNSUPPORTED: line longer than GSPN_MAX_LINE or grid too large";
         case GSPN_ERR_HIP: return "GSPN_ERR_HIP: a HIP launch failed";
+        case GSPN_ERR_WORKSPACE: return "GSPN_ERR_WORKSPACE: the workspace is smaller than required";
         default: return "unknown gspn_status";
     }
 }
@@ -188,9 +192,64 @@ gspn_status gspn_proxy_project(int64_t n, int64_t c_in, int64_t h, int64_t w, in
     return from_hip(gspn::launch_project(n, c_in, h * w, c_out, in, weight, out, dtype, as_stream(stream)));
 }
 
+gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                           int64_t chunk_len, const void* x, const void* const logits[4],
+                           const void* const lam[4], void* const out[4], int dtype, void* stream) {
+    int64_t chunks[4];
+    for (int d = 0; d < 4; ++d) {
+        bool empty = false;
+        const ScanCheck ck = check_scan(d, chunk_len, n, c, h, w, cw, dtype, &empty);
+        if (ck.st != GSPN_OK || empty) return ck.st;
+        chunks[d] = ck.chunk;
+    }
+    if (!gspn::fused4_supported(h, w)) return GSPN_ERR_UNSUPPORTED;
+    if (!x || !logits || !lam || !out) return GSPN_ERR_NULL_POINTER;
+    for (int d = 0; d < 4; ++d)
+        if (!logits[d] || !lam[d] || !out[d]) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    if (!aligned(x, es)) return GSPN_ERR_MISALIGNED;
+    for (int d = 0; d < 4; ++d)
+        if (!aligned(logits[d], es) || !aligned(lam[d], es) || !aligned(out[d], es))
+            return GSPN_ERR_MISALIGNED;
+    const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
+    const int64_t wb = n * cw * 3 * h * w * static_cast<int64_t>(es);
+    for (int d = 0; d < 4; ++d) {
+        if (overlap(out[d], xb, x, xb)) return GSPN_ERR_ALIASING;
+        for (int e = 0; e < 4; ++e) {
+            if (overlap(out[d], xb, logits[e], wb) || overlap(out[d], xb, lam[e], xb))
+                return GSPN_ERR_ALIASING;
+            if (e != d && overlap(out[d], xb, out[e], xb)) return GSPN_ERR_ALIASING;
+        }
+    }
+    gspn::ScanParams p[4];
+    for (int d = 0; d < 4; ++d) {
+        p[d].x = x;
+        p[d].wts = logits[d];
+        p[d].lam = lam[d];
+        p[d].out = out[d];
+        p[d].n = n;
+        p[d].c = c;
+        p[d].cw = cw;
+        p[d].h = h;
+        p[d].w = w;
+        p[d].dir = d;
+        p[d].chunk = chunks[d];
+        p[d].wts_are_logits = 1;
+        p[d].accumulate = 0;
+        p[d].dtype = dtype;
+    }
+    return from_hip(gspn::launch_scan4(p, as_stream(stream)));
+}
+
+int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int dtype) {
+    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w})) return -1;
+    return 3 * checked_product({n, c, h, w}) * static_cast<int64_t>(elem_size(dtype));
+}
+
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
-                          const void* const lam[4], void* y, int dtype, void* stream) {
+                          const void* const lam[4], void* y, void* workspace,
+                          int64_t workspace_bytes, int dtype, void* stream) {
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -210,26 +269,54 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (overlap(y, xb, x, xb)) return GSPN_ERR_ALIASING;
     for (int d = 0; d < 4; ++d)
         if (overlap(y, xb, logits[d], wb) || overlap(y, xb, lam[d], xb)) return GSPN_ERR_ALIASING;
+    const bool have_ws = workspace != nullptr && workspace_bytes > 0;
+    if (have_ws) {
+        if (workspace_bytes < 3 * xb) return GSPN_ERR_WORKSPACE;
+        if (!aligned(workspace, es)) return GSPN_ERR_MISALIGNED;
+        const int64_t sb = 3 * xb;
+        if (overlap(workspace, sb, y, xb) || overlap(workspace, sb, x, xb)) return GSPN_ERR_ALIASING;
+        for (int d = 0; d < 4; ++d)
+            if (overlap(workspace, sb, logits[d], wb) || overlap(workspace, sb, lam[d], xb))
+                return GSPN_ERR_ALIASING;
+    }
 
-    // Four passes on one stream: the first writes y, the others add to it.
+    gspn::ScanParams p[4];
     for (int d = 0; d < 4; ++d) {
-        gspn::ScanParams p;
-        p.x = x;
-        p.wts = logits[d];
-        p.lam = lam[d];
-        p.out = y;
-        p.n = n;
-        p.c = c;
-        p.cw = cw;
-        p.h = h;
-        p.w = w;
-        p.dir = d;
-        p.chunk = chunks[d];
-        p.wts_are_logits = 1;
-        p.accumulate = d > 0 ? 1 : 0;
-        p.dtype = dtype;
-        const hipError_t e = gspn::launch_scan(p, as_stream(stream));
-        if (e != hipSuccess) return GSPN_ERR_HIP;
+        p[d].x = x;
+        p[d].wts = logits[d];
+        p[d].lam = lam[d];
+        p[d].out = y;
+        p[d].n = n;
+        p[d].c = c;
+        p[d].cw = cw;
+        p[d].h = h;
+        p[d].w = w;
+        p[d].dir = d;
+        p[d].chunk = chunks[d];
+        p[d].wts_are_logits = 1;
+        p[d].accumulate = 0;
+        p[d].dtype = dtype;
+    }
+    // Concurrent path: worth it while one direction's (plane, chunk) lines
+    // cannot keep the GPU's 256 compute units busy twice over.
+    int64_t most_blocks = 0;
+    for (int d = 0; d < 4; ++d) {
+        const int64_t S = horizontal(d) ? w : h;
+        const int64_t nb = n * c * ((S + chunks[d] - 1) / chunks[d]);
+        most_blocks = nb > most_blocks ? nb : most_blocks;
+    }
+    if (have_ws && most_blocks < kFuse4MaxBlocks && gspn::fused4_supported(h, w)) {
+        char* ws = static_cast<char*>(workspace);
+        for (int d = 1; d < 4; ++d) p[d].out = ws + (d - 1) * xb;
+        if (gspn::launch_scan4(p, as_stream(stream)) != hipSuccess) return GSPN_ERR_HIP;
+        return from_hip(gspn::launch_merge_into(y, p[1].out, p[2].out, p[3].out, n * c * h * w, dtype,
+                                                as_stream(stream)));
+    }
+    // Sequential path: one direction per launch; the first writes y, the
+    // others add to it.
+    for (int d = 0; d < 4; ++d) {
+        p[d].accumulate = d > 0 ? 1 : 0;
+        if (gspn::launch_scan(p[d], as_stream(stream)) != hipSuccess) return GSPN_ERR_HIP;
     }
     return GSPN_OK;
 }

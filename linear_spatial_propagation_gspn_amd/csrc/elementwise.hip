@@ -45,6 +45,43 @@ __global__ __launch_bounds__(256) void merge4_kernel(const T* __restrict__ h0, c
     }
 }
 
+// y = ((y + w1) + w2) + w3, 16 bytes per lane per access where aligned.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_into_kernel(T* y, const T* __restrict__ w1,
+                                                         const T* __restrict__ w2,
+                                                         const T* __restrict__ w3, int64_t numel,
+                                                         int vec) {
+    constexpr int VW = 16 / static_cast<int>(sizeof(T));
+    struct alignas(16) V {
+        T e[VW];
+    };
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    int64_t done = 0;
+    if (vec) {
+        const int64_t nv = numel / VW;
+        for (int64_t e = first; e < nv; e += stride) {
+            V a = reinterpret_cast<const V*>(y)[e];
+            const V b = reinterpret_cast<const V*>(w1)[e];
+            const V c = reinterpret_cast<const V*>(w2)[e];
+            const V d = reinterpret_cast<const V*>(w3)[e];
+#pragma unroll
+            for (int j = 0; j < VW; ++j) {
+                const float v = ((Store<T>::ld(&a.e[j]) + Store<T>::ld(&b.e[j])) + Store<T>::ld(&c.e[j])) +
+                                Store<T>::ld(&d.e[j]);
+                Store<T>::st(&a.e[j], v);
+            }
+            reinterpret_cast<V*>(y)[e] = a;
+        }
+        done = nv * VW;
+    }
+    for (int64_t e = done + first; e < numel; e += stride) {
+        const float v = ((Store<T>::ld(y + e) + Store<T>::ld(w1 + e)) + Store<T>::ld(w2 + e)) +
+                        Store<T>::ld(w3 + e);
+        Store<T>::st(y + e, v);
+    }
+}
+
 unsigned grid_for(int64_t total, int threads) {
     int64_t blocks = (total + threads - 1) / threads;
     const int64_t cap = 256 * 64;  // 64 workgroups per CU is plenty for a grid-stride loop
@@ -53,7 +90,26 @@ unsigned grid_for(int64_t total, int threads) {
     return static_cast<unsigned>(blocks);
 }
 
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
 }  // namespace
+
+hipError_t launch_merge_into(void* y, const void* w1, const void* w2, const void* w3, int64_t numel,
+                             int dtype, hipStream_t stream) {
+    const int vec = aligned16(y) && aligned16(w1) && aligned16(w2) && aligned16(w3);
+    const int64_t per = vec ? (dtype == kF32 ? 4 : 8) : 1;
+    const unsigned grid = grid_for((numel + per - 1) / per, 256);
+    if (dtype == kF32) {
+        hipLaunchKernelGGL(merge_into_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<float*>(y), static_cast<const float*>(w1),
+                           static_cast<const float*>(w2), static_cast<const float*>(w3), numel, vec);
+    } else {
+        hipLaunchKernelGGL(merge_into_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<bf16_t*>(y), static_cast<const bf16_t*>(w1),
+                           static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w3), numel, vec);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
                             const void* logits, void* w_out, int dtype, hipStream_t stream) {

@@ -24,11 +24,20 @@ struct ScanParams {
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
 
+// The four directions of one forward in one launch; p[d] describes direction d
+// (each with its own output buffer, accumulate = 0).
+hipError_t launch_scan4(const ScanParams (&p)[4], hipStream_t stream);
+bool fused4_supported(int64_t h, int64_t w);
+
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
                             const void* logits, void* w_out, int dtype, hipStream_t stream);
 
 hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
                          int64_t numel, int dtype, hipStream_t stream);
+
+// y = ((y + w1) + w2) + w3 in place.
+hipError_t launch_merge_into(void* y, const void* w1, const void* w2, const void* w3, int64_t numel,
+                             int dtype, hipStream_t stream);
 
 hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const void* in,
                           const void* weight, void* out, int dtype, hipStream_t stream);

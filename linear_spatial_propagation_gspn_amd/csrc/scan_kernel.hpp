@@ -60,56 +60,119 @@ struct alignas(sizeof(T) * N) VecT {
     T e[N];
 };
 
+// Streaming access: the scan reads each logit, lambda and (vertical) x value
+// once and writes each output once.  With GSPN_STREAM_NT=1 those accesses
+// carry the nontemporal hint; measured on MI355X it slows the scan by about
+// half (profile workload, scan4 3.35 -> 4.97 ms), so it is off by default.
+#ifndef GSPN_STREAM_NT
+#define GSPN_STREAM_NT 0
+#endif
+
+template <typename T, int N>
+struct Ext {
+    typedef T type __attribute__((ext_vector_type(N)));
+};
+template <typename T>
+struct Ext<T, 1> {
+    typedef T type;
+};
+
+template <typename T, int N, bool NT>
+__device__ __forceinline__ VecT<T, N> vload(const T* p) {
+    if constexpr (NT && GSPN_STREAM_NT) {
+        using V = typename Ext<T, N>::type;
+        const V v = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+        VecT<T, N> r;
+        if constexpr (N == 1) {
+            r.e[0] = v;
+        } else {
+#pragma unroll
+            for (int j = 0; j < N; ++j) r.e[j] = v[j];
+        }
+        return r;
+    } else {
+        return *reinterpret_cast<const VecT<T, N>*>(p);
+    }
+}
+
+template <typename T, int N, bool NT>
+__device__ __forceinline__ void vstore(T* p, const VecT<T, N>& r) {
+    if constexpr (NT && GSPN_STREAM_NT) {
+        using V = typename Ext<T, N>::type;
+        V v;
+        if constexpr (N == 1) {
+            v = r.e[0];
+        } else {
+#pragma unroll
+            for (int j = 0; j < N; ++j) v[j] = r.e[j];
+        }
+        __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+    } else {
+        *reinterpret_cast<VecT<T, N>*>(p) = r;
+    }
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ float sload(const T* p) {
+    const VecT<T, 1> r = vload<T, 1, NT>(p);
+    return Store<T>::ld(&r.e[0]);
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void sstore(T* p, float v) {
+    VecT<T, 1> r;
+    Store<T>::st(&r.e[0], v);
+    vstore<T, 1, NT>(p, r);
+}
+
 // P values of a line starting at position k0; positions >= L read as 0.
-template <typename T, int P>
+template <typename T, int P, bool NT>
 __device__ __forceinline__ void load_run(const T* __restrict__ base, int k0, int L, bool vec,
                                          float (&dst)[P]) {
     if (vec) {
-        const VecT<T, P> v = *reinterpret_cast<const VecT<T, P>*>(base + k0);
+        const VecT<T, P> v = vload<T, P, NT>(base + k0);
 #pragma unroll
         for (int j = 0; j < P; ++j) dst[j] = Store<T>::ld(&v.e[j]);
     } else {
 #pragma unroll
-        for (int j = 0; j < P; ++j) dst[j] = (k0 + j < L) ? Store<T>::ld(base + k0 + j) : 0.0f;
+        for (int j = 0; j < P; ++j) dst[j] = (k0 + j < L) ? sload<T, NT>(base + k0 + j) : 0.0f;
     }
 }
 
-template <typename T, int P>
+template <typename T, int P, bool NT>
 __device__ __forceinline__ void store_run(T* __restrict__ base, int k0, int L, bool vec,
                                           const float (&src)[P]) {
     if (vec) {
         VecT<T, P> v;
 #pragma unroll
         for (int j = 0; j < P; ++j) Store<T>::st(&v.e[j], src[j]);
-        *reinterpret_cast<VecT<T, P>*>(base + k0) = v;
+        vstore<T, P, NT>(base + k0, v);
     } else {
 #pragma unroll
         for (int j = 0; j < P; ++j)
-            if (k0 + j < L) Store<T>::st(base + k0 + j, src[j]);
+            if (k0 + j < L) sstore<T, NT>(base + k0 + j, src[j]);
     }
 }
 
+// One line scan: plane p, chunk q of the direction described by a.
 // T: storage type.  P: positions per lane.  D: prefetch ring depth.
 // U: steps per block (a multiple of D; the horizontal tile width).
-// HORIZ / REV: direction.  MAXT: most lanes per workgroup.
-template <typename T, int P, int D, int U, bool HORIZ, bool REV, int MAXT>
-__global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
+// HORIZ / REV: direction.  Every lane of the workgroup takes part (lanes past
+// the end of the line hold no positions but join every barrier).
+// edge_raw: 4 * blockDim.x floats of LDS for the neighbour exchange.
+template <typename T, int P, int D, int U, bool HORIZ, bool REV>
+__device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, float* edge_raw) {
     static_assert(U % D == 0, "a block must hold whole ring turns");
     constexpr int VW = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte vector
     static_assert(!HORIZ || U % VW == 0, "tile width must be whole vectors");
 
-    // Edge exchange, [buffer][0 = first position, 1 = last position][lane],
-    // sized to the launch (4 * blockDim.x floats).
-    extern __shared__ float s_edge_raw[];
+    // Edge exchange, [buffer][0 = first position, 1 = last position][lane].
     auto edge = [&](int b, int which, int lane) -> float& {
-        return s_edge_raw[(b * 2 + which) * blockDim.x + lane];
+        return edge_raw[(b * 2 + which) * blockDim.x + lane];
     };
 
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
-    const int64_t blk = blockIdx.x;
-    const int64_t p = blk / a.nchunks;  // plane n * c + ci
-    const int q = static_cast<int>(blk - p * a.nchunks);
     const int64_t nidx = p / a.c;
     const int64_t ci = p - nidx * a.c;
     const int S = a.S;
@@ -144,11 +207,11 @@ __global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
         const int i = rev ? S - 1 - t : t;
         const int64_t lo = static_cast<int64_t>(i) * L;
 #pragma unroll
-        for (int o = 0; o < 3; ++o) load_run<T, P>(zp + o * plane + lo, k0, L, vf, rz[slot][o]);
-        load_run<T, P>(lp + lo, k0, L, vf, rl[slot]);
+        for (int o = 0; o < 3; ++o) load_run<T, P, true>(zp + o * plane + lo, k0, L, vf, rz[slot][o]);
+        load_run<T, P, true>(lp + lo, k0, L, vf, rl[slot]);
         if constexpr (!HORIZ) {
-            load_run<T, P>(xp + lo, k0, L, va, rx[slot]);
-            if (acc) load_run<T, P>(op + lo, k0, L, va, ry[slot]);
+            load_run<T, P, true>(xp + lo, k0, L, va, rx[slot]);
+            if (acc) load_run<T, P, true>(op + lo, k0, L, va, ry[slot]);
         }
     };
 
@@ -174,8 +237,7 @@ __global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
 #pragma unroll
                         for (int e = 0; e < VW; ++e) xd[j][v * VW + e] = Store<T>::ld(&xv.e[e]);
                         if (acc) {
-                            const VecT<T, VW> yv =
-                                *reinterpret_cast<const VecT<T, VW>*>(yr + clo + v * VW);
+                            const VecT<T, VW> yv = vload<T, VW, true>(yr + clo + v * VW);
 #pragma unroll
                             for (int e = 0; e < VW; ++e) yd[j][v * VW + e] = Store<T>::ld(&yv.e[e]);
                         }
@@ -186,7 +248,7 @@ __global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
                         const int s = REV ? U - 1 - u : u;
                         const bool on = row && (tb + s < t1);
                         xd[j][u] = on ? Store<T>::ld(xr + clo + u) : 0.0f;
-                        yd[j][u] = (on && acc) ? Store<T>::ld(yr + clo + u) : 0.0f;
+                        yd[j][u] = (on && acc) ? sload<T, true>(yr + clo + u) : 0.0f;
                     }
                 }
             }
@@ -209,13 +271,13 @@ __global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
                         VecT<T, VW> yv;
 #pragma unroll
                         for (int e = 0; e < VW; ++e) Store<T>::st(&yv.e[e], yd[j][v * VW + e]);
-                        *reinterpret_cast<VecT<T, VW>*>(yr + clo + v * VW) = yv;
+                        vstore<T, VW, true>(yr + clo + v * VW, yv);
                     }
                 } else {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int s = REV ? U - 1 - u : u;
-                        if (tb + s < t1) Store<T>::st(yr + clo + u, yd[j][u]);
+                        if (tb + s < t1) sstore<T, true>(yr + clo + u, yd[j][u]);
                     }
                 }
             }
@@ -285,7 +347,7 @@ __global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
                     float ov[P];
 #pragma unroll
                     for (int j = 0; j < P; ++j) ov[j] = acc ? ry[slot][j] + hn[j] : hn[j];
-                    store_run<T, P>(op + static_cast<int64_t>(i) * L, k0, L, va, ov);
+                    store_run<T, P, true>(op + static_cast<int64_t>(i) * L, k0, L, va, ov);
                 }
 #pragma unroll
                 for (int j = 0; j < P; ++j) h[j] = hn[j];
@@ -308,6 +370,16 @@ __global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
 }
 
 
+// Single-direction launch: one workgroup per (plane, chunk).
+template <typename T, int P, int D, int U, bool HORIZ, bool REV, int MAXT>
+__global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
+    extern __shared__ float s_edge_raw[];
+    const int64_t blk = blockIdx.x;
+    const int64_t p = blk / a.nchunks;  // plane n * c + ci
+    const int q = static_cast<int>(blk - p * a.nchunks);
+    scan_line<T, P, D, U, HORIZ, REV>(a, p, q, s_edge_raw);
+}
+
 // ---------------------------------------------------------------------------
 // Launch families
 // ---------------------------------------------------------------------------
@@ -320,16 +392,17 @@ struct ScanConfig {
 
 // Horizontal tile width: 16 steps for one position per lane, fewer for more
 // positions so the two tiles of x and y stay in registers; at least one
-// 16-byte vector per row.
-template <typename T, int P>
+// 16-byte vector per row and one turn of the prefetch ring.
+template <typename T, int P, int D>
 constexpr int tile_width() {
     constexpr int vw = 16 / static_cast<int>(sizeof(T));
-    return (16 / P) > vw ? (16 / P) : vw;
+    constexpr int u = (16 / P) > vw ? (16 / P) : vw;
+    return u > D ? u : D;
 }
 
 template <typename T, int P, int D, int MAXT, bool HORIZ, bool REV>
 hipError_t launch_one(const ScanK& k, int64_t nblocks, int nthreads, hipStream_t stream) {
-    constexpr int U = HORIZ ? tile_width<T, P>() : D;
+    constexpr int U = HORIZ ? tile_width<T, P, D>() : D;
     const size_t lds = 4 * sizeof(float) * static_cast<size_t>(nthreads);
     hipLaunchKernelGGL((scan_kernel<T, P, D, U, HORIZ, REV, MAXT>), dim3(static_cast<unsigned>(nblocks)),
                        dim3(nthreads), lds, stream, k);
@@ -350,38 +423,90 @@ hipError_t launch_rev(bool rev, const ScanK& k, int64_t nblocks, int nthreads, h
     }
 }
 
-// Instantiated families.  Vertical: up to 256 lanes with P in {1,2,4,8} and
-// a GSPN_RING_D-deep ring; lines over 2048 positions take P = 8 on up to 1024
-// lanes with a 2-deep ring.  Horizontal: up to 1024 lanes with P in
-// {1,2,4,8}.  Builds with GSPN_TUNING instantiate every (P, MAXT) pair.
+// Instantiated families.  Up to 256 lanes: one position per lane.  Up to
+// 1024 lanes: P in {1, 2, 4} with a GSPN_RING_D-deep ring; P = 8 (lines over
+// 4096 positions) with a 2-deep ring.  Builds with GSPN_TUNING also
+// instantiate P in {2, 4, 8} on 256 lanes.
 template <typename T, bool HORIZ>
 hipError_t launch_family(const ScanConfig& c, bool rev, const ScanK& k, int64_t nblocks, int nthreads,
                          hipStream_t stream) {
     constexpr int D = GSPN_RING_D;
+    if (c.maxt == 256) {
 #ifdef GSPN_TUNING
-    constexpr bool all = true;
-#else
-    constexpr bool all = false;
-#endif
-    if constexpr (!HORIZ || all) {
-        if (c.maxt == 256) {
-            switch (c.P) {
-                case 1: return launch_rev<T, 1, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-                case 2: return launch_rev<T, 2, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-                case 4: return launch_rev<T, 4, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-                default: return launch_rev<T, 8, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-            }
-        }
-    }
-    if constexpr (HORIZ || all) {
         switch (c.P) {
-            case 1: return launch_rev<T, 1, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
-            case 2: return launch_rev<T, 2, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
-            case 4: return launch_rev<T, 4, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
+            case 2: return launch_rev<T, 2, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
+            case 4: return launch_rev<T, 4, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
+            case 8: return launch_rev<T, 8, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
             default: break;
         }
+#endif
+        return launch_rev<T, 1, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
     }
-    return launch_rev<T, 8, 2, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
+    switch (c.P) {
+        case 1: return launch_rev<T, 1, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
+        case 2: return launch_rev<T, 2, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
+        case 4: return launch_rev<T, 4, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
+        default: return launch_rev<T, 8, 2, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Four directions in one launch
+// ---------------------------------------------------------------------------
+
+// The four directions' scans of one forward, each writing its own output
+// buffer, so that all of them run concurrently and a small plane count still
+// fills the chip.  Block b belongs to direction b % 4 when every direction has
+// the same number of blocks (interleave = 1), else to consecutive ranges.
+struct Scan4K {
+    ScanK d[4];
+    int64_t blocks[4];
+    int interleave;
+};
+
+template <typename T, int PV, int PH>
+__global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
+    extern __shared__ float s_edge_raw[];
+    constexpr int D = GSPN_RING_D;
+    constexpr int UH = tile_width<T, PH, D>();
+    const int64_t b = blockIdx.x;
+    int dir = 0;
+    int64_t idx = b;
+    if (a.interleave) {
+        dir = static_cast<int>(b & 3);
+        idx = b >> 2;
+    } else {
+        while (dir < 3 && idx >= a.blocks[dir]) {
+            idx -= a.blocks[dir];
+            ++dir;
+        }
+    }
+    const ScanK& k = a.d[dir];
+    const int64_t p = idx / k.nchunks;
+    const int q = static_cast<int>(idx - p * k.nchunks);
+    switch (dir) {
+        case 0:
+        case 1: scan_line<T, PV, D, D, false, false>(k, p, q, s_edge_raw); break;
+        case 2: scan_line<T, PH, D, UH, true, false>(k, p, q, s_edge_raw); break;
+        default: scan_line<T, PH, D, UH, true, true>(k, p, q, s_edge_raw); break;
+    }
+}
+
+template <typename T>
+hipError_t launch_fused4(const Scan4K& k, int pv, int ph, int nthreads, hipStream_t stream) {
+    const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
+    const size_t lds = 4 * sizeof(float) * static_cast<size_t>(nthreads);
+    const dim3 grid(static_cast<unsigned>(nblocks));
+    if (pv == 1 && ph == 1) {
+        hipLaunchKernelGGL((scan4_kernel<T, 1, 1>), grid, dim3(nthreads), lds, stream, k);
+    } else if (pv == 1) {
+        hipLaunchKernelGGL((scan4_kernel<T, 1, 2>), grid, dim3(nthreads), lds, stream, k);
+    } else if (ph == 1) {
+        hipLaunchKernelGGL((scan4_kernel<T, 2, 1>), grid, dim3(nthreads), lds, stream, k);
+    } else {
+        hipLaunchKernelGGL((scan4_kernel<T, 2, 2>), grid, dim3(nthreads), lds, stream, k);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace gspn

@@ -19,7 +19,8 @@ from typing import Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgspn.so")
+# GSPN_LIBRARY may point the binding at another build of libgspn.
+LIB_PATH = os.environ.get("GSPN_LIBRARY") or os.path.join(_PKG, "libgspn.so")
 
 T2B, B2T, L2R, R2L = 0, 1, 2, 3
 DIRECTIONS = ("T2B", "B2T", "L2R", "R2L")
@@ -29,11 +30,12 @@ STATUS = {
     0: "GSPN_OK", 1: "GSPN_ERR_NULL_POINTER", 2: "GSPN_ERR_BAD_SHAPE", 3: "GSPN_ERR_BAD_DIRECTION",
     4: "GSPN_ERR_BAD_DTYPE", 5: "GSPN_ERR_BAD_CHUNK", 6: "GSPN_ERR_BAD_WEIGHT_CHANNELS",
     7: "GSPN_ERR_MISALIGNED", 8: "GSPN_ERR_ALIASING", 9: "GSPN_ERR_UNSUPPORTED", 10: "GSPN_ERR_HIP",
+    11: "GSPN_ERR_WORKSPACE",
 }
 
 # Symbols declared in include/gspn.h.
 EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy_project",
-           "gspn_forward4", "gspn_status_string", "gspn_abi_version")
+           "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4", "gspn_status_string", "gspn_abi_version")
 
 
 class GspnError(RuntimeError):
@@ -61,8 +63,13 @@ def lib() -> ctypes.CDLL:
             h.gspn_scan_fwd.argtypes = [ci, i64, i64, i64, i64, i64, i64, vp, vp, ci, vp, vp, ci, ci, vp]
             h.gspn_merge4.argtypes = [vp, vp, vp, vp, vp, i64, ci, vp]
             h.gspn_proxy_project.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, ci, vp]
+            h.gspn_scan4_fwd.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
+                                         ctypes.POINTER(vp), ctypes.POINTER(vp), ci, vp]
+            h.gspn_scan4_fwd.restype = ci
+            h.gspn_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+            h.gspn_forward4_workspace_bytes.restype = i64
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
-                                        ctypes.POINTER(vp), vp, ci, vp]
+                                        ctypes.POINTER(vp), vp, vp, i64, ci, vp]
             for name in ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4",
                          "gspn_proxy_project", "gspn_forward4"):
                 getattr(h, name).restype = ci
@@ -187,10 +194,46 @@ def gspn_proxy_project(inp: torch.Tensor, weight: torch.Tensor,
     return out
 
 
+def gspn_scan4_fwd(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                   chunk_len: int = 0, outs: Sequence[torch.Tensor] | None = None) -> list:
+    """The four directions' scans in one launch, each into its own output."""
+    n, c, h, w = x.shape
+    dt = x.dtype
+    cw = logits[0].shape[1]
+    _check(x, "x", (n, c, h, w), dt, x.device)
+    for d in range(4):
+        S, L = frame_shape(d, h, w)
+        _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
+        _check(lams[d], "lam[%d]" % d, (n, c, S, L), dt, x.device)
+    if outs is None:
+        outs = [torch.empty_like(x) for _ in range(4)]
+    for d in range(4):
+        _check(outs[d], "out[%d]" % d, (n, c, h, w), dt, x.device)
+    zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
+    lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
+    op = (ctypes.c_void_p * 4)(*[o.data_ptr() for o in outs])
+    _raise(lib().gspn_scan4_fwd(n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, op, _dtype_code(x),
+                                _stream(x.device)), "gspn_scan4_fwd")
+    return list(outs)
+
+
+def gspn_forward4_workspace_bytes(x: torch.Tensor) -> int:
+    """Bytes of the optional gspn_forward4 workspace for inputs shaped like x."""
+    n, c, h, w = x.shape
+    return int(lib().gspn_forward4_workspace_bytes(n, c, h, w, _dtype_code(x)))
+
+
+def forward4_workspace(x: torch.Tensor) -> torch.Tensor:
+    """A workspace buffer (uint8 tensor on x's device) for gspn_forward4."""
+    return torch.empty(gspn_forward4_workspace_bytes(x), dtype=torch.uint8, device=x.device)
+
+
 def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
-                  chunk_len: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+                  chunk_len: int = 0, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Four-direction propagation with summed merge; logits[d] / lams[d] in
-    direction d's scan frame."""
+    direction d's scan frame.  ``workspace`` (see forward4_workspace) lets the
+    library run the four directions concurrently when that pays."""
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
@@ -202,10 +245,15 @@ def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequenc
     if out is None:
         out = torch.empty_like(x)
     _check(out, "out", (n, c, h, w), dt, x.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device != x.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
-    _raise(lib().gspn_forward4(n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, _ptr(out),
-                               _dtype_code(x), _stream(x.device)), "gspn_forward4")
+    _raise(lib().gspn_forward4(n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, _ptr(out), ws_ptr,
+                               ws_bytes, _dtype_code(x), _stream(x.device)), "gspn_forward4")
     return out
 
 
@@ -215,5 +263,5 @@ def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tenso
     """Compressive-proxy forward: C -> C_proxy projection, four-direction scan in
     proxy space, C_proxy -> C projection (three libgspn calls)."""
     xp = gspn_proxy_project(x, w_down)
-    yp = gspn_forward4(xp, logits, lams, chunk_len)
+    yp = gspn_forward4(xp, logits, lams, chunk_len, workspace=forward4_workspace(xp))
     return gspn_proxy_project(yp, w_up)

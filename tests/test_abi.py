@@ -13,7 +13,7 @@ from linear_spatial_propagation_gspn_amd import gspn as G
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gspn.h")
 
-OK, NULLP, SHAPE, DIR, DTYPE, CHUNK, WCH, MISAL, ALIAS, UNSUP, HIP = range(11)
+OK, NULLP, SHAPE, DIR, DTYPE, CHUNK, WCH, MISAL, ALIAS, UNSUP, HIP, WSPACE = range(12)
 
 # Fake, never-dereferenced device addresses (validation only compares them).
 A = 0x10000000
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.gspn_abi_version() == 1
-    for code in range(11):
+    for code in range(12):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
     assert lib.gspn_status_string(99).decode() == "unknown gspn_status"
@@ -89,16 +89,49 @@ def test_forward4_validation(lib):
     vp4 = ctypes.c_void_p * 4
     zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
     ls = vp4(C_, C_, C_, C_)
-    f = lib.gspn_forward4
-    assert f(1, 2, 8, 8, 2, 0, A, zs, ls, D_, 3, None) == DTYPE
-    assert f(1, 2, 8, 8, 3, 0, A, zs, ls, D_, 0, None) == WCH
-    assert f(1, 2, 8, 8, 2, -2, A, zs, ls, D_, 0, None) == CHUNK
-    assert f(1, 2, 8, 8, 2, 0, 0, zs, ls, D_, 0, None) == NULLP
-    assert f(1, 2, 8, 8, 2, 0, A, vp4(B, 0, B, B), ls, D_, 0, None) == NULLP
-    assert f(1, 2, 8, 8, 2, 0, A, zs, ls, A, 0, None) == ALIAS
-    assert f(1, 2, 8, 8, 2, 0, A, zs, ls, C_, 0, None) == ALIAS
-    assert f(1, 2, 8, 8, 2, 0, A, zs, vp4(C_, C_, C_, C_ + 1), D_, 0, None) == MISAL
-    assert f(0, 2, 8, 8, 2, 0, 0, None, None, 0, 0, None) == OK
+    W = 0x60000000
+    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 0)
+    assert wsb == 3 * 2 * 64 * 4
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1) == 3 * 2 * 64 * 2
+    assert lib.gspn_forward4_workspace_bytes(1, -2, 8, 8, 0) == -1
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 5) == -1
+
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, y=D_, ws=None, wsb=0, dt=0):
+        return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, y, ws, wsb, dt, None)
+
+    assert f(dt=3) == DTYPE
+    assert f(cw=3) == WCH
+    assert f(chunk=-2) == CHUNK
+    assert f(x=0) == NULLP
+    assert f(z=vp4(B, 0, B, B)) == NULLP
+    assert f(y=A) == ALIAS
+    assert f(y=C_) == ALIAS
+    assert f(l=vp4(C_, C_, C_, C_ + 1)) == MISAL
+    assert f(ws=W, wsb=wsb - 1) == WSPACE
+    assert f(ws=W + 2, wsb=wsb) == MISAL
+    assert f(ws=D_ - 100, wsb=wsb) == ALIAS          # workspace overlaps y
+    assert f(ws=A + 4, wsb=wsb) == ALIAS             # workspace overlaps x
+    assert f(n=0, x=0, z=None, l=None, y=0) == OK
+
+
+def test_scan4_validation(lib):
+    vp4 = ctypes.c_void_p * 4
+    zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
+    ls = vp4(C_, C_, C_, C_)
+    outs = vp4(D_, D_ + 0x1000000, D_ + 0x2000000, D_ + 0x3000000)
+
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, o=outs, dt=0):
+        return lib.gspn_scan4_fwd(n, c, h, w, cw, chunk, x, z, l, o, dt, None)
+
+    assert f(dt=2) == DTYPE
+    assert f(chunk=-1) == CHUNK
+    assert f(cw=5) == WCH
+    assert f(h=2049) == UNSUP                        # longer than the fused kernel's lines
+    assert f(o=vp4(D_, 0, D_, D_)) == NULLP
+    assert f(o=vp4(D_, D_ + 0x1000000, D_ + 0x2000000, D_ + 2)) == MISAL
+    assert f(o=vp4(D_, D_ + 16, D_ + 0x2000000, D_ + 0x3000000)) == ALIAS   # outputs overlap
+    assert f(o=vp4(D_, A, D_ + 0x2000000, D_ + 0x3000000)) == ALIAS         # output on x
+    assert f(n=0, x=0, z=None, l=None, o=None) == OK
 
 
 def test_normalize_merge_project_validation(lib):

@@ -149,19 +149,37 @@ def test_project(cin, cout, dtype):
     assert _err(got, ref) <= (1e-5 if dtype == "f32" else 1e-2)
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("chunk", [0, 8, 5])
-@pytest.mark.parametrize("shape", [(1, 2, 16, 16), (2, 3, 23, 41), (1, 2, 64, 130)])
-def test_forward4_small(shape, chunk, dtype):
+@pytest.mark.parametrize("shape", [(1, 2, 16, 16), (2, 3, 23, 41), (1, 2, 64, 130), (1, 1, 1100, 40)])
+def test_forward4_small(shape, chunk, dtype, use_ws):
     n, c, h, w = shape
     for shared in (False, True):
         wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=shared, seed=h * w + chunk)
-        _say("forward4 %s chunk=%d %s shared=%s" % (shape, chunk, dtype, shared))
+        _say("forward4 %s chunk=%d %s shared=%s ws=%s" % (shape, chunk, dtype, shared, use_ws))
         inp = make_inputs(wl, DEV)
-        got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk)
+        ws = G.forward4_workspace(inp["x"]) if use_ws else None
+        got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk, workspace=ws)
         torch.cuda.synchronize()
         ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk)
         assert _err(got, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,chunk", [((1, 2, 16, 16), 0), ((2, 3, 23, 41), 0), ((2, 3, 23, 41), 7),
+                                         ((1, 2, 1030, 70), 0), ((1, 1, 70, 1500), 9),
+                                         ((1, 2, 2048, 33), 0)])
+def test_scan4_outputs(shape, chunk, dtype):
+    n, c, h, w = shape
+    wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, seed=h + 3 * w + chunk)
+    _say("scan4 %s chunk=%d %s" % (shape, chunk, dtype))
+    inp = make_inputs(wl, DEV)
+    outs = G.gspn_scan4_fwd(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk)
+    torch.cuda.synchronize()
+    for d in range(4):
+        ref = oracle.scan(d, inp["x"], inp["logits"][d], inp["lam"][d], chunk=chunk)
+        assert _err(outs[d], ref) <= TOL[dtype], d
 
 
 def test_forward4_closed_form_constant_input():
@@ -226,7 +244,8 @@ def test_full_tstage(name):
     wl = WORKLOADS[name]
     _say("full %s" % name)
     inp = make_inputs(wl, DEV)
-    got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk)
+    got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk,
+                          workspace=G.forward4_workspace(inp["x"]))
     torch.cuda.synchronize()
     ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=wl.chunk)
     assert _err(got, ref) <= TOL[wl.dtype]
@@ -240,7 +259,8 @@ def test_full_size_sampled_planes(name, planes):
     wl = WORKLOADS[name]
     _say("full %s" % name)
     inp = make_inputs(wl, DEV)
-    got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk)
+    got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk,
+                          workspace=G.forward4_workspace(inp["x"]))
     torch.cuda.synchronize()
     assert torch.isfinite(got).all()
     for n, c in planes:
