@@ -196,7 +196,7 @@ def main():
     print("bench: workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
     inp = make_inputs(wl, "cuda")
     out = torch.empty_like(inp["x"]) if not wl.c_proxy else None
-    ws = G.forward4_workspace(inp["x"]) if not wl.c_proxy else None
+    ws = G.forward4_workspace(inp["x"], wl.cw) if not wl.c_proxy else None
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):

@@ -67,7 +67,7 @@ extern "C" {
 #endif
 
 #define GSPN_ABI_VERSION 1
-#define GSPN_MAX_LINE 8192
+#define GSPN_MAX_LINE 4096
 
 typedef enum {
     GSPN_OK = 0,
@@ -154,11 +154,15 @@ gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
 
 /*
  * gspn_forward4_workspace_bytes -- bytes of the optional gspn_forward4
- * workspace: three partial output maps, 3 * n*c*h*w elements of the storage
- * type.  Returns -1 when the arguments are invalid (negative or overflowing
- * dimensions, unknown dtype).
+ * workspace: four maps of n*c*h*w elements of the storage type (x transposed
+ * into the horizontal scan frame and three partial outputs) and, for
+ * channel-shared weights over more than one channel (cw == 1 < c), the four
+ * directions' normalised weights in fp32 (4 * 3 * n*h*w floats).  Returns -1
+ * when the arguments are invalid (negative or overflowing dimensions, cw not
+ * in {1, c}, unknown dtype).
  */
-int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int dtype);
+int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                                      int dtype);
 
 /*
  * gspn_forward4 -- the four-direction propagation with summed merge:
@@ -167,17 +171,22 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *   lam[d]     [n][c][S_d][L_d]; the same pointer may be given for all d.
  *   logits and lam are host arrays of 4 device pointers, indexed by gspn_dir.
  *   y          [n][c][h][w] output; may not overlap any input.
- *   workspace  optional device buffer of workspace_bytes bytes.  NULL (or 0
- *              bytes): the directions run one after another, the first
- *              writing y and the others adding to it.  Otherwise it must hold
- *              gspn_forward4_workspace_bytes() bytes (else GSPN_ERR_WORKSPACE)
- *              and overlap neither y nor any input (else GSPN_ERR_ALIASING);
- *              when there are too few planes to fill the GPU with one
- *              direction at a time, the library then runs all four
- *              directions in one launch, three of them into the workspace,
- *              and adds those into y.  Its contents afterwards are
- *              unspecified.  Either way y is the same up to fp32 rounding
- *              order (and, for bf16, rounding of the partial maps).
+ *   workspace  optional device buffer of workspace_bytes bytes, 4-byte
+ *              aligned.  NULL (or 0 bytes): the directions run one after
+ *              another, the first writing y and the others adding to it, and
+ *              the logits are normalised inside the scans.  Otherwise it
+ *              must hold gspn_forward4_workspace_bytes() bytes (else
+ *              GSPN_ERR_WORKSPACE) and overlap neither y nor any input (else
+ *              GSPN_ERR_ALIASING).  The library then (a) normalises
+ *              channel-shared logits once into fp32 weights that every
+ *              channel's scan reads, (b) transposes x once so that the
+ *              horizontal directions run as row-coalesced scans whose
+ *              outputs a transposing merge adds into y, and (c) when there
+ *              are too few planes to fill the GPU with one direction at a
+ *              time, runs all four directions in one launch into separate
+ *              maps.  Its contents afterwards are unspecified.  Either way y
+ *              is the same up to fp32 rounding order (and, for bf16,
+ *              rounding of the partial maps).
  */
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],

@@ -19,13 +19,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgspn.so")
-SOURCES = ["api.cpp", "scan.hip", "scan_f32_vert.hip", "scan_f32_horiz.hip", "scan_bf16_vert.hip", "scan4_f32.hip", "scan4_bf16.hip",
-           "scan_bf16_horiz.hip", "elementwise.hip", "project.hip"]
+SOURCES = ["api.cpp", "scan.hip", "scan_f32_vert.hip", "scan_f32_horiz.hip", "scan_bf16_vert.hip",
+           "scan_bf16_horiz.hip", "scan_bf16w32_vert.hip", "scan_bf16w32_horiz.hip", "scan4_f32.hip",
+           "scan4_bf16.hip", "scan4_bf16w32.hip", "elementwise.hip", "transpose.hip", "project.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [
-    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 DEVICE = [

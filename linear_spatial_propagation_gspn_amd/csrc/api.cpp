@@ -155,6 +155,7 @@ gspn_status gspn_scan_fwd(int dir, int64_t chunk_len, int64_t n, int64_t c, int6
     p.wts_are_logits = wts_are_logits ? 1 : 0;
     p.accumulate = accumulate ? 1 : 0;
     p.dtype = dtype;
+    p.wdtype = dtype;
     return from_hip(gspn::launch_scan(p, as_stream(stream)));
 }
 
@@ -237,13 +238,18 @@ gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
         p[d].wts_are_logits = 1;
         p[d].accumulate = 0;
         p[d].dtype = dtype;
+        p[d].wdtype = dtype;
     }
     return from_hip(gspn::launch_scan4(p, as_stream(stream)));
 }
 
-int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int dtype) {
-    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w})) return -1;
-    return 3 * checked_product({n, c, h, w}) * static_cast<int64_t>(elem_size(dtype));
+int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                                      int dtype) {
+    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
+    const int64_t elems = checked_product({n, c, h, w});
+    const int64_t maps = 4 * elems * static_cast<int64_t>(elem_size(dtype));
+    const int64_t weights = (cw == 1 && c > 1) ? 4 * 3 * checked_product({n, h, w}) * 4 : 0;
+    return maps + weights;
 }
 
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
@@ -271,14 +277,15 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         if (overlap(y, xb, logits[d], wb) || overlap(y, xb, lam[d], xb)) return GSPN_ERR_ALIASING;
     const bool have_ws = workspace != nullptr && workspace_bytes > 0;
     if (have_ws) {
-        if (workspace_bytes < 3 * xb) return GSPN_ERR_WORKSPACE;
-        if (!aligned(workspace, es)) return GSPN_ERR_MISALIGNED;
-        const int64_t sb = 3 * xb;
-        if (overlap(workspace, sb, y, xb) || overlap(workspace, sb, x, xb)) return GSPN_ERR_ALIASING;
+        const int64_t need = gspn_forward4_workspace_bytes(n, c, h, w, cw, dtype);
+        if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
+        if (overlap(workspace, need, y, xb) || overlap(workspace, need, x, xb)) return GSPN_ERR_ALIASING;
         for (int d = 0; d < 4; ++d)
-            if (overlap(workspace, sb, logits[d], wb) || overlap(workspace, sb, lam[d], xb))
+            if (overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], xb))
                 return GSPN_ERR_ALIASING;
     }
+    const hipStream_t st = as_stream(stream);
 
     gspn::ScanParams p[4];
     for (int d = 0; d < 4; ++d) {
@@ -296,7 +303,53 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].wts_are_logits = 1;
         p[d].accumulate = 0;
         p[d].dtype = dtype;
+        p[d].wdtype = dtype;
     }
+
+    if (!have_ws) {
+        // No workspace: one direction per launch; the first writes y, the
+        // others add to it; horizontal lines use per-lane row tiles.
+        for (int d = 0; d < 4; ++d) {
+            p[d].accumulate = d > 0 ? 1 : 0;
+            if (gspn::launch_scan(p[d], st) != hipSuccess) return GSPN_ERR_HIP;
+        }
+        return GSPN_OK;
+    }
+
+    // Workspace layout: [fp32 weights of the four directions, only for
+    // channel-shared weights over several channels][x transposed into the
+    // horizontal scan frame][three output maps].
+    char* ws = static_cast<char*>(workspace);
+    const bool prenorm = cw == 1 && c > 1;
+    const int64_t wdir = n * 3 * h * w;  // fp32 weights per direction
+    char* xt = ws + (prenorm ? 4 * wdir * 4 : 0);
+    char* m1 = xt + xb;
+    char* m2 = m1 + xb;
+    char* m3 = m2 + xb;
+    if (prenorm) {
+        // One normalisation per position and direction, shared by all c
+        // channels, kept in fp32 so the scans run without transcendentals.
+        for (int d = 0; d < 4; ++d) {
+            float* wd = reinterpret_cast<float*>(ws) + d * wdir;
+            if (gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32) != hipSuccess)
+                return GSPN_ERR_HIP;
+            p[d].wts = wd;
+            p[d].wts_are_logits = 0;
+            p[d].wdtype = GSPN_F32;
+        }
+    }
+    // The horizontal directions become vertical-form scans of x transposed
+    // (their scan frame): line k of step i is x[.., k, i].
+    if (gspn::launch_transpose(x, xt, n * c, static_cast<int>(h), static_cast<int>(w), dtype, st) !=
+        hipSuccess)
+        return GSPN_ERR_HIP;
+    for (int d = 2; d < 4; ++d) {
+        p[d].x = xt;
+        p[d].h = w;
+        p[d].w = h;
+        p[d].dir = d - 2;  // L2R runs like T2B, R2L like B2T, in the transposed frame
+    }
+
     // Concurrent path: worth it while one direction's (plane, chunk) lines
     // cannot keep the GPU's 256 compute units busy twice over.
     int64_t most_blocks = 0;
@@ -305,20 +358,24 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         const int64_t nb = n * c * ((S + chunks[d] - 1) / chunks[d]);
         most_blocks = nb > most_blocks ? nb : most_blocks;
     }
-    if (have_ws && most_blocks < kFuse4MaxBlocks && gspn::fused4_supported(h, w)) {
-        char* ws = static_cast<char*>(workspace);
-        for (int d = 1; d < 4; ++d) p[d].out = ws + (d - 1) * xb;
-        if (gspn::launch_scan4(p, as_stream(stream)) != hipSuccess) return GSPN_ERR_HIP;
-        return from_hip(gspn::launch_merge_into(y, p[1].out, p[2].out, p[3].out, n * c * h * w, dtype,
-                                                as_stream(stream)));
+    if (most_blocks < kFuse4MaxBlocks && gspn::fused4_supported(h, w)) {
+        p[1].out = m1;
+        p[2].out = m2;
+        p[3].out = m3;
+        if (gspn::launch_scan4v(p, st) != hipSuccess) return GSPN_ERR_HIP;
+        return from_hip(gspn::launch_combine(y, m1, m2, m3, n * c, static_cast<int>(h), static_cast<int>(w),
+                                             1, dtype, st));
     }
-    // Sequential path: one direction per launch; the first writes y, the
-    // others add to it.
-    for (int d = 0; d < 4; ++d) {
-        p[d].accumulate = d > 0 ? 1 : 0;
-        if (gspn::launch_scan(p[d], as_stream(stream)) != hipSuccess) return GSPN_ERR_HIP;
-    }
-    return GSPN_OK;
+    // Sequential path: T2B writes y, B2T adds to it; L2R writes the
+    // transposed map, R2L adds to it; a transposing merge adds that into y.
+    p[1].accumulate = 1;
+    p[2].out = m1;
+    p[3].out = m1;
+    p[3].accumulate = 1;
+    for (int d = 0; d < 4; ++d)
+        if (gspn::launch_scan(p[d], st) != hipSuccess) return GSPN_ERR_HIP;
+    return from_hip(gspn::launch_combine(y, nullptr, m1, nullptr, n * c, static_cast<int>(h),
+                                         static_cast<int>(w), 1, dtype, st));
 }
 
 }  // extern "C"

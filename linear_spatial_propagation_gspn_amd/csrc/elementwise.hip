@@ -10,8 +10,8 @@ namespace {
 // w = sigmoid row normalisation of the logit triple at every (plane, i, k)
 // (GSPN summary page, "Approach"; rows sum to 1, border rows renormalised
 // over the neighbours that exist).  Layout [planes][3][S][L].
-template <typename T>
-__global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ z, T* __restrict__ w,
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ z, TO* __restrict__ w,
                                                         int64_t planes, int64_t S, int64_t L) {
     const int64_t per_plane = S * L;
     const int64_t total = planes * per_plane;
@@ -25,9 +25,9 @@ __global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ z,
         float w0, w1, w2;
         normalise_row(Store<T>::ld(z + base), Store<T>::ld(z + base + per_plane),
                       Store<T>::ld(z + base + 2 * per_plane), k > 0, k + 1 < L, w0, w1, w2);
-        Store<T>::st(w + base, w0);
-        Store<T>::st(w + base + per_plane, w1);
-        Store<T>::st(w + base + 2 * per_plane, w2);
+        Store<TO>::st(w + base, w0);
+        Store<TO>::st(w + base + per_plane, w1);
+        Store<TO>::st(w + base + 2 * per_plane, w2);
     }
 }
 
@@ -112,17 +112,22 @@ hipError_t launch_merge_into(void* y, const void* w1, const void* w2, const void
 }
 
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
-                            const void* logits, void* w_out, int dtype, hipStream_t stream) {
+                            const void* logits, void* w_out, int dtype, hipStream_t stream,
+                            int out_dtype) {
     const bool horiz = (dir == 2 || dir == 3);
     const int64_t S = horiz ? w : h;
     const int64_t L = horiz ? h : w;
     const int64_t planes = n * cw;
     const unsigned grid = grid_for(planes * S * L, 256);
+    if (out_dtype < 0) out_dtype = dtype;
     if (dtype == kF32) {
-        hipLaunchKernelGGL(normalize_kernel<float>, dim3(grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((normalize_kernel<float, float>), dim3(grid), dim3(256), 0, stream,
                            static_cast<const float*>(logits), static_cast<float*>(w_out), planes, S, L);
+    } else if (out_dtype == kF32) {
+        hipLaunchKernelGGL((normalize_kernel<bf16_t, float>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<const bf16_t*>(logits), static_cast<float*>(w_out), planes, S, L);
     } else {
-        hipLaunchKernelGGL(normalize_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((normalize_kernel<bf16_t, bf16_t>), dim3(grid), dim3(256), 0, stream,
                            static_cast<const bf16_t*>(logits), static_cast<bf16_t*>(w_out), planes, S,
                            L);
     }

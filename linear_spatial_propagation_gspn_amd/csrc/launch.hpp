@@ -19,7 +19,8 @@ struct ScanParams {
     int64_t chunk;       // steps per chunk, already clamped to [1, S]
     int wts_are_logits;
     int accumulate;
-    int dtype;
+    int dtype;   // storage type of x, lam, out
+    int wdtype;  // storage type of wts (dtype, or kF32 for weights normalised beforehand)
 };
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
@@ -29,8 +30,24 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
 hipError_t launch_scan4(const ScanParams (&p)[4], hipStream_t stream);
 bool fused4_supported(int64_t h, int64_t w);
 
+// Four vertical-form scans in one launch (p[d].dir in {0, 1}): used for the
+// vertical directions on x and the horizontal ones on the transposed x.
+hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream);
+
+// dst[p][c][r] = src[p][r][c] for `planes` planes of R x Cc elements.
+hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, int Cc, int dtype,
+                            hipStream_t stream);
+
+// y[p][r][c] = ((z2[p][c][r] + z3[p][c][r]) + y[p][r][c] (if accumulate)) + a[p][r][c]
+// over planes of R x Cc; a, z2, z3 may be NULL; z2, z3 are Cc x R planes.
+hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3, int64_t planes, int R,
+                          int Cc, int accumulate, int dtype, hipStream_t stream);
+
+// out_dtype: storage type of w_out (-1: the same as dtype; kF32 is allowed
+// for bf16 logits).
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
-                            const void* logits, void* w_out, int dtype, hipStream_t stream);
+                            const void* logits, void* w_out, int dtype, hipStream_t stream,
+                            int out_dtype = -1);
 
 hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
                          int64_t numel, int dtype, hipStream_t stream);

@@ -6,36 +6,49 @@
 
 namespace gspn {
 
-extern template hipError_t launch_family<float, false>(const ScanConfig&, bool, const ScanK&, int64_t,
-                                                       int, hipStream_t);
-extern template hipError_t launch_family<float, true>(const ScanConfig&, bool, const ScanK&, int64_t,
-                                                      int, hipStream_t);
-extern template hipError_t launch_family<bf16_t, false>(const ScanConfig&, bool, const ScanK&, int64_t,
-                                                        int, hipStream_t);
-extern template hipError_t launch_family<bf16_t, true>(const ScanConfig&, bool, const ScanK&, int64_t,
-                                                       int, hipStream_t);
-extern template hipError_t launch_fused4<float>(const Scan4K&, int, int, int, hipStream_t);
-extern template hipError_t launch_fused4<bf16_t>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_family<float, float, false>(const ScanConfig&, bool, bool, const ScanK&,
+                                                              int64_t, int, hipStream_t);
+extern template hipError_t launch_family<float, float, true>(const ScanConfig&, bool, bool, const ScanK&,
+                                                             int64_t, int, hipStream_t);
+extern template hipError_t launch_family<bf16_t, bf16_t, false>(const ScanConfig&, bool, bool, const ScanK&,
+                                                                int64_t, int, hipStream_t);
+extern template hipError_t launch_family<bf16_t, bf16_t, true>(const ScanConfig&, bool, bool, const ScanK&,
+                                                               int64_t, int, hipStream_t);
+extern template hipError_t launch_family<bf16_t, float, false>(const ScanConfig&, bool, bool, const ScanK&,
+                                                               int64_t, int, hipStream_t);
+extern template hipError_t launch_family<bf16_t, float, true>(const ScanConfig&, bool, bool, const ScanK&,
+                                                              int64_t, int, hipStream_t);
+extern template hipError_t launch_fused4<float, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4<bf16_t, bf16_t>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4<bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4v<float, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4v<bf16_t, bf16_t>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4v<bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
 
 namespace {
 
-// Positions per lane and workgroup size for a line of L positions: one
-// position per lane up to 1024 lanes (16 waves, four per SIMD, which hides the
-// latency of each step's chain better than fewer, fatter lanes), then 2, 4
-// or 8 positions per lane for longer lines.
+// Positions per lane for a line of L positions: one position per lane up to
+// 1024 lanes (16 waves, four per SIMD, which hides the latency of each step's
+// chain better than fewer, fatter lanes), then 2 or 4 for longer lines.
 ScanConfig choose_config(bool horiz, int L) {
-#if defined(GSPN_VERT_P) && defined(GSPN_VERT_MAXT)
-    if (!horiz && (L + GSPN_VERT_P - 1) / GSPN_VERT_P <= GSPN_VERT_MAXT) return {GSPN_VERT_P, GSPN_VERT_MAXT};
+#if defined(GSPN_VERT_P)
+    if (!horiz && (L + GSPN_VERT_P - 1) / GSPN_VERT_P <= 1024) return {GSPN_VERT_P};
 #endif
-#if defined(GSPN_HORIZ_P) && defined(GSPN_HORIZ_MAXT)
-    if (horiz && (L + GSPN_HORIZ_P - 1) / GSPN_HORIZ_P <= GSPN_HORIZ_MAXT)
-        return {GSPN_HORIZ_P, GSPN_HORIZ_MAXT};
+#if defined(GSPN_HORIZ_P)
+    if (horiz && (L + GSPN_HORIZ_P - 1) / GSPN_HORIZ_P <= 1024) return {GSPN_HORIZ_P};
 #endif
     (void)horiz;
-    ScanConfig c{1, 256};
-    while (c.P < 8 && (L + c.P - 1) / c.P > 1024) c.P *= 2;
-    c.maxt = (L + c.P - 1) / c.P > 256 ? 1024 : 256;
+    ScanConfig c{1};
+    while (c.P < 4 && (L + c.P - 1) / c.P > 1024) c.P *= 2;
     return c;
+}
+
+// Horizontal tile width in steps (mirrors Blocking<T, P, true>::UT).
+int horiz_tile_width(size_t esz, int P) {
+    const int vw = static_cast<int>(16 / esz);
+    const int u = GSPN_SUB_U / P > 1 ? GSPN_SUB_U / P : 1;
+    const int t0 = (16 / P) > vw ? (16 / P) : vw;
+    return t0 > u ? t0 : u;
 }
 
 bool aligned_to(const void* ptr, size_t bytes) {
@@ -63,10 +76,11 @@ ScanK make_args(const ScanParams& p, int P) {
     k.nchunks = (S + k.K - 1) / k.K;
     k.reverse = (p.dir == 1 || p.dir == 3) ? 1 : 0;
     k.logits = p.wts_are_logits ? 1 : 0;
-    k.accumulate = p.accumulate ? 1 : 0;
-    k.vec_frame = (L % P == 0) && aligned_to(p.wts, esz * P) && aligned_to(p.lam, esz * P);
-    k.vec_arr = (L % P == 0) && aligned_to(p.x, esz * P) && aligned_to(p.out, esz * P);
-    k.vec_tile = (S % vw == 0) && aligned_to(p.x, 16) && aligned_to(p.out, 16);
+    // Row tiles take 16-byte accesses when every tile of every chunk starts
+    // on a 16-byte column: rows and chunk starts are whole vectors apart.
+    const int ut = horiz_tile_width(esz, P);
+    k.vec_tile = horiz && S % vw == 0 && (k.nchunks == 1 || k.K % vw == 0) && S >= ut &&
+                 aligned_to(p.x, 16) && aligned_to(p.out, 16);
     return k;
 }
 
@@ -82,12 +96,17 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
     const ScanK k = make_args(p, cfg.P);
     const int64_t nblocks = p.n * p.c * k.nchunks;
     const int nthreads = lanes_for(L, cfg.P);
+    const bool acc = p.accumulate != 0;
     if (p.dtype == kF32) {
-        return horiz ? launch_family<float, true>(cfg, rev, k, nblocks, nthreads, stream)
-                     : launch_family<float, false>(cfg, rev, k, nblocks, nthreads, stream);
+        return horiz ? launch_family<float, float, true>(cfg, rev, acc, k, nblocks, nthreads, stream)
+                     : launch_family<float, float, false>(cfg, rev, acc, k, nblocks, nthreads, stream);
     }
-    return horiz ? launch_family<bf16_t, true>(cfg, rev, k, nblocks, nthreads, stream)
-                 : launch_family<bf16_t, false>(cfg, rev, k, nblocks, nthreads, stream);
+    if (p.wdtype == kF32) {
+        return horiz ? launch_family<bf16_t, float, true>(cfg, rev, acc, k, nblocks, nthreads, stream)
+                     : launch_family<bf16_t, float, false>(cfg, rev, acc, k, nblocks, nthreads, stream);
+    }
+    return horiz ? launch_family<bf16_t, bf16_t, true>(cfg, rev, acc, k, nblocks, nthreads, stream)
+                 : launch_family<bf16_t, bf16_t, false>(cfg, rev, acc, k, nblocks, nthreads, stream);
 }
 
 bool fused4_supported(int64_t h, int64_t w) { return h <= 2048 && w <= 2048; }
@@ -107,8 +126,31 @@ hipError_t launch_scan4(const ScanParams (&p)[4], hipStream_t stream) {
     const int lv = lanes_for(Lv, pv);
     const int lh = lanes_for(Lh, ph);
     const int nthreads = lv > lh ? lv : lh;
-    if (p[0].dtype == kF32) return launch_fused4<float>(k, pv, ph, nthreads, stream);
-    return launch_fused4<bf16_t>(k, pv, ph, nthreads, stream);
+    if (p[0].dtype == kF32) return launch_fused4<float, float>(k, pv, ph, nthreads, stream);
+    if (p[0].wdtype == kF32) return launch_fused4<bf16_t, float>(k, pv, ph, nthreads, stream);
+    return launch_fused4<bf16_t, bf16_t>(k, pv, ph, nthreads, stream);
+}
+
+hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream) {
+    // every p[d] is a vertical-form scan (dir 0 or 1); p[0..1] share one line
+    // length, p[2..3] another
+    const int l01 = static_cast<int>(p[0].w);
+    const int l23 = static_cast<int>(p[2].w);
+    const int pv = l01 > 1024 ? 2 : 1;
+    const int ph = l23 > 1024 ? 2 : 1;
+    Scan4K k;
+    for (int d = 0; d < 4; ++d) {
+        k.d[d] = make_args(p[d], d < 2 ? pv : ph);
+        k.blocks[d] = p[d].n * p[d].c * k.d[d].nchunks;
+    }
+    k.interleave = (k.blocks[0] == k.blocks[1] && k.blocks[1] == k.blocks[2] &&
+                    k.blocks[2] == k.blocks[3]) ? 1 : 0;
+    const int a = lanes_for(l01, pv);
+    const int b = lanes_for(l23, ph);
+    const int nthreads = a > b ? a : b;
+    if (p[0].dtype == kF32) return launch_fused4v<float, float>(k, pv, ph, nthreads, stream);
+    if (p[0].wdtype == kF32) return launch_fused4v<bf16_t, float>(k, pv, ph, nthreads, stream);
+    return launch_fused4v<bf16_t, bf16_t>(k, pv, ph, nthreads, stream);
 }
 
 }  // namespace gspn

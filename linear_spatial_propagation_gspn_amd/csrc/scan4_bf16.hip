@@ -1,8 +1,9 @@
-// scan4_bf16.hip -- instantiates the four-directions-in-one-launch scan for bf16 storage.
+// scan4_bf16.hip -- instantiates the four-scans-in-one-launch kernels for bf16 storage with bf16 weights.
 #include "scan_kernel.hpp"
 
 namespace gspn {
 
-template hipError_t launch_fused4<bf16_t>(const Scan4K&, int, int, int, hipStream_t);
+template hipError_t launch_fused4<bf16_t, bf16_t>(const Scan4K&, int, int, int, hipStream_t);
+template hipError_t launch_fused4v<bf16_t, bf16_t>(const Scan4K&, int, int, int, hipStream_t);
 
 }  // namespace gspn

@@ -1,8 +1,9 @@
-// scan4_f32.hip -- instantiates the four-directions-in-one-launch scan for f32 storage.
+// scan4_f32.hip -- instantiates the four-scans-in-one-launch kernels for fp32 storage with fp32 weights.
 #include "scan_kernel.hpp"
 
 namespace gspn {
 
-template hipError_t launch_fused4<float>(const Scan4K&, int, int, int, hipStream_t);
+template hipError_t launch_fused4<float, float>(const Scan4K&, int, int, int, hipStream_t);
+template hipError_t launch_fused4v<float, float>(const Scan4K&, int, int, int, hipStream_t);
 
 }  // namespace gspn

@@ -1,9 +1,9 @@
-// scan_f32_horiz.hip -- instantiates the horizontal (L2R, R2L) line-scan kernels for f32 storage.
+// scan_f32_horiz.hip -- instantiates the horizontal (L2R, R2L) line-scan kernels for fp32 storage with fp32 weights.
 #include "scan_kernel.hpp"
 
 namespace gspn {
 
-template hipError_t launch_family<float, true>(const ScanConfig&, bool, const ScanK&, int64_t, int,
-                                          hipStream_t);
+template hipError_t launch_family<float, float, true>(const ScanConfig&, bool, bool, const ScanK&, int64_t,
+                                                 int, hipStream_t);
 
 }  // namespace gspn

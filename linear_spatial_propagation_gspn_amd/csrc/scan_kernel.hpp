@@ -1,6 +1,6 @@
 // scan_kernel.hpp -- the line-scan kernel template and its launch families
 // (internal to libgspn; instantiated per storage type and direction family in
-// scan_{f32,bf16}_{vert,horiz}.hip).
+// scan_*_{vert,horiz}.hip and scan4_*.hip).
 //
 // What it computes (GSPN-2 paper notes, "2D spatial propagation recap"):
 //   h_i[k] = sum_{o in {-1,0,+1}, 0 <= k+o < L} w_i[k,o] h_{i-1}[k+o]
@@ -15,21 +15,24 @@
 //    positions.  h stays in VGPRs for the whole scan.  The two values a lane
 //    needs from its neighbours (h[k0-1], h[k0+P]) go through a
 //    double-buffered LDS edge array: one barrier per step.
-//  - The scan-frame tensors (logits, lambda) are line-contiguous, so every
-//    step reads P contiguous values per lane: one coalesced row per stream.
-//    Their next D steps sit in a register ring, so HBM latency overlaps the
-//    serial chain of steps.
-//  - Vertical directions (T2B, B2T): x and y rows are lines too and go
-//    through the same ring.
+//  - The scan-frame tensors (logits, lambda) are line-contiguous, so a step
+//    reads one coalesced row per stream.  Vertical directions (T2B, B2T) read
+//    and write x and y rows the same way.
 //  - Horizontal directions (L2R, R2L): a line is an array column, so x and y
-//    are read and written as per-lane row tiles: for a block of U steps each
-//    lane loads the U consecutive columns of each of its rows (16-byte vector
-//    loads), keeps the y tile in registers while the block runs, and writes
-//    it back in one piece.  The next block's tiles are loaded while the
-//    current block runs.
+//    move as per-lane row tiles: for a tile of UT steps each lane loads the UT
+//    consecutive columns of each of its rows with 16-byte loads, keeps the y
+//    tile in registers while the tile runs and writes it back in one piece.
+//  - Latency hiding: per-step inputs are fetched a sub-block of U steps ahead
+//    and tiles a tile ahead, into double buffers selected at compile time.
+//    In the main loop every load address is clamped into the tensors instead
+//    of being guarded by a branch, so the loads form one straight sequence and
+//    the compiler waits only for the sub-block it needs (a guarded or
+//    branching load sequence makes it wait for every load in flight at every
+//    step).  A guarded tail loop finishes the last partial blocks.
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -43,16 +46,13 @@ struct ScanK {
     void* out;
     int64_t c;
     int64_t cw;
-    int S;          // scan steps
-    int L;          // line length
-    int K;          // steps per chunk
+    int S;         // scan steps
+    int L;         // line length
+    int K;         // steps per chunk
     int nchunks;
-    int reverse;    // scan runs from line S-1 down to 0
-    int logits;     // wts holds logits (1) or normalised weights (0)
-    int accumulate;
-    int vec_frame;  // wts / lam allow P-wide vector access
-    int vec_arr;    // vertical: x / out allow P-wide vector access
-    int vec_tile;   // horizontal: x / out rows allow 16-byte access at 16-byte columns
+    int reverse;   // scan runs from line S-1 down to 0
+    int logits;    // wts holds logits (1) or normalised weights (0)
+    int vec_tile;  // horizontal: every full tile of every chunk allows 16-byte row access
 };
 
 template <typename T, int N>
@@ -60,113 +60,24 @@ struct alignas(sizeof(T) * N) VecT {
     T e[N];
 };
 
-// Streaming access: the scan reads each logit, lambda and (vertical) x value
-// once and writes each output once.  With GSPN_STREAM_NT=1 those accesses
-// carry the nontemporal hint; measured on MI355X it slows the scan by about
-// half (profile workload, scan4 3.35 -> 4.97 ms), so it is off by default.
-#ifndef GSPN_STREAM_NT
-#define GSPN_STREAM_NT 0
-#endif
-
-template <typename T, int N>
-struct Ext {
-    typedef T type __attribute__((ext_vector_type(N)));
-};
-template <typename T>
-struct Ext<T, 1> {
-    typedef T type;
-};
-
-template <typename T, int N, bool NT>
-__device__ __forceinline__ VecT<T, N> vload(const T* p) {
-    if constexpr (NT && GSPN_STREAM_NT) {
-        using V = typename Ext<T, N>::type;
-        const V v = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
-        VecT<T, N> r;
-        if constexpr (N == 1) {
-            r.e[0] = v;
-        } else {
-#pragma unroll
-            for (int j = 0; j < N; ++j) r.e[j] = v[j];
-        }
-        return r;
-    } else {
-        return *reinterpret_cast<const VecT<T, N>*>(p);
-    }
-}
-
-template <typename T, int N, bool NT>
-__device__ __forceinline__ void vstore(T* p, const VecT<T, N>& r) {
-    if constexpr (NT && GSPN_STREAM_NT) {
-        using V = typename Ext<T, N>::type;
-        V v;
-        if constexpr (N == 1) {
-            v = r.e[0];
-        } else {
-#pragma unroll
-            for (int j = 0; j < N; ++j) v[j] = r.e[j];
-        }
-        __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
-    } else {
-        *reinterpret_cast<VecT<T, N>*>(p) = r;
-    }
-}
-
-template <typename T, bool NT>
-__device__ __forceinline__ float sload(const T* p) {
-    const VecT<T, 1> r = vload<T, 1, NT>(p);
-    return Store<T>::ld(&r.e[0]);
-}
-
-template <typename T, bool NT>
-__device__ __forceinline__ void sstore(T* p, float v) {
-    VecT<T, 1> r;
-    Store<T>::st(&r.e[0], v);
-    vstore<T, 1, NT>(p, r);
-}
-
-// P values of a line starting at position k0; positions >= L read as 0.
-template <typename T, int P, bool NT>
-__device__ __forceinline__ void load_run(const T* __restrict__ base, int k0, int L, bool vec,
-                                         float (&dst)[P]) {
-    if (vec) {
-        const VecT<T, P> v = vload<T, P, NT>(base + k0);
-#pragma unroll
-        for (int j = 0; j < P; ++j) dst[j] = Store<T>::ld(&v.e[j]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < P; ++j) dst[j] = (k0 + j < L) ? sload<T, NT>(base + k0 + j) : 0.0f;
-    }
-}
-
-template <typename T, int P, bool NT>
-__device__ __forceinline__ void store_run(T* __restrict__ base, int k0, int L, bool vec,
-                                          const float (&src)[P]) {
-    if (vec) {
-        VecT<T, P> v;
-#pragma unroll
-        for (int j = 0; j < P; ++j) Store<T>::st(&v.e[j], src[j]);
-        vstore<T, P, NT>(base + k0, v);
-    } else {
-#pragma unroll
-        for (int j = 0; j < P; ++j)
-            if (k0 + j < L) sstore<T, NT>(base + k0 + j, src[j]);
-    }
-}
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 // One line scan: plane p, chunk q of the direction described by a.
-// T: storage type.  P: positions per lane.  D: prefetch ring depth.
-// U: steps per block (a multiple of D; the horizontal tile width).
-// HORIZ / REV: direction.  Every lane of the workgroup takes part (lanes past
-// the end of the line hold no positions but join every barrier).
-// edge_raw: 4 * blockDim.x floats of LDS for the neighbour exchange.
-template <typename T, int P, int D, int U, bool HORIZ, bool REV>
+// T: storage type of x, lambda and the output; TW: storage type of the
+// logits / weights (the same as T, or fp32 weights normalised beforehand).
+// P: positions per lane.  U: steps per prefetch sub-block.  UT: steps per
+// tile (a multiple of U; the horizontal tile width).  HORIZ / REV: direction.
+// ACC: add into the output instead of overwriting it.
+// Every lane of the workgroup takes part: lanes past the end of the line hold
+// no positions but join every barrier.  edge_raw: 4 * blockDim.x floats of LDS.
+template <typename T, typename TW, int P, int U, int UT, bool HORIZ, bool REV, bool ACC>
 __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, float* edge_raw) {
-    static_assert(U % D == 0, "a block must hold whole ring turns");
-    constexpr int VW = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte vector
-    static_assert(!HORIZ || U % VW == 0, "tile width must be whole vectors");
+    static_assert(UT % U == 0, "a tile holds whole sub-blocks");
+    constexpr int NS = UT / U;                             // sub-blocks per tile
+    constexpr int VW = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte vector
+    static_assert(!HORIZ || UT % VW == 0, "tile width must be whole vectors");
 
-    // Edge exchange, [buffer][0 = first position, 1 = last position][lane].
     auto edge = [&](int b, int which, int lane) -> float& {
         return edge_raw[(b * 2 + which) * blockDim.x + lane];
     };
@@ -181,103 +92,138 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
 
     const T* __restrict__ xp = static_cast<const T*>(a.x) + p * plane;
     const T* __restrict__ lp = static_cast<const T*>(a.lam) + p * plane;
-    const T* __restrict__ zp =
-        static_cast<const T*>(a.wts) + (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane;
+    const TW* __restrict__ zp =
+        static_cast<const TW*>(a.wts) + (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane;
     T* __restrict__ op = static_cast<T*>(a.out) + p * plane;
 
     const int k0 = tid * P;
     const int t0 = q * a.K;
     const int t1 = min(t0 + a.K, S);
     const bool rev = HORIZ ? REV : (a.reverse != 0);
-    const bool vf = a.vec_frame && (k0 + P <= L);
-    const bool va = !HORIZ && a.vec_arr && (k0 + P <= L);
-    const bool acc = a.accumulate != 0;
+    const bool logits = a.logits != 0;
 
-    // Register ring: per-step inputs of the next D steps.
-    float rz[D][3][P];
-    float rl[D][P];
-    float rx[HORIZ ? 1 : D][P];
-    float ry[HORIZ ? 1 : D][P];
-    // Horizontal tiles (two blocks: current and next).
-    float xt[HORIZ ? 2 : 1][P][HORIZ ? U : 1];
-    float yt[HORIZ ? 2 : 1][P][HORIZ ? U : 1];
-
-    auto fetch = [&](int slot, int t) {
-        if (t >= t1) return;
-        const int i = rev ? S - 1 - t : t;
-        const int64_t lo = static_cast<int64_t>(i) * L;
+    // Positions of this lane, clamped into the line for addressing.
+    int kk[P];
+    bool kin[P];
 #pragma unroll
-        for (int o = 0; o < 3; ++o) load_run<T, P, true>(zp + o * plane + lo, k0, L, vf, rz[slot][o]);
-        load_run<T, P, true>(lp + lo, k0, L, vf, rl[slot]);
-        if constexpr (!HORIZ) {
-            load_run<T, P, true>(xp + lo, k0, L, va, rx[slot]);
-            if (acc) load_run<T, P, true>(op + lo, k0, L, va, ry[slot]);
+    for (int j = 0; j < P; ++j) {
+        kk[j] = min(k0 + j, L - 1);
+        kin[j] = k0 + j < L;
+    }
+
+    // Double-buffered per-step inputs: [buffer][step of the sub-block].
+    float rz[2][U][3][P];
+    float rl[2][U][P];
+    float rx[HORIZ ? 1 : 2][U][P];
+    float ry[(!HORIZ && ACC) ? 2 : 1][U][P];
+    // Horizontal tiles: [buffer][position][step of the tile].
+    float xt[HORIZ ? 2 : 1][P][HORIZ ? UT : 1];
+    float yt[HORIZ ? 2 : 1][P][HORIZ ? UT : 1];
+
+    auto line_of = [&](int t) { return rev ? S - 1 - t : t; };
+
+    // Inputs of the U steps from tb into ring buffer R; steps past the chunk
+    // read the chunk's last line (loaded, never used).
+    auto load_ring = [&](auto rc, int tb) {
+        constexpr int R = decltype(rc)::value;
+#pragma unroll
+        for (int s = 0; s < U; ++s) {
+            const int64_t lo = static_cast<int64_t>(line_of(min(tb + s, t1 - 1))) * L;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+#pragma unroll
+                for (int o = 0; o < 3; ++o) rz[R][s][o][j] = Store<TW>::ld(zp + o * plane + lo + kk[j]);
+                rl[R][s][j] = Store<T>::ld(lp + lo + kk[j]);
+                if constexpr (!HORIZ) {
+                    rx[R][s][j] = Store<T>::ld(xp + lo + kk[j]);
+                    if constexpr (ACC) ry[R][s][j] = Store<T>::ld(op + lo + kk[j]);
+                }
+            }
         }
     };
 
-    // Horizontal tile of the block starting at step tb: array columns
-    // [c_lo, c_lo + U); step tb + s sits at column offset (REV ? U-1-s : s).
-    auto tile_lo = [&](int tb) { return REV ? S - tb - U : tb; };
+    // Horizontal tile of the UT steps from tb: array columns [c_lo, c_lo+UT);
+    // step tb + s sits at column offset (REV ? UT-1-s : s).
+    auto tile_lo = [&](int tb) { return REV ? S - tb - UT : tb; };
 
-    auto load_tile = [&](float (&xd)[P][HORIZ ? U : 1], float (&yd)[P][HORIZ ? U : 1], int tb) {
+    // Full tile with 16-byte loads; the column range is clamped into the row
+    // (a tile past the chunk end is loaded but never used).
+    auto load_tile_vec = [&](auto tc, int tb) {
         if constexpr (HORIZ) {
-            const int clo = tile_lo(tb);
-            const bool full = tb + U <= t1;
-            const bool vec = full && a.vec_tile && (clo % VW == 0);
+            constexpr int C = decltype(tc)::value;
+            const int clo = min(max(tile_lo(tb), 0), S - UT);
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                const int k = k0 + j;
-                const bool row = k < L;
-                const T* xr = xp + static_cast<int64_t>(k) * S;
-                const T* yr = op + static_cast<int64_t>(k) * S;
-                if (vec && row) {
+                const T* xr = xp + static_cast<int64_t>(kk[j]) * S + clo;
+                const T* yr = op + static_cast<int64_t>(kk[j]) * S + clo;
 #pragma unroll
-                    for (int v = 0; v < U / VW; ++v) {
-                        const VecT<T, VW> xv = *reinterpret_cast<const VecT<T, VW>*>(xr + clo + v * VW);
+                for (int v = 0; v < UT / VW; ++v) {
+                    const VecT<T, VW> xv = *reinterpret_cast<const VecT<T, VW>*>(xr + v * VW);
 #pragma unroll
-                        for (int e = 0; e < VW; ++e) xd[j][v * VW + e] = Store<T>::ld(&xv.e[e]);
-                        if (acc) {
-                            const VecT<T, VW> yv = vload<T, VW, true>(yr + clo + v * VW);
+                    for (int e = 0; e < VW; ++e) xt[C][j][v * VW + e] = Store<T>::ld(&xv.e[e]);
+                    if constexpr (ACC) {
+                        const VecT<T, VW> yv = *reinterpret_cast<const VecT<T, VW>*>(yr + v * VW);
 #pragma unroll
-                            for (int e = 0; e < VW; ++e) yd[j][v * VW + e] = Store<T>::ld(&yv.e[e]);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int s = REV ? U - 1 - u : u;
-                        const bool on = row && (tb + s < t1);
-                        xd[j][u] = on ? Store<T>::ld(xr + clo + u) : 0.0f;
-                        yd[j][u] = (on && acc) ? sload<T, true>(yr + clo + u) : 0.0f;
+                        for (int e = 0; e < VW; ++e) yt[C][j][v * VW + e] = Store<T>::ld(&yv.e[e]);
                     }
                 }
             }
         }
     };
 
-    auto store_tile = [&](const float (&yd)[P][HORIZ ? U : 1], int tb) {
+    // Any tile with element loads, columns clamped into the row.
+    auto load_tile_elem = [&](auto tc, int tb) {
         if constexpr (HORIZ) {
+            constexpr int C = decltype(tc)::value;
             const int clo = tile_lo(tb);
-            const bool full = tb + U <= t1;
-            const bool vec = full && a.vec_tile && (clo % VW == 0);
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                const int k = k0 + j;
-                if (k >= L) continue;
-                T* yr = op + static_cast<int64_t>(k) * S;
-                if (vec) {
+                const T* xr = xp + static_cast<int64_t>(kk[j]) * S;
+                const T* yr = op + static_cast<int64_t>(kk[j]) * S;
 #pragma unroll
-                    for (int v = 0; v < U / VW; ++v) {
+                for (int u = 0; u < UT; ++u) {
+                    const int col = min(max(clo + u, 0), S - 1);
+                    xt[C][j][u] = Store<T>::ld(xr + col);
+                    if constexpr (ACC) yt[C][j][u] = Store<T>::ld(yr + col);
+                }
+            }
+        }
+    };
+
+    // Full tile with 16-byte stores (its columns lie inside the chunk).
+    auto store_tile_vec = [&](auto tc, int tb) {
+        if constexpr (HORIZ) {
+            constexpr int C = decltype(tc)::value;
+            const int clo = tile_lo(tb);
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                if (kin[j]) {
+                    T* yr = op + static_cast<int64_t>(k0 + j) * S + clo;
+#pragma unroll
+                    for (int v = 0; v < UT / VW; ++v) {
                         VecT<T, VW> yv;
 #pragma unroll
-                        for (int e = 0; e < VW; ++e) Store<T>::st(&yv.e[e], yd[j][v * VW + e]);
-                        vstore<T, VW, true>(yr + clo + v * VW, yv);
+                        for (int e = 0; e < VW; ++e) Store<T>::st(&yv.e[e], yt[C][j][v * VW + e]);
+                        *reinterpret_cast<VecT<T, VW>*>(yr + v * VW) = yv;
                     }
-                } else {
+                }
+            }
+        }
+    };
+
+    // Partial tile: element stores for the steps inside the chunk only.
+    auto store_tile_elem = [&](auto tc, int tb) {
+        if constexpr (HORIZ) {
+            constexpr int C = decltype(tc)::value;
+            const int clo = tile_lo(tb);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int s = REV ? U - 1 - u : u;
-                        if (tb + s < t1) sstore<T, true>(yr + clo + u, yd[j][u]);
+            for (int j = 0; j < P; ++j) {
+                if (kin[j]) {
+                    T* yr = op + static_cast<int64_t>(k0 + j) * S;
+#pragma unroll
+                    for (int u = 0; u < UT; ++u) {
+                        const int s = REV ? UT - 1 - u : u;
+                        if (tb + s < t1) Store<T>::st(yr + clo + u, yt[C][j][u]);
                     }
                 }
             }
@@ -287,28 +233,20 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
     float h[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) h[j] = 0.0f;
-
-#pragma unroll
-    for (int s = 0; s < D; ++s) fetch(s, t0 + s);
-    if constexpr (HORIZ) load_tile(xt[0], yt[0], t0);
-
     int buf = 0;
 
-    // One block of U steps; CUR selects the tile buffers statically.
-    auto run_block = [&](auto cur_c, int tb) {
-        constexpr int CUR = decltype(cur_c)::value;
-        constexpr int NXT = HORIZ ? 1 - CUR : 0;
-        constexpr int CB = HORIZ ? CUR : 0;
-        if constexpr (HORIZ) {
-            if (tb + U < t1) load_tile(xt[NXT], yt[NXT], tb + U);
-        }
+    // U steps from tb, inputs in ring buffer R, inside the tile of buffer C
+    // whose first step is tb - M * U.  GUARD: steps at or past t1 are skipped.
+    auto sub_block = [&](auto rc, auto tc, auto mc, auto gc, int tb) {
+        constexpr int R = decltype(rc)::value;
+        constexpr int C = HORIZ ? decltype(tc)::value : 0;
+        constexpr int M = decltype(mc)::value;
+        constexpr bool GUARD = decltype(gc)::value != 0;
 #pragma unroll
         for (int s = 0; s < U; ++s) {
             const int t = tb + s;
-            if (t < t1) {
-                const int slot = s % D;
-                const int off = HORIZ ? (REV ? U - 1 - s : s) : 0;
-                const int i = rev ? S - 1 - t : t;
+            if (!GUARD || t < t1) {
+                const int off = HORIZ ? (REV ? UT - 1 - (M * U + s) : (M * U + s)) : 0;
                 const bool first = (t == t0);
                 float left = 0.0f, right = 0.0f;
                 if (!first) {
@@ -318,135 +256,178 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
                 float hn[P];
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
-                    const int k = k0 + j;
-                    const float xv = HORIZ ? xt[CB][j][off] : rx[HORIZ ? 0 : slot][j];
-                    float u = rl[slot][j] * xv;
+                    const float xv = HORIZ ? xt[C][j][off] : rx[HORIZ ? 0 : R][s][j];
+                    float u = rl[R][s][j] * xv;
                     if (!first) {
+                        const bool has_l = k0 + j > 0;
+                        const bool has_r = k0 + j + 1 < L;
                         float w0, w1, w2;
-                        const bool has_l = k > 0;
-                        const bool has_r = k + 1 < L;
-                        if (a.logits) {
-                            normalise_row(rz[slot][0][j], rz[slot][1][j], rz[slot][2][j], has_l, has_r,
-                                          w0, w1, w2);
+                        if (logits) {
+                            normalise_row(rz[R][s][0][j], rz[R][s][1][j], rz[R][s][2][j], has_l, has_r, w0,
+                                          w1, w2);
                         } else {
-                            w0 = has_l ? rz[slot][0][j] : 0.0f;
-                            w1 = rz[slot][1][j];
-                            w2 = has_r ? rz[slot][2][j] : 0.0f;
+                            w0 = has_l ? rz[R][s][0][j] : 0.0f;
+                            w1 = rz[R][s][1][j];
+                            w2 = has_r ? rz[R][s][2][j] : 0.0f;
                         }
                         const float hl = (j == 0) ? left : h[j - 1];
                         const float hr = (j == P - 1) ? right : h[j + 1];
                         u = __builtin_fmaf(w0, hl, __builtin_fmaf(w1, h[j], __builtin_fmaf(w2, hr, u)));
                     }
-                    hn[j] = (k < L) ? u : 0.0f;
+                    hn[j] = kin[j] ? u : 0.0f;
                 }
                 if constexpr (HORIZ) {
 #pragma unroll
-                    for (int j = 0; j < P; ++j)
-                        yt[CB][j][off] = acc ? yt[CB][j][off] + hn[j] : hn[j];
+                    for (int j = 0; j < P; ++j) yt[C][j][off] = ACC ? yt[C][j][off] + hn[j] : hn[j];
                 } else {
-                    float ov[P];
+                    T* orow = op + static_cast<int64_t>(line_of(t)) * L;
 #pragma unroll
-                    for (int j = 0; j < P; ++j) ov[j] = acc ? ry[slot][j] + hn[j] : hn[j];
-                    store_run<T, P, true>(op + static_cast<int64_t>(i) * L, k0, L, va, ov);
+                    for (int j = 0; j < P; ++j) {
+                        const float v = ACC ? ry[(HORIZ || !ACC) ? 0 : R][s][j] + hn[j] : hn[j];
+                        if (kin[j]) Store<T>::st(orow + k0 + j, v);
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < P; ++j) h[j] = hn[j];
-
-                fetch(slot, t + D);
-
                 buf ^= 1;
                 edge(buf, 0, tid) = h[0];
                 edge(buf, 1, tid) = h[P - 1];
                 __syncthreads();
             }
         }
-        if constexpr (HORIZ) store_tile(yt[CB], tb);
     };
 
-    for (int tb = t0; tb < t1; tb += 2 * U) {
-        run_block(std::integral_constant<int, 0>{}, tb);
-        if (tb + U < t1) run_block(std::integral_constant<int, 1>{}, tb + U);
+    // One tile of UT steps from tb with tile buffer C; the ring parity of its
+    // first sub-block is R0.  Loads for the next tile / sub-block are issued
+    // before the steps that precede their use.
+    auto run_tile = [&](auto tc, auto r0c, auto gc, int tb) {
+        constexpr int C = decltype(tc)::value;
+        constexpr int R0 = decltype(r0c)::value;
+        constexpr bool GUARD = decltype(gc)::value != 0;
+        if constexpr (HORIZ) {
+            if constexpr (GUARD) {
+                if (tb + UT < t1) load_tile_elem(IC<1 - C>{}, tb + UT);
+            } else {
+                load_tile_vec(IC<1 - C>{}, tb + UT);
+            }
+        }
+        auto one = [&](auto mc) {
+            constexpr int M = decltype(mc)::value;
+            constexpr int R = (R0 + M) & 1;
+            load_ring(IC<1 - R>{}, tb + (M + 1) * U);
+            sub_block(IC<R>{}, IC<C>{}, IC<M>{}, gc, tb + M * U);
+        };
+        [&]<int... Ms>(std::integer_sequence<int, Ms...>) {
+            (one(IC<Ms>{}), ...);
+        }(std::make_integer_sequence<int, NS>{});
+        if constexpr (HORIZ) {
+            if constexpr (GUARD) {
+                store_tile_elem(IC<C>{}, tb);
+            } else {
+                store_tile_vec(IC<C>{}, tb);
+            }
+        }
+    };
+
+    constexpr int RT1 = NS & 1;  // ring parity at the start of the second tile
+    int tb = t0;
+    const bool fast = !HORIZ || a.vec_tile;
+    if (fast) {
+        load_ring(IC<0>{}, t0);
+        load_tile_vec(IC<0>{}, t0);
+        for (; tb + 2 * UT <= t1; tb += 2 * UT) {
+            run_tile(IC<0>{}, IC<0>{}, IC<0>{}, tb);
+            run_tile(IC<1>{}, IC<RT1>{}, IC<0>{}, tb + UT);
+        }
+    }
+    if (tb < t1) {
+        load_ring(IC<0>{}, tb);
+        load_tile_elem(IC<0>{}, tb);
+        for (; tb < t1; tb += 2 * UT) {
+            run_tile(IC<0>{}, IC<0>{}, IC<1>{}, tb);
+            if (tb + UT < t1) run_tile(IC<1>{}, IC<RT1>{}, IC<1>{}, tb + UT);
+        }
     }
 }
 
+#ifndef GSPN_VERT_WAVES
+#define GSPN_VERT_WAVES 8
+#endif
+
+// Waves per SIMD to budget registers for: vertical-form scans with one
+// position per lane fit in 64 VGPRs, so two 1024-lane workgroups share a CU.
+template <bool HORIZ, int P>
+constexpr int waves_per_eu() {
+    return (!HORIZ && P == 1) ? GSPN_VERT_WAVES : 4;
+}
 
 // Single-direction launch: one workgroup per (plane, chunk).
-template <typename T, int P, int D, int U, bool HORIZ, bool REV, int MAXT>
-__global__ __launch_bounds__(MAXT) void scan_kernel(const ScanK a) {
+template <typename T, typename TW, int P, int U, int UT, bool HORIZ, bool REV, bool ACC>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(waves_per_eu<HORIZ, P>())))
+void scan_kernel(const ScanK a) {
     extern __shared__ float s_edge_raw[];
     const int64_t blk = blockIdx.x;
     const int64_t p = blk / a.nchunks;  // plane n * c + ci
     const int q = static_cast<int>(blk - p * a.nchunks);
-    scan_line<T, P, D, U, HORIZ, REV>(a, p, q, s_edge_raw);
+    scan_line<T, TW, P, U, UT, HORIZ, REV, ACC>(a, p, q, s_edge_raw);
 }
 
 // ---------------------------------------------------------------------------
 // Launch families
 // ---------------------------------------------------------------------------
 
-// Positions per lane and most lanes per workgroup.
+// Positions per lane (P in {1, 2, 4}: up to 1024 lanes per workgroup).
 struct ScanConfig {
     int P;
-    int maxt;
 };
 
-// Horizontal tile width: 16 steps for one position per lane, fewer for more
-// positions so the two tiles of x and y stay in registers; at least one
-// 16-byte vector per row and one turn of the prefetch ring.
-template <typename T, int P, int D>
-constexpr int tile_width() {
-    constexpr int vw = 16 / static_cast<int>(sizeof(T));
-    constexpr int u = (16 / P) > vw ? (16 / P) : vw;
-    return u > D ? u : D;
-}
+#ifndef GSPN_SUB_U
+#define GSPN_SUB_U 2
+#endif
 
-template <typename T, int P, int D, int MAXT, bool HORIZ, bool REV>
+// Steps per prefetch sub-block and per tile.  The sub-block shrinks with the
+// positions per lane and horizontal tiles hold 16 steps (64 bytes of fp32 or
+// 32 of bf16 per row) for one position per lane, fewer for more positions, so
+// that the double buffers stay in registers.
+template <typename T, int P, bool HORIZ>
+struct Blocking {
+    static constexpr int U = GSPN_SUB_U / P > 1 ? GSPN_SUB_U / P : 1;
+    static constexpr int VW = 16 / static_cast<int>(sizeof(T));
+    static constexpr int T0 = (16 / P) > VW ? (16 / P) : VW;
+    static constexpr int UT = HORIZ ? (T0 > U ? T0 : U) : 2 * U;
+};
+
+template <typename T, typename TW, int P, bool HORIZ, bool REV, bool ACC>
 hipError_t launch_one(const ScanK& k, int64_t nblocks, int nthreads, hipStream_t stream) {
-    constexpr int U = HORIZ ? tile_width<T, P, D>() : D;
+    using B = Blocking<T, P, HORIZ>;
     const size_t lds = 4 * sizeof(float) * static_cast<size_t>(nthreads);
-    hipLaunchKernelGGL((scan_kernel<T, P, D, U, HORIZ, REV, MAXT>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(nthreads), lds, stream, k);
+    hipLaunchKernelGGL((scan_kernel<T, TW, P, B::U, B::UT, HORIZ, REV, ACC>),
+                       dim3(static_cast<unsigned>(nblocks)), dim3(nthreads), lds, stream, k);
     return hipGetLastError();
 }
 
-#ifndef GSPN_RING_D
-#define GSPN_RING_D 4
-#endif
-
-template <typename T, int P, int D, int MAXT, bool HORIZ>
-hipError_t launch_rev(bool rev, const ScanK& k, int64_t nblocks, int nthreads, hipStream_t stream) {
+template <typename T, typename TW, int P, bool HORIZ>
+hipError_t launch_p(bool rev, bool acc, const ScanK& k, int64_t nblocks, int nthreads, hipStream_t stream) {
     if constexpr (HORIZ) {
-        return rev ? launch_one<T, P, D, MAXT, true, true>(k, nblocks, nthreads, stream)
-                   : launch_one<T, P, D, MAXT, true, false>(k, nblocks, nthreads, stream);
+        if (rev) {
+            return acc ? launch_one<T, TW, P, true, true, true>(k, nblocks, nthreads, stream)
+                       : launch_one<T, TW, P, true, true, false>(k, nblocks, nthreads, stream);
+        }
+        return acc ? launch_one<T, TW, P, true, false, true>(k, nblocks, nthreads, stream)
+                   : launch_one<T, TW, P, true, false, false>(k, nblocks, nthreads, stream);
     } else {
-        return launch_one<T, P, D, MAXT, false, false>(k, nblocks, nthreads, stream);
+        return acc ? launch_one<T, TW, P, false, false, true>(k, nblocks, nthreads, stream)
+                   : launch_one<T, TW, P, false, false, false>(k, nblocks, nthreads, stream);
     }
 }
 
-// Instantiated families.  Up to 256 lanes: one position per lane.  Up to
-// 1024 lanes: P in {1, 2, 4} with a GSPN_RING_D-deep ring; P = 8 (lines over
-// 4096 positions) with a 2-deep ring.  Builds with GSPN_TUNING also
-// instantiate P in {2, 4, 8} on 256 lanes.
-template <typename T, bool HORIZ>
-hipError_t launch_family(const ScanConfig& c, bool rev, const ScanK& k, int64_t nblocks, int nthreads,
-                         hipStream_t stream) {
-    constexpr int D = GSPN_RING_D;
-    if (c.maxt == 256) {
-#ifdef GSPN_TUNING
-        switch (c.P) {
-            case 2: return launch_rev<T, 2, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-            case 4: return launch_rev<T, 4, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-            case 8: return launch_rev<T, 8, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-            default: break;
-        }
-#endif
-        return launch_rev<T, 1, D, 256, HORIZ>(rev, k, nblocks, nthreads, stream);
-    }
+template <typename T, typename TW, bool HORIZ>
+hipError_t launch_family(const ScanConfig& c, bool rev, bool acc, const ScanK& k, int64_t nblocks,
+                         int nthreads, hipStream_t stream) {
     switch (c.P) {
-        case 1: return launch_rev<T, 1, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
-        case 2: return launch_rev<T, 2, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
-        case 4: return launch_rev<T, 4, D, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
-        default: return launch_rev<T, 8, 2, 1024, HORIZ>(rev, k, nblocks, nthreads, stream);
+        case 1: return launch_p<T, TW, 1, HORIZ>(rev, acc, k, nblocks, nthreads, stream);
+        case 2: return launch_p<T, TW, 2, HORIZ>(rev, acc, k, nblocks, nthreads, stream);
+        default: return launch_p<T, TW, 4, HORIZ>(rev, acc, k, nblocks, nthreads, stream);
     }
 }
 
@@ -464,11 +445,11 @@ struct Scan4K {
     int interleave;
 };
 
-template <typename T, int PV, int PH>
+template <typename T, typename TW, int PV, int PH>
 __global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
     extern __shared__ float s_edge_raw[];
-    constexpr int D = GSPN_RING_D;
-    constexpr int UH = tile_width<T, PH, D>();
+    using BV = Blocking<T, PV, false>;
+    using BH = Blocking<T, PH, true>;
     const int64_t b = blockIdx.x;
     int dir = 0;
     int64_t idx = b;
@@ -486,25 +467,75 @@ __global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
     const int q = static_cast<int>(idx - p * k.nchunks);
     switch (dir) {
         case 0:
-        case 1: scan_line<T, PV, D, D, false, false>(k, p, q, s_edge_raw); break;
-        case 2: scan_line<T, PH, D, UH, true, false>(k, p, q, s_edge_raw); break;
-        default: scan_line<T, PH, D, UH, true, true>(k, p, q, s_edge_raw); break;
+        case 1: scan_line<T, TW, PV, BV::U, BV::UT, false, false, false>(k, p, q, s_edge_raw); break;
+        case 2: scan_line<T, TW, PH, BH::U, BH::UT, true, false, false>(k, p, q, s_edge_raw); break;
+        default: scan_line<T, TW, PH, BH::U, BH::UT, true, true, false>(k, p, q, s_edge_raw); break;
     }
 }
 
-template <typename T>
+// Four scans in one launch, all in the vertical form: the horizontal
+// directions are described as vertical scans of the transposed input (their
+// scan frame), so every access is a coalesced row.  PV / PH: positions per
+// lane of the first two / last two scans.
+template <typename T, typename TW, int PV, int PH>
+__global__ __launch_bounds__(1024)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<false, (PV > PH ? PV : PH)>())))
+void scan4v_kernel(const Scan4K a) {
+    extern __shared__ float s_edge_raw[];
+    using BV = Blocking<T, PV, false>;
+    using BH = Blocking<T, PH, false>;
+    const int64_t b = blockIdx.x;
+    int dir = 0;
+    int64_t idx = b;
+    if (a.interleave) {
+        dir = static_cast<int>(b & 3);
+        idx = b >> 2;
+    } else {
+        while (dir < 3 && idx >= a.blocks[dir]) {
+            idx -= a.blocks[dir];
+            ++dir;
+        }
+    }
+    const ScanK& k = a.d[dir];
+    const int64_t p = idx / k.nchunks;
+    const int q = static_cast<int>(idx - p * k.nchunks);
+    if (dir < 2) {
+        scan_line<T, TW, PV, BV::U, BV::UT, false, false, false>(k, p, q, s_edge_raw);
+    } else {
+        scan_line<T, TW, PH, BH::U, BH::UT, false, false, false>(k, p, q, s_edge_raw);
+    }
+}
+
+template <typename T, typename TW>
+hipError_t launch_fused4v(const Scan4K& k, int pv, int ph, int nthreads, hipStream_t stream) {
+    const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
+    const size_t lds = 4 * sizeof(float) * static_cast<size_t>(nthreads);
+    const dim3 grid(static_cast<unsigned>(nblocks));
+    if (pv == 1 && ph == 1) {
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 1, 1>), grid, dim3(nthreads), lds, stream, k);
+    } else if (pv == 1) {
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 1, 2>), grid, dim3(nthreads), lds, stream, k);
+    } else if (ph == 1) {
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 2, 1>), grid, dim3(nthreads), lds, stream, k);
+    } else {
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 2, 2>), grid, dim3(nthreads), lds, stream, k);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename TW>
 hipError_t launch_fused4(const Scan4K& k, int pv, int ph, int nthreads, hipStream_t stream) {
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
     const size_t lds = 4 * sizeof(float) * static_cast<size_t>(nthreads);
     const dim3 grid(static_cast<unsigned>(nblocks));
     if (pv == 1 && ph == 1) {
-        hipLaunchKernelGGL((scan4_kernel<T, 1, 1>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4_kernel<T, TW, 1, 1>), grid, dim3(nthreads), lds, stream, k);
     } else if (pv == 1) {
-        hipLaunchKernelGGL((scan4_kernel<T, 1, 2>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4_kernel<T, TW, 1, 2>), grid, dim3(nthreads), lds, stream, k);
     } else if (ph == 1) {
-        hipLaunchKernelGGL((scan4_kernel<T, 2, 1>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4_kernel<T, TW, 2, 1>), grid, dim3(nthreads), lds, stream, k);
     } else {
-        hipLaunchKernelGGL((scan4_kernel<T, 2, 2>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4_kernel<T, TW, 2, 2>), grid, dim3(nthreads), lds, stream, k);
     }
     return hipGetLastError();
 }

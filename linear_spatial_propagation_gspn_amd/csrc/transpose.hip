@@ -1,0 +1,197 @@
+// transpose.hip -- plane transposes that let the horizontal directions run as
+// row-coalesced scans: x is transposed once into the horizontal scan frame
+// (column i of the array becomes row i), the horizontal scans run on that
+// copy with the same kernel as the vertical ones, and their outputs are
+// folded back into y through a transposing merge.
+//
+// Both kernels move 64 x 64 tiles through LDS: every global access is a
+// 16-byte vector (where the shapes allow) within a run of 64 consecutive
+// elements along the row of the tensor it touches, and the transpose happens
+// in LDS (rows padded by one element so the column reads hit different banks).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace gspn {
+namespace {
+
+constexpr int kTile = 64;
+constexpr int kThreads = 256;
+
+struct TileIndex {
+    int64_t plane;
+    int r0;  // first row of the tile in the source frame
+    int c0;  // first column of the tile in the source frame
+};
+
+__device__ __forceinline__ TileIndex tile_of(int64_t blk, int R, int Cc) {
+    const int tr = (R + kTile - 1) / kTile;
+    const int tc = (Cc + kTile - 1) / kTile;
+    const int64_t per_plane = static_cast<int64_t>(tr) * tc;
+    TileIndex t;
+    t.plane = blk / per_plane;
+    const int64_t r = blk - t.plane * per_plane;
+    t.r0 = static_cast<int>(r / tc) * kTile;
+    t.c0 = static_cast<int>(r % tc) * kTile;
+    return t;
+}
+
+template <typename T>
+struct alignas(16) Vec16 {
+    T e[16 / sizeof(T)];
+};
+
+// Moves one 64 x 64 tile of a (rows x cols) plane between global memory and
+// an fp32 LDS tile, 16 bytes per lane per access along the rows: row r, column
+// c of the tile is element (r0 + r, c0 + c) of the plane.  vec: the plane's
+// rows allow 16-byte accesses (cols and the base are whole vectors);
+// otherwise single elements.  Elements outside the plane read as 0 / are not
+// written.
+template <typename T>
+struct TileIO {
+    static constexpr int VW = 16 / static_cast<int>(sizeof(T));  // elements per vector
+    static constexpr int LPR = kTile / VW;                        // lanes per tile row
+    static constexpr int RPP = kThreads / LPR;                    // rows per pass
+
+    template <typename F>
+    static __device__ __forceinline__ void read(const T* plane, int rows, int cols, int r0, int c0, bool vec,
+                                                F&& put) {
+        const int lr = threadIdx.x / LPR;
+        const int lc = (threadIdx.x % LPR) * VW;
+#pragma unroll
+        for (int i = 0; i < kTile / RPP; ++i) {
+            const int r = lr + i * RPP;
+            const int gr = r0 + r;
+            const int gc = c0 + lc;
+            const T* src = plane + static_cast<int64_t>(gr) * cols + gc;
+            if (vec && gr < rows && gc + VW <= cols) {
+                const Vec16<T> v = *reinterpret_cast<const Vec16<T>*>(src);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) put(r, lc + e, Store<T>::ld(&v.e[e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < VW; ++e)
+                    put(r, lc + e, (gr < rows && gc + e < cols) ? Store<T>::ld(src + e) : 0.0f);
+            }
+        }
+    }
+
+    template <typename F>
+    static __device__ __forceinline__ void write(T* plane, int rows, int cols, int r0, int c0, bool vec, F&& get) {
+        const int lr = threadIdx.x / LPR;
+        const int lc = (threadIdx.x % LPR) * VW;
+#pragma unroll
+        for (int i = 0; i < kTile / RPP; ++i) {
+            const int r = lr + i * RPP;
+            const int gr = r0 + r;
+            const int gc = c0 + lc;
+            if (gr >= rows) continue;
+            T* dst = plane + static_cast<int64_t>(gr) * cols + gc;
+            if (vec && gc + VW <= cols) {
+                Vec16<T> v;
+#pragma unroll
+                for (int e = 0; e < VW; ++e) Store<T>::st(&v.e[e], get(r, lc + e, dst + e));
+                *reinterpret_cast<Vec16<T>*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < VW; ++e)
+                    if (gc + e < cols) Store<T>::st(dst + e, get(r, lc + e, dst + e));
+            }
+        }
+    }
+};
+
+// dst[p][c][r] = src[p][r][c] for planes of R x Cc.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                             int R, int Cc, int vec_src, int vec_dst) {
+    __shared__ float tile[kTile][kTile + 1];
+    const TileIndex ti = tile_of(blockIdx.x, R, Cc);
+    const int64_t plane = static_cast<int64_t>(R) * Cc;
+    TileIO<T>::read(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_src,
+                    [&](int r, int c, float v) { tile[r][c] = v; });
+    __syncthreads();
+    // destination plane is Cc x R: its row c holds source column c
+    TileIO<T>::write(dst + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_dst,
+                     [&](int c, int r, const T*) { return tile[r][c]; });
+}
+
+// For planes of R x Cc in the array frame:
+//   y[p][r][c] = ((z2[p][c][r] + z3[p][c][r]) + y[p][r][c] (if accumulate)) + a[p][r][c]
+// where a, z2, z3 may each be absent (NULL) and z2, z3 are in the transposed
+// frame (Cc x R planes).  Every source is read into the LDS tile with
+// row-vector accesses of its own frame; y is read completely before it is
+// written, so it may be updated in place.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const T* __restrict__ a,
+                                                           const T* __restrict__ z2, const T* __restrict__ z3,
+                                                           int R, int Cc, int accumulate, int vec_y, int vec_z) {
+    __shared__ float tile[kTile][kTile + 1];
+    const TileIndex ti = tile_of(blockIdx.x, R, Cc);
+    const int64_t plane = static_cast<int64_t>(R) * Cc;
+    bool any = false;
+    auto add_t = [&](const T* z) {  // transposed source: its row c is column c of the tile
+        if (any) __syncthreads();
+        const bool first = !any;
+        TileIO<T>::read(z + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_z,
+                        [&](int c, int r, float v) { tile[r][c] = first ? v : tile[r][c] + v; });
+        any = true;
+    };
+    auto add_a = [&](const T* src) {  // array-frame source
+        if (any) __syncthreads();
+        const bool first = !any;
+        TileIO<T>::read(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
+                        [&](int r, int c, float v) { tile[r][c] = first ? v : tile[r][c] + v; });
+        any = true;
+    };
+    if (z2) add_t(z2);
+    if (z3) add_t(z3);
+    if (accumulate) add_a(y);
+    if (a) add_a(a);
+    __syncthreads();
+    TileIO<T>::write(y + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
+                     [&](int r, int c, const T*) { return any ? tile[r][c] : 0.0f; });
+}
+
+int64_t tiles_for(int64_t planes, int R, int Cc) {
+    return planes * ((R + kTile - 1) / kTile) * ((Cc + kTile - 1) / kTile);
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+}  // namespace
+
+hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, int Cc, int dtype,
+                            hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(tiles_for(planes, R, Cc)));
+    const int vw = dtype == kF32 ? 4 : 8;
+    const int vs = (Cc % vw == 0) && aligned16(src);
+    const int vd = (R % vw == 0) && aligned16(dst);
+    if (dtype == kF32) {
+        hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const float*>(src), static_cast<float*>(dst), R, Cc, vs, vd);
+    } else {
+        hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), R, Cc, vs, vd);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3, int64_t planes, int R,
+                          int Cc, int accumulate, int dtype, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(tiles_for(planes, R, Cc)));
+    const int vw = dtype == kF32 ? 4 : 8;
+    const int vy = (Cc % vw == 0) && aligned16(y) && (!a || aligned16(a));
+    const int vz = (R % vw == 0) && (!z2 || aligned16(z2)) && (!z3 || aligned16(z3));
+    if (dtype == kF32) {
+        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
+                           static_cast<const float*>(a), static_cast<const float*>(z2),
+                           static_cast<const float*>(z3), R, Cc, accumulate, vy, vz);
+    } else {
+        hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, static_cast<bf16_t*>(y),
+                           static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(z2),
+                           static_cast<const bf16_t*>(z3), R, Cc, accumulate, vy, vz);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gspn

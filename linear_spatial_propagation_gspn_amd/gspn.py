@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
             h.gspn_scan4_fwd.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), ctypes.POINTER(vp), ci, vp]
             h.gspn_scan4_fwd.restype = ci
-            h.gspn_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+            h.gspn_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
             h.gspn_forward4_workspace_bytes.restype = i64
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp, vp, i64, ci, vp]
@@ -217,15 +217,19 @@ def gspn_scan4_fwd(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
     return list(outs)
 
 
-def gspn_forward4_workspace_bytes(x: torch.Tensor) -> int:
-    """Bytes of the optional gspn_forward4 workspace for inputs shaped like x."""
+def gspn_forward4_workspace_bytes(x: torch.Tensor, cw: int) -> int:
+    """Bytes of the optional gspn_forward4 workspace for inputs shaped like x
+    with cw weight channels (1 = channel-shared)."""
     n, c, h, w = x.shape
-    return int(lib().gspn_forward4_workspace_bytes(n, c, h, w, _dtype_code(x)))
+    return int(lib().gspn_forward4_workspace_bytes(n, c, h, w, cw, _dtype_code(x)))
 
 
-def forward4_workspace(x: torch.Tensor) -> torch.Tensor:
+def forward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
     """A workspace buffer (uint8 tensor on x's device) for gspn_forward4."""
-    return torch.empty(gspn_forward4_workspace_bytes(x), dtype=torch.uint8, device=x.device)
+    nbytes = gspn_forward4_workspace_bytes(x, cw)
+    if nbytes < 0:
+        raise ValueError("invalid shape for a gspn_forward4 workspace")
+    return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
 def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
@@ -263,5 +267,5 @@ def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tenso
     """Compressive-proxy forward: C -> C_proxy projection, four-direction scan in
     proxy space, C_proxy -> C projection (three libgspn calls)."""
     xp = gspn_proxy_project(x, w_down)
-    yp = gspn_forward4(xp, logits, lams, chunk_len, workspace=forward4_workspace(xp))
+    yp = gspn_forward4(xp, logits, lams, chunk_len, workspace=forward4_workspace(xp, logits[0].shape[1]))
     return gspn_proxy_project(yp, w_up)

@@ -64,8 +64,8 @@ def test_scan_validation(lib):
     assert scan(lib, chunk=-1) == CHUNK
     assert scan(lib, cw=3) == WCH
     assert scan(lib, c=1, cw=2) == WCH
-    assert scan(lib, w=8193) == UNSUP                    # vertical line longer than the limit
-    assert scan(lib, dir=2, h=8193, w=4) == UNSUP        # horizontal lines run along H
+    assert scan(lib, w=4097) == UNSUP                    # vertical line longer than the limit
+    assert scan(lib, dir=2, h=4097, w=4) == UNSUP        # horizontal lines run along H
     assert scan(lib, x=0) == NULLP
     assert scan(lib, wts=0) == NULLP
     assert scan(lib, lam=0) == NULLP
@@ -90,11 +90,15 @@ def test_forward4_validation(lib):
     zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
     ls = vp4(C_, C_, C_, C_)
     W = 0x60000000
-    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 0)
-    assert wsb == 3 * 2 * 64 * 4
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1) == 3 * 2 * 64 * 2
-    assert lib.gspn_forward4_workspace_bytes(1, -2, 8, 8, 0) == -1
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 5) == -1
+    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 0)
+    assert wsb == 4 * 2 * 64 * 4
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 1) == 4 * 2 * 64 * 2
+    # channel-shared weights add the four directions' fp32 weights
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1) == 4 * 2 * 64 * 2 + 4 * 3 * 64 * 4
+    assert lib.gspn_forward4_workspace_bytes(1, 1, 8, 8, 1, 0) == 4 * 64 * 4
+    assert lib.gspn_forward4_workspace_bytes(1, -2, 8, 8, 2, 0) == -1
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 5) == -1
 
     def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, y=D_, ws=None, wsb=0, dt=0):
         return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, y, ws, wsb, dt, None)
@@ -109,6 +113,7 @@ def test_forward4_validation(lib):
     assert f(l=vp4(C_, C_, C_, C_ + 1)) == MISAL
     assert f(ws=W, wsb=wsb - 1) == WSPACE
     assert f(ws=W + 2, wsb=wsb) == MISAL
+    assert f(dt=1, ws=W + 2, wsb=wsb) == MISAL         # the workspace holds fp32 weights
     assert f(ws=D_ - 100, wsb=wsb) == ALIAS          # workspace overlaps y
     assert f(ws=A + 4, wsb=wsb) == ALIAS             # workspace overlaps x
     assert f(n=0, x=0, z=None, l=None, y=0) == OK

@@ -159,7 +159,7 @@ def test_forward4_small(shape, chunk, dtype, use_ws):
         wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=shared, seed=h * w + chunk)
         _say("forward4 %s chunk=%d %s shared=%s ws=%s" % (shape, chunk, dtype, shared, use_ws))
         inp = make_inputs(wl, DEV)
-        ws = G.forward4_workspace(inp["x"]) if use_ws else None
+        ws = G.forward4_workspace(inp["x"], wl.cw) if use_ws else None
         got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk, workspace=ws)
         torch.cuda.synchronize()
         ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk)
@@ -245,7 +245,7 @@ def test_full_tstage(name):
     _say("full %s" % name)
     inp = make_inputs(wl, DEV)
     got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk,
-                          workspace=G.forward4_workspace(inp["x"]))
+                          workspace=G.forward4_workspace(inp["x"], wl.cw))
     torch.cuda.synchronize()
     ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=wl.chunk)
     assert _err(got, ref) <= TOL[wl.dtype]
@@ -260,7 +260,7 @@ def test_full_size_sampled_planes(name, planes):
     _say("full %s" % name)
     inp = make_inputs(wl, DEV)
     got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk,
-                          workspace=G.forward4_workspace(inp["x"]))
+                          workspace=G.forward4_workspace(inp["x"], wl.cw))
     torch.cuda.synchronize()
     assert torch.isfinite(got).all()
     for n, c in planes:
