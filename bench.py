@@ -94,7 +94,7 @@ def uses_fused_path(wl) -> bool:
 def run_step(wl, inp, out, ws):
     if wl.c_proxy:
         return G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
-                                     chunk_len=wl.chunk)
+                                     chunk_len=wl.chunk, out=out, workspace=ws)
     return G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out,
                            workspace=ws)
 
@@ -195,8 +195,9 @@ def main():
     G.lib()
     print("bench: workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
     inp = make_inputs(wl, "cuda")
-    out = torch.empty_like(inp["x"]) if not wl.c_proxy else None
-    ws = G.forward4_workspace(inp["x"], wl.cw) if not wl.c_proxy else None
+    out = torch.empty_like(inp["x"])
+    ws = (G.proxy_forward4_workspace(inp["x"], wl.c_proxy, wl.cw) if wl.c_proxy
+          else G.forward4_workspace(inp["x"], wl.cw))
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):

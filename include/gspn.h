@@ -193,6 +193,36 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                           const void* const lam[4], void* y, void* workspace,
                           int64_t workspace_bytes, int dtype, void* stream);
 
+/*
+ * gspn_proxy_forward4_workspace_bytes -- bytes of the gspn_proxy_forward4
+ * workspace: the projected input and the merged output in proxy space (2 *
+ * n*c_proxy*h*w elements) plus gspn_forward4_workspace_bytes(n, c_proxy, h,
+ * w, cw).  Returns -1 for invalid arguments.
+ */
+int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
+                                            int64_t cw, int dtype);
+
+/*
+ * gspn_proxy_forward4 -- the compressive-proxy propagation (GSPN-2 notes,
+ * "Optimisation 2"): project C -> C_proxy, run the four-direction
+ * propagation with summed merge in proxy space, project back C_proxy -> C:
+ *   x_p = w_down . x,   y_p = forward4(x_p, logits, lam),   y = w_up . y_p
+ * (1x1 projections, no bias).
+ *   x        [n][c][h][w];  y [n][c][h][w] output (may not overlap any input)
+ *   w_down   [c_proxy][c];  w_up [c][c_proxy]
+ *   logits[d] [n][cw][3][S_d][L_d] (cw = 1 or c_proxy), lam[d] [n][c_proxy][S_d][L_d]
+ *   workspace required: gspn_proxy_forward4_workspace_bytes() bytes, 4-byte
+ *            aligned, overlapping nothing else (else GSPN_ERR_WORKSPACE /
+ *            GSPN_ERR_MISALIGNED / GSPN_ERR_ALIASING; NULL is
+ *            GSPN_ERR_NULL_POINTER).
+ * Intermediates are stored in the storage type (bf16 intermediates round
+ * once at each store).
+ */
+gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                const void* const logits[4], const void* const lam[4], void* y,
+                                void* workspace, int64_t workspace_bytes, int dtype, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);
 

@@ -378,4 +378,59 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                                          static_cast<int>(w), 1, dtype, st));
 }
 
+int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
+                                            int64_t cw, int dtype) {
+    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w}) || c_proxy < 1)
+        return -1;
+    const int64_t f4 = gspn_forward4_workspace_bytes(n, c_proxy, h, w, cw, dtype);
+    if (f4 < 0) return -1;
+    return 2 * checked_product({n, c_proxy, h, w}) * static_cast<int64_t>(elem_size(dtype)) + f4;
+}
+
+gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                const void* const logits[4], const void* const lam[4], void* y,
+                                void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
+    if (!dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w})) return GSPN_ERR_BAD_SHAPE;
+    if (chunk_len < 0) return GSPN_ERR_BAD_CHUNK;
+    if (!(cw == 1 || cw == c_proxy)) return GSPN_ERR_BAD_WEIGHT_CHANNELS;
+    if (checked_product({n, c, h, w}) == 0) return GSPN_OK;
+    if (c_proxy < 1) return GSPN_ERR_BAD_SHAPE;
+    if (h > GSPN_MAX_LINE || w > GSPN_MAX_LINE) return GSPN_ERR_UNSUPPORTED;
+    if (!x || !w_down || !w_up || !y || !logits || !lam || !workspace) return GSPN_ERR_NULL_POINTER;
+    for (int d = 0; d < 4; ++d)
+        if (!logits[d] || !lam[d]) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    if (!aligned(x, es) || !aligned(y, es) || !aligned(w_down, es) || !aligned(w_up, es))
+        return GSPN_ERR_MISALIGNED;
+    const int64_t need = gspn_proxy_forward4_workspace_bytes(n, c, h, w, c_proxy, cw, dtype);
+    if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
+    const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
+    const int64_t pb = n * c_proxy * h * w * static_cast<int64_t>(es);
+    const int64_t wb = n * cw * 3 * h * w * static_cast<int64_t>(es);
+    const int64_t mb = c * c_proxy * static_cast<int64_t>(es);
+    if (overlap(y, xb, x, xb) || overlap(y, xb, w_down, mb) || overlap(y, xb, w_up, mb)) return GSPN_ERR_ALIASING;
+    if (overlap(workspace, need, x, xb) || overlap(workspace, need, y, xb) ||
+        overlap(workspace, need, w_down, mb) || overlap(workspace, need, w_up, mb))
+        return GSPN_ERR_ALIASING;
+    for (int d = 0; d < 4; ++d) {
+        if (!aligned(logits[d], es) || !aligned(lam[d], es)) return GSPN_ERR_MISALIGNED;
+        if (overlap(y, xb, logits[d], wb) || overlap(y, xb, lam[d], pb) ||
+            overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], pb))
+            return GSPN_ERR_ALIASING;
+    }
+    char* ws = static_cast<char*>(workspace);
+    void* xp = ws;
+    void* yp = ws + pb;
+    char* fws = ws + 2 * pb;
+    const hipStream_t st = as_stream(stream);
+    if (gspn::launch_project(n, c, h * w, c_proxy, x, w_down, xp, dtype, st) != hipSuccess) return GSPN_ERR_HIP;
+    const gspn_status s4 = gspn_forward4(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, yp, fws,
+                                         need - 2 * pb, dtype, stream);
+    if (s4 != GSPN_OK) return s4;
+    return from_hip(gspn::launch_project(n, c_proxy, h * w, c, yp, w_up, y, dtype, st));
+}
+
 }  // extern "C"

@@ -2,15 +2,142 @@
 // "Optimisation 2", compressive channel proxy):
 //   out[n][o][p] = sum_c weight[o][c] * in[n][c][p]   (no bias, fp32 accumulate)
 //
-// Generic VALU kernel: one lane per pixel, OB output channels accumulated in
-// registers per pass over the input channels.  The weight index is uniform
-// across the wavefront, so weights come through the scalar cache.
+// bf16 storage runs on the matrix cores (gfx950 bf16 MFMA, fp32 accumulate):
+//  - narrow output (c_out <= 16, e.g. C -> C_proxy): v_mfma_f32_16x16x32_bf16
+//    with M = output channels, N = 16 pixels, K = 32 input channels per
+//    instruction.  A wave covers 64 pixels: each lane loads 4 pixels of 8
+//    input channels with 8-byte loads (16 lanes make one 128-byte run of a
+//    channel row) and feeds four MFMAs, one per pixel of its quad.
+//  - narrow input (c_in <= 8, e.g. C_proxy -> C): v_mfma_f32_32x32x8_bf16
+//    with M = 32 output channels, N = 32 pixels, K = 8.  A wave covers 64
+//    pixels as even / odd halves, so each lane ends with two adjacent pixels
+//    of 16 output channels and stores them as one dword (32 lanes make one
+//    128-byte run of an output row).
+// Operand layouts (checked on gfx950): lane l holds row l % M of A and column
+// l % M of B, with k = (l / M) * KE + e for its KE elements; the 16x16 result
+// holds rows (l/16)*4 + i of column l % 16, the 32x32 result rows
+// (i/4)*8 + (l/32)*4 + i%4 of column l % 32.
+// Everything else (fp32 storage, other channel counts, ragged pixel counts)
+// takes a VALU kernel: one lane per pixel, 8 output channels per pass.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace gspn {
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ __bf16 as_bf(uint32_t bits16) {
+    return __builtin_bit_cast(__bf16, static_cast<uint16_t>(bits16));
+}
+
+// Narrow output: c_out <= 16.  Requires hw % 64 == 0 and 8-byte aligned rows.
+__global__ __launch_bounds__(256) void project_narrow_out_mfma(const bf16_t* __restrict__ in,
+                                                               const bf16_t* __restrict__ wt,
+                                                               bf16_t* __restrict__ out, int64_t waves,
+                                                               int64_t hw, int cin, int cout) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (wave >= waves) return;
+    const int64_t per_img = hw / 64;
+    const int64_t ni = wave / per_img;
+    const int64_t px0 = (wave - ni * per_img) * 64;
+    const int q = lane & 15;  // pixel quad: pixels px0 + 4q .. +3; output row of A
+    const int g = lane >> 4;  // k-group: channels 8g .. 8g+7 of each 32-channel step
+    const bf16_t* src = in + ni * cin * hw + px0 + 4 * q;
+
+    floatx4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int k0 = 0; k0 < cin; k0 += 32) {
+        bf16x8 a;
+        uint2 v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = k0 + 8 * g + e;
+            const bool ok = c < cin;
+            a[e] = as_bf((q < cout && ok) ? wt[q * cin + c] : 0);
+            v[e] = ok ? *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(c) * hw) : make_uint2(0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8 b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t word = (j < 2) ? v[e].x : v[e].y;
+                b[e] = as_bf((j & 1) ? (word >> 16) : (word & 0xffffu));
+            }
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        }
+    }
+    // lane holds output rows (l/16)*4 + i for pixels px0 + 4q + j
+    bf16_t* dst = out + ni * cout * hw + px0 + 4 * q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int o = g * 4 + i;
+        if (o < cout) {
+            uint2 w;
+            w.x = static_cast<uint32_t>(f32_to_bf16(acc[0][i])) | (static_cast<uint32_t>(f32_to_bf16(acc[1][i])) << 16);
+            w.y = static_cast<uint32_t>(f32_to_bf16(acc[2][i])) | (static_cast<uint32_t>(f32_to_bf16(acc[3][i])) << 16);
+            *reinterpret_cast<uint2*>(dst + static_cast<int64_t>(o) * hw) = w;
+        }
+    }
+}
+
+// Narrow input: c_in <= 8.  Requires hw % 64 == 0 and 4-byte aligned rows.
+__global__ __launch_bounds__(256) void project_narrow_in_mfma(const bf16_t* __restrict__ in,
+                                                              const bf16_t* __restrict__ wt,
+                                                              bf16_t* __restrict__ out, int64_t waves,
+                                                              int64_t hw, int cin, int cout) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (wave >= waves) return;
+    const int64_t per_img = hw / 64;
+    const int64_t ni = wave / per_img;
+    const int64_t px0 = (wave - ni * per_img) * 64;
+    const int n = lane & 31;  // pixel pair: pixels px0 + 2n, px0 + 2n + 1; output row of A
+    const int g = lane >> 5;  // k-group: input channels 4g .. 4g+3
+    const bf16_t* src = in + ni * cin * hw + px0 + 2 * n;
+
+    short4v b_even, b_odd;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = 4 * g + e;
+        const uint32_t word = c < cin ? *reinterpret_cast<const uint32_t*>(src + static_cast<int64_t>(c) * hw) : 0u;
+        b_even[e] = static_cast<short>(word & 0xffffu);
+        b_odd[e] = static_cast<short>(word >> 16);
+    }
+    bf16_t* dst = out + ni * cout * hw + px0 + 2 * n;
+    for (int o0 = 0; o0 < cout; o0 += 32) {
+        short4v a;
+        const int orow = o0 + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 4 * g + e;
+            a[e] = static_cast<short>((orow < cout && c < cin) ? wt[orow * cin + c] : 0);
+        }
+        floatx16 ce = {}, co = {};
+        ce = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b_even, ce, 0, 0, 0);
+        co = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b_odd, co, 0, 0, 0);
+        // lane holds output rows (i/4)*8 + (l/32)*4 + i%4 for the pixel pair
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int o = o0 + (i / 4) * 8 + g * 4 + (i % 4);
+            if (o < cout) {
+                const uint32_t word = static_cast<uint32_t>(f32_to_bf16(ce[i])) |
+                                      (static_cast<uint32_t>(f32_to_bf16(co[i])) << 16);
+                *reinterpret_cast<uint32_t*>(dst + static_cast<int64_t>(o) * hw) = word;
+            }
+        }
+    }
+}
+
+// VALU projection: one lane per pixel, OB output channels per pass over the
+// input channels (weights are wave-uniform and come through the scalar cache).
 template <typename T, int OB>
 __global__ __launch_bounds__(256) void project_kernel(const T* __restrict__ in, const T* __restrict__ wt,
                                                       T* __restrict__ out, int64_t n, int64_t cin,
@@ -42,10 +169,30 @@ __global__ __launch_bounds__(256) void project_kernel(const T* __restrict__ in, 
     }
 }
 
+bool aligned_to(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
 }  // namespace
 
 hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const void* in,
                           const void* weight, void* out, int dtype, hipStream_t stream) {
+    if (dtype == kBF16 && hw % 64 == 0 && c_in <= 1 << 20 && c_out <= 1 << 20) {
+        const int64_t waves = n * (hw / 64);
+        const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+        if (c_out <= 16 && aligned_to(in, 8) && aligned_to(out, 8)) {
+            hipLaunchKernelGGL(project_narrow_out_mfma, grid, dim3(256), 0, stream,
+                               static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
+                               static_cast<bf16_t*>(out), waves, hw, static_cast<int>(c_in),
+                               static_cast<int>(c_out));
+            return hipGetLastError();
+        }
+        if (c_in <= 8 && aligned_to(in, 4) && aligned_to(out, 4)) {
+            hipLaunchKernelGGL(project_narrow_in_mfma, grid, dim3(256), 0, stream,
+                               static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
+                               static_cast<bf16_t*>(out), waves, hw, static_cast<int>(c_in),
+                               static_cast<int>(c_out));
+            return hipGetLastError();
+        }
+    }
     const int64_t total = n * hw;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 256 * 32) blocks = 256 * 32;

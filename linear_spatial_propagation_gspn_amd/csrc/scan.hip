@@ -46,7 +46,7 @@ ScanConfig choose_config(bool horiz, int L) {
 // Horizontal tile width in steps (mirrors Blocking<T, P, true>::UT).
 int horiz_tile_width(size_t esz, int P) {
     const int vw = static_cast<int>(16 / esz);
-    const int u = GSPN_SUB_U / P > 1 ? GSPN_SUB_U / P : 1;
+    const int u = P == 1 ? GSPN_SUB_U : (P == 2 ? GSPN_SUB_U2 : 2);
     const int t0 = (16 / P) > vw ? (16 / P) : vw;
     return t0 > u ? t0 : u;
 }

@@ -385,13 +385,25 @@ struct ScanConfig {
 #define GSPN_SUB_U 2
 #endif
 
-// Steps per prefetch sub-block and per tile.  The sub-block shrinks with the
-// positions per lane and horizontal tiles hold 16 steps (64 bytes of fp32 or
-// 32 of bf16 per row) for one position per lane, fewer for more positions, so
-// that the double buffers stay in registers.
+// Steps per prefetch sub-block and per tile.  One position per lane (lines
+// up to 1024) keeps the sub-block short so that two 1024-lane workgroups fit a
+// CU; two positions per lane serve lines up to 2048, which come in small
+// numbers (few workgroups, each on the critical path), so their sub-block is
+// deeper.  Horizontal tiles hold 16 steps (64 bytes of fp32 or 32 of bf16 per
+// row) for one position per lane, fewer for more positions, so that the
+// double buffers stay in registers.
+#ifndef GSPN_SUB_U2
+#define GSPN_SUB_U2 4
+#endif
+
+template <int P>
+constexpr int sub_block_steps() {
+    return P == 1 ? GSPN_SUB_U : (P == 2 ? GSPN_SUB_U2 : 2);
+}
+
 template <typename T, int P, bool HORIZ>
 struct Blocking {
-    static constexpr int U = GSPN_SUB_U / P > 1 ? GSPN_SUB_U / P : 1;
+    static constexpr int U = sub_block_steps<P>();
     static constexpr int VW = 16 / static_cast<int>(sizeof(T));
     static constexpr int T0 = (16 / P) > VW ? (16 / P) : VW;
     static constexpr int UT = HORIZ ? (T0 > U ? T0 : U) : 2 * U;

@@ -35,7 +35,8 @@ STATUS = {
 
 # Symbols declared in include/gspn.h.
 EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy_project",
-           "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4", "gspn_status_string", "gspn_abi_version")
+           "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4",
+           "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_status_string", "gspn_abi_version")
 
 
 class GspnError(RuntimeError):
@@ -68,6 +69,11 @@ def lib() -> ctypes.CDLL:
             h.gspn_scan4_fwd.restype = ci
             h.gspn_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
             h.gspn_forward4_workspace_bytes.restype = i64
+            h.gspn_proxy_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+            h.gspn_proxy_forward4_workspace_bytes.restype = i64
+            h.gspn_proxy_forward4.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp,
+                                              ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, i64, ci, vp]
+            h.gspn_proxy_forward4.restype = ci
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp, vp, i64, ci, vp]
             for name in ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4",
@@ -261,11 +267,43 @@ def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequenc
     return out
 
 
+def proxy_forward4_workspace(x: torch.Tensor, c_proxy: int, cw: int) -> torch.Tensor:
+    """A workspace buffer (uint8 tensor on x's device) for gspn_proxy_forward4."""
+    n, c, h, w = x.shape
+    nbytes = int(lib().gspn_proxy_forward4_workspace_bytes(n, c, h, w, c_proxy, cw, _dtype_code(x)))
+    if nbytes < 0:
+        raise ValueError("invalid shape for a gspn_proxy_forward4 workspace")
+    return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+
+
 def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
                         logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
-                        chunk_len: int = 0) -> torch.Tensor:
-    """Compressive-proxy forward: C -> C_proxy projection, four-direction scan in
-    proxy space, C_proxy -> C projection (three libgspn calls)."""
-    xp = gspn_proxy_project(x, w_down)
-    yp = gspn_forward4(xp, logits, lams, chunk_len, workspace=forward4_workspace(xp, logits[0].shape[1]))
-    return gspn_proxy_project(yp, w_up)
+                        chunk_len: int = 0, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Compressive-proxy forward: C -> C_proxy 1x1 projection, four-direction
+    scan with summed merge in proxy space, C_proxy -> C projection."""
+    n, c, h, w = x.shape
+    dt = x.dtype
+    cp = w_down.shape[0]
+    cw = logits[0].shape[1]
+    _check(x, "x", (n, c, h, w), dt, x.device)
+    _check(w_down, "w_down", (cp, c), dt, x.device)
+    _check(w_up, "w_up", (c, cp), dt, x.device)
+    for d in range(4):
+        S, L = frame_shape(d, h, w)
+        _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
+        _check(lams[d], "lam[%d]" % d, (n, cp, S, L), dt, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (n, c, h, w), dt, x.device)
+    if workspace is None:
+        workspace = proxy_forward4_workspace(x, cp, cw)
+    if workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
+    zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
+    lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
+    _raise(lib().gspn_proxy_forward4(n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up),
+                                     zp, lp, _ptr(out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _dtype_code(x),
+                                     _stream(x.device)), "gspn_proxy_forward4")
+    return out

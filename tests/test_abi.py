@@ -139,6 +139,33 @@ def test_scan4_validation(lib):
     assert f(n=0, x=0, z=None, l=None, o=None) == OK
 
 
+def test_proxy_forward4_validation(lib):
+    vp4 = ctypes.c_void_p * 4
+    zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
+    ls = vp4(C_, C_ + 0x1000000, C_ + 0x2000000, C_ + 0x3000000)
+    WD, WU, WS = 0x70000000, 0x71000000, 0x72000000
+    need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1)
+    assert need == 2 * 2 * 64 * 2 + lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1)
+    assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 0, 1, 1) == -1
+    assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 3, 1) == -1
+
+    def f(n=1, c=6, h=8, w=8, cp=2, cw=1, chunk=0, x=A, wd=WD, wu=WU, z=zs, l=ls, y=D_, ws=WS, wsb=need, dt=1):
+        return lib.gspn_proxy_forward4(n, c, h, w, cp, cw, chunk, x, wd, wu, z, l, y, ws, wsb, dt, None)
+
+    assert f(dt=2) == DTYPE
+    assert f(cp=-1) == SHAPE
+    assert f(chunk=-1) == CHUNK
+    assert f(cw=3) == WCH
+    assert f(h=5000) == UNSUP
+    assert f(ws=0) == NULLP
+    assert f(wd=0) == NULLP
+    assert f(wsb=need - 1) == WSPACE
+    assert f(ws=WS + 2) == MISAL
+    assert f(y=A + 64) == ALIAS
+    assert f(ws=A - 16) == ALIAS
+    assert f(n=0, x=0, wd=0, wu=0, z=None, l=None, y=0, ws=0) == OK
+
+
 def test_normalize_merge_project_validation(lib):
     nw = lib.gspn_normalize_weights
     assert nw(0, 1, 1, 4, 4, A, B, 5, None) == DTYPE

@@ -135,12 +135,13 @@ def test_merge4():
     assert np.max(np.abs(_np(y) - ref)) <= 1e-5
 
 
+@pytest.mark.parametrize("hw", [(13, 29), (16, 32)])   # ragged (VALU) / multiple of 64 pixels (MFMA for bf16)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("cin,cout", [(320, 8), (8, 320), (37, 5), (3, 11)])
-def test_project(cin, cout, dtype):
+@pytest.mark.parametrize("cin,cout", [(320, 8), (8, 320), (37, 5), (3, 11), (40, 16), (64, 17), (5, 33)])
+def test_project(cin, cout, dtype, hw):
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     g = torch.Generator(device=DEV).manual_seed(cin * 1000 + cout)
-    x = torch.randn(2, cin, 13, 29, device=DEV, generator=g).to(tdt)
+    x = torch.randn(2, cin, hw[0], hw[1], device=DEV, generator=g).to(tdt)
     wt = (torch.randn(cout, cin, device=DEV, generator=g) / math.sqrt(cin)).to(tdt)
     _say("project %d->%d %s" % (cin, cout, dtype))
     got = G.gspn_proxy_project(x, wt)
@@ -216,14 +217,18 @@ def test_deterministic():
 # Proxy pipeline, small
 # ----------------------------------------------------------------------------
 
-def test_proxy_forward4_small():
-    wl = _wl(n=1, c=40, h=33, w=47, dtype="bf16", shared=True, seed=13, cp=8)
-    _say("proxy small")
-    inp = make_inputs(wl, DEV)
-    got = G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"])
-    torch.cuda.synchronize()
-    ref = oracle.proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"])
-    assert _err(got, ref) <= 2e-2
+@pytest.mark.parametrize("shape", [(1, 40, 33, 47, 8), (2, 64, 32, 64, 8), (1, 24, 64, 48, 4)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_proxy_forward4_small(shape, dtype):
+    n, c, h, w, cp = shape
+    for shared in (True, False):
+        wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=shared, seed=13 + h, cp=cp)
+        _say("proxy %s %s shared=%s" % (shape, dtype, shared))
+        inp = make_inputs(wl, DEV)
+        got = G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"])
+        torch.cuda.synchronize()
+        ref = oracle.proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"])
+        assert _err(got, ref) <= TOL[dtype]
 
 
 # ----------------------------------------------------------------------------
