@@ -11,17 +11,24 @@ up).  Prints one JSON line.
 Measurements:
   - ms per step: HIP events on the stream the library launches on, bracketing
     the K timed steps (synchronised on both sides).
-  - roofline: the dominant kernel (the line-scan kernel) timed per launch with
-    HIP events in its own loop over the same inputs and launch configuration;
-    achieved = its algorithmic bytes per launch / its average duration.
-  - effective bandwidth of the whole step = algorithmic bytes of the forward
+  - stage times: the same call through its *_timed entry point, which records
+    HIP events on that stream around every launch of the step.  The dominant
+    kernel is the line scan; its per-launch duration is the scan stage's time
+    divided by its launch count.
+  - roofline.achieved: the scan launch's algorithmic bytes (each tensor the
+    launch reads or writes, moved once) / its per-launch duration.
+  - roofline.traffic: HBM bytes per scan launch measured with the FETCH_SIZE
+    and WRITE_SIZE counters, read from the committed counter summary under
+    profiles/ when it was taken on the current kernel sources, else null.
+  - effective bandwidth of the whole step: algorithmic bytes of the forward
     (every distinct input read once, y written once) / ms per step.
   - cpu_baseline: the fp64 oracle on a bounded sample of the same workload,
-    on the host's cores (rank 0, N = 1 only).
+    on the host's cores (N = 1 only).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,127 +45,196 @@ from linear_spatial_propagation_gspn_amd.workloads import WORKLOADS, make_inputs
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "ms per 4-direction GSPN forward at 1024², B=16, C=8; achieved HBM GB/s"
+CSRC = os.path.join(ROOT, "linear_spatial_propagation_gspn_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def esize(wl) -> int:
     return 4 if wl.dtype == "f32" else 2
 
 
+def unit_bytes(wl) -> int:
+    """U: one map of the scanned tensor (n * c_scan * h * w elements)."""
+    return wl.n * wl.c_scan * wl.h * wl.w * esize(wl)
+
+
+def prenormalised(wl) -> bool:
+    """Channel-shared logits over several channels are normalised once into
+    fp32 weights that the scans read."""
+    return wl.cw == 1 and wl.c_scan > 1
+
+
+def weight_bytes_per_direction(wl) -> int:
+    """Bytes of one direction's weights as the scan reads them."""
+    if prenormalised(wl):
+        return wl.n * 3 * wl.h * wl.w * 4
+    return wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
+
+
 def algorithmic_bytes(wl) -> int:
-    """Every distinct input read once and y written once."""
+    """Every distinct input of the step read once and y written once."""
     es = esize(wl)
     hw = wl.h * wl.w
-    if wl.c_proxy:
-        x = wl.n * wl.c * hw * es
-        y = x
-        lam = 4 * wl.n * wl.c_proxy * hw * es
-        z = 4 * wl.n * wl.cw * 3 * hw * es
-        wts = 2 * wl.c * wl.c_proxy * es
-        return x + y + lam + z + wts
-    u = wl.n * wl.c * hw * es
+    x = wl.n * wl.c * hw * es
+    lam = 4 * wl.n * wl.c_scan * hw * es
     z = 4 * wl.n * wl.cw * 3 * hw * es
-    return u + 4 * u + z + u
+    wts = 2 * wl.c * wl.c_proxy * es if wl.c_proxy else 0
+    return x + lam + z + wts + x
 
 
-def scan_launch_bytes(wl, accumulate: bool) -> int:
-    """Compulsory bytes of one direction's scan launch: x, its logits and
-    lambda read once, the output written once (and read once when the launch
-    accumulates into it)."""
-    es = esize(wl)
-    c = wl.c_scan
-    u = wl.n * c * wl.h * wl.w * es
-    z = wl.n * wl.cw * 3 * wl.h * wl.w * es
-    return u + z + u + u + (u if accumulate else 0)
+def scan_launch_bytes(wl, launches: int) -> int:
+    """Algorithmic bytes of one scan launch: every tensor the launch reads or
+    writes, moved once.
+      fused (1 launch): x and its transpose, four directions' weights and
+        lambdas, four output maps written;
+      one launch per direction: x (or its transpose), the direction's weights
+        and lambda, the output written, and read as well by the two launches
+        that add into a map (average over the four launches)."""
+    u = unit_bytes(wl)
+    wd = weight_bytes_per_direction(wl)
+    if launches == 1:
+        return 2 * u + 4 * wd + 4 * u + 4 * u
+    total = 4 * u + 4 * wd + 4 * u + 4 * u + 2 * u
+    return total // 4
 
 
-def scan4_launch_bytes(wl) -> int:
-    """Compulsory bytes of one four-direction launch: x once, the four
-    directions' logits and lambda once, four output maps written once."""
-    es = esize(wl)
-    u = wl.n * wl.c_scan * wl.h * wl.w * es
-    z = wl.n * wl.cw * 3 * wl.h * wl.w * es
-    return u + 4 * z + 4 * u + 4 * u
-
-
-# Mirror of the library's rule (api.cpp): with a workspace, gspn_forward4 runs
-# the four directions in one launch when one direction has fewer than 512
-# (plane, chunk) lines and no line exceeds 2048 positions.
-def uses_fused_path(wl) -> bool:
-    most = 0
-    for S in (wl.h, wl.w):
-        k = S if wl.chunk in (0,) or wl.chunk >= S else wl.chunk
-        most = max(most, wl.n * wl.c_scan * ((S + k - 1) // k))
-    return most < 512 and max(wl.h, wl.w) <= 2048
-
-
-def run_step(wl, inp, out, ws):
+def run_step(wl, inp, out, ws, timed=False):
     if wl.c_proxy:
-        return G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
-                                     chunk_len=wl.chunk, out=out, workspace=ws)
-    return G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out,
-                           workspace=ws)
+        f = G.gspn_proxy_forward4_timed if timed else G.gspn_proxy_forward4
+        return f(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
+                 chunk_len=wl.chunk, out=out, workspace=ws)
+    f = G.gspn_forward4_timed if timed else G.gspn_forward4
+    return f(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out, workspace=ws)
 
 
-def _time(fn, reps: int) -> float:
-    """Average ms of fn() over reps launches, HIP events on the current stream."""
-    stream = torch.cuda.current_stream()
-    fn()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / reps
+def stage_times(wl, inp, out, ws, reps: int) -> dict:
+    """Mean per-step duration and launch count of each stage over reps timed
+    steps."""
+    acc = {name: {"ms": 0.0, "launches": 0} for name in G.STAGES}
+    for _ in range(reps):
+        _, t = run_step(wl, inp, out, ws, timed=True)
+        for name, v in t.items():
+            acc[name]["ms"] += v["ms"] / reps
+            acc[name]["launches"] = v["launches"]
+    return acc
 
 
-def time_dominant_kernel(wl, inp, reps: int) -> dict:
-    """Per-launch duration of the scan kernel in the configuration the step uses."""
-    x = G.gspn_proxy_project(inp["x"], inp["w_down"]) if wl.c_proxy else inp["x"]
-    if uses_fused_path(wl):
-        outs = [torch.empty_like(x) for _ in range(4)]
-        ms = _time(lambda: G.gspn_scan4_fwd(x, inp["logits"], inp["lam"], wl.chunk, outs), reps)
-        return {"kernel": "scan4_kernel", "kernel_ms": ms, "bytes_per_launch": scan4_launch_bytes(wl)}
-    out = torch.empty_like(x)
-    per_dir, total_bytes = [], 0
-    for d in range(4):
-        acc = d > 0
-        ms = _time(lambda: G.gspn_scan_fwd(d, x, inp["logits"][d], inp["lam"][d], wl.chunk, out=out,
-                                           accumulate=acc), reps)
-        per_dir.append(ms)
-        total_bytes += scan_launch_bytes(wl, acc)
-    return {"kernel": "scan_kernel", "kernel_ms": sum(per_dir) / 4, "bytes_per_launch": total_bytes // 4,
-            "per_direction_ms": [round(m, 4) for m in per_dir]}
+def kernel_sources_digest() -> str:
+    """sha256 over the library's kernel and launch sources (sorted by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
-def cpu_baseline(wl, inp):
-    """The fp64 oracle on a bounded sample of the workload (whole planes),
-    scaled to ms per full forward."""
-    import oracle
-    nthreads = os.cpu_count() or 1
+def counter_traffic(kernel: str, wl) -> tuple:
+    """(bytes per launch, file) from profiles/<kernel>_<workload>_traffic.txt
+    when that summary was taken on the current sources; (None, reason) else."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (kernel, wl.name))
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_sources_digest():
+        return None, "kernel sources changed since the counters were taken"
+    try:
+        return int(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    except (KeyError, ValueError):
+        return None, "malformed counter summary"
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample
+# ----------------------------------------------------------------------------
+
+CPU_TARGET_S = 10.0          # repeat the sample until this much oracle time
+CPU_MAX_REPEATS = 50
+CPU_MEM_BYTES = 8 << 30      # host memory the fp64 sample may take
+
+
+def _np64(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def cpu_baseline_planes(wl, inp, oracle) -> dict:
+    """Whole (n, c) planes through the oracle's four-direction forward, each
+    plane run as its own image; repeated until CPU_TARGET_S, extrapolated to
+    the workload's n * c planes."""
     planes = wl.n * wl.c
-    if wl.c_proxy:
-        # sample: the proxy-space four-direction scan (all proxy planes) plus
-        # the two projections restricted to a pixel band
-        return None
-    budget_planes = max(1, min(planes, 16 if wl.h * wl.w >= 1 << 20 else 512))
-    idx = [(p // wl.c, p % wl.c) for p in range(budget_planes)]
-    xs = torch.stack([inp["x"][n, c] for n, c in idx])[:, None].float().cpu()
+    per_plane = (6 + (0 if wl.shared_w else 12)) * wl.h * wl.w * 8
+    sample = max(1, min(planes, CPU_MEM_BYTES // per_plane))
+    if sample >= 16:
+        sample -= sample % 16
+    step = max(1, planes // sample)
+    idx = [((p * step) // wl.c, (p * step) % wl.c) for p in range(sample)]
+    nn = torch.tensor([n for n, _ in idx], device=inp["x"].device)
+    cc = torch.tensor([c for _, c in idx], device=inp["x"].device)
+    xs = _np64(inp["x"][nn, cc][:, None])
     zs, ls = [], []
     for d in range(4):
-        zs.append(torch.stack([inp["logits"][d][n, 0 if wl.shared_w else c] for n, c in idx])[:, None]
-                  .float().cpu())
-        ls.append(torch.stack([inp["lam"][d][n, c] for n, c in idx])[:, None].float().cpu())
+        zs.append(_np64(inp["logits"][d][nn, torch.zeros_like(cc) if wl.shared_w else cc][:, None]))
+        ls.append(_np64(inp["lam"][d][nn, cc][:, None]))
+    reps, spent = 0, 0.0
+    while reps < CPU_MAX_REPEATS and (reps == 0 or spent < CPU_TARGET_S):
+        t = time.perf_counter()
+        oracle.forward4(xs, zs, ls, chunk=wl.chunk)
+        spent += time.perf_counter() - t
+        reps += 1
+    per_call = spent / reps
+    return {"value": round(per_call * 1e3 * planes / sample, 3), "unit": "ms per forward (extrapolated)",
+            "cores": min(oracle.max_threads(), sample), "kind": "oracle",
+            "sample": "%d of %d planes (%dx%d, every %d-th), all 4 directions, fp64; %d runs, %.1f s of "
+                      "oracle time" % (sample, planes, wl.h, wl.w, step, reps, spent)}
+
+
+def cpu_baseline_proxy(wl, inp, oracle) -> dict:
+    """The whole proxy pipeline once: the down projection over bands of rows,
+    the four-direction forward on all proxy planes, the up projection over
+    bands of rows (band conversions to fp64 are outside the timed parts)."""
+    import numpy as np
+    band = 128
+    n, c, h, w, cp = wl.n, wl.c, wl.h, wl.w, wl.c_proxy
+    wd = _np64(inp["w_down"])
+    wu = _np64(inp["w_up"])
+    xp = np.empty((n, cp, h, w))
+    t_down = t_scan = t_up = 0.0
+    for r0 in range(0, h, band):
+        xb = np.ascontiguousarray(_np64(inp["x"][:, :, r0:r0 + band]))
+        t = time.perf_counter()
+        xp[:, :, r0:r0 + band] = oracle.project(xb, wd)
+        t_down += time.perf_counter() - t
+        del xb
+    zs = [_np64(z) for z in inp["logits"]]
+    ls = [_np64(l) for l in inp["lam"]]
     t = time.perf_counter()
-    oracle.forward4(xs, zs, ls, chunk=wl.chunk)
-    dt = time.perf_counter() - t
-    ms_full = dt * 1e3 * planes / budget_planes
-    return {"value": round(ms_full, 3), "unit": "ms per forward (extrapolated)", "cores": nthreads,
+    yp = oracle.forward4(xp, zs, ls, chunk=wl.chunk)
+    t_scan = time.perf_counter() - t
+    del xp, zs, ls
+    for r0 in range(0, h, band):
+        yb = np.ascontiguousarray(yp[:, :, r0:r0 + band])
+        t = time.perf_counter()
+        oracle.project(yb, wu)
+        t_up += time.perf_counter() - t
+    total = t_down + t_scan + t_up
+    return {"value": round(total * 1e3, 3), "unit": "ms per forward", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": "%d of %d planes (%dx%d), all 4 directions, fp64, %.2f s measured"
-                      % (budget_planes, planes, wl.h, wl.w, dt)}
+            "sample": "the whole workload once, fp64: projection down %.2f s and up %.2f s over %d-row bands "
+                      "(all threads), four-direction scan of the %d proxy planes %.2f s (%d threads busy)"
+                      % (t_down, t_up, band, cp, t_scan, min(oracle.max_threads(), n * cp))}
+
+
+def cpu_baseline(wl, inp) -> dict:
+    import oracle
+    if wl.c_proxy:
+        return cpu_baseline_proxy(wl, inp, oracle)
+    return cpu_baseline_planes(wl, inp, oracle)
 
 
 def copy_check(mib: int) -> None:
@@ -167,7 +243,16 @@ def copy_check(mib: int) -> None:
     n = mib * (1 << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    ms = _time(lambda: b.copy_(a), 10)
+    stream = torch.cuda.current_stream()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(10):
+        b.copy_(a)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 10
     print(json.dumps({"copy_MiB": mib, "ms": round(ms, 4),
                       "GBps_read_plus_write": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}))
 
@@ -183,8 +268,8 @@ def main():
                     help="only run a device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the four-direction scan has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_check:
@@ -219,10 +304,18 @@ def main():
     print("bench: %.3f ms/step (wall %.3f ms/step)" % (ms, wall * 1e3 / args.steps),
           file=sys.stderr, flush=True)
 
-    dom = time_dominant_kernel(wl, inp, reps=max(3, min(args.steps, 10)))
-    achieved = dom["bytes_per_launch"] / (dom["kernel_ms"] * 1e-3) / 1e9
+    st = stage_times(wl, inp, out, ws, reps=max(3, min(args.steps, 10)))
+    scan = st["scan"]
+    launches = scan["launches"]
+    kernel_ms = scan["ms"] / launches
+    kernel = "scan4v_kernel" if launches == 1 else "scan_kernel"
+    bpl = scan_launch_bytes(wl, launches)
+    achieved = bpl / (kernel_ms * 1e-3) / 1e9
+    traffic, traffic_src = counter_traffic(kernel, wl)
     alg = algorithmic_bytes(wl)
     eff = alg / (ms * 1e-3) / 1e9
+    print("bench: %s %.4f ms per launch (%d per step), %.1f GB/s algorithmic"
+          % (kernel, kernel_ms, launches, achieved), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -248,9 +341,11 @@ def main():
         "effective_GBps": round(eff, 1),
         "effective_frac": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": alg,
-        "roofline": dict({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
-                         **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in dom.items()}),
+        "stages_ms": {k: round(v["ms"], 4) for k, v in st.items() if v["launches"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": kernel, "kernel_ms": round(kernel_ms, 4), "launches_per_step": launches,
+                     "bytes_per_launch": bpl, "traffic_source": traffic_src},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

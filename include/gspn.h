@@ -39,8 +39,9 @@
  *    GSPN_BF16.  Arithmetic is always fp32 (bf16 values are widened exactly;
  *    bf16 results are rounded to nearest even at each store).
  *  - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
- *    call is asynchronous on that stream; the library never synchronises,
- *    never allocates or frees memory, and keeps no mutable global state.
+ *    call is asynchronous on that stream; the library never allocates or
+ *    frees memory, keeps no mutable global state, and never synchronises
+ *    (except the *_timed measurement calls, which wait for their own events).
  *  - Ownership: the caller owns every buffer and must keep it alive until the
  *    work queued on `stream` has finished.
  *  - Errors: arguments are validated on the host before anything is queued.
@@ -66,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 1
+#define GSPN_ABI_VERSION 2
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -222,6 +223,49 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                 const void* const logits[4], const void* const lam[4], void* y,
                                 void* workspace, int64_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * Stage timing of one forward call (measurement only).
+ *
+ * gspn_forward4_timed / gspn_proxy_forward4_timed take the arguments of
+ * gspn_forward4 / gspn_proxy_forward4, validate them identically and launch
+ * exactly the same kernels in the same order on the same stream, with a pair
+ * of HIP timing events recorded on that stream around every launch.  Before
+ * returning they wait for the last event (the only calls in the library that
+ * block the host) and fill *times: per stage, the summed duration in
+ * milliseconds of its launches and the number of launches.  The events are
+ * created and destroyed inside the call; no device memory is allocated.
+ * Stages that did not run read 0 ms / 0 launches.  times == NULL is
+ * GSPN_ERR_NULL_POINTER.  If a launch fails the call still waits for what
+ * was queued, then returns GSPN_ERR_HIP.
+ */
+typedef enum {
+    GSPN_STAGE_PROJECT_DOWN = 0, /* 1x1 projection C -> C_proxy */
+    GSPN_STAGE_NORMALIZE = 1,    /* channel-shared logits -> fp32 weights */
+    GSPN_STAGE_TRANSPOSE = 2,    /* x into the horizontal scan frame */
+    GSPN_STAGE_SCAN = 3,         /* the line-scan launches (1 fused or 4) */
+    GSPN_STAGE_COMBINE = 4,      /* transposing merge of the partial maps into y */
+    GSPN_STAGE_PROJECT_UP = 5,   /* 1x1 projection C_proxy -> C */
+    GSPN_NUM_STAGES = 6
+} gspn_stage;
+
+typedef struct {
+    float ms[GSPN_NUM_STAGES];
+    int32_t launches[GSPN_NUM_STAGES];
+} gspn_stage_times;
+
+gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                                int64_t chunk_len, const void* x, const void* const logits[4],
+                                const void* const lam[4], void* y, void* workspace,
+                                int64_t workspace_bytes, int dtype, void* stream,
+                                gspn_stage_times* times);
+
+gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
+                                      int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
+                                      const void* w_up, const void* const logits[4],
+                                      const void* const lam[4], void* y, void* workspace,
+                                      int64_t workspace_bytes, int dtype, void* stream,
+                                      gspn_stage_times* times);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);

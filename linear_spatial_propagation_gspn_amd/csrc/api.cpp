@@ -58,6 +58,69 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 gspn_status from_hip(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR_HIP; }
 
+// Optional event timing of the launches of one forward call: a pair of HIP
+// events around each launch, read back by finish().
+struct Timer {
+    static constexpr int kMax = 16;
+    hipStream_t st = nullptr;
+    int count = 0;
+    int stage[kMax] = {};
+    hipEvent_t a[kMax] = {};
+    hipEvent_t b[kMax] = {};
+    hipError_t err = hipSuccess;
+
+    ~Timer() {
+        for (int i = 0; i < count; ++i) {
+            (void)hipEventDestroy(a[i]);
+            (void)hipEventDestroy(b[i]);
+        }
+    }
+    // Records the opening event of a launch of stage s.
+    hipError_t open(int s) {
+        if (count >= kMax) return hipErrorInvalidValue;
+        hipError_t e = hipEventCreate(&a[count]);
+        if (e != hipSuccess) return e;
+        e = hipEventCreate(&b[count]);
+        if (e != hipSuccess) {
+            (void)hipEventDestroy(a[count]);
+            return e;
+        }
+        stage[count] = s;
+        ++count;
+        return hipEventRecord(a[count - 1], st);
+    }
+    hipError_t close() { return hipEventRecord(b[count - 1], st); }
+    // Waits for the last event and sums the durations per stage.
+    hipError_t finish(gspn_stage_times* t) {
+        for (int s = 0; s < GSPN_NUM_STAGES; ++s) {
+            t->ms[s] = 0.0f;
+            t->launches[s] = 0;
+        }
+        if (count == 0) return hipSuccess;
+        hipError_t e = hipEventSynchronize(b[count - 1]);
+        if (e != hipSuccess) return e;
+        for (int i = 0; i < count; ++i) {
+            float ms = 0.0f;
+            e = hipEventElapsedTime(&ms, a[i], b[i]);
+            if (e != hipSuccess) return e;
+            t->ms[stage[i]] += ms;
+            t->launches[stage[i]] += 1;
+        }
+        return hipSuccess;
+    }
+};
+
+// Runs one launch, bracketed by timing events when a timer is given.
+template <typename F>
+hipError_t timed(Timer* t, int stage, F&& launch) {
+    if (!t) return launch();
+    hipError_t e = t->open(stage);
+    if (e != hipSuccess) return e;
+    const hipError_t el = launch();
+    e = t->close();
+    return el != hipSuccess ? el : e;
+}
+
 struct ScanCheck {
     gspn_status st;
     int64_t chunk;  // clamped to [1, S]
@@ -252,10 +315,13 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
     return maps + weights;
 }
 
-gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
-                          int64_t chunk_len, const void* x, const void* const logits[4],
-                          const void* const lam[4], void* y, void* workspace,
-                          int64_t workspace_bytes, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
+                          const void* x, const void* const logits[4], const void* const lam[4], void* y,
+                          void* workspace, int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -311,7 +377,8 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         // others add to it; horizontal lines use per-lane row tiles.
         for (int d = 0; d < 4; ++d) {
             p[d].accumulate = d > 0 ? 1 : 0;
-            if (gspn::launch_scan(p[d], st) != hipSuccess) return GSPN_ERR_HIP;
+            if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan(p[d], st); }) != hipSuccess)
+                return GSPN_ERR_HIP;
         }
         return GSPN_OK;
     }
@@ -331,7 +398,9 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         // channels, kept in fp32 so the scans run without transcendentals.
         for (int d = 0; d < 4; ++d) {
             float* wd = reinterpret_cast<float*>(ws) + d * wdir;
-            if (gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32) != hipSuccess)
+            if (timed(tm, GSPN_STAGE_NORMALIZE,
+                      [&] { return gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32); }) !=
+                hipSuccess)
                 return GSPN_ERR_HIP;
             p[d].wts = wd;
             p[d].wts_are_logits = 0;
@@ -340,8 +409,9 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     }
     // The horizontal directions become vertical-form scans of x transposed
     // (their scan frame): line k of step i is x[.., k, i].
-    if (gspn::launch_transpose(x, xt, n * c, static_cast<int>(h), static_cast<int>(w), dtype, st) !=
-        hipSuccess)
+    if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] {
+            return gspn::launch_transpose(x, xt, n * c, static_cast<int>(h), static_cast<int>(w), dtype, st);
+        }) != hipSuccess)
         return GSPN_ERR_HIP;
     for (int d = 2; d < 4; ++d) {
         p[d].x = xt;
@@ -362,9 +432,12 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[1].out = m1;
         p[2].out = m2;
         p[3].out = m3;
-        if (gspn::launch_scan4v(p, st) != hipSuccess) return GSPN_ERR_HIP;
-        return from_hip(gspn::launch_combine(y, m1, m2, m3, n * c, static_cast<int>(h), static_cast<int>(w),
-                                             1, dtype, st));
+        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
+            return gspn::launch_combine(y, m1, m2, m3, n * c, static_cast<int>(h), static_cast<int>(w), 1, dtype,
+                                        st);
+        }));
     }
     // Sequential path: T2B writes y, B2T adds to it; L2R writes the
     // transposed map, R2L adds to it; a transposing merge adds that into y.
@@ -373,24 +446,18 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     p[3].out = m1;
     p[3].accumulate = 1;
     for (int d = 0; d < 4; ++d)
-        if (gspn::launch_scan(p[d], st) != hipSuccess) return GSPN_ERR_HIP;
-    return from_hip(gspn::launch_combine(y, nullptr, m1, nullptr, n * c, static_cast<int>(h),
-                                         static_cast<int>(w), 1, dtype, st));
+        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan(p[d], st); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+    return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
+        return gspn::launch_combine(y, nullptr, m1, nullptr, n * c, static_cast<int>(h), static_cast<int>(w), 1,
+                                    dtype, st);
+    }));
 }
 
-int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
-                                            int64_t cw, int dtype) {
-    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w}) || c_proxy < 1)
-        return -1;
-    const int64_t f4 = gspn_forward4_workspace_bytes(n, c_proxy, h, w, cw, dtype);
-    if (f4 < 0) return -1;
-    return 2 * checked_product({n, c_proxy, h, w}) * static_cast<int64_t>(elem_size(dtype)) + f4;
-}
-
-gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
-                                int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
-                                const void* const logits[4], const void* const lam[4], void* y,
-                                void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
+gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw, int64_t chunk_len,
+                       const void* x, const void* w_down, const void* w_up, const void* const logits[4],
+                       const void* const lam[4], void* y, void* workspace, int64_t workspace_bytes, int dtype,
+                       void* stream, Timer* tm) {
     if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
     if (!dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w})) return GSPN_ERR_BAD_SHAPE;
     if (chunk_len < 0) return GSPN_ERR_BAD_CHUNK;
@@ -426,11 +493,72 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
     void* yp = ws + pb;
     char* fws = ws + 2 * pb;
     const hipStream_t st = as_stream(stream);
-    if (gspn::launch_project(n, c, h * w, c_proxy, x, w_down, xp, dtype, st) != hipSuccess) return GSPN_ERR_HIP;
-    const gspn_status s4 = gspn_forward4(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, yp, fws,
-                                         need - 2 * pb, dtype, stream);
+    if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
+              [&] { return gspn::launch_project(n, c, h * w, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, yp, fws,
+                                         need - 2 * pb, dtype, stream, tm);
     if (s4 != GSPN_OK) return s4;
-    return from_hip(gspn::launch_project(n, c_proxy, h * w, c, yp, w_up, y, dtype, st));
+    return from_hip(timed(tm, GSPN_STAGE_PROJECT_UP,
+                          [&] { return gspn::launch_project(n, c_proxy, h * w, c, yp, w_up, y, dtype, st); }));
+}
+
+}  // namespace
+
+extern "C" {
+
+gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                          int64_t chunk_len, const void* x, const void* const logits[4],
+                          const void* const lam[4], void* y, void* workspace,
+                          int64_t workspace_bytes, int dtype, void* stream) {
+    return forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, y, workspace, workspace_bytes, dtype, stream,
+                         nullptr);
+}
+
+gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                                int64_t chunk_len, const void* x, const void* const logits[4],
+                                const void* const lam[4], void* y, void* workspace,
+                                int64_t workspace_bytes, int dtype, void* stream,
+                                gspn_stage_times* times) {
+    if (!times) return GSPN_ERR_NULL_POINTER;
+    Timer tm;
+    tm.st = as_stream(stream);
+    const gspn_status s = forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, y, workspace,
+                                        workspace_bytes, dtype, stream, &tm);
+    const hipError_t e = tm.finish(times);
+    return s != GSPN_OK ? s : from_hip(e);
+}
+
+int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
+                                            int64_t cw, int dtype) {
+    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w}) || c_proxy < 1)
+        return -1;
+    const int64_t f4 = gspn_forward4_workspace_bytes(n, c_proxy, h, w, cw, dtype);
+    if (f4 < 0) return -1;
+    return 2 * checked_product({n, c_proxy, h, w}) * static_cast<int64_t>(elem_size(dtype)) + f4;
+}
+
+gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                const void* const logits[4], const void* const lam[4], void* y,
+                                void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
+    return proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, y, workspace,
+                      workspace_bytes, dtype, stream, nullptr);
+}
+
+gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
+                                      int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
+                                      const void* w_up, const void* const logits[4],
+                                      const void* const lam[4], void* y, void* workspace,
+                                      int64_t workspace_bytes, int dtype, void* stream,
+                                      gspn_stage_times* times) {
+    if (!times) return GSPN_ERR_NULL_POINTER;
+    Timer tm;
+    tm.st = as_stream(stream);
+    const gspn_status s = proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, y,
+                                     workspace, workspace_bytes, dtype, stream, &tm);
+    const hipError_t e = tm.finish(times);
+    return s != GSPN_OK ? s : from_hip(e);
 }
 
 }  // extern "C"

@@ -36,7 +36,19 @@ STATUS = {
 # Symbols declared in include/gspn.h.
 EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy_project",
            "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4",
-           "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_status_string", "gspn_abi_version")
+           "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_forward4_timed",
+           "gspn_proxy_forward4_timed", "gspn_status_string", "gspn_abi_version")
+
+# gspn_stage, in order.
+STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up")
+
+
+class StageTimes(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_float * len(STAGES)), ("launches", ctypes.c_int32 * len(STAGES))]
+
+    def as_dict(self) -> dict:
+        return {name: {"ms": float(self.ms[i]), "launches": int(self.launches[i])}
+                for i, name in enumerate(STAGES)}
 
 
 class GspnError(RuntimeError):
@@ -76,6 +88,10 @@ def lib() -> ctypes.CDLL:
             h.gspn_proxy_forward4.restype = ci
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp, vp, i64, ci, vp]
+            h.gspn_forward4_timed.argtypes = h.gspn_forward4.argtypes + [ctypes.POINTER(StageTimes)]
+            h.gspn_forward4_timed.restype = ci
+            h.gspn_proxy_forward4_timed.argtypes = h.gspn_proxy_forward4.argtypes + [ctypes.POINTER(StageTimes)]
+            h.gspn_proxy_forward4_timed.restype = ci
             for name in ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4",
                          "gspn_proxy_project", "gspn_forward4"):
                 getattr(h, name).restype = ci
@@ -238,12 +254,7 @@ def forward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
-def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
-                  chunk_len: int = 0, out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Four-direction propagation with summed merge; logits[d] / lams[d] in
-    direction d's scan frame.  ``workspace`` (see forward4_workspace) lets the
-    library run the four directions concurrently when that pays."""
+def _forward4(x, logits, lams, chunk_len, out, workspace, times):
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
@@ -262,9 +273,32 @@ def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequenc
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
-    _raise(lib().gspn_forward4(n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, _ptr(out), ws_ptr,
-                               ws_bytes, _dtype_code(x), _stream(x.device)), "gspn_forward4")
+    args = (n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, _ptr(out), ws_ptr, ws_bytes, _dtype_code(x),
+            _stream(x.device))
+    if times is None:
+        _raise(lib().gspn_forward4(*args), "gspn_forward4")
+    else:
+        _raise(lib().gspn_forward4_timed(*args, ctypes.byref(times)), "gspn_forward4_timed")
     return out
+
+
+def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                  chunk_len: int = 0, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Four-direction propagation with summed merge; logits[d] / lams[d] in
+    direction d's scan frame.  ``workspace`` (see forward4_workspace) lets the
+    library run the four directions concurrently when that pays."""
+    return _forward4(x, logits, lams, chunk_len, out, workspace, None)
+
+
+def gspn_forward4_timed(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                        chunk_len: int = 0, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+    """gspn_forward4 with HIP events around every launch; returns (out,
+    {stage: {"ms", "launches"}}).  Waits for the stream to reach its end."""
+    times = StageTimes()
+    out = _forward4(x, logits, lams, chunk_len, out, workspace, times)
+    return out, times.as_dict()
 
 
 def proxy_forward4_workspace(x: torch.Tensor, c_proxy: int, cw: int) -> torch.Tensor:
@@ -276,12 +310,7 @@ def proxy_forward4_workspace(x: torch.Tensor, c_proxy: int, cw: int) -> torch.Te
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
-def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
-                        logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
-                        chunk_len: int = 0, out: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Compressive-proxy forward: C -> C_proxy 1x1 projection, four-direction
-    scan with summed merge in proxy space, C_proxy -> C projection."""
+def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times):
     n, c, h, w = x.shape
     dt = x.dtype
     cp = w_down.shape[0]
@@ -302,8 +331,30 @@ def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tenso
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
-    _raise(lib().gspn_proxy_forward4(n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up),
-                                     zp, lp, _ptr(out), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), _dtype_code(x),
-                                     _stream(x.device)), "gspn_proxy_forward4")
+    args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up), zp, lp, _ptr(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x), _stream(x.device))
+    if times is None:
+        _raise(lib().gspn_proxy_forward4(*args), "gspn_proxy_forward4")
+    else:
+        _raise(lib().gspn_proxy_forward4_timed(*args, ctypes.byref(times)), "gspn_proxy_forward4_timed")
     return out
+
+
+def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
+                        logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                        chunk_len: int = 0, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Compressive-proxy forward: C -> C_proxy 1x1 projection, four-direction
+    scan with summed merge in proxy space, C_proxy -> C projection."""
+    return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None)
+
+
+def gspn_proxy_forward4_timed(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
+                              logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                              chunk_len: int = 0, out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+    """gspn_proxy_forward4 with HIP events around every launch; returns (out,
+    {stage: {"ms", "launches"}})."""
+    times = StageTimes()
+    out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times)
+    return out, times.as_dict()

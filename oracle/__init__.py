@@ -73,6 +73,8 @@ def _lib():
             for f in (lib.oracle_normalize, lib.oracle_scan, lib.oracle_forward4,
                       lib.oracle_project):
                 f.restype = ctypes.c_int
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = ctypes.c_int
             _handle = lib
         return _handle
 
@@ -185,6 +187,12 @@ def proxy_forward4(x, w_down, w_up, logits: Sequence, lams: Sequence, chunk: int
     xp = project(x, w_down)
     yp = forward4(xp, logits, lams, chunk)
     return project(yp, w_up)
+
+
+def max_threads() -> int:
+    """Threads the oracle's OpenMP loops may use (OMP_NUM_THREADS, else all
+    cores)."""
+    return int(_lib().oracle_max_threads())
 
 
 def normwise_error(got, ref) -> float:

@@ -50,6 +50,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <omp.h>
+
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
 
@@ -255,3 +257,6 @@ int oracle_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const dou
 }
 
 int oracle_abi_version(void) { return 1; }
+
+/* Threads an OpenMP parallel region of this library may use. */
+int oracle_max_threads(void) { return omp_get_max_threads(); }

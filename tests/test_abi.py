@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 1
+    assert lib.gspn_abi_version() == 2
     for code in range(12):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -203,3 +203,34 @@ def test_binding_rejects_mismatched_tensors():
         G.gspn_scan_fwd(0, x, torch.zeros(1, 2, 3, 4, 4), torch.zeros(1, 2, 4, 4))
     with pytest.raises(TypeError):
         G.gspn_merge4([x.double()] * 4)
+
+
+def test_timed_variants_validate_like_untimed(lib):
+    vp4 = ctypes.c_void_p * 4
+    zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
+    ls = vp4(C_, C_, C_, C_)
+    t = G.StageTimes()
+    for i in range(len(G.STAGES)):
+        t.ms[i], t.launches[i] = 7.0, 7
+
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, y=D_, dt=0, times=ctypes.byref(t)):
+        return lib.gspn_forward4_timed(n, c, h, w, cw, chunk, x, zs, ls, y, None, 0, dt, None, times)
+
+    assert f(times=None) == NULLP
+    assert f(dt=3) == DTYPE
+    assert f(cw=3) == WCH
+    assert f(y=A) == ALIAS
+    assert f(n=0, x=0, y=0) == OK
+    assert list(t.ms) == [0.0] * len(G.STAGES) and list(t.launches) == [0] * len(G.STAGES)
+
+    WD, WU, WS = 0x70000000, 0x71000000, 0x72000000
+    need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1)
+
+    def g(n=1, cp=2, ws=WS, wsb=need, dt=1, times=ctypes.byref(t)):
+        return lib.gspn_proxy_forward4_timed(n, 6, 8, 8, cp, 1, 0, A, WD, WU, zs, ls, D_, ws, wsb, dt, None, times)
+
+    assert g(times=None) == NULLP
+    assert g(dt=2) == DTYPE
+    assert g(wsb=need - 1) == WSPACE
+    assert g(ws=0) == NULLP
+    assert g(n=0) == OK

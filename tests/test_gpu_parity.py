@@ -213,6 +213,47 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("shape,shared,expect", [
+    # few planes: fused four-direction launch
+    ((1, 2, 40, 56), False, {"transpose": 1, "scan": 1, "combine": 1, "normalize": 0}),
+    # channel-shared weights over several channels: normalised once per direction
+    ((1, 3, 40, 56), True, {"transpose": 1, "scan": 1, "combine": 1, "normalize": 4}),
+    # many planes: one launch per direction
+    ((8, 80, 8, 16), False, {"transpose": 1, "scan": 4, "combine": 1, "normalize": 0}),
+])
+def test_forward4_timed_matches_untimed(shape, shared, expect):
+    n, c, h, w = shape
+    wl = _wl(n=n, c=c, h=h, w=w, shared=shared, seed=31)
+    _say("forward4_timed %s shared=%s" % (shape, shared))
+    inp = make_inputs(wl, DEV)
+    ws = G.forward4_workspace(inp["x"], wl.cw)
+    a = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], workspace=ws)
+    b, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for stage, count in expect.items():
+        assert times[stage]["launches"] == count, (stage, times)
+        assert (times[stage]["ms"] > 0) == (count > 0), (stage, times)
+    assert times["project_down"]["launches"] == 0 and times["project_up"]["launches"] == 0
+    # without a workspace: four scans and nothing else
+    _, t2 = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"])
+    assert t2["scan"]["launches"] == 4 and sum(v["launches"] for v in t2.values()) == 4
+
+
+def test_proxy_forward4_timed_matches_untimed():
+    wl = _wl(n=1, c=40, h=32, w=64, dtype="bf16", shared=True, seed=32, cp=8)
+    _say("proxy_forward4_timed")
+    inp = make_inputs(wl, DEV)
+    ws = G.proxy_forward4_workspace(inp["x"], 8, 1)
+    a = G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"], workspace=ws)
+    b, times = G.gspn_proxy_forward4_timed(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
+                                           workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert times["project_down"]["launches"] == 1 and times["project_up"]["launches"] == 1
+    assert times["scan"]["launches"] == 1 and times["normalize"]["launches"] == 4
+
+
 # ----------------------------------------------------------------------------
 # Proxy pipeline, small
 # ----------------------------------------------------------------------------
