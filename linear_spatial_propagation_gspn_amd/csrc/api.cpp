@@ -20,7 +20,10 @@ constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxElems = int64_t{1} << 58;
 // Most (plane, chunk) lines per direction for which gspn_forward4 runs the
 // four directions concurrently when given a workspace.
-constexpr int64_t kFuse4MaxBlocks = 512;
+#ifndef GSPN_FUSE4_MAX_BLOCKS
+#define GSPN_FUSE4_MAX_BLOCKS 512
+#endif
+constexpr int64_t kFuse4MaxBlocks = GSPN_FUSE4_MAX_BLOCKS;
 
 bool valid_dtype(int dt) { return dt == GSPN_F32 || dt == GSPN_BF16; }
 size_t elem_size(int dt) { return dt == GSPN_F32 ? 4 : 2; }

@@ -3,6 +3,7 @@
 // and direction family in scan_{f32,bf16}_{vert,horiz}.hip and
 // scan4_{f32,bf16}.hip).
 #include "scan_kernel.hpp"
+#include "scan_lp.hpp"
 
 namespace gspn {
 
@@ -24,6 +25,10 @@ extern template hipError_t launch_fused4<bf16_t, float>(const Scan4K&, int, int,
 extern template hipError_t launch_fused4v<float, float>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4v<bf16_t, bf16_t>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4v<bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4lp<float, float, true>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4lp<float, float, false>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4lp<bf16_t, float, false>(const Scan4K&, int, hipStream_t);
 
 namespace {
 
@@ -131,11 +136,58 @@ hipError_t launch_scan4(const ScanParams (&p)[4], hipStream_t stream) {
     return launch_fused4<bf16_t, bf16_t>(k, pv, ph, nthreads, stream);
 }
 
+#ifndef GSPN_LP_MAX_BLOCKS
+#define GSPN_LP_MAX_BLOCKS 256
+#endif
+
+// The long-line kernel (scan_lp.hpp) serves launches of at most
+// GSPN_LP_MAX_BLOCKS lines (each then has a compute unit to itself, and the
+// step latency decides the time) whose lines split into whole 16-byte
+// vectors on at most lp::kMaxLanes lanes, with 16-byte aligned tensors.
+bool lp_eligible(const ScanParams (&p)[4], int64_t blocks) {
+    if (blocks > GSPN_LP_MAX_BLOCKS) return false;
+    const int esz = p[0].dtype == kF32 ? 4 : 2;
+    const int P = 16 / esz;
+    for (int d = 0; d < 4; ++d) {
+        const int64_t L = p[d].w;
+        if (L % P != 0 || L / P > lp::kMaxLanes) return false;
+        if (!aligned_to(p[d].x, 16) || !aligned_to(p[d].lam, 16) || !aligned_to(p[d].out, 16) ||
+            !aligned_to(p[d].wts, 16))
+            return false;
+    }
+    return true;
+}
+
 hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream) {
     // every p[d] is a vertical-form scan (dir 0 or 1); p[0..1] share one line
     // length, p[2..3] another
     const int l01 = static_cast<int>(p[0].w);
     const int l23 = static_cast<int>(p[2].w);
+    int64_t total = 0;
+    for (int d = 0; d < 4; ++d) {
+        const int64_t K = p[d].chunk;
+        total += p[d].n * p[d].c * ((p[d].h + K - 1) / K);
+    }
+    if (lp_eligible(p, total)) {
+        const int P = p[0].dtype == kF32 ? 4 : 8;
+        Scan4K k;
+        for (int d = 0; d < 4; ++d) {
+            k.d[d] = make_args(p[d], P);
+            k.blocks[d] = p[d].n * p[d].c * k.d[d].nchunks;
+        }
+        k.interleave = (k.blocks[0] == k.blocks[1] && k.blocks[1] == k.blocks[2] &&
+                        k.blocks[2] == k.blocks[3]) ? 1 : 0;
+        const int a = lanes_for(l01, P);
+        const int b = lanes_for(l23, P);
+        const int nthreads = a > b ? a : b;
+        const bool logits = p[0].wts_are_logits != 0;
+        if (p[0].dtype == kF32) {
+            return logits ? launch_fused4lp<float, float, true>(k, nthreads, stream)
+                          : launch_fused4lp<float, float, false>(k, nthreads, stream);
+        }
+        if (p[0].wdtype == kF32) return launch_fused4lp<bf16_t, float, false>(k, nthreads, stream);
+        return launch_fused4lp<bf16_t, bf16_t, true>(k, nthreads, stream);
+    }
     const int pv = l01 > 1024 ? 2 : 1;
     const int ph = l23 > 1024 ? 2 : 1;
     Scan4K k;

@@ -1,0 +1,257 @@
+// scan_lp.hpp -- the four-direction line scan for few, long lines (internal
+// to libgspn; instantiated in scan4_*.hip).
+//
+// Same recurrence as scan_kernel.hpp (GSPN-2 paper notes, "2D spatial
+// propagation recap"; chunks from "Optimisation 1"), for the case where the
+// (plane, chunk) lines of a forward are too few to fill the GPU, e.g. the
+// eight proxy-space planes of 2048 positions in the compressive-proxy
+// pipeline ("Optimisation 2").  There each workgroup owns a CU by itself and
+// the time per scan step is the latency of one step, not bandwidth, so the
+// kernel minimises the work on the step's critical path:
+//  - each lane owns P contiguous positions (16 bytes of the storage type), so
+//    every stream moves one 16-byte vector per lane and step, and the line
+//    needs few waves (256 lanes for 2048 bf16 positions);
+//  - loads and stores go through buffer resources: the lane's byte offset is
+//    fixed for the whole scan and the step's row offset is a scalar, so no
+//    vector address arithmetic runs per step;
+//  - the neighbour values inside a wave move with DPP lane shifts; only the
+//    two wave-edge values of each wave go through LDS, with one barrier per
+//    step;
+//  - the inputs of the next D steps are in flight at all times: D ring slots,
+//    each refilled as soon as its step has read it (the loop is unrolled by
+//    D so the slot indices are compile-time constants).
+// All four directions are described in vertical form (the horizontal ones on
+// x transposed into their scan frame), as for scan4v_kernel.
+#pragma once
+
+#include <utility>
+
+#include "scan_kernel.hpp"
+
+namespace gspn {
+
+namespace lp {
+
+constexpr int kMaxLanes = 256;
+constexpr int kMaxWaves = kMaxLanes / 64;
+
+#ifndef GSPN_LP_DEPTH
+#define GSPN_LP_DEPTH 6
+#endif
+
+// Raw buffer resource over `bytes` bytes from `base` (untyped dword accesses).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    const int n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// W 32-bit words from the buffer at voff + soff (W a multiple of 4).
+template <int W>
+__device__ __forceinline__ void load_words(uint32_t (&d)[W], __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                           uint32_t soff) {
+#pragma unroll
+    for (int v = 0; v < W / 4; ++v) {
+        const int4v q = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * v, soff, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[4 * v + e] = static_cast<uint32_t>(q[e]);
+    }
+}
+
+// Element j of P values of type E packed in 32-bit words, widened to fp32.
+template <typename E, int W>
+__device__ __forceinline__ float elem(const uint32_t (&w)[W], int j) {
+    if constexpr (sizeof(E) == 4) {
+        return __uint_as_float(w[j]);
+    } else {
+        const uint32_t word = w[j >> 1];
+        return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+    }
+}
+
+__device__ __forceinline__ float shift_from_lower_lane(float v) {  // lane i gets lane i-1 (0 for lane 0)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ float shift_from_upper_lane(float v) {  // lane i gets lane i+1 (0 for lane 63)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true));
+}
+
+}  // namespace lp
+
+// One (plane, chunk) line of a vertical-form scan.  T: storage of x, lambda
+// and the output; TW: storage of the weights; LOGITS: the weights are logits
+// normalised here (else normalised weights, zero outside the line).
+template <typename T, typename TW, bool LOGITS>
+__device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
+    constexpr int P = 16 / static_cast<int>(sizeof(T));              // positions per lane
+    constexpr int WT = P * static_cast<int>(sizeof(T)) / 4;          // words per lane: x, lambda, out
+    constexpr int WW = P * static_cast<int>(sizeof(TW)) / 4;         // words per lane: one weight row
+    constexpr int D = GSPN_LP_DEPTH;                                  // steps in flight
+    __shared__ float edges[2][lp::kMaxWaves][2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int S = a.S;
+    const int L = a.L;
+    const int64_t plane = static_cast<int64_t>(S) * L;
+    const int64_t nidx = p / a.c;
+    const int64_t ci = p - nidx * a.c;
+
+    const auto rx = lp::rsrc(static_cast<const T*>(a.x) + p * plane, plane * sizeof(T));
+    const auto rl = lp::rsrc(static_cast<const T*>(a.lam) + p * plane, plane * sizeof(T));
+    const auto ro = lp::rsrc(static_cast<T*>(a.out) + p * plane, plane * sizeof(T));
+    const auto rz = lp::rsrc(static_cast<const TW*>(a.wts) + (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane,
+                             3 * plane * sizeof(TW));
+
+    const int k0 = tid * P;
+    const bool active = k0 < L;
+    const int k0c = active ? k0 : L - P;  // lanes past the line read its last vector (unused)
+    const uint32_t vt = static_cast<uint32_t>(k0c) * sizeof(T);
+    const uint32_t vw = static_cast<uint32_t>(k0c) * sizeof(TW);
+    const uint32_t rowT = static_cast<uint32_t>(L) * sizeof(T);
+    const uint32_t rowW = static_cast<uint32_t>(L) * sizeof(TW);
+    const uint32_t planeW = static_cast<uint32_t>(plane) * sizeof(TW);
+    const bool has_l0 = k0 > 0;       // the lane's first position has a left neighbour
+    const bool has_rP = k0 + P < L;   // the lane's last position has a right neighbour
+
+    const int t0 = q * a.K;
+    const int t1 = min(t0 + a.K, S);
+    const bool rev = a.reverse != 0;
+    auto line_of = [&](int t) { return static_cast<uint32_t>(rev ? S - 1 - t : t); };
+
+    uint32_t sx[D][WT], sl[D][WT], sz[D][3][WW];
+    auto fill = [&](auto slot, int t) {
+        constexpr int s = decltype(slot)::value;
+        const uint32_t i = line_of(min(t, t1 - 1));
+        lp::load_words<WT>(sx[s], rx, vt, i * rowT);
+        lp::load_words<WT>(sl[s], rl, vt, i * rowT);
+#pragma unroll
+        for (int o = 0; o < 3; ++o) lp::load_words<WW>(sz[s][o], rz, vw, o * planeW + i * rowW);
+    };
+
+    float h[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) h[j] = 0.0f;
+    int buf = 0;
+
+    // Step t from slot s; FIRST: the first line of the chunk (h_prev = 0 and
+    // its weights unused).  The slot is refilled with step t + D.
+    auto step = [&](auto slot, auto firstc, int t) {
+        constexpr int s = decltype(slot)::value;
+        constexpr bool FIRST = decltype(firstc)::value != 0;
+        float u[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) u[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+        float hn[P];
+        if constexpr (FIRST) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) hn[j] = u[j];
+        } else {
+            float w[3][P];
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const float z0 = lp::elem<TW, WW>(sz[s][0], j);
+                const float z1 = lp::elem<TW, WW>(sz[s][1], j);
+                const float z2 = lp::elem<TW, WW>(sz[s][2], j);
+                if constexpr (LOGITS) {
+                    const bool hl = j > 0 || has_l0;
+                    const bool hr = j < P - 1 || has_rP;
+                    normalise_row(z0, z1, z2, hl, hr, w[0][j], w[1][j], w[2][j]);
+                } else {
+                    w[0][j] = z0;
+                    w[1][j] = z1;
+                    w[2][j] = z2;
+                }
+            }
+            // neighbours from the previous step: inside the wave by DPP, across
+            // wave edges from LDS (0 beyond the line)
+            const float eleft = wave > 0 ? edges[buf][wave - 1][1] : 0.0f;
+            const float eright = wave + 1 < nwaves ? edges[buf][wave + 1][0] : 0.0f;
+            const float dl = lp::shift_from_lower_lane(h[P - 1]);
+            const float dr = lp::shift_from_upper_lane(h[0]);
+            const float left = lane == 0 ? eleft : dl;
+            const float right = lane == 63 ? eright : dr;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const float hl = j == 0 ? left : h[j - 1];
+                const float hr = j == P - 1 ? right : h[j + 1];
+                hn[j] = __builtin_fmaf(w[0][j], hl, __builtin_fmaf(w[1][j], h[j], __builtin_fmaf(w[2][j], hr, u[j])));
+            }
+        }
+        fill(slot, t + D);
+#pragma unroll
+        for (int j = 0; j < P; ++j) h[j] = active ? hn[j] : 0.0f;
+        if (active) {
+            lp::int4v o;
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = __float_as_int(h[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = static_cast<int>(static_cast<uint32_t>(f32_to_bf16(h[2 * e])) |
+                                            (static_cast<uint32_t>(f32_to_bf16(h[2 * e + 1])) << 16));
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(o, ro, vt, line_of(t) * rowT, 0);
+        }
+        buf ^= 1;
+        if (lane == 0) edges[buf][wave][0] = h[0];
+        if (lane == 63) edges[buf][wave][1] = h[P - 1];
+        __syncthreads();
+    };
+
+    // prologue: D steps in flight, then the chunk's first line
+    [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        (fill(IC<Ss>{}, t0 + Ss), ...);
+    }(std::make_integer_sequence<int, D>{});
+    step(IC<0>{}, IC<1>{}, t0);
+
+    // main loop: D steps per iteration, slots 1, 2, .., D-1, 0
+    int t = t0 + 1;
+    for (; t + D <= t1; t += D) {
+        [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+            (step(IC<(Ss + 1) % D>{}, IC<0>{}, t + Ss), ...);
+        }(std::make_integer_sequence<int, D>{});
+    }
+    // tail: fewer than D steps, uniform guards around whole steps
+    [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        ((t + Ss < t1 ? step(IC<(Ss + 1) % D>{}, IC<0>{}, t + Ss) : void()), ...);
+    }(std::make_integer_sequence<int, D - 1>{});
+}
+
+// Four vertical-form scans in one launch; block b is direction b % 4 when the
+// directions have equal block counts (Scan4K::interleave), else consecutive
+// ranges, as in scan4v_kernel.
+template <typename T, typename TW, bool LOGITS>
+__global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) {
+    const int64_t b = blockIdx.x;
+    int dir = 0;
+    int64_t idx = b;
+    if (a.interleave) {
+        dir = static_cast<int>(b & 3);
+        idx = b >> 2;
+    } else {
+        while (dir < 3 && idx >= a.blocks[dir]) {
+            idx -= a.blocks[dir];
+            ++dir;
+        }
+    }
+    const ScanK& k = a.d[dir];
+    const int64_t p = idx / k.nchunks;
+    const int q = static_cast<int>(idx - p * k.nchunks);
+    lp_line<T, TW, LOGITS>(k, p, q);
+}
+
+template <typename T, typename TW, bool LOGITS>
+hipError_t launch_fused4lp(const Scan4K& k, int nthreads, hipStream_t stream) {
+    const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
+    hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads), 0,
+                       stream, k);
+    return hipGetLastError();
+}
+
+}  // namespace gspn
