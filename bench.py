@@ -82,17 +82,21 @@ def algorithmic_bytes(wl) -> int:
     return x + lam + z + wts + x
 
 
-def scan_launch_bytes(wl, launches: int) -> int:
-    """Algorithmic bytes of one scan launch: every tensor the launch reads or
-    writes, moved once.
-      fused (1 launch): x and its transpose, four directions' weights and
-        lambdas, four output maps written;
-      one launch per direction: x (or its transpose), the direction's weights
-        and lambda, the output written, and read as well by the two launches
-        that add into a map (average over the four launches)."""
+def scan_launch_bytes(wl, kernel: str) -> int:
+    """Algorithmic bytes of one launch of the scan kernel the step ran: every
+    tensor the launch reads or writes, moved once.
+      plane4_kernel (one launch, planes in LDS): x, the four directions'
+        logits and lambdas, y written;
+      scan4v_kernel / scan4lp_kernel (one launch): x and its transpose, four
+        directions' weights and lambdas, four output maps written;
+      scan_kernel (one launch per direction): x (or its transpose), the
+        direction's weights and lambda, the output written, and read as well
+        by the two launches that add into a map (average over the four)."""
     u = unit_bytes(wl)
+    if kernel == "plane4_kernel":
+        return u + 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl) + 4 * u + u
     wd = weight_bytes_per_direction(wl)
-    if launches == 1:
+    if kernel in ("scan4v_kernel", "scan4lp_kernel"):
         return 2 * u + 4 * wd + 4 * u + 4 * u
     total = 4 * u + 4 * wd + 4 * u + 4 * u + 2 * u
     return total // 4
@@ -111,12 +115,14 @@ def stage_times(wl, inp, out, ws, reps: int) -> dict:
     """Mean per-step duration and launch count of each stage over reps timed
     steps."""
     acc = {name: {"ms": 0.0, "launches": 0} for name in G.STAGES}
+    kernel = None
     for _ in range(reps):
         _, t = run_step(wl, inp, out, ws, timed=True)
+        kernel = t.pop("scan_kernel")
         for name, v in t.items():
             acc[name]["ms"] += v["ms"] / reps
             acc[name]["launches"] = v["launches"]
-    return acc
+    return acc, kernel
 
 
 def kernel_sources_digest() -> str:
@@ -304,12 +310,11 @@ def main():
     print("bench: %.3f ms/step (wall %.3f ms/step)" % (ms, wall * 1e3 / args.steps),
           file=sys.stderr, flush=True)
 
-    st = stage_times(wl, inp, out, ws, reps=max(3, min(args.steps, 10)))
+    st, kernel = stage_times(wl, inp, out, ws, reps=max(3, min(args.steps, 10)))
     scan = st["scan"]
     launches = scan["launches"]
     kernel_ms = scan["ms"] / launches
-    kernel = "scan4v_kernel" if launches == 1 else "scan_kernel"
-    bpl = scan_launch_bytes(wl, launches)
+    bpl = scan_launch_bytes(wl, kernel)
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
     traffic, traffic_src = counter_traffic(kernel, wl)
     alg = algorithmic_bytes(wl)

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 2
+#define GSPN_ABI_VERSION 3
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -235,7 +235,8 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
  * block the host) and fill *times: per stage, the summed duration in
  * milliseconds of its launches and the number of launches.  The events are
  * created and destroyed inside the call; no device memory is allocated.
- * Stages that did not run read 0 ms / 0 launches.  times == NULL is
+ * Stages that did not run read 0 ms / 0 launches; scan_kernel names the
+ * scan kernel the call ran.  times == NULL is
  * GSPN_ERR_NULL_POINTER.  If a launch fails the call still waits for what
  * was queued, then returns GSPN_ERR_HIP.
  */
@@ -249,9 +250,19 @@ typedef enum {
     GSPN_NUM_STAGES = 6
 } gspn_stage;
 
+/* Which scan kernel a forward call ran (gspn_stage_times.scan_kernel). */
+typedef enum {
+    GSPN_SCAN_NONE = 0,         /* no scan (empty input or failed validation) */
+    GSPN_SCAN_PER_DIRECTION = 1,/* one launch per direction */
+    GSPN_SCAN_FUSED4 = 2,       /* four directions in one launch, one workgroup per line */
+    GSPN_SCAN_LONG_LINE = 3,    /* four directions in one launch, 16-byte vectors per lane */
+    GSPN_SCAN_PLANE = 4         /* one workgroup per plane, all four directions, y written once */
+} gspn_scan_kernel;
+
 typedef struct {
     float ms[GSPN_NUM_STAGES];
     int32_t launches[GSPN_NUM_STAGES];
+    int32_t scan_kernel; /* a gspn_scan_kernel value */
 } gspn_stage_times;
 
 gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,

@@ -70,7 +70,7 @@ struct Timer {
     int stage[kMax] = {};
     hipEvent_t a[kMax] = {};
     hipEvent_t b[kMax] = {};
-    hipError_t err = hipSuccess;
+    int scan_kernel = GSPN_SCAN_NONE;
 
     ~Timer() {
         for (int i = 0; i < count; ++i) {
@@ -99,6 +99,7 @@ struct Timer {
             t->ms[s] = 0.0f;
             t->launches[s] = 0;
         }
+        t->scan_kernel = scan_kernel;
         if (count == 0) return hipSuccess;
         hipError_t e = hipEventSynchronize(b[count - 1]);
         if (e != hipSuccess) return e;
@@ -375,9 +376,19 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].wdtype = dtype;
     }
 
+    // Planes of at most 64 x 64: one pass over LDS-resident planes, whether
+    // or not a workspace is given.
+    if (gspn::plane4_supported(h, w)) {
+        if (tm) tm->scan_kernel = GSPN_SCAN_PLANE;
+        return from_hip(timed(tm, GSPN_STAGE_SCAN, [&] {
+            return gspn::launch_plane4(x, logits, lam, y, n, c, cw, h, w, chunks, dtype, st);
+        }));
+    }
+
     if (!have_ws) {
         // No workspace: one direction per launch; the first writes y, the
         // others add to it; horizontal lines use per-lane row tiles.
+        if (tm) tm->scan_kernel = GSPN_SCAN_PER_DIRECTION;
         for (int d = 0; d < 4; ++d) {
             p[d].accumulate = d > 0 ? 1 : 0;
             if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan(p[d], st); }) != hipSuccess)
@@ -435,8 +446,10 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[1].out = m1;
         p[2].out = m2;
         p[3].out = m3;
-        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st); }) != hipSuccess)
+        int kind = GSPN_SCAN_FUSED4;
+        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
             return GSPN_ERR_HIP;
+        if (tm) tm->scan_kernel = kind;
         return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
             return gspn::launch_combine(y, m1, m2, m3, n * c, static_cast<int>(h), static_cast<int>(w), 1, dtype,
                                         st);
@@ -444,6 +457,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     }
     // Sequential path: T2B writes y, B2T adds to it; L2R writes the
     // transposed map, R2L adds to it; a transposing merge adds that into y.
+    if (tm) tm->scan_kernel = GSPN_SCAN_PER_DIRECTION;
     p[1].accumulate = 1;
     p[2].out = m1;
     p[3].out = m1;

@@ -32,7 +32,16 @@ bool fused4_supported(int64_t h, int64_t w);
 
 // Four vertical-form scans in one launch (p[d].dir in {0, 1}): used for the
 // vertical directions on x and the horizontal ones on the transposed x.
-hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream);
+// *kind (if given) receives the kernel used: 2 = one workgroup per line,
+// 3 = the long-line kernel (gspn_scan_kernel values).
+hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind = nullptr);
+
+// All four directions of planes of at most 64 x 64 in one pass, y written
+// once (chunk[d]: steps per chunk of direction d, clamped to [1, S_d]).
+bool plane4_supported(int64_t h, int64_t w);
+hipError_t launch_plane4(const void* x, const void* const logits[4], const void* const lam[4], void* y,
+                         int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w, const int64_t chunk[4],
+                         int dtype, hipStream_t stream);
 
 // dst[p][c][r] = src[p][r][c] for `planes` planes of R x Cc elements.
 hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, int Cc, int dtype,

@@ -158,7 +158,7 @@ bool lp_eligible(const ScanParams (&p)[4], int64_t blocks) {
     return true;
 }
 
-hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream) {
+hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind) {
     // every p[d] is a vertical-form scan (dir 0 or 1); p[0..1] share one line
     // length, p[2..3] another
     const int l01 = static_cast<int>(p[0].w);
@@ -181,6 +181,7 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream) {
         const int b = lanes_for(l23, P);
         const int nthreads = a > b ? a : b;
         const bool logits = p[0].wts_are_logits != 0;
+        if (kind) *kind = 3;
         if (p[0].dtype == kF32) {
             return logits ? launch_fused4lp<float, float, true>(k, nthreads, stream)
                           : launch_fused4lp<float, float, false>(k, nthreads, stream);
@@ -188,6 +189,7 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream) {
         if (p[0].wdtype == kF32) return launch_fused4lp<bf16_t, float, false>(k, nthreads, stream);
         return launch_fused4lp<bf16_t, bf16_t, true>(k, nthreads, stream);
     }
+    if (kind) *kind = 2;
     const int pv = l01 > 1024 ? 2 : 1;
     const int ph = l23 > 1024 ? 2 : 1;
     Scan4K k;

@@ -43,12 +43,19 @@ EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy
 STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up")
 
 
+# gspn_scan_kernel, in order.
+SCAN_KERNELS = ("none", "scan_kernel", "scan4v_kernel", "scan4lp_kernel", "plane4_kernel")
+
+
 class StageTimes(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_float * len(STAGES)), ("launches", ctypes.c_int32 * len(STAGES))]
+    _fields_ = [("ms", ctypes.c_float * len(STAGES)), ("launches", ctypes.c_int32 * len(STAGES)),
+                ("scan_kernel", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        return {name: {"ms": float(self.ms[i]), "launches": int(self.launches[i])}
-                for i, name in enumerate(STAGES)}
+        d = {name: {"ms": float(self.ms[i]), "launches": int(self.launches[i])}
+             for i, name in enumerate(STAGES)}
+        d["scan_kernel"] = SCAN_KERNELS[self.scan_kernel]
+        return d
 
 
 class GspnError(RuntimeError):

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 2
+    assert lib.gspn_abi_version() == 3
     for code in range(12):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -220,8 +220,10 @@ def test_timed_variants_validate_like_untimed(lib):
     assert f(dt=3) == DTYPE
     assert f(cw=3) == WCH
     assert f(y=A) == ALIAS
+    t.scan_kernel = 7
     assert f(n=0, x=0, y=0) == OK
     assert list(t.ms) == [0.0] * len(G.STAGES) and list(t.launches) == [0] * len(G.STAGES)
+    assert t.scan_kernel == 0
 
     WD, WU, WS = 0x70000000, 0x71000000, 0x72000000
     need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1)

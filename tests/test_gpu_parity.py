@@ -153,7 +153,8 @@ def test_project(cin, cout, dtype, hw):
 @pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("chunk", [0, 8, 5])
-@pytest.mark.parametrize("shape", [(1, 2, 16, 16), (2, 3, 23, 41), (1, 2, 64, 130), (1, 1, 1100, 40)])
+@pytest.mark.parametrize("shape", [(1, 2, 16, 16), (2, 3, 23, 41), (1, 2, 64, 64), (2, 2, 65, 33), (1, 2, 40, 72),
+                                   (1, 2, 64, 130), (1, 1, 1100, 40)])
 def test_forward4_small(shape, chunk, dtype, use_ws):
     n, c, h, w = shape
     for shared in (False, True):
@@ -213,15 +214,20 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("shape,shared,expect", [
-    # few planes: fused four-direction launch
-    ((1, 2, 40, 56), False, {"transpose": 1, "scan": 1, "combine": 1, "normalize": 0}),
+@pytest.mark.parametrize("shape,shared,kernel,expect", [
+    # planes of at most 64 x 64: one pass, nothing else
+    ((2, 3, 40, 56), False, "plane4_kernel", {"transpose": 0, "scan": 1, "combine": 0, "normalize": 0}),
+    ((2, 3, 64, 64), True, "plane4_kernel", {"transpose": 0, "scan": 1, "combine": 0, "normalize": 0}),
+    # few planes, lines whose 16-byte vectors fit 256 lanes: long-line kernel
+    ((1, 2, 40, 72), False, "scan4lp_kernel", {"transpose": 1, "scan": 1, "combine": 1, "normalize": 0}),
     # channel-shared weights over several channels: normalised once per direction
-    ((1, 3, 40, 56), True, {"transpose": 1, "scan": 1, "combine": 1, "normalize": 4}),
+    ((1, 3, 40, 72), True, "scan4lp_kernel", {"transpose": 1, "scan": 1, "combine": 1, "normalize": 4}),
+    # few planes, lines not a whole number of vectors: one workgroup per line
+    ((1, 2, 40, 70), False, "scan4v_kernel", {"transpose": 1, "scan": 1, "combine": 1, "normalize": 0}),
     # many planes: one launch per direction
-    ((8, 80, 8, 16), False, {"transpose": 1, "scan": 4, "combine": 1, "normalize": 0}),
+    ((8, 80, 8, 72), False, "scan_kernel", {"transpose": 1, "scan": 4, "combine": 1, "normalize": 0}),
 ])
-def test_forward4_timed_matches_untimed(shape, shared, expect):
+def test_forward4_timed_matches_untimed(shape, shared, kernel, expect):
     n, c, h, w = shape
     wl = _wl(n=n, c=c, h=h, w=w, shared=shared, seed=31)
     _say("forward4_timed %s shared=%s" % (shape, shared))
@@ -231,17 +237,22 @@ def test_forward4_timed_matches_untimed(shape, shared, expect):
     b, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    assert times["scan_kernel"] == kernel, times
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"])
+    assert _err(b, ref) <= TOL["f32"]
     for stage, count in expect.items():
         assert times[stage]["launches"] == count, (stage, times)
         assert (times[stage]["ms"] > 0) == (count > 0), (stage, times)
     assert times["project_down"]["launches"] == 0 and times["project_up"]["launches"] == 0
-    # without a workspace: four scans and nothing else
+    # without a workspace: four scans and nothing else (one pass for small planes)
     _, t2 = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"])
-    assert t2["scan"]["launches"] == 4 and sum(v["launches"] for v in t2.values()) == 4
+    nscan = 1 if kernel == "plane4_kernel" else 4
+    assert t2["scan"]["launches"] == nscan
+    assert sum(v["launches"] for k, v in t2.items() if k != "scan_kernel") == nscan
 
 
 def test_proxy_forward4_timed_matches_untimed():
-    wl = _wl(n=1, c=40, h=32, w=64, dtype="bf16", shared=True, seed=32, cp=8)
+    wl = _wl(n=1, c=40, h=40, w=72, dtype="bf16", shared=True, seed=32, cp=8)
     _say("proxy_forward4_timed")
     inp = make_inputs(wl, DEV)
     ws = G.proxy_forward4_workspace(inp["x"], 8, 1)
@@ -251,7 +262,8 @@ def test_proxy_forward4_timed_matches_untimed():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert times["project_down"]["launches"] == 1 and times["project_up"]["launches"] == 1
-    assert times["scan"]["launches"] == 1 and times["normalize"]["launches"] == 4
+    assert times["scan"]["launches"] == 1 and times["scan_kernel"] == "scan4lp_kernel"
+    assert times["normalize"]["launches"] == 4
 
 
 # ----------------------------------------------------------------------------
