@@ -158,7 +158,8 @@ gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
  * workspace: four maps of n*c*h*w elements of the storage type (x transposed
  * into the horizontal scan frame and three partial outputs) and, for
  * channel-shared weights over more than one channel (cw == 1 < c), the four
- * directions' normalised weights in fp32 (4 * 3 * n*h*w floats).  Returns -1
+ * directions' normalised weights: 4 * 3 * n*h*w floats for GSPN_F32, 4 *
+ * n*h*w 32-bit half pairs for GSPN_BF16 (see gspn_forward4).  Returns -1
  * when the arguments are invalid (negative or overflowing dimensions, cw not
  * in {1, c}, unknown dtype).
  */
@@ -179,15 +180,20 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              must hold gspn_forward4_workspace_bytes() bytes (else
  *              GSPN_ERR_WORKSPACE) and overlap neither y nor any input (else
  *              GSPN_ERR_ALIASING).  The library then (a) normalises
- *              channel-shared logits once into fp32 weights that every
- *              channel's scan reads, (b) transposes x once so that the
- *              horizontal directions run as row-coalesced scans whose
- *              outputs a transposing merge adds into y, and (c) when there
- *              are too few planes to fill the GPU with one direction at a
- *              time, runs all four directions in one launch into separate
- *              maps.  Its contents afterwards are unspecified.  Either way y
- *              is the same up to fp32 rounding order (and, for bf16,
- *              rounding of the partial maps).
+ *              channel-shared logits once into weights that every channel's
+ *              scan reads: fp32 triples for GSPN_F32; for GSPN_BF16 the two
+ *              side weights w_{k-1}, w_{k+1} as IEEE half precision, the
+ *              centre weight recomputed in fp32 as 1 minus their sum (rows
+ *              still sum to 1; the side weights carry about 2^-11 relative
+ *              rounding), (b) transposes x once so that the horizontal
+ *              directions run as row-coalesced scans whose outputs a
+ *              transposing merge adds into y, and (c) runs all four
+ *              directions in one launch into separate maps (lines up to 2048
+ *              positions).  Its contents afterwards are unspecified.
+ *              Planes of at most 64 x 64 take a one-pass path (x read once,
+ *              y written once) with or without a workspace.  In all cases y
+ *              is the same up to fp32 rounding order and, for bf16, rounding
+ *              of the intermediates.
  */
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
@@ -242,7 +248,7 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
  */
 typedef enum {
     GSPN_STAGE_PROJECT_DOWN = 0, /* 1x1 projection C -> C_proxy */
-    GSPN_STAGE_NORMALIZE = 1,    /* channel-shared logits -> fp32 weights */
+    GSPN_STAGE_NORMALIZE = 1,    /* channel-shared logits -> normalised weights */
     GSPN_STAGE_TRANSPOSE = 2,    /* x into the horizontal scan frame */
     GSPN_STAGE_SCAN = 3,         /* the line-scan launches (1 fused or 4) */
     GSPN_STAGE_COMBINE = 4,      /* transposing merge of the partial maps into y */

@@ -18,12 +18,6 @@ using gspn::kF32;
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxElems = int64_t{1} << 58;
-// Most (plane, chunk) lines per direction for which gspn_forward4 runs the
-// four directions concurrently when given a workspace.
-#ifndef GSPN_FUSE4_MAX_BLOCKS
-#define GSPN_FUSE4_MAX_BLOCKS 512
-#endif
-constexpr int64_t kFuse4MaxBlocks = GSPN_FUSE4_MAX_BLOCKS;
 
 bool valid_dtype(int dt) { return dt == GSPN_F32 || dt == GSPN_BF16; }
 size_t elem_size(int dt) { return dt == GSPN_F32 ? 4 : 2; }
@@ -315,7 +309,10 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
     if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
     const int64_t elems = checked_product({n, c, h, w});
     const int64_t maps = 4 * elems * static_cast<int64_t>(elem_size(dtype));
-    const int64_t weights = (cw == 1 && c > 1) ? 4 * 3 * checked_product({n, h, w}) * 4 : 0;
+    // channel-shared weights over several channels, normalised once per
+    // direction: fp32 triples for fp32 storage, packed half pairs for bf16
+    const int64_t per_dir = checked_product({n, h, w}) * (dtype == GSPN_F32 ? 3 * 4 : 4);
+    const int64_t weights = (cw == 1 && c > 1) ? 4 * per_dir : 0;
     return maps + weights;
 }
 
@@ -397,28 +394,32 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         return GSPN_OK;
     }
 
-    // Workspace layout: [fp32 weights of the four directions, only for
+    // Workspace layout: [normalised weights of the four directions, only for
     // channel-shared weights over several channels][x transposed into the
     // horizontal scan frame][three output maps].
     char* ws = static_cast<char*>(workspace);
     const bool prenorm = cw == 1 && c > 1;
-    const int64_t wdir = n * 3 * h * w;  // fp32 weights per direction
-    char* xt = ws + (prenorm ? 4 * wdir * 4 : 0);
+    const int64_t wdir = n * h * w * (dtype == GSPN_F32 ? 3 * 4 : 4);  // weight bytes per direction
+    char* xt = ws + (prenorm ? 4 * wdir : 0);
     char* m1 = xt + xb;
     char* m2 = m1 + xb;
     char* m3 = m2 + xb;
     if (prenorm) {
         // One normalisation per position and direction, shared by all c
-        // channels, kept in fp32 so the scans run without transcendentals.
+        // channels, so the scans run without transcendentals: fp32 triples
+        // for fp32 storage; for bf16 storage packed half pairs (w_{k-1},
+        // w_{k+1}) with the centre weight recovered as 1 minus their sum, a
+        // third of the bytes every channel's scan reads.
         for (int d = 0; d < 4; ++d) {
-            float* wd = reinterpret_cast<float*>(ws) + d * wdir;
-            if (timed(tm, GSPN_STAGE_NORMALIZE,
-                      [&] { return gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32); }) !=
-                hipSuccess)
-                return GSPN_ERR_HIP;
+            char* wd = ws + d * wdir;
+            const hipError_t e = timed(tm, GSPN_STAGE_NORMALIZE, [&] {
+                return dtype == GSPN_F32 ? gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32)
+                                         : gspn::launch_normalize_pair(d, n, h, w, logits[d], wd, dtype, st);
+            });
+            if (e != hipSuccess) return GSPN_ERR_HIP;
             p[d].wts = wd;
             p[d].wts_are_logits = 0;
-            p[d].wdtype = GSPN_F32;
+            p[d].wdtype = dtype == GSPN_F32 ? GSPN_F32 : gspn::kPairF16;
         }
     }
     // The horizontal directions become vertical-form scans of x transposed
@@ -434,15 +435,9 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].dir = d - 2;  // L2R runs like T2B, R2L like B2T, in the transposed frame
     }
 
-    // Concurrent path: worth it while one direction's (plane, chunk) lines
-    // cannot keep the GPU's 256 compute units busy twice over.
-    int64_t most_blocks = 0;
-    for (int d = 0; d < 4; ++d) {
-        const int64_t S = horizontal(d) ? w : h;
-        const int64_t nb = n * c * ((S + chunks[d] - 1) / chunks[d]);
-        most_blocks = nb > most_blocks ? nb : most_blocks;
-    }
-    if (most_blocks < kFuse4MaxBlocks && gspn::fused4_supported(h, w)) {
+    // Concurrent path: the four directions in one launch, each into its own
+    // map (lines up to 2048 positions).
+    if (gspn::fused4_supported(h, w)) {
         p[1].out = m1;
         p[2].out = m2;
         p[3].out = m3;
@@ -455,8 +450,8 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                                         st);
         }));
     }
-    // Sequential path: T2B writes y, B2T adds to it; L2R writes the
-    // transposed map, R2L adds to it; a transposing merge adds that into y.
+    // Longer lines, sequential path: T2B writes y, B2T adds to it; L2R writes
+    // the transposed map, R2L adds to it; a transposing merge adds that into y.
     if (tm) tm->scan_kernel = GSPN_SCAN_PER_DIRECTION;
     p[1].accumulate = 1;
     p[2].out = m1;

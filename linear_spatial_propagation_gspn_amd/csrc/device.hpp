@@ -35,6 +35,26 @@ struct Store<bf16_t> {
     static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
+// Pre-normalised channel-shared weights for 16-bit storage: one 32-bit word
+// per position holding w_{k-1} (low half) and w_{k+1} (high half) as IEEE
+// half precision; the centre weight is recovered as 1 - w_{k-1} - w_{k+1} in
+// fp32, so every row still sums to 1.  (fp16 keeps 11 significant bits over
+// the weights' range [0, 1].)  WPair tags this format as a weight type.
+struct WPair {};
+
+__device__ __forceinline__ uint32_t pack_pair(float wl, float wr) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(wl))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(wr))) << 16);
+}
+
+__device__ __forceinline__ float pair_lo(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b & 0xffffu)));
+}
+
+__device__ __forceinline__ float pair_hi(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b >> 16)));
+}
+
 // 1 / d to within about half an ulp: the hardware reciprocal (1 ulp) refined
 // by one Newton step.
 __device__ __forceinline__ float recip(float d) {

@@ -31,6 +31,27 @@ __global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ z,
     }
 }
 
+// The same normalisation into packed half pairs (w_{k-1}, w_{k+1}) per
+// position; layout [planes][S][L] of 32-bit words.
+template <typename T>
+__global__ __launch_bounds__(256) void normalize_pair_kernel(const T* __restrict__ z, uint32_t* __restrict__ w,
+                                                             int64_t planes, int64_t S, int64_t L) {
+    const int64_t per_plane = S * L;
+    const int64_t total = planes * per_plane;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+         e += stride) {
+        const int64_t pl = e / per_plane;
+        const int64_t r = e - pl * per_plane;
+        const int64_t k = r % L;
+        const int64_t base = pl * 3 * per_plane + r;
+        float w0, w1, w2;
+        normalise_row(Store<T>::ld(z + base), Store<T>::ld(z + base + per_plane),
+                      Store<T>::ld(z + base + 2 * per_plane), k > 0, k + 1 < L, w0, w1, w2);
+        w[e] = pack_pair(w0, w2);
+    }
+}
+
 // y = ((h0 + h1) + h2) + h3
 template <typename T>
 __global__ __launch_bounds__(256) void merge4_kernel(const T* __restrict__ h0, const T* __restrict__ h1,
@@ -130,6 +151,22 @@ hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w
         hipLaunchKernelGGL((normalize_kernel<bf16_t, bf16_t>), dim3(grid), dim3(256), 0, stream,
                            static_cast<const bf16_t*>(logits), static_cast<bf16_t*>(w_out), planes, S,
                            L);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_normalize_pair(int dir, int64_t n, int64_t h, int64_t w, const void* logits, void* w_out,
+                                 int dtype, hipStream_t stream) {
+    const bool horiz = (dir == 2 || dir == 3);
+    const int64_t S = horiz ? w : h;
+    const int64_t L = horiz ? h : w;
+    const unsigned grid = grid_for(n * S * L, 256);
+    if (dtype == kF32) {
+        hipLaunchKernelGGL(normalize_pair_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const float*>(logits), static_cast<uint32_t*>(w_out), n, S, L);
+    } else {
+        hipLaunchKernelGGL(normalize_pair_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const bf16_t*>(logits), static_cast<uint32_t*>(w_out), n, S, L);
     }
     return hipGetLastError();
 }

@@ -9,6 +9,11 @@ namespace gspn {
 
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
+// Weight formats a scan can read besides the storage type itself: fp32
+// triples (kF32) or, for 16-bit storage, packed half pairs (kPairF16, see
+// WPair in device.hpp).
+enum WeightFormat { kPairF16 = 2 };
+
 struct ScanParams {
     const void* x;
     const void* wts;
@@ -20,7 +25,7 @@ struct ScanParams {
     int wts_are_logits;
     int accumulate;
     int dtype;   // storage type of x, lam, out
-    int wdtype;  // storage type of wts (dtype, or kF32 for weights normalised beforehand)
+    int wdtype;  // format of wts: dtype, or for weights normalised beforehand kF32 / kPairF16
 };
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
@@ -57,6 +62,11 @@ hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
                             const void* logits, void* w_out, int dtype, hipStream_t stream,
                             int out_dtype = -1);
+
+// Channel-shared logits of one direction ([n][1][3][S][L]) into packed half
+// pairs [n][S][L] (WPair format).
+hipError_t launch_normalize_pair(int dir, int64_t n, int64_t h, int64_t w, const void* logits, void* w_out,
+                                 int dtype, hipStream_t stream);
 
 hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
                          int64_t numel, int dtype, hipStream_t stream);

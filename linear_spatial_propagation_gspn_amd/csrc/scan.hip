@@ -1,7 +1,7 @@
 // scan.hip -- launch configuration of the line-scan kernels (the kernels and
 // their launch families live in scan_kernel.hpp, instantiated per storage type
-// and direction family in scan_{f32,bf16}_{vert,horiz}.hip and
-// scan4_{f32,bf16}.hip).
+// and direction family in scan_{f32,bf16,bf16pair}_{vert,horiz}.hip and
+// scan4_{f32,bf16,bf16pair}.hip).
 #include "scan_kernel.hpp"
 #include "scan_lp.hpp"
 
@@ -15,20 +15,20 @@ extern template hipError_t launch_family<bf16_t, bf16_t, false>(const ScanConfig
                                                                 int64_t, int, hipStream_t);
 extern template hipError_t launch_family<bf16_t, bf16_t, true>(const ScanConfig&, bool, bool, const ScanK&,
                                                                int64_t, int, hipStream_t);
-extern template hipError_t launch_family<bf16_t, float, false>(const ScanConfig&, bool, bool, const ScanK&,
+extern template hipError_t launch_family<bf16_t, WPair, false>(const ScanConfig&, bool, bool, const ScanK&,
                                                                int64_t, int, hipStream_t);
-extern template hipError_t launch_family<bf16_t, float, true>(const ScanConfig&, bool, bool, const ScanK&,
+extern template hipError_t launch_family<bf16_t, WPair, true>(const ScanConfig&, bool, bool, const ScanK&,
                                                               int64_t, int, hipStream_t);
 extern template hipError_t launch_fused4<float, float>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4<bf16_t, bf16_t>(const Scan4K&, int, int, int, hipStream_t);
-extern template hipError_t launch_fused4<bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4<bf16_t, WPair>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4v<float, float>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4v<bf16_t, bf16_t>(const Scan4K&, int, int, int, hipStream_t);
-extern template hipError_t launch_fused4v<bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4v<bf16_t, WPair>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4lp<float, float, true>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<float, float, false>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true>(const Scan4K&, int, hipStream_t);
-extern template hipError_t launch_fused4lp<bf16_t, float, false>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4lp<bf16_t, WPair, false>(const Scan4K&, int, hipStream_t);
 
 namespace {
 
@@ -106,9 +106,9 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
         return horiz ? launch_family<float, float, true>(cfg, rev, acc, k, nblocks, nthreads, stream)
                      : launch_family<float, float, false>(cfg, rev, acc, k, nblocks, nthreads, stream);
     }
-    if (p.wdtype == kF32) {
-        return horiz ? launch_family<bf16_t, float, true>(cfg, rev, acc, k, nblocks, nthreads, stream)
-                     : launch_family<bf16_t, float, false>(cfg, rev, acc, k, nblocks, nthreads, stream);
+    if (p.wdtype == kPairF16) {
+        return horiz ? launch_family<bf16_t, WPair, true>(cfg, rev, acc, k, nblocks, nthreads, stream)
+                     : launch_family<bf16_t, WPair, false>(cfg, rev, acc, k, nblocks, nthreads, stream);
     }
     return horiz ? launch_family<bf16_t, bf16_t, true>(cfg, rev, acc, k, nblocks, nthreads, stream)
                  : launch_family<bf16_t, bf16_t, false>(cfg, rev, acc, k, nblocks, nthreads, stream);
@@ -132,20 +132,16 @@ hipError_t launch_scan4(const ScanParams (&p)[4], hipStream_t stream) {
     const int lh = lanes_for(Lh, ph);
     const int nthreads = lv > lh ? lv : lh;
     if (p[0].dtype == kF32) return launch_fused4<float, float>(k, pv, ph, nthreads, stream);
-    if (p[0].wdtype == kF32) return launch_fused4<bf16_t, float>(k, pv, ph, nthreads, stream);
+    if (p[0].wdtype == kPairF16) return launch_fused4<bf16_t, WPair>(k, pv, ph, nthreads, stream);
     return launch_fused4<bf16_t, bf16_t>(k, pv, ph, nthreads, stream);
 }
 
-#ifndef GSPN_LP_MAX_BLOCKS
-#define GSPN_LP_MAX_BLOCKS 256
-#endif
-
-// The long-line kernel (scan_lp.hpp) serves launches of at most
-// GSPN_LP_MAX_BLOCKS lines (each then has a compute unit to itself, and the
-// step latency decides the time) whose lines split into whole 16-byte
-// vectors on at most lp::kMaxLanes lanes, with 16-byte aligned tensors.
-bool lp_eligible(const ScanParams (&p)[4], int64_t blocks) {
-    if (blocks > GSPN_LP_MAX_BLOCKS) return false;
+// The long-line kernel (scan_lp.hpp) serves every launch whose lines split
+// into whole 16-byte vectors on at most lp::kMaxLanes lanes, with 16-byte
+// aligned tensors: its per-step work is a fraction of the one-position-per-
+// lane kernel's, which matters most when few lines run (the step latency
+// decides the time) and still pays when the GPU is full.
+bool lp_eligible(const ScanParams (&p)[4]) {
     const int esz = p[0].dtype == kF32 ? 4 : 2;
     const int P = 16 / esz;
     for (int d = 0; d < 4; ++d) {
@@ -163,12 +159,7 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
     // length, p[2..3] another
     const int l01 = static_cast<int>(p[0].w);
     const int l23 = static_cast<int>(p[2].w);
-    int64_t total = 0;
-    for (int d = 0; d < 4; ++d) {
-        const int64_t K = p[d].chunk;
-        total += p[d].n * p[d].c * ((p[d].h + K - 1) / K);
-    }
-    if (lp_eligible(p, total)) {
+    if (lp_eligible(p)) {
         const int P = p[0].dtype == kF32 ? 4 : 8;
         Scan4K k;
         for (int d = 0; d < 4; ++d) {
@@ -186,7 +177,7 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
             return logits ? launch_fused4lp<float, float, true>(k, nthreads, stream)
                           : launch_fused4lp<float, float, false>(k, nthreads, stream);
         }
-        if (p[0].wdtype == kF32) return launch_fused4lp<bf16_t, float, false>(k, nthreads, stream);
+        if (p[0].wdtype == kPairF16) return launch_fused4lp<bf16_t, WPair, false>(k, nthreads, stream);
         return launch_fused4lp<bf16_t, bf16_t, true>(k, nthreads, stream);
     }
     if (kind) *kind = 2;
@@ -203,7 +194,7 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
     const int b = lanes_for(l23, ph);
     const int nthreads = a > b ? a : b;
     if (p[0].dtype == kF32) return launch_fused4v<float, float>(k, pv, ph, nthreads, stream);
-    if (p[0].wdtype == kF32) return launch_fused4v<bf16_t, float>(k, pv, ph, nthreads, stream);
+    if (p[0].wdtype == kPairF16) return launch_fused4v<bf16_t, WPair>(k, pv, ph, nthreads, stream);
     return launch_fused4v<bf16_t, bf16_t>(k, pv, ph, nthreads, stream);
 }
 

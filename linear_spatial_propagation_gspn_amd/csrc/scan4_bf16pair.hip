@@ -1,0 +1,11 @@
+// scan4_bf16pair.hip -- instantiates the four-scans-in-one-launch kernels for bf16 storage with channel-shared weights pre-normalised as packed half pairs.
+#include "scan_kernel.hpp"
+#include "scan_lp.hpp"
+
+namespace gspn {
+
+template hipError_t launch_fused4<bf16_t, WPair>(const Scan4K&, int, int, int, hipStream_t);
+template hipError_t launch_fused4v<bf16_t, WPair>(const Scan4K&, int, int, int, hipStream_t);
+template hipError_t launch_fused4lp<bf16_t, WPair, false>(const Scan4K&, int, hipStream_t);
+
+}  // namespace gspn

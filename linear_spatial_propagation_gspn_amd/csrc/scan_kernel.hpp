@@ -65,7 +65,8 @@ using IC = std::integral_constant<int, V>;
 
 // One line scan: plane p, chunk q of the direction described by a.
 // T: storage type of x, lambda and the output; TW: storage type of the
-// logits / weights (the same as T, or fp32 weights normalised beforehand).
+// logits / weights (the same as T, fp32 weights normalised beforehand, or
+// WPair: channel-shared weights normalised beforehand as packed half pairs).
 // P: positions per lane.  U: steps per prefetch sub-block.  UT: steps per
 // tile (a multiple of U; the horizontal tile width).  HORIZ / REV: direction.
 // ACC: add into the output instead of overwriting it.
@@ -92,15 +93,17 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
 
     const T* __restrict__ xp = static_cast<const T*>(a.x) + p * plane;
     const T* __restrict__ lp = static_cast<const T*>(a.lam) + p * plane;
-    const TW* __restrict__ zp =
-        static_cast<const TW*>(a.wts) + (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane;
+    constexpr bool PAIR = std::is_same_v<TW, WPair>;
+    using ZT = std::conditional_t<PAIR, uint32_t, TW>;
+    const ZT* __restrict__ zp =
+        static_cast<const ZT*>(a.wts) + (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane);
     T* __restrict__ op = static_cast<T*>(a.out) + p * plane;
 
     const int k0 = tid * P;
     const int t0 = q * a.K;
     const int t1 = min(t0 + a.K, S);
     const bool rev = HORIZ ? REV : (a.reverse != 0);
-    const bool logits = a.logits != 0;
+    const bool logits = !PAIR && a.logits != 0;
 
     // Positions of this lane, clamped into the line for addressing.
     int kk[P];
@@ -112,7 +115,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
     }
 
     // Double-buffered per-step inputs: [buffer][step of the sub-block].
-    float rz[2][U][3][P];
+    float rz[2][U][PAIR ? 1 : 3][P];
     float rl[2][U][P];
     float rx[HORIZ ? 1 : 2][U][P];
     float ry[(!HORIZ && ACC) ? 2 : 1][U][P];
@@ -131,8 +134,12 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
             const int64_t lo = static_cast<int64_t>(line_of(min(tb + s, t1 - 1))) * L;
 #pragma unroll
             for (int j = 0; j < P; ++j) {
+                if constexpr (PAIR) {
+                    rz[R][s][0][j] = __uint_as_float(zp[lo + kk[j]]);
+                } else {
 #pragma unroll
-                for (int o = 0; o < 3; ++o) rz[R][s][o][j] = Store<TW>::ld(zp + o * plane + lo + kk[j]);
+                    for (int o = 0; o < 3; ++o) rz[R][s][o][j] = Store<TW>::ld(zp + o * plane + lo + kk[j]);
+                }
                 rl[R][s][j] = Store<T>::ld(lp + lo + kk[j]);
                 if constexpr (!HORIZ) {
                     rx[R][s][j] = Store<T>::ld(xp + lo + kk[j]);
@@ -262,7 +269,12 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
                         const bool has_l = k0 + j > 0;
                         const bool has_r = k0 + j + 1 < L;
                         float w0, w1, w2;
-                        if (logits) {
+                        if constexpr (PAIR) {
+                            const uint32_t b = __float_as_uint(rz[R][s][0][j]);
+                            w0 = has_l ? pair_lo(b) : 0.0f;
+                            w2 = has_r ? pair_hi(b) : 0.0f;
+                            w1 = (1.0f - w0) - w2;
+                        } else if (logits) {
                             normalise_row(rz[R][s][0][j], rz[R][s][1][j], rz[R][s][2][j], has_l, has_r, w0,
                                           w1, w2);
                         } else {

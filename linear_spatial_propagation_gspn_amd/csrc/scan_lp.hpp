@@ -81,13 +81,17 @@ __device__ __forceinline__ float shift_from_upper_lane(float v) {  // lane i get
 }  // namespace lp
 
 // One (plane, chunk) line of a vertical-form scan.  T: storage of x, lambda
-// and the output; TW: storage of the weights; LOGITS: the weights are logits
-// normalised here (else normalised weights, zero outside the line).
+// and the output; TW: storage of the weights (WPair: packed half pairs of
+// channel-shared weights); LOGITS: the weights are logits normalised here
+// (else normalised weights, zero outside the line).
 template <typename T, typename TW, bool LOGITS>
 __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     constexpr int P = 16 / static_cast<int>(sizeof(T));              // positions per lane
     constexpr int WT = P * static_cast<int>(sizeof(T)) / 4;          // words per lane: x, lambda, out
-    constexpr int WW = P * static_cast<int>(sizeof(TW)) / 4;         // words per lane: one weight row
+    constexpr bool PAIR = std::is_same_v<TW, WPair>;
+    constexpr int ZB = PAIR ? 4 : static_cast<int>(sizeof(TW));      // weight bytes per position and row
+    constexpr int NZ = PAIR ? 1 : 3;                                  // weight rows
+    constexpr int WW = P * ZB / 4;                                    // words per lane: one weight row
     constexpr int D = GSPN_LP_DEPTH;                                  // steps in flight
     __shared__ float edges[2][lp::kMaxWaves][2];
 
@@ -104,17 +108,18 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     const auto rx = lp::rsrc(static_cast<const T*>(a.x) + p * plane, plane * sizeof(T));
     const auto rl = lp::rsrc(static_cast<const T*>(a.lam) + p * plane, plane * sizeof(T));
     const auto ro = lp::rsrc(static_cast<T*>(a.out) + p * plane, plane * sizeof(T));
-    const auto rz = lp::rsrc(static_cast<const TW*>(a.wts) + (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane,
-                             3 * plane * sizeof(TW));
+    const auto rz = lp::rsrc(static_cast<const char*>(a.wts) +
+                                 (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane) * ZB,
+                             NZ * plane * ZB);
 
     const int k0 = tid * P;
     const bool active = k0 < L;
     const int k0c = active ? k0 : L - P;  // lanes past the line read its last vector (unused)
     const uint32_t vt = static_cast<uint32_t>(k0c) * sizeof(T);
-    const uint32_t vw = static_cast<uint32_t>(k0c) * sizeof(TW);
+    const uint32_t vw = static_cast<uint32_t>(k0c) * ZB;
     const uint32_t rowT = static_cast<uint32_t>(L) * sizeof(T);
-    const uint32_t rowW = static_cast<uint32_t>(L) * sizeof(TW);
-    const uint32_t planeW = static_cast<uint32_t>(plane) * sizeof(TW);
+    const uint32_t rowW = static_cast<uint32_t>(L) * ZB;
+    const uint32_t planeW = static_cast<uint32_t>(plane) * ZB;
     const bool has_l0 = k0 > 0;       // the lane's first position has a left neighbour
     const bool has_rP = k0 + P < L;   // the lane's last position has a right neighbour
 
@@ -123,14 +128,14 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     const bool rev = a.reverse != 0;
     auto line_of = [&](int t) { return static_cast<uint32_t>(rev ? S - 1 - t : t); };
 
-    uint32_t sx[D][WT], sl[D][WT], sz[D][3][WW];
+    uint32_t sx[D][WT], sl[D][WT], sz[D][NZ][WW];
     auto fill = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
         const uint32_t i = line_of(min(t, t1 - 1));
         lp::load_words<WT>(sx[s], rx, vt, i * rowT);
         lp::load_words<WT>(sl[s], rl, vt, i * rowT);
 #pragma unroll
-        for (int o = 0; o < 3; ++o) lp::load_words<WW>(sz[s][o], rz, vw, o * planeW + i * rowW);
+        for (int o = 0; o < NZ; ++o) lp::load_words<WW>(sz[s][o], rz, vw, o * planeW + i * rowW);
     };
 
     float h[P];
@@ -154,17 +159,24 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
             float w[3][P];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                const float z0 = lp::elem<TW, WW>(sz[s][0], j);
-                const float z1 = lp::elem<TW, WW>(sz[s][1], j);
-                const float z2 = lp::elem<TW, WW>(sz[s][2], j);
-                if constexpr (LOGITS) {
-                    const bool hl = j > 0 || has_l0;
-                    const bool hr = j < P - 1 || has_rP;
-                    normalise_row(z0, z1, z2, hl, hr, w[0][j], w[1][j], w[2][j]);
+                if constexpr (PAIR) {
+                    // missing neighbours were stored as exact zeros
+                    w[0][j] = pair_lo(sz[s][0][j]);
+                    w[2][j] = pair_hi(sz[s][0][j]);
+                    w[1][j] = (1.0f - w[0][j]) - w[2][j];
                 } else {
-                    w[0][j] = z0;
-                    w[1][j] = z1;
-                    w[2][j] = z2;
+                    const float z0 = lp::elem<TW, WW>(sz[s][0], j);
+                    const float z1 = lp::elem<TW, WW>(sz[s][NZ > 1 ? 1 : 0], j);
+                    const float z2 = lp::elem<TW, WW>(sz[s][NZ > 2 ? 2 : 0], j);
+                    if constexpr (LOGITS) {
+                        const bool hl = j > 0 || has_l0;
+                        const bool hr = j < P - 1 || has_rP;
+                        normalise_row(z0, z1, z2, hl, hr, w[0][j], w[1][j], w[2][j]);
+                    } else {
+                        w[0][j] = z0;
+                        w[1][j] = z1;
+                        w[2][j] = z2;
+                    }
                 }
             }
             // neighbours from the previous step: inside the wave by DPP, across

@@ -94,7 +94,8 @@ def test_forward4_validation(lib):
     assert wsb == 4 * 2 * 64 * 4
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 1) == 4 * 2 * 64 * 2
     # channel-shared weights add the four directions' fp32 weights
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1) == 4 * 2 * 64 * 2 + 4 * 3 * 64 * 4
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 0) == 4 * 2 * 64 * 4 + 4 * 3 * 64 * 4  # fp32 triples
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1) == 4 * 2 * 64 * 2 + 4 * 64 * 4      # half pairs
     assert lib.gspn_forward4_workspace_bytes(1, 1, 8, 8, 1, 0) == 4 * 64 * 4
     assert lib.gspn_forward4_workspace_bytes(1, -2, 8, 8, 2, 0) == -1
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1

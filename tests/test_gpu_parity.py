@@ -184,6 +184,28 @@ def test_scan4_outputs(shape, chunk, dtype):
         assert _err(outs[d], ref) <= TOL[dtype], d
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [0, 7])
+@pytest.mark.parametrize("shape", [
+    (1, 3, 40, 72),     # long-line kernel
+    (2, 4, 40, 70),     # one workgroup per line (70 is not a whole number of vectors)
+    (1, 2, 30, 2100),   # lines longer than the fused launch takes: one launch per direction
+    (2, 3, 50, 60),     # plane-resident kernel (logits normalised per channel)
+])
+def test_forward4_shared_weights(shape, chunk, dtype):
+    """Channel-shared logits over several channels: normalised once per
+    direction into fp32 triples (fp32 storage) or packed half pairs (bf16)."""
+    n, c, h, w = shape
+    wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=True, chunk=chunk, seed=41 + w)
+    _say("forward4 shared %s chunk=%d %s" % (shape, chunk, dtype))
+    inp = make_inputs(wl, DEV)
+    got = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk,
+                          workspace=G.forward4_workspace(inp["x"], wl.cw))
+    torch.cuda.synchronize()
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk)
+    assert _err(got, ref) <= TOL[dtype]
+
+
 def test_forward4_closed_form_constant_input():
     # lambda = 1, x = c: every direction's h at scan step t is (t+1) c, so the
     # merged output is (H + W + 2) c everywhere, whatever the logits.
@@ -224,8 +246,10 @@ def test_deterministic():
     ((1, 3, 40, 72), True, "scan4lp_kernel", {"transpose": 1, "scan": 1, "combine": 1, "normalize": 4}),
     # few planes, lines not a whole number of vectors: one workgroup per line
     ((1, 2, 40, 70), False, "scan4v_kernel", {"transpose": 1, "scan": 1, "combine": 1, "normalize": 0}),
-    # many planes: one launch per direction
-    ((8, 80, 8, 72), False, "scan_kernel", {"transpose": 1, "scan": 4, "combine": 1, "normalize": 0}),
+    # many planes: still one fused launch
+    ((8, 80, 8, 72), False, "scan4lp_kernel", {"transpose": 1, "scan": 1, "combine": 1, "normalize": 0}),
+    # lines longer than the fused launch takes: one launch per direction
+    ((1, 1, 40, 2100), False, "scan_kernel", {"transpose": 1, "scan": 4, "combine": 1, "normalize": 0}),
 ])
 def test_forward4_timed_matches_untimed(shape, shared, kernel, expect):
     n, c, h, w = shape
