@@ -3,11 +3,12 @@
 //   out[n][o][p] = sum_c weight[o][c] * in[n][c][p]   (no bias, fp32 accumulate)
 //
 // bf16 storage runs on the matrix cores (gfx950 bf16 MFMA, fp32 accumulate):
-//  - narrow output (c_out <= 16, e.g. C -> C_proxy): v_mfma_f32_16x16x32_bf16
-//    with M = output channels, N = 16 pixels, K = 32 input channels per
-//    instruction.  A wave covers 64 pixels: each lane loads 4 pixels of 8
-//    input channels with 8-byte loads (16 lanes make one 128-byte run of a
-//    channel row) and feeds four MFMAs, one per pixel of its quad.
+//  - narrow output (c_out <= 16, c_in % 8 == 0, e.g. C -> C_proxy):
+//    v_mfma_f32_16x16x32_bf16 with M = output channels, N = 16 pixels, K = 32
+//    input channels per instruction.  A wave covers 64 pixels: each lane
+//    loads 4 pixels of 8 input channels with 8-byte loads (16 lanes make one
+//    128-byte run of a channel row) and its 8 weights with one 16-byte load,
+//    and feeds four MFMAs, one per pixel of its quad.
 //  - narrow input (c_in <= 8, e.g. C_proxy -> C): v_mfma_f32_32x32x8_bf16
 //    with M = 32 output channels, N = 32 pixels, K = 8.  A wave covers 64
 //    pixels as even / odd halves, so each lane ends with two adjacent pixels
@@ -34,8 +35,16 @@ __device__ __forceinline__ __bf16 as_bf(uint32_t bits16) {
     return __builtin_bit_cast(__bf16, static_cast<uint16_t>(bits16));
 }
 
-// Narrow output: c_out <= 16.  Requires hw % 64 == 0 and 8-byte aligned rows.
-__global__ __launch_bounds__(256) void project_narrow_out_mfma(const bf16_t* __restrict__ in,
+// Narrow output: c_out <= 16.  Requires hw % 64 == 0, c_in % 8 == 0, 8-byte
+// aligned rows and a 16-byte aligned weight matrix.  Each 32-channel block's
+// loads are issued before the previous block's MFMAs (double buffer); channel
+// indices past c_in are clamped into the tensor and their values replaced by
+// zeros, so no load sits behind a branch.
+#ifndef GSPN_PROJ_THREADS
+#define GSPN_PROJ_THREADS 512
+#endif
+
+__global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(const bf16_t* __restrict__ in,
                                                                const bf16_t* __restrict__ wt,
                                                                bf16_t* __restrict__ out, int64_t waves,
                                                                int64_t hw, int cin, int cout) {
@@ -48,32 +57,55 @@ __global__ __launch_bounds__(256) void project_narrow_out_mfma(const bf16_t* __r
     const int q = lane & 15;  // pixel quad: pixels px0 + 4q .. +3; output row of A
     const int g = lane >> 4;  // k-group: channels 8g .. 8g+7 of each 32-channel step
     const bf16_t* src = in + ni * cin * hw + px0 + 4 * q;
+    const bf16_t* wrow = wt + static_cast<int64_t>(q < cout ? q : cout - 1) * cin;
+    const bool qok = q < cout;
+
+    struct Block {
+        uint4 a;     // 8 weights (bf16) of output row q
+        uint2 v[8];  // 4 pixels of 8 channels
+        bool ok;     // the channels exist
+    };
+    auto fetch = [&](int k0, Block& b) {
+        const int c0 = k0 + 8 * g;
+        b.ok = c0 < cin;
+        const int cc = b.ok ? c0 : cin - 8;  // clamped into the tensor (cin % 8 == 0)
+        b.a = *reinterpret_cast<const uint4*>(wrow + cc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b.v[e] = *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(cc + e) * hw);
+    };
 
     floatx4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    for (int k0 = 0; k0 < cin; k0 += 32) {
+    auto consume = [&](const Block& b) {
+        const bool use = b.ok && qok;
+        const uint32_t aw[4] = {use ? b.a.x : 0u, use ? b.a.y : 0u, use ? b.a.z : 0u, use ? b.a.w : 0u};
         bf16x8 a;
-        uint2 v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = k0 + 8 * g + e;
-            const bool ok = c < cin;
-            a[e] = as_bf((q < cout && ok) ? wt[q * cin + c] : 0);
-            v[e] = ok ? *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(c) * hw) : make_uint2(0, 0);
-        }
+        for (int e = 0; e < 8; ++e) a[e] = as_bf((e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xffffu));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bf16x8 b;
+            bf16x8 bv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t word = (j < 2) ? v[e].x : v[e].y;
-                b[e] = as_bf((j & 1) ? (word >> 16) : (word & 0xffffu));
+                const uint32_t word = b.ok ? ((j < 2) ? b.v[e].x : b.v[e].y) : 0u;
+                bv[e] = as_bf((j & 1) ? (word >> 16) : (word & 0xffffu));
             }
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[j], 0, 0, 0);
         }
+    };
+
+    Block b0, b1;
+    fetch(0, b0);
+    int k0 = 0;
+    for (; k0 + 32 < cin; k0 += 64) {
+        fetch(k0 + 32, b1);
+        consume(b0);
+        fetch(k0 + 64, b0);  // past c_in it reads clamped channels and yields zeros
+        consume(b1);
     }
+    if (k0 < cin) consume(b0);
+
     // lane holds output rows (l/16)*4 + i for pixels px0 + 4q + j
     bf16_t* dst = out + ni * cout * hw + px0 + 4 * q;
 #pragma unroll
@@ -107,7 +139,8 @@ __global__ __launch_bounds__(256) void project_narrow_in_mfma(const bf16_t* __re
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int c = 4 * g + e;
-        const uint32_t word = c < cin ? *reinterpret_cast<const uint32_t*>(src + static_cast<int64_t>(c) * hw) : 0u;
+        const uint32_t raw = *reinterpret_cast<const uint32_t*>(src + static_cast<int64_t>(c < cin ? c : cin - 1) * hw);
+        const uint32_t word = c < cin ? raw : 0u;
         b_even[e] = static_cast<short>(word & 0xffffu);
         b_odd[e] = static_cast<short>(word >> 16);
     }
@@ -115,10 +148,12 @@ __global__ __launch_bounds__(256) void project_narrow_in_mfma(const bf16_t* __re
     for (int o0 = 0; o0 < cout; o0 += 32) {
         short4v a;
         const int orow = o0 + n;
+        const int oc = orow < cout ? orow : cout - 1;  // clamped: loads stay unguarded
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = 4 * g + e;
-            a[e] = static_cast<short>((orow < cout && c < cin) ? wt[orow * cin + c] : 0);
+            const bf16_t v = wt[oc * cin + (c < cin ? c : cin - 1)];
+            a[e] = static_cast<short>((orow < cout && c < cin) ? v : 0);
         }
         floatx16 ce = {}, co = {};
         ce = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b_even, ce, 0, 0, 0);
@@ -178,8 +213,10 @@ hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, co
     if (dtype == kBF16 && hw % 64 == 0 && c_in <= 1 << 20 && c_out <= 1 << 20) {
         const int64_t waves = n * (hw / 64);
         const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
-        if (c_out <= 16 && aligned_to(in, 8) && aligned_to(out, 8)) {
-            hipLaunchKernelGGL(project_narrow_out_mfma, grid, dim3(256), 0, stream,
+        if (c_out <= 16 && c_in % 8 == 0 && aligned_to(in, 8) && aligned_to(out, 8) && aligned_to(weight, 16)) {
+            constexpr int per = GSPN_PROJ_THREADS / 64;
+            const dim3 g2(static_cast<unsigned>((waves + per - 1) / per));
+            hipLaunchKernelGGL(project_narrow_out_mfma, g2, dim3(GSPN_PROJ_THREADS), 0, stream,
                                static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
                                static_cast<bf16_t*>(out), waves, hw, static_cast<int>(c_in),
                                static_cast<int>(c_out));
