@@ -12,8 +12,10 @@ it.  Each wrapper cites the passage of the GSPN pages it follows; the C file
 holds the full list of readings taken where the pages are silent.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-(closed forms, brute-force dense matrices, exact rational arithmetic,
-symmetry invariants and library routines); none is "parity unpinned".
+and ``tests/test_oracle_backward_pins.py`` (closed forms, brute-force dense
+matrices, exact rational arithmetic, symmetry invariants, library routines,
+and for the gradients central finite differences of the pinned forward and
+adjoint dot-product identities); none is "parity unpinned".
 
 Layouts (contiguous, row-major):
   x, y, h           [N][C][H][W]
@@ -73,6 +75,12 @@ def _lib():
             for f in (lib.oracle_normalize, lib.oracle_scan, lib.oracle_forward4,
                       lib.oracle_project):
                 f.restype = ctypes.c_int
+            lib.oracle_scan_backward.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, dp, dp, dp, dp,
+                                                 dp, dp, dp]
+            lib.oracle_scan_backward.restype = ctypes.c_int
+            lib.oracle_backward4.argtypes = [i64, i64, i64, i64, i64, i64, dp, ctypes.POINTER(dp),
+                                             ctypes.POINTER(dp), dp, dp, ctypes.POINTER(dp), ctypes.POINTER(dp)]
+            lib.oracle_backward4.restype = ctypes.c_int
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = ctypes.c_int
             _handle = lib
@@ -187,6 +195,56 @@ def proxy_forward4(x, w_down, w_up, logits: Sequence, lams: Sequence, chunk: int
     xp = project(x, w_down)
     yp = forward4(xp, logits, lams, chunk)
     return project(yp, w_up)
+
+
+def scan_backward(direction: int, x, logits, lam, gy, chunk: int = 0):
+    """Gradient of one direction's scan (the exact derivative of ``scan``):
+    returns (dx, dlam, dlogits) for dL/dh = gy.  x, gy [N][C][H][W];
+    logits [N][Cw][3][S][L]; lam [N][C][S][L].  Channel-shared logits get
+    the sum over channels."""
+    xx = _f64(x)
+    n, c, h, w = xx.shape
+    S, L = frame_shape(direction, h, w)
+    zz = _f64(logits)
+    ll = _f64(lam)
+    gg = _f64(gy)
+    cw = zz.shape[1]
+    if zz.shape != (n, cw, 3, S, L) or ll.shape != (n, c, S, L) or gg.shape != xx.shape:
+        raise ValueError("shapes do not fit x for direction %s" % DIRECTIONS[direction])
+    dx = np.zeros_like(xx)
+    dl = np.empty_like(ll)
+    dz = np.zeros_like(zz)
+    rc = _lib().oracle_scan_backward(direction, int(chunk), n, c, h, w, cw, _ptr(xx), _ptr(zz), _ptr(ll),
+                                     _ptr(gg), _ptr(dx), _ptr(dl), _ptr(dz))
+    if rc != 0:
+        raise ValueError("oracle_scan_backward rejected its arguments")
+    return dx, dl, dz
+
+
+def backward4(x, logits: Sequence, lams: Sequence, gy, chunk: int = 0):
+    """Gradient of forward4 for dL/dy = gy: (dx, [dlam_d], [dlogits_d])."""
+    xx = _f64(x)
+    n, c, h, w = xx.shape
+    zs = [_f64(z) for z in logits]
+    ls = [_f64(l) for l in lams]
+    gg = _f64(gy)
+    cw = zs[0].shape[1]
+    for d in range(4):
+        S, L = frame_shape(d, h, w)
+        if zs[d].shape != (n, cw, 3, S, L) or ls[d].shape != (n, c, S, L):
+            raise ValueError("direction %s tensors do not fit x" % DIRECTIONS[d])
+    if gg.shape != xx.shape:
+        raise ValueError("gy does not fit x")
+    dx = np.empty_like(xx)
+    dls = [np.empty_like(l) for l in ls]
+    dzs = [np.empty_like(z) for z in zs]
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _lib().oracle_backward4(n, c, h, w, cw, int(chunk), _ptr(xx), (dp * 4)(*[_ptr(z) for z in zs]),
+                                 (dp * 4)(*[_ptr(l) for l in ls]), _ptr(gg), _ptr(dx),
+                                 (dp * 4)(*[_ptr(a) for a in dls]), (dp * 4)(*[_ptr(a) for a in dzs]))
+    if rc != 0:
+        raise ValueError("oracle_backward4 rejected its arguments")
+    return dx, dls, dzs
 
 
 def max_threads() -> int:

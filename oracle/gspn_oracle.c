@@ -49,6 +49,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <omp.h>
 
@@ -220,6 +221,168 @@ int oracle_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int6
     for (int64_t e = 0; e < total; ++e) y[e] = 0.0;
     for (int d = 0; d < 4; ++d) {
         int rc = oracle_scan(d, chunk, n, c, h, w, cw, x, logits[d], 1, lam[d], y, 1);
+        if (rc != ORACLE_OK) return rc;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Backward pass: the exact gradient of the scan above.  The pages define only
+ * the forward propagation (GSPN-2 notes, "2D spatial propagation recap") and
+ * list forward/backward runtime among the measured quantities (GSPN-2
+ * summary page, "Experimental setup"); the gradient is the derivative of
+ * that definition, written out step by step:
+ *
+ *   forward, in scan order t (line i = t or S-1-t):
+ *     h_t = M_t h_{t-1} + u_t,   u_t[k] = lambda_t[k] x_t[k],
+ *     (M_t v)[k] = sum_o w_t[k,o] v[k+o],   M_t = 0 at the first step of a chunk
+ *   with g_t = dL/dh_t coming from y (y = sum of the four h), the adjoint runs
+ *   backwards in t:
+ *     a_t = g_t + M_{t+1}^T a_{t+1}   (no M_{t+1} term past the chunk's end),
+ *     (M^T v)[k] = sum_o w[k-o, o] v[k-o]
+ *   and
+ *     d lambda_t[k] = a_t[k] x_t[k],      dx_t[k] += a_t[k] lambda_t[k],
+ *     dw_t[k,o]     = a_t[k] h_{t-1}[k+o] (existing neighbours, not at a chunk start),
+ *     dz_t[k,q]     = sum_o dw_t[k,o] d w_t[k,o] / d z_t[k,q]
+ *                   = w_q (1 - s_q) (dw_q - sum_o dw_o w_o)   for existing q, else 0,
+ *   with s_q = sigmoid(z_q) and w_q = s_q / sum_existing s (the derivative of
+ *   the row normalisation).  Channel-shared logits receive the sum over
+ *   channels.
+ *
+ * oracle_scan_backward: one direction.  gy [n][c][h][w] (array frame) is
+ * dL/dy; dx (array frame) is accumulated (+=); dlam [n][c][S][L] is written;
+ * dlogits [n][cw][3][S][L] is accumulated (+=).  Planes run in parallel only
+ * for per-channel logits (shared logits are summed over channels in order).
+ */
+int oracle_scan_backward(int dir, int64_t chunk, int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                         const double* x, const double* logits, const double* lam, const double* gy,
+                         double* dx, double* dlam, double* dlogits) {
+    if (dir < 0 || dir > 3 || chunk < 0 || n < 0 || c < 0 || h < 0 || w < 0) return ORACLE_BAD_ARG;
+    if (!(cw == 1 || cw == c)) return ORACLE_BAD_ARG;
+    if (!x || !logits || !lam || !gy || !dx || !dlam || !dlogits) return ORACLE_BAD_ARG;
+    int64_t S, L;
+    frame_sizes(dir, h, w, &S, &L);
+    const int64_t plane = S * L;
+    const int horizontal = dir_is_horizontal(dir);
+    const int reversed = dir_is_reversed(dir);
+    const int64_t K = (chunk == 0 || chunk >= S) ? S : chunk;
+    const int64_t nplanes = n * c;
+    const int shared = (cw == 1 && c > 1);
+
+#pragma omp parallel for schedule(dynamic, 1) if (!shared)
+    for (int64_t p = 0; p < nplanes; ++p) {
+        const int64_t ni = p / (c > 0 ? c : 1);
+        const int64_t ci = p % (c > 0 ? c : 1);
+        const int64_t wplane = ni * cw + (cw == 1 ? 0 : ci);
+        const double* xp = x + p * plane;
+        const double* zp = logits + wplane * 3 * plane;
+        const double* lp = lam + p * plane;
+        const double* gp = gy + p * plane;
+        double* dxp = dx + p * plane;
+        double* dlp = dlam + p * plane;
+        double* dzp = dlogits + wplane * 3 * plane;
+
+        /* forward states of every step, h[t][k], and the weights w[t][k][o] */
+        double* hs = (double*)calloc((size_t)(plane > 0 ? plane : 1), sizeof(double));
+        double* ws = (double*)calloc((size_t)(3 * plane > 0 ? 3 * plane : 1), sizeof(double));
+        double* ss = (double*)calloc((size_t)(3 * plane > 0 ? 3 * plane : 1), sizeof(double));
+        double* anext = (double*)calloc((size_t)(L > 0 ? L : 1), sizeof(double));
+        double* acur = (double*)calloc((size_t)(L > 0 ? L : 1), sizeof(double));
+        for (int64_t t = 0; t < S; ++t) {
+            const int64_t i = reversed ? (S - 1 - t) : t;
+            for (int64_t k = 0; k < L; ++k) {
+                double z[3], ww[3];
+                for (int o = 0; o < 3; ++o) z[o] = zp[o * plane + i * L + k];
+                normalise_row(z, k, L, ww);
+                for (int o = 0; o < 3; ++o) {
+                    const int64_t nb = k + (o - 1);
+                    ws[(t * L + k) * 3 + o] = ww[o];
+                    ss[(t * L + k) * 3 + o] = (nb >= 0 && nb < L) ? sigmoid(z[o]) : 0.0;
+                }
+            }
+        }
+        for (int64_t t = 0; t < S; ++t) {
+            const int64_t i = reversed ? (S - 1 - t) : t;
+            const int chunk_start = (t % K) == 0;
+            for (int64_t k = 0; k < L; ++k) {
+                const int64_t aidx = horizontal ? (k * w + i) : (i * w + k);
+                double acc = lp[i * L + k] * xp[aidx];
+                if (!chunk_start) {
+                    for (int o = 0; o < 3; ++o) {
+                        const int64_t nb = k + (o - 1);
+                        if (nb >= 0 && nb < L) acc += ws[(t * L + k) * 3 + o] * hs[(t - 1) * L + nb];
+                    }
+                }
+                hs[t * L + k] = acc;
+            }
+        }
+
+        /* adjoint, t = S-1 down to 0 */
+        for (int64_t k = 0; k < L; ++k) anext[k] = 0.0;
+        for (int64_t t = S - 1; t >= 0; --t) {
+            const int64_t i = reversed ? (S - 1 - t) : t;
+            const int next_in_chunk = (t + 1 < S) && ((t + 1) % K) != 0;
+            for (int64_t k = 0; k < L; ++k) {
+                const int64_t aidx = horizontal ? (k * w + i) : (i * w + k);
+                double a = gp[aidx];
+                if (next_in_chunk) {
+                    for (int o = 0; o < 3; ++o) {
+                        const int64_t m = k - (o - 1); /* row m of M_{t+1} reads position k with offset o */
+                        if (m >= 0 && m < L) a += ws[((t + 1) * L + m) * 3 + o] * anext[m];
+                    }
+                }
+                acur[k] = a;
+            }
+            const int chunk_start = (t % K) == 0;
+            for (int64_t k = 0; k < L; ++k) {
+                const int64_t aidx = horizontal ? (k * w + i) : (i * w + k);
+                const double a = acur[k];
+                dlp[i * L + k] = a * xp[aidx];
+                dxp[aidx] += a * lp[i * L + k];
+                if (!chunk_start) {
+                    double dw[3] = {0.0, 0.0, 0.0};
+                    double dot = 0.0;
+                    for (int o = 0; o < 3; ++o) {
+                        const int64_t nb = k + (o - 1);
+                        if (nb >= 0 && nb < L) dw[o] = a * hs[(t - 1) * L + nb];
+                        dot += dw[o] * ws[(t * L + k) * 3 + o];
+                    }
+                    for (int q = 0; q < 3; ++q) {
+                        const int64_t nb = k + (q - 1);
+                        if (nb < 0 || nb >= L) continue;
+                        const double wq = ws[(t * L + k) * 3 + q];
+                        const double sq = ss[(t * L + k) * 3 + q];
+                        dzp[q * plane + i * L + k] += wq * (1.0 - sq) * (dw[q] - dot);
+                    }
+                }
+            }
+            double* tmp = anext;
+            anext = acur;
+            acur = tmp;
+        }
+        free(hs);
+        free(ws);
+        free(ss);
+        free(anext);
+        free(acur);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * oracle_backward4: gradient of y = sum_d scan_d(x, logits[d], lam[d]) for
+ * dL/dy = gy: dx (written), dlam[d] (written), dlogits[d] (written).
+ */
+int oracle_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk,
+                     const double* x, const double* const* logits, const double* const* lam, const double* gy,
+                     double* dx, double* const* dlam, double* const* dlogits) {
+    if (!logits || !lam || !gy || !dx || !dlam || !dlogits) return ORACLE_BAD_ARG;
+    const int64_t total = n * c * h * w;
+    const int64_t ztotal = n * cw * 3 * h * w;
+    for (int64_t e = 0; e < total; ++e) dx[e] = 0.0;
+    for (int d = 0; d < 4; ++d) {
+        for (int64_t e = 0; e < ztotal; ++e) dlogits[d][e] = 0.0;
+        int rc = oracle_scan_backward(d, chunk, n, c, h, w, cw, x, logits[d], lam[d], gy, dx, dlam[d], dlogits[d]);
         if (rc != ORACLE_OK) return rc;
     }
     return ORACLE_OK;
