@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 3
+#define GSPN_ABI_VERSION 4
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -229,6 +229,41 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                 const void* const logits[4], const void* const lam[4], void* y,
                                 void* workspace, int64_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * gspn_backward4_workspace_bytes -- bytes of the gspn_backward4 workspace:
+ * the four directions' forward states in fp32 (4 * n*c*h*w floats), five
+ * maps of n*c*h*w elements of the storage type (x and dL/dy transposed into
+ * the horizontal scan frame, three per-direction dx terms) and, for
+ * channel-shared logits over more than one channel (cw == 1 < c), 4 * 3 *
+ * n*h*w floats of gradient sums.  Returns -1 for invalid arguments.
+ */
+int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype);
+
+/*
+ * gspn_backward4 -- gradients of the four-direction propagation of
+ * gspn_forward4 (same x, logits, lam, cw, chunk_len) for dL/dy = gy: the exact
+ * derivative of the scan that the GSPN-2 paper notes define in "2D spatial
+ * propagation recap" (the GSPN-2 summary page, "Experimental setup", reports
+ * forward and backward runtimes).  Per direction, in its scan frame, the
+ * adjoint a_t = g_t + M_{t+1}^T a_{t+1} runs against the scan order
+ * (restarting at chunk ends), and
+ *   dlam[d]      = a * x                      [n][c][S_d][L_d]   (written)
+ *   dx           = sum_d a_d * lam[d]          [n][c][h][w]       (written)
+ *   dlogits[d]   = d w / d z applied to a_t h_{t-1}   [n][cw][3][S_d][L_d]
+ *                  (written; 0 on each chunk's first line, whose logits the
+ *                  forward does not use; for cw == 1 < c the sum over
+ *                  channels, accumulated in fp32 in an order that may vary
+ *                  between calls).
+ * workspace: required, gspn_backward4_workspace_bytes() bytes, 4-byte
+ * aligned.  Outputs may overlap neither an input, the workspace nor each
+ * other.  Lines may hold at most 2048 positions (else GSPN_ERR_UNSUPPORTED).
+ * The forward states are recomputed inside and kept in fp32.
+ */
+gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
+                           const void* x, const void* const logits[4], const void* const lam[4], const void* gy,
+                           void* dx, void* const dlogits[4], void* const dlam[4], void* workspace,
+                           int64_t workspace_bytes, int dtype, void* stream);
 
 /*
  * Stage timing of one forward call (measurement only).

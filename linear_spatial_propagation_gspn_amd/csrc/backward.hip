@@ -1,0 +1,324 @@
+// backward.hip -- the adjoint line scan: gradients of the four-direction
+// propagation with respect to x, lambda and the logits.
+//
+// The pages define the forward propagation (GSPN-2 paper notes, "2D spatial
+// propagation recap"; chunks from "Optimisation 1", channel-shared logits
+// from "Optimisation 2") and report backward runtimes (GSPN-2 summary page,
+// "Experimental setup"); the gradient is its exact derivative.  In the scan
+// frame of a direction, with u_t = lambda_t * x_t and
+// h_t = M_t h_{t-1} + u_t ((M_t v)[k] = sum_o w_t[k,o] v[k+o], no M_t at a
+// chunk's first step), and g_t = dL/dy at line t:
+//   a_t          = g_t + M_{t+1}^T a_{t+1}        (backwards in t, per chunk)
+//   dlambda_t[k] = a_t[k] x_t[k]
+//   dx_t[k]     += a_t[k] lambda_t[k]             (summed over the directions)
+//   dw_t[k,o]    = a_t[k] h_{t-1}[k+o]            (not at a chunk's first step)
+//   dz_t[k,q]    = w_q (1 - s_q) (dw_q - sum_o dw_o w_o),  s_q = sigmoid(z_q)
+// (M^T v)[k] = w[k+1,-1] v[k+1] + w[k,0] v[k] + w[k-1,+1] v[k-1], so each lane
+// publishes the products w[k,-1] a[k] and w[k,+1] a[k] of its outer positions
+// for its neighbours, the same one-barrier LDS edge exchange as the forward.
+//
+// One workgroup per (direction, plane, chunk) line in vertical form: the
+// horizontal directions run on x and dL/dy transposed into their scan frame,
+// reading the forward states h recomputed beforehand into separate maps.  The
+// per-step inputs of the next D steps are in flight (ring slots refilled as
+// soon as read, compile-time slot indices, addresses clamped instead of
+// guarded).
+#include <utility>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace gspn {
+namespace {
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// steps in flight: 4 for one position per lane, 2 for two (register budget)
+template <int P>
+constexpr int adj_depth() { return P == 1 ? 4 : 2; }
+
+struct AdjK {
+    const void* x;    // [planes][S][L] (x, or x transposed for horizontal)
+    const void* g;    // dL/dy in the same frame
+    const void* lam;  // [planes][S][L]
+    const void* z;    // logits [n][cw][3][S][L]
+    const float* hs;  // forward states [planes][S][L], fp32
+    void* dlam;       // [planes][S][L]
+    void* dz;         // [n][cw][3][S][L] in the storage type, or fp32 sums for shared logits
+    void* dx;         // this direction's dx term [planes][S][L]
+    int64_t c;
+    int64_t cw;
+    int S;
+    int L;
+    int K;
+    int nchunks;
+    int reverse;
+    int shared;  // dz is an fp32 sum over channels (atomic adds)
+};
+
+struct Adj4K {
+    AdjK d[4];
+    int64_t blocks[4];
+};
+
+template <typename T, int P>
+__device__ __forceinline__ void adj_line(const AdjK& a, int64_t p, int q, float* edge_raw) {
+    constexpr int D = adj_depth<P>();
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int S = a.S;
+    const int L = a.L;
+    const int64_t plane = static_cast<int64_t>(S) * L;
+    const int64_t nidx = p / a.c;
+    const int64_t ci = p - nidx * a.c;
+    const T* xp = static_cast<const T*>(a.x) + p * plane;
+    const T* gp = static_cast<const T*>(a.g) + p * plane;
+    const T* lp = static_cast<const T*>(a.lam) + p * plane;
+    const float* hp = a.hs + p * plane;
+    const int64_t zplane = (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane;
+    const T* zp = static_cast<const T*>(a.z) + zplane;
+    T* dlp = static_cast<T*>(a.dlam) + p * plane;
+    T* dxp = static_cast<T*>(a.dx) + p * plane;
+
+    auto edge = [&](int b, int which, int lane) -> float& { return edge_raw[(b * 2 + which) * nt + lane]; };
+
+    const int k0 = tid * P;
+    int kk[P];
+    bool kin[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        kk[j] = min(k0 + j, L - 1);
+        kin[j] = k0 + j < L;
+    }
+    const int kl = max(k0 - 1, 0);          // left neighbour of the first position (clamped)
+    const int kr = min(k0 + P, L - 1);      // right neighbour of the last position (clamped)
+
+    const int t0 = q * a.K;
+    const int t1 = min(t0 + a.K, S);
+    const bool rev = a.reverse != 0;
+    auto line_of = [&](int t) { return rev ? S - 1 - t : t; };
+
+    // ring: per step g, x, lambda, z0..z2 per position and h_{t-1} at the
+    // positions plus their two outer neighbours
+    float rg[D][P], rx[D][P], rl[D][P], rz[D][3][P], rh[D][P + 2];
+    auto fill = [&](auto slot, int t) {
+        constexpr int s = decltype(slot)::value;
+        const int tc = max(t, t0);
+        const int64_t lo = static_cast<int64_t>(line_of(tc)) * L;
+        const int64_t hlo = static_cast<int64_t>(line_of(max(tc - 1, t0))) * L;  // h_{t-1} (clamped)
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            rg[s][j] = Store<T>::ld(gp + lo + kk[j]);
+            rx[s][j] = Store<T>::ld(xp + lo + kk[j]);
+            rl[s][j] = Store<T>::ld(lp + lo + kk[j]);
+#pragma unroll
+            for (int o = 0; o < 3; ++o) rz[s][o][j] = Store<T>::ld(zp + o * plane + lo + kk[j]);
+            rh[s][j + 1] = hp[hlo + kk[j]];
+        }
+        rh[s][0] = hp[hlo + kl];
+        rh[s][P + 1] = hp[hlo + kr];
+    };
+
+    float an[P];     // a_{t+1}
+    float qn0[P];    // w_{t+1}[k,-1] a_{t+1}[k]  (for position k-1)
+    float qn1[P];    // w_{t+1}[k, 0] a_{t+1}[k]
+    float qn2[P];    // w_{t+1}[k,+1] a_{t+1}[k]  (for position k+1)
+#pragma unroll
+    for (int j = 0; j < P; ++j) an[j] = qn0[j] = qn1[j] = qn2[j] = 0.0f;
+    int buf = 0;
+
+    auto step = [&](auto slot, auto lastc, int t) {
+        constexpr int s = decltype(slot)::value;
+        constexpr bool LAST = decltype(lastc)::value != 0;  // t = t1 - 1: no line after it in the chunk
+        float right_in = 0.0f, left_in = 0.0f;  // products from the neighbour lanes
+        if constexpr (!LAST) {
+            right_in = tid + 1 < nt ? edge(buf, 0, tid + 1) : 0.0f;  // w[k0+P,-1] a[k0+P]
+            left_in = tid > 0 ? edge(buf, 1, tid - 1) : 0.0f;        // w[k0-1,+1] a[k0-1]
+        }
+        const bool first = (t == t0);  // chunk's first line: logits unused, no h_{t-1}
+        const int i = line_of(t);
+        const int64_t lo = static_cast<int64_t>(i) * L;
+        float a_t[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            float v = rg[s][j];
+            if constexpr (!LAST) {
+                const float from_r = (j == P - 1) ? right_in : qn0[j + 1];
+                const float from_l = (j == 0) ? left_in : qn2[j - 1];
+                v += (qn1[j] + from_r) + from_l;
+            }
+            a_t[j] = kin[j] ? v : 0.0f;
+        }
+        float w[3][P], sg[3][P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const bool has_l = k0 + j > 0;
+            const bool has_r = k0 + j + 1 < L;
+            const float s0 = has_l ? sigmoid(rz[s][0][j]) : 0.0f;
+            const float s1 = sigmoid(rz[s][1][j]);
+            const float s2 = has_r ? sigmoid(rz[s][2][j]) : 0.0f;
+            const float r = recip((s0 + s1) + s2);
+            sg[0][j] = s0;
+            sg[1][j] = s1;
+            sg[2][j] = s2;
+            w[0][j] = s0 * r;
+            w[1][j] = s1 * r;
+            w[2][j] = s2 * r;
+        }
+        // outputs of this line
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            if (kin[j]) {
+                Store<T>::st(dlp + lo + k0 + j, a_t[j] * rx[s][j]);
+                Store<T>::st(dxp + lo + k0 + j, a_t[j] * rl[s][j]);
+            }
+            float dz[3] = {0.0f, 0.0f, 0.0f};
+            if (!first) {
+                float dw[3];
+#pragma unroll
+                for (int o = 0; o < 3; ++o) dw[o] = a_t[j] * rh[s][j + o];  // h_{t-1}[k+o-1]
+                const float dot = (dw[0] * w[0][j] + dw[1] * w[1][j]) + dw[2] * w[2][j];
+#pragma unroll
+                for (int o = 0; o < 3; ++o) dz[o] = w[o][j] * (1.0f - sg[o][j]) * (dw[o] - dot);
+                if (k0 + j == 0) dz[0] = 0.0f;
+                if (k0 + j + 1 >= L) dz[2] = 0.0f;
+                if (L == 1) dz[1] = 0.0f;  // a single neighbour: w = [1] whatever its logit
+            }
+            if (kin[j]) {
+                if (a.shared) {
+                    float* dzs = static_cast<float*>(a.dz) + nidx * 3 * plane;
+#pragma unroll
+                    for (int o = 0; o < 3; ++o) atomicAdd(dzs + o * plane + lo + k0 + j, dz[o]);
+                } else {
+                    T* dzp = static_cast<T*>(a.dz) + zplane;
+#pragma unroll
+                    for (int o = 0; o < 3; ++o) Store<T>::st(dzp + o * plane + lo + k0 + j, dz[o]);
+                }
+            }
+        }
+        fill(slot, t - D);
+        // products for the previous line (none across a chunk's first line)
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            an[j] = a_t[j];
+            qn0[j] = first ? 0.0f : w[0][j] * a_t[j];
+            qn1[j] = first ? 0.0f : w[1][j] * a_t[j];
+            qn2[j] = first ? 0.0f : w[2][j] * a_t[j];
+        }
+        buf ^= 1;
+        edge(buf, 0, tid) = qn0[0];
+        edge(buf, 1, tid) = qn2[P - 1];
+        __syncthreads();
+    };
+
+    [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        (fill(IC<Ss>{}, t1 - 1 - Ss), ...);
+    }(std::make_integer_sequence<int, D>{});
+    step(IC<0>{}, IC<1>{}, t1 - 1);
+    int t = t1 - 2;
+    for (; t - (D - 1) >= t0; t -= D) {
+        [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+            (step(IC<(Ss + 1) % D>{}, IC<0>{}, t - Ss), ...);
+        }(std::make_integer_sequence<int, D>{});
+    }
+    [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        ((t - Ss >= t0 ? step(IC<(Ss + 1) % D>{}, IC<0>{}, t - Ss) : void()), ...);
+    }(std::make_integer_sequence<int, D - 1>{});
+}
+
+template <typename T, int P>
+__global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
+    extern __shared__ float s_edge_raw[];
+    int dir = 0;
+    int64_t idx = blockIdx.x;
+    while (dir < 3 && idx >= a.blocks[dir]) {
+        idx -= a.blocks[dir];
+        ++dir;
+    }
+    const AdjK& k = a.d[dir];
+    const int64_t p = idx / k.nchunks;
+    const int q = static_cast<int>(idx - p * k.nchunks);
+    adj_line<T, P>(k, p, q, s_edge_raw);
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) p[e] = 0.0f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void store_sums_kernel(const float* __restrict__ src, T* __restrict__ dst,
+                                                         int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride)
+        Store<T>::st(dst + e, src[e]);
+}
+
+unsigned grid_for(int64_t total) {
+    int64_t b = (total + 255) / 256;
+    if (b > 256 * 64) b = 256 * 64;
+    if (b < 1) b = 1;
+    return static_cast<unsigned>(b);
+}
+
+}  // namespace
+
+hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
+    Adj4K k;
+    int maxL = 1;
+    int64_t total = 0;
+    for (int d = 0; d < 4; ++d) {
+        AdjK& a = k.d[d];
+        a.x = p[d].x;
+        a.g = p[d].g;
+        a.lam = p[d].lam;
+        a.z = p[d].logits;
+        a.hs = static_cast<const float*>(p[d].hs);
+        a.dlam = p[d].dlam;
+        a.dz = p[d].dz;
+        a.dx = p[d].dx;
+        a.c = p[d].c;
+        a.cw = p[d].cw;
+        a.S = static_cast<int>(p[d].S);
+        a.L = static_cast<int>(p[d].L);
+        a.K = static_cast<int>(p[d].chunk);
+        a.nchunks = static_cast<int>((p[d].S + p[d].chunk - 1) / p[d].chunk);
+        a.reverse = p[d].reverse;
+        a.shared = p[d].shared;
+        k.blocks[d] = p[d].n * p[d].c * a.nchunks;
+        total += k.blocks[d];
+        maxL = a.L > maxL ? a.L : maxL;
+    }
+    const int P = maxL <= 1024 ? 1 : 2;  // lines of at most 2048 positions
+    const int lanes = ((maxL + P - 1) / P + 63) / 64 * 64;
+    const size_t lds = 4 * sizeof(float) * static_cast<size_t>(lanes);
+    const dim3 grid(static_cast<unsigned>(total));
+    const bool f32 = p[0].dtype == kF32;
+    if (P == 1) {
+        if (f32) hipLaunchKernelGGL((adj4_kernel<float, 1>), grid, dim3(lanes), lds, stream, k);
+        else hipLaunchKernelGGL((adj4_kernel<bf16_t, 1>), grid, dim3(lanes), lds, stream, k);
+    } else {
+        if (f32) hipLaunchKernelGGL((adj4_kernel<float, 2>), grid, dim3(lanes), lds, stream, k);
+        else hipLaunchKernelGGL((adj4_kernel<bf16_t, 2>), grid, dim3(lanes), lds, stream, k);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_store_sums(const float* src, void* dst, int64_t n, int dtype, hipStream_t stream) {
+    if (dtype == kF32) {
+        hipLaunchKernelGGL(store_sums_kernel<float>, dim3(grid_for(n)), dim3(256), 0, stream, src,
+                           static_cast<float*>(dst), n);
+    } else {
+        hipLaunchKernelGGL(store_sums_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, stream, src,
+                           static_cast<bf16_t*>(dst), n);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gspn

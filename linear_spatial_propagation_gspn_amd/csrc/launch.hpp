@@ -26,6 +26,7 @@ struct ScanParams {
     int accumulate;
     int dtype;   // storage type of x, lam, out
     int wdtype;  // format of wts: dtype, or for weights normalised beforehand kF32 / kPairF16
+    int odtype = -1;  // storage type of out: -1 = dtype; kF32 for fp32 states of bf16 scans
 };
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
@@ -74,6 +75,30 @@ hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const v
 // y = ((y + w1) + w2) + w3 in place.
 hipError_t launch_merge_into(void* y, const void* w1, const void* w2, const void* w3, int64_t numel,
                              int dtype, hipStream_t stream);
+
+// One direction of the adjoint scan, in vertical form (horizontal directions
+// on x and dL/dy transposed into their scan frame).  hs: the direction's
+// forward states in fp32; dz: logits gradient in the storage type, or
+// (shared) fp32 sums over channels [n][3][S][L] that the kernel adds into.
+struct AdjointParams {
+    const void* x;
+    const void* g;
+    const void* lam;
+    const void* logits;
+    const void* hs;
+    void* dlam;
+    void* dz;
+    void* dx;
+    int64_t n, c, cw, S, L;
+    int64_t chunk;  // clamped to [1, S]
+    int reverse;
+    int shared;
+    int dtype;
+};
+
+hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_store_sums(const float* src, void* dst, int64_t n, int dtype, hipStream_t stream);
 
 hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const void* in,
                           const void* weight, void* out, int dtype, hipStream_t stream);

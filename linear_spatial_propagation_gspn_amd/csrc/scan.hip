@@ -28,6 +28,8 @@ extern template hipError_t launch_fused4v<bf16_t, WPair>(const Scan4K&, int, int
 extern template hipError_t launch_fused4lp<float, float, true>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<float, float, false>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4v<bf16_t, bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true, float>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, WPair, false>(const Scan4K&, int, hipStream_t);
 
 namespace {
@@ -159,6 +161,9 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
     // length, p[2..3] another
     const int l01 = static_cast<int>(p[0].w);
     const int l23 = static_cast<int>(p[2].w);
+    // fp32 outputs of a bf16 scan (states kept at full precision): logits only
+    const bool wide_out = p[0].dtype == kBF16 && p[0].odtype == kF32;
+    if (wide_out && (p[0].wdtype != kBF16 || !p[0].wts_are_logits)) return hipErrorInvalidValue;
     if (lp_eligible(p)) {
         const int P = p[0].dtype == kF32 ? 4 : 8;
         Scan4K k;
@@ -178,6 +183,7 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
                           : launch_fused4lp<float, float, false>(k, nthreads, stream);
         }
         if (p[0].wdtype == kPairF16) return launch_fused4lp<bf16_t, WPair, false>(k, nthreads, stream);
+        if (wide_out) return launch_fused4lp<bf16_t, bf16_t, true, float>(k, nthreads, stream);
         return launch_fused4lp<bf16_t, bf16_t, true>(k, nthreads, stream);
     }
     if (kind) *kind = 2;
@@ -195,6 +201,7 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
     const int nthreads = a > b ? a : b;
     if (p[0].dtype == kF32) return launch_fused4v<float, float>(k, pv, ph, nthreads, stream);
     if (p[0].wdtype == kPairF16) return launch_fused4v<bf16_t, WPair>(k, pv, ph, nthreads, stream);
+    if (wide_out) return launch_fused4v<bf16_t, bf16_t, float>(k, pv, ph, nthreads, stream);
     return launch_fused4v<bf16_t, bf16_t>(k, pv, ph, nthreads, stream);
 }
 

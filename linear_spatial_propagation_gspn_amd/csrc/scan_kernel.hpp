@@ -72,8 +72,11 @@ using IC = std::integral_constant<int, V>;
 // ACC: add into the output instead of overwriting it.
 // Every lane of the workgroup takes part: lanes past the end of the line hold
 // no positions but join every barrier.  edge_raw: 4 * blockDim.x floats of LDS.
-template <typename T, typename TW, int P, int U, int UT, bool HORIZ, bool REV, bool ACC>
+// TO: element type of the output (T, or fp32 for vertical-form scans that
+// keep their states at full precision).
+template <typename T, typename TW, int P, int U, int UT, bool HORIZ, bool REV, bool ACC, typename TO = T>
 __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, float* edge_raw) {
+    static_assert(std::is_same_v<TO, T> || (!HORIZ && !ACC), "a wider output only for plain vertical scans");
     static_assert(UT % U == 0, "a tile holds whole sub-blocks");
     constexpr int NS = UT / U;                             // sub-blocks per tile
     constexpr int VW = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte vector
@@ -98,6 +101,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
     const ZT* __restrict__ zp =
         static_cast<const ZT*>(a.wts) + (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane);
     T* __restrict__ op = static_cast<T*>(a.out) + p * plane;
+    TO* __restrict__ oq = static_cast<TO*>(a.out) + p * plane;
 
     const int k0 = tid * P;
     const int t0 = q * a.K;
@@ -292,11 +296,11 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
 #pragma unroll
                     for (int j = 0; j < P; ++j) yt[C][j][off] = ACC ? yt[C][j][off] + hn[j] : hn[j];
                 } else {
-                    T* orow = op + static_cast<int64_t>(line_of(t)) * L;
+                    TO* orow = oq + static_cast<int64_t>(line_of(t)) * L;
 #pragma unroll
                     for (int j = 0; j < P; ++j) {
                         const float v = ACC ? ry[(HORIZ || !ACC) ? 0 : R][s][j] + hn[j] : hn[j];
-                        if (kin[j]) Store<T>::st(orow + k0 + j, v);
+                        if (kin[j]) Store<TO>::st(orow + k0 + j, v);
                     }
                 }
 #pragma unroll
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
 // directions are described as vertical scans of the transposed input (their
 // scan frame), so every access is a coalesced row.  PV / PH: positions per
 // lane of the first two / last two scans.
-template <typename T, typename TW, int PV, int PH>
+template <typename T, typename TW, int PV, int PH, typename TO = T>
 __global__ __launch_bounds__(1024)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<false, (PV > PH ? PV : PH)>())))
 void scan4v_kernel(const Scan4K a) {
@@ -524,25 +528,25 @@ void scan4v_kernel(const Scan4K a) {
     const int64_t p = idx / k.nchunks;
     const int q = static_cast<int>(idx - p * k.nchunks);
     if (dir < 2) {
-        scan_line<T, TW, PV, BV::U, BV::UT, false, false, false>(k, p, q, s_edge_raw);
+        scan_line<T, TW, PV, BV::U, BV::UT, false, false, false, TO>(k, p, q, s_edge_raw);
     } else {
-        scan_line<T, TW, PH, BH::U, BH::UT, false, false, false>(k, p, q, s_edge_raw);
+        scan_line<T, TW, PH, BH::U, BH::UT, false, false, false, TO>(k, p, q, s_edge_raw);
     }
 }
 
-template <typename T, typename TW>
+template <typename T, typename TW, typename TO = T>
 hipError_t launch_fused4v(const Scan4K& k, int pv, int ph, int nthreads, hipStream_t stream) {
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
     const size_t lds = 4 * sizeof(float) * static_cast<size_t>(nthreads);
     const dim3 grid(static_cast<unsigned>(nblocks));
     if (pv == 1 && ph == 1) {
-        hipLaunchKernelGGL((scan4v_kernel<T, TW, 1, 1>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 1, 1, TO>), grid, dim3(nthreads), lds, stream, k);
     } else if (pv == 1) {
-        hipLaunchKernelGGL((scan4v_kernel<T, TW, 1, 2>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 1, 2, TO>), grid, dim3(nthreads), lds, stream, k);
     } else if (ph == 1) {
-        hipLaunchKernelGGL((scan4v_kernel<T, TW, 2, 1>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 2, 1, TO>), grid, dim3(nthreads), lds, stream, k);
     } else {
-        hipLaunchKernelGGL((scan4v_kernel<T, TW, 2, 2>), grid, dim3(nthreads), lds, stream, k);
+        hipLaunchKernelGGL((scan4v_kernel<T, TW, 2, 2, TO>), grid, dim3(nthreads), lds, stream, k);
     }
     return hipGetLastError();
 }

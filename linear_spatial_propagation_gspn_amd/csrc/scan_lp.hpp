@@ -84,7 +84,7 @@ __device__ __forceinline__ float shift_from_upper_lane(float v) {  // lane i get
 // and the output; TW: storage of the weights (WPair: packed half pairs of
 // channel-shared weights); LOGITS: the weights are logits normalised here
 // (else normalised weights, zero outside the line).
-template <typename T, typename TW, bool LOGITS>
+template <typename T, typename TW, bool LOGITS, typename TO = T>
 __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     constexpr int P = 16 / static_cast<int>(sizeof(T));              // positions per lane
     constexpr int WT = P * static_cast<int>(sizeof(T)) / 4;          // words per lane: x, lambda, out
@@ -107,7 +107,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
 
     const auto rx = lp::rsrc(static_cast<const T*>(a.x) + p * plane, plane * sizeof(T));
     const auto rl = lp::rsrc(static_cast<const T*>(a.lam) + p * plane, plane * sizeof(T));
-    const auto ro = lp::rsrc(static_cast<T*>(a.out) + p * plane, plane * sizeof(T));
+    const auto ro = lp::rsrc(static_cast<TO*>(a.out) + p * plane, plane * sizeof(TO));
     const auto rz = lp::rsrc(static_cast<const char*>(a.wts) +
                                  (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane) * ZB,
                              NZ * plane * ZB);
@@ -118,6 +118,8 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     const uint32_t vt = static_cast<uint32_t>(k0c) * sizeof(T);
     const uint32_t vw = static_cast<uint32_t>(k0c) * ZB;
     const uint32_t rowT = static_cast<uint32_t>(L) * sizeof(T);
+    const uint32_t vo = static_cast<uint32_t>(k0c) * sizeof(TO);
+    const uint32_t rowO = static_cast<uint32_t>(L) * sizeof(TO);
     const uint32_t rowW = static_cast<uint32_t>(L) * ZB;
     const uint32_t planeW = static_cast<uint32_t>(plane) * ZB;
     const bool has_l0 = k0 > 0;       // the lane's first position has a left neighbour
@@ -198,17 +200,23 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
 #pragma unroll
         for (int j = 0; j < P; ++j) h[j] = active ? hn[j] : 0.0f;
         if (active) {
-            lp::int4v o;
-            if constexpr (sizeof(T) == 4) {
+            constexpr int WO = P * static_cast<int>(sizeof(TO)) / 4;  // output words per lane
+            uint32_t ow[WO];
+            if constexpr (sizeof(TO) == 4) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = __float_as_int(h[e]);
+                for (int e = 0; e < WO; ++e) ow[e] = __float_as_uint(h[e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = static_cast<int>(static_cast<uint32_t>(f32_to_bf16(h[2 * e])) |
-                                            (static_cast<uint32_t>(f32_to_bf16(h[2 * e + 1])) << 16));
+                for (int e = 0; e < WO; ++e)
+                    ow[e] = static_cast<uint32_t>(f32_to_bf16(h[2 * e])) |
+                            (static_cast<uint32_t>(f32_to_bf16(h[2 * e + 1])) << 16);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(o, ro, vt, line_of(t) * rowT, 0);
+#pragma unroll
+            for (int v = 0; v < WO / 4; ++v) {
+                const lp::int4v o = {static_cast<int>(ow[4 * v]), static_cast<int>(ow[4 * v + 1]),
+                                     static_cast<int>(ow[4 * v + 2]), static_cast<int>(ow[4 * v + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(o, ro, vo + 16 * v, line_of(t) * rowO, 0);
+            }
         }
         buf ^= 1;
         if (lane == 0) edges[buf][wave][0] = h[0];
@@ -238,7 +246,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
 // Four vertical-form scans in one launch; block b is direction b % 4 when the
 // directions have equal block counts (Scan4K::interleave), else consecutive
 // ranges, as in scan4v_kernel.
-template <typename T, typename TW, bool LOGITS>
+template <typename T, typename TW, bool LOGITS, typename TO = T>
 __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) {
     const int64_t b = blockIdx.x;
     int dir = 0;
@@ -255,13 +263,13 @@ __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) 
     const ScanK& k = a.d[dir];
     const int64_t p = idx / k.nchunks;
     const int q = static_cast<int>(idx - p * k.nchunks);
-    lp_line<T, TW, LOGITS>(k, p, q);
+    lp_line<T, TW, LOGITS, TO>(k, p, q);
 }
 
-template <typename T, typename TW, bool LOGITS>
+template <typename T, typename TW, bool LOGITS, typename TO = T>
 hipError_t launch_fused4lp(const Scan4K& k, int nthreads, hipStream_t stream) {
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
-    hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads), 0,
+    hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS, TO>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads), 0,
                        stream, k);
     return hipGetLastError();
 }

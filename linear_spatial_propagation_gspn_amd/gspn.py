@@ -37,7 +37,8 @@ STATUS = {
 EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy_project",
            "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4",
            "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_forward4_timed",
-           "gspn_proxy_forward4_timed", "gspn_status_string", "gspn_abi_version")
+           "gspn_proxy_forward4_timed", "gspn_backward4_workspace_bytes", "gspn_backward4", "gspn_status_string",
+           "gspn_abi_version")
 
 # gspn_stage, in order.
 STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up")
@@ -102,6 +103,11 @@ def lib() -> ctypes.CDLL:
             for name in ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4",
                          "gspn_proxy_project", "gspn_forward4"):
                 getattr(h, name).restype = ci
+            h.gspn_backward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
+            h.gspn_backward4_workspace_bytes.restype = i64
+            h.gspn_backward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                                         vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, i64, ci, vp]
+            h.gspn_backward4.restype = ci
             h.gspn_status_string.argtypes = [ci]
             h.gspn_status_string.restype = ctypes.c_char_p
             h.gspn_abi_version.argtypes = []
@@ -365,3 +371,49 @@ def gspn_proxy_forward4_timed(x: torch.Tensor, w_down: torch.Tensor, w_up: torch
     times = StageTimes()
     out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times)
     return out, times.as_dict()
+
+
+def backward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
+    """A workspace buffer (uint8 tensor on x's device) for gspn_backward4."""
+    n, c, h, w = x.shape
+    nbytes = int(lib().gspn_backward4_workspace_bytes(n, c, h, w, cw, _dtype_code(x)))
+    if nbytes < 0:
+        raise ValueError("invalid shape for a gspn_backward4 workspace")
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+
+
+def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                   gy: torch.Tensor, chunk_len: int = 0, workspace: torch.Tensor | None = None,
+                   out: tuple | None = None) -> tuple:
+    """Gradients of gspn_forward4 for dL/dy = gy: returns (dx, [dlogits_d],
+    [dlam_d]) in the inputs' layouts.  ``out`` may supply those tensors."""
+    n, c, h, w = x.shape
+    dt = x.dtype
+    cw = logits[0].shape[1]
+    _check(x, "x", (n, c, h, w), dt, x.device)
+    _check(gy, "gy", (n, c, h, w), dt, x.device)
+    for d in range(4):
+        S, L = frame_shape(d, h, w)
+        _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
+        _check(lams[d], "lam[%d]" % d, (n, c, S, L), dt, x.device)
+    if out is None:
+        dx = torch.empty_like(x)
+        dz = [torch.empty_like(z) for z in logits]
+        dl = [torch.empty_like(l) for l in lams]
+    else:
+        dx, dz, dl = out
+    _check(dx, "dx", (n, c, h, w), dt, x.device)
+    for d in range(4):
+        _check(dz[d], "dlogits[%d]" % d, tuple(logits[d].shape), dt, x.device)
+        _check(dl[d], "dlam[%d]" % d, tuple(lams[d].shape), dt, x.device)
+    if workspace is None:
+        workspace = backward4_workspace(x, cw)
+    if workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
+    vp4 = ctypes.c_void_p * 4
+    _raise(lib().gspn_backward4(n, c, h, w, cw, int(chunk_len), _ptr(x), vp4(*[z.data_ptr() for z in logits]),
+                                vp4(*[l.data_ptr() for l in lams]), _ptr(gy), _ptr(dx),
+                                vp4(*[t.data_ptr() for t in dz]), vp4(*[t.data_ptr() for t in dl]),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x),
+                                _stream(x.device)), "gspn_backward4")
+    return dx, dz, dl

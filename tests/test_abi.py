@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 3
+    assert lib.gspn_abi_version() == 4
     for code in range(12):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -237,3 +237,33 @@ def test_timed_variants_validate_like_untimed(lib):
     assert g(wsb=need - 1) == WSPACE
     assert g(ws=0) == NULLP
     assert g(n=0) == OK
+
+
+def test_backward4_validation(lib):
+    vp4 = ctypes.c_void_p * 4
+    zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
+    ls = vp4(C_, C_ + 0x1000000, C_ + 0x2000000, C_ + 0x3000000)
+    dzs = vp4(0x60000000, 0x61000000, 0x62000000, 0x63000000)
+    dls = vp4(0x64000000, 0x65000000, 0x66000000, 0x67000000)
+    GY, DX, WS = 0x70000000, 0x71000000, 0x72000000
+    need = lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 2, 0)
+    assert need == 9 * 2 * 64 * 4
+    assert lib.gspn_backward4_workspace_bytes(1, 3, 8, 8, 1, 1) == 4 * 3 * 64 * 4 + 4 * 3 * 64 * 4 + 5 * 3 * 64 * 2
+    assert lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
+
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, gy=GY, dx=DX, dz=dzs, dl=dls, ws=WS, wsb=need, dt=0):
+        return lib.gspn_backward4(n, c, h, w, cw, chunk, x, zs, ls, gy, dx, dz, dl, ws, wsb, dt, None)
+
+    assert f(dt=2) == DTYPE
+    assert f(chunk=-1) == CHUNK
+    assert f(cw=3) == WCH
+    assert f(h=3000) == UNSUP                      # longer lines than the recomputed forward takes
+    assert f(ws=0) == NULLP
+    assert f(gy=0) == NULLP
+    assert f(dz=vp4(0x60000000, 0, 0x62000000, 0x63000000)) == NULLP
+    assert f(wsb=need - 1) == WSPACE
+    assert f(ws=WS + 2) == MISAL
+    assert f(dx=A + 8) == ALIAS                     # dx on x
+    assert f(dx=dls[1]) == ALIAS                    # dx on dlam[1]
+    assert f(dx=WS + 64) == ALIAS                   # dx in the workspace
+    assert f(n=0, x=0, gy=0, dx=0, dz=None, dl=None, ws=0) == OK
