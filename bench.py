@@ -102,6 +102,26 @@ def scan_launch_bytes(wl, kernel: str) -> int:
     return total // 4
 
 
+def backward_algorithmic_bytes(wl) -> int:
+    """Backward: x, dL/dy, the logits and lambdas read once; dx, dlambda and
+    dlogits written once."""
+    u = unit_bytes(wl)
+    z = 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
+    return 2 * u + z + 4 * u + u + 4 * u + z
+
+
+def adjoint_launch_bytes(wl) -> int:
+    """Algorithmic bytes of the adjoint launch: x and dL/dy in both frames,
+    four lambdas and logits, four fp32 state maps read; four dlambda and dx
+    terms written; the logit gradients written (per-channel) or added into fp32
+    sums (shared)."""
+    u = unit_bytes(wl)
+    z = 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
+    states = 4 * wl.n * wl.c_scan * wl.h * wl.w * 4
+    dz = 4 * wl.n * 3 * wl.h * wl.w * 4 if prenormalised(wl) else z
+    return 2 * u + 2 * u + 4 * u + z + states + 4 * u + 4 * u + dz
+
+
 def run_step(wl, inp, out, ws, timed=False):
     if wl.c_proxy:
         f = G.gspn_proxy_forward4_timed if timed else G.gspn_proxy_forward4
@@ -169,12 +189,12 @@ def _np64(t):
     return t.detach().to("cpu").double().numpy()
 
 
-def cpu_baseline_planes(wl, inp, oracle) -> dict:
-    """Whole (n, c) planes through the oracle's four-direction forward, each
-    plane run as its own image; repeated until CPU_TARGET_S, extrapolated to
-    the workload's n * c planes."""
+def cpu_baseline_planes(wl, inp, oracle, gy=None) -> dict:
+    """Whole (n, c) planes through the oracle's four-direction forward (or,
+    given dL/dy, its backward), each plane run as its own image; repeated
+    until CPU_TARGET_S, extrapolated to the workload's n * c planes."""
     planes = wl.n * wl.c
-    per_plane = (6 + (0 if wl.shared_w else 12)) * wl.h * wl.w * 8
+    per_plane = (6 + (0 if wl.shared_w else 12)) * wl.h * wl.w * 8 * (2 if gy is not None else 1)
     sample = max(1, min(planes, CPU_MEM_BYTES // per_plane))
     if sample >= 16:
         sample -= sample % 16
@@ -187,17 +207,23 @@ def cpu_baseline_planes(wl, inp, oracle) -> dict:
     for d in range(4):
         zs.append(_np64(inp["logits"][d][nn, torch.zeros_like(cc) if wl.shared_w else cc][:, None]))
         ls.append(_np64(inp["lam"][d][nn, cc][:, None]))
+    gs = _np64(gy[nn, cc][:, None]) if gy is not None else None
     reps, spent = 0, 0.0
     while reps < CPU_MAX_REPEATS and (reps == 0 or spent < CPU_TARGET_S):
         t = time.perf_counter()
-        oracle.forward4(xs, zs, ls, chunk=wl.chunk)
+        if gs is None:
+            oracle.forward4(xs, zs, ls, chunk=wl.chunk)
+        else:
+            oracle.backward4(xs, zs, ls, gs, chunk=wl.chunk)
         spent += time.perf_counter() - t
         reps += 1
     per_call = spent / reps
-    return {"value": round(per_call * 1e3 * planes / sample, 3), "unit": "ms per forward (extrapolated)",
-            "cores": min(oracle.max_threads(), sample), "kind": "oracle",
-            "sample": "%d of %d planes (%dx%d, every %d-th), all 4 directions, fp64; %d runs, %.1f s of "
-                      "oracle time" % (sample, planes, wl.h, wl.w, step, reps, spent)}
+    what = "forward" if gs is None else "backward"
+    threads = min(oracle.max_threads(), sample)  # planes run in parallel (each its own image)
+    return {"value": round(per_call * 1e3 * planes / sample, 3), "unit": "ms per %s (extrapolated)" % what,
+            "cores": threads, "kind": "oracle",
+            "sample": "%d of %d planes (%dx%d, every %d-th), each as its own image, all 4 directions, fp64 %s; "
+                      "%d runs, %.1f s of oracle time" % (sample, planes, wl.h, wl.w, step, what, reps, spent)}
 
 
 def cpu_baseline_proxy(wl, inp, oracle) -> dict:
@@ -263,6 +289,78 @@ def copy_check(mib: int) -> None:
                       "GBps_read_plus_write": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}))
 
 
+def bench_backward(args, wl):
+    """The backward leg: gspn_backward4 over the same inputs and a seeded
+    dL/dy ~ N(0, 1); the dominant kernel is the adjoint launch."""
+    if wl.c_proxy:
+        print("bench.py: the backward pass covers gspn_forward4 (no proxy projections)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.init()
+    G.lib()
+    print("bench: backward, workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
+    inp = make_inputs(wl, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 1000)
+    gy = torch.randn(inp["x"].shape, generator=g, device="cuda", dtype=torch.float32).to(wl.torch_dtype)
+    outs = (torch.empty_like(inp["x"]), [torch.empty_like(z) for z in inp["logits"]],
+            [torch.empty_like(l) for l in inp["lam"]])
+    ws = G.backward4_workspace(inp["x"], wl.cw)
+
+    def step(times=None):
+        return G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=wl.chunk, workspace=ws,
+                                out=outs, times=times)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    print("bench: backward %.3f ms/step" % ms, file=sys.stderr, flush=True)
+
+    reps = max(3, min(args.steps, 10))
+    acc = {name: 0.0 for name in G.STAGES}
+    for _ in range(reps):
+        t = G.StageTimes()
+        step(times=t)
+        for name, v in t.as_dict().items():
+            if name != "scan_kernel":
+                acc[name] += v["ms"] / reps
+    kernel_ms = acc["adjoint"]
+    bpl = adjoint_launch_bytes(wl)
+    achieved = bpl / (kernel_ms * 1e-3) / 1e9
+    alg = backward_algorithmic_bytes(wl)
+    eff = alg / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle's backward on a sample", file=sys.stderr, flush=True)
+        import oracle
+        cpu = cpu_baseline_planes(wl, inp, oracle, gy=gy)
+    traffic, traffic_src = counter_traffic("adj4_kernel", wl)
+    rec = {
+        "metric": "ms per 4-direction GSPN backward (dx, dlambda, dlogits); achieved HBM GB/s",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded)",
+        "config": {"workload": wl.name, "pass": "backward", "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
+                   "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk},
+        "effective_GBps": round(eff, 1), "effective_frac": round(eff / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
+        "stages_ms": {k: round(v, 4) for k, v in acc.items() if v > 0},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": "adj4_kernel",
+                     "kernel_ms": round(kernel_ms, 4), "launches_per_step": 1, "bytes_per_launch": bpl,
+                     "traffic_source": traffic_src},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +368,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="profile", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "backward"),
+                    help="time the forward (default) or the backward (gradients for a seeded dL/dy)")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -282,6 +382,9 @@ def main():
         copy_check(args.copy_check)
         return
     wl = WORKLOADS[args.workload]
+    if args.pass_ == "backward":
+        bench_backward(args, wl)
+        return
     torch.cuda.init()
     G.lib()
     print("bench: workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)

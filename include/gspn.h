@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 4
+#define GSPN_ABI_VERSION 5
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -288,7 +288,9 @@ typedef enum {
     GSPN_STAGE_SCAN = 3,         /* the line-scan launches (1 fused or 4) */
     GSPN_STAGE_COMBINE = 4,      /* transposing merge of the partial maps into y */
     GSPN_STAGE_PROJECT_UP = 5,   /* 1x1 projection C_proxy -> C */
-    GSPN_NUM_STAGES = 6
+    GSPN_STAGE_ADJOINT = 6,      /* backward: the adjoint line-scan launch */
+    GSPN_STAGE_REDUCE = 7,       /* backward: clearing / storing the shared-logit sums */
+    GSPN_NUM_STAGES = 8
 } gspn_stage;
 
 /* Which scan kernel a forward call ran (gspn_stage_times.scan_kernel). */
@@ -318,6 +320,14 @@ gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w
                                       const void* const lam[4], void* y, void* workspace,
                                       int64_t workspace_bytes, int dtype, void* stream,
                                       gspn_stage_times* times);
+
+/* gspn_backward4 with stage timing (same contract as gspn_forward4_timed);
+ * the forward recompute is reported as GSPN_STAGE_SCAN. */
+gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
+                                 const void* x, const void* const logits[4], const void* const lam[4],
+                                 const void* gy, void* dx, void* const dlogits[4], void* const dlam[4],
+                                 void* workspace, int64_t workspace_bytes, int dtype, void* stream,
+                                 gspn_stage_times* times);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);

@@ -515,6 +515,145 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
                           [&] { return gspn::launch_project(n, c_proxy, h * w, c, yp, w_up, y, dtype, st); }));
 }
 
+gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len, const void* x,
+                          const void* const logits[4], const void* const lam[4], const void* gy, void* dx,
+                          void* const dlogits[4], void* const dlam[4], void* workspace, int64_t workspace_bytes,
+                          int dtype, void* stream, Timer* tm) {
+    int64_t chunks[4];
+    for (int d = 0; d < 4; ++d) {
+        bool empty = false;
+        const ScanCheck ck = check_scan(d, chunk_len, n, c, h, w, cw, dtype, &empty);
+        if (ck.st != GSPN_OK || empty) return ck.st;
+        chunks[d] = ck.chunk;
+    }
+    if (!gspn::fused4_supported(h, w)) return GSPN_ERR_UNSUPPORTED;
+    if (!x || !gy || !dx || !logits || !lam || !dlogits || !dlam || !workspace) return GSPN_ERR_NULL_POINTER;
+    for (int d = 0; d < 4; ++d)
+        if (!logits[d] || !lam[d] || !dlogits[d] || !dlam[d]) return GSPN_ERR_NULL_POINTER;
+    const size_t es = elem_size(dtype);
+    const int64_t need = gspn_backward4_workspace_bytes(n, c, h, w, cw, dtype);
+    if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
+    if (!aligned(x, es) || !aligned(gy, es) || !aligned(dx, es)) return GSPN_ERR_MISALIGNED;
+    const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
+    const int64_t wb = n * cw * 3 * h * w * static_cast<int64_t>(es);
+    // outputs: dx, dlam[4], dlogits[4]; none may overlap an input, the
+    // workspace or another output
+    const void* outs[9] = {dx, dlam[0], dlam[1], dlam[2], dlam[3], dlogits[0], dlogits[1], dlogits[2], dlogits[3]};
+    const int64_t ob[9] = {xb, xb, xb, xb, xb, wb, wb, wb, wb};
+    for (int i = 0; i < 9; ++i) {
+        if (!aligned(outs[i], es)) return GSPN_ERR_MISALIGNED;
+        if (overlap(outs[i], ob[i], x, xb) || overlap(outs[i], ob[i], gy, xb) ||
+            overlap(outs[i], ob[i], workspace, need))
+            return GSPN_ERR_ALIASING;
+        for (int d = 0; d < 4; ++d)
+            if (overlap(outs[i], ob[i], logits[d], wb) || overlap(outs[i], ob[i], lam[d], xb)) return GSPN_ERR_ALIASING;
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], ob[i], outs[j], ob[j])) return GSPN_ERR_ALIASING;
+    }
+    for (int d = 0; d < 4; ++d) {
+        if (!aligned(logits[d], es) || !aligned(lam[d], es)) return GSPN_ERR_MISALIGNED;
+        if (overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], xb))
+            return GSPN_ERR_ALIASING;
+    }
+    if (overlap(workspace, need, x, xb) || overlap(workspace, need, gy, xb)) return GSPN_ERR_ALIASING;
+    const hipStream_t st = as_stream(stream);
+
+    // Workspace: [fp32 logit-gradient sums of the four directions (shared
+    // logits only)][fp32 forward states H0..H3][x^T][gy^T][dx terms D1..D3].
+    // The states stay fp32 for bf16 storage too: the logit gradient takes
+    // differences of neighbouring states, which bf16 rounding would swamp.
+    const bool shared = cw == 1 && c > 1;
+    const int64_t zsum = 3 * n * h * w;  // floats per direction
+    const int64_t hb = n * c * h * w * 4;  // bytes of one fp32 state map
+    char* ws = static_cast<char*>(workspace);
+    float* sums = reinterpret_cast<float*>(ws);
+    char* hs[4];
+    hs[0] = ws + (shared ? 4 * zsum * 4 : 0);
+    for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
+    char* xt = hs[3] + hb;
+    char* gt = xt + xb;
+    char* dterm[4];
+    dterm[0] = static_cast<char*>(dx);
+    dterm[1] = gt + xb;
+    dterm[2] = dterm[1] + xb;
+    dterm[3] = dterm[2] + xb;
+    const int H = static_cast<int>(h);
+    const int W = static_cast<int>(w);
+    if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] { return gspn::launch_transpose(x, xt, n * c, H, W, dtype, st); }) !=
+            hipSuccess ||
+        timed(tm, GSPN_STAGE_TRANSPOSE, [&] { return gspn::launch_transpose(gy, gt, n * c, H, W, dtype, st); }) !=
+            hipSuccess)
+        return GSPN_ERR_HIP;
+
+    // forward states of every direction (vertical form; horizontal in the
+    // transposed frame)
+    gspn::ScanParams p[4];
+    for (int d = 0; d < 4; ++d) {
+        const bool hz = horizontal(d);
+        p[d].x = hz ? static_cast<const void*>(xt) : x;
+        p[d].wts = logits[d];
+        p[d].lam = lam[d];
+        p[d].out = hs[d];
+        p[d].n = n;
+        p[d].c = c;
+        p[d].cw = cw;
+        p[d].h = hz ? w : h;
+        p[d].w = hz ? h : w;
+        p[d].dir = hz ? d - 2 : d;
+        p[d].chunk = chunks[d];
+        p[d].wts_are_logits = 1;
+        p[d].accumulate = 0;
+        p[d].dtype = dtype;
+        p[d].wdtype = dtype;
+        p[d].odtype = GSPN_F32;
+    }
+    int kind = GSPN_SCAN_FUSED4;
+    if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    if (tm) tm->scan_kernel = kind;
+    if (shared &&
+        timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(sums, 4 * zsum, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+
+    gspn::AdjointParams a[4];
+    for (int d = 0; d < 4; ++d) {
+        const bool hz = horizontal(d);
+        a[d].x = hz ? static_cast<const void*>(xt) : x;
+        a[d].g = hz ? static_cast<const void*>(gt) : gy;
+        a[d].lam = lam[d];
+        a[d].logits = logits[d];
+        a[d].hs = hs[d];
+        a[d].dlam = dlam[d];
+        a[d].dz = shared ? static_cast<void*>(sums + d * zsum) : dlogits[d];
+        a[d].dx = dterm[d];
+        a[d].n = n;
+        a[d].c = c;
+        a[d].cw = cw;
+        a[d].S = hz ? w : h;
+        a[d].L = hz ? h : w;
+        a[d].chunk = chunks[d];
+        a[d].reverse = (d == GSPN_B2T || d == GSPN_R2L) ? 1 : 0;
+        a[d].shared = shared ? 1 : 0;
+        a[d].dtype = dtype;
+    }
+    if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjoint4(a, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    // dx = ((D2^T + D3^T) + D0) + D1, D0 written into dx directly
+    if (timed(tm, GSPN_STAGE_COMBINE, [&] {
+            return gspn::launch_combine(dx, dterm[1], dterm[2], dterm[3], n * c, H, W, 1, dtype, st);
+        }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    if (shared) {
+        for (int d = 0; d < 4; ++d)
+            if (timed(tm, GSPN_STAGE_REDUCE, [&] {
+                    return gspn::launch_store_sums(sums + d * zsum, dlogits[d], zsum, dtype, st);
+                }) != hipSuccess)
+                return GSPN_ERR_HIP;
+    }
+    return GSPN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -586,126 +725,22 @@ gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
                            const void* x, const void* const logits[4], const void* const lam[4], const void* gy,
                            void* dx, void* const dlogits[4], void* const dlam[4], void* workspace,
                            int64_t workspace_bytes, int dtype, void* stream) {
-    int64_t chunks[4];
-    for (int d = 0; d < 4; ++d) {
-        bool empty = false;
-        const ScanCheck ck = check_scan(d, chunk_len, n, c, h, w, cw, dtype, &empty);
-        if (ck.st != GSPN_OK || empty) return ck.st;
-        chunks[d] = ck.chunk;
-    }
-    if (!gspn::fused4_supported(h, w)) return GSPN_ERR_UNSUPPORTED;
-    if (!x || !gy || !dx || !logits || !lam || !dlogits || !dlam || !workspace) return GSPN_ERR_NULL_POINTER;
-    for (int d = 0; d < 4; ++d)
-        if (!logits[d] || !lam[d] || !dlogits[d] || !dlam[d]) return GSPN_ERR_NULL_POINTER;
-    const size_t es = elem_size(dtype);
-    const int64_t need = gspn_backward4_workspace_bytes(n, c, h, w, cw, dtype);
-    if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
-    if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
-    if (!aligned(x, es) || !aligned(gy, es) || !aligned(dx, es)) return GSPN_ERR_MISALIGNED;
-    const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
-    const int64_t wb = n * cw * 3 * h * w * static_cast<int64_t>(es);
-    // outputs: dx, dlam[4], dlogits[4]; none may overlap an input, the
-    // workspace or another output
-    const void* outs[9] = {dx, dlam[0], dlam[1], dlam[2], dlam[3], dlogits[0], dlogits[1], dlogits[2], dlogits[3]};
-    const int64_t ob[9] = {xb, xb, xb, xb, xb, wb, wb, wb, wb};
-    for (int i = 0; i < 9; ++i) {
-        if (!aligned(outs[i], es)) return GSPN_ERR_MISALIGNED;
-        if (overlap(outs[i], ob[i], x, xb) || overlap(outs[i], ob[i], gy, xb) ||
-            overlap(outs[i], ob[i], workspace, need))
-            return GSPN_ERR_ALIASING;
-        for (int d = 0; d < 4; ++d)
-            if (overlap(outs[i], ob[i], logits[d], wb) || overlap(outs[i], ob[i], lam[d], xb)) return GSPN_ERR_ALIASING;
-        for (int j = 0; j < i; ++j)
-            if (overlap(outs[i], ob[i], outs[j], ob[j])) return GSPN_ERR_ALIASING;
-    }
-    for (int d = 0; d < 4; ++d) {
-        if (!aligned(logits[d], es) || !aligned(lam[d], es)) return GSPN_ERR_MISALIGNED;
-        if (overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], xb))
-            return GSPN_ERR_ALIASING;
-    }
-    if (overlap(workspace, need, x, xb) || overlap(workspace, need, gy, xb)) return GSPN_ERR_ALIASING;
-    const hipStream_t st = as_stream(stream);
+    return backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, gy, dx, dlogits, dlam, workspace,
+                         workspace_bytes, dtype, stream, nullptr);
+}
 
-    // Workspace: [fp32 logit-gradient sums of the four directions (shared
-    // logits only)][fp32 forward states H0..H3][x^T][gy^T][dx terms D1..D3].
-    // The states stay fp32 for bf16 storage too: the logit gradient takes
-    // differences of neighbouring states, which bf16 rounding would swamp.
-    const bool shared = cw == 1 && c > 1;
-    const int64_t zsum = 3 * n * h * w;  // floats per direction
-    const int64_t hb = n * c * h * w * 4;  // bytes of one fp32 state map
-    char* ws = static_cast<char*>(workspace);
-    float* sums = reinterpret_cast<float*>(ws);
-    char* hs[4];
-    hs[0] = ws + (shared ? 4 * zsum * 4 : 0);
-    for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
-    char* xt = hs[3] + hb;
-    char* gt = xt + xb;
-    char* dterm[4];
-    dterm[0] = static_cast<char*>(dx);
-    dterm[1] = gt + xb;
-    dterm[2] = dterm[1] + xb;
-    dterm[3] = dterm[2] + xb;
-    const int H = static_cast<int>(h);
-    const int W = static_cast<int>(w);
-    if (gspn::launch_transpose(x, xt, n * c, H, W, dtype, st) != hipSuccess) return GSPN_ERR_HIP;
-    if (gspn::launch_transpose(gy, gt, n * c, H, W, dtype, st) != hipSuccess) return GSPN_ERR_HIP;
-
-    // forward states of every direction (vertical form; horizontal in the
-    // transposed frame)
-    gspn::ScanParams p[4];
-    for (int d = 0; d < 4; ++d) {
-        const bool hz = horizontal(d);
-        p[d].x = hz ? static_cast<const void*>(xt) : x;
-        p[d].wts = logits[d];
-        p[d].lam = lam[d];
-        p[d].out = hs[d];
-        p[d].n = n;
-        p[d].c = c;
-        p[d].cw = cw;
-        p[d].h = hz ? w : h;
-        p[d].w = hz ? h : w;
-        p[d].dir = hz ? d - 2 : d;
-        p[d].chunk = chunks[d];
-        p[d].wts_are_logits = 1;
-        p[d].accumulate = 0;
-        p[d].dtype = dtype;
-        p[d].wdtype = dtype;
-        p[d].odtype = GSPN_F32;
-    }
-    if (gspn::launch_scan4v(p, st) != hipSuccess) return GSPN_ERR_HIP;
-    if (shared && gspn::launch_fill_zero(sums, 4 * zsum, st) != hipSuccess) return GSPN_ERR_HIP;
-
-    gspn::AdjointParams a[4];
-    for (int d = 0; d < 4; ++d) {
-        const bool hz = horizontal(d);
-        a[d].x = hz ? static_cast<const void*>(xt) : x;
-        a[d].g = hz ? static_cast<const void*>(gt) : gy;
-        a[d].lam = lam[d];
-        a[d].logits = logits[d];
-        a[d].hs = hs[d];
-        a[d].dlam = dlam[d];
-        a[d].dz = shared ? static_cast<void*>(sums + d * zsum) : dlogits[d];
-        a[d].dx = dterm[d];
-        a[d].n = n;
-        a[d].c = c;
-        a[d].cw = cw;
-        a[d].S = hz ? w : h;
-        a[d].L = hz ? h : w;
-        a[d].chunk = chunks[d];
-        a[d].reverse = (d == GSPN_B2T || d == GSPN_R2L) ? 1 : 0;
-        a[d].shared = shared ? 1 : 0;
-        a[d].dtype = dtype;
-    }
-    if (gspn::launch_adjoint4(a, st) != hipSuccess) return GSPN_ERR_HIP;
-    // dx = ((D2^T + D3^T) + D0) + D1, D0 written into dx directly
-    if (gspn::launch_combine(dx, dterm[1], dterm[2], dterm[3], n * c, H, W, 1, dtype, st) != hipSuccess)
-        return GSPN_ERR_HIP;
-    if (shared) {
-        for (int d = 0; d < 4; ++d)
-            if (gspn::launch_store_sums(sums + d * zsum, dlogits[d], zsum, dtype, st) != hipSuccess)
-                return GSPN_ERR_HIP;
-    }
-    return GSPN_OK;
+gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
+                                 const void* x, const void* const logits[4], const void* const lam[4],
+                                 const void* gy, void* dx, void* const dlogits[4], void* const dlam[4],
+                                 void* workspace, int64_t workspace_bytes, int dtype, void* stream,
+                                 gspn_stage_times* times) {
+    if (!times) return GSPN_ERR_NULL_POINTER;
+    Timer tm;
+    tm.st = as_stream(stream);
+    const gspn_status s = backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, gy, dx, dlogits, dlam, workspace,
+                                        workspace_bytes, dtype, stream, &tm);
+    const hipError_t e = tm.finish(times);
+    return s != GSPN_OK ? s : from_hip(e);
 }
 
 }  // extern "C"

@@ -37,11 +37,11 @@ STATUS = {
 EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy_project",
            "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4",
            "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_forward4_timed",
-           "gspn_proxy_forward4_timed", "gspn_backward4_workspace_bytes", "gspn_backward4", "gspn_status_string",
-           "gspn_abi_version")
+           "gspn_proxy_forward4_timed", "gspn_backward4_workspace_bytes", "gspn_backward4", "gspn_backward4_timed",
+           "gspn_status_string", "gspn_abi_version")
 
 # gspn_stage, in order.
-STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up")
+STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up", "adjoint", "reduce")
 
 
 # gspn_scan_kernel, in order.
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
             h.gspn_backward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
                                          vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, i64, ci, vp]
             h.gspn_backward4.restype = ci
+            h.gspn_backward4_timed.argtypes = h.gspn_backward4.argtypes + [ctypes.POINTER(StageTimes)]
+            h.gspn_backward4_timed.restype = ci
             h.gspn_status_string.argtypes = [ci]
             h.gspn_status_string.restype = ctypes.c_char_p
             h.gspn_abi_version.argtypes = []
@@ -384,9 +386,11 @@ def backward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
 
 def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                    gy: torch.Tensor, chunk_len: int = 0, workspace: torch.Tensor | None = None,
-                   out: tuple | None = None) -> tuple:
+                   out: tuple | None = None, times: StageTimes | None = None) -> tuple:
     """Gradients of gspn_forward4 for dL/dy = gy: returns (dx, [dlogits_d],
-    [dlam_d]) in the inputs' layouts.  ``out`` may supply those tensors."""
+    [dlam_d]) in the inputs' layouts.  ``out`` may supply those tensors;
+    ``times`` (a StageTimes) selects gspn_backward4_timed and receives the
+    stage durations."""
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
@@ -411,9 +415,12 @@ def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
     vp4 = ctypes.c_void_p * 4
-    _raise(lib().gspn_backward4(n, c, h, w, cw, int(chunk_len), _ptr(x), vp4(*[z.data_ptr() for z in logits]),
-                                vp4(*[l.data_ptr() for l in lams]), _ptr(gy), _ptr(dx),
-                                vp4(*[t.data_ptr() for t in dz]), vp4(*[t.data_ptr() for t in dl]),
-                                _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x),
-                                _stream(x.device)), "gspn_backward4")
+    args = (n, c, h, w, cw, int(chunk_len), _ptr(x), vp4(*[z.data_ptr() for z in logits]),
+            vp4(*[l.data_ptr() for l in lams]), _ptr(gy), _ptr(dx), vp4(*[t.data_ptr() for t in dz]),
+            vp4(*[t.data_ptr() for t in dl]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _dtype_code(x), _stream(x.device))
+    if times is None:
+        _raise(lib().gspn_backward4(*args), "gspn_backward4")
+    else:
+        _raise(lib().gspn_backward4_timed(*args, ctypes.byref(times)), "gspn_backward4_timed")
     return dx, dz, dl

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 4
+    assert lib.gspn_abi_version() == 5
     for code in range(12):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -267,3 +267,7 @@ def test_backward4_validation(lib):
     assert f(dx=dls[1]) == ALIAS                    # dx on dlam[1]
     assert f(dx=WS + 64) == ALIAS                   # dx in the workspace
     assert f(n=0, x=0, gy=0, dx=0, dz=None, dl=None, ws=0) == OK
+    t = G.StageTimes()
+    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, GY, DX, dzs, dls, WS, need, 0, None, None) == NULLP
+    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, GY, DX, dzs, dls, WS, need - 1, 0, None,
+                                    ctypes.byref(t)) == WSPACE

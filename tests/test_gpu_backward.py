@@ -78,6 +78,26 @@ def test_backward_small(shape, shared, chunk, dtype):
     _check_all(got, ref, TOL[dtype], "all outputs")
 
 
+def test_backward_timed_matches_untimed():
+    wl = Workload("case", 1, 3, 40, 72, "bf16", True, 0, 12)
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 4)
+    a = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy)
+    t = G.StageTimes()
+    b = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, times=t)
+    torch.cuda.synchronize()
+    st = t.as_dict()
+    assert st["transpose"]["launches"] == 2 and st["scan"]["launches"] == 1
+    assert st["adjoint"]["launches"] == 1 and st["combine"]["launches"] == 1
+    assert st["reduce"]["launches"] == 5          # clear the sums, store four directions
+    assert st["adjoint"]["ms"] > 0
+    assert torch.equal(a[0], b[0])
+    for d in range(4):
+        assert torch.equal(a[2][d], b[2][d])
+        # shared-logit sums are fp32 atomics: equal up to their summation order
+        assert torch.allclose(a[1][d].float(), b[1][d].float(), rtol=2e-2, atol=1e-2)
+
+
 def test_backward_deterministic_per_channel():
     wl = Workload("case", 2, 3, 30, 50, "f32", False, 0, 9)
     inp = make_inputs(wl, DEV)
