@@ -34,9 +34,15 @@ namespace {
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-// steps in flight: 4 for one position per lane, 2 for two (register budget)
+// steps in flight: 4 for one position and channel per lane, else 2
+// (register budget)
+template <int P, int G>
+constexpr int adj_depth() { return (P == 1 && G == 1) ? 4 : 2; }
+
+// channels per workgroup for channel-shared logits (fewer for two positions
+// per lane: register budget)
 template <int P>
-constexpr int adj_depth() { return P == 1 ? 4 : 2; }
+constexpr int shared_group() { return P == 1 ? 4 : 2; }
 
 struct AdjK {
     const void* x;    // [planes][S][L] (x, or x transposed for horizontal)
@@ -54,7 +60,7 @@ struct AdjK {
     int K;
     int nchunks;
     int reverse;
-    int shared;  // dz is an fp32 sum over channels (atomic adds)
+    int shared;  // dz is an fp32 sum over channels (atomic adds; groups of shared_group<P>() channels)
 };
 
 struct Adj4K {
@@ -62,26 +68,42 @@ struct Adj4K {
     int64_t blocks[4];
 };
 
-template <typename T, int P>
-__device__ __forceinline__ void adj_line(const AdjK& a, int64_t p, int q, float* edge_raw) {
-    constexpr int D = adj_depth<P>();
+// One (plane group, chunk) line of one direction.  G channels of the same
+// image run together (G > 1 only for channel-shared logits): the logits of a
+// position are normalised once for all of them, and the logit gradient, which
+// sums over channels, is accumulated over the G channels in registers before
+// it leaves the workgroup (one atomic add per logit and G channels).
+template <typename T, int P, int G>
+__device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float* edge_raw) {
+    constexpr int D = adj_depth<P, G>();
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
     const int S = a.S;
     const int L = a.L;
     const int64_t plane = static_cast<int64_t>(S) * L;
-    const int64_t nidx = p / a.c;
-    const int64_t ci = p - nidx * a.c;
-    const T* xp = static_cast<const T*>(a.x) + p * plane;
-    const T* gp = static_cast<const T*>(a.g) + p * plane;
-    const T* lp = static_cast<const T*>(a.lam) + p * plane;
-    const float* hp = a.hs + p * plane;
-    const int64_t zplane = (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane;
+    const int64_t groups = (a.c + G - 1) / G;
+    const int64_t nidx = pg / groups;
+    const int64_t c0 = (pg - nidx * groups) * G;  // first channel of the group
+    const int64_t p0 = nidx * a.c + c0;           // its plane
+    int gc[G];                                    // channel offset of each member, clamped
+    bool gok[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        gok[g] = c0 + g < a.c;
+        gc[g] = gok[g] ? g : 0;
+    }
+    const T* xp = static_cast<const T*>(a.x) + p0 * plane;
+    const T* gp = static_cast<const T*>(a.g) + p0 * plane;
+    const T* lp = static_cast<const T*>(a.lam) + p0 * plane;
+    const float* hp = a.hs + p0 * plane;
+    const int64_t zplane = (nidx * a.cw + (a.cw == 1 ? 0 : c0)) * 3 * plane;
     const T* zp = static_cast<const T*>(a.z) + zplane;
-    T* dlp = static_cast<T*>(a.dlam) + p * plane;
-    T* dxp = static_cast<T*>(a.dx) + p * plane;
+    T* dlp = static_cast<T*>(a.dlam) + p0 * plane;
+    T* dxp = static_cast<T*>(a.dx) + p0 * plane;
 
-    auto edge = [&](int b, int which, int lane) -> float& { return edge_raw[(b * 2 + which) * nt + lane]; };
+    auto edge = [&](int b, int side, int g, int lane) -> float& {
+        return edge_raw[((b * 2 + side) * G + g) * nt + lane];
+    };
 
     const int k0 = tid * P;
     int kk[P];
@@ -91,17 +113,17 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t p, int q, float*
         kk[j] = min(k0 + j, L - 1);
         kin[j] = k0 + j < L;
     }
-    const int kl = max(k0 - 1, 0);          // left neighbour of the first position (clamped)
-    const int kr = min(k0 + P, L - 1);      // right neighbour of the last position (clamped)
+    const int kl = max(k0 - 1, 0);      // left neighbour of the first position (clamped)
+    const int kr = min(k0 + P, L - 1);  // right neighbour of the last position (clamped)
 
     const int t0 = q * a.K;
     const int t1 = min(t0 + a.K, S);
     const bool rev = a.reverse != 0;
     auto line_of = [&](int t) { return rev ? S - 1 - t : t; };
 
-    // ring: per step g, x, lambda, z0..z2 per position and h_{t-1} at the
-    // positions plus their two outer neighbours
-    float rg[D][P], rx[D][P], rl[D][P], rz[D][3][P], rh[D][P + 2];
+    // ring: per step and channel g, x, lambda and h_{t-1} at the positions
+    // and their two outer neighbours; the three logits (shared by the group)
+    float rg[D][G][P], rx[D][G][P], rl[D][G][P], rh[D][G][P + 2], rz[D][3][P];
     auto fill = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
         const int tc = max(t, t0);
@@ -109,47 +131,40 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t p, int q, float*
         const int64_t hlo = static_cast<int64_t>(line_of(max(tc - 1, t0))) * L;  // h_{t-1} (clamped)
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-            rg[s][j] = Store<T>::ld(gp + lo + kk[j]);
-            rx[s][j] = Store<T>::ld(xp + lo + kk[j]);
-            rl[s][j] = Store<T>::ld(lp + lo + kk[j]);
 #pragma unroll
             for (int o = 0; o < 3; ++o) rz[s][o][j] = Store<T>::ld(zp + o * plane + lo + kk[j]);
-            rh[s][j + 1] = hp[hlo + kk[j]];
         }
-        rh[s][0] = hp[hlo + kl];
-        rh[s][P + 1] = hp[hlo + kr];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t go = gc[g] * plane;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                rg[s][g][j] = Store<T>::ld(gp + go + lo + kk[j]);
+                rx[s][g][j] = Store<T>::ld(xp + go + lo + kk[j]);
+                rl[s][g][j] = Store<T>::ld(lp + go + lo + kk[j]);
+                rh[s][g][j + 1] = hp[go + hlo + kk[j]];
+            }
+            rh[s][g][0] = hp[go + hlo + kl];
+            rh[s][g][P + 1] = hp[go + hlo + kr];
+        }
     };
 
-    float an[P];     // a_{t+1}
-    float qn0[P];    // w_{t+1}[k,-1] a_{t+1}[k]  (for position k-1)
-    float qn1[P];    // w_{t+1}[k, 0] a_{t+1}[k]
-    float qn2[P];    // w_{t+1}[k,+1] a_{t+1}[k]  (for position k+1)
+    float qn0[G][P];  // w_{t+1}[k,-1] a_{t+1}[k]  (for position k-1)
+    float qn1[G][P];  // w_{t+1}[k, 0] a_{t+1}[k]
+    float qn2[G][P];  // w_{t+1}[k,+1] a_{t+1}[k]  (for position k+1)
 #pragma unroll
-    for (int j = 0; j < P; ++j) an[j] = qn0[j] = qn1[j] = qn2[j] = 0.0f;
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < P; ++j) qn0[g][j] = qn1[g][j] = qn2[g][j] = 0.0f;
     int buf = 0;
 
     auto step = [&](auto slot, auto lastc, int t) {
         constexpr int s = decltype(slot)::value;
         constexpr bool LAST = decltype(lastc)::value != 0;  // t = t1 - 1: no line after it in the chunk
-        float right_in = 0.0f, left_in = 0.0f;  // products from the neighbour lanes
-        if constexpr (!LAST) {
-            right_in = tid + 1 < nt ? edge(buf, 0, tid + 1) : 0.0f;  // w[k0+P,-1] a[k0+P]
-            left_in = tid > 0 ? edge(buf, 1, tid - 1) : 0.0f;        // w[k0-1,+1] a[k0-1]
-        }
         const bool first = (t == t0);  // chunk's first line: logits unused, no h_{t-1}
         const int i = line_of(t);
         const int64_t lo = static_cast<int64_t>(i) * L;
-        float a_t[P];
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            float v = rg[s][j];
-            if constexpr (!LAST) {
-                const float from_r = (j == P - 1) ? right_in : qn0[j + 1];
-                const float from_l = (j == 0) ? left_in : qn2[j - 1];
-                v += (qn1[j] + from_r) + from_l;
-            }
-            a_t[j] = kin[j] ? v : 0.0f;
-        }
+        // this line's weights (and sigmoids), shared by the group
         float w[3][P], sg[3][P];
 #pragma unroll
         for (int j = 0; j < P; ++j) {
@@ -166,21 +181,49 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t p, int q, float*
             w[1][j] = s1 * r;
             w[2][j] = s2 * r;
         }
-        // outputs of this line
+        float dw[P][3];  // weight gradient summed over the group
+#pragma unroll
+        for (int j = 0; j < P; ++j) dw[j][0] = dw[j][1] = dw[j][2] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float right_in = 0.0f, left_in = 0.0f;  // products from the neighbour lanes
+            if constexpr (!LAST) {
+                right_in = tid + 1 < nt ? edge(buf, 0, g, tid + 1) : 0.0f;  // w[k0+P,-1] a[k0+P]
+                left_in = tid > 0 ? edge(buf, 1, g, tid - 1) : 0.0f;        // w[k0-1,+1] a[k0-1]
+            }
+            float a_t[P];
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                float v = rg[s][g][j];
+                if constexpr (!LAST) {
+                    const float from_r = (j == P - 1) ? right_in : qn0[g][j + 1];
+                    const float from_l = (j == 0) ? left_in : qn2[g][j - 1];
+                    v += (qn1[g][j] + from_r) + from_l;
+                }
+                a_t[j] = (kin[j] && gok[g]) ? v : 0.0f;
+            }
+            const int64_t go = gc[g] * plane;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                if (kin[j] && gok[g]) {
+                    Store<T>::st(dlp + go + lo + k0 + j, a_t[j] * rx[s][g][j]);
+                    Store<T>::st(dxp + go + lo + k0 + j, a_t[j] * rl[s][g][j]);
+                }
+#pragma unroll
+                for (int o = 0; o < 3; ++o) dw[j][o] += a_t[j] * rh[s][g][j + o];  // h_{t-1}[k+o-1]
+                qn0[g][j] = first ? 0.0f : w[0][j] * a_t[j];
+                qn1[g][j] = first ? 0.0f : w[1][j] * a_t[j];
+                qn2[g][j] = first ? 0.0f : w[2][j] * a_t[j];
+            }
+        }
+        // logit gradient of this line (none on a chunk's first line)
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-            if (kin[j]) {
-                Store<T>::st(dlp + lo + k0 + j, a_t[j] * rx[s][j]);
-                Store<T>::st(dxp + lo + k0 + j, a_t[j] * rl[s][j]);
-            }
             float dz[3] = {0.0f, 0.0f, 0.0f};
             if (!first) {
-                float dw[3];
+                const float dot = (dw[j][0] * w[0][j] + dw[j][1] * w[1][j]) + dw[j][2] * w[2][j];
 #pragma unroll
-                for (int o = 0; o < 3; ++o) dw[o] = a_t[j] * rh[s][j + o];  // h_{t-1}[k+o-1]
-                const float dot = (dw[0] * w[0][j] + dw[1] * w[1][j]) + dw[2] * w[2][j];
-#pragma unroll
-                for (int o = 0; o < 3; ++o) dz[o] = w[o][j] * (1.0f - sg[o][j]) * (dw[o] - dot);
+                for (int o = 0; o < 3; ++o) dz[o] = w[o][j] * (1.0f - sg[o][j]) * (dw[j][o] - dot);
                 if (k0 + j == 0) dz[0] = 0.0f;
                 if (k0 + j + 1 >= L) dz[2] = 0.0f;
                 if (L == 1) dz[1] = 0.0f;  // a single neighbour: w = [1] whatever its logit
@@ -198,17 +241,12 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t p, int q, float*
             }
         }
         fill(slot, t - D);
-        // products for the previous line (none across a chunk's first line)
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            an[j] = a_t[j];
-            qn0[j] = first ? 0.0f : w[0][j] * a_t[j];
-            qn1[j] = first ? 0.0f : w[1][j] * a_t[j];
-            qn2[j] = first ? 0.0f : w[2][j] * a_t[j];
-        }
         buf ^= 1;
-        edge(buf, 0, tid) = qn0[0];
-        edge(buf, 1, tid) = qn2[P - 1];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            edge(buf, 0, g, tid) = qn0[g][0];
+            edge(buf, 1, g, tid) = qn2[g][P - 1];
+        }
         __syncthreads();
     };
 
@@ -227,7 +265,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t p, int q, float*
     }(std::make_integer_sequence<int, D - 1>{});
 }
 
-template <typename T, int P>
+template <typename T, int P, int G>
 __global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
     extern __shared__ float s_edge_raw[];
     int dir = 0;
@@ -237,9 +275,9 @@ __global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
         ++dir;
     }
     const AdjK& k = a.d[dir];
-    const int64_t p = idx / k.nchunks;
-    const int q = static_cast<int>(idx - p * k.nchunks);
-    adj_line<T, P>(k, p, q, s_edge_raw);
+    const int64_t pg = idx / k.nchunks;
+    const int q = static_cast<int>(idx - pg * k.nchunks);
+    adj_line<T, P, G>(k, pg, q, s_edge_raw);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -268,6 +306,10 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
     Adj4K k;
     int maxL = 1;
     int64_t total = 0;
+    const bool shared = p[0].shared != 0;
+    int maxL0 = 1;
+    for (int d = 0; d < 4; ++d) maxL0 = p[d].L > maxL0 ? static_cast<int>(p[d].L) : maxL0;
+    const int G = shared ? (maxL0 <= 1024 ? shared_group<1>() : shared_group<2>()) : 1;
     for (int d = 0; d < 4; ++d) {
         AdjK& a = k.d[d];
         a.x = p[d].x;
@@ -286,22 +328,28 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
         a.nchunks = static_cast<int>((p[d].S + p[d].chunk - 1) / p[d].chunk);
         a.reverse = p[d].reverse;
         a.shared = p[d].shared;
-        k.blocks[d] = p[d].n * p[d].c * a.nchunks;
+        k.blocks[d] = p[d].n * ((p[d].c + G - 1) / G) * a.nchunks;
         total += k.blocks[d];
         maxL = a.L > maxL ? a.L : maxL;
     }
     const int P = maxL <= 1024 ? 1 : 2;  // lines of at most 2048 positions
     const int lanes = ((maxL + P - 1) / P + 63) / 64 * 64;
-    const size_t lds = 4 * sizeof(float) * static_cast<size_t>(lanes);
+    const size_t lds = 4 * sizeof(float) * static_cast<size_t>(G) * static_cast<size_t>(lanes);
     const dim3 grid(static_cast<unsigned>(total));
     const bool f32 = p[0].dtype == kF32;
+#define GSPN_ADJ_LAUNCH(PP, GG)                                                                                    \
+    do {                                                                                                          \
+        if (f32) hipLaunchKernelGGL((adj4_kernel<float, PP, GG>), grid, dim3(lanes), lds, stream, k);            \
+        else hipLaunchKernelGGL((adj4_kernel<bf16_t, PP, GG>), grid, dim3(lanes), lds, stream, k);               \
+    } while (0)
     if (P == 1) {
-        if (f32) hipLaunchKernelGGL((adj4_kernel<float, 1>), grid, dim3(lanes), lds, stream, k);
-        else hipLaunchKernelGGL((adj4_kernel<bf16_t, 1>), grid, dim3(lanes), lds, stream, k);
+        if (shared) GSPN_ADJ_LAUNCH(1, shared_group<1>());
+        else GSPN_ADJ_LAUNCH(1, 1);
     } else {
-        if (f32) hipLaunchKernelGGL((adj4_kernel<float, 2>), grid, dim3(lanes), lds, stream, k);
-        else hipLaunchKernelGGL((adj4_kernel<bf16_t, 2>), grid, dim3(lanes), lds, stream, k);
+        if (shared) GSPN_ADJ_LAUNCH(2, shared_group<2>());
+        else GSPN_ADJ_LAUNCH(2, 1);
     }
+#undef GSPN_ADJ_LAUNCH
     return hipGetLastError();
 }
 
