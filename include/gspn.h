@@ -236,7 +236,8 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
  * maps of n*c*h*w elements of the storage type (x and dL/dy transposed into
  * the horizontal scan frame, three per-direction dx terms) and, for
  * channel-shared logits over more than one channel (cw == 1 < c), 4 * 3 *
- * n*h*w floats of gradient sums.  Returns -1 for invalid arguments.
+ * n*h*w floats of gradient sums plus the four directions' normalised weights
+ * as in gspn_forward4_workspace_bytes.  Returns -1 for invalid arguments.
  */
 int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype);
 

@@ -559,8 +559,9 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (overlap(workspace, need, x, xb) || overlap(workspace, need, gy, xb)) return GSPN_ERR_ALIASING;
     const hipStream_t st = as_stream(stream);
 
-    // Workspace: [fp32 logit-gradient sums of the four directions (shared
-    // logits only)][fp32 forward states H0..H3][x^T][gy^T][dx terms D1..D3].
+    // Workspace: [fp32 logit-gradient sums and normalised weights of the four
+    // directions (shared logits only)][fp32 forward states H0..H3][x^T][gy^T]
+    // [dx terms D1..D3].
     // The states stay fp32 for bf16 storage too: the logit gradient takes
     // differences of neighbouring states, which bf16 rounding would swamp.
     const bool shared = cw == 1 && c > 1;
@@ -569,7 +570,9 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     char* ws = static_cast<char*>(workspace);
     float* sums = reinterpret_cast<float*>(ws);
     char* hs[4];
-    hs[0] = ws + (shared ? 4 * zsum * 4 : 0);
+    const int64_t wdir = n * h * w * (dtype == GSPN_F32 ? 3 * 4 : 4);  // normalised weight bytes per direction
+    char* wnorm = ws + 4 * zsum * 4;
+    hs[0] = ws + (shared ? 4 * zsum * 4 + 4 * wdir : 0);
     for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
     char* xt = hs[3] + hb;
     char* gt = xt + xb;
@@ -607,6 +610,18 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].dtype = dtype;
         p[d].wdtype = dtype;
         p[d].odtype = GSPN_F32;
+        if (shared) {
+            // channel-shared logits: normalised once, as in the forward
+            char* wd = wnorm + d * wdir;
+            const hipError_t e = timed(tm, GSPN_STAGE_NORMALIZE, [&] {
+                return dtype == GSPN_F32 ? gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32)
+                                         : gspn::launch_normalize_pair(d, n, h, w, logits[d], wd, dtype, st);
+            });
+            if (e != hipSuccess) return GSPN_ERR_HIP;
+            p[d].wts = wd;
+            p[d].wts_are_logits = 0;
+            p[d].wdtype = dtype == GSPN_F32 ? GSPN_F32 : gspn::kPairF16;
+        }
     }
     int kind = GSPN_SCAN_FUSED4;
     if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
@@ -715,10 +730,13 @@ gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w
 int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype) {
     if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
     const int64_t elems = checked_product({n, c, h, w});
-    // x^T, gy^T and three dx terms in the storage type; four fp32 state maps
+    // x^T, gy^T and three dx terms in the storage type; four fp32 state maps;
+    // for channel-shared logits over several channels the gradient sums and
+    // the normalised weights of the recomputed forward
     const int64_t maps = 5 * elems * static_cast<int64_t>(elem_size(dtype)) + 4 * elems * 4;
-    const int64_t sums = (cw == 1 && c > 1) ? 4 * 3 * checked_product({n, h, w}) * 4 : 0;
-    return sums + maps;
+    const int64_t nhw = checked_product({n, h, w});
+    const int64_t shared = (cw == 1 && c > 1) ? 4 * 3 * nhw * 4 + 4 * nhw * (dtype == GSPN_F32 ? 3 * 4 : 4) : 0;
+    return shared + maps;
 }
 
 gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,

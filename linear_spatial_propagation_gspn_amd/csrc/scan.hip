@@ -30,6 +30,8 @@ extern template hipError_t launch_fused4lp<float, float, false>(const Scan4K&, i
 extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4v<bf16_t, bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true, float>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4v<bf16_t, WPair, float>(const Scan4K&, int, int, int, hipStream_t);
+extern template hipError_t launch_fused4lp<bf16_t, WPair, false, float>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, WPair, false>(const Scan4K&, int, hipStream_t);
 
 namespace {
@@ -161,9 +163,11 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
     // length, p[2..3] another
     const int l01 = static_cast<int>(p[0].w);
     const int l23 = static_cast<int>(p[2].w);
-    // fp32 outputs of a bf16 scan (states kept at full precision): logits only
+    // fp32 outputs of a bf16 scan (states kept at full precision): logits or
+    // half-pair weights
     const bool wide_out = p[0].dtype == kBF16 && p[0].odtype == kF32;
-    if (wide_out && (p[0].wdtype != kBF16 || !p[0].wts_are_logits)) return hipErrorInvalidValue;
+    if (wide_out && !((p[0].wdtype == kBF16 && p[0].wts_are_logits) || p[0].wdtype == kPairF16))
+        return hipErrorInvalidValue;
     if (lp_eligible(p)) {
         const int P = p[0].dtype == kF32 ? 4 : 8;
         Scan4K k;
@@ -182,7 +186,10 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
             return logits ? launch_fused4lp<float, float, true>(k, nthreads, stream)
                           : launch_fused4lp<float, float, false>(k, nthreads, stream);
         }
-        if (p[0].wdtype == kPairF16) return launch_fused4lp<bf16_t, WPair, false>(k, nthreads, stream);
+        if (p[0].wdtype == kPairF16) {
+            return wide_out ? launch_fused4lp<bf16_t, WPair, false, float>(k, nthreads, stream)
+                            : launch_fused4lp<bf16_t, WPair, false>(k, nthreads, stream);
+        }
         if (wide_out) return launch_fused4lp<bf16_t, bf16_t, true, float>(k, nthreads, stream);
         return launch_fused4lp<bf16_t, bf16_t, true>(k, nthreads, stream);
     }
@@ -200,7 +207,10 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
     const int b = lanes_for(l23, ph);
     const int nthreads = a > b ? a : b;
     if (p[0].dtype == kF32) return launch_fused4v<float, float>(k, pv, ph, nthreads, stream);
-    if (p[0].wdtype == kPairF16) return launch_fused4v<bf16_t, WPair>(k, pv, ph, nthreads, stream);
+    if (p[0].wdtype == kPairF16) {
+        return wide_out ? launch_fused4v<bf16_t, WPair, float>(k, pv, ph, nthreads, stream)
+                        : launch_fused4v<bf16_t, WPair>(k, pv, ph, nthreads, stream);
+    }
     if (wide_out) return launch_fused4v<bf16_t, bf16_t, float>(k, pv, ph, nthreads, stream);
     return launch_fused4v<bf16_t, bf16_t>(k, pv, ph, nthreads, stream);
 }

@@ -7,5 +7,8 @@ namespace gspn {
 template hipError_t launch_fused4<bf16_t, WPair>(const Scan4K&, int, int, int, hipStream_t);
 template hipError_t launch_fused4v<bf16_t, WPair>(const Scan4K&, int, int, int, hipStream_t);
 template hipError_t launch_fused4lp<bf16_t, WPair, false>(const Scan4K&, int, hipStream_t);
+// fp32 states (the backward pass's recomputed forward)
+template hipError_t launch_fused4v<bf16_t, WPair, float>(const Scan4K&, int, int, int, hipStream_t);
+template hipError_t launch_fused4lp<bf16_t, WPair, false, float>(const Scan4K&, int, hipStream_t);
 
 }  // namespace gspn

@@ -248,7 +248,8 @@ def test_backward4_validation(lib):
     GY, DX, WS = 0x70000000, 0x71000000, 0x72000000
     need = lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 2, 0)
     assert need == 9 * 2 * 64 * 4
-    assert lib.gspn_backward4_workspace_bytes(1, 3, 8, 8, 1, 1) == 4 * 3 * 64 * 4 + 4 * 3 * 64 * 4 + 5 * 3 * 64 * 2
+    assert lib.gspn_backward4_workspace_bytes(1, 3, 8, 8, 1, 1) == (4 * 3 * 64 * 4 + 4 * 64 * 4 + 4 * 3 * 64 * 4 +
+                                                                   5 * 3 * 64 * 2)
     assert lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
 
     def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, gy=GY, dx=DX, dz=dzs, dl=dls, ws=WS, wsb=need, dt=0):
