@@ -31,6 +31,36 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+#ifndef GSPN_PROJ_NT
+#define GSPN_PROJ_NT 1  // bit 0: activation loads, bit 1: output stores (measured slower)
+#endif
+
+// Activation loads and output stores: each touched once per projection;
+// with GSPN_PROJ_NT they carry the non-temporal hint.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ldx(const uint2* p) {
+    if constexpr ((GSPN_PROJ_NT & 1) != 0) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        return make_uint2(v.x, v.y);
+    } else {
+        return *p;
+    }
+}
+__device__ __forceinline__ void stx(uint2* p, uint2 v) {
+    if constexpr ((GSPN_PROJ_NT & 2) != 0) {
+        __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+    } else {
+        *p = v;
+    }
+}
+__device__ __forceinline__ void stx(uint32_t* p, uint32_t v) {
+    if constexpr ((GSPN_PROJ_NT & 2) != 0) {
+        __builtin_nontemporal_store(v, p);
+    } else {
+        *p = v;
+    }
+}
+
 __device__ __forceinline__ __bf16 as_bf(uint32_t bits16) {
     return __builtin_bit_cast(__bf16, static_cast<uint16_t>(bits16));
 }
@@ -71,7 +101,7 @@ __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(con
         const int cc = b.ok ? c0 : cin - 8;  // clamped into the tensor (cin % 8 == 0)
         b.a = *reinterpret_cast<const uint4*>(wrow + cc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b.v[e] = *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(cc + e) * hw);
+        for (int e = 0; e < 8; ++e) b.v[e] = ldx(reinterpret_cast<const uint2*>(src + static_cast<int64_t>(cc + e) * hw));
     };
 
     floatx4 acc[4];
@@ -115,7 +145,7 @@ __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(con
             uint2 w;
             w.x = static_cast<uint32_t>(f32_to_bf16(acc[0][i])) | (static_cast<uint32_t>(f32_to_bf16(acc[1][i])) << 16);
             w.y = static_cast<uint32_t>(f32_to_bf16(acc[2][i])) | (static_cast<uint32_t>(f32_to_bf16(acc[3][i])) << 16);
-            *reinterpret_cast<uint2*>(dst + static_cast<int64_t>(o) * hw) = w;
+            stx(reinterpret_cast<uint2*>(dst + static_cast<int64_t>(o) * hw), w);
         }
     }
 }
@@ -165,7 +195,7 @@ __global__ __launch_bounds__(256) void project_narrow_in_mfma(const bf16_t* __re
             if (o < cout) {
                 const uint32_t word = static_cast<uint32_t>(f32_to_bf16(ce[i])) |
                                       (static_cast<uint32_t>(f32_to_bf16(co[i])) << 16);
-                *reinterpret_cast<uint32_t*>(dst + static_cast<int64_t>(o) * hw) = word;
+                stx(reinterpret_cast<uint32_t*>(dst + static_cast<int64_t>(o) * hw), word);
             }
         }
     }

@@ -55,6 +55,9 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 #ifndef GSPN_LP_STREAM_AUX
 #define GSPN_LP_STREAM_AUX 2
 #endif
+#ifndef GSPN_LP_X_AUX
+#define GSPN_LP_X_AUX 0
+#endif
 
 // W 32-bit words from the buffer at voff + soff (W a multiple of 4).
 template <int W, int AUX = 0>
@@ -143,7 +146,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     auto fill = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
         const uint32_t i = line_of(min(t, t1 - 1));
-        lp::load_words<WT>(sx[s], rx, vt, i * rowT);
+        lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, i * rowT);
         lp::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, i * rowT);
         // logits are per channel here unless a single channel shares them;
         // normalised weights are always shared

@@ -40,6 +40,35 @@ struct alignas(16) Vec16 {
     T e[16 / sizeof(T)];
 };
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte vector load / store, with the non-temporal hint when NT (data the
+// kernel touches once and nothing reads back soon).
+template <bool NT, typename V>
+__device__ __forceinline__ V vld(const V* p) {
+    if constexpr (NT) {
+        return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+    } else {
+        return *p;
+    }
+}
+
+template <bool NT, typename V>
+__device__ __forceinline__ void vst(V* p, const V& v) {
+    if constexpr (NT) {
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+    } else {
+        *p = v;
+    }
+}
+
+#ifndef GSPN_COMBINE_NT
+#define GSPN_COMBINE_NT 1
+#endif
+#ifndef GSPN_TRANSPOSE_NT
+#define GSPN_TRANSPOSE_NT 3  // bit 0: reads, bit 1: writes with the non-temporal hint
+#endif
+
 // Moves one 64 x 64 tile of a (rows x cols) plane between global memory and
 // an fp32 LDS tile, 16 bytes per lane per access along the rows: row r, column
 // c of the tile is element (r0 + r, c0 + c) of the plane.  vec: the plane's
@@ -52,7 +81,7 @@ struct TileIO {
     static constexpr int LPR = kTile / VW;                        // lanes per tile row
     static constexpr int RPP = kThreads / LPR;                    // rows per pass
 
-    template <typename F>
+    template <bool NT = false, typename F>
     static __device__ __forceinline__ void read(const T* plane, int rows, int cols, int r0, int c0, bool vec,
                                                 F&& put) {
         const int lr = threadIdx.x / LPR;
@@ -64,7 +93,7 @@ struct TileIO {
             const int gc = c0 + lc;
             const T* src = plane + static_cast<int64_t>(gr) * cols + gc;
             if (vec && gr < rows && gc + VW <= cols) {
-                const Vec16<T> v = *reinterpret_cast<const Vec16<T>*>(src);
+                const Vec16<T> v = vld<NT>(reinterpret_cast<const Vec16<T>*>(src));
 #pragma unroll
                 for (int e = 0; e < VW; ++e) put(r, lc + e, Store<T>::ld(&v.e[e]));
             } else {
@@ -75,7 +104,7 @@ struct TileIO {
         }
     }
 
-    template <typename F>
+    template <bool NT = false, typename F>
     static __device__ __forceinline__ void write(T* plane, int rows, int cols, int r0, int c0, bool vec, F&& get) {
         const int lr = threadIdx.x / LPR;
         const int lc = (threadIdx.x % LPR) * VW;
@@ -90,7 +119,7 @@ struct TileIO {
                 Vec16<T> v;
 #pragma unroll
                 for (int e = 0; e < VW; ++e) Store<T>::st(&v.e[e], get(r, lc + e, dst + e));
-                *reinterpret_cast<Vec16<T>*>(dst) = v;
+                vst<NT>(reinterpret_cast<Vec16<T>*>(dst), v);
             } else {
 #pragma unroll
                 for (int e = 0; e < VW; ++e)
@@ -107,11 +136,11 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict
     __shared__ float tile[kTile][kTile + 1];
     const TileIndex ti = tile_of(blockIdx.x, R, Cc);
     const int64_t plane = static_cast<int64_t>(R) * Cc;
-    TileIO<T>::read(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_src,
+    TileIO<T>::template read<(GSPN_TRANSPOSE_NT & 1) != 0>(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_src,
                     [&](int r, int c, float v) { tile[r][c] = v; });
     __syncthreads();
     // destination plane is Cc x R: its row c holds source column c
-    TileIO<T>::write(dst + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_dst,
+    TileIO<T>::template write<(GSPN_TRANSPOSE_NT & 2) != 0>(dst + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_dst,
                      [&](int c, int r, const T*) { return tile[r][c]; });
 }
 
@@ -132,14 +161,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const T* __rest
     auto add_t = [&](const T* z) {  // transposed source: its row c is column c of the tile
         if (any) __syncthreads();
         const bool first = !any;
-        TileIO<T>::read(z + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_z,
+        TileIO<T>::template read<GSPN_COMBINE_NT != 0>(z + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_z,
                         [&](int c, int r, float v) { tile[r][c] = first ? v : tile[r][c] + v; });
         any = true;
     };
     auto add_a = [&](const T* src) {  // array-frame source
         if (any) __syncthreads();
         const bool first = !any;
-        TileIO<T>::read(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
+        TileIO<T>::template read<GSPN_COMBINE_NT != 0>(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
                         [&](int r, int c, float v) { tile[r][c] = first ? v : tile[r][c] + v; });
         any = true;
     };
@@ -148,8 +177,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const T* __rest
     if (accumulate) add_a(y);
     if (a) add_a(a);
     __syncthreads();
-    TileIO<T>::write(y + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
-                     [&](int r, int c, const T*) { return any ? tile[r][c] : 0.0f; });
+    TileIO<T>::template write<GSPN_COMBINE_NT != 0>(y + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
+                                                    [&](int r, int c, const T*) { return any ? tile[r][c] : 0.0f; });
 }
 
 int64_t tiles_for(int64_t planes, int R, int Cc) {
