@@ -22,7 +22,7 @@
 // reading the forward states h recomputed beforehand into separate maps.  The
 // per-step inputs of the next D steps are in flight (ring slots refilled as
 // soon as read, compile-time slot indices, addresses clamped instead of
-// guarded).
+// guarded).  Streams touched once carry the non-temporal hint.
 #include <utility>
 
 #include "device.hpp"
@@ -132,16 +132,19 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
 #pragma unroll
         for (int j = 0; j < P; ++j) {
 #pragma unroll
-            for (int o = 0; o < 3; ++o) rz[s][o][j] = Store<T>::ld(zp + o * plane + lo + kk[j]);
+            for (int o = 0; o < 3; ++o) {
+                // per-channel logits are read once; a channel group's shared logits are re-read
+                rz[s][o][j] = G == 1 ? ld_stream(zp + o * plane + lo + kk[j]) : Store<T>::ld(zp + o * plane + lo + kk[j]);
+            }
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t go = gc[g] * plane;
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                rg[s][g][j] = Store<T>::ld(gp + go + lo + kk[j]);
+                rg[s][g][j] = ld_stream(gp + go + lo + kk[j]);
                 rx[s][g][j] = Store<T>::ld(xp + go + lo + kk[j]);
-                rl[s][g][j] = Store<T>::ld(lp + go + lo + kk[j]);
+                rl[s][g][j] = ld_stream(lp + go + lo + kk[j]);
                 rh[s][g][j + 1] = hp[go + hlo + kk[j]];
             }
             rh[s][g][0] = hp[go + hlo + kl];
@@ -206,8 +209,8 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 if (kin[j] && gok[g]) {
-                    Store<T>::st(dlp + go + lo + k0 + j, a_t[j] * rx[s][g][j]);
-                    Store<T>::st(dxp + go + lo + k0 + j, a_t[j] * rl[s][g][j]);
+                    st_stream(dlp + go + lo + k0 + j, a_t[j] * rx[s][g][j]);
+                    st_stream(dxp + go + lo + k0 + j, a_t[j] * rl[s][g][j]);
                 }
 #pragma unroll
                 for (int o = 0; o < 3; ++o) dw[j][o] += a_t[j] * rh[s][g][j + o];  // h_{t-1}[k+o-1]
@@ -236,7 +239,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 } else {
                     T* dzp = static_cast<T*>(a.dz) + zplane;
 #pragma unroll
-                    for (int o = 0; o < 3; ++o) Store<T>::st(dzp + o * plane + lo + k0 + j, dz[o]);
+                    for (int o = 0; o < 3; ++o) st_stream(dzp + o * plane + lo + k0 + j, dz[o]);
                 }
             }
         }

@@ -55,6 +55,26 @@ __device__ __forceinline__ float pair_hi(uint32_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b >> 16)));
 }
 
+// Element loads / stores with the non-temporal hint, for data a kernel
+// touches once (widened / rounded like Store<T>).
+template <typename T>
+__device__ __forceinline__ float ld_stream(const T* p) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
+    } else {
+        return bf16_to_f32(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, float v) {
+    if constexpr (sizeof(T) == 4) {
+        __builtin_nontemporal_store(v, reinterpret_cast<float*>(p));
+    } else {
+        __builtin_nontemporal_store(f32_to_bf16(v), reinterpret_cast<uint16_t*>(p));
+    }
+}
+
 // 1 / d to within about half an ulp: the hardware reciprocal (1 ulp) refined
 // by one Newton step.
 __device__ __forceinline__ float recip(float d) {
