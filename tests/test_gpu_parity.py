@@ -353,6 +353,49 @@ def test_full_size_sampled_planes(name, planes):
         assert e <= TOL[wl.dtype]
 
 
+def test_full_size_no_workspace_sampled_planes():
+    """The 1024^2, B=16, C=8 workload without a workspace: one launch per
+    direction, horizontal lines as per-lane row tiles."""
+    wl = WORKLOADS["profile"]
+    _say("full profile, no workspace")
+    inp = make_inputs(wl, DEV)
+    got, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk)
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "scan_kernel" and times["scan"]["launches"] == 4
+    for n, c in [(0, 0), (9, 5)]:
+        x, zs, ls = _plane_inputs(inp, wl, n, c)
+        ref = oracle.forward4(x, zs, ls, chunk=wl.chunk)
+        e = _err(got[n:n + 1, c:c + 1], ref)
+        _say("  plane (%d, %d): normwise error %.3g" % (n, c, e))
+        assert e <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shared", [False, True])
+def test_forward4_unaligned_views(dtype, shared):
+    """Tensors that are element-aligned but not 16-byte aligned (views one
+    element into a larger buffer): the vector kernels must step aside."""
+    n, c, h, w = 1, 3, 40, 72
+    wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=shared, seed=51)
+    inp = make_inputs(wl, DEV)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    x = shifted(inp["x"])
+    zs = [shifted(z) for z in inp["logits"]]
+    ls = [shifted(l) for l in inp["lam"]]
+    out = shifted(torch.zeros_like(inp["x"]))
+    got, times = G.gspn_forward4_timed(x, zs, ls, out=out, workspace=G.forward4_workspace(x, wl.cw))
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "scan4v_kernel", times["scan_kernel"]
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"])
+    assert _err(got, ref) <= TOL[dtype]
+
+
 def test_full_size_proxy_sampled_channels():
     wl = WORKLOADS["proxy"]
     _say("full proxy")
