@@ -20,6 +20,14 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float v) {
     return __builtin_bit_cast(bf16_t, static_cast<__bf16>(v));
 }
 
+// Two values rounded the same way, packed low-half first in one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    typedef float f32x2_v __attribute__((ext_vector_type(2)));
+    const f32x2_v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+}
+
 template <typename T>
 struct Store;
 

@@ -165,35 +165,50 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     auto step = [&](auto slot, auto firstc, int t) {
         constexpr int s = decltype(slot)::value;
         constexpr bool FIRST = decltype(firstc)::value != 0;
-        float u[P];
-#pragma unroll
-        for (int j = 0; j < P; ++j) u[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
         float hn[P];
         if constexpr (FIRST) {
 #pragma unroll
-            for (int j = 0; j < P; ++j) hn[j] = u[j];
+            for (int j = 0; j < P; ++j) hn[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+        } else if constexpr (PAIR) {
+            // h + w_{k-1} (h_{k-1} - h) + w_{k+1} (h_{k+1} - h) + lambda x: the
+            // same row-stochastic combination with the centre weight
+            // (1 - w_{k-1} - w_{k+1}) eliminated, so the half-precision side
+            // weights enter the fused multiply-adds as they are stored, and two
+            // neighbouring positions share one difference.
+            const float eleft = wave > 0 ? edges[buf][wave - 1][1] : 0.0f;
+            const float eright = wave + 1 < nwaves ? edges[buf][wave + 1][0] : 0.0f;
+            const float dl = lp::shift_from_lower_lane(h[P - 1]);
+            const float dr = lp::shift_from_upper_lane(h[0]);
+            const float left = lane == 0 ? eleft : dl;
+            const float right = lane == 63 ? eright : dr;
+            float dd[P + 1];  // dd[j] = h[j] - h[j - 1], with h[-1] = left and h[P] = right
+            dd[0] = h[0] - left;
+#pragma unroll
+            for (int j = 1; j < P; ++j) dd[j] = h[j] - h[j - 1];
+            dd[P] = right - h[P - 1];
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const float base = __builtin_fmaf(lp::elem<T, WT>(sl[s], j), lp::elem<T, WT>(sx[s], j), h[j]);
+                hn[j] = __builtin_fmaf(pair_hi(sz[s][0][j]), dd[j + 1], __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base));
+            }
         } else {
+            float u[P];
+#pragma unroll
+            for (int j = 0; j < P; ++j) u[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
             float w[3][P];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                if constexpr (PAIR) {
-                    // missing neighbours were stored as exact zeros
-                    w[0][j] = pair_lo(sz[s][0][j]);
-                    w[2][j] = pair_hi(sz[s][0][j]);
-                    w[1][j] = (1.0f - w[0][j]) - w[2][j];
+                const float z0 = lp::elem<TW, WW>(sz[s][0], j);
+                const float z1 = lp::elem<TW, WW>(sz[s][NZ > 1 ? 1 : 0], j);
+                const float z2 = lp::elem<TW, WW>(sz[s][NZ > 2 ? 2 : 0], j);
+                if constexpr (LOGITS) {
+                    const bool hl = j > 0 || has_l0;
+                    const bool hr = j < P - 1 || has_rP;
+                    normalise_row(z0, z1, z2, hl, hr, w[0][j], w[1][j], w[2][j]);
                 } else {
-                    const float z0 = lp::elem<TW, WW>(sz[s][0], j);
-                    const float z1 = lp::elem<TW, WW>(sz[s][NZ > 1 ? 1 : 0], j);
-                    const float z2 = lp::elem<TW, WW>(sz[s][NZ > 2 ? 2 : 0], j);
-                    if constexpr (LOGITS) {
-                        const bool hl = j > 0 || has_l0;
-                        const bool hr = j < P - 1 || has_rP;
-                        normalise_row(z0, z1, z2, hl, hr, w[0][j], w[1][j], w[2][j]);
-                    } else {
-                        w[0][j] = z0;
-                        w[1][j] = z1;
-                        w[2][j] = z2;
-                    }
+                    w[0][j] = z0;
+                    w[1][j] = z1;
+                    w[2][j] = z2;
                 }
             }
             // neighbours from the previous step: inside the wave by DPP, across
@@ -212,8 +227,12 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
             }
         }
         fill(slot, t + D);
+        // only h[0] of a lane past the line reaches a position on it (as the
+        // right neighbour of the line's last position, whose weight to it is
+        // 0), so only h[0] is cleared there
+        h[0] = active ? hn[0] : 0.0f;
 #pragma unroll
-        for (int j = 0; j < P; ++j) h[j] = active ? hn[j] : 0.0f;
+        for (int j = 1; j < P; ++j) h[j] = hn[j];
         if (active) {
             constexpr int WO = P * static_cast<int>(sizeof(TO)) / 4;  // output words per lane
             uint32_t ow[WO];
@@ -222,9 +241,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
                 for (int e = 0; e < WO; ++e) ow[e] = __float_as_uint(h[e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < WO; ++e)
-                    ow[e] = static_cast<uint32_t>(f32_to_bf16(h[2 * e])) |
-                            (static_cast<uint32_t>(f32_to_bf16(h[2 * e + 1])) << 16);
+                for (int e = 0; e < WO; ++e) ow[e] = pack_bf16x2(h[2 * e], h[2 * e + 1]);
             }
 #pragma unroll
             for (int v = 0; v < WO / 4; ++v) {

@@ -206,6 +206,28 @@ def test_forward4_shared_weights(shape, chunk, dtype):
     assert _err(got, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("chunk", [0, 5])
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("dtype,shape", [
+    ("bf16", (1, 2, 24, 560)),   # 70 lanes of 8 positions: a second wave with 6 lanes on the line
+    ("f32", (1, 2, 36, 280)),    # 70 lanes of 4 positions
+    ("bf16", (2, 1, 16, 1032)),  # 129 lanes: a third wave with one lane on the line
+])
+def test_long_line_kernel_partial_waves(dtype, shape, shared, chunk):
+    """The long-line kernel with lines that end inside a wave after the first:
+    the lanes past the line must not leak into it."""
+    n, c, h, w = shape
+    wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=shared, chunk=chunk, seed=61 + w)
+    _say("long-line partial waves %s %s shared=%s chunk=%d" % (shape, dtype, shared, chunk))
+    inp = make_inputs(wl, DEV)
+    got, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk,
+                                       workspace=G.forward4_workspace(inp["x"], wl.cw))
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "scan4lp_kernel", times["scan_kernel"]
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk)
+    assert _err(got, ref) <= TOL[dtype]
+
+
 def test_forward4_closed_form_constant_input():
     # lambda = 1, x = c: every direction's h at scan step t is (t+1) c, so the
     # merged output is (H + W + 2) c everywhere, whatever the logits.
