@@ -132,6 +132,8 @@ hipError_t launch_scan4(const ScanParams (&p)[4], hipStream_t stream) {
     }
     k.interleave = (k.blocks[0] == k.blocks[1] && k.blocks[1] == k.blocks[2] &&
                     k.blocks[2] == k.blocks[3]) ? 1 : 0;
+    k.group = 1;
+    k.planes = p[0].n * p[0].c;
     const int lv = lanes_for(Lv, pv);
     const int lh = lanes_for(Lh, ph);
     const int nthreads = lv > lh ? lv : lh;
@@ -145,6 +147,11 @@ hipError_t launch_scan4(const ScanParams (&p)[4], hipStream_t stream) {
 // aligned tensors: its per-step work is a fraction of the one-position-per-
 // lane kernel's, which matters most when few lines run (the step latency
 // decides the time) and still pays when the GPU is full.
+#ifndef GSPN_LP_MAX_GROUP
+#define GSPN_LP_MAX_GROUP 2
+#endif
+constexpr int64_t kLpGroupMinBlocks = 2048;  // workgroups left after grouping: 8 per CU
+
 bool lp_eligible(const ScanParams (&p)[4]) {
     const int esz = p[0].dtype == kF32 ? 4 : 2;
     const int P = 16 / esz;
@@ -170,17 +177,30 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
         return hipErrorInvalidValue;
     if (lp_eligible(p)) {
         const int P = p[0].dtype == kF32 ? 4 : 8;
+        const int a = lanes_for(l01, P);
+        const int b = lanes_for(l23, P);
+        const int lanes = a > b ? a : b;
+        const bool logits = p[0].wts_are_logits != 0;
+        // Normalised weights are shared by every channel: when the launch is
+        // large enough to fill the GPU anyway, run several channels of a line
+        // in one workgroup so that their weight loads coincide.
+        const int64_t planes = p[0].n * p[0].c;
+        int group = 1;
+        if (!logits) {
+            while (group * 2 <= GSPN_LP_MAX_GROUP && group * 2 * lanes <= lp::kMaxLanes &&
+                   (planes + group * 2 - 1) / (group * 2) * 4 >= kLpGroupMinBlocks)
+                group *= 2;
+        }
         Scan4K k;
         for (int d = 0; d < 4; ++d) {
             k.d[d] = make_args(p[d], P);
-            k.blocks[d] = p[d].n * p[d].c * k.d[d].nchunks;
+            k.blocks[d] = (planes + group - 1) / group * k.d[d].nchunks;
         }
         k.interleave = (k.blocks[0] == k.blocks[1] && k.blocks[1] == k.blocks[2] &&
                         k.blocks[2] == k.blocks[3]) ? 1 : 0;
-        const int a = lanes_for(l01, P);
-        const int b = lanes_for(l23, P);
-        const int nthreads = a > b ? a : b;
-        const bool logits = p[0].wts_are_logits != 0;
+        k.group = group;
+        k.planes = planes;
+        const int nthreads = lanes * group;
         if (kind) *kind = 3;
         if (p[0].dtype == kF32) {
             return logits ? launch_fused4lp<float, float, true>(k, nthreads, stream)
@@ -203,6 +223,8 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
     }
     k.interleave = (k.blocks[0] == k.blocks[1] && k.blocks[1] == k.blocks[2] &&
                     k.blocks[2] == k.blocks[3]) ? 1 : 0;
+    k.group = 1;
+    k.planes = p[0].n * p[0].c;
     const int a = lanes_for(l01, pv);
     const int b = lanes_for(l23, ph);
     const int nthreads = a > b ? a : b;

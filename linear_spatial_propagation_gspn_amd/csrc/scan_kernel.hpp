@@ -471,6 +471,8 @@ struct Scan4K {
     ScanK d[4];
     int64_t blocks[4];
     int interleave;
+    int group;       // long-line kernel: planes per workgroup
+    int64_t planes;  // long-line kernel: planes per direction (n * c)
 };
 
 template <typename T, typename TW, int PV, int PH>

@@ -92,12 +92,16 @@ __device__ __forceinline__ float shift_from_upper_lane(float v) {  // lane i get
 
 }  // namespace lp
 
-// One (plane, chunk) line of a vertical-form scan.  T: storage of x, lambda
-// and the output; TW: storage of the weights (WPair: packed half pairs of
+// One (plane, chunk) line of a vertical-form scan, run by `nwaves` waves of
+// the workgroup starting at wave `wave0`; tid is the thread's index among
+// them.  valid = false: the waves only keep step with the workgroup's
+// barriers (p is then any existing plane).  T: storage of x, lambda and the
+// output; TW: storage of the weights (WPair: packed half pairs of
 // channel-shared weights); LOGITS: the weights are logits normalised here
 // (else normalised weights, zero outside the line).
 template <typename T, typename TW, bool LOGITS, typename TO = T>
-__device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
+__device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool valid, int tid, int wave0,
+                                        int nwaves) {
     constexpr int P = 16 / static_cast<int>(sizeof(T));              // positions per lane
     constexpr int WT = P * static_cast<int>(sizeof(T)) / 4;          // words per lane: x, lambda, out
     constexpr bool PAIR = std::is_same_v<TW, WPair>;
@@ -107,10 +111,8 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
     constexpr int D = GSPN_LP_DEPTH;                                  // steps in flight
     __shared__ float edges[2][lp::kMaxWaves][2];
 
-    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
     const int S = a.S;
     const int L = a.L;
     const int64_t plane = static_cast<int64_t>(S) * L;
@@ -125,7 +127,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
                              NZ * plane * ZB);
 
     const int k0 = tid * P;
-    const bool active = k0 < L;
+    const bool active = valid && k0 < L;
     const int k0c = active ? k0 : L - P;  // lanes past the line read its last vector (unused)
     const uint32_t vt = static_cast<uint32_t>(k0c) * sizeof(T);
     const uint32_t vw = static_cast<uint32_t>(k0c) * ZB;
@@ -175,8 +177,8 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
             // (1 - w_{k-1} - w_{k+1}) eliminated, so the half-precision side
             // weights enter the fused multiply-adds as they are stored, and two
             // neighbouring positions share one difference.
-            const float eleft = wave > 0 ? edges[buf][wave - 1][1] : 0.0f;
-            const float eright = wave + 1 < nwaves ? edges[buf][wave + 1][0] : 0.0f;
+            const float eleft = wave > 0 ? edges[buf][wave0 + wave - 1][1] : 0.0f;
+            const float eright = wave + 1 < nwaves ? edges[buf][wave0 + wave + 1][0] : 0.0f;
             const float dl = lp::shift_from_lower_lane(h[P - 1]);
             const float dr = lp::shift_from_upper_lane(h[0]);
             const float left = lane == 0 ? eleft : dl;
@@ -213,8 +215,8 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
             }
             // neighbours from the previous step: inside the wave by DPP, across
             // wave edges from LDS (0 beyond the line)
-            const float eleft = wave > 0 ? edges[buf][wave - 1][1] : 0.0f;
-            const float eright = wave + 1 < nwaves ? edges[buf][wave + 1][0] : 0.0f;
+            const float eleft = wave > 0 ? edges[buf][wave0 + wave - 1][1] : 0.0f;
+            const float eright = wave + 1 < nwaves ? edges[buf][wave0 + wave + 1][0] : 0.0f;
             const float dl = lp::shift_from_lower_lane(h[P - 1]);
             const float dr = lp::shift_from_upper_lane(h[0]);
             const float left = lane == 0 ? eleft : dl;
@@ -251,8 +253,8 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q) {
             }
         }
         buf ^= 1;
-        if (lane == 0) edges[buf][wave][0] = h[0];
-        if (lane == 63) edges[buf][wave][1] = h[P - 1];
+        if (lane == 0) edges[buf][wave0 + wave][0] = h[0];
+        if (lane == 63) edges[buf][wave0 + wave][1] = h[P - 1];
         __syncthreads();
     };
 
@@ -293,9 +295,19 @@ __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) 
         }
     }
     const ScanK& k = a.d[dir];
-    const int64_t p = idx / k.nchunks;
-    const int q = static_cast<int>(idx - p * k.nchunks);
-    lp_line<T, TW, LOGITS, TO>(k, p, q);
+    const int64_t pg = idx / k.nchunks;
+    const int q = static_cast<int>(idx - pg * k.nchunks);
+    // a.group consecutive planes share the workgroup, each on its own waves;
+    // with channel-shared weights their weight loads coincide in time, so all
+    // but the first are served by the cache
+    const int per = static_cast<int>(blockDim.x) / a.group;
+    // per is a whole number of waves, so g is uniform in the wave: say so, to
+    // keep the plane's buffer resources in scalar registers
+    const int g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / per);
+    const int64_t p = pg * a.group + g;
+    const bool valid = p < a.planes;
+    lp_line<T, TW, LOGITS, TO>(k, valid ? p : a.planes - 1, q, valid, static_cast<int>(threadIdx.x) - g * per,
+                               g * (per >> 6), per >> 6);
 }
 
 template <typename T, typename TW, bool LOGITS, typename TO = T>

@@ -228,6 +228,26 @@ def test_long_line_kernel_partial_waves(dtype, shape, shared, chunk):
     assert _err(got, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [
+    (1, 1031, 8, 72),   # an odd plane count: the last workgroup has a plane too few
+    (2, 515, 8, 72),    # a workgroup whose planes belong to two images (different weights)
+])
+def test_long_line_kernel_plane_groups(shape, dtype):
+    """Channel-shared weights over enough planes that the long-line kernel runs
+    several planes per workgroup."""
+    n, c, h, w = shape
+    wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=True, seed=71 + c)
+    _say("long-line plane groups %s %s" % (shape, dtype))
+    inp = make_inputs(wl, DEV)
+    got, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"],
+                                       workspace=G.forward4_workspace(inp["x"], wl.cw))
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "scan4lp_kernel", times["scan_kernel"]
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"])
+    assert _err(got, ref) <= TOL[dtype]
+
+
 def test_forward4_closed_form_constant_input():
     # lambda = 1, x = c: every direction's h at scan step t is (t+1) c, so the
     # merged output is (H + W + 2) c everywhere, whatever the logits.
