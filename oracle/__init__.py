@@ -11,11 +11,12 @@ OpenMP over independent planes); this module only marshals numpy arrays into
 it.  Each wrapper cites the passage of the GSPN pages it follows; the C file
 holds the full list of readings taken where the pages are silent.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-and ``tests/test_oracle_backward_pins.py`` (closed forms, brute-force dense
-matrices, exact rational arithmetic, symmetry invariants, library routines,
-and for the gradients central finite differences of the pinned forward and
-adjoint dot-product identities); none is "parity unpinned".
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_backward_pins.py`` and ``tests/test_oracle_merge_pins.py``
+(closed forms, brute-force dense matrices, exact rational arithmetic,
+symmetry invariants, library routines, and for the gradients central finite
+differences of the pinned forward and adjoint dot-product identities); none
+is "parity unpinned".
 
 Layouts (contiguous, row-major):
   x, y, h           [N][C][H][W]
@@ -151,11 +152,27 @@ def scan(direction: int, x, wts, lam, chunk: int = 0, wts_are_logits: bool = Tru
     return out
 
 
-def forward4(x, logits: Sequence, lams: Sequence, chunk: int = 0) -> np.ndarray:
-    """All four directions on the same x, merged by an elementwise sum
-    (four line scans, GSPN-2 notes, "2D spatial propagation recap")."""
+def _merge_weights(merge, c: int) -> np.ndarray:
+    m = _f64(merge)
+    if m.shape != (4, c):
+        raise ValueError("merge weights %r do not fit (4, %d)" % (m.shape, c))
+    return m
+
+
+def forward4(x, logits: Sequence, lams: Sequence, chunk: int = 0, merge=None) -> np.ndarray:
+    """All four directions on the same x (four line scans, GSPN-2 notes, "2D
+    spatial propagation recap"), merged by an elementwise sum, or with
+    ``merge`` [4][C] by the learnable merge that the GSPN summary page's
+    ablation table puts in place of max-pooling, read as one weight per
+    direction and channel: y[:, c] = sum_d merge[d, c] h_d[:, c]."""
     xx = _f64(x)
     n, c, h, w = xx.shape
+    if merge is not None:
+        m = _merge_weights(merge, c)
+        y = np.zeros((n, c, h, w), dtype=np.float64)
+        for d in range(4):
+            y += m[d][None, :, None, None] * scan(d, xx, logits[d], lams[d], chunk)
+        return y
     zs = [_f64(z) for z in logits]
     ls = [_f64(l) for l in lams]
     cw = zs[0].shape[1]
@@ -188,12 +205,12 @@ def project(inp, weight) -> np.ndarray:
     return out
 
 
-def proxy_forward4(x, w_down, w_up, logits: Sequence, lams: Sequence, chunk: int = 0) -> np.ndarray:
+def proxy_forward4(x, w_down, w_up, logits: Sequence, lams: Sequence, chunk: int = 0, merge=None) -> np.ndarray:
     """Compressive-proxy forward: project C -> C_proxy, run the four-direction
-    scan in proxy space, project back C_proxy -> C (GSPN-2 notes,
-    "Optimisation 2")."""
+    scan in proxy space (merge weights, if any, over the proxy channels),
+    project back C_proxy -> C (GSPN-2 notes, "Optimisation 2")."""
     xp = project(x, w_down)
-    yp = forward4(xp, logits, lams, chunk)
+    yp = forward4(xp, logits, lams, chunk, merge=merge)
     return project(yp, w_up)
 
 
@@ -221,14 +238,32 @@ def scan_backward(direction: int, x, logits, lam, gy, chunk: int = 0):
     return dx, dl, dz
 
 
-def backward4(x, logits: Sequence, lams: Sequence, gy, chunk: int = 0):
-    """Gradient of forward4 for dL/dy = gy: (dx, [dlam_d], [dlogits_d])."""
+def backward4(x, logits: Sequence, lams: Sequence, gy, chunk: int = 0, merge=None):
+    """Gradient of forward4 for dL/dy = gy: (dx, [dlam_d], [dlogits_d]), and
+    with ``merge`` also dmerge [4][C].  With merge weights m, direction d's
+    output enters y as m[d, c] h_d, so its scan receives dL/dh_d =
+    m[d, c] gy, and dL/dm[d, c] = sum over images and positions of
+    gy * h_d (h_d recomputed by ``scan``)."""
     xx = _f64(x)
     n, c, h, w = xx.shape
     zs = [_f64(z) for z in logits]
     ls = [_f64(l) for l in lams]
     gg = _f64(gy)
     cw = zs[0].shape[1]
+    if merge is not None:
+        m = _merge_weights(merge, c)
+        if gg.shape != xx.shape:
+            raise ValueError("gy does not fit x")
+        dx = np.zeros_like(xx)
+        dls, dzs = [], []
+        dm = np.zeros((4, c), dtype=np.float64)
+        for d in range(4):
+            dxd, dld, dzd = scan_backward(d, xx, zs[d], ls[d], m[d][None, :, None, None] * gg, chunk)
+            dx += dxd
+            dls.append(dld)
+            dzs.append(dzd)
+            dm[d] = np.sum(gg * scan(d, xx, zs[d], ls[d], chunk), axis=(0, 2, 3))
+        return dx, dls, dzs, dm
     for d in range(4):
         S, L = frame_shape(d, h, w)
         if zs[d].shape != (n, cw, 3, S, L) or ls[d].shape != (n, c, S, L):
