@@ -3,10 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload profile]
 
 A step is one gspn_forward4 call (normalise the logits, scan T->B, B->T,
-L->R, R->L, merge by summation) over one batch of seeded synthetic inputs
-already resident in HBM; for the proxy workload a step is the compressive
-proxy pipeline (1x1 projection down, forward4 in proxy space, 1x1 projection
-up).  Prints one JSON line.
+L->R, R->L, merge by summation, or with --merge by seeded learnable weights
+per direction and channel) over one batch of seeded synthetic inputs already
+resident in HBM; for the proxy workload a step is the compressive proxy
+pipeline (1x1 projection down, forward4 in proxy space, 1x1 projection up).
+--pass backward times gspn_backward4 instead.  Prints one JSON line.
 
 Measurements:
   - ms per step: HIP events on the stream the library launches on, bracketing
@@ -122,22 +123,31 @@ def adjoint_launch_bytes(wl) -> int:
     return 2 * u + 2 * u + 4 * u + z + states + 4 * u + 4 * u + dz
 
 
-def run_step(wl, inp, out, ws, timed=False):
+def merge_weights(wl, on: bool):
+    """Seeded learnable merge weights [4][C] (C of the scanned tensor), or None."""
+    if not on:
+        return None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 2000)
+    return torch.randn((4, wl.c_scan), generator=g, device="cuda", dtype=torch.float32)
+
+
+def run_step(wl, inp, out, ws, timed=False, merge=None):
     if wl.c_proxy:
         f = G.gspn_proxy_forward4_timed if timed else G.gspn_proxy_forward4
         return f(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
-                 chunk_len=wl.chunk, out=out, workspace=ws)
+                 chunk_len=wl.chunk, out=out, workspace=ws, merge=merge)
     f = G.gspn_forward4_timed if timed else G.gspn_forward4
-    return f(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out, workspace=ws)
+    return f(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out, workspace=ws, merge=merge)
 
 
-def stage_times(wl, inp, out, ws, reps: int) -> dict:
+def stage_times(wl, inp, out, ws, reps: int, merge=None) -> dict:
     """Mean per-step duration and launch count of each stage over reps timed
     steps."""
     acc = {name: {"ms": 0.0, "launches": 0} for name in G.STAGES}
     kernel = None
     for _ in range(reps):
-        _, t = run_step(wl, inp, out, ws, timed=True)
+        _, t = run_step(wl, inp, out, ws, timed=True, merge=merge)
         kernel = t.pop("scan_kernel")
         for name, v in t.items():
             acc[name]["ms"] += v["ms"] / reps
@@ -189,10 +199,12 @@ def _np64(t):
     return t.detach().to("cpu").double().numpy()
 
 
-def cpu_baseline_planes(wl, inp, oracle, gy=None) -> dict:
+def cpu_baseline_planes(wl, inp, oracle, gy=None, merge=None) -> dict:
     """Whole (n, c) planes through the oracle's four-direction forward (or,
     given dL/dy, its backward), each plane run as its own image; repeated
-    until CPU_TARGET_S, extrapolated to the workload's n * c planes."""
+    until CPU_TARGET_S, extrapolated to the workload's n * c planes.  With
+    merge weights every sampled plane takes those of channel 0 (the cost does
+    not depend on their values)."""
     planes = wl.n * wl.c
     per_plane = (6 + (0 if wl.shared_w else 12)) * wl.h * wl.w * 8 * (2 if gy is not None else 1)
     sample = max(1, min(planes, CPU_MEM_BYTES // per_plane))
@@ -208,13 +220,14 @@ def cpu_baseline_planes(wl, inp, oracle, gy=None) -> dict:
         zs.append(_np64(inp["logits"][d][nn, torch.zeros_like(cc) if wl.shared_w else cc][:, None]))
         ls.append(_np64(inp["lam"][d][nn, cc][:, None]))
     gs = _np64(gy[nn, cc][:, None]) if gy is not None else None
+    ms = _np64(merge[:, :1]) if merge is not None else None
     reps, spent = 0, 0.0
     while reps < CPU_MAX_REPEATS and (reps == 0 or spent < CPU_TARGET_S):
         t = time.perf_counter()
         if gs is None:
-            oracle.forward4(xs, zs, ls, chunk=wl.chunk)
+            oracle.forward4(xs, zs, ls, chunk=wl.chunk, merge=ms)
         else:
-            oracle.backward4(xs, zs, ls, gs, chunk=wl.chunk)
+            oracle.backward4(xs, zs, ls, gs, chunk=wl.chunk, merge=ms)
         spent += time.perf_counter() - t
         reps += 1
     per_call = spent / reps
@@ -226,7 +239,7 @@ def cpu_baseline_planes(wl, inp, oracle, gy=None) -> dict:
                       "%d runs, %.1f s of oracle time" % (sample, planes, wl.h, wl.w, step, what, reps, spent)}
 
 
-def cpu_baseline_proxy(wl, inp, oracle) -> dict:
+def cpu_baseline_proxy(wl, inp, oracle, merge=None) -> dict:
     """The whole proxy pipeline once: the down projection over bands of rows,
     the four-direction forward on all proxy planes, the up projection over
     bands of rows (band conversions to fp64 are outside the timed parts)."""
@@ -246,7 +259,7 @@ def cpu_baseline_proxy(wl, inp, oracle) -> dict:
     zs = [_np64(z) for z in inp["logits"]]
     ls = [_np64(l) for l in inp["lam"]]
     t = time.perf_counter()
-    yp = oracle.forward4(xp, zs, ls, chunk=wl.chunk)
+    yp = oracle.forward4(xp, zs, ls, chunk=wl.chunk, merge=None if merge is None else _np64(merge))
     t_scan = time.perf_counter() - t
     del xp, zs, ls
     for r0 in range(0, h, band):
@@ -262,11 +275,11 @@ def cpu_baseline_proxy(wl, inp, oracle) -> dict:
                       % (t_down, t_up, band, cp, t_scan, min(oracle.max_threads(), n * cp))}
 
 
-def cpu_baseline(wl, inp) -> dict:
+def cpu_baseline(wl, inp, merge=None) -> dict:
     import oracle
     if wl.c_proxy:
-        return cpu_baseline_proxy(wl, inp, oracle)
-    return cpu_baseline_planes(wl, inp, oracle)
+        return cpu_baseline_proxy(wl, inp, oracle, merge)
+    return cpu_baseline_planes(wl, inp, oracle, merge=merge)
 
 
 def copy_check(mib: int) -> None:
@@ -305,10 +318,12 @@ def bench_backward(args, wl):
     outs = (torch.empty_like(inp["x"]), [torch.empty_like(z) for z in inp["logits"]],
             [torch.empty_like(l) for l in inp["lam"]])
     ws = G.backward4_workspace(inp["x"], wl.cw)
+    merge = merge_weights(wl, args.merge)
+    dmerge = torch.empty((4, wl.c_scan), dtype=torch.float32, device="cuda") if args.merge else None
 
     def step(times=None):
         return G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=wl.chunk, workspace=ws,
-                                out=outs, times=times)
+                                out=outs, times=times, merge=merge, dmerge=dmerge)
 
     for _ in range(args.warmup):
         step()
@@ -341,15 +356,17 @@ def bench_backward(args, wl):
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle's backward on a sample", file=sys.stderr, flush=True)
         import oracle
-        cpu = cpu_baseline_planes(wl, inp, oracle, gy=gy)
+        cpu = cpu_baseline_planes(wl, inp, oracle, gy=gy, merge=merge)
     traffic, traffic_src = counter_traffic("adj4_kernel", wl)
     rec = {
-        "metric": "ms per 4-direction GSPN backward (dx, dlambda, dlogits); achieved HBM GB/s",
+        "metric": "ms per 4-direction GSPN backward (dx, dlambda, dlogits%s); achieved HBM GB/s"
+                  % (", dmerge" if args.merge else ""),
         "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded)",
         "config": {"workload": wl.name, "pass": "backward", "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
-                   "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk},
+                   "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
+                   "merge": "learnable" if args.merge else "sum"},
         "effective_GBps": round(eff, 1), "effective_frac": round(eff / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
         "stages_ms": {k: round(v, 4) for k, v in acc.items() if v > 0},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -370,6 +387,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "backward"),
                     help="time the forward (default) or the backward (gradients for a seeded dL/dy)")
+    ap.add_argument("--merge", action="store_true",
+                    help="merge the directions with seeded learnable weights per direction and channel")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -392,10 +411,11 @@ def main():
     out = torch.empty_like(inp["x"])
     ws = (G.proxy_forward4_workspace(inp["x"], wl.c_proxy, wl.cw) if wl.c_proxy
           else G.forward4_workspace(inp["x"], wl.cw))
+    merge = merge_weights(wl, args.merge)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        run_step(wl, inp, out, ws)
+        run_step(wl, inp, out, ws, merge=merge)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -405,7 +425,7 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        run_step(wl, inp, out, ws)
+        run_step(wl, inp, out, ws, merge=merge)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -413,7 +433,7 @@ def main():
     print("bench: %.3f ms/step (wall %.3f ms/step)" % (ms, wall * 1e3 / args.steps),
           file=sys.stderr, flush=True)
 
-    st, kernel = stage_times(wl, inp, out, ws, reps=max(3, min(args.steps, 10)))
+    st, kernel = stage_times(wl, inp, out, ws, reps=max(3, min(args.steps, 10)), merge=merge)
     scan = st["scan"]
     launches = scan["launches"]
     kernel_ms = scan["ms"] / launches
@@ -428,10 +448,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, inp)
+        cpu = cpu_baseline(wl, inp, merge)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if not args.merge else METRIC.replace("forward", "forward (learnable merge)"),
         "value": round(ms, 4),
         "unit": "ms",
         "n_gpus": 1,
@@ -445,7 +465,7 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": wl.name, "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
-                   "c_proxy": wl.c_proxy},
+                   "c_proxy": wl.c_proxy, "merge": "learnable" if args.merge else "sum"},
         "effective_GBps": round(eff, 1),
         "effective_frac": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": alg,

@@ -13,10 +13,12 @@
  * positions k-1, k, k+1 of the previous line with weights obtained from three
  * logits by a sigmoid followed by division by their sum; at a line border
  * the sum runs over the neighbours that exist (a missing neighbour has
- * weight 0).  The four direction outputs are merged by an elementwise sum.
- * Variants: channel-shared w (GSPN-2 notes, "Optimisation 2"), independent
- * chunks along the scan axis ("Optimisation 1") and the 1x1 projections to
- * and from a C_proxy-channel space ("Optimisation 2").
+ * weight 0).  The four direction outputs are merged by an elementwise sum,
+ * or by the learnable merge of the GSPN summary page's ablation table (one
+ * weight per direction and channel, see gspn_forward4).  Variants:
+ * channel-shared w (GSPN-2 notes, "Optimisation 2"), independent chunks
+ * along the scan axis ("Optimisation 1") and the 1x1 projections to and from
+ * a C_proxy-channel space ("Optimisation 2").
  *
  * Conventions shared by every call
  * --------------------------------
@@ -67,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 5
+#define GSPN_ABI_VERSION 6
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -167,11 +169,21 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
                                       int dtype);
 
 /*
- * gspn_forward4 -- the four-direction propagation with summed merge:
- *   y = sum over d in (T2B, B2T, L2R, R2L) of scan_d(x, logits[d], lam[d]).
+ * gspn_forward4 -- the four-direction propagation with summed or learnable
+ * merge:
+ *   y[:, k] = sum over d in (T2B, B2T, L2R, R2L) of
+ *             m[d][k] * scan_d(x, logits[d], lam[d])[:, k]   (channel k)
  *   logits[d]  [n][cw][3][S_d][L_d] logits of direction d (normalised inside).
  *   lam[d]     [n][c][S_d][L_d]; the same pointer may be given for all d.
  *   logits and lam are host arrays of 4 device pointers, indexed by gspn_dir.
+ *   merge      NULL: m = 1, the plain sum.  Otherwise a device array of
+ *              4 * c fp32 values [4][c] indexed by gspn_dir then channel,
+ *              whatever the storage type: the learnable merge that the GSPN
+ *              summary page's ablation table puts in place of SPN's
+ *              max-pooling merge, read as one weight per direction and
+ *              channel.  The scans apply it to lambda * x (each h_d is
+ *              linear in it), so it costs no extra pass.  4-byte aligned;
+ *              y may not overlap it.
  *   y          [n][c][h][w] output; may not overlap any input.
  *   workspace  optional device buffer of workspace_bytes bytes, 4-byte
  *              aligned.  NULL (or 0 bytes): the directions run one after
@@ -197,7 +209,7 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  */
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
-                          const void* const lam[4], void* y, void* workspace,
+                          const void* const lam[4], const float* merge, void* y, void* workspace,
                           int64_t workspace_bytes, int dtype, void* stream);
 
 /*
@@ -212,12 +224,13 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
 /*
  * gspn_proxy_forward4 -- the compressive-proxy propagation (GSPN-2 notes,
  * "Optimisation 2"): project C -> C_proxy, run the four-direction
- * propagation with summed merge in proxy space, project back C_proxy -> C:
- *   x_p = w_down . x,   y_p = forward4(x_p, logits, lam),   y = w_up . y_p
+ * propagation in proxy space, project back C_proxy -> C:
+ *   x_p = w_down . x,   y_p = forward4(x_p, logits, lam, merge),   y = w_up . y_p
  * (1x1 projections, no bias).
  *   x        [n][c][h][w];  y [n][c][h][w] output (may not overlap any input)
  *   w_down   [c_proxy][c];  w_up [c][c_proxy]
  *   logits[d] [n][cw][3][S_d][L_d] (cw = 1 or c_proxy), lam[d] [n][c_proxy][S_d][L_d]
+ *   merge    NULL (sum) or fp32 [4][c_proxy], as in gspn_forward4
  *   workspace required: gspn_proxy_forward4_workspace_bytes() bytes, 4-byte
  *            aligned, overlapping nothing else (else GSPN_ERR_WORKSPACE /
  *            GSPN_ERR_MISALIGNED / GSPN_ERR_ALIASING; NULL is
@@ -227,8 +240,8 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
  */
 gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
-                                const void* const logits[4], const void* const lam[4], void* y,
-                                void* workspace, int64_t workspace_bytes, int dtype, void* stream);
+                                const void* const logits[4], const void* const lam[4], const float* merge,
+                                void* y, void* workspace, int64_t workspace_bytes, int dtype, void* stream);
 
 /*
  * gspn_backward4_workspace_bytes -- bytes of the gspn_backward4 workspace:
@@ -243,28 +256,34 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
 
 /*
  * gspn_backward4 -- gradients of the four-direction propagation of
- * gspn_forward4 (same x, logits, lam, cw, chunk_len) for dL/dy = gy: the exact
- * derivative of the scan that the GSPN-2 paper notes define in "2D spatial
- * propagation recap" (the GSPN-2 summary page, "Experimental setup", reports
- * forward and backward runtimes).  Per direction, in its scan frame, the
- * adjoint a_t = g_t + M_{t+1}^T a_{t+1} runs against the scan order
- * (restarting at chunk ends), and
- *   dlam[d]      = a * x                      [n][c][S_d][L_d]   (written)
- *   dx           = sum_d a_d * lam[d]          [n][c][h][w]       (written)
- *   dlogits[d]   = d w / d z applied to a_t h_{t-1}   [n][cw][3][S_d][L_d]
+ * gspn_forward4 (same x, logits, lam, merge, cw, chunk_len) for dL/dy = gy:
+ * the exact derivative of the scan that the GSPN-2 paper notes define in "2D
+ * spatial propagation recap" (the GSPN-2 summary page, "Experimental setup",
+ * reports forward and backward runtimes).  Per direction, in its scan frame,
+ * the adjoint a_t = g_t + M_{t+1}^T a_{t+1} runs against the scan order
+ * (restarting at chunk ends), and with m_d = merge[d][k] (1 if merge is NULL)
+ *   dlam[d]      = m_d a * x                  [n][c][S_d][L_d]   (written)
+ *   dx           = sum_d m_d a_d * lam[d]      [n][c][h][w]       (written)
+ *   dlogits[d]   = d w / d z applied to m_d a_t h_{t-1}   [n][cw][3][S_d][L_d]
  *                  (written; 0 on each chunk's first line, whose logits the
  *                  forward does not use; for cw == 1 < c the sum over
  *                  channels, accumulated in fp32 in an order that may vary
- *                  between calls).
+ *                  between calls)
+ *   dmerge       [4][c] fp32 (written, optional: NULL skips it; computed also
+ *                  when merge is NULL, as the gradient at m = 1): the sum
+ *                  over images and positions of gy * h_d, evaluated as
+ *                  sum_t <a_t, lam_t * x_t> (the same value for the linear
+ *                  recurrence), accumulated in fp32 in an order that may vary
+ *                  between calls.
  * workspace: required, gspn_backward4_workspace_bytes() bytes, 4-byte
  * aligned.  Outputs may overlap neither an input, the workspace nor each
  * other.  Lines may hold at most 2048 positions (else GSPN_ERR_UNSUPPORTED).
  * The forward states are recomputed inside and kept in fp32.
  */
 gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
-                           const void* x, const void* const logits[4], const void* const lam[4], const void* gy,
-                           void* dx, void* const dlogits[4], void* const dlam[4], void* workspace,
-                           int64_t workspace_bytes, int dtype, void* stream);
+                           const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
+                           const void* gy, void* dx, void* const dlogits[4], void* const dlam[4], float* dmerge,
+                           void* workspace, int64_t workspace_bytes, int dtype, void* stream);
 
 /*
  * Stage timing of one forward call (measurement only).
@@ -290,7 +309,7 @@ typedef enum {
     GSPN_STAGE_COMBINE = 4,      /* transposing merge of the partial maps into y */
     GSPN_STAGE_PROJECT_UP = 5,   /* 1x1 projection C_proxy -> C */
     GSPN_STAGE_ADJOINT = 6,      /* backward: the adjoint line-scan launch */
-    GSPN_STAGE_REDUCE = 7,       /* backward: clearing / storing the shared-logit sums */
+    GSPN_STAGE_REDUCE = 7,       /* backward: clearing / storing the shared-logit sums, clearing dmerge */
     GSPN_NUM_STAGES = 8
 } gspn_stage;
 
@@ -311,14 +330,14 @@ typedef struct {
 
 gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* const logits[4],
-                                const void* const lam[4], void* y, void* workspace,
+                                const void* const lam[4], const float* merge, void* y, void* workspace,
                                 int64_t workspace_bytes, int dtype, void* stream,
                                 gspn_stage_times* times);
 
 gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
                                       int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
                                       const void* w_up, const void* const logits[4],
-                                      const void* const lam[4], void* y, void* workspace,
+                                      const void* const lam[4], const float* merge, void* y, void* workspace,
                                       int64_t workspace_bytes, int dtype, void* stream,
                                       gspn_stage_times* times);
 
@@ -326,9 +345,9 @@ gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w
  * the forward recompute is reported as GSPN_STAGE_SCAN. */
 gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                                  const void* x, const void* const logits[4], const void* const lam[4],
-                                 const void* gy, void* dx, void* const dlogits[4], void* const dlam[4],
-                                 void* workspace, int64_t workspace_bytes, int dtype, void* stream,
-                                 gspn_stage_times* times);
+                                 const float* merge, const void* gy, void* dx, void* const dlogits[4],
+                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
+                                 int dtype, void* stream, gspn_stage_times* times);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);

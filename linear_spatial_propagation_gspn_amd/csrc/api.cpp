@@ -321,8 +321,8 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
 namespace {
 
 gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
-                          const void* x, const void* const logits[4], const void* const lam[4], void* y,
-                          void* workspace, int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
+                          const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
+                          void* y, void* workspace, int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -342,12 +342,16 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (overlap(y, xb, x, xb)) return GSPN_ERR_ALIASING;
     for (int d = 0; d < 4; ++d)
         if (overlap(y, xb, logits[d], wb) || overlap(y, xb, lam[d], xb)) return GSPN_ERR_ALIASING;
+    const int64_t mgb = 4 * c * 4;  // merge weights, fp32 [4][c]
+    if (merge && !aligned(merge, 4)) return GSPN_ERR_MISALIGNED;
+    if (merge && overlap(y, xb, merge, mgb)) return GSPN_ERR_ALIASING;
     const bool have_ws = workspace != nullptr && workspace_bytes > 0;
     if (have_ws) {
         const int64_t need = gspn_forward4_workspace_bytes(n, c, h, w, cw, dtype);
         if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
         if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
         if (overlap(workspace, need, y, xb) || overlap(workspace, need, x, xb)) return GSPN_ERR_ALIASING;
+        if (merge && overlap(workspace, need, merge, mgb)) return GSPN_ERR_ALIASING;
         for (int d = 0; d < 4; ++d)
             if (overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], xb))
                 return GSPN_ERR_ALIASING;
@@ -371,6 +375,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].accumulate = 0;
         p[d].dtype = dtype;
         p[d].wdtype = dtype;
+        p[d].mscale = merge ? merge + d * c : nullptr;
     }
 
     // Planes of at most 64 x 64: one pass over LDS-resident planes, whether
@@ -378,7 +383,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (gspn::plane4_supported(h, w)) {
         if (tm) tm->scan_kernel = GSPN_SCAN_PLANE;
         return from_hip(timed(tm, GSPN_STAGE_SCAN, [&] {
-            return gspn::launch_plane4(x, logits, lam, y, n, c, cw, h, w, chunks, dtype, st);
+            return gspn::launch_plane4(x, logits, lam, merge, y, n, c, cw, h, w, chunks, dtype, st);
         }));
     }
 
@@ -468,8 +473,8 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
 
 gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw, int64_t chunk_len,
                        const void* x, const void* w_down, const void* w_up, const void* const logits[4],
-                       const void* const lam[4], void* y, void* workspace, int64_t workspace_bytes, int dtype,
-                       void* stream, Timer* tm) {
+                       const void* const lam[4], const float* merge, void* y, void* workspace,
+                       int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
     if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
     if (!dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w})) return GSPN_ERR_BAD_SHAPE;
     if (chunk_len < 0) return GSPN_ERR_BAD_CHUNK;
@@ -494,6 +499,9 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
     if (overlap(workspace, need, x, xb) || overlap(workspace, need, y, xb) ||
         overlap(workspace, need, w_down, mb) || overlap(workspace, need, w_up, mb))
         return GSPN_ERR_ALIASING;
+    const int64_t mgb = 4 * c_proxy * 4;  // merge weights over the proxy channels, fp32 [4][c_proxy]
+    if (merge && !aligned(merge, 4)) return GSPN_ERR_MISALIGNED;
+    if (merge && (overlap(y, xb, merge, mgb) || overlap(workspace, need, merge, mgb))) return GSPN_ERR_ALIASING;
     for (int d = 0; d < 4; ++d) {
         if (!aligned(logits[d], es) || !aligned(lam[d], es)) return GSPN_ERR_MISALIGNED;
         if (overlap(y, xb, logits[d], wb) || overlap(y, xb, lam[d], pb) ||
@@ -508,7 +516,7 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
     if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
               [&] { return gspn::launch_project(n, c, h * w, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
-    const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, yp, fws,
+    const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, fws,
                                          need - 2 * pb, dtype, stream, tm);
     if (s4 != GSPN_OK) return s4;
     return from_hip(timed(tm, GSPN_STAGE_PROJECT_UP,
@@ -516,9 +524,9 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
 }
 
 gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len, const void* x,
-                          const void* const logits[4], const void* const lam[4], const void* gy, void* dx,
-                          void* const dlogits[4], void* const dlam[4], void* workspace, int64_t workspace_bytes,
-                          int dtype, void* stream, Timer* tm) {
+                          const void* const logits[4], const void* const lam[4], const float* merge, const void* gy,
+                          void* dx, void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                          int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -557,6 +565,22 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
             return GSPN_ERR_ALIASING;
     }
     if (overlap(workspace, need, x, xb) || overlap(workspace, need, gy, xb)) return GSPN_ERR_ALIASING;
+    const int64_t mgb = 4 * c * 4;  // merge weights and their gradient, fp32 [4][c]
+    if ((merge && !aligned(merge, 4)) || (dmerge && !aligned(dmerge, 4))) return GSPN_ERR_MISALIGNED;
+    if (merge) {
+        if (overlap(workspace, need, merge, mgb)) return GSPN_ERR_ALIASING;
+        for (int i = 0; i < 9; ++i)
+            if (overlap(outs[i], ob[i], merge, mgb)) return GSPN_ERR_ALIASING;
+    }
+    if (dmerge) {
+        if (overlap(dmerge, mgb, x, xb) || overlap(dmerge, mgb, gy, xb) || overlap(dmerge, mgb, workspace, need) ||
+            (merge && overlap(dmerge, mgb, merge, mgb)))
+            return GSPN_ERR_ALIASING;
+        for (int d = 0; d < 4; ++d)
+            if (overlap(dmerge, mgb, logits[d], wb) || overlap(dmerge, mgb, lam[d], xb)) return GSPN_ERR_ALIASING;
+        for (int i = 0; i < 9; ++i)
+            if (overlap(dmerge, mgb, outs[i], ob[i])) return GSPN_ERR_ALIASING;
+    }
     const hipStream_t st = as_stream(stream);
 
     // Workspace: [fp32 logit-gradient sums and normalised weights of the four
@@ -630,6 +654,9 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (shared &&
         timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(sums, 4 * zsum, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
+    if (dmerge &&
+        timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(dmerge, 4 * c, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
 
     gspn::AdjointParams a[4];
     for (int d = 0; d < 4; ++d) {
@@ -651,6 +678,10 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         a[d].reverse = (d == GSPN_B2T || d == GSPN_R2L) ? 1 : 0;
         a[d].shared = shared ? 1 : 0;
         a[d].dtype = dtype;
+        // the states above are those of the unweighted scans; the adjoint
+        // applies the merge weights
+        a[d].mscale = merge ? merge + d * c : nullptr;
+        a[d].dmerge = dmerge ? dmerge + d * c : nullptr;
     }
     if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjoint4(a, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
@@ -675,21 +706,21 @@ extern "C" {
 
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
-                          const void* const lam[4], void* y, void* workspace,
+                          const void* const lam[4], const float* merge, void* y, void* workspace,
                           int64_t workspace_bytes, int dtype, void* stream) {
-    return forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, y, workspace, workspace_bytes, dtype, stream,
-                         nullptr);
+    return forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, workspace, workspace_bytes, dtype,
+                         stream, nullptr);
 }
 
 gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* const logits[4],
-                                const void* const lam[4], void* y, void* workspace,
+                                const void* const lam[4], const float* merge, void* y, void* workspace,
                                 int64_t workspace_bytes, int dtype, void* stream,
                                 gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
-    const gspn_status s = forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, y, workspace,
+    const gspn_status s = forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, workspace,
                                         workspace_bytes, dtype, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
@@ -706,22 +737,22 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
 
 gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
-                                const void* const logits[4], const void* const lam[4], void* y,
-                                void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
-    return proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, y, workspace,
+                                const void* const logits[4], const void* const lam[4], const float* merge,
+                                void* y, void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
+    return proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, y, workspace,
                       workspace_bytes, dtype, stream, nullptr);
 }
 
 gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
                                       int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
                                       const void* w_up, const void* const logits[4],
-                                      const void* const lam[4], void* y, void* workspace,
+                                      const void* const lam[4], const float* merge, void* y, void* workspace,
                                       int64_t workspace_bytes, int dtype, void* stream,
                                       gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
-    const gspn_status s = proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, y,
+    const gspn_status s = proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, y,
                                      workspace, workspace_bytes, dtype, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
@@ -740,23 +771,23 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
 }
 
 gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
-                           const void* x, const void* const logits[4], const void* const lam[4], const void* gy,
-                           void* dx, void* const dlogits[4], void* const dlam[4], void* workspace,
-                           int64_t workspace_bytes, int dtype, void* stream) {
-    return backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, gy, dx, dlogits, dlam, workspace,
+                           const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
+                           const void* gy, void* dx, void* const dlogits[4], void* const dlam[4], float* dmerge,
+                           void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
+    return backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, gy, dx, dlogits, dlam, dmerge, workspace,
                          workspace_bytes, dtype, stream, nullptr);
 }
 
 gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                                  const void* x, const void* const logits[4], const void* const lam[4],
-                                 const void* gy, void* dx, void* const dlogits[4], void* const dlam[4],
-                                 void* workspace, int64_t workspace_bytes, int dtype, void* stream,
-                                 gspn_stage_times* times) {
+                                 const float* merge, const void* gy, void* dx, void* const dlogits[4],
+                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
+                                 int dtype, void* stream, gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
-    const gspn_status s = backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, gy, dx, dlogits, dlam, workspace,
-                                        workspace_bytes, dtype, stream, &tm);
+    const gspn_status s = backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, gy, dx, dlogits, dlam,
+                                        dmerge, workspace, workspace_bytes, dtype, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }

@@ -61,6 +61,8 @@ struct AdjK {
     int nchunks;
     int reverse;
     int shared;  // dz is an fp32 sum over channels (atomic adds; groups of shared_group<P>() channels)
+    const float* mscale;  // learnable merge weight of each channel for this direction ([c]), or null for 1
+    float* dmerge;        // its gradient [c] (fp32 atomic adds), or null
 };
 
 struct Adj4K {
@@ -73,6 +75,11 @@ struct Adj4K {
 // position are normalised once for all of them, and the logit gradient, which
 // sums over channels, is accumulated over the G channels in registers before
 // it leaves the workgroup (one atomic add per logit and G channels).
+// With a learnable merge weight m for (direction, channel), the direction's
+// output enters y as m h, so its adjoint input is m g: the adjoint a runs on
+// g itself and every gradient it feeds is scaled by m, while
+// dL/dm = sum_t <g_t, h_t> = sum_t <a_t, lambda_t x_t> (the adjoint identity
+// of the linear recurrence, per chunk) is summed on the way.
 template <typename T, int P, int G>
 __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float* edge_raw) {
     constexpr int D = adj_depth<P, G>();
@@ -87,10 +94,14 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     const int64_t p0 = nidx * a.c + c0;           // its plane
     int gc[G];                                    // channel offset of each member, clamped
     bool gok[G];
+    float msc[G];                                 // merge weight of each member
+    float dm[G];                                  // this lane's share of dL/dm
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         gok[g] = c0 + g < a.c;
         gc[g] = gok[g] ? g : 0;
+        msc[g] = a.mscale ? a.mscale[c0 + gc[g]] : 1.0f;
+        dm[g] = 0.0f;
     }
     const T* xp = static_cast<const T*>(a.x) + p0 * plane;
     const T* gp = static_cast<const T*>(a.g) + p0 * plane;
@@ -208,12 +219,14 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
             const int64_t go = gc[g] * plane;
 #pragma unroll
             for (int j = 0; j < P; ++j) {
+                const float am = a_t[j] * msc[g];  // the adjoint of the merged output
+                dm[g] = __builtin_fmaf(a_t[j], rl[s][g][j] * rx[s][g][j], dm[g]);
                 if (kin[j] && gok[g]) {
-                    st_stream(dlp + go + lo + k0 + j, a_t[j] * rx[s][g][j]);
-                    st_stream(dxp + go + lo + k0 + j, a_t[j] * rl[s][g][j]);
+                    st_stream(dlp + go + lo + k0 + j, am * rx[s][g][j]);
+                    st_stream(dxp + go + lo + k0 + j, am * rl[s][g][j]);
                 }
 #pragma unroll
-                for (int o = 0; o < 3; ++o) dw[j][o] += a_t[j] * rh[s][g][j + o];  // h_{t-1}[k+o-1]
+                for (int o = 0; o < 3; ++o) dw[j][o] += am * rh[s][g][j + o];  // h_{t-1}[k+o-1]
                 qn0[g][j] = first ? 0.0f : w[0][j] * a_t[j];
                 qn1[g][j] = first ? 0.0f : w[1][j] * a_t[j];
                 qn2[g][j] = first ? 0.0f : w[2][j] * a_t[j];
@@ -266,6 +279,17 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         ((t - Ss >= t0 ? step(IC<(Ss + 1) % D>{}, IC<0>{}, t - Ss) : void()), ...);
     }(std::make_integer_sequence<int, D - 1>{});
+
+    if (a.dmerge) {
+        // sum over the wave, one atomic add per wave and member
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float v = dm[g];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+            if ((tid & 63) == 0 && gok[g]) atomicAdd(a.dmerge + c0 + g, v);
+        }
+    }
 }
 
 template <typename T, int P, int G>
@@ -331,6 +355,8 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
         a.nchunks = static_cast<int>((p[d].S + p[d].chunk - 1) / p[d].chunk);
         a.reverse = p[d].reverse;
         a.shared = p[d].shared;
+        a.mscale = p[d].mscale;
+        a.dmerge = p[d].dmerge;
         k.blocks[d] = p[d].n * ((p[d].c + G - 1) / G) * a.nchunks;
         total += k.blocks[d];
         maxL = a.L > maxL ? a.L : maxL;

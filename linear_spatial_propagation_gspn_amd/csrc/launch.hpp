@@ -27,6 +27,7 @@ struct ScanParams {
     int dtype;   // storage type of x, lam, out
     int wdtype;  // format of wts: dtype, or for weights normalised beforehand kF32 / kPairF16
     int odtype = -1;  // storage type of out: -1 = dtype; kF32 for fp32 states of bf16 scans
+    const float* mscale = nullptr;  // learnable merge: weight of each channel ([c]) for this direction
 };
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
@@ -43,10 +44,11 @@ bool fused4_supported(int64_t h, int64_t w);
 hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind = nullptr);
 
 // All four directions of planes of at most 64 x 64 in one pass, y written
-// once (chunk[d]: steps per chunk of direction d, clamped to [1, S_d]).
+// once (chunk[d]: steps per chunk of direction d, clamped to [1, S_d];
+// merge: learnable merge weights [4][c], or null for the plain sum).
 bool plane4_supported(int64_t h, int64_t w);
-hipError_t launch_plane4(const void* x, const void* const logits[4], const void* const lam[4], void* y,
-                         int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w, const int64_t chunk[4],
+hipError_t launch_plane4(const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
+                         void* y, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w, const int64_t chunk[4],
                          int dtype, hipStream_t stream);
 
 // dst[p][c][r] = src[p][r][c] for `planes` planes of R x Cc elements.
@@ -94,6 +96,8 @@ struct AdjointParams {
     int reverse;
     int shared;
     int dtype;
+    const float* mscale = nullptr;  // learnable merge: weight of each channel ([c]) for this direction
+    float* dmerge = nullptr;        // its gradient [c], fp32, added into (null: not wanted)
 };
 
 hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream);

@@ -44,6 +44,7 @@ struct Plane4K {
     int H;
     int W;
     int K[4];  // steps per chunk of each direction (S_d for one chunk)
+    const float* merge;  // learnable merge weights [4][c], or null for the plain sum
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -147,6 +148,7 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
     const int64_t plane = static_cast<int64_t>(S) * L;
     const int64_t nidx = p / a.c;
     const int64_t ci = p - nidx * a.c;
+    const float msc = a.merge ? a.merge[d * a.c + ci] : 1.0f;
     const auto rl = rsrc(static_cast<const T*>(a.lam[d]) + p * plane, plane * sizeof(T));
     const auto rz = rsrc(static_cast<const T*>(a.logits[d]) + (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane,
                          3 * plane * sizeof(T));
@@ -183,7 +185,7 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
         constexpr int s = decltype(slot)::value;
         const int i = line_of(t);
         const int pos = HORIZ ? k * ld + i : i * ld + k;
-        const float u = widen<T>(rlam[s]) * xs[pos];
+        const float u = (widen<T>(rlam[s]) * msc) * xs[pos];
         float hn = u;
         const bool first = cpos == 0;  // chunk start: h_prev = 0, logits unused
         cpos = cpos + 1 == K ? 0 : cpos + 1;
@@ -241,12 +243,13 @@ __global__ __launch_bounds__(256) void plane4_kernel(const Plane4K a) {
 
 bool plane4_supported(int64_t h, int64_t w) { return h >= 1 && w >= 1 && h <= kPlaneMax && w <= kPlaneMax; }
 
-hipError_t launch_plane4(const void* x, const void* const logits[4], const void* const lam[4], void* y,
-                         int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w, const int64_t chunk[4],
+hipError_t launch_plane4(const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
+                         void* y, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w, const int64_t chunk[4],
                          int dtype, hipStream_t stream) {
     Plane4K k;
     k.x = x;
     k.y = y;
+    k.merge = merge;
     for (int d = 0; d < 4; ++d) {
         k.logits[d] = logits[d];
         k.lam[d] = lam[d];

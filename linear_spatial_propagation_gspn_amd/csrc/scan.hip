@@ -85,6 +85,7 @@ ScanK make_args(const ScanParams& p, int P) {
     k.nchunks = (S + k.K - 1) / k.K;
     k.reverse = (p.dir == 1 || p.dir == 3) ? 1 : 0;
     k.logits = p.wts_are_logits ? 1 : 0;
+    k.mscale = p.mscale;
     // Row tiles take 16-byte accesses when every tile of every chunk starts
     // on a 16-byte column: rows and chunk starts are whole vectors apart.
     const int ut = horiz_tile_width(esz, P);

@@ -53,6 +53,7 @@ struct ScanK {
     int reverse;   // scan runs from line S-1 down to 0
     int logits;    // wts holds logits (1) or normalised weights (0)
     int vec_tile;  // horizontal: every full tile of every chunk allows 16-byte row access
+    const float* mscale;  // merge weight of each channel for this direction ([c]), or null for 1
 };
 
 template <typename T, int N>
@@ -96,6 +97,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
 
     const T* __restrict__ xp = static_cast<const T*>(a.x) + p * plane;
     const T* __restrict__ lp = static_cast<const T*>(a.lam) + p * plane;
+    const float msc = a.mscale ? a.mscale[ci] : 1.0f;  // learnable merge: this direction's weight
     constexpr bool PAIR = std::is_same_v<TW, WPair>;
     using ZT = std::conditional_t<PAIR, uint32_t, TW>;
     const ZT* __restrict__ zp =
@@ -268,7 +270,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
                     const float xv = HORIZ ? xt[C][j][off] : rx[HORIZ ? 0 : R][s][j];
-                    float u = rl[R][s][j] * xv;
+                    float u = (rl[R][s][j] * msc) * xv;
                     if (!first) {
                         const bool has_l = k0 + j > 0;
                         const bool has_r = k0 + j + 1 < L;

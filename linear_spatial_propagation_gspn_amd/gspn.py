@@ -92,10 +92,10 @@ def lib() -> ctypes.CDLL:
             h.gspn_proxy_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
             h.gspn_proxy_forward4_workspace_bytes.restype = i64
             h.gspn_proxy_forward4.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp,
-                                              ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, i64, ci, vp]
+                                              ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, i64, ci, vp]
             h.gspn_proxy_forward4.restype = ci
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
-                                        ctypes.POINTER(vp), vp, vp, i64, ci, vp]
+                                        ctypes.POINTER(vp), vp, vp, vp, i64, ci, vp]
             h.gspn_forward4_timed.argtypes = h.gspn_forward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_forward4_timed.restype = ci
             h.gspn_proxy_forward4_timed.argtypes = h.gspn_proxy_forward4.argtypes + [ctypes.POINTER(StageTimes)]
@@ -106,7 +106,7 @@ def lib() -> ctypes.CDLL:
             h.gspn_backward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
             h.gspn_backward4_workspace_bytes.restype = i64
             h.gspn_backward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
-                                         vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, i64, ci, vp]
+                                         vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, i64, ci, vp]
             h.gspn_backward4.restype = ci
             h.gspn_backward4_timed.argtypes = h.gspn_backward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_backward4_timed.restype = ci
@@ -269,7 +269,15 @@ def forward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
-def _forward4(x, logits, lams, chunk_len, out, workspace, times):
+def _merge_ptr(merge, c: int, device, name: str = "merge"):
+    """The device pointer of fp32 merge weights [4][c] (None: the plain sum)."""
+    if merge is None:
+        return None
+    _check(merge, name, (4, c), torch.float32, device)
+    return _ptr(merge)
+
+
+def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None):
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
@@ -288,7 +296,8 @@ def _forward4(x, logits, lams, chunk_len, out, workspace, times):
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
-    args = (n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, _ptr(out), ws_ptr, ws_bytes, _dtype_code(x),
+    mp = _merge_ptr(merge, c, x.device)
+    args = (n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, mp, _ptr(out), ws_ptr, ws_bytes, _dtype_code(x),
             _stream(x.device))
     if times is None:
         _raise(lib().gspn_forward4(*args), "gspn_forward4")
@@ -299,20 +308,23 @@ def _forward4(x, logits, lams, chunk_len, out, workspace, times):
 
 def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                   chunk_len: int = 0, out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Four-direction propagation with summed merge; logits[d] / lams[d] in
-    direction d's scan frame.  ``workspace`` (see forward4_workspace) lets the
-    library run the four directions concurrently when that pays."""
-    return _forward4(x, logits, lams, chunk_len, out, workspace, None)
+                  workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None) -> torch.Tensor:
+    """Four-direction propagation; logits[d] / lams[d] in direction d's scan
+    frame.  The directions are summed, or with ``merge`` (fp32 [4][C] on the
+    device) weighted per direction and channel.  ``workspace`` (see
+    forward4_workspace) lets the library run the four directions
+    concurrently when that pays."""
+    return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge)
 
 
 def gspn_forward4_timed(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                         chunk_len: int = 0, out: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+                        workspace: torch.Tensor | None = None,
+                        merge: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
     """gspn_forward4 with HIP events around every launch; returns (out,
     {stage: {"ms", "launches"}}).  Waits for the stream to reach its end."""
     times = StageTimes()
-    out = _forward4(x, logits, lams, chunk_len, out, workspace, times)
+    out = _forward4(x, logits, lams, chunk_len, out, workspace, times, merge)
     return out, times.as_dict()
 
 
@@ -325,7 +337,7 @@ def proxy_forward4_workspace(x: torch.Tensor, c_proxy: int, cw: int) -> torch.Te
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
-def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times):
+def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge=None):
     n, c, h, w = x.shape
     dt = x.dtype
     cp = w_down.shape[0]
@@ -346,7 +358,8 @@ def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, ti
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
-    args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up), zp, lp, _ptr(out),
+    mp = _merge_ptr(merge, cp, x.device)
+    args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up), zp, lp, mp, _ptr(out),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x), _stream(x.device))
     if times is None:
         _raise(lib().gspn_proxy_forward4(*args), "gspn_proxy_forward4")
@@ -358,20 +371,22 @@ def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, ti
 def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
                         logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                         chunk_len: int = 0, out: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+                        workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None) -> torch.Tensor:
     """Compressive-proxy forward: C -> C_proxy 1x1 projection, four-direction
-    scan with summed merge in proxy space, C_proxy -> C projection."""
-    return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None)
+    scan in proxy space (summed, or weighted by ``merge`` fp32 [4][C_proxy]),
+    C_proxy -> C projection."""
+    return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None, merge)
 
 
 def gspn_proxy_forward4_timed(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
                               logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                               chunk_len: int = 0, out: torch.Tensor | None = None,
-                              workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+                              workspace: torch.Tensor | None = None,
+                              merge: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
     """gspn_proxy_forward4 with HIP events around every launch; returns (out,
     {stage: {"ms", "launches"}})."""
     times = StageTimes()
-    out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times)
+    out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge)
     return out, times.as_dict()
 
 
@@ -386,11 +401,14 @@ def backward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
 
 def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                    gy: torch.Tensor, chunk_len: int = 0, workspace: torch.Tensor | None = None,
-                   out: tuple | None = None, times: StageTimes | None = None) -> tuple:
-    """Gradients of gspn_forward4 for dL/dy = gy: returns (dx, [dlogits_d],
-    [dlam_d]) in the inputs' layouts.  ``out`` may supply those tensors;
-    ``times`` (a StageTimes) selects gspn_backward4_timed and receives the
-    stage durations."""
+                   out: tuple | None = None, times: StageTimes | None = None,
+                   merge: torch.Tensor | None = None, dmerge: torch.Tensor | bool | None = None) -> tuple:
+    """Gradients of gspn_forward4 (with the same ``merge``) for dL/dy = gy:
+    returns (dx, [dlogits_d], [dlam_d]) in the inputs' layouts, and also the
+    merge weights' gradient (fp32 [4][C]) as a fourth element when ``merge``
+    is given or ``dmerge`` is (a tensor to fill, or True).  ``out`` may
+    supply the first three; ``times`` (a StageTimes) selects
+    gspn_backward4_timed and receives the stage durations."""
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
@@ -410,17 +428,22 @@ def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
     for d in range(4):
         _check(dz[d], "dlogits[%d]" % d, tuple(logits[d].shape), dt, x.device)
         _check(dl[d], "dlam[%d]" % d, tuple(lams[d].shape), dt, x.device)
+    want_dm = merge is not None or (dmerge is not None and dmerge is not False)
+    if want_dm and not isinstance(dmerge, torch.Tensor):
+        dmerge = torch.empty((4, c), dtype=torch.float32, device=x.device)
+    mp = _merge_ptr(merge, c, x.device)
+    dmp = _merge_ptr(dmerge, c, x.device, "dmerge") if want_dm else None
     if workspace is None:
         workspace = backward4_workspace(x, cw)
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
     vp4 = ctypes.c_void_p * 4
     args = (n, c, h, w, cw, int(chunk_len), _ptr(x), vp4(*[z.data_ptr() for z in logits]),
-            vp4(*[l.data_ptr() for l in lams]), _ptr(gy), _ptr(dx), vp4(*[t.data_ptr() for t in dz]),
-            vp4(*[t.data_ptr() for t in dl]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            vp4(*[l.data_ptr() for l in lams]), mp, _ptr(gy), _ptr(dx), vp4(*[t.data_ptr() for t in dz]),
+            vp4(*[t.data_ptr() for t in dl]), dmp, _ptr(workspace), workspace.numel() * workspace.element_size(),
             _dtype_code(x), _stream(x.device))
     if times is None:
         _raise(lib().gspn_backward4(*args), "gspn_backward4")
     else:
         _raise(lib().gspn_backward4_timed(*args, ctypes.byref(times)), "gspn_backward4_timed")
-    return dx, dz, dl
+    return (dx, dz, dl, dmerge) if want_dm else (dx, dz, dl)

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 5
+    assert lib.gspn_abi_version() == 6
     for code in range(12):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -101,8 +101,8 @@ def test_forward4_validation(lib):
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 5) == -1
 
-    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, y=D_, ws=None, wsb=0, dt=0):
-        return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, y, ws, wsb, dt, None)
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, m=None, y=D_, ws=None, wsb=0, dt=0):
+        return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, m, y, ws, wsb, dt, None)
 
     assert f(dt=3) == DTYPE
     assert f(cw=3) == WCH
@@ -117,6 +117,10 @@ def test_forward4_validation(lib):
     assert f(dt=1, ws=W + 2, wsb=wsb) == MISAL         # the workspace holds fp32 weights
     assert f(ws=D_ - 100, wsb=wsb) == ALIAS          # workspace overlaps y
     assert f(ws=A + 4, wsb=wsb) == ALIAS             # workspace overlaps x
+    M = 0x68000000                                   # merge weights, fp32 [4][c]
+    assert f(m=M + 2) == MISAL
+    assert f(m=D_ + 8) == ALIAS                      # y overlaps the merge weights
+    assert f(m=W + 16, ws=W, wsb=wsb) == ALIAS       # the workspace overlaps them
     assert f(n=0, x=0, z=None, l=None, y=0) == OK
 
 
@@ -150,8 +154,9 @@ def test_proxy_forward4_validation(lib):
     assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 0, 1, 1) == -1
     assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 3, 1) == -1
 
-    def f(n=1, c=6, h=8, w=8, cp=2, cw=1, chunk=0, x=A, wd=WD, wu=WU, z=zs, l=ls, y=D_, ws=WS, wsb=need, dt=1):
-        return lib.gspn_proxy_forward4(n, c, h, w, cp, cw, chunk, x, wd, wu, z, l, y, ws, wsb, dt, None)
+    def f(n=1, c=6, h=8, w=8, cp=2, cw=1, chunk=0, x=A, wd=WD, wu=WU, z=zs, l=ls, m=None, y=D_, ws=WS, wsb=need,
+          dt=1):
+        return lib.gspn_proxy_forward4(n, c, h, w, cp, cw, chunk, x, wd, wu, z, l, m, y, ws, wsb, dt, None)
 
     assert f(dt=2) == DTYPE
     assert f(cp=-1) == SHAPE
@@ -164,6 +169,8 @@ def test_proxy_forward4_validation(lib):
     assert f(ws=WS + 2) == MISAL
     assert f(y=A + 64) == ALIAS
     assert f(ws=A - 16) == ALIAS
+    assert f(m=0x73000001) == MISAL
+    assert f(m=WS + 64) == ALIAS                     # merge weights inside the workspace
     assert f(n=0, x=0, wd=0, wu=0, z=None, l=None, y=0, ws=0) == OK
 
 
@@ -215,7 +222,7 @@ def test_timed_variants_validate_like_untimed(lib):
         t.ms[i], t.launches[i] = 7.0, 7
 
     def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, y=D_, dt=0, times=ctypes.byref(t)):
-        return lib.gspn_forward4_timed(n, c, h, w, cw, chunk, x, zs, ls, y, None, 0, dt, None, times)
+        return lib.gspn_forward4_timed(n, c, h, w, cw, chunk, x, zs, ls, None, y, None, 0, dt, None, times)
 
     assert f(times=None) == NULLP
     assert f(dt=3) == DTYPE
@@ -230,7 +237,8 @@ def test_timed_variants_validate_like_untimed(lib):
     need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1)
 
     def g(n=1, cp=2, ws=WS, wsb=need, dt=1, times=ctypes.byref(t)):
-        return lib.gspn_proxy_forward4_timed(n, 6, 8, 8, cp, 1, 0, A, WD, WU, zs, ls, D_, ws, wsb, dt, None, times)
+        return lib.gspn_proxy_forward4_timed(n, 6, 8, 8, cp, 1, 0, A, WD, WU, zs, ls, None, D_, ws, wsb, dt, None,
+                                             times)
 
     assert g(times=None) == NULLP
     assert g(dt=2) == DTYPE
@@ -252,8 +260,9 @@ def test_backward4_validation(lib):
                                                                    5 * 3 * 64 * 2)
     assert lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
 
-    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, gy=GY, dx=DX, dz=dzs, dl=dls, ws=WS, wsb=need, dt=0):
-        return lib.gspn_backward4(n, c, h, w, cw, chunk, x, zs, ls, gy, dx, dz, dl, ws, wsb, dt, None)
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, m=None, gy=GY, dx=DX, dz=dzs, dl=dls, dm=None, ws=WS, wsb=need,
+          dt=0):
+        return lib.gspn_backward4(n, c, h, w, cw, chunk, x, zs, ls, m, gy, dx, dz, dl, dm, ws, wsb, dt, None)
 
     assert f(dt=2) == DTYPE
     assert f(chunk=-1) == CHUNK
@@ -267,8 +276,16 @@ def test_backward4_validation(lib):
     assert f(dx=A + 8) == ALIAS                     # dx on x
     assert f(dx=dls[1]) == ALIAS                    # dx on dlam[1]
     assert f(dx=WS + 64) == ALIAS                   # dx in the workspace
+    M, DM = 0x68000000, 0x69000000                  # merge weights and their gradient, fp32 [4][c]
+    assert f(m=M + 1) == MISAL
+    assert f(dm=DM + 2) == MISAL
+    assert f(m=M, dm=M + 4) == ALIAS                # dmerge on the merge weights
+    assert f(dm=DX + 8) == ALIAS                    # dmerge on dx
+    assert f(dm=WS + 8) == ALIAS                    # dmerge in the workspace
+    assert f(m=dls[2] + 4) == ALIAS                 # an output on the merge weights
     assert f(n=0, x=0, gy=0, dx=0, dz=None, dl=None, ws=0) == OK
     t = G.StageTimes()
-    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, GY, DX, dzs, dls, WS, need, 0, None, None) == NULLP
-    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, GY, DX, dzs, dls, WS, need - 1, 0, None,
+    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, GY, DX, dzs, dls, None, WS, need, 0, None,
+                                    None) == NULLP
+    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, GY, DX, dzs, dls, None, WS, need - 1, 0, None,
                                     ctypes.byref(t)) == WSPACE

@@ -1,0 +1,153 @@
+"""GPU parity of the learnable merge (one weight per direction and channel):
+gspn_forward4 / gspn_proxy_forward4 with merge weights and gspn_backward4's
+dmerge, through the C ABI, against the fp64 oracle on the same seeded inputs.
+Tolerances as for the plain sum: normwise 1e-5 (fp32 storage), 2e-2 (bf16)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_spatial_propagation_gspn_amd import gspn as G
+from linear_spatial_propagation_gspn_amd.workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _np(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def _err(got, ref):
+    return oracle.normwise_error(_np(got), ref)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _merge(c, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randn((4, c), generator=g, device=DEV, dtype=torch.float32)
+
+
+def _gy(wl, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    t = torch.randn((wl.n, wl.c_scan, wl.h, wl.w), generator=g, device=DEV, dtype=torch.float32)
+    return t.to(wl.torch_dtype)
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [0, 5])
+@pytest.mark.parametrize("shape,shared,kernel", [
+    ((2, 3, 23, 41), False, "plane4_kernel"),
+    ((1, 3, 40, 72), False, "scan4lp_kernel"),
+    ((1, 3, 40, 72), True, "scan4lp_kernel"),
+    ((2, 2, 40, 70), True, "scan4v_kernel"),
+    ((1, 2, 30, 2100), False, "scan_kernel"),
+])
+def test_forward4_merge(shape, shared, kernel, chunk, dtype, use_ws):
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, dtype, shared, chunk, 500 + h + w)
+    _say("forward4 merge %s shared=%s chunk=%d %s ws=%s" % (shape, shared, chunk, dtype, use_ws))
+    inp = make_inputs(wl, DEV)
+    m = _merge(c, 7 + w)
+    ws = G.forward4_workspace(inp["x"], wl.cw) if use_ws else None
+    got, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk, workspace=ws,
+                                       merge=m)
+    torch.cuda.synchronize()
+    if use_ws or kernel in ("plane4_kernel", "scan_kernel"):
+        assert times["scan_kernel"] == kernel, times["scan_kernel"]
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk, merge=_np(m))
+    assert _err(got, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 23, 41), (1, 2, 40, 72), (1, 2, 40, 70)])
+def test_unit_merge_is_the_plain_sum_bit_for_bit(shape):
+    """Weights of 1 leave every product unchanged: the same bits as no merge."""
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, "f32", False, 0, 9)
+    inp = make_inputs(wl, DEV)
+    ws = G.forward4_workspace(inp["x"], wl.cw)
+    a = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], workspace=ws)
+    b = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], workspace=ws,
+                        merge=torch.ones((4, c), device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_proxy_forward4_merge(dtype):
+    n, c, h, w, cp = 1, 40, 33, 47, 8
+    wl = Workload("case", n, c, h, w, dtype, True, 0, 77, c_proxy=cp)
+    inp = make_inputs(wl, DEV)
+    m = _merge(cp, 3)
+    got = G.gspn_proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"], merge=m)
+    torch.cuda.synchronize()
+    ref = oracle.proxy_forward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"], merge=_np(m))
+    assert _err(got, ref) <= (1e-5 if dtype == "f32" else 2e-2)
+
+
+def _check_backward(got, ref, tol, label):
+    dx, dz, dl, dm = got
+    rdx, rdl, rdz, rdm = ref
+    errs = {"dx": _err(dx, rdx), "dmerge": _err(dm, rdm)}
+    for d in range(4):
+        errs["dlam%d" % d] = _err(dl[d], rdl[d])
+        errs["dlogits%d" % d] = _err(dz[d], rdz[d])
+    worst = max(errs.values())
+    _say("  %s: worst normwise error %.3g (dmerge %.3g)" % (label, worst, errs["dmerge"]))
+    assert worst <= tol, errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [0, 5])
+@pytest.mark.parametrize("shape,shared", [
+    ((2, 3, 23, 41), False),
+    ((1, 3, 40, 72), True),      # channel groups of the shared-logit adjoint, a partial last group
+    ((1, 2, 5, 1500), False),    # two positions per lane
+    ((1, 5, 3, 1100), True),     # two positions per lane, shared
+])
+def test_backward4_merge(shape, shared, chunk, dtype):
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, dtype, shared, chunk, 600 + h + w)
+    _say("backward4 merge %s shared=%s chunk=%d %s" % (shape, shared, chunk, dtype))
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 19)
+    m = _merge(c, 11 + h)
+    got = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=chunk, merge=m)
+    torch.cuda.synchronize()
+    ref = oracle.backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk=chunk, merge=_np(m))
+    _check_backward(got, ref, TOL[dtype], "all outputs")
+
+
+def test_backward4_dmerge_without_merge():
+    """dmerge requested with no merge weights: the gradient at m = 1, and the
+    other outputs equal those of the plain call."""
+    wl = Workload("case", 2, 3, 30, 50, "f32", False, 0, 13)
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 5)
+    plain = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy)
+    got = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, dmerge=True)
+    torch.cuda.synchronize()
+    assert len(plain) == 3 and len(got) == 4
+    assert torch.equal(plain[0], got[0])
+    for d in range(4):
+        assert torch.equal(plain[1][d], got[1][d]) and torch.equal(plain[2][d], got[2][d])
+    ref = oracle.backward4(inp["x"], inp["logits"], inp["lam"], gy, merge=np.ones((4, 3)))
+    assert _err(got[3], ref[3]) <= 1e-5
