@@ -83,13 +83,16 @@ def algorithmic_bytes(wl) -> int:
     return x + lam + z + wts + x
 
 
-def scan_launch_bytes(wl, kernel: str) -> int:
+def scan_launch_bytes(wl, kernel: str, launches: int = 1) -> int:
     """Algorithmic bytes of one launch of the scan kernel the step ran: every
     tensor the launch reads or writes, moved once.
       plane4_kernel (one launch, planes in LDS): x, the four directions'
         logits and lambdas, y written;
       scan4v_kernel / scan4lp_kernel (one launch): x and its transpose, four
         directions' weights and lambdas, four output maps written;
+      scan4band_kernel (one launch per band of steps): the long-line
+        kernel's bytes spread over the bands (the band-boundary states, a few
+        MB, are not counted);
       scan_kernel (one launch per direction): x (or its transpose), the
         direction's weights and lambda, the output written, and read as well
         by the two launches that add into a map (average over the four)."""
@@ -99,6 +102,8 @@ def scan_launch_bytes(wl, kernel: str) -> int:
     wd = weight_bytes_per_direction(wl)
     if kernel in ("scan4v_kernel", "scan4lp_kernel"):
         return 2 * u + 4 * wd + 4 * u + 4 * u
+    if kernel == "scan4band_kernel":
+        return (2 * u + 4 * wd + 4 * u + 4 * u) // launches
     total = 4 * u + 4 * wd + 4 * u + 4 * u + 2 * u
     return total // 4
 
@@ -437,7 +442,7 @@ def main():
     scan = st["scan"]
     launches = scan["launches"]
     kernel_ms = scan["ms"] / launches
-    bpl = scan_launch_bytes(wl, kernel)
+    bpl = scan_launch_bytes(wl, kernel, launches)
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
     traffic, traffic_src = counter_traffic(kernel, wl)
     alg = algorithmic_bytes(wl)

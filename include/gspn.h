@@ -158,12 +158,14 @@ gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
 /*
  * gspn_forward4_workspace_bytes -- bytes of the optional gspn_forward4
  * workspace: four maps of n*c*h*w elements of the storage type (x transposed
- * into the horizontal scan frame and three partial outputs) and, for
+ * into the horizontal scan frame and three partial outputs); for
  * channel-shared weights over more than one channel (cw == 1 < c), the four
  * directions' normalised weights: 4 * 3 * n*h*w floats for GSPN_F32, 4 *
- * n*h*w 32-bit half pairs for GSPN_BF16 (see gspn_forward4).  Returns -1
- * when the arguments are invalid (negative or overflowing dimensions, cw not
- * in {1, c}, unknown dtype).
+ * n*h*w 32-bit half pairs for GSPN_BF16 (see gspn_forward4); rounded up to a
+ * multiple of 4 bytes; then 2 * 4 * n*c * max(h, w) floats of scan states at
+ * band boundaries (used when very few long lines are split across
+ * workgroups).  Returns -1 when the arguments are invalid (negative or
+ * overflowing dimensions, cw not in {1, c}, unknown dtype).
  */
 int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                                       int dtype);
@@ -201,7 +203,10 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              directions run as row-coalesced scans whose outputs a
  *              transposing merge adds into y, and (c) runs all four
  *              directions in one launch into separate maps (lines up to 2048
- *              positions).  Its contents afterwards are unspecified.
+ *              positions), or, when the planes are so few that the four
+ *              directions make at most 64 long lines, splits each line
+ *              across workgroups and runs the scan in bands of steps, one
+ *              launch per band.  Its contents afterwards are unspecified.
  *              Planes of at most 64 x 64 take a one-pass path (x read once,
  *              y written once) with or without a workspace.  In all cases y
  *              is the same up to fp32 rounding order and, for bf16, rounding
@@ -319,7 +324,8 @@ typedef enum {
     GSPN_SCAN_PER_DIRECTION = 1,/* one launch per direction */
     GSPN_SCAN_FUSED4 = 2,       /* four directions in one launch, one workgroup per line */
     GSPN_SCAN_LONG_LINE = 3,    /* four directions in one launch, 16-byte vectors per lane */
-    GSPN_SCAN_PLANE = 4         /* one workgroup per plane, all four directions, y written once */
+    GSPN_SCAN_PLANE = 4,        /* one workgroup per plane, all four directions, y written once */
+    GSPN_SCAN_BANDED = 5        /* very few long lines: lines split across workgroups, one launch per band of steps */
 } gspn_scan_kernel;
 
 typedef struct {

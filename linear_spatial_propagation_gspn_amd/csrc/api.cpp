@@ -58,7 +58,7 @@ gspn_status from_hip(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR
 // Optional event timing of the launches of one forward call: a pair of HIP
 // events around each launch, read back by finish().
 struct Timer {
-    static constexpr int kMax = 16;
+    static constexpr int kMax = 64;
     hipStream_t st = nullptr;
     int count = 0;
     int stage[kMax] = {};
@@ -313,7 +313,9 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
     // direction: fp32 triples for fp32 storage, packed half pairs for bf16
     const int64_t per_dir = checked_product({n, h, w}) * (dtype == GSPN_F32 ? 3 * 4 : 4);
     const int64_t weights = (cw == 1 && c > 1) ? 4 * per_dir : 0;
-    return maps + weights;
+    // fp32 states at band boundaries for the banded scan of very few lines
+    const int64_t states = gspn::band_state_floats(checked_product({n, c}), h > w ? h : w) * 4;
+    return (maps + weights + 3) / 4 * 4 + states;
 }
 
 }  // extern "C"
@@ -441,18 +443,30 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     }
 
     // Concurrent path: the four directions in one launch, each into its own
-    // map (lines up to 2048 positions).
+    // map (lines up to 2048 positions); very few long lines instead run split
+    // across workgroups, one launch per band of steps.
     if (gspn::fused4_supported(h, w)) {
         p[1].out = m1;
         p[2].out = m2;
         p[3].out = m3;
-        int kind = GSPN_SCAN_FUSED4;
-        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
-            return GSPN_ERR_HIP;
-        if (tm) tm->scan_kernel = kind;
+        for (int d = 0; d < 4; ++d) p[d].mscale = nullptr;  // the transposing merge applies the merge weights
+        const int nbands = gspn::band_launches(p);
+        if (nbands > 0) {
+            float* state = reinterpret_cast<float*>(ws + ((prenorm ? 4 * wdir : 0) + 4 * xb + 3) / 4 * 4);
+            for (int b = 0; b < nbands; ++b)
+                if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4_band(p, state, b, st); }) !=
+                    hipSuccess)
+                    return GSPN_ERR_HIP;
+            if (tm) tm->scan_kernel = GSPN_SCAN_BANDED;
+        } else {
+            int kind = GSPN_SCAN_FUSED4;
+            if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
+                return GSPN_ERR_HIP;
+            if (tm) tm->scan_kernel = kind;
+        }
         return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
             return gspn::launch_combine(y, m1, m2, m3, n * c, static_cast<int>(h), static_cast<int>(w), 1, dtype,
-                                        st);
+                                        st, merge, c);
         }));
     }
     // Longer lines, sequential path: T2B writes y, B2T adds to it; L2R writes

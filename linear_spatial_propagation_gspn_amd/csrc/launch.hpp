@@ -39,9 +39,21 @@ bool fused4_supported(int64_t h, int64_t w);
 
 // Four vertical-form scans in one launch (p[d].dir in {0, 1}): used for the
 // vertical directions on x and the horizontal ones on the transposed x.
+// Merge weights (mscale) are not taken: the merge of the separate outputs
+// applies them.
 // *kind (if given) receives the kernel used: 2 = one workgroup per line,
 // 3 = the long-line kernel (gspn_scan_kernel values).
 hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind = nullptr);
+
+// The same four vertical-form scans (outputs in the storage type) for
+// launches of very few long lines: each line is split across workgroups and
+// the scan advances in bands of steps, one launch per band.
+// band_launches: the number of bands, or 0 when this path does not apply.
+// state: band_state_floats(n * c, max line length) floats of scratch (fp32
+// states at the band boundaries); bands run in order 0 .. band_launches - 1.
+int band_launches(const ScanParams (&p)[4]);
+int64_t band_state_floats(int64_t planes, int64_t lmax);
+hipError_t launch_scan4_band(const ScanParams (&p)[4], float* state, int band, hipStream_t stream);
 
 // All four directions of planes of at most 64 x 64 in one pass, y written
 // once (chunk[d]: steps per chunk of direction d, clamped to [1, S_d];
@@ -55,10 +67,12 @@ hipError_t launch_plane4(const void* x, const void* const logits[4], const void*
 hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, int Cc, int dtype,
                             hipStream_t stream);
 
-// y[p][r][c] = ((z2[p][c][r] + z3[p][c][r]) + y[p][r][c] (if accumulate)) + a[p][r][c]
-// over planes of R x Cc; a, z2, z3 may be NULL; z2, z3 are Cc x R planes.
+// y[p][r][c] = ((m2 z2[p][c][r] + m3 z3[p][c][r]) + m0 y[p][r][c] (if accumulate)) + m1 a[p][r][c]
+// over planes of R x Cc; a, z2, z3 may be NULL; z2, z3 are Cc x R planes;
+// m0..m3: merge[k][p % nch] (learnable merge weights [4][nch]), or 1 if merge is null.
 hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3, int64_t planes, int R,
-                          int Cc, int accumulate, int dtype, hipStream_t stream);
+                          int Cc, int accumulate, int dtype, hipStream_t stream, const float* merge = nullptr,
+                          int64_t nch = 1);
 
 // out_dtype: storage type of w_out (-1: the same as dtype; kF32 is allowed
 // for bf16 logits).

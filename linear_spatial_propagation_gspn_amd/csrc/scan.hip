@@ -2,6 +2,7 @@
 // their launch families live in scan_kernel.hpp, instantiated per storage type
 // and direction family in scan_{f32,bf16,bf16pair}_{vert,horiz}.hip and
 // scan4_{f32,bf16,bf16pair}.hip).
+#include "scan_band.hpp"
 #include "scan_kernel.hpp"
 #include "scan_lp.hpp"
 
@@ -33,6 +34,10 @@ extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true, float>(const Sc
 extern template hipError_t launch_fused4v<bf16_t, WPair, float>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, WPair, false, float>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, WPair, false>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_band4<float, float, true>(const BandK&, hipStream_t);
+extern template hipError_t launch_band4<float, float, false>(const BandK&, hipStream_t);
+extern template hipError_t launch_band4<bf16_t, bf16_t, true>(const BandK&, hipStream_t);
+extern template hipError_t launch_band4<bf16_t, WPair, false>(const BandK&, hipStream_t);
 
 namespace {
 
@@ -166,7 +171,70 @@ bool lp_eligible(const ScanParams (&p)[4]) {
     return true;
 }
 
+// The banded kernel (scan_band.hpp) serves long-line launches with so few
+// lines that one workgroup per line would leave most CUs idle: one wave of
+// 16-byte vectors covers a segment of half its positions plus a halo of a
+// quarter on each side, and a band runs as many steps as the halo is wide.
+namespace {
+
+constexpr int64_t kBandMaxLines = 64;  // lines (planes x 4 directions) below which it pays
+constexpr int kBandMaxLaunches = 32;
+
+int band_positions(int dtype) { return 64 * (dtype == kF32 ? 4 : 8); }
+
+}  // namespace
+
+int band_launches(const ScanParams (&p)[4]) {
+    if (!lp_eligible(p)) return 0;
+    for (int d = 0; d < 4; ++d)
+        if (p[d].mscale) return 0;  // merge weights are applied after the scan (launch_combine)
+    if (p[0].odtype != -1 && p[0].odtype != p[0].dtype) return 0;
+    const int span = band_positions(p[0].dtype);
+    const int64_t planes = p[0].n * p[0].c;
+    if (planes * 4 > kBandMaxLines) return 0;
+    int smax = 0;
+    for (int d = 0; d < 4; ++d) {
+        if (p[d].w < span) return 0;  // lines shorter than one workgroup's span gain nothing
+        smax = static_cast<int>(p[d].h > smax ? p[d].h : smax);
+    }
+    const int halo = span / 4;
+    const int n = (smax + halo - 1) / halo;
+    return n <= kBandMaxLaunches ? n : 0;
+}
+
+int64_t band_state_floats(int64_t planes, int64_t lmax) { return 2 * 4 * planes * lmax; }
+
+hipError_t launch_scan4_band(const ScanParams (&p)[4], float* state, int index, hipStream_t stream) {
+    const int P = p[0].dtype == kF32 ? 4 : 8;
+    const int span = band_positions(p[0].dtype);
+    const int64_t planes = p[0].n * p[0].c;
+    BandK b;
+    b.seg = span / 2;
+    b.halo = span / 4;
+    b.t0 = index * b.halo;
+    int64_t lmax = 0;
+    for (int d = 0; d < 4; ++d) {
+        b.d[d] = make_args(p[d], P);
+        b.nseg[d] = (b.d[d].L + b.seg - 1) / b.seg;
+        b.blocks[d] = b.t0 < b.d[d].S ? planes * b.nseg[d] : 0;
+        lmax = b.d[d].L > lmax ? b.d[d].L : lmax;
+    }
+    b.sstride = planes * lmax;
+    b.hin = state + (index & 1) * 4 * b.sstride;
+    b.hout = state + ((index + 1) & 1) * 4 * b.sstride;
+    if (p[0].dtype == kF32) {
+        return p[0].wts_are_logits ? launch_band4<float, float, true>(b, stream)
+                                   : launch_band4<float, float, false>(b, stream);
+    }
+    if (p[0].wdtype == kPairF16) return launch_band4<bf16_t, WPair, false>(b, stream);
+    return launch_band4<bf16_t, bf16_t, true>(b, stream);
+}
+
 hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind) {
+    // the separate output maps are merged afterwards (launch_combine), which
+    // applies any merge weights
+    for (int d = 0; d < 4; ++d)
+        if (p[d].mscale) return hipErrorInvalidValue;
     // every p[d] is a vertical-form scan (dir 0 or 1); p[0..1] share one line
     // length, p[2..3] another
     const int l01 = static_cast<int>(p[0].w);

@@ -1,5 +1,6 @@
 // scan4_bf16pair.hip -- instantiates the four-scans-in-one-launch kernels for bf16 storage with channel-shared weights pre-normalised as packed half pairs.
 #include "scan_kernel.hpp"
+#include "scan_band.hpp"
 #include "scan_lp.hpp"
 
 namespace gspn {
@@ -10,5 +11,8 @@ template hipError_t launch_fused4lp<bf16_t, WPair, false>(const Scan4K&, int, hi
 // fp32 states (the backward pass's recomputed forward)
 template hipError_t launch_fused4v<bf16_t, WPair, float>(const Scan4K&, int, int, int, hipStream_t);
 template hipError_t launch_fused4lp<bf16_t, WPair, false, float>(const Scan4K&, int, hipStream_t);
+
+// the banded kernel for very few long lines
+template hipError_t launch_band4<bf16_t, WPair, false>(const BandK&, hipStream_t);
 
 }  // namespace gspn

@@ -1,0 +1,220 @@
+// scan_band.hpp -- the four-direction line scan for very few, long lines,
+// split across workgroups (internal to libgspn; instantiated in scan4_*.hip).
+//
+// Same recurrence as scan_lp.hpp (GSPN-2 paper notes, "2D spatial
+// propagation recap"; chunks from "Optimisation 1"), for launches whose
+// lines are so few that one workgroup per line leaves most of the GPU idle:
+// the eight proxy-space planes of the compressive proxy ("Optimisation 2")
+// make 32 lines of 2048 positions, and a workgroup moves only about 60 GB/s,
+// so each step of such a scan costs the time one CU needs to pull the line's
+// inputs.  Here a line is cut into segments of `seg` positions, one
+// single-wave workgroup per segment, and the scan advances in bands of
+// `halo` steps, one launch per band:
+//  - a workgroup is one wave of 16-byte vectors (8 bf16 or 4 fp32 positions
+//    per lane): its segment of half those positions plus `halo`, a quarter,
+//    on each side (the line borders clip this), starting from the exact
+//    states at the band's first step, which the previous band stored;
+//  - the tridiagonal coupling moves information one position per step, so
+//    the values that the halo's outer edge gets wrong (its outer neighbours
+//    are taken as 0) reach at most `halo` positions inwards by the band's
+//    end: the segment itself stays exact, and only it is stored;
+//  - at the band's end the segment's states go to a state buffer (fp32) from
+//    which the next band's workgroups, including the neighbours' halos,
+//    start.  Bands are separate launches, so no workgroup waits for another.
+// The halos double the arithmetic and the cache traffic, not the HBM traffic
+// (neighbouring workgroups read the same lines within the same steps).
+#pragma once
+
+#include "scan_lp.hpp"
+
+namespace gspn {
+
+#ifndef GSPN_BAND_DEPTH
+#define GSPN_BAND_DEPTH 8
+#endif
+
+struct BandK {
+    ScanK d[4];
+    int64_t blocks[4];  // workgroups of each direction in this band (0: its scan has ended)
+    int nseg[4];        // segments per line of each direction
+    const float* hin;   // states at the band's first step: direction d, plane p at hin + d * sstride + p * L_d
+    float* hout;        // states at the band's last step, same layout
+    int64_t sstride;    // floats per direction in the state buffers
+    int t0;             // first scan step of the band
+    int seg;            // positions per segment (a multiple of the lane width P)
+    int halo;           // steps per band = positions of halo on each side (a multiple of P)
+};
+
+template <typename T, typename TW, bool LOGITS>
+__device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p, int g) {
+    const ScanK& a = b.d[dir];
+    constexpr int P = 16 / static_cast<int>(sizeof(T));  // positions per lane
+    constexpr int WT = P * static_cast<int>(sizeof(T)) / 4;
+    constexpr bool PAIR = std::is_same_v<TW, WPair>;
+    constexpr int ZB = PAIR ? 4 : static_cast<int>(sizeof(TW));
+    constexpr int NZ = PAIR ? 1 : 3;
+    constexpr int WW = P * ZB / 4;
+    constexpr int D = GSPN_BAND_DEPTH;
+
+    const int lane = threadIdx.x;
+    const int S = a.S;
+    const int L = a.L;
+    const int64_t plane = static_cast<int64_t>(S) * L;
+    const int64_t nidx = p / a.c;
+    const int64_t ci = p - nidx * a.c;
+
+    const auto rx = lp::rsrc(static_cast<const T*>(a.x) + p * plane, plane * sizeof(T));
+    const auto rl = lp::rsrc(static_cast<const T*>(a.lam) + p * plane, plane * sizeof(T));
+    const auto ro = lp::rsrc(static_cast<T*>(a.out) + p * plane, plane * sizeof(T));
+    const auto rz = lp::rsrc(static_cast<const char*>(a.wts) +
+                                 (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane) * ZB,
+                             NZ * plane * ZB);
+
+    const int s0 = g * b.seg;
+    const int s1 = min(s0 + b.seg, L);
+    const int k0 = s0 - b.halo + lane * P;   // the lane's first position (may lie outside the line)
+    const bool active = k0 >= 0 && k0 < L && k0 < s1 + b.halo;
+    const bool owned = k0 >= s0 && k0 < s1;  // positions this workgroup stores
+    const int k0c = min(max(k0, 0), L - P);  // addresses of lanes outside the line stay inside it
+    const uint32_t vt = static_cast<uint32_t>(k0c) * sizeof(T);
+    const uint32_t vw = static_cast<uint32_t>(k0c) * ZB;
+    const uint32_t rowT = static_cast<uint32_t>(L) * sizeof(T);
+    const uint32_t rowW = static_cast<uint32_t>(L) * ZB;
+    const uint32_t planeW = static_cast<uint32_t>(plane) * ZB;
+    const bool has_l0 = k0 > 0;
+    const bool has_rP = k0 + P < L;
+
+    const int t0 = b.t0;
+    const int t1 = min(t0 + b.halo, S);
+    const int K = a.K;
+    int cpos = t0 % K;  // step within the current chunk
+    const bool rev = a.reverse != 0;
+    auto line_of = [&](int t) { return static_cast<uint32_t>(rev ? S - 1 - t : t); };
+
+    uint32_t sx[D][WT], sl[D][WT], sz[D][NZ][WW];
+    auto fill = [&](auto slot, int t) {
+        constexpr int s = decltype(slot)::value;
+        const uint32_t i = line_of(min(t, t1 - 1));
+        lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, i * rowT);
+        lp::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, i * rowT);
+        constexpr int ZAUX = LOGITS ? GSPN_LP_STREAM_AUX : 0;
+#pragma unroll
+        for (int o = 0; o < NZ; ++o) lp::load_words<WW, ZAUX>(sz[s][o], rz, vw, o * planeW + i * rowW);
+    };
+
+    // states at the band's start (a chunk's first step ignores them)
+    float h[P];
+    const float* hin = b.hin + dir * b.sstride + p * L;
+#pragma unroll
+    for (int j = 0; j < P; ++j) h[j] = (t0 > 0 && active) ? hin[k0c + j] : 0.0f;
+
+    auto step = [&](auto slot, int t) {
+        constexpr int s = decltype(slot)::value;
+        float hn[P];
+        const bool first = cpos == 0;
+        cpos = cpos + 1 == K ? 0 : cpos + 1;
+        if (first) {  // a chunk's first line: h_prev = 0, its weights unused
+#pragma unroll
+            for (int j = 0; j < P; ++j) hn[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+        } else {
+            const float left = lp::shift_from_lower_lane(h[P - 1]);   // 0 beyond the wave
+            const float right = lp::shift_from_upper_lane(h[0]);
+            if constexpr (PAIR) {
+                // centre weight eliminated, as in the long-line kernel
+                float dd[P + 1];
+                dd[0] = h[0] - left;
+#pragma unroll
+                for (int j = 1; j < P; ++j) dd[j] = h[j] - h[j - 1];
+                dd[P] = right - h[P - 1];
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const float base =
+                        __builtin_fmaf(lp::elem<T, WT>(sl[s], j), lp::elem<T, WT>(sx[s], j), h[j]);
+                    hn[j] = __builtin_fmaf(pair_hi(sz[s][0][j]), dd[j + 1],
+                                           __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const float z0 = lp::elem<TW, WW>(sz[s][0], j);
+                    const float z1 = lp::elem<TW, WW>(sz[s][NZ > 1 ? 1 : 0], j);
+                    const float z2 = lp::elem<TW, WW>(sz[s][NZ > 2 ? 2 : 0], j);
+                    float w0, w1, w2;
+                    if constexpr (LOGITS) {
+                        normalise_row(z0, z1, z2, j > 0 || has_l0, j < P - 1 || has_rP, w0, w1, w2);
+                    } else {
+                        w0 = z0;
+                        w1 = z1;
+                        w2 = z2;
+                    }
+                    const float u = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+                    const float hl = j == 0 ? left : h[j - 1];
+                    const float hr = j == P - 1 ? right : h[j + 1];
+                    hn[j] = __builtin_fmaf(w0, hl, __builtin_fmaf(w1, h[j], __builtin_fmaf(w2, hr, u)));
+                }
+            }
+        }
+        fill(slot, t + D);
+        // lanes outside the line hold exact zeros: their values reach the
+        // line's border positions, whose weights to them are 0
+#pragma unroll
+        for (int j = 0; j < P; ++j) h[j] = active ? hn[j] : 0.0f;
+        if (owned) {
+            uint32_t ow[WT];
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+                for (int e = 0; e < WT; ++e) ow[e] = __float_as_uint(h[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < WT; ++e) ow[e] = pack_bf16x2(h[2 * e], h[2 * e + 1]);
+            }
+            const lp::int4v o = {static_cast<int>(ow[0]), static_cast<int>(ow[1]), static_cast<int>(ow[2]),
+                                 static_cast<int>(ow[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(o, ro, vt, line_of(t) * rowT, GSPN_LP_STREAM_AUX);
+        }
+    };
+
+    [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        (fill(IC<Ss>{}, t0 + Ss), ...);
+    }(std::make_integer_sequence<int, D>{});
+    int t = t0;
+    for (; t + D <= t1; t += D) {
+        [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+            (step(IC<Ss>{}, t + Ss), ...);
+        }(std::make_integer_sequence<int, D>{});
+    }
+    [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        ((t + Ss < t1 ? step(IC<Ss>{}, t + Ss) : void()), ...);
+    }(std::make_integer_sequence<int, D - 1>{});
+
+    if (owned) {
+        float* ho = b.hout + dir * b.sstride + p * L + k0;
+#pragma unroll
+        for (int j = 0; j < P; ++j) ho[j] = h[j];
+    }
+}
+
+template <typename T, typename TW, bool LOGITS>
+__global__ __launch_bounds__(64) void scan4band_kernel(const BandK b) {
+    int dir = 0;
+    int64_t idx = blockIdx.x;
+    while (dir < 3 && idx >= b.blocks[dir]) {
+        idx -= b.blocks[dir];
+        ++dir;
+    }
+    const int64_t p = idx / b.nseg[dir];
+    const int g = static_cast<int>(idx - p * b.nseg[dir]);
+    band_segment<T, TW, LOGITS>(b, dir, p, g);
+}
+
+// One band: every direction whose scan has not ended by step b.t0.
+template <typename T, typename TW, bool LOGITS>
+hipError_t launch_band4(const BandK& b, hipStream_t stream) {
+    const int64_t nblocks = b.blocks[0] + b.blocks[1] + b.blocks[2] + b.blocks[3];
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS>), dim3(static_cast<unsigned>(nblocks)), dim3(64), 0, stream,
+                       b);
+    return hipGetLastError();
+}
+
+}  // namespace gspn

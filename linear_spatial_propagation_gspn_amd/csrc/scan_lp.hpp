@@ -21,7 +21,9 @@
 //    each refilled as soon as its step has read it (the loop is unrolled by
 //    D so the slot indices are compile-time constants).
 // All four directions are described in vertical form (the horizontal ones on
-// x transposed into their scan frame), as for scan4v_kernel.
+// x transposed into their scan frame), as for scan4v_kernel.  The outputs are
+// the unweighted scans: learnable merge weights are applied where the
+// separate outputs are merged.
 #pragma once
 
 #include <utility>
@@ -118,7 +120,6 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
     const int64_t plane = static_cast<int64_t>(S) * L;
     const int64_t nidx = p / a.c;
     const int64_t ci = p - nidx * a.c;
-    const float msc = a.mscale ? a.mscale[ci] : 1.0f;  // learnable merge: this direction's weight
 
     const auto rx = lp::rsrc(static_cast<const T*>(a.x) + p * plane, plane * sizeof(T));
     const auto rl = lp::rsrc(static_cast<const T*>(a.lam) + p * plane, plane * sizeof(T));
@@ -171,7 +172,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
         float hn[P];
         if constexpr (FIRST) {
 #pragma unroll
-            for (int j = 0; j < P; ++j) hn[j] = (lp::elem<T, WT>(sl[s], j) * msc) * lp::elem<T, WT>(sx[s], j);
+            for (int j = 0; j < P; ++j) hn[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
         } else if constexpr (PAIR) {
             // h + w_{k-1} (h_{k-1} - h) + w_{k+1} (h_{k+1} - h) + lambda x: the
             // same row-stochastic combination with the centre weight
@@ -191,13 +192,13 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
             dd[P] = right - h[P - 1];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                const float base = __builtin_fmaf(lp::elem<T, WT>(sl[s], j) * msc, lp::elem<T, WT>(sx[s], j), h[j]);
+                const float base = __builtin_fmaf(lp::elem<T, WT>(sl[s], j), lp::elem<T, WT>(sx[s], j), h[j]);
                 hn[j] = __builtin_fmaf(pair_hi(sz[s][0][j]), dd[j + 1], __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base));
             }
         } else {
             float u[P];
 #pragma unroll
-            for (int j = 0; j < P; ++j) u[j] = (lp::elem<T, WT>(sl[s], j) * msc) * lp::elem<T, WT>(sx[s], j);
+            for (int j = 0; j < P; ++j) u[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
             float w[3][P];
 #pragma unroll
             for (int j = 0; j < P; ++j) {

@@ -90,13 +90,20 @@ def test_forward4_validation(lib):
     zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
     ls = vp4(C_, C_, C_, C_)
     W = 0x60000000
+    def states(planes, lmax):  # fp32 scan states at band boundaries, two buffers of four directions
+        return 2 * 4 * planes * lmax * 4
+
     wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 0)
-    assert wsb == 4 * 2 * 64 * 4
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 1) == 4 * 2 * 64 * 2
+    assert wsb == 4 * 2 * 64 * 4 + states(2, 8)
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 1) == 4 * 2 * 64 * 2 + states(2, 8)
     # channel-shared weights add the four directions' fp32 weights
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 0) == 4 * 2 * 64 * 4 + 4 * 3 * 64 * 4  # fp32 triples
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1) == 4 * 2 * 64 * 2 + 4 * 64 * 4      # half pairs
-    assert lib.gspn_forward4_workspace_bytes(1, 1, 8, 8, 1, 0) == 4 * 64 * 4
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 0) == (4 * 2 * 64 * 4 + 4 * 3 * 64 * 4  # fp32 triples
+                                                                  + states(2, 8))
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1) == (4 * 2 * 64 * 2 + 4 * 64 * 4      # half pairs
+                                                                  + states(2, 8))
+    assert lib.gspn_forward4_workspace_bytes(1, 1, 8, 8, 1, 0) == 4 * 64 * 4 + states(1, 8)
+    assert lib.gspn_forward4_workspace_bytes(1, 1, 3, 5, 1, 1) == 4 * 15 * 2 + states(1, 5)
+    assert lib.gspn_forward4_workspace_bytes(2, 3, 6, 40, 3, 1) == 4 * 2 * 3 * 240 * 2 + states(6, 40)
     assert lib.gspn_forward4_workspace_bytes(1, -2, 8, 8, 2, 0) == -1
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 5) == -1

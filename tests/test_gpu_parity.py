@@ -248,6 +248,30 @@ def test_long_line_kernel_plane_groups(shape, dtype):
     assert _err(got, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("chunk", [0, 7])
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("dtype,shape,bands", [
+    ("f32", (1, 2, 520, 600), 10),    # segments of 128 positions, halos and bands of 64 steps; ragged last segments
+    ("bf16", (1, 2, 520, 600), 5),    # segments of 256, halos and bands of 128
+    ("bf16", (2, 3, 1024, 512), 8),   # 24 lines; the horizontal scans outlast the vertical ones
+])
+def test_banded_kernel(dtype, shape, bands, shared, chunk):
+    """Very few long lines: each line split across workgroups, the scan run
+    in bands of steps (one launch per band)."""
+    n, c, h, w = shape
+    wl = _wl(n=n, c=c, h=h, w=w, dtype=dtype, shared=shared, chunk=chunk, seed=81 + h + w)
+    _say("banded %s %s shared=%s chunk=%d" % (shape, dtype, shared, chunk))
+    inp = make_inputs(wl, DEV)
+    m = torch.randn((4, c), device=DEV) if chunk else None
+    got, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk,
+                                       workspace=G.forward4_workspace(inp["x"], wl.cw), merge=m)
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "scan4band_kernel", times["scan_kernel"]
+    assert times["scan"]["launches"] == bands
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk, merge=None if m is None else _np(m))
+    assert _err(got, ref) <= TOL[dtype]
+
+
 def test_forward4_closed_form_constant_input():
     # lambda = 1, x = c: every direction's h at scan step t is (t+1) c, so the
     # merged output is (H + W + 2) c everywhere, whatever the logits.
