@@ -5,15 +5,20 @@
 // bf16 storage runs on the matrix cores (gfx950 bf16 MFMA, fp32 accumulate):
 //  - narrow output (c_out <= 16, c_in % 8 == 0, e.g. C -> C_proxy):
 //    v_mfma_f32_16x16x32_bf16 with M = output channels, N = 16 pixels, K = 32
-//    input channels per instruction.  A wave covers 64 pixels: each lane
-//    loads 4 pixels of 8 input channels with 8-byte loads (16 lanes make one
-//    128-byte run of a channel row) and its 8 weights with one 16-byte load,
-//    and feeds four MFMAs, one per pixel of its quad.
+//    input channels per instruction.  A wave covers 128 pixels: each lane
+//    loads 8 pixels of 8 input channels with 16-byte loads (16 lanes make one
+//    256-byte run of a channel row) and its 8 weights with one 16-byte load,
+//    and feeds eight MFMAs, one per pixel of its group (64 pixels and 8-byte
+//    loads where the pixel count is not a multiple of 128).
 //  - narrow input (c_in <= 8, e.g. C_proxy -> C): v_mfma_f32_32x32x8_bf16
-//    with M = 32 output channels, N = 32 pixels, K = 8.  A wave covers 64
-//    pixels as even / odd halves, so each lane ends with two adjacent pixels
-//    of 16 output channels and stores them as one dword (32 lanes make one
-//    128-byte run of an output row).
+//    with M = 32 output channels, N = 32 pixels, K = 8.  A wave covers 128
+//    pixels as four interleaved quarters, so each lane ends with four
+//    adjacent pixels of 16 output channels and stores them as one 8-byte
+//    vector (32 lanes make one 256-byte run of an output row; 64 pixels and
+//    dwords where the pixel count is not a multiple of 128).
+// Longer runs per channel row measured faster on MI355X: each wave touches
+// every channel row of its pixels once, so fewer, longer runs per row cut
+// the rows opened per byte moved.
 // Operand layouts (checked on gfx950): lane l holds row l % M of A and column
 // l % M of B, with k = (l / M) * KE + e for its KE elements; the 16x16 result
 // holds rows (l/16)*4 + i of column l % 16, the 32x32 result rows
@@ -46,6 +51,22 @@ __device__ __forceinline__ uint2 ldx(const uint2* p) {
         return *p;
     }
 }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldx(const uint4* p) {
+    if constexpr ((GSPN_PROJ_NT & 1) != 0) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+__device__ __forceinline__ void stx(uint4* p, uint4 v) {
+    if constexpr ((GSPN_PROJ_NT & 2) != 0) {
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+    } else {
+        *p = v;
+    }
+}
 __device__ __forceinline__ void stx(uint2* p, uint2 v) {
     if constexpr ((GSPN_PROJ_NT & 2) != 0) {
         __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
@@ -65,35 +86,59 @@ __device__ __forceinline__ __bf16 as_bf(uint32_t bits16) {
     return __builtin_bit_cast(__bf16, static_cast<uint16_t>(bits16));
 }
 
-// Narrow output: c_out <= 16.  Requires hw % 64 == 0, c_in % 8 == 0, 8-byte
-// aligned rows and a 16-byte aligned weight matrix.  Each 32-channel block's
-// loads are issued before the previous block's MFMAs (double buffer); channel
-// indices past c_in are clamped into the tensor and their values replaced by
-// zeros, so no load sits behind a branch.
+// Narrow output: c_out <= 16.  Requires hw % (16 * PX) == 0, c_in % 8 == 0,
+// 2 * PX-byte aligned rows and a 16-byte aligned weight matrix.  A wave
+// covers 16 * PX pixels, each lane PX consecutive pixels of 8 channels, so 16
+// lanes read one run of 32 * PX bytes of a channel row.  Each 32-channel
+// block's loads are issued before the previous block's MFMAs (double buffer);
+// channel indices past c_in are clamped into the tensor and their values
+// replaced by zeros, so no load sits behind a branch.
 #ifndef GSPN_PROJ_THREADS
-#define GSPN_PROJ_THREADS 512
+#define GSPN_PROJ_THREADS 256
+#endif
+#ifndef GSPN_PROJ_PX
+#define GSPN_PROJ_PX 8
 #endif
 
+template <int PX>
+struct PixVec;
+template <>
+struct PixVec<4> {
+    using T = uint2;
+    static __device__ __forceinline__ uint32_t word(const T& v, int k) { return k == 0 ? v.x : v.y; }
+};
+template <>
+struct PixVec<8> {
+    using T = uint4;
+    static __device__ __forceinline__ uint32_t word(const T& v, int k) {
+        return k == 0 ? v.x : (k == 1 ? v.y : (k == 2 ? v.z : v.w));
+    }
+};
+
+template <int PX>
 __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(const bf16_t* __restrict__ in,
-                                                               const bf16_t* __restrict__ wt,
-                                                               bf16_t* __restrict__ out, int64_t waves,
-                                                               int64_t hw, int cin, int cout) {
+                                                                              const bf16_t* __restrict__ wt,
+                                                                              bf16_t* __restrict__ out, int64_t waves,
+                                                                              int64_t hw, int cin, int cout) {
+    using PV = PixVec<PX>;
+    using VT = typename PV::T;
+    constexpr int WPX = 16 * PX;  // pixels per wave
     const int lane = threadIdx.x & 63;
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (wave >= waves) return;
-    const int64_t per_img = hw / 64;
+    const int64_t per_img = hw / WPX;
     const int64_t ni = wave / per_img;
-    const int64_t px0 = (wave - ni * per_img) * 64;
-    const int q = lane & 15;  // pixel quad: pixels px0 + 4q .. +3; output row of A
+    const int64_t px0 = (wave - ni * per_img) * WPX;
+    const int q = lane & 15;  // pixel group: pixels px0 + PX q .. + PX - 1; output row of A
     const int g = lane >> 4;  // k-group: channels 8g .. 8g+7 of each 32-channel step
-    const bf16_t* src = in + ni * cin * hw + px0 + 4 * q;
+    const bf16_t* src = in + ni * cin * hw + px0 + PX * q;
     const bf16_t* wrow = wt + static_cast<int64_t>(q < cout ? q : cout - 1) * cin;
     const bool qok = q < cout;
 
     struct Block {
-        uint4 a;     // 8 weights (bf16) of output row q
-        uint2 v[8];  // 4 pixels of 8 channels
-        bool ok;     // the channels exist
+        uint4 a;   // 8 weights (bf16) of output row q
+        VT v[8];   // PX pixels of 8 channels
+        bool ok;   // the channels exist
     };
     auto fetch = [&](int k0, Block& b) {
         const int c0 = k0 + 8 * g;
@@ -101,12 +146,12 @@ __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(con
         const int cc = b.ok ? c0 : cin - 8;  // clamped into the tensor (cin % 8 == 0)
         b.a = *reinterpret_cast<const uint4*>(wrow + cc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b.v[e] = ldx(reinterpret_cast<const uint2*>(src + static_cast<int64_t>(cc + e) * hw));
+        for (int e = 0; e < 8; ++e) b.v[e] = ldx(reinterpret_cast<const VT*>(src + static_cast<int64_t>(cc + e) * hw));
     };
 
-    floatx4 acc[4];
+    floatx4 acc[PX];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < PX; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     auto consume = [&](const Block& b) {
         const bool use = b.ok && qok;
         const uint32_t aw[4] = {use ? b.a.x : 0u, use ? b.a.y : 0u, use ? b.a.z : 0u, use ? b.a.w : 0u};
@@ -114,11 +159,11 @@ __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(con
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] = as_bf((e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xffffu));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < PX; ++j) {
             bf16x8 bv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t word = b.ok ? ((j < 2) ? b.v[e].x : b.v[e].y) : 0u;
+                const uint32_t word = b.ok ? PV::word(b.v[e], j >> 1) : 0u;
                 bv[e] = as_bf((j & 1) ? (word >> 16) : (word & 0xffffu));
             }
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[j], 0, 0, 0);
@@ -136,45 +181,70 @@ __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(con
     }
     if (k0 < cin) consume(b0);
 
-    // lane holds output rows (l/16)*4 + i for pixels px0 + 4q + j
-    bf16_t* dst = out + ni * cout * hw + px0 + 4 * q;
+    // lane holds output rows (l/16)*4 + i for pixels px0 + PX q + j
+    bf16_t* dst = out + ni * cout * hw + px0 + PX * q;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int o = g * 4 + i;
         if (o < cout) {
-            uint2 w;
-            w.x = static_cast<uint32_t>(f32_to_bf16(acc[0][i])) | (static_cast<uint32_t>(f32_to_bf16(acc[1][i])) << 16);
-            w.y = static_cast<uint32_t>(f32_to_bf16(acc[2][i])) | (static_cast<uint32_t>(f32_to_bf16(acc[3][i])) << 16);
-            stx(reinterpret_cast<uint2*>(dst + static_cast<int64_t>(o) * hw), w);
+            uint32_t w[PX / 2];
+#pragma unroll
+            for (int k = 0; k < PX / 2; ++k) w[k] = pack_bf16x2(acc[2 * k][i], acc[2 * k + 1][i]);
+            bf16_t* d = dst + static_cast<int64_t>(o) * hw;
+            if constexpr (PX == 4) {
+                stx(reinterpret_cast<uint2*>(d), make_uint2(w[0], w[1]));
+            } else {
+                stx(reinterpret_cast<uint4*>(d), make_uint4(w[0], w[1], w[2], w[3]));
+            }
         }
     }
 }
 
-// Narrow input: c_in <= 8.  Requires hw % 64 == 0 and 4-byte aligned rows.
+// Narrow input: c_in <= 8.  Requires hw % (32 * PQ) == 0 and 2 * PQ-byte
+// aligned rows.  A wave covers 32 * PQ pixels: lane n holds PQ consecutive
+// pixels, one MFMA per pixel of its group, so each lane stores PQ adjacent
+// pixels of an output row at once (32 lanes make one run of 64 * PQ bytes).
+#ifndef GSPN_PROJ_PQ
+#define GSPN_PROJ_PQ 4
+#endif
+
+template <int PQ>
 __global__ __launch_bounds__(256) void project_narrow_in_mfma(const bf16_t* __restrict__ in,
                                                               const bf16_t* __restrict__ wt,
                                                               bf16_t* __restrict__ out, int64_t waves,
                                                               int64_t hw, int cin, int cout) {
+    static_assert(PQ == 2 || PQ == 4, "2 or 4 pixels per lane");
+    constexpr int WPX = 32 * PQ;  // pixels per wave
     const int lane = threadIdx.x & 63;
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (wave >= waves) return;
-    const int64_t per_img = hw / 64;
+    const int64_t per_img = hw / WPX;
     const int64_t ni = wave / per_img;
-    const int64_t px0 = (wave - ni * per_img) * 64;
-    const int n = lane & 31;  // pixel pair: pixels px0 + 2n, px0 + 2n + 1; output row of A
+    const int64_t px0 = (wave - ni * per_img) * WPX;
+    const int n = lane & 31;  // pixel group: pixels px0 + PQ n .. + PQ - 1; output row of A
     const int g = lane >> 5;  // k-group: input channels 4g .. 4g+3
-    const bf16_t* src = in + ni * cin * hw + px0 + 2 * n;
+    const bf16_t* src = in + ni * cin * hw + px0 + PQ * n;
 
-    short4v b_even, b_odd;
+    short4v b[PQ];  // B operand of each pixel of the group
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int c = 4 * g + e;
-        const uint32_t raw = *reinterpret_cast<const uint32_t*>(src + static_cast<int64_t>(c < cin ? c : cin - 1) * hw);
-        const uint32_t word = c < cin ? raw : 0u;
-        b_even[e] = static_cast<short>(word & 0xffffu);
-        b_odd[e] = static_cast<short>(word >> 16);
+        const bf16_t* row = src + static_cast<int64_t>(c < cin ? c : cin - 1) * hw;
+        uint32_t words[PQ / 2];
+        if constexpr (PQ == 2) {
+            words[0] = *reinterpret_cast<const uint32_t*>(row);
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(row);
+            words[0] = v.x;
+            words[1] = v.y;
+        }
+#pragma unroll
+        for (int k = 0; k < PQ; ++k) {
+            const uint32_t word = c < cin ? words[k >> 1] : 0u;
+            b[k][e] = static_cast<short>((k & 1) ? (word >> 16) : (word & 0xffffu));
+        }
     }
-    bf16_t* dst = out + ni * cout * hw + px0 + 2 * n;
+    bf16_t* dst = out + ni * cout * hw + px0 + PQ * n;
     for (int o0 = 0; o0 < cout; o0 += 32) {
         short4v a;
         const int orow = o0 + n;
@@ -185,17 +255,21 @@ __global__ __launch_bounds__(256) void project_narrow_in_mfma(const bf16_t* __re
             const bf16_t v = wt[oc * cin + (c < cin ? c : cin - 1)];
             a[e] = static_cast<short>((orow < cout && c < cin) ? v : 0);
         }
-        floatx16 ce = {}, co = {};
-        ce = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b_even, ce, 0, 0, 0);
-        co = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b_odd, co, 0, 0, 0);
-        // lane holds output rows (i/4)*8 + (l/32)*4 + i%4 for the pixel pair
+        floatx16 acc[PQ];
+#pragma unroll
+        for (int k = 0; k < PQ; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b[k], floatx16{}, 0, 0, 0);
+        // lane holds output rows (i/4)*8 + (l/32)*4 + i%4 for its pixel group
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int o = o0 + (i / 4) * 8 + g * 4 + (i % 4);
             if (o < cout) {
-                const uint32_t word = static_cast<uint32_t>(f32_to_bf16(ce[i])) |
-                                      (static_cast<uint32_t>(f32_to_bf16(co[i])) << 16);
-                stx(reinterpret_cast<uint32_t*>(dst + static_cast<int64_t>(o) * hw), word);
+                bf16_t* d = dst + static_cast<int64_t>(o) * hw;
+                if constexpr (PQ == 2) {
+                    stx(reinterpret_cast<uint32_t*>(d), pack_bf16x2(acc[0][i], acc[1][i]));
+                } else {
+                    stx(reinterpret_cast<uint2*>(d), make_uint2(pack_bf16x2(acc[0][i], acc[1][i]),
+                                                                pack_bf16x2(acc[2][i], acc[3][i])));
+                }
             }
         }
     }
@@ -243,17 +317,36 @@ hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, co
     if (dtype == kBF16 && hw % 64 == 0 && c_in <= 1 << 20 && c_out <= 1 << 20) {
         const int64_t waves = n * (hw / 64);
         const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+        constexpr int PX = GSPN_PROJ_PX;
+        if (c_out <= 16 && c_in % 8 == 0 && hw % (16 * PX) == 0 && aligned_to(in, 2 * PX) &&
+            aligned_to(out, 2 * PX) && aligned_to(weight, 16)) {
+            constexpr int per = GSPN_PROJ_THREADS / 64;
+            const int64_t w2 = n * (hw / (16 * PX));
+            const dim3 g2(static_cast<unsigned>((w2 + per - 1) / per));
+            hipLaunchKernelGGL(project_narrow_out_mfma<PX>, g2, dim3(GSPN_PROJ_THREADS), 0, stream,
+                               static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
+                               static_cast<bf16_t*>(out), w2, hw, static_cast<int>(c_in), static_cast<int>(c_out));
+            return hipGetLastError();
+        }
         if (c_out <= 16 && c_in % 8 == 0 && aligned_to(in, 8) && aligned_to(out, 8) && aligned_to(weight, 16)) {
             constexpr int per = GSPN_PROJ_THREADS / 64;
             const dim3 g2(static_cast<unsigned>((waves + per - 1) / per));
-            hipLaunchKernelGGL(project_narrow_out_mfma, g2, dim3(GSPN_PROJ_THREADS), 0, stream,
+            hipLaunchKernelGGL(project_narrow_out_mfma<4>, g2, dim3(GSPN_PROJ_THREADS), 0, stream,
                                static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
                                static_cast<bf16_t*>(out), waves, hw, static_cast<int>(c_in),
                                static_cast<int>(c_out));
             return hipGetLastError();
         }
+        constexpr int PQ = GSPN_PROJ_PQ;
+        if (c_in <= 8 && hw % (32 * PQ) == 0 && aligned_to(in, 2 * PQ) && aligned_to(out, 2 * PQ)) {
+            const int64_t w2 = n * (hw / (32 * PQ));
+            hipLaunchKernelGGL(project_narrow_in_mfma<PQ>, dim3(static_cast<unsigned>((w2 + 3) / 4)), dim3(256), 0,
+                               stream, static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
+                               static_cast<bf16_t*>(out), w2, hw, static_cast<int>(c_in), static_cast<int>(c_out));
+            return hipGetLastError();
+        }
         if (c_in <= 8 && aligned_to(in, 4) && aligned_to(out, 4)) {
-            hipLaunchKernelGGL(project_narrow_in_mfma, grid, dim3(256), 0, stream,
+            hipLaunchKernelGGL(project_narrow_in_mfma<2>, grid, dim3(256), 0, stream,
                                static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
                                static_cast<bf16_t*>(out), waves, hw, static_cast<int>(c_in),
                                static_cast<int>(c_out));

@@ -135,7 +135,7 @@ def test_merge4():
     assert np.max(np.abs(_np(y) - ref)) <= 1e-5
 
 
-@pytest.mark.parametrize("hw", [(13, 29), (16, 32)])   # ragged (VALU) / multiple of 64 pixels (MFMA for bf16)
+@pytest.mark.parametrize("hw", [(13, 29), (16, 32), (8, 24)])   # ragged (VALU) / 128 or 64 pixels per wave (MFMA, bf16)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("cin,cout", [(320, 8), (8, 320), (37, 5), (3, 11), (40, 16), (64, 17), (5, 33)])
 def test_project(cin, cout, dtype, hw):
