@@ -160,14 +160,35 @@ def stage_times(wl, inp, out, ws, reps: int, merge=None) -> dict:
     return acc, kernel
 
 
-def kernel_sources_digest() -> str:
-    """sha256 over the library's kernel and launch sources (sorted by name)."""
+# The sources each measured kernel is built from: its own file, the headers
+# it includes, the launch code that configures it and the build flags.
+_SCAN4 = ["scan_kernel.hpp", "scan_lp.hpp", "scan_band.hpp", "scan.hip", "scan4_f32.hip", "scan4_bf16.hip",
+          "scan4_bf16pair.hip"]
+KERNEL_SOURCES = {
+    "scan4lp_kernel": _SCAN4,
+    "scan4band_kernel": _SCAN4,
+    "scan4v_kernel": _SCAN4,
+    "plane4_kernel": ["plane4.hip"],
+    "adj4_kernel": ["backward.hip"],
+}
+_COMMON = ["device.hpp", "launch.hpp"]
+
+
+def kernel_sources_digest(kernel: str | None = None) -> str:
+    """sha256 over the sources of one kernel (KERNEL_SOURCES, plus the shared
+    device helpers, the launch declarations and build.py), or over every
+    kernel source of the library for an unlisted kernel."""
+    if kernel in KERNEL_SOURCES:
+        names = sorted(set(KERNEL_SOURCES[kernel] + _COMMON))
+    else:
+        names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".hpp", ".cpp", ".h")))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(os.path.dirname(CSRC), "build.py"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()
 
 
@@ -183,7 +204,7 @@ def counter_traffic(kernel: str, wl) -> tuple:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != kernel_sources_digest():
+    if fields.get("source_sha256") != kernel_sources_digest(kernel):
         return None, "kernel sources changed since the counters were taken"
     try:
         return int(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)

@@ -51,19 +51,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
-// AUX: cache-policy bits (2: non-temporal, for data read once).
-template <typename E, int AUX>
+// Default cache policy: the per-step rows are not 128-byte aligned, so
+// consecutive steps share cache lines (with the non-temporal hint the
+// logits and lambda streams fetched 20% more bytes, and ran no faster).
+template <typename E>
 __device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     if constexpr (sizeof(E) == 4) {
-        return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+        return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
     } else {
-        return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX));
+        return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
     }
 }
-
-#ifndef GSPN_PLANE_STREAM_AUX
-#define GSPN_PLANE_STREAM_AUX 2
-#endif
 
 template <typename E>
 __device__ __forceinline__ float widen(uint32_t raw) {
@@ -136,9 +134,7 @@ __device__ __forceinline__ void store_plane(T* yg, int64_t hw, int W, int ld, co
 // the vertical directions and (k, i) for the horizontal ones.  The first
 // kDepth steps' logits and lambdas are requested before x reaches LDS, so
 // their latency overlaps the plane load.
-// ZNT: the logits are read by this plane only (per-channel), so they stream
-// past the caches like lambda; shared logits are re-read by every channel.
-template <typename T, bool HORIZ, bool REV, bool ZNT>
+template <typename T, bool HORIZ, bool REV>
 __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t p, const float* xs, float* part,
                                                 int ld, const T* xg, int64_t hw) {
     const int lane = threadIdx.x & 63;
@@ -165,11 +161,10 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
     auto fill = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
         const uint32_t o = static_cast<uint32_t>(line_of(min(t, S - 1))) * row;
-        constexpr int ZA = ZNT ? GSPN_PLANE_STREAM_AUX : 0;
-        rz0[s] = load_raw<T, ZA>(rz, vk, o);
-        rz1[s] = load_raw<T, ZA>(rz, vk, o + pz);
-        rz2[s] = load_raw<T, ZA>(rz, vk, o + 2 * pz);
-        rlam[s] = load_raw<T, GSPN_PLANE_STREAM_AUX>(rl, vk, o);
+        rz0[s] = load_raw<T>(rz, vk, o);
+        rz1[s] = load_raw<T>(rz, vk, o + pz);
+        rz2[s] = load_raw<T>(rz, vk, o + 2 * pz);
+        rlam[s] = load_raw<T>(rl, vk, o);
     };
 
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
@@ -212,7 +207,7 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
     }(std::make_integer_sequence<int, kDepth - 1>{});
 }
 
-template <typename T, bool ZNT>
+template <typename T>
 __global__ __launch_bounds__(256) void plane4_kernel(const Plane4K a) {
     extern __shared__ float lds[];
     const int H = a.H;
@@ -229,10 +224,10 @@ __global__ __launch_bounds__(256) void plane4_kernel(const Plane4K a) {
         ph[e] = 0.0f;
     }
     switch (threadIdx.x >> 6) {
-        case 0: plane_direction<T, false, false, ZNT>(a, 0, p, xs, pv, ld, xp, hw); break;
-        case 1: plane_direction<T, false, true, ZNT>(a, 1, p, xs, pv, ld, xp, hw); break;
-        case 2: plane_direction<T, true, false, ZNT>(a, 2, p, xs, ph, ld, xp, hw); break;
-        default: plane_direction<T, true, true, ZNT>(a, 3, p, xs, ph, ld, xp, hw); break;
+        case 0: plane_direction<T, false, false>(a, 0, p, xs, pv, ld, xp, hw); break;
+        case 1: plane_direction<T, false, true>(a, 1, p, xs, pv, ld, xp, hw); break;
+        case 2: plane_direction<T, true, false>(a, 2, p, xs, ph, ld, xp, hw); break;
+        default: plane_direction<T, true, true>(a, 3, p, xs, ph, ld, xp, hw); break;
     }
     __syncthreads();
     T* yp = static_cast<T*>(a.y) + p * hw;
@@ -261,13 +256,10 @@ hipError_t launch_plane4(const void* x, const void* const logits[4], const void*
     k.W = static_cast<int>(w);
     const size_t lds = 3 * sizeof(float) * static_cast<size_t>(h) * static_cast<size_t>(w + 1);
     const dim3 grid(static_cast<unsigned>(n * c));
-    const bool own = cw == c || c == 1;  // each plane reads its own logits
     if (dtype == kF32) {
-        if (own) hipLaunchKernelGGL((plane4_kernel<float, true>), grid, dim3(256), lds, stream, k);
-        else hipLaunchKernelGGL((plane4_kernel<float, false>), grid, dim3(256), lds, stream, k);
+        hipLaunchKernelGGL(plane4_kernel<float>, grid, dim3(256), lds, stream, k);
     } else {
-        if (own) hipLaunchKernelGGL((plane4_kernel<bf16_t, true>), grid, dim3(256), lds, stream, k);
-        else hipLaunchKernelGGL((plane4_kernel<bf16_t, false>), grid, dim3(256), lds, stream, k);
+        hipLaunchKernelGGL(plane4_kernel<bf16_t>, grid, dim3(256), lds, stream, k);
     }
     return hipGetLastError();
 }
