@@ -22,7 +22,8 @@
 // reading the forward states h recomputed beforehand into separate maps.  The
 // per-step inputs of the next D steps are in flight (ring slots refilled as
 // soon as read, compile-time slot indices, addresses clamped instead of
-// guarded).  Streams touched once carry the non-temporal hint.
+// guarded).  Streams touched once carry the non-temporal hint when the
+// lines are whole cache lines.
 #include <utility>
 
 #include "device.hpp"
@@ -40,7 +41,9 @@ template <int P, int G>
 constexpr int adj_depth() { return (P == 1 && G == 1) ? 4 : 2; }
 
 // channels per workgroup for channel-shared logits (fewer for two positions
-// per lane: register budget)
+// per lane: register budget; with the learnable merge's extra state the
+// four-channel groups spill a few registers, and still measured faster than
+// groups of two)
 template <int P>
 constexpr int shared_group() { return P == 1 ? 4 : 2; }
 
@@ -75,12 +78,28 @@ struct Adj4K {
 // position are normalised once for all of them, and the logit gradient, which
 // sums over channels, is accumulated over the G channels in registers before
 // it leaves the workgroup (one atomic add per logit and G channels).
-// With a learnable merge weight m for (direction, channel), the direction's
-// output enters y as m h, so its adjoint input is m g: the adjoint a runs on
-// g itself and every gradient it feeds is scaled by m, while
+// MERGE: learnable merge weights or their gradient are in play.  With a
+// merge weight m for (direction, channel), the direction's output enters y as
+// m h, so its adjoint input is m g: the adjoint a runs on g itself and every
+// gradient it feeds is scaled by m, while
 // dL/dm = sum_t <g_t, h_t> = sum_t <a_t, lambda_t x_t> (the adjoint identity
-// of the linear recurrence, per chunk) is summed on the way.
-template <typename T, int P, int G>
+// of the linear recurrence, per chunk) is summed on the way.  Without MERGE
+// none of this costs registers.
+// NT: the streams touched once carry the non-temporal hint; only for lines
+// of whole 128-byte cache lines (for shorter, unaligned rows the hint makes
+// consecutive steps fetch their shared lines twice).
+template <typename T, bool NT>
+__device__ __forceinline__ float ld_once(const T* p) {
+    if constexpr (NT) return ld_stream(p);
+    else return Store<T>::ld(p);
+}
+template <typename T, bool NT>
+__device__ __forceinline__ void st_once(T* p, float v) {
+    if constexpr (NT) st_stream(p, v);
+    else Store<T>::st(p, v);
+}
+
+template <typename T, int P, int G, bool MERGE, bool NT>
 __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float* edge_raw) {
     constexpr int D = adj_depth<P, G>();
     const int tid = threadIdx.x;
@@ -94,13 +113,13 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     const int64_t p0 = nidx * a.c + c0;           // its plane
     int gc[G];                                    // channel offset of each member, clamped
     bool gok[G];
-    float msc[G];                                 // merge weight of each member
-    float dm[G];                                  // this lane's share of dL/dm
+    float msc[G];                                 // merge weight of each member (MERGE)
+    float dm[G];                                  // this lane's share of dL/dm (MERGE)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         gok[g] = c0 + g < a.c;
         gc[g] = gok[g] ? g : 0;
-        msc[g] = a.mscale ? a.mscale[c0 + gc[g]] : 1.0f;
+        msc[g] = (MERGE && a.mscale) ? a.mscale[c0 + gc[g]] : 1.0f;
         dm[g] = 0.0f;
     }
     const T* xp = static_cast<const T*>(a.x) + p0 * plane;
@@ -145,7 +164,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
 #pragma unroll
             for (int o = 0; o < 3; ++o) {
                 // per-channel logits are read once; a channel group's shared logits are re-read
-                rz[s][o][j] = G == 1 ? ld_stream(zp + o * plane + lo + kk[j]) : Store<T>::ld(zp + o * plane + lo + kk[j]);
+                rz[s][o][j] = G == 1 ? ld_once<T, NT>(zp + o * plane + lo + kk[j]) : Store<T>::ld(zp + o * plane + lo + kk[j]);
             }
         }
 #pragma unroll
@@ -153,9 +172,9 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
             const int64_t go = gc[g] * plane;
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                rg[s][g][j] = ld_stream(gp + go + lo + kk[j]);
+                rg[s][g][j] = ld_once<T, NT>(gp + go + lo + kk[j]);
                 rx[s][g][j] = Store<T>::ld(xp + go + lo + kk[j]);
-                rl[s][g][j] = ld_stream(lp + go + lo + kk[j]);
+                rl[s][g][j] = ld_once<T, NT>(lp + go + lo + kk[j]);
                 rh[s][g][j + 1] = hp[go + hlo + kk[j]];
             }
             rh[s][g][0] = hp[go + hlo + kl];
@@ -219,11 +238,14 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
             const int64_t go = gc[g] * plane;
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                const float am = a_t[j] * msc[g];  // the adjoint of the merged output
-                dm[g] = __builtin_fmaf(a_t[j], rl[s][g][j] * rx[s][g][j], dm[g]);
+                float am = a_t[j];
+                if constexpr (MERGE) {
+                    am = a_t[j] * msc[g];  // the adjoint of the merged output
+                    dm[g] = __builtin_fmaf(a_t[j], rl[s][g][j] * rx[s][g][j], dm[g]);
+                }
                 if (kin[j] && gok[g]) {
-                    st_stream(dlp + go + lo + k0 + j, am * rx[s][g][j]);
-                    st_stream(dxp + go + lo + k0 + j, am * rl[s][g][j]);
+                    st_once<T, NT>(dlp + go + lo + k0 + j, am * rx[s][g][j]);
+                    st_once<T, NT>(dxp + go + lo + k0 + j, am * rl[s][g][j]);
                 }
 #pragma unroll
                 for (int o = 0; o < 3; ++o) dw[j][o] += am * rh[s][g][j + o];  // h_{t-1}[k+o-1]
@@ -252,7 +274,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 } else {
                     T* dzp = static_cast<T*>(a.dz) + zplane;
 #pragma unroll
-                    for (int o = 0; o < 3; ++o) st_stream(dzp + o * plane + lo + k0 + j, dz[o]);
+                    for (int o = 0; o < 3; ++o) st_once<T, NT>(dzp + o * plane + lo + k0 + j, dz[o]);
                 }
             }
         }
@@ -280,7 +302,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
         ((t - Ss >= t0 ? step(IC<(Ss + 1) % D>{}, IC<0>{}, t - Ss) : void()), ...);
     }(std::make_integer_sequence<int, D - 1>{});
 
-    if (a.dmerge) {
+    if (MERGE && a.dmerge) {
         // sum over the wave, one atomic add per wave and member
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -292,7 +314,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     }
 }
 
-template <typename T, int P, int G>
+template <typename T, int P, int G, bool MERGE, bool NT>
 __global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
     extern __shared__ float s_edge_raw[];
     int dir = 0;
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
     const AdjK& k = a.d[dir];
     const int64_t pg = idx / k.nchunks;
     const int q = static_cast<int>(idx - pg * k.nchunks);
-    adj_line<T, P, G>(k, pg, q, s_edge_raw);
+    adj_line<T, P, G, MERGE, NT>(k, pg, q, s_edge_raw);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -334,9 +356,13 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
     int maxL = 1;
     int64_t total = 0;
     const bool shared = p[0].shared != 0;
-    int maxL0 = 1;
-    for (int d = 0; d < 4; ++d) maxL0 = p[d].L > maxL0 ? static_cast<int>(p[d].L) : maxL0;
-    const int G = shared ? (maxL0 <= 1024 ? shared_group<1>() : shared_group<2>()) : 1;
+    bool merge = false;
+    for (int d = 0; d < 4; ++d) {
+        maxL = p[d].L > maxL ? static_cast<int>(p[d].L) : maxL;
+        merge = merge || p[d].mscale || p[d].dmerge;
+    }
+    const int P = maxL <= 1024 ? 1 : 2;  // lines of at most 2048 positions
+    const int G = !shared ? 1 : (P == 1 ? shared_group<1>() : shared_group<2>());
     for (int d = 0; d < 4; ++d) {
         AdjK& a = k.d[d];
         a.x = p[d].x;
@@ -359,25 +385,37 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
         a.dmerge = p[d].dmerge;
         k.blocks[d] = p[d].n * ((p[d].c + G - 1) / G) * a.nchunks;
         total += k.blocks[d];
-        maxL = a.L > maxL ? a.L : maxL;
     }
-    const int P = maxL <= 1024 ? 1 : 2;  // lines of at most 2048 positions
     const int lanes = ((maxL + P - 1) / P + 63) / 64 * 64;
     const size_t lds = 4 * sizeof(float) * static_cast<size_t>(G) * static_cast<size_t>(lanes);
     const dim3 grid(static_cast<unsigned>(total));
     const bool f32 = p[0].dtype == kF32;
-#define GSPN_ADJ_LAUNCH(PP, GG)                                                                                    \
+    // non-temporal streams only when every line is a whole number of cache lines
+    bool nt = true;
+    for (int d = 0; d < 4; ++d) nt = nt && (p[d].L * (f32 ? 4 : 2)) % 128 == 0;
+#define GSPN_ADJ_LAUNCH(PP, GG, MM)                                                                               \
     do {                                                                                                          \
-        if (f32) hipLaunchKernelGGL((adj4_kernel<float, PP, GG>), grid, dim3(lanes), lds, stream, k);            \
-        else hipLaunchKernelGGL((adj4_kernel<bf16_t, PP, GG>), grid, dim3(lanes), lds, stream, k);               \
+        if (f32) {                                                                                                \
+            if (nt) hipLaunchKernelGGL((adj4_kernel<float, PP, GG, MM, true>), grid, dim3(lanes), lds, stream, k);  \
+            else hipLaunchKernelGGL((adj4_kernel<float, PP, GG, MM, false>), grid, dim3(lanes), lds, stream, k);    \
+        } else {                                                                                                  \
+            if (nt) hipLaunchKernelGGL((adj4_kernel<bf16_t, PP, GG, MM, true>), grid, dim3(lanes), lds, stream, k); \
+            else hipLaunchKernelGGL((adj4_kernel<bf16_t, PP, GG, MM, false>), grid, dim3(lanes), lds, stream, k);   \
+        }                                                                                                         \
+    } while (0)
+#define GSPN_ADJ_LAUNCH_P(PP, MM)                                                                                 \
+    do {                                                                                                          \
+        if (shared) GSPN_ADJ_LAUNCH(PP, shared_group<PP>(), MM);                                                  \
+        else GSPN_ADJ_LAUNCH(PP, 1, MM);                                                                          \
     } while (0)
     if (P == 1) {
-        if (shared) GSPN_ADJ_LAUNCH(1, shared_group<1>());
-        else GSPN_ADJ_LAUNCH(1, 1);
+        if (merge) GSPN_ADJ_LAUNCH_P(1, true);
+        else GSPN_ADJ_LAUNCH_P(1, false);
     } else {
-        if (shared) GSPN_ADJ_LAUNCH(2, shared_group<2>());
-        else GSPN_ADJ_LAUNCH(2, 1);
+        if (merge) GSPN_ADJ_LAUNCH_P(2, true);
+        else GSPN_ADJ_LAUNCH_P(2, false);
     }
+#undef GSPN_ADJ_LAUNCH_P
 #undef GSPN_ADJ_LAUNCH
     return hipGetLastError();
 }
