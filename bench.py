@@ -162,11 +162,10 @@ def stage_times(wl, inp, out, ws, reps: int, merge=None) -> dict:
 
 # The sources each measured kernel is built from: its own file, the headers
 # it includes, the launch code that configures it and the build flags.
-_SCAN4 = ["scan_kernel.hpp", "scan_lp.hpp", "scan_band.hpp", "scan.hip", "scan4_f32.hip", "scan4_bf16.hip",
-          "scan4_bf16pair.hip"]
+_SCAN4 = ["scan_kernel.hpp", "scan_lp.hpp", "scan.hip", "scan4_f32.hip", "scan4_bf16.hip", "scan4_bf16pair.hip"]
 KERNEL_SOURCES = {
     "scan4lp_kernel": _SCAN4,
-    "scan4band_kernel": _SCAN4,
+    "scan4band_kernel": _SCAN4 + ["scan_band.hpp"],
     "scan4v_kernel": _SCAN4,
     "plane4_kernel": ["plane4.hip"],
     "adj4_kernel": ["backward.hip"],

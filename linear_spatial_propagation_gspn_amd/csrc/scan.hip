@@ -220,6 +220,10 @@ hipError_t launch_scan4_band(const ScanParams (&p)[4], float* state, int index, 
         lmax = b.d[d].L > lmax ? b.d[d].L : lmax;
     }
     b.sstride = planes * lmax;
+    b.planes = planes;
+    b.xcd_lines = (planes * 4) % 8 == 0;
+    for (int d = 0; d < 4; ++d)
+        b.xcd_lines = b.xcd_lines && b.blocks[d] > 0 && b.nseg[d] == b.nseg[0];
     b.hin = state + (index & 1) * 4 * b.sstride;
     b.hout = state + ((index + 1) & 1) * 4 * b.sstride;
     if (p[0].dtype == kF32) {

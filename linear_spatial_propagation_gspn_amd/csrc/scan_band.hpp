@@ -43,6 +43,8 @@ struct BandK {
     int t0;             // first scan step of the band
     int seg;            // positions per segment (a multiple of the lane width P)
     int halo;           // steps per band = positions of halo on each side (a multiple of P)
+    int64_t planes;     // planes per direction
+    int xcd_lines;      // 1: the segments of a line share an XCD (see scan4band_kernel)
 };
 
 template <typename T, typename TW, bool LOGITS>
@@ -194,16 +196,32 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
     }
 }
 
+// Block b runs on XCD b % 8 (round-robin dispatch).  With xcd_lines, the
+// segments of one line all go to the same XCD, so a segment's halo rows,
+// which its neighbours read in the same steps, come from that XCD's L2
+// (every direction active, equal segment counts, lines a multiple of 8).
 template <typename T, typename TW, bool LOGITS>
 __global__ __launch_bounds__(64) void scan4band_kernel(const BandK b) {
     int dir = 0;
-    int64_t idx = blockIdx.x;
-    while (dir < 3 && idx >= b.blocks[dir]) {
-        idx -= b.blocks[dir];
-        ++dir;
+    int64_t p;
+    int g;
+    if (b.xcd_lines) {
+        const int64_t x = blockIdx.x % 8;
+        const int64_t k = blockIdx.x / 8;
+        const int nseg = b.nseg[0];
+        const int64_t line = x + 8 * (k / nseg);  // dir * planes + plane
+        g = static_cast<int>(k % nseg);
+        dir = static_cast<int>(line / b.planes);
+        p = line - dir * b.planes;
+    } else {
+        int64_t idx = blockIdx.x;
+        while (dir < 3 && idx >= b.blocks[dir]) {
+            idx -= b.blocks[dir];
+            ++dir;
+        }
+        p = idx / b.nseg[dir];
+        g = static_cast<int>(idx - p * b.nseg[dir]);
     }
-    const int64_t p = idx / b.nseg[dir];
-    const int g = static_cast<int>(idx - p * b.nseg[dir]);
     band_segment<T, TW, LOGITS>(b, dir, p, g);
 }
 
