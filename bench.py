@@ -412,6 +412,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "backward"),
                     help="time the forward (default) or the backward (gradients for a seeded dL/dy)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (forward only)")
     ap.add_argument("--merge", action="store_true",
                     help="merge the directions with seeded learnable weights per direction and channel")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
@@ -442,6 +444,24 @@ def main():
     for _ in range(args.warmup):
         run_step(wl, inp, out, ws, merge=merge)
     torch.cuda.synchronize()
+    step = lambda: run_step(wl, inp, out, ws, merge=merge)
+    if args.graph:
+        # the library allocates nothing and launches only kernels on the
+        # current stream, so one step captures whole; its replays are timed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_step(wl, inp, out, ws, merge=merge)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step(wl, inp, out, ws, merge=merge)
+        torch.cuda.synchronize()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
@@ -450,7 +470,7 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        run_step(wl, inp, out, ws, merge=merge)
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -490,7 +510,8 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": wl.name, "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
-                   "c_proxy": wl.c_proxy, "merge": "learnable" if args.merge else "sum"},
+                   "c_proxy": wl.c_proxy, "merge": "learnable" if args.merge else "sum",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "effective_GBps": round(eff, 1),
         "effective_frac": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": alg,
