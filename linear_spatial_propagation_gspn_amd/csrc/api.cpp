@@ -322,6 +322,35 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
 
 namespace {
 
+// Channel-shared logits of the four directions normalised once into dst
+// (direction d at dst + d * wdir): fp32 triples for fp32 storage, one
+// launch per direction; packed half pairs for bf16, one launch for all four.
+// Points the scans p[d] at them.
+hipError_t prenormalise(int64_t n, int64_t h, int64_t w, const void* const logits[4], char* dst, int64_t wdir,
+                        int dtype, hipStream_t st, Timer* tm, gspn::ScanParams (&p)[4]) {
+    void* wd[4];
+    for (int d = 0; d < 4; ++d) wd[d] = dst + d * wdir;
+    if (dtype == GSPN_F32) {
+        for (int d = 0; d < 4; ++d) {
+            const hipError_t e = timed(tm, GSPN_STAGE_NORMALIZE, [&] {
+                return gspn::launch_normalize(d, n, 1, h, w, logits[d], wd[d], dtype, st, GSPN_F32);
+            });
+            if (e != hipSuccess) return e;
+        }
+    } else {
+        const hipError_t e = timed(tm, GSPN_STAGE_NORMALIZE, [&] {
+            return gspn::launch_normalize_pair4(n, h, w, logits, wd, dtype, st);
+        });
+        if (e != hipSuccess) return e;
+    }
+    for (int d = 0; d < 4; ++d) {
+        p[d].wts = wd[d];
+        p[d].wts_are_logits = 0;
+        p[d].wdtype = dtype == GSPN_F32 ? GSPN_F32 : gspn::kPairF16;
+    }
+    return hipSuccess;
+}
+
 gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                           const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
                           void* y, void* workspace, int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
@@ -416,18 +445,9 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         // channels, so the scans run without transcendentals: fp32 triples
         // for fp32 storage; for bf16 storage packed half pairs (w_{k-1},
         // w_{k+1}) with the centre weight recovered as 1 minus their sum, a
-        // third of the bytes every channel's scan reads.
-        for (int d = 0; d < 4; ++d) {
-            char* wd = ws + d * wdir;
-            const hipError_t e = timed(tm, GSPN_STAGE_NORMALIZE, [&] {
-                return dtype == GSPN_F32 ? gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32)
-                                         : gspn::launch_normalize_pair(d, n, h, w, logits[d], wd, dtype, st);
-            });
-            if (e != hipSuccess) return GSPN_ERR_HIP;
-            p[d].wts = wd;
-            p[d].wts_are_logits = 0;
-            p[d].wdtype = dtype == GSPN_F32 ? GSPN_F32 : gspn::kPairF16;
-        }
+        // third of the bytes every channel's scan reads (all four directions
+        // in one launch).
+        if (prenormalise(n, h, w, logits, ws, wdir, dtype, st, tm, p) != hipSuccess) return GSPN_ERR_HIP;
     }
     // The horizontal directions become vertical-form scans of x transposed
     // (their scan frame): line k of step i is x[.., k, i].
@@ -648,19 +668,9 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].dtype = dtype;
         p[d].wdtype = dtype;
         p[d].odtype = GSPN_F32;
-        if (shared) {
-            // channel-shared logits: normalised once, as in the forward
-            char* wd = wnorm + d * wdir;
-            const hipError_t e = timed(tm, GSPN_STAGE_NORMALIZE, [&] {
-                return dtype == GSPN_F32 ? gspn::launch_normalize(d, n, 1, h, w, logits[d], wd, dtype, st, GSPN_F32)
-                                         : gspn::launch_normalize_pair(d, n, h, w, logits[d], wd, dtype, st);
-            });
-            if (e != hipSuccess) return GSPN_ERR_HIP;
-            p[d].wts = wd;
-            p[d].wts_are_logits = 0;
-            p[d].wdtype = dtype == GSPN_F32 ? GSPN_F32 : gspn::kPairF16;
-        }
     }
+    // channel-shared logits: normalised once, as in the forward
+    if (shared && prenormalise(n, h, w, logits, wnorm, wdir, dtype, st, tm, p) != hipSuccess) return GSPN_ERR_HIP;
     int kind = GSPN_SCAN_FUSED4;
     if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
         return GSPN_ERR_HIP;

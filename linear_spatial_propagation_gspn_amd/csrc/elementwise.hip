@@ -52,6 +52,73 @@ __global__ __launch_bounds__(256) void normalize_pair_kernel(const T* __restrict
     }
 }
 
+// The four directions' channel-shared logits into packed half pairs in one
+// launch (blockIdx.y = direction).  vec: every line is whole 16-byte vectors
+// and every tensor is 16-byte aligned, so a lane normalises one vector of
+// positions with three 16-byte loads and writes its pairs with 16-byte
+// stores; otherwise one position per lane.
+struct Pair4K {
+    const void* z[4];
+    uint32_t* w[4];
+    int64_t planes;
+    int64_t S[4];
+    int64_t L[4];
+    int vec;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void normalize_pair4_kernel(const Pair4K a) {
+    constexpr int VW = 16 / static_cast<int>(sizeof(T));
+    const int d = blockIdx.y;
+    const T* __restrict__ z = static_cast<const T*>(a.z[d]);
+    uint32_t* __restrict__ w = a.w[d];
+    const int64_t L = a.L[d];
+    const int64_t per_plane = a.S[d] * L;
+    const int64_t total = a.planes * per_plane;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (a.vec) {
+        struct alignas(16) V {
+            T e[VW];
+        };
+        struct alignas(16) W4 {
+            uint32_t e[4];
+        };
+        for (int64_t v = first; v < total / VW; v += stride) {
+            const int64_t e = v * VW;
+            const int64_t pl = e / per_plane;
+            const int64_t r = e - pl * per_plane;
+            const int64_t k0 = r % L;
+            const T* zb = z + pl * 3 * per_plane + r;
+            const V z0 = *reinterpret_cast<const V*>(zb);
+            const V z1 = *reinterpret_cast<const V*>(zb + per_plane);
+            const V z2 = *reinterpret_cast<const V*>(zb + 2 * per_plane);
+            uint32_t out[VW];
+#pragma unroll
+            for (int j = 0; j < VW; ++j) {
+                float w0, w1, w2;
+                normalise_row(Store<T>::ld(&z0.e[j]), Store<T>::ld(&z1.e[j]), Store<T>::ld(&z2.e[j]), k0 + j > 0,
+                              k0 + j + 1 < L, w0, w1, w2);
+                out[j] = pack_pair(w0, w2);
+            }
+#pragma unroll
+            for (int q = 0; q < VW / 4; ++q)
+                *reinterpret_cast<W4*>(w + e + 4 * q) = W4{{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]}};
+        }
+    } else {
+        for (int64_t e = first; e < total; e += stride) {
+            const int64_t pl = e / per_plane;
+            const int64_t r = e - pl * per_plane;
+            const int64_t k = r % L;
+            const int64_t base = pl * 3 * per_plane + r;
+            float w0, w1, w2;
+            normalise_row(Store<T>::ld(z + base), Store<T>::ld(z + base + per_plane),
+                          Store<T>::ld(z + base + 2 * per_plane), k > 0, k + 1 < L, w0, w1, w2);
+            w[e] = pack_pair(w0, w2);
+        }
+    }
+}
+
 // y = ((h0 + h1) + h2) + h3
 template <typename T>
 __global__ __launch_bounds__(256) void merge4_kernel(const T* __restrict__ h0, const T* __restrict__ h1,
@@ -168,6 +235,27 @@ hipError_t launch_normalize_pair(int dir, int64_t n, int64_t h, int64_t w, const
         hipLaunchKernelGGL(normalize_pair_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
                            static_cast<const bf16_t*>(logits), static_cast<uint32_t*>(w_out), n, S, L);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_normalize_pair4(int64_t n, int64_t h, int64_t w, const void* const logits[4],
+                                  void* const w_out[4], int dtype, hipStream_t stream) {
+    Pair4K k;
+    const int vw = dtype == kF32 ? 4 : 8;
+    k.planes = n;
+    k.vec = 1;
+    for (int d = 0; d < 4; ++d) {
+        const bool horiz = (d == 2 || d == 3);
+        k.z[d] = logits[d];
+        k.w[d] = static_cast<uint32_t*>(w_out[d]);
+        k.S[d] = horiz ? w : h;
+        k.L[d] = horiz ? h : w;
+        k.vec = k.vec && k.L[d] % vw == 0 && aligned16(logits[d]) && aligned16(w_out[d]);
+    }
+    const int64_t total = n * h * w;
+    const dim3 grid(grid_for(k.vec ? total / vw : total, 256), 4);
+    if (dtype == kF32) hipLaunchKernelGGL(normalize_pair4_kernel<float>, grid, dim3(256), 0, stream, k);
+    else hipLaunchKernelGGL(normalize_pair4_kernel<bf16_t>, grid, dim3(256), 0, stream, k);
     return hipGetLastError();
 }
 

@@ -85,6 +85,11 @@ hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w
 hipError_t launch_normalize_pair(int dir, int64_t n, int64_t h, int64_t w, const void* logits, void* w_out,
                                  int dtype, hipStream_t stream);
 
+// The same for all four directions in one launch (logits[d] in direction
+// d's scan frame, w_out[d] its pairs).
+hipError_t launch_normalize_pair4(int64_t n, int64_t h, int64_t w, const void* const logits[4],
+                                  void* const w_out[4], int dtype, hipStream_t stream);
+
 hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
                          int64_t numel, int dtype, hipStream_t stream);
 
