@@ -161,7 +161,8 @@ def stage_times(wl, inp, out, ws, reps: int, merge=None) -> dict:
 
 
 # The sources each measured kernel is built from: its own file, the headers
-# it includes, the launch code that configures it and the build flags.
+# its device code includes, the launch code that configures it (in the same
+# files) and the build flags.  launch.hpp only declares host launchers.
 _SCAN4 = ["scan_kernel.hpp", "scan_lp.hpp", "scan.hip", "scan4_f32.hip", "scan4_bf16.hip", "scan4_bf16pair.hip"]
 KERNEL_SOURCES = {
     "scan4lp_kernel": _SCAN4,
@@ -170,13 +171,13 @@ KERNEL_SOURCES = {
     "plane4_kernel": ["plane4.hip"],
     "adj4_kernel": ["backward.hip"],
 }
-_COMMON = ["device.hpp", "launch.hpp"]
+_COMMON = ["device.hpp"]
 
 
 def kernel_sources_digest(kernel: str | None = None) -> str:
     """sha256 over the sources of one kernel (KERNEL_SOURCES, plus the shared
-    device helpers, the launch declarations and build.py), or over every
-    kernel source of the library for an unlisted kernel."""
+    device helpers and build.py), or over every kernel source of the library
+    for an unlisted kernel."""
     if kernel in KERNEL_SOURCES:
         names = sorted(set(KERNEL_SOURCES[kernel] + _COMMON))
     else:
