@@ -31,29 +31,9 @@ __global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ z,
     }
 }
 
-// The same normalisation into packed half pairs (w_{k-1}, w_{k+1}) per
-// position; layout [planes][S][L] of 32-bit words.
-template <typename T>
-__global__ __launch_bounds__(256) void normalize_pair_kernel(const T* __restrict__ z, uint32_t* __restrict__ w,
-                                                             int64_t planes, int64_t S, int64_t L) {
-    const int64_t per_plane = S * L;
-    const int64_t total = planes * per_plane;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-         e += stride) {
-        const int64_t pl = e / per_plane;
-        const int64_t r = e - pl * per_plane;
-        const int64_t k = r % L;
-        const int64_t base = pl * 3 * per_plane + r;
-        float w0, w1, w2;
-        normalise_row(Store<T>::ld(z + base), Store<T>::ld(z + base + per_plane),
-                      Store<T>::ld(z + base + 2 * per_plane), k > 0, k + 1 < L, w0, w1, w2);
-        w[e] = pack_pair(w0, w2);
-    }
-}
-
-// The four directions' channel-shared logits into packed half pairs in one
-// launch (blockIdx.y = direction).  vec: every line is whole 16-byte vectors
+// The four directions' channel-shared logits normalised into packed half
+// pairs (w_{k-1}, w_{k+1}) per position, layout [planes][S][L] of 32-bit
+// words, in one launch (blockIdx.y = direction).  vec: every line is whole 16-byte vectors
 // and every tensor is 16-byte aligned, so a lane normalises one vector of
 // positions with three 16-byte loads and writes its pairs with 16-byte
 // stores; otherwise one position per lane.
@@ -133,43 +113,6 @@ __global__ __launch_bounds__(256) void merge4_kernel(const T* __restrict__ h0, c
     }
 }
 
-// y = ((y + w1) + w2) + w3, 16 bytes per lane per access where aligned.
-template <typename T>
-__global__ __launch_bounds__(256) void merge_into_kernel(T* y, const T* __restrict__ w1,
-                                                         const T* __restrict__ w2,
-                                                         const T* __restrict__ w3, int64_t numel,
-                                                         int vec) {
-    constexpr int VW = 16 / static_cast<int>(sizeof(T));
-    struct alignas(16) V {
-        T e[VW];
-    };
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    const int64_t first = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    int64_t done = 0;
-    if (vec) {
-        const int64_t nv = numel / VW;
-        for (int64_t e = first; e < nv; e += stride) {
-            V a = reinterpret_cast<const V*>(y)[e];
-            const V b = reinterpret_cast<const V*>(w1)[e];
-            const V c = reinterpret_cast<const V*>(w2)[e];
-            const V d = reinterpret_cast<const V*>(w3)[e];
-#pragma unroll
-            for (int j = 0; j < VW; ++j) {
-                const float v = ((Store<T>::ld(&a.e[j]) + Store<T>::ld(&b.e[j])) + Store<T>::ld(&c.e[j])) +
-                                Store<T>::ld(&d.e[j]);
-                Store<T>::st(&a.e[j], v);
-            }
-            reinterpret_cast<V*>(y)[e] = a;
-        }
-        done = nv * VW;
-    }
-    for (int64_t e = done + first; e < numel; e += stride) {
-        const float v = ((Store<T>::ld(y + e) + Store<T>::ld(w1 + e)) + Store<T>::ld(w2 + e)) +
-                        Store<T>::ld(w3 + e);
-        Store<T>::st(y + e, v);
-    }
-}
-
 unsigned grid_for(int64_t total, int threads) {
     int64_t blocks = (total + threads - 1) / threads;
     const int64_t cap = 256 * 64;  // 64 workgroups per CU is plenty for a grid-stride loop
@@ -181,23 +124,6 @@ unsigned grid_for(int64_t total, int threads) {
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 }  // namespace
-
-hipError_t launch_merge_into(void* y, const void* w1, const void* w2, const void* w3, int64_t numel,
-                             int dtype, hipStream_t stream) {
-    const int vec = aligned16(y) && aligned16(w1) && aligned16(w2) && aligned16(w3);
-    const int64_t per = vec ? (dtype == kF32 ? 4 : 8) : 1;
-    const unsigned grid = grid_for((numel + per - 1) / per, 256);
-    if (dtype == kF32) {
-        hipLaunchKernelGGL(merge_into_kernel<float>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<float*>(y), static_cast<const float*>(w1),
-                           static_cast<const float*>(w2), static_cast<const float*>(w3), numel, vec);
-    } else {
-        hipLaunchKernelGGL(merge_into_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<bf16_t*>(y), static_cast<const bf16_t*>(w1),
-                           static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w3), numel, vec);
-    }
-    return hipGetLastError();
-}
 
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
                             const void* logits, void* w_out, int dtype, hipStream_t stream,
@@ -218,22 +144,6 @@ hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w
         hipLaunchKernelGGL((normalize_kernel<bf16_t, bf16_t>), dim3(grid), dim3(256), 0, stream,
                            static_cast<const bf16_t*>(logits), static_cast<bf16_t*>(w_out), planes, S,
                            L);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_normalize_pair(int dir, int64_t n, int64_t h, int64_t w, const void* logits, void* w_out,
-                                 int dtype, hipStream_t stream) {
-    const bool horiz = (dir == 2 || dir == 3);
-    const int64_t S = horiz ? w : h;
-    const int64_t L = horiz ? h : w;
-    const unsigned grid = grid_for(n * S * L, 256);
-    if (dtype == kF32) {
-        hipLaunchKernelGGL(normalize_pair_kernel<float>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<const float*>(logits), static_cast<uint32_t*>(w_out), n, S, L);
-    } else {
-        hipLaunchKernelGGL(normalize_pair_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<const bf16_t*>(logits), static_cast<uint32_t*>(w_out), n, S, L);
     }
     return hipGetLastError();
 }

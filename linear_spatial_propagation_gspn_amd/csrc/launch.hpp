@@ -80,22 +80,15 @@ hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w
                             const void* logits, void* w_out, int dtype, hipStream_t stream,
                             int out_dtype = -1);
 
-// Channel-shared logits of one direction ([n][1][3][S][L]) into packed half
-// pairs [n][S][L] (WPair format).
-hipError_t launch_normalize_pair(int dir, int64_t n, int64_t h, int64_t w, const void* logits, void* w_out,
-                                 int dtype, hipStream_t stream);
-
-// The same for all four directions in one launch (logits[d] in direction
-// d's scan frame, w_out[d] its pairs).
+// Channel-shared logits of the four directions ([n][1][3][S][L], in each
+// direction's scan frame) into packed half pairs [n][S][L] (WPair format),
+// one launch.
 hipError_t launch_normalize_pair4(int64_t n, int64_t h, int64_t w, const void* const logits[4],
                                   void* const w_out[4], int dtype, hipStream_t stream);
 
 hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const void* h3, void* y,
                          int64_t numel, int dtype, hipStream_t stream);
 
-// y = ((y + w1) + w2) + w3 in place.
-hipError_t launch_merge_into(void* y, const void* w1, const void* w2, const void* w3, int64_t numel,
-                             int dtype, hipStream_t stream);
 
 // One direction of the adjoint scan, in vertical form (horizontal directions
 // on x and dL/dy transposed into their scan frame).  hs: the direction's
