@@ -447,3 +447,38 @@ def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
     else:
         _raise(lib().gspn_backward4_timed(*args, ctypes.byref(times)), "gspn_backward4_timed")
     return (dx, dz, dl, dmerge) if want_dm else (dx, dz, dl)
+
+
+class _Forward4(torch.autograd.Function):
+    """gspn_forward4 as an autograd node whose backward is gspn_backward4."""
+
+    @staticmethod
+    def forward(ctx, chunk_len, has_merge, x, merge, *tensors):
+        logits, lams = list(tensors[:4]), list(tensors[4:])
+        cw = logits[0].shape[1]
+        y = gspn_forward4(x, logits, lams, chunk_len=chunk_len, workspace=forward4_workspace(x, cw),
+                          merge=merge if has_merge else None)
+        ctx.chunk_len = chunk_len
+        ctx.has_merge = has_merge
+        ctx.save_for_backward(x, merge, *tensors)
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, merge, *tensors = ctx.saved_tensors
+        logits, lams = tensors[:4], tensors[4:]
+        res = gspn_backward4(x, logits, lams, gy.to(x.dtype).contiguous(), chunk_len=ctx.chunk_len,
+                             merge=merge if ctx.has_merge else None)
+        dx, dz, dl = res[0], res[1], res[2]
+        dm = res[3] if ctx.has_merge else None
+        return (None, None, dx, dm, *dz, *dl)
+
+
+def gspn4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor], chunk_len: int = 0,
+          merge: torch.Tensor | None = None) -> torch.Tensor:
+    """The four-direction propagation as a differentiable op: gspn_forward4
+    forward, gspn_backward4 for the gradients of x, the logits, the lambdas
+    and (if given) the merge weights."""
+    has_merge = merge is not None
+    m = merge if has_merge else torch.empty(0, device=x.device)
+    return _Forward4.apply(int(chunk_len), has_merge, x, m, *logits, *lams)
