@@ -308,9 +308,9 @@ def cpu_baseline(wl, inp, merge=None) -> dict:
     return cpu_baseline_planes(wl, inp, oracle, merge=merge)
 
 
-def copy_check(mib: int) -> None:
-    """A plain device-to-device copy of known size: reads and writes mib MiB
-    per launch.  Used to calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+def copy_rate(mib: int, reps: int = 10) -> tuple:
+    """ms per launch and read + write GB/s of a plain device-to-device copy
+    of mib MiB."""
     n = mib * (1 << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -319,13 +319,33 @@ def copy_check(mib: int) -> None:
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
-    for _ in range(10):
+    for _ in range(reps):
         b.copy_(a)
     ev[1].record(stream)
     torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / 10
-    print(json.dumps({"copy_MiB": mib, "ms": round(ms, 4),
-                      "GBps_read_plus_write": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}))
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del a, b
+    return ms, 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def copy_check(mib: int) -> None:
+    """A plain device-to-device copy of known size: reads and writes mib MiB
+    per launch.  Used to calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    ms, gbps = copy_rate(mib)
+    print(json.dumps({"copy_MiB": mib, "ms": round(ms, 4), "GBps_read_plus_write": round(gbps, 1)}))
+
+
+def per_step_ms(step, n: int) -> list:
+    """Durations (ms) of n single steps, each between its own pair of events
+    on the current stream."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
 
 
 def bench_backward(args, wl):
@@ -364,6 +384,7 @@ def bench_backward(args, wl):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
     print("bench: backward %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    singles = per_step_ms(step, args.steps)
 
     reps = max(3, min(args.steps, 10))
     acc = {name: 0.0 for name in G.STAGES}
@@ -393,6 +414,7 @@ def bench_backward(args, wl):
         "config": {"workload": wl.name, "pass": "backward", "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
                    "merge": "learnable" if args.merge else "sum"},
+        "ms_median": round(singles[len(singles) // 2], 4), "ms_min": round(singles[0], 4),
         "effective_GBps": round(eff, 1), "effective_frac": round(eff / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
         "stages_ms": {k: round(v, 4) for k, v in acc.items() if v > 0},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -479,6 +501,7 @@ def main():
     print("bench: %.3f ms/step (wall %.3f ms/step)" % (ms, wall * 1e3 / args.steps),
           file=sys.stderr, flush=True)
 
+    singles = per_step_ms(step, args.steps)
     st, kernel = stage_times(wl, inp, out, ws, reps=max(3, min(args.steps, 10)), merge=merge)
     scan = st["scan"]
     launches = scan["launches"]
@@ -490,6 +513,9 @@ def main():
     eff = alg / (ms * 1e-3) / 1e9
     print("bench: %s %.4f ms per launch (%d per step), %.1f GB/s algorithmic"
           % (kernel, kernel_ms, launches, achieved), file=sys.stderr, flush=True)
+
+    # a 4 GiB device copy (8 GiB moved) on the same GPU, for scale
+    _, copy_gbps = copy_rate(4096, reps=5)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -513,9 +539,14 @@ def main():
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
                    "c_proxy": wl.c_proxy, "merge": "learnable" if args.merge else "sum",
                    "launch": "hip graph replay" if args.graph else "eager"},
+        "ms_median": round(singles[len(singles) // 2], 4),
+        "ms_min": round(singles[0], 4),
         "effective_GBps": round(eff, 1),
         "effective_frac": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": alg,
+        "copy_GBps": round(copy_gbps, 1),
+        "effective_frac_of_copy": round(eff / copy_gbps, 4),
+        "achieved_frac_of_copy": round(achieved / copy_gbps, 4),
         "stages_ms": {k: round(v["ms"], 4) for k, v in st.items() if v["launches"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
