@@ -15,9 +15,12 @@
 //  - the per-step logits and lambda stream from HBM in the directions' scan
 //    frames (one contiguous line per step), prefetched D steps ahead;
 //  - T2B and B2T add their h into one LDS partial, L2R and R2L into another,
-//    with LDS float atomics: every element of a partial receives exactly two
-//    additions onto 0, and fl(a + b) = fl(b + a), so the result does not
-//    depend on their order;
+//    with plain LDS reads and writes, no atomics (LDS float atomics made the
+//    kernel 1.6x slower): each direction of a pair first writes the lines of
+//    the first half of its steps, which the two directions split between
+//    them, and after one barrier adds onto the lines the other one wrote.
+//    Every element receives exactly two additions onto 0, and
+//    fl(a + b) = fl(b + a), so the result does not depend on their order;
 //  - y = partial_vertical + partial_horizontal is written to HBM once.
 // Compulsory traffic only: x, the four directions' logits and lambdas, y.
 #include <utility>
@@ -176,8 +179,16 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
 
     float h = 0.0f;
     int cpos = 0;  // step within the current chunk
+    // The two directions of a pair share `part` without atomics: up to the
+    // barrier each writes the lines of its first half of the steps (disjoint:
+    // the forward direction stops after floor(S/2) steps, the reverse one
+    // after ceil(S/2)), after it each adds onto lines the other one wrote.
+    // Every element takes two additions onto 0, so the order of the pair does
+    // not matter.
+    const int split = REV ? (S + 1) / 2 : S / 2;
     auto step = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
+        if (t == split) __syncthreads();
         const int i = line_of(t);
         const int pos = HORIZ ? k * ld + i : i * ld + k;
         const float u = (widen<T>(rlam[s]) * msc) * xs[pos];
@@ -193,7 +204,7 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
         }
         fill(slot, t + kDepth);
         h = active ? hn : 0.0f;
-        if (active) atomicAdd(&part[pos], h);
+        if (active) part[pos] = part[pos] + h;
     };
 
     int t = 0;
@@ -205,6 +216,7 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         ((t + Ss < S ? step(IC<Ss>{}, t + Ss) : void()), ...);
     }(std::make_integer_sequence<int, kDepth - 1>{});
+    if (split >= S) __syncthreads();  // a one-step reverse scan
 }
 
 template <typename T>
