@@ -33,6 +33,8 @@ namespace gspn {
 #define GSPN_BAND_DEPTH 8
 #endif
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 struct BandK {
     ScanK d[4];
     int64_t blocks[4];  // workgroups of each direction in this band (0: its scan has ended)
@@ -47,7 +49,10 @@ struct BandK {
     int xcd_lines;      // 1: the segments of a line share an XCD (see scan4band_kernel)
 };
 
-template <typename T, typename TW, bool LOGITS>
+// CH: chunks restart inside the band (chunk_len below the scan length), so
+// every step checks for a chunk's first line; otherwise only step 0 of the
+// scan can be one.
+template <typename T, typename TW, bool LOGITS, bool CH>
 __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p, int g) {
     const ScanK& a = b.d[dir];
     constexpr int P = 16 / static_cast<int>(sizeof(T));  // positions per lane
@@ -94,14 +99,31 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
     auto line_of = [&](int t) { return static_cast<uint32_t>(rev ? S - 1 - t : t); };
 
     uint32_t sx[D][WT], sl[D][WT], sz[D][NZ][WW];
-    auto fill = [&](auto slot, int t) {
+    // Row offsets advance by one line per step (downwards for a reverse scan;
+    // unsigned wrap-around does the subtraction).  Fills run in step order,
+    // so the next fill's offsets are kept as running sums (fT, fW) wherever
+    // no clamping is needed, and the store's offset (sT) likewise.
+    const uint32_t dT = rev ? 0u - rowT : rowT;
+    const uint32_t dW = rev ? 0u - rowW : rowW;
+    uint32_t fT = 0, fW = 0;
+    auto load_slot = [&](auto slot, uint32_t oT, uint32_t oW) {
         constexpr int s = decltype(slot)::value;
-        const uint32_t i = line_of(min(t, t1 - 1));
-        lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, i * rowT);
-        lp::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, i * rowT);
+        lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, oT);
+        lp::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, oT);
         constexpr int ZAUX = LOGITS ? GSPN_LP_STREAM_AUX : 0;
 #pragma unroll
-        for (int o = 0; o < NZ; ++o) lp::load_words<WW, ZAUX>(sz[s][o], rz, vw, o * planeW + i * rowW);
+        for (int o = 0; o < NZ; ++o) lp::load_words<WW, ZAUX>(sz[s][o], rz, vw, o * planeW + oW);
+    };
+    // step t's inputs, the row clamped to the band (rows past it are never used)
+    auto fill = [&](auto slot, int t) {
+        const uint32_t i = line_of(min(t, t1 - 1));
+        load_slot(slot, i * rowT, i * rowW);
+    };
+    // the next step's inputs where that row lies inside the band
+    auto fill_next = [&](auto slot) {
+        load_slot(slot, fT, fW);
+        fT += dT;
+        fW += dW;
     };
 
     // states at the band's start (a chunk's first step ignores them)
@@ -110,14 +132,39 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 #pragma unroll
     for (int j = 0; j < P; ++j) h[j] = (t0 > 0 && active) ? hin[k0c + j] : 0.0f;
 
-    auto step = [&](auto slot, int t) {
+    uint32_t sT = line_of(t0) * rowT;
+    // lambda_j x_j + c for the bf16 pair (j, j + 1) in word e: one bf16 dot
+    // product with the other half of x masked to 0 (exact products, one
+    // rounding, as fmaf)
+    auto lamx = [&](auto slot, int j, float c) {
+        constexpr int s = decltype(slot)::value;
+        const uint32_t xw = sx[s][j >> 1] & ((j & 1) ? 0xffff0000u : 0x0000ffffu);
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, sl[s][j >> 1]),
+                                               __builtin_bit_cast(bf16x2_t, xw), c, false);
+    };
+
+    // CLAMP: fill with the row clamped to the band (the last D steps);
+    // PEEL: the band's first step, the only one that can start the scan
+    // when chunks do not restart (CH false)
+    auto step = [&](auto slot, auto clampc, auto peelc, int t) {
         constexpr int s = decltype(slot)::value;
         float hn[P];
-        const bool first = cpos == 0;
-        cpos = cpos + 1 == K ? 0 : cpos + 1;
+        bool first;
+        if constexpr (CH) {
+            first = cpos == 0;
+            cpos = cpos + 1 == K ? 0 : cpos + 1;
+        } else {
+            first = decltype(peelc)::value != 0 && t == 0;
+        }
         if (first) {  // a chunk's first line: h_prev = 0, its weights unused
 #pragma unroll
-            for (int j = 0; j < P; ++j) hn[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+            for (int j = 0; j < P; ++j) {
+                if constexpr (PAIR) {
+                    hn[j] = lamx(slot, j, 0.0f);
+                } else {
+                    hn[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+                }
+            }
         } else {
             const float left = lp::shift_from_lower_lane(h[P - 1]);   // 0 beyond the wave
             const float right = lp::shift_from_upper_lane(h[0]);
@@ -128,13 +175,16 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 #pragma unroll
                 for (int j = 1; j < P; ++j) dd[j] = h[j] - h[j - 1];
                 dd[P] = right - h[P - 1];
+                // all dot products first: their results are not read back
+                // at once (a dot product's result needs extra cycles before
+                // the next instruction may read it)
+                float base[P];
 #pragma unroll
-                for (int j = 0; j < P; ++j) {
-                    const float base =
-                        __builtin_fmaf(lp::elem<T, WT>(sl[s], j), lp::elem<T, WT>(sx[s], j), h[j]);
+                for (int j = 0; j < P; ++j) base[j] = lamx(slot, j, h[j]);
+#pragma unroll
+                for (int j = 0; j < P; ++j)
                     hn[j] = __builtin_fmaf(pair_hi(sz[s][0][j]), dd[j + 1],
-                                           __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base));
-                }
+                                           __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base[j]));
             } else {
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
@@ -156,11 +206,18 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
                 }
             }
         }
-        fill(slot, t + D);
-        // lanes outside the line hold exact zeros: their values reach the
-        // line's border positions, whose weights to them are 0
+        if constexpr (decltype(clampc)::value != 0) {
+            fill(slot, t + D);
+        } else {
+            fill_next(slot);
+        }
+        // lanes outside the line: only their edge values leave the lane, and
+        // those are held at exact zeros, whose weights at the line's border
+        // positions are 0 anyway
 #pragma unroll
-        for (int j = 0; j < P; ++j) h[j] = active ? hn[j] : 0.0f;
+        for (int j = 0; j < P; ++j) h[j] = (j == 0 || j == P - 1) && !active ? 0.0f : hn[j];
+        const uint32_t oT = sT;
+        sT += dT;
         if (owned) {
             uint32_t ow[WT];
             if constexpr (sizeof(T) == 4) {
@@ -172,21 +229,31 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
             }
             const lp::int4v o = {static_cast<int>(ow[0]), static_cast<int>(ow[1]), static_cast<int>(ow[2]),
                                  static_cast<int>(ow[3])};
-            __builtin_amdgcn_raw_buffer_store_b128(o, ro, vt, line_of(t) * rowT, GSPN_LP_STREAM_AUX);
+            __builtin_amdgcn_raw_buffer_store_b128(o, ro, vt, oT, GSPN_LP_STREAM_AUX);
         }
     };
 
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         (fill(IC<Ss>{}, t0 + Ss), ...);
     }(std::make_integer_sequence<int, D>{});
-    int t = t0;
+    step(IC<0>{}, IC<1>{}, IC<1>{}, t0);
+    // then slots 1, 2, .., D-1, 0; while every fill of an iteration (rows
+    // t + D .. t + 2D - 1) lies inside the band, from running offsets
+    int t = t0 + 1;
+    fT = line_of(t0 + D + 1) * rowT;
+    fW = line_of(t0 + D + 1) * rowW;
+    for (; t + 2 * D <= t1; t += D) {
+        [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+            (step(IC<(Ss + 1) % D>{}, IC<0>{}, IC<0>{}, t + Ss), ...);
+        }(std::make_integer_sequence<int, D>{});
+    }
     for (; t + D <= t1; t += D) {
         [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
-            (step(IC<Ss>{}, t + Ss), ...);
+            (step(IC<(Ss + 1) % D>{}, IC<1>{}, IC<0>{}, t + Ss), ...);
         }(std::make_integer_sequence<int, D>{});
     }
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
-        ((t + Ss < t1 ? step(IC<Ss>{}, t + Ss) : void()), ...);
+        ((t + Ss < t1 ? step(IC<(Ss + 1) % D>{}, IC<1>{}, IC<0>{}, t + Ss) : void()), ...);
     }(std::make_integer_sequence<int, D - 1>{});
 
     if (owned) {
@@ -200,7 +267,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 // segments of one line all go to the same XCD, so a segment's halo rows,
 // which its neighbours read in the same steps, come from that XCD's L2
 // (every direction active, equal segment counts, lines a multiple of 8).
-template <typename T, typename TW, bool LOGITS>
+template <typename T, typename TW, bool LOGITS, bool CH>
 __global__ __launch_bounds__(64) void scan4band_kernel(const BandK b) {
     int dir = 0;
     int64_t p;
@@ -222,7 +289,7 @@ __global__ __launch_bounds__(64) void scan4band_kernel(const BandK b) {
         p = idx / b.nseg[dir];
         g = static_cast<int>(idx - p * b.nseg[dir]);
     }
-    band_segment<T, TW, LOGITS>(b, dir, p, g);
+    band_segment<T, TW, LOGITS, CH>(b, dir, p, g);
 }
 
 // One band: every direction whose scan has not ended by step b.t0.
@@ -230,8 +297,15 @@ template <typename T, typename TW, bool LOGITS>
 hipError_t launch_band4(const BandK& b, hipStream_t stream) {
     const int64_t nblocks = b.blocks[0] + b.blocks[1] + b.blocks[2] + b.blocks[3];
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS>), dim3(static_cast<unsigned>(nblocks)), dim3(64), 0, stream,
-                       b);
+    bool chunked = false;
+    for (int d = 0; d < 4; ++d) chunked = chunked || (b.blocks[d] > 0 && b.d[d].K < b.d[d].S);
+    if (chunked) {
+        hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, true>), dim3(static_cast<unsigned>(nblocks)), dim3(64),
+                           0, stream, b);
+    } else {
+        hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, false>), dim3(static_cast<unsigned>(nblocks)), dim3(64),
+                           0, stream, b);
+    }
     return hipGetLastError();
 }
 
