@@ -149,7 +149,9 @@ gspn_status gspn_proxy_project(int64_t n, int64_t c_in, int64_t h, int64_t w, in
  * recap": four line scans over the same x).  The four directions run
  * concurrently.  Shapes as for gspn_forward4; out is a host array of 4
  * device pointers, each [n][c][h][w], pairwise disjoint and overlapping no
- * input.  Lines may hold at most 2048 positions (else GSPN_ERR_UNSUPPORTED).
+ * input.  Lines may hold at most 2048 positions, and the four directions
+ * together at most 2^31 - 1 (plane, chunk) pairs (else
+ * GSPN_ERR_UNSUPPORTED).
  */
 gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                            int64_t chunk_len, const void* x, const void* const logits[4],
@@ -203,7 +205,9 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              directions run as row-coalesced scans whose outputs a
  *              transposing merge adds into y, and (c) runs all four
  *              directions in one launch into separate maps (lines up to 2048
- *              positions), or, when the planes are so few that the four
+ *              positions and at most 2^31 - 1 (plane, chunk) pairs over the
+ *              four; beyond either, one direction after another through
+ *              the workspace's maps), or, when the planes are so few that the four
  *              directions make at most 64 long lines, splits each line
  *              across workgroups and runs the scan in bands of steps, one
  *              launch per band.  Its contents afterwards are unspecified.
@@ -282,8 +286,10 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
  *                  between calls.
  * workspace: required, gspn_backward4_workspace_bytes() bytes, 4-byte
  * aligned.  Outputs may overlap neither an input, the workspace nor each
- * other.  Lines may hold at most 2048 positions (else GSPN_ERR_UNSUPPORTED).
- * The forward states are recomputed inside and kept in fp32.
+ * other.  Lines may hold at most 2048 positions, and the four directions
+ * together at most 2^31 - 1 (plane, chunk) pairs (else
+ * GSPN_ERR_UNSUPPORTED).  The forward states are recomputed inside and kept
+ * in fp32.
  */
 gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                            const void* x, const void* const logits[4], const void* const lam[4], const float* merge,

@@ -146,6 +146,17 @@ ScanCheck check_scan(int dir, int64_t chunk_len, int64_t n, int64_t c, int64_t h
     return {GSPN_OK, K};
 }
 
+// The four-direction launches run a workgroup per (plane, chunk) of every
+// direction: the total must fit one launch's grid.
+bool fused_grid_ok(int64_t n, int64_t c, int64_t h, int64_t w, const int64_t chunks[4]) {
+    int64_t total = 0;
+    for (int d = 0; d < 4; ++d) {
+        const int64_t S = horizontal(d) ? w : h;
+        total += n * c * ((S + chunks[d] - 1) / chunks[d]);  // each term <= INT_MAX (check_scan)
+    }
+    return total <= INT_MAX;
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,7 +275,7 @@ gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
         if (ck.st != GSPN_OK || empty) return ck.st;
         chunks[d] = ck.chunk;
     }
-    if (!gspn::fused4_supported(h, w)) return GSPN_ERR_UNSUPPORTED;
+    if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c, h, w, chunks)) return GSPN_ERR_UNSUPPORTED;
     if (!x || !logits || !lam || !out) return GSPN_ERR_NULL_POINTER;
     for (int d = 0; d < 4; ++d)
         if (!logits[d] || !lam[d] || !out[d]) return GSPN_ERR_NULL_POINTER;
@@ -465,7 +476,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     // Concurrent path: the four directions in one launch, each into its own
     // map (lines up to 2048 positions); very few long lines instead run split
     // across workgroups, one launch per band of steps.
-    if (gspn::fused4_supported(h, w)) {
+    if (gspn::fused4_supported(h, w) && fused_grid_ok(n, c, h, w, chunks)) {
         p[1].out = m1;
         p[2].out = m2;
         p[3].out = m3;
@@ -568,7 +579,7 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         if (ck.st != GSPN_OK || empty) return ck.st;
         chunks[d] = ck.chunk;
     }
-    if (!gspn::fused4_supported(h, w)) return GSPN_ERR_UNSUPPORTED;
+    if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c, h, w, chunks)) return GSPN_ERR_UNSUPPORTED;
     if (!x || !gy || !dx || !logits || !lam || !dlogits || !dlam || !workspace) return GSPN_ERR_NULL_POINTER;
     for (int d = 0; d < 4; ++d)
         if (!logits[d] || !lam[d] || !dlogits[d] || !dlam[d]) return GSPN_ERR_NULL_POINTER;

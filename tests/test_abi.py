@@ -144,6 +144,8 @@ def test_scan4_validation(lib):
     assert f(chunk=-1) == CHUNK
     assert f(cw=5) == WCH
     assert f(h=2049) == UNSUP                        # longer than the fused kernel's lines
+    # each direction's (plane, chunk) count fits a grid, the four together do not
+    assert f(n=700000, c=1, cw=1, h=2048, w=2048, chunk=1) == UNSUP
     assert f(o=vp4(D_, 0, D_, D_)) == NULLP
     assert f(o=vp4(D_, D_ + 0x1000000, D_ + 0x2000000, D_ + 2)) == MISAL
     assert f(o=vp4(D_, D_ + 16, D_ + 0x2000000, D_ + 0x3000000)) == ALIAS   # outputs overlap
@@ -275,6 +277,7 @@ def test_backward4_validation(lib):
     assert f(chunk=-1) == CHUNK
     assert f(cw=3) == WCH
     assert f(h=3000) == UNSUP                      # longer lines than the recomputed forward takes
+    assert f(n=700000, c=1, cw=1, h=2048, w=2048, chunk=1) == UNSUP   # four directions' workgroups overflow a grid
     assert f(ws=0) == NULLP
     assert f(gy=0) == NULLP
     assert f(dz=vp4(0x60000000, 0, 0x62000000, 0x63000000)) == NULLP
