@@ -350,9 +350,15 @@ def per_step_ms(step, n: int) -> list:
 
 def bench_backward(args, wl):
     """The backward leg: gspn_backward4 over the same inputs and a seeded
-    dL/dy ~ N(0, 1); the dominant kernel is the adjoint launch."""
+    dL/dy ~ N(0, 1); the dominant kernel is the adjoint launch.  With
+    --pass train a step is a training step instead: gspn_forward4 keeping
+    its fp32 states, then gspn_backward4 from those states (no recompute)."""
+    train = args.pass_ == "train"
     if wl.c_proxy:
         print("bench.py: the backward pass covers gspn_forward4 (no proxy projections)", file=sys.stderr)
+        sys.exit(2)
+    if train and wl.h <= 64 and wl.w <= 64:
+        print("bench.py: the forward keeps its states only for planes larger than 64 x 64", file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()
     G.lib()
@@ -363,13 +369,24 @@ def bench_backward(args, wl):
     gy = torch.randn(inp["x"].shape, generator=g, device="cuda", dtype=torch.float32).to(wl.torch_dtype)
     outs = (torch.empty_like(inp["x"]), [torch.empty_like(z) for z in inp["logits"]],
             [torch.empty_like(l) for l in inp["lam"]])
-    ws = G.backward4_workspace(inp["x"], wl.cw)
+    ws = G.backward4_workspace(inp["x"], wl.cw, with_states=train)
     merge = merge_weights(wl, args.merge)
     dmerge = torch.empty((4, wl.c_scan), dtype=torch.float32, device="cuda") if args.merge else None
+    fws = G.forward4_workspace(inp["x"], wl.cw) if train else None
+    states = G.states_buffer(inp["x"]) if train else None
+    y = torch.empty_like(inp["x"]) if train else None
 
-    def step(times=None):
+    def step(times=None, ftimes=None):
+        if train:
+            if ftimes is None:
+                G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=y, workspace=fws,
+                                merge=merge, states=states)
+            else:
+                _, ft = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=y,
+                                              workspace=fws, merge=merge, states=states)
+                ftimes.update(ft)
         return G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=wl.chunk, workspace=ws,
-                                out=outs, times=times, merge=merge, dmerge=dmerge)
+                                out=outs, times=times, merge=merge, dmerge=dmerge, states=states)
 
     for _ in range(args.warmup):
         step()
@@ -383,22 +400,31 @@ def bench_backward(args, wl):
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
-    print("bench: backward %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    print("bench: %s %.3f ms/step" % (args.pass_, ms), file=sys.stderr, flush=True)
     singles = per_step_ms(step, args.steps)
 
     reps = max(3, min(args.steps, 10))
     acc = {name: 0.0 for name in G.STAGES}
+    facc = {name: 0.0 for name in G.STAGES}
     for _ in range(reps):
         t = G.StageTimes()
-        step(times=t)
+        ft = {}
+        step(times=t, ftimes=ft if train else None)
         for name, v in t.as_dict().items():
             if name != "scan_kernel":
                 acc[name] += v["ms"] / reps
+        for name, v in ft.items():
+            if name != "scan_kernel":
+                facc[name] += v["ms"] / reps
     kernel_ms = acc["adjoint"]
     bpl = adjoint_launch_bytes(wl)
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
-    alg = backward_algorithmic_bytes(wl)
+    alg = backward_algorithmic_bytes(wl) + (algorithmic_bytes(wl) if train else 0)
     eff = alg / (ms * 1e-3) / 1e9
+    stages = {k: round(v, 4) for k, v in acc.items() if v > 0}
+    if train:
+        stages = dict([("forward_" + k, round(v, 4)) for k, v in facc.items() if v > 0] +
+                      [("backward_" + k, v) for k, v in stages.items()])
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle's backward on a sample", file=sys.stderr, flush=True)
@@ -406,17 +432,19 @@ def bench_backward(args, wl):
         cpu = cpu_baseline_planes(wl, inp, oracle, gy=gy, merge=merge)
     traffic, traffic_src = counter_traffic("adj4_kernel", wl)
     rec = {
-        "metric": "ms per 4-direction GSPN backward (dx, dlambda, dlogits%s); achieved HBM GB/s"
+        "metric": ("ms per 4-direction GSPN training step (forward keeping fp32 states, then backward: dx, "
+                   "dlambda, dlogits%s); achieved HBM GB/s" if train else
+                   "ms per 4-direction GSPN backward (dx, dlambda, dlogits%s); achieved HBM GB/s")
                   % (", dmerge" if args.merge else ""),
         "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded)",
-        "config": {"workload": wl.name, "pass": "backward", "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
+        "config": {"workload": wl.name, "pass": args.pass_, "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
                    "merge": "learnable" if args.merge else "sum"},
         "ms_median": round(singles[len(singles) // 2], 4), "ms_min": round(singles[0], 4),
         "effective_GBps": round(eff, 1), "effective_frac": round(eff / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
-        "stages_ms": {k: round(v, 4) for k, v in acc.items() if v > 0},
+        "stages_ms": stages,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": "adj4_kernel",
                      "kernel_ms": round(kernel_ms, 4), "launches_per_step": 1, "bytes_per_launch": bpl,
@@ -433,8 +461,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="profile", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "backward"),
-                    help="time the forward (default) or the backward (gradients for a seeded dL/dy)")
+    ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "backward", "train"),
+                    help="time the forward (default), the backward (gradients for a seeded dL/dy), or a "
+                         "training step (forward keeping its states, then the backward from them)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays (forward only)")
     ap.add_argument("--merge", action="store_true",
@@ -451,7 +480,7 @@ def main():
         copy_check(args.copy_check)
         return
     wl = WORKLOADS[args.workload]
-    if args.pass_ == "backward":
+    if args.pass_ in ("backward", "train"):
         bench_backward(args, wl)
         return
     torch.cuda.init()

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 6
+#define GSPN_ABI_VERSION 7
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -189,6 +189,19 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              linear in it), so it costs no extra pass.  4-byte aligned;
  *              y may not overlap it.
  *   y          [n][c][h][w] output; may not overlap any input.
+ *   states     NULL, or a device buffer of 4 * n*c*h*w fp32 values, 4-byte
+ *              aligned, overlapping neither y, an input nor the workspace
+ *              (else GSPN_ERR_MISALIGNED / GSPN_ERR_ALIASING): the four
+ *              directions' unweighted scans h_d in fp32, kept for
+ *              gspn_backward4, which then skips its own recompute.  Map d
+ *              starts at states + d*n*c*h*w and lies in direction d's scan
+ *              frame: [n][c][h][w] for T2B and B2T, [n][c][w][h] for L2R and
+ *              R2L.  It needs the workspace, lines of at most 2048
+ *              positions and planes larger than 64 x 64 in at least one
+ *              dimension (else GSPN_ERR_WORKSPACE / GSPN_ERR_UNSUPPORTED); y
+ *              is then merged from these fp32 maps, so for bf16 storage it
+ *              can differ from the y of a call without states in the last
+ *              bf16 place.
  *   workspace  optional device buffer of workspace_bytes bytes, 4-byte
  *              aligned.  NULL (or 0 bytes): the directions run one after
  *              another, the first writing y and the others adding to it, and
@@ -212,13 +225,14 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              across workgroups and runs the scan in bands of steps, one
  *              launch per band.  Its contents afterwards are unspecified.
  *              Planes of at most 64 x 64 take a one-pass path (x read once,
- *              y written once) with or without a workspace.  In all cases y
+ *              y written once) with or without a workspace, unless states
+ *              are wanted.  In all cases y
  *              is the same up to fp32 rounding order and, for bf16, rounding
  *              of the intermediates.
  */
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
-                          const void* const lam[4], const float* merge, void* y, void* workspace,
+                          const void* const lam[4], const float* merge, void* y, float* states, void* workspace,
                           int64_t workspace_bytes, int dtype, void* stream);
 
 /*
@@ -254,12 +268,14 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
 
 /*
  * gspn_backward4_workspace_bytes -- bytes of the gspn_backward4 workspace:
- * the four directions' forward states in fp32 (4 * n*c*h*w floats), five
- * maps of n*c*h*w elements of the storage type (x and dL/dy transposed into
- * the horizontal scan frame, three per-direction dx terms) and, for
- * channel-shared logits over more than one channel (cw == 1 < c), 4 * 3 *
- * n*h*w floats of gradient sums plus the four directions' normalised weights
- * as in gspn_forward4_workspace_bytes.  Returns -1 for invalid arguments.
+ * for channel-shared logits over more than one channel (cw == 1 < c), 4 * 3
+ * * n*h*w floats of gradient sums plus the four directions' normalised
+ * weights as in gspn_forward4_workspace_bytes; five maps of n*c*h*w
+ * elements of the storage type (x and dL/dy transposed into the horizontal
+ * scan frame, three per-direction dx terms), rounded up to a multiple of 4
+ * bytes; last, the four directions' forward states in fp32 (4 * n*c*h*w
+ * floats), which a call given the states does not need: it may pass 16 *
+ * n*c*h*w bytes less.  Returns -1 for invalid arguments.
  */
 int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype);
 
@@ -284,17 +300,23 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
  *                  sum_t <a_t, lam_t * x_t> (the same value for the linear
  *                  recurrence), accumulated in fp32 in an order that may vary
  *                  between calls.
- * workspace: required, gspn_backward4_workspace_bytes() bytes, 4-byte
- * aligned.  Outputs may overlap neither an input, the workspace nor each
- * other.  Lines may hold at most 2048 positions, and the four directions
- * together at most 2^31 - 1 (plane, chunk) pairs (else
- * GSPN_ERR_UNSUPPORTED).  The forward states are recomputed inside and kept
- * in fp32.
+ * states: NULL, or the fp32 states that gspn_forward4 wrote for the same
+ * inputs (layout there; planes larger than 64 x 64, else
+ * GSPN_ERR_UNSUPPORTED), 4-byte aligned, overlapping no output and not the
+ * workspace: the adjoint reads them instead of recomputing the forward.
+ * Without them the forward states are recomputed inside, in fp32 and with
+ * the same kernel, so both ways give the same gradients bit for bit.
+ * workspace: required, gspn_backward4_workspace_bytes() bytes (16 * n*c*h*w
+ * fewer with states), 4-byte aligned.  Outputs may overlap neither an input,
+ * the workspace nor each other.  Lines may hold at most 2048 positions, and
+ * the four directions together at most 2^31 - 1 (plane, chunk) pairs (else
+ * GSPN_ERR_UNSUPPORTED).
  */
 gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                            const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
-                           const void* gy, void* dx, void* const dlogits[4], void* const dlam[4], float* dmerge,
-                           void* workspace, int64_t workspace_bytes, int dtype, void* stream);
+                           const float* states, const void* gy, void* dx, void* const dlogits[4],
+                           void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes, int dtype,
+                           void* stream);
 
 /*
  * Stage timing of one forward call (measurement only).
@@ -342,8 +364,8 @@ typedef struct {
 
 gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* const logits[4],
-                                const void* const lam[4], const float* merge, void* y, void* workspace,
-                                int64_t workspace_bytes, int dtype, void* stream,
+                                const void* const lam[4], const float* merge, void* y, float* states,
+                                void* workspace, int64_t workspace_bytes, int dtype, void* stream,
                                 gspn_stage_times* times);
 
 gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
@@ -357,9 +379,9 @@ gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w
  * the forward recompute is reported as GSPN_STAGE_SCAN. */
 gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                                  const void* x, const void* const logits[4], const void* const lam[4],
-                                 const float* merge, const void* gy, void* dx, void* const dlogits[4],
-                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
-                                 int dtype, void* stream, gspn_stage_times* times);
+                                 const float* merge, const float* states, const void* gy, void* dx,
+                                 void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                                 int64_t workspace_bytes, int dtype, void* stream, gspn_stage_times* times);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);

@@ -364,7 +364,8 @@ hipError_t prenormalise(int64_t n, int64_t h, int64_t w, const void* const logit
 
 gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                           const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
-                          void* y, void* workspace, int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
+                          void* y, float* states, void* workspace, int64_t workspace_bytes, int dtype, void* stream,
+                          Timer* tm) {
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -388,12 +389,27 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (merge && !aligned(merge, 4)) return GSPN_ERR_MISALIGNED;
     if (merge && overlap(y, xb, merge, mgb)) return GSPN_ERR_ALIASING;
     const bool have_ws = workspace != nullptr && workspace_bytes > 0;
+    const int64_t sb = 4 * n * c * h * w * 4;  // four fp32 state maps
+    if (states) {
+        // the states come from the four-direction launch, which takes lines
+        // of at most 2048 positions and a workspace; planes of at most
+        // 64 x 64 (the plane-resident path's) are not supported
+        if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c, h, w, chunks) || gspn::plane4_supported(h, w))
+            return GSPN_ERR_UNSUPPORTED;
+        if (!have_ws) return GSPN_ERR_WORKSPACE;
+        if (!aligned(states, 4)) return GSPN_ERR_MISALIGNED;
+        if (overlap(states, sb, y, xb) || overlap(states, sb, x, xb)) return GSPN_ERR_ALIASING;
+        for (int d = 0; d < 4; ++d)
+            if (overlap(states, sb, logits[d], wb) || overlap(states, sb, lam[d], xb)) return GSPN_ERR_ALIASING;
+        if (merge && overlap(states, sb, merge, mgb)) return GSPN_ERR_ALIASING;
+    }
     if (have_ws) {
         const int64_t need = gspn_forward4_workspace_bytes(n, c, h, w, cw, dtype);
         if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
         if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
         if (overlap(workspace, need, y, xb) || overlap(workspace, need, x, xb)) return GSPN_ERR_ALIASING;
         if (merge && overlap(workspace, need, merge, mgb)) return GSPN_ERR_ALIASING;
+        if (states && overlap(workspace, need, states, sb)) return GSPN_ERR_ALIASING;
         for (int d = 0; d < 4; ++d)
             if (overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], xb))
                 return GSPN_ERR_ALIASING;
@@ -421,8 +437,8 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     }
 
     // Planes of at most 64 x 64: one pass over LDS-resident planes, whether
-    // or not a workspace is given.
-    if (gspn::plane4_supported(h, w)) {
+    // or not a workspace is given (unless the states are wanted).
+    if (gspn::plane4_supported(h, w) && !states) {
         if (tm) tm->scan_kernel = GSPN_SCAN_PLANE;
         return from_hip(timed(tm, GSPN_STAGE_SCAN, [&] {
             return gspn::launch_plane4(x, logits, lam, merge, y, n, c, cw, h, w, chunks, dtype, st);
@@ -471,6 +487,26 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].h = w;
         p[d].w = h;
         p[d].dir = d - 2;  // L2R runs like T2B, R2L like B2T, in the transposed frame
+    }
+
+    // With the states wanted: the four directions in one launch, each into
+    // its fp32 state map, then y merged from those maps.
+    if (states) {
+        const int64_t elems = n * c * h * w;
+        for (int d = 0; d < 4; ++d) {
+            p[d].out = states + d * elems;
+            p[d].odtype = GSPN_F32;
+            p[d].mscale = nullptr;  // the merge below applies the merge weights
+        }
+        int kind = GSPN_SCAN_FUSED4;
+        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        if (tm) tm->scan_kernel = kind;
+        return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
+            return gspn::launch_combine_states(y, states, states + elems, states + 2 * elems, states + 3 * elems,
+                                               n * c, static_cast<int>(h), static_cast<int>(w), dtype, st, merge,
+                                               c);
+        }));
     }
 
     // Concurrent path: the four directions in one launch, each into its own
@@ -561,7 +597,7 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
     if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
               [&] { return gspn::launch_project(n, c, h * w, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
-    const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, fws,
+    const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, nullptr, fws,
                                          need - 2 * pb, dtype, stream, tm);
     if (s4 != GSPN_OK) return s4;
     return from_hip(timed(tm, GSPN_STAGE_PROJECT_UP,
@@ -569,9 +605,10 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
 }
 
 gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len, const void* x,
-                          const void* const logits[4], const void* const lam[4], const float* merge, const void* gy,
-                          void* dx, void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
-                          int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
+                          const void* const logits[4], const void* const lam[4], const float* merge,
+                          const float* states, const void* gy, void* dx, void* const dlogits[4], void* const dlam[4],
+                          float* dmerge, void* workspace, int64_t workspace_bytes, int dtype, void* stream,
+                          Timer* tm) {
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -584,7 +621,9 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     for (int d = 0; d < 4; ++d)
         if (!logits[d] || !lam[d] || !dlogits[d] || !dlam[d]) return GSPN_ERR_NULL_POINTER;
     const size_t es = elem_size(dtype);
-    const int64_t need = gspn_backward4_workspace_bytes(n, c, h, w, cw, dtype);
+    const int64_t hb = n * c * h * w * 4;  // bytes of one fp32 state map
+    // given the states, the workspace's last part (room for them) is not needed
+    const int64_t need = gspn_backward4_workspace_bytes(n, c, h, w, cw, dtype) - (states ? 4 * hb : 0);
     if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
     if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
     if (!aligned(x, es) || !aligned(gy, es) || !aligned(dx, es)) return GSPN_ERR_MISALIGNED;
@@ -610,6 +649,14 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
             return GSPN_ERR_ALIASING;
     }
     if (overlap(workspace, need, x, xb) || overlap(workspace, need, gy, xb)) return GSPN_ERR_ALIASING;
+    if (states) {
+        if (gspn::plane4_supported(h, w)) return GSPN_ERR_UNSUPPORTED;  // as in gspn_forward4
+        if (!aligned(states, 4)) return GSPN_ERR_MISALIGNED;
+        if (overlap(workspace, need, states, 4 * hb)) return GSPN_ERR_ALIASING;
+        for (int i = 0; i < 9; ++i)
+            if (overlap(outs[i], ob[i], states, 4 * hb)) return GSPN_ERR_ALIASING;
+        if (dmerge && overlap(dmerge, 4 * c * 4, states, 4 * hb)) return GSPN_ERR_ALIASING;
+    }
     const int64_t mgb = 4 * c * 4;  // merge weights and their gradient, fp32 [4][c]
     if ((merge && !aligned(merge, 4)) || (dmerge && !aligned(dmerge, 4))) return GSPN_ERR_MISALIGNED;
     if (merge) {
@@ -629,27 +676,29 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     const hipStream_t st = as_stream(stream);
 
     // Workspace: [fp32 logit-gradient sums and normalised weights of the four
-    // directions (shared logits only)][fp32 forward states H0..H3][x^T][gy^T]
-    // [dx terms D1..D3].
+    // directions (shared logits only)][x^T][gy^T][dx terms D1..D3][fp32
+    // forward states H0..H3, unless the caller passes them].
     // The states stay fp32 for bf16 storage too: the logit gradient takes
     // differences of neighbouring states, which bf16 rounding would swamp.
     const bool shared = cw == 1 && c > 1;
     const int64_t zsum = 3 * n * h * w;  // floats per direction
-    const int64_t hb = n * c * h * w * 4;  // bytes of one fp32 state map
     char* ws = static_cast<char*>(workspace);
     float* sums = reinterpret_cast<float*>(ws);
-    char* hs[4];
     const int64_t wdir = n * h * w * (dtype == GSPN_F32 ? 3 * 4 : 4);  // normalised weight bytes per direction
     char* wnorm = ws + 4 * zsum * 4;
-    hs[0] = ws + (shared ? 4 * zsum * 4 + 4 * wdir : 0);
-    for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
-    char* xt = hs[3] + hb;
+    char* xt = ws + (shared ? 4 * zsum * 4 + 4 * wdir : 0);
     char* gt = xt + xb;
     char* dterm[4];
     dterm[0] = static_cast<char*>(dx);
     dterm[1] = gt + xb;
     dterm[2] = dterm[1] + xb;
     dterm[3] = dterm[2] + xb;
+    // the recomputed states after the five storage-type maps, rounded up to
+    // 4 bytes (the sums and weights before them are whole floats)
+    char* hs[4];
+    const int64_t hoff = ((dterm[3] - ws) + xb + 3) / 4 * 4;
+    hs[0] = states ? reinterpret_cast<char*>(const_cast<float*>(states)) : ws + hoff;
+    for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
     const int H = static_cast<int>(h);
     const int W = static_cast<int>(w);
     if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] { return gspn::launch_transpose(x, xt, n * c, H, W, dtype, st); }) !=
@@ -680,12 +729,15 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].wdtype = dtype;
         p[d].odtype = GSPN_F32;
     }
-    // channel-shared logits: normalised once, as in the forward
-    if (shared && prenormalise(n, h, w, logits, wnorm, wdir, dtype, st, tm, p) != hipSuccess) return GSPN_ERR_HIP;
-    int kind = GSPN_SCAN_FUSED4;
-    if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
-        return GSPN_ERR_HIP;
-    if (tm) tm->scan_kernel = kind;
+    if (!states) {
+        // channel-shared logits: normalised once, as in the forward
+        if (shared && prenormalise(n, h, w, logits, wnorm, wdir, dtype, st, tm, p) != hipSuccess)
+            return GSPN_ERR_HIP;
+        int kind = GSPN_SCAN_FUSED4;
+        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        if (tm) tm->scan_kernel = kind;
+    }
     if (shared &&
         timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(sums, 4 * zsum, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
@@ -741,21 +793,21 @@ extern "C" {
 
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
-                          const void* const lam[4], const float* merge, void* y, void* workspace,
+                          const void* const lam[4], const float* merge, void* y, float* states, void* workspace,
                           int64_t workspace_bytes, int dtype, void* stream) {
-    return forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, workspace, workspace_bytes, dtype,
-                         stream, nullptr);
+    return forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, states, workspace, workspace_bytes,
+                         dtype, stream, nullptr);
 }
 
 gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* const logits[4],
-                                const void* const lam[4], const float* merge, void* y, void* workspace,
-                                int64_t workspace_bytes, int dtype, void* stream,
+                                const void* const lam[4], const float* merge, void* y, float* states,
+                                void* workspace, int64_t workspace_bytes, int dtype, void* stream,
                                 gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
-    const gspn_status s = forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, workspace,
+    const gspn_status s = forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, states, workspace,
                                         workspace_bytes, dtype, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
@@ -796,10 +848,12 @@ gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w
 int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype) {
     if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
     const int64_t elems = checked_product({n, c, h, w});
-    // x^T, gy^T and three dx terms in the storage type; four fp32 state maps;
-    // for channel-shared logits over several channels the gradient sums and
-    // the normalised weights of the recomputed forward
-    const int64_t maps = 5 * elems * static_cast<int64_t>(elem_size(dtype)) + 4 * elems * 4;
+    // x^T, gy^T and three dx terms in the storage type, rounded up to 4
+    // bytes; four fp32 state maps (last, so that a caller passing the states
+    // may give that much less); for channel-shared logits over several
+    // channels the gradient sums and the normalised weights of the recomputed
+    // forward (first)
+    const int64_t maps = (5 * elems * static_cast<int64_t>(elem_size(dtype)) + 3) / 4 * 4 + 4 * elems * 4;
     const int64_t nhw = checked_product({n, h, w});
     const int64_t shared = (cw == 1 && c > 1) ? 4 * 3 * nhw * 4 + 4 * nhw * (dtype == GSPN_F32 ? 3 * 4 : 4) : 0;
     return shared + maps;
@@ -807,22 +861,23 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
 
 gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                            const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
-                           const void* gy, void* dx, void* const dlogits[4], void* const dlam[4], float* dmerge,
-                           void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
-    return backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, gy, dx, dlogits, dlam, dmerge, workspace,
-                         workspace_bytes, dtype, stream, nullptr);
+                           const float* states, const void* gy, void* dx, void* const dlogits[4],
+                           void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes, int dtype,
+                           void* stream) {
+    return backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, states, gy, dx, dlogits, dlam, dmerge,
+                         workspace, workspace_bytes, dtype, stream, nullptr);
 }
 
 gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                                  const void* x, const void* const logits[4], const void* const lam[4],
-                                 const float* merge, const void* gy, void* dx, void* const dlogits[4],
-                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
-                                 int dtype, void* stream, gspn_stage_times* times) {
+                                 const float* merge, const float* states, const void* gy, void* dx,
+                                 void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                                 int64_t workspace_bytes, int dtype, void* stream, gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
-    const gspn_status s = backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, gy, dx, dlogits, dlam,
-                                        dmerge, workspace, workspace_bytes, dtype, stream, &tm);
+    const gspn_status s = backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, states, gy, dx, dlogits,
+                                        dlam, dmerge, workspace, workspace_bytes, dtype, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }

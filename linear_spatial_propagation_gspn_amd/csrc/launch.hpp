@@ -74,6 +74,13 @@ hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3
                           int Cc, int accumulate, int dtype, hipStream_t stream, const float* merge = nullptr,
                           int64_t nch = 1);
 
+// y[p][r][c] = ((m2 s2[p][c][r] + m3 s3[p][c][r]) + m0 s0[p][r][c]) + m1 s1[p][r][c]:
+// the same merge from four fp32 state maps (s2, s3 in the transposed frame),
+// y in the storage type.
+hipError_t launch_combine_states(void* y, const float* s0, const float* s1, const float* s2, const float* s3,
+                                 int64_t planes, int R, int Cc, int dtype, hipStream_t stream,
+                                 const float* merge = nullptr, int64_t nch = 1);
+
 // out_dtype: storage type of w_out (-1: the same as dtype; kF32 is allowed
 // for bf16 logits).
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,

@@ -8,6 +8,8 @@
 // 16-byte vector (where the shapes allow) within a run of 64 consecutive
 // elements along the row of the tensor it touches, and the transpose happens
 // in LDS (rows padded by one element so the column reads hit different banks).
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -145,18 +147,20 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict
 }
 
 // For planes of R x Cc in the array frame:
-//   y[p][r][c] = ((m2 z2[p][c][r] + m3 z3[p][c][r]) + m0 y[p][r][c] (if accumulate)) + m1 a[p][r][c]
-// where a, z2, z3 may each be absent (NULL) and z2, z3 are in the transposed
-// frame (Cc x R planes); m0..m3 are the learnable merge weights merge[k][ch]
-// of the plane's channel ch = p % nch, or 1 without merge weights.  Every
+//   y[p][r][c] = ((m2 z2[p][c][r] + m3 z3[p][c][r]) + m0 b[p][r][c]) + m1 a[p][r][c]
+// where b is y itself (accumulate), a separate source y0, or absent; a, z2,
+// z3 may each be absent (NULL) and z2, z3 are in the transposed frame
+// (Cc x R planes); m0..m3 are the learnable merge weights merge[k][ch] of
+// the plane's channel ch = p % nch, or 1 without merge weights.  The sources
+// other than y are of type TS (the storage type, or fp32 states).  Every
 // source is read into the LDS tile with row-vector accesses of its own
 // frame; y is read completely before it is written, so it may be updated in
 // place.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const T* __restrict__ a,
-                                                           const T* __restrict__ z2, const T* __restrict__ z3,
-                                                           int R, int Cc, int accumulate, int vec_y, int vec_z,
-                                                           const float* __restrict__ merge, int64_t nch) {
+template <typename T, typename TS>
+__global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const TS* __restrict__ y0, const TS* __restrict__ a,
+                                                           const TS* __restrict__ z2, const TS* __restrict__ z3,
+                                                           int R, int Cc, int accumulate, int vec_y, int vec_s,
+                                                           int vec_z, const float* __restrict__ merge, int64_t nch) {
     __shared__ float tile[kTile][kTile + 1];
     const TileIndex ti = tile_of(blockIdx.x, R, Cc);
     const int64_t plane = static_cast<int64_t>(R) * Cc;
@@ -167,24 +171,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const T* __rest
         for (int k = 0; k < 4; ++k) m[k] = merge[k * nch + ch];
     }
     bool any = false;
-    auto add_t = [&](const T* z, float wt) {  // transposed source: its row c is column c of the tile
+    auto add_t = [&](const TS* z, float wt) {  // transposed source: its row c is column c of the tile
         if (any) __syncthreads();
         const bool first = !any;
-        TileIO<T>::template read<GSPN_COMBINE_NT != 0>(z + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_z,
+        TileIO<TS>::template read<GSPN_COMBINE_NT != 0>(z + ti.plane * plane, Cc, R, ti.c0, ti.r0, vec_z,
                         [&](int c, int r, float v) { tile[r][c] = first ? wt * v : tile[r][c] + wt * v; });
         any = true;
     };
-    auto add_a = [&](const T* src, float wt) {  // array-frame source
+    auto add_a = [&](const auto* src, int vec, float wt) {  // array-frame source (y itself or a TS source)
+        using E = std::remove_cv_t<std::remove_pointer_t<decltype(src)>>;
         if (any) __syncthreads();
         const bool first = !any;
-        TileIO<T>::template read<GSPN_COMBINE_NT != 0>(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
+        TileIO<E>::template read<GSPN_COMBINE_NT != 0>(src + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec,
                         [&](int r, int c, float v) { tile[r][c] = first ? wt * v : tile[r][c] + wt * v; });
         any = true;
     };
     if (z2) add_t(z2, m[2]);
     if (z3) add_t(z3, m[3]);
-    if (accumulate) add_a(y, m[0]);
-    if (a) add_a(a, m[1]);
+    if (y0) add_a(y0, vec_s, m[0]);
+    else if (accumulate) add_a(static_cast<const T*>(y), vec_y, m[0]);
+    if (a) add_a(a, vec_s, m[1]);
     __syncthreads();
     TileIO<T>::template write<GSPN_COMBINE_NT != 0>(y + ti.plane * plane, R, Cc, ti.r0, ti.c0, vec_y,
                                                     [&](int r, int c, const T*) { return any ? tile[r][c] : 0.0f; });
@@ -218,16 +224,36 @@ hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3
                           int Cc, int accumulate, int dtype, hipStream_t stream, const float* merge, int64_t nch) {
     const dim3 grid(static_cast<unsigned>(tiles_for(planes, R, Cc)));
     const int vw = dtype == kF32 ? 4 : 8;
-    const int vy = (Cc % vw == 0) && aligned16(y) && (!a || aligned16(a));
+    const int vy = (Cc % vw == 0) && aligned16(y);
+    const int vs = vy && (!a || aligned16(a));
     const int vz = (R % vw == 0) && (!z2 || aligned16(z2)) && (!z3 || aligned16(z3));
     if (dtype == kF32) {
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
-                           static_cast<const float*>(a), static_cast<const float*>(z2),
-                           static_cast<const float*>(z3), R, Cc, accumulate, vy, vz, merge, nch);
+        hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
+                           static_cast<const float*>(nullptr), static_cast<const float*>(a),
+                           static_cast<const float*>(z2), static_cast<const float*>(z3), R, Cc, accumulate, vs, vs,
+                           vz, merge, nch);
     } else {
-        hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, static_cast<bf16_t*>(y),
+        hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), grid, dim3(kThreads), 0, stream,
+                           static_cast<bf16_t*>(y), static_cast<const bf16_t*>(nullptr),
                            static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(z2),
-                           static_cast<const bf16_t*>(z3), R, Cc, accumulate, vy, vz, merge, nch);
+                           static_cast<const bf16_t*>(z3), R, Cc, accumulate, vs, vs, vz, merge, nch);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_states(void* y, const float* s0, const float* s1, const float* s2, const float* s3,
+                                 int64_t planes, int R, int Cc, int dtype, hipStream_t stream, const float* merge,
+                                 int64_t nch) {
+    const dim3 grid(static_cast<unsigned>(tiles_for(planes, R, Cc)));
+    const int vy = (Cc % (dtype == kF32 ? 4 : 8) == 0) && aligned16(y);
+    const int vs = (Cc % 4 == 0) && aligned16(s0) && aligned16(s1);
+    const int vz = (R % 4 == 0) && aligned16(s2) && aligned16(s3);
+    if (dtype == kF32) {
+        hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
+                           s0, s1, s2, s3, R, Cc, 0, vy, vs, vz, merge, nch);
+    } else {
+        hipLaunchKernelGGL((combine_kernel<bf16_t, float>), grid, dim3(kThreads), 0, stream,
+                           static_cast<bf16_t*>(y), s0, s1, s2, s3, R, Cc, 0, vy, vs, vz, merge, nch);
     }
     return hipGetLastError();
 }

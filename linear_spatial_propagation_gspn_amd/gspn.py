@@ -95,7 +95,7 @@ def lib() -> ctypes.CDLL:
                                               ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, i64, ci, vp]
             h.gspn_proxy_forward4.restype = ci
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
-                                        ctypes.POINTER(vp), vp, vp, vp, i64, ci, vp]
+                                        ctypes.POINTER(vp), vp, vp, vp, vp, i64, ci, vp]
             h.gspn_forward4_timed.argtypes = h.gspn_forward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_forward4_timed.restype = ci
             h.gspn_proxy_forward4_timed.argtypes = h.gspn_proxy_forward4.argtypes + [ctypes.POINTER(StageTimes)]
@@ -106,7 +106,7 @@ def lib() -> ctypes.CDLL:
             h.gspn_backward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
             h.gspn_backward4_workspace_bytes.restype = i64
             h.gspn_backward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
-                                         vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, i64, ci, vp]
+                                         vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, i64, ci, vp]
             h.gspn_backward4.restype = ci
             h.gspn_backward4_timed.argtypes = h.gspn_backward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_backward4_timed.restype = ci
@@ -277,7 +277,29 @@ def _merge_ptr(merge, c: int, device, name: str = "merge"):
     return _ptr(merge)
 
 
-def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None):
+def states_buffer(x: torch.Tensor) -> torch.Tensor:
+    """A buffer for the four directions' fp32 forward states of inputs shaped
+    like x (see gspn_forward4's ``states``)."""
+    return torch.empty(4 * x.numel(), dtype=torch.float32, device=x.device)
+
+
+def state_map(states: torch.Tensor, d: int, x_shape: tuple) -> torch.Tensor:
+    """Direction d's map in a states buffer: [N][C][S_d][L_d] in its scan
+    frame ([N][C][H][W] for T2B / B2T, [N][C][W][H] for L2R / R2L)."""
+    n, c, h, w = x_shape
+    S, L = frame_shape(d, h, w)
+    e = n * c * h * w
+    return states.view(-1)[d * e:(d + 1) * e].view(n, c, S, L)
+
+
+def _states_ptr(states, x):
+    if states is None:
+        return None
+    _check(states, "states", (4 * x.numel(),), torch.float32, x.device)
+    return _ptr(states)
+
+
+def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None, states=None):
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
@@ -297,7 +319,8 @@ def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None):
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
     mp = _merge_ptr(merge, c, x.device)
-    args = (n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, mp, _ptr(out), ws_ptr, ws_bytes, _dtype_code(x),
+    sp = _states_ptr(states, x)
+    args = (n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, mp, _ptr(out), sp, ws_ptr, ws_bytes, _dtype_code(x),
             _stream(x.device))
     if times is None:
         _raise(lib().gspn_forward4(*args), "gspn_forward4")
@@ -308,23 +331,32 @@ def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None):
 
 def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                   chunk_len: int = 0, out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None) -> torch.Tensor:
+                  workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None,
+                  states: torch.Tensor | bool | None = None):
     """Four-direction propagation; logits[d] / lams[d] in direction d's scan
     frame.  The directions are summed, or with ``merge`` (fp32 [4][C] on the
     device) weighted per direction and channel.  ``workspace`` (see
     forward4_workspace) lets the library run the four directions
-    concurrently when that pays."""
-    return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge)
+    concurrently when that pays.  ``states`` (True, or a buffer from
+    states_buffer) also keeps the four directions' fp32 scans for
+    gspn_backward4 (needs the workspace); the call then returns (out,
+    states)."""
+    if states is True:
+        states = states_buffer(x)
+    if states is None or states is False:
+        return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge)
+    return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge, states), states
 
 
 def gspn_forward4_timed(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                         chunk_len: int = 0, out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None,
-                        merge: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+                        merge: torch.Tensor | None = None,
+                        states: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
     """gspn_forward4 with HIP events around every launch; returns (out,
     {stage: {"ms", "launches"}}).  Waits for the stream to reach its end."""
     times = StageTimes()
-    out = _forward4(x, logits, lams, chunk_len, out, workspace, times, merge)
+    out = _forward4(x, logits, lams, chunk_len, out, workspace, times, merge, states)
     return out, times.as_dict()
 
 
@@ -390,25 +422,31 @@ def gspn_proxy_forward4_timed(x: torch.Tensor, w_down: torch.Tensor, w_up: torch
     return out, times.as_dict()
 
 
-def backward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
-    """A workspace buffer (uint8 tensor on x's device) for gspn_backward4."""
+def backward4_workspace(x: torch.Tensor, cw: int, with_states: bool = False) -> torch.Tensor:
+    """A workspace buffer (uint8 tensor on x's device) for gspn_backward4;
+    with_states: for calls given the forward states (16 * x.numel() bytes
+    smaller)."""
     n, c, h, w = x.shape
     nbytes = int(lib().gspn_backward4_workspace_bytes(n, c, h, w, cw, _dtype_code(x)))
     if nbytes < 0:
         raise ValueError("invalid shape for a gspn_backward4 workspace")
+    if with_states:
+        nbytes -= 16 * x.numel()
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
 
 
 def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                    gy: torch.Tensor, chunk_len: int = 0, workspace: torch.Tensor | None = None,
                    out: tuple | None = None, times: StageTimes | None = None,
-                   merge: torch.Tensor | None = None, dmerge: torch.Tensor | bool | None = None) -> tuple:
+                   merge: torch.Tensor | None = None, dmerge: torch.Tensor | bool | None = None,
+                   states: torch.Tensor | None = None) -> tuple:
     """Gradients of gspn_forward4 (with the same ``merge``) for dL/dy = gy:
     returns (dx, [dlogits_d], [dlam_d]) in the inputs' layouts, and also the
     merge weights' gradient (fp32 [4][C]) as a fourth element when ``merge``
     is given or ``dmerge`` is (a tensor to fill, or True).  ``out`` may
     supply the first three; ``times`` (a StageTimes) selects
-    gspn_backward4_timed and receives the stage durations."""
+    gspn_backward4_timed and receives the stage durations; ``states`` (from
+    gspn_forward4) spares the recompute of the forward."""
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
@@ -433,13 +471,14 @@ def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
         dmerge = torch.empty((4, c), dtype=torch.float32, device=x.device)
     mp = _merge_ptr(merge, c, x.device)
     dmp = _merge_ptr(dmerge, c, x.device, "dmerge") if want_dm else None
+    sp = _states_ptr(states, x)
     if workspace is None:
-        workspace = backward4_workspace(x, cw)
+        workspace = backward4_workspace(x, cw, with_states=states is not None)
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
     vp4 = ctypes.c_void_p * 4
     args = (n, c, h, w, cw, int(chunk_len), _ptr(x), vp4(*[z.data_ptr() for z in logits]),
-            vp4(*[l.data_ptr() for l in lams]), mp, _ptr(gy), _ptr(dx), vp4(*[t.data_ptr() for t in dz]),
+            vp4(*[l.data_ptr() for l in lams]), mp, sp, _ptr(gy), _ptr(dx), vp4(*[t.data_ptr() for t in dz]),
             vp4(*[t.data_ptr() for t in dl]), dmp, _ptr(workspace), workspace.numel() * workspace.element_size(),
             _dtype_code(x), _stream(x.device))
     if times is None:
@@ -453,32 +492,42 @@ class _Forward4(torch.autograd.Function):
     """gspn_forward4 as an autograd node whose backward is gspn_backward4."""
 
     @staticmethod
-    def forward(ctx, chunk_len, has_merge, x, merge, *tensors):
+    def forward(ctx, chunk_len, has_merge, keep, x, merge, *tensors):
         logits, lams = list(tensors[:4]), list(tensors[4:])
         cw = logits[0].shape[1]
-        y = gspn_forward4(x, logits, lams, chunk_len=chunk_len, workspace=forward4_workspace(x, cw),
-                          merge=merge if has_merge else None)
+        m = merge if has_merge else None
+        states = states_buffer(x) if keep else torch.empty(0, device=x.device)
+        y = gspn_forward4(x, logits, lams, chunk_len=chunk_len, workspace=forward4_workspace(x, cw), merge=m,
+                          states=states if keep else None)
+        if keep:
+            y = y[0]
         ctx.chunk_len = chunk_len
         ctx.has_merge = has_merge
-        ctx.save_for_backward(x, merge, *tensors)
+        ctx.keep = keep
+        ctx.save_for_backward(x, merge, states, *tensors)
         return y
 
     @staticmethod
     def backward(ctx, gy):
-        x, merge, *tensors = ctx.saved_tensors
+        x, merge, states, *tensors = ctx.saved_tensors
         logits, lams = tensors[:4], tensors[4:]
         res = gspn_backward4(x, logits, lams, gy.to(x.dtype).contiguous(), chunk_len=ctx.chunk_len,
-                             merge=merge if ctx.has_merge else None)
+                             merge=merge if ctx.has_merge else None, states=states if ctx.keep else None)
         dx, dz, dl = res[0], res[1], res[2]
         dm = res[3] if ctx.has_merge else None
-        return (None, None, dx, dm, *dz, *dl)
+        return (None, None, None, dx, dm, *dz, *dl)
 
 
 def gspn4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor], chunk_len: int = 0,
-          merge: torch.Tensor | None = None) -> torch.Tensor:
+          merge: torch.Tensor | None = None, keep_states: bool = False) -> torch.Tensor:
     """The four-direction propagation as a differentiable op: gspn_forward4
     forward, gspn_backward4 for the gradients of x, the logits, the lambdas
-    and (if given) the merge weights."""
+    and (if given) the merge weights.  keep_states: the forward keeps its
+    fp32 scans (16 bytes per element of x, held until the backward) so the
+    backward need not recompute them; only for planes larger than 64 x 64
+    (smaller ones recompute them either way)."""
     has_merge = merge is not None
     m = merge if has_merge else torch.empty(0, device=x.device)
-    return _Forward4.apply(int(chunk_len), has_merge, x, m, *logits, *lams)
+    h, w = x.shape[-2:]
+    keep = bool(keep_states) and (h > 64 or w > 64)
+    return _Forward4.apply(int(chunk_len), has_merge, keep, x, m, *logits, *lams)

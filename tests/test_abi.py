@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 6
+    assert lib.gspn_abi_version() == 7
     for code in range(12):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -108,8 +108,8 @@ def test_forward4_validation(lib):
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
     assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 5) == -1
 
-    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, m=None, y=D_, ws=None, wsb=0, dt=0):
-        return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, m, y, ws, wsb, dt, None)
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, m=None, y=D_, s=None, ws=None, wsb=0, dt=0):
+        return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, m, y, s, ws, wsb, dt, None)
 
     assert f(dt=3) == DTYPE
     assert f(cw=3) == WCH
@@ -128,6 +128,22 @@ def test_forward4_validation(lib):
     assert f(m=M + 2) == MISAL
     assert f(m=D_ + 8) == ALIAS                      # y overlaps the merge weights
     assert f(m=W + 16, ws=W, wsb=wsb) == ALIAS       # the workspace overlaps them
+    S = 0x6a000000                                   # fp32 forward states, 4 maps of n*c*h*w
+    assert f(s=S, ws=W, wsb=wsb) == UNSUP            # not for planes of at most 64 x 64
+    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 80, 2, 0)
+    f0 = f
+
+    def f(**kw):
+        kw.setdefault("w", 80)
+        return f0(**kw)
+
+    assert f(s=S) == WSPACE                          # states need the workspace
+    assert f(s=S, ws=W, wsb=wsb, h=3000) == UNSUP    # and lines the four-direction launch takes
+    assert f(s=S + 2, ws=W, wsb=wsb) == MISAL
+    assert f(s=D_ - 16, ws=W, wsb=wsb) == ALIAS      # states overlap y
+    assert f(s=C_ + 8, ws=W, wsb=wsb) == ALIAS       # states overlap lam
+    assert f(s=W + 64, ws=W, wsb=wsb) == ALIAS       # states in the workspace
+    assert f(s=M, m=M + 64, ws=W, wsb=wsb) == ALIAS  # states overlap the merge weights
     assert f(n=0, x=0, z=None, l=None, y=0) == OK
 
 
@@ -231,7 +247,7 @@ def test_timed_variants_validate_like_untimed(lib):
         t.ms[i], t.launches[i] = 7.0, 7
 
     def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, y=D_, dt=0, times=ctypes.byref(t)):
-        return lib.gspn_forward4_timed(n, c, h, w, cw, chunk, x, zs, ls, None, y, None, 0, dt, None, times)
+        return lib.gspn_forward4_timed(n, c, h, w, cw, chunk, x, zs, ls, None, y, None, None, 0, dt, None, times)
 
     assert f(times=None) == NULLP
     assert f(dt=3) == DTYPE
@@ -269,9 +285,9 @@ def test_backward4_validation(lib):
                                                                    5 * 3 * 64 * 2)
     assert lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
 
-    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, m=None, gy=GY, dx=DX, dz=dzs, dl=dls, dm=None, ws=WS, wsb=need,
-          dt=0):
-        return lib.gspn_backward4(n, c, h, w, cw, chunk, x, zs, ls, m, gy, dx, dz, dl, dm, ws, wsb, dt, None)
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, m=None, s=None, gy=GY, dx=DX, dz=dzs, dl=dls, dm=None, ws=WS,
+          wsb=need, dt=0):
+        return lib.gspn_backward4(n, c, h, w, cw, chunk, x, zs, ls, m, s, gy, dx, dz, dl, dm, ws, wsb, dt, None)
 
     assert f(dt=2) == DTYPE
     assert f(chunk=-1) == CHUNK
@@ -293,9 +309,21 @@ def test_backward4_validation(lib):
     assert f(dm=DX + 8) == ALIAS                    # dmerge on dx
     assert f(dm=WS + 8) == ALIAS                    # dmerge in the workspace
     assert f(m=dls[2] + 4) == ALIAS                 # an output on the merge weights
+    S = 0x6a000000                                  # fp32 forward states, 4 maps of n*c*h*w
+    assert f(s=S) == UNSUP                          # not for planes of at most 64 x 64
+    need80 = lib.gspn_backward4_workspace_bytes(1, 2, 8, 80, 2, 0)
+    smaller = need80 - 16 * 2 * 8 * 80              # the states' room in the workspace is not needed
+    assert f(w=80, wsb=smaller) == WSPACE           # without states it is
+    assert f(w=80, s=S, wsb=smaller - 1) == WSPACE
+    assert f(w=80, s=S + 2, wsb=smaller) == MISAL
+    assert f(w=80, s=WS + smaller - 4, wsb=smaller) == ALIAS   # states in the workspace
+    assert f(w=80, s=DX - 16, wsb=smaller) == ALIAS       # dx on the states
+    assert f(w=80, s=dzs[3] + 4, wsb=smaller) == ALIAS    # dlogits on the states
+    assert f(w=80, s=0x6b000000, dm=0x6b000000 + 8, wsb=smaller) == ALIAS   # dmerge on the states
     assert f(n=0, x=0, gy=0, dx=0, dz=None, dl=None, ws=0) == OK
     t = G.StageTimes()
-    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, GY, DX, dzs, dls, None, WS, need, 0, None,
+    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, None, GY, DX, dzs, dls, None, WS, need, 0, None,
                                     None) == NULLP
-    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, GY, DX, dzs, dls, None, WS, need - 1, 0, None,
+    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, None, GY, DX, dzs, dls, None, WS, need - 1, 0,
+                                    None,
                                     ctypes.byref(t)) == WSPACE
