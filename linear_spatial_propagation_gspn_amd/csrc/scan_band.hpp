@@ -134,8 +134,10 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 
     uint32_t sT = line_of(t0) * rowT;
     // lambda_j x_j + c for the bf16 pair (j, j + 1) in word e: one bf16 dot
-    // product with the other half of x masked to 0 (exact products, one
-    // rounding, as fmaf)
+    // product with the other half of x masked to 0.  Its fp32 result can
+    // differ from fmaf's by one unit in the last place (measured on gfx950:
+    // in 2-18% of random operands), far below the bf16 rounding of the
+    // stored h.
     auto lamx = [&](auto slot, int j, float c) {
         constexpr int s = decltype(slot)::value;
         const uint32_t xw = sx[s][j >> 1] & ((j & 1) ? 0xffff0000u : 0x0000ffffu);
