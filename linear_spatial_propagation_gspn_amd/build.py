@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libgspn.so")
 SOURCES = ["api.cpp", "scan.hip", "scan_f32_vert.hip", "scan_f32_horiz.hip", "scan_bf16_vert.hip",
            "scan_bf16_horiz.hip", "scan_bf16pair_vert.hip", "scan_bf16pair_horiz.hip", "scan4_f32.hip",
            "scan4_bf16.hip", "scan4_bf16pair.hip", "elementwise.hip", "transpose.hip", "project.hip",
-           "plane4.hip", "backward.hip"]
+           "plane4.hip", "backward.hip", "adjplane.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -701,6 +701,58 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
     const int H = static_cast<int>(h);
     const int W = static_cast<int>(w);
+
+    // Planes of at most 64 x 64 (recomputed states only): the four
+    // directions' states in one pass over LDS-resident planes, then their
+    // adjoints likewise, x, gy and dx in the array frame: no transposes and
+    // no per-direction dx terms.
+    if (gspn::plane4_supported(h, w) && !states) {
+        if (shared &&
+            timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(sums, 4 * zsum, st); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        if (dmerge &&
+            timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(dmerge, 4 * c, st); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        float* hf[4];
+        for (int d = 0; d < 4; ++d) hf[d] = reinterpret_cast<float*>(hs[d]);
+        if (timed(tm, GSPN_STAGE_SCAN, [&] {
+                return gspn::launch_plane4_states(x, logits, lam, hf, n, c, cw, h, w, chunks, dtype, st);
+            }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        if (tm) tm->scan_kernel = GSPN_SCAN_PLANE;
+        gspn::AdjPlaneParams ap;
+        ap.x = x;
+        ap.g = gy;
+        for (int d = 0; d < 4; ++d) {
+            ap.z[d] = logits[d];
+            ap.lam[d] = lam[d];
+            ap.hs[d] = hf[d];
+            ap.dlam[d] = dlam[d];
+            ap.dz[d] = shared ? static_cast<void*>(sums + d * zsum) : dlogits[d];
+            ap.chunk[d] = chunks[d];
+        }
+        ap.dx = dx;
+        ap.merge = merge;
+        ap.dmerge = dmerge;
+        ap.n = n;
+        ap.c = c;
+        ap.cw = cw;
+        ap.h = h;
+        ap.w = w;
+        ap.shared = shared ? 1 : 0;
+        ap.dtype = dtype;
+        if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjplane(ap, st); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        if (shared) {
+            for (int d = 0; d < 4; ++d)
+                if (timed(tm, GSPN_STAGE_REDUCE, [&] {
+                        return gspn::launch_store_sums(sums + d * zsum, dlogits[d], zsum, dtype, st);
+                    }) != hipSuccess)
+                    return GSPN_ERR_HIP;
+        }
+        return GSPN_OK;
+    }
+
     if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] { return gspn::launch_transpose(x, xt, n * c, H, W, dtype, st); }) !=
             hipSuccess ||
         timed(tm, GSPN_STAGE_TRANSPOSE, [&] { return gspn::launch_transpose(gy, gt, n * c, H, W, dtype, st); }) !=

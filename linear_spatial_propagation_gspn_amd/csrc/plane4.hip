@@ -48,6 +48,7 @@ struct Plane4K {
     int W;
     int K[4];  // steps per chunk of each direction (S_d for one chunk)
     const float* merge;  // learnable merge weights [4][c], or null for the plain sum
+    float* states[4];    // STATES: direction d's fp32 scan h_d in its scan frame [planes][S_d][L_d]
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -137,7 +138,9 @@ __device__ __forceinline__ void store_plane(T* yg, int64_t hw, int W, int ld, co
 // the vertical directions and (k, i) for the horizontal ones.  The first
 // kDepth steps' logits and lambdas are requested before x reaches LDS, so
 // their latency overlaps the plane load.
-template <typename T, bool HORIZ, bool REV>
+// STATES: write the direction's unweighted h to a.states[d] (fp32, scan
+// frame) instead of adding it into the partial.
+template <typename T, bool HORIZ, bool REV, bool STATES>
 __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t p, const float* xs, float* part,
                                                 int ld, const T* xg, int64_t hw) {
     const int lane = threadIdx.x & 63;
@@ -147,7 +150,8 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
     const int64_t plane = static_cast<int64_t>(S) * L;
     const int64_t nidx = p / a.c;
     const int64_t ci = p - nidx * a.c;
-    const float msc = a.merge ? a.merge[d * a.c + ci] : 1.0f;
+    const float msc = (!STATES && a.merge) ? a.merge[d * a.c + ci] : 1.0f;
+    float* hst = STATES ? a.states[d] + p * plane : nullptr;
     const auto rl = rsrc(static_cast<const T*>(a.lam[d]) + p * plane, plane * sizeof(T));
     const auto rz = rsrc(static_cast<const T*>(a.logits[d]) + (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane,
                          3 * plane * sizeof(T));
@@ -188,7 +192,7 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
     const int split = REV ? (S + 1) / 2 : S / 2;
     auto step = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
-        if (t == split) __syncthreads();
+        if (!STATES && t == split) __syncthreads();
         const int i = line_of(t);
         const int pos = HORIZ ? k * ld + i : i * ld + k;
         const float u = (widen<T>(rlam[s]) * msc) * xs[pos];
@@ -204,7 +208,11 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
         }
         fill(slot, t + kDepth);
         h = active ? hn : 0.0f;
-        if (active) part[pos] = part[pos] + h;
+        if constexpr (STATES) {
+            if (active) hst[static_cast<int64_t>(i) * L + k] = h;
+        } else {
+            if (active) part[pos] = part[pos] + h;
+        }
     };
 
     int t = 0;
@@ -216,10 +224,12 @@ __device__ __forceinline__ void plane_direction(const Plane4K& a, int d, int64_t
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         ((t + Ss < S ? step(IC<Ss>{}, t + Ss) : void()), ...);
     }(std::make_integer_sequence<int, kDepth - 1>{});
-    if (split >= S) __syncthreads();  // a one-step reverse scan
+    if (!STATES && split >= S) __syncthreads();  // a one-step reverse scan
 }
 
-template <typename T>
+// STATES: the four directions' fp32 scans go to a.states (only the x tile
+// in LDS), with no merge and no y.
+template <typename T, bool STATES>
 __global__ __launch_bounds__(256) void plane4_kernel(const Plane4K a) {
     extern __shared__ float lds[];
     const int H = a.H;
@@ -231,19 +241,23 @@ __global__ __launch_bounds__(256) void plane4_kernel(const Plane4K a) {
     const int64_t p = blockIdx.x;
     const int64_t hw = static_cast<int64_t>(H) * W;
     const T* xp = static_cast<const T*>(a.x) + p * hw;
-    for (int e = threadIdx.x; e < H * ld; e += blockDim.x) {
-        pv[e] = 0.0f;
-        ph[e] = 0.0f;
+    if constexpr (!STATES) {
+        for (int e = threadIdx.x; e < H * ld; e += blockDim.x) {
+            pv[e] = 0.0f;
+            ph[e] = 0.0f;
+        }
     }
     switch (threadIdx.x >> 6) {
-        case 0: plane_direction<T, false, false>(a, 0, p, xs, pv, ld, xp, hw); break;
-        case 1: plane_direction<T, false, true>(a, 1, p, xs, pv, ld, xp, hw); break;
-        case 2: plane_direction<T, true, false>(a, 2, p, xs, ph, ld, xp, hw); break;
-        default: plane_direction<T, true, true>(a, 3, p, xs, ph, ld, xp, hw); break;
+        case 0: plane_direction<T, false, false, STATES>(a, 0, p, xs, pv, ld, xp, hw); break;
+        case 1: plane_direction<T, false, true, STATES>(a, 1, p, xs, pv, ld, xp, hw); break;
+        case 2: plane_direction<T, true, false, STATES>(a, 2, p, xs, ph, ld, xp, hw); break;
+        default: plane_direction<T, true, true, STATES>(a, 3, p, xs, ph, ld, xp, hw); break;
     }
-    __syncthreads();
-    T* yp = static_cast<T*>(a.y) + p * hw;
-    store_plane<T>(yp, hw, W, ld, pv, ph);
+    if constexpr (!STATES) {
+        __syncthreads();
+        T* yp = static_cast<T*>(a.y) + p * hw;
+        store_plane<T>(yp, hw, W, ld, pv, ph);
+    }
 }
 
 }  // namespace
@@ -266,12 +280,44 @@ hipError_t launch_plane4(const void* x, const void* const logits[4], const void*
     k.cw = cw;
     k.H = static_cast<int>(h);
     k.W = static_cast<int>(w);
+    for (int d = 0; d < 4; ++d) k.states[d] = nullptr;
     const size_t lds = 3 * sizeof(float) * static_cast<size_t>(h) * static_cast<size_t>(w + 1);
     const dim3 grid(static_cast<unsigned>(n * c));
     if (dtype == kF32) {
-        hipLaunchKernelGGL(plane4_kernel<float>, grid, dim3(256), lds, stream, k);
+        hipLaunchKernelGGL((plane4_kernel<float, false>), grid, dim3(256), lds, stream, k);
     } else {
-        hipLaunchKernelGGL(plane4_kernel<bf16_t>, grid, dim3(256), lds, stream, k);
+        hipLaunchKernelGGL((plane4_kernel<bf16_t, false>), grid, dim3(256), lds, stream, k);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gspn
+
+namespace gspn {
+
+hipError_t launch_plane4_states(const void* x, const void* const logits[4], const void* const lam[4],
+                                float* const states[4], int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w,
+                                const int64_t chunk[4], int dtype, hipStream_t stream) {
+    Plane4K k;
+    k.x = x;
+    k.y = nullptr;
+    k.merge = nullptr;
+    for (int d = 0; d < 4; ++d) {
+        k.logits[d] = logits[d];
+        k.lam[d] = lam[d];
+        k.K[d] = static_cast<int>(chunk[d]);
+        k.states[d] = states[d];
+    }
+    k.c = c;
+    k.cw = cw;
+    k.H = static_cast<int>(h);
+    k.W = static_cast<int>(w);
+    const size_t lds = sizeof(float) * static_cast<size_t>(h) * static_cast<size_t>(w + 1);  // the x tile only
+    const dim3 grid(static_cast<unsigned>(n * c));
+    if (dtype == kF32) {
+        hipLaunchKernelGGL((plane4_kernel<float, true>), grid, dim3(256), lds, stream, k);
+    } else {
+        hipLaunchKernelGGL((plane4_kernel<bf16_t, true>), grid, dim3(256), lds, stream, k);
     }
     return hipGetLastError();
 }

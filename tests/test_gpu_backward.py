@@ -65,6 +65,9 @@ def _check_all(got, ref, tol, label):
     ((1, 2, 5, 1000), False),     # one position per lane, 16 waves
     ((1, 1, 3, 1500), True),      # two positions per lane
     ((2, 3, 9, 1), False),        # lines of length 1 / single-step scans
+    ((1, 3, 30, 50), True),       # plane-resident adjoint, shared-logit sums over channels
+    ((1, 2, 64, 64), False),      # the largest plane-resident plane
+    ((2, 2, 1, 7), False),        # a single line per plane
 ])
 def test_backward_small(shape, shared, chunk, dtype):
     n, c, h, w = shape
@@ -123,6 +126,27 @@ def test_backward_full_profile_sampled_planes():
     torch.cuda.synchronize()
     assert torch.isfinite(dx).all()
     for n, c in [(0, 0), (15, 7)]:
+        sl = (slice(n, n + 1), slice(c, c + 1))
+        ref = oracle.backward4(inp["x"][sl], [z[sl] for z in inp["logits"]], [l[sl] for l in inp["lam"]],
+                               gy[sl])
+        got = (dx[sl], [z[sl] for z in dz], [l[sl] for l in dl])
+        _check_all(got, ref, TOL["f32"], "plane (%d, %d)" % (n, c))
+
+
+def test_backward_full_tstage_sampled_planes():
+    """The 64 x 96 x 56 x 56 stage map (plane-resident backward): the call
+    on the whole batch, checked on sampled planes that the oracle computes on
+    their own."""
+    wl = WORKLOADS["tstage"]
+    _say("backward full tstage")
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 29)
+    t = G.StageTimes()
+    dx, dz, dl = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, times=t)
+    torch.cuda.synchronize()
+    assert t.as_dict()["scan_kernel"] == "plane4_kernel"
+    assert torch.isfinite(dx).all()
+    for n, c in [(0, 0), (63, 95), (17, 40)]:
         sl = (slice(n, n + 1), slice(c, c + 1))
         ref = oracle.backward4(inp["x"][sl], [z[sl] for z in inp["logits"]], [l[sl] for l in inp["lam"]],
                                gy[sl])

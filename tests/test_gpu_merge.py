@@ -118,7 +118,8 @@ def _check_backward(got, ref, tol, label):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("chunk", [0, 5])
 @pytest.mark.parametrize("shape,shared", [
-    ((2, 3, 23, 41), False),
+    ((2, 3, 23, 41), False),     # plane-resident adjoint
+    ((1, 3, 30, 44), True),      # plane-resident adjoint, shared logits
     ((1, 3, 40, 72), True),      # channel groups of the shared-logit adjoint, a partial last group
     ((1, 2, 5, 1500), False),    # two positions per lane
     ((1, 5, 3, 1100), True),     # two positions per lane, shared
