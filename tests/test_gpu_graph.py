@@ -71,8 +71,10 @@ def test_forward4_graph_replays(shape, dtype, shared, kernel):
         del junk
 
 
-def test_backward4_graph_replays():
-    wl = Workload("case", 1, 3, 40, 72, "f32", True, 5, 93)
+@pytest.mark.parametrize("shape", [(1, 3, 40, 72), (2, 3, 30, 44)])   # long-line / plane-resident backward
+def test_backward4_graph_replays(shape):
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, "f32", True, 5, 93)
     inp = make_inputs(wl, DEV)
     gy = torch.randn(inp["x"].shape, device=DEV)
     ws = G.backward4_workspace(inp["x"], wl.cw)
