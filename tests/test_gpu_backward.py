@@ -68,6 +68,8 @@ def _check_all(got, ref, tol, label):
     ((1, 3, 30, 50), True),       # plane-resident adjoint, shared-logit sums over channels
     ((1, 2, 64, 64), False),      # the largest plane-resident plane
     ((2, 2, 1, 7), False),        # a single line per plane
+    ((1, 2, 17, 1), True),        # a single column per plane
+    ((1, 3, 1, 1), True),         # one-position planes: no neighbours, centre weight 1
 ])
 def test_backward_small(shape, shared, chunk, dtype):
     n, c, h, w = shape

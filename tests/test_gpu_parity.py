@@ -154,7 +154,8 @@ def test_project(cin, cout, dtype, hw):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("chunk", [0, 8, 5])
 @pytest.mark.parametrize("shape", [(1, 2, 16, 16), (2, 3, 23, 41), (1, 2, 64, 64), (2, 2, 65, 33), (1, 2, 40, 72),
-                                   (1, 2, 64, 130), (1, 1, 1100, 40)])
+                                   (1, 2, 64, 130), (1, 1, 1100, 40),
+                                   (1, 3, 1, 17), (2, 2, 17, 1), (1, 2, 1, 1)])   # single rows, columns, positions
 def test_forward4_small(shape, chunk, dtype, use_ws):
     n, c, h, w = shape
     for shared in (False, True):
