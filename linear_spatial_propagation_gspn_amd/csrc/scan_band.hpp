@@ -30,7 +30,7 @@
 namespace gspn {
 
 #ifndef GSPN_BAND_DEPTH
-#define GSPN_BAND_DEPTH 8
+#define GSPN_BAND_DEPTH 12
 #endif
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
