@@ -66,9 +66,11 @@ def prenormalised(wl) -> bool:
 
 
 def weight_bytes_per_direction(wl) -> int:
-    """Bytes of one direction's weights as the scan reads them."""
+    """Bytes of one direction's weights as the scan reads them: the logits
+    (three per position and channel), or for prenormalised weights fp32
+    triples (fp32 storage) or packed half pairs, 4 bytes a position (bf16)."""
     if prenormalised(wl):
-        return wl.n * 3 * wl.h * wl.w * 4
+        return wl.n * wl.h * wl.w * (3 * 4 if wl.dtype == "f32" else 4)
     return wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
 
 

@@ -21,8 +21,9 @@
 //  - at the band's end the segment's states go to a state buffer (fp32) from
 //    which the next band's workgroups, including the neighbours' halos,
 //    start.  Bands are separate launches, so no workgroup waits for another.
-// The halos double the arithmetic and the cache traffic, not the HBM traffic
-// (neighbouring workgroups read the same lines within the same steps).
+// The halos double the arithmetic and the rows each workgroup reads.  Those
+// rows are the neighbouring segments' own rows at the same steps, but the
+// counters find most of them fetched again from beyond the L2.
 #pragma once
 
 #include "scan_lp.hpp"
