@@ -132,14 +132,15 @@ def adjoint_launch_bytes(wl) -> int:
 
 def adjplane_launch_bytes(wl) -> int:
     """Algorithmic bytes of the plane-resident adjoint launch (planes of at
-    most 64 x 64): x and dL/dy once in the array frame, four lambdas and
-    logits, four fp32 state maps read; four dlambda, the logit gradients
-    (per-channel) or their fp32 sums (shared) and dx written once."""
+    most 64 x 64), which recomputes the forward states itself: x and dL/dy,
+    four lambdas and logits read once; four dlambda, the logit gradients
+    (per-channel) or their fp32 sums (shared) and dx written once.  The fp32
+    states it writes and reads back are its own scratch, not counted (the
+    counters show what they cost)."""
     u = unit_bytes(wl)
     z = 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
-    states = 4 * wl.n * wl.c_scan * wl.h * wl.w * 4
     dz = 4 * wl.n * 3 * wl.h * wl.w * 4 if prenormalised(wl) else z
-    return 2 * u + 4 * u + z + states + 4 * u + dz + u
+    return 2 * u + 4 * u + z + 4 * u + dz + u
 
 
 def merge_weights(wl, on: bool):
@@ -182,9 +183,9 @@ KERNEL_SOURCES = {
     "scan4lp_kernel": _SCAN4,
     "scan4band_kernel": _SCAN4 + ["scan_band.hpp"],
     "scan4v_kernel": _SCAN4,
-    "plane4_kernel": ["plane4.hip"],
+    "plane4_kernel": ["plane4.hip", "plane_common.hpp"],
     "adj4_kernel": ["backward.hip"],
-    "adjplane_kernel": ["adjplane.hip"],
+    "adjplane_kernel": ["adjplane.hip", "plane_common.hpp"],
 }
 _COMMON = ["device.hpp"]
 

@@ -376,7 +376,9 @@ gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w
                                       gspn_stage_times* times);
 
 /* gspn_backward4 with stage timing (same contract as gspn_forward4_timed);
- * the forward recompute is reported as GSPN_STAGE_SCAN. */
+ * the forward recompute is reported as GSPN_STAGE_SCAN, except for planes of
+ * at most 64 x 64, whose adjoint launch (GSPN_STAGE_ADJOINT) recomputes the
+ * states itself (scan_kernel GSPN_SCAN_PLANE, no scan launches). */
 gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                                  const void* x, const void* const logits[4], const void* const lam[4],
                                  const float* merge, const float* states, const void* gy, void* dx,

@@ -16,8 +16,12 @@
 //  - wave d runs direction d with one lane per line position (lines of at
 //    most 64), a_t in a VGPR, the neighbour products moved by DPP lane
 //    shifts, so no step needs a barrier;
-//  - the logits, lambda and the forward states h_{t-1} (fp32, written before
-//    by the plane-resident forward) stream from HBM, D steps ahead;
+//  - the forward states h_{t-1} are recomputed in the same launch: each wave
+//    first runs its direction's forward scan (plane_common.hpp) on the x
+//    tile, writing its fp32 states to a workspace; after one barrier it
+//    reads them back, newest first, while they are still in the cache (the
+//    same lanes wrote them, so no other wave's writes are involved);
+//  - the logits, lambda and those states stream in, D steps ahead;
 //  - dx is summed in two LDS partials, T2B + B2T and L2R + R2L, with plain
 //    reads and writes: each direction of a pair first writes the lines of the
 //    first half of its steps, the two halves disjoint, and after one barrier
@@ -28,11 +32,16 @@
 
 #include "device.hpp"
 #include "launch.hpp"
+#include "plane_common.hpp"
 
 namespace gspn {
 namespace {
 
-constexpr int kPlaneMax = 64;
+using plane::kPlaneMax;
+using plane::load_raw;
+using plane::rsrc;
+using plane::widen;
+
 constexpr int kDepth = 8;  // steps of logits, lambda and states in flight per wave
 
 template <int V>
@@ -43,7 +52,7 @@ struct AdjPlaneK {
     const void* g;       // dL/dy, [planes][H][W]
     const void* z[4];    // logits of direction d, [n][cw][3][S_d][L_d]
     const void* lam[4];  // [planes][S_d][L_d]
-    const float* hs[4];  // forward states, fp32 [planes][S_d][L_d]
+    float* hs[4];        // forward states, fp32 [planes][S_d][L_d], written by the kernel's forward phase
     void* dlam[4];       // [planes][S_d][L_d]
     void* dz[4];         // [n][cw][3][S_d][L_d], or for shared logits fp32 sums [n][3][S_d][L_d] (added into)
     void* dx;            // [planes][H][W]
@@ -57,28 +66,6 @@ struct AdjPlaneK {
     int shared;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-
-template <typename E>
-__device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    if constexpr (sizeof(E) == 4) {
-        return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-    } else {
-        return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-    }
-}
-
-template <typename E>
-__device__ __forceinline__ float widen(uint32_t raw) {
-    if constexpr (sizeof(E) == 4) {
-        return __uint_as_float(raw);
-    } else {
-        return __uint_as_float(raw << 16);
-    }
-}
-
 __device__ __forceinline__ float from_lower_lane(float v) {  // lane i gets lane i-1 (0 for lane 0)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, true));
 }
@@ -86,46 +73,37 @@ __device__ __forceinline__ float from_upper_lane(float v) {  // lane i gets lane
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true));
 }
 
-// Two planes (x and dL/dy, n elements each, rows of W) into padded fp32 LDS
-// tiles: every thread's 16-byte loads are issued before its first LDS write
-// (256 threads, at most 64 x 64 elements: at most four vectors per plane).
+// dL/dy (n elements, rows of W) into its padded fp32 LDS tile (x is there
+// already, loaded by the forward phase): every thread's 16-byte loads are
+// issued before its first LDS write (256 threads, at most 64 x 64 elements:
+// at most four vectors).
 template <typename T>
-__device__ __forceinline__ void load_tiles(const T* xg, const T* gg, int n, int W, int ld, float* xs, float* gs) {
+__device__ __forceinline__ void load_g_tile(const T* gg, int n, int W, int ld, float* gs) {
     constexpr int VW = 16 / static_cast<int>(sizeof(T));
     constexpr int NV = kPlaneMax * kPlaneMax / VW / 256;
-    const bool vec = n % VW == 0 && (reinterpret_cast<uintptr_t>(xg) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(gg) & 15) == 0;
-    if (!vec) {
-        for (int e = threadIdx.x; e < n; e += blockDim.x) {
-            const int a = e + (e / W) * (ld - W);
-            xs[a] = Store<T>::ld(xg + e);
-            gs[a] = Store<T>::ld(gg + e);
-        }
+    if (n % VW != 0 || (reinterpret_cast<uintptr_t>(gg) & 15) != 0) {
+        for (int e = threadIdx.x; e < n; e += blockDim.x) gs[e + (e / W) * (ld - W)] = Store<T>::ld(gg + e);
         return;
     }
     const int nv = n / VW;
-    uint4 qx[NV], qg[NV];
+    uint4 qg[NV];
 #pragma unroll
     for (int b = 0; b < NV; ++b) {
         const int v = min(static_cast<int>(threadIdx.x) + 256 * b, nv - 1);
-        qx[b] = reinterpret_cast<const uint4*>(xg)[v];
         qg[b] = reinterpret_cast<const uint4*>(gg)[v];
     }
 #pragma unroll
     for (int b = 0; b < NV; ++b) {
         const int v = static_cast<int>(threadIdx.x) + 256 * b;
         if (v >= nv) continue;
-        const uint32_t wx[4] = {qx[b].x, qx[b].y, qx[b].z, qx[b].w};
         const uint32_t wg[4] = {qg[b].x, qg[b].y, qg[b].z, qg[b].w};
 #pragma unroll
         for (int j = 0; j < VW; ++j) {
             const int e = v * VW + j;
             const int a = e + (e / W) * (ld - W);
             if constexpr (sizeof(T) == 4) {
-                xs[a] = __uint_as_float(wx[j]);
                 gs[a] = __uint_as_float(wg[j]);
             } else {
-                xs[a] = __uint_as_float((j & 1) ? (wx[j >> 1] & 0xffff0000u) : (wx[j >> 1] << 16));
                 gs[a] = __uint_as_float((j & 1) ? (wg[j >> 1] & 0xffff0000u) : (wg[j >> 1] << 16));
             }
         }
@@ -185,10 +163,9 @@ __device__ __forceinline__ void adj_direction(const AdjPlaneK& a, int d, int64_t
         (fill(IC<Ss>{}, Ss), ...);
     }(std::make_integer_sequence<int, kDepth>{});
 
-    // x, dL/dy into LDS (all four waves), the dx partials cleared
+    // dL/dy into LDS (all four waves)
     const int64_t hw = static_cast<int64_t>(a.H) * a.W;
-    load_tiles<T>(static_cast<const T*>(a.x) + p * hw, static_cast<const T*>(a.g) + p * hw,
-                  static_cast<int>(hw), a.W, ld, xs, gs);
+    load_g_tile<T>(static_cast<const T*>(a.g) + p * hw, static_cast<int>(hw), a.W, ld, gs);
     __syncthreads();
 
     float qn0 = 0.0f, qn1 = 0.0f, qn2 = 0.0f;  // w_{t+1}[k, o] a_{t+1}[k] for o = -1, 0, +1
@@ -272,8 +249,11 @@ __device__ __forceinline__ void adj_direction(const AdjPlaneK& a, int d, int64_t
     }
 }
 
+// Each wave first runs its direction's forward scan, writing the states to
+// a.hs[d] (f describes that forward: the same x, logits, lambdas and chunks,
+// states at a.hs), then, after a barrier, its adjoint reading them back.
 template <typename T, bool MERGE>
-__global__ __launch_bounds__(256) void adjplane_kernel(const AdjPlaneK a) {
+__global__ __launch_bounds__(256) void adjplane_kernel(const AdjPlaneK a, const plane::Plane4K f) {
     extern __shared__ float lds[];
     const int H = a.H;
     const int W = a.W;
@@ -287,6 +267,18 @@ __global__ __launch_bounds__(256) void adjplane_kernel(const AdjPlaneK a) {
         pv[e] = 0.0f;
         ph[e] = 0.0f;
     }
+    // the forward: x into its tile (all waves), then direction d's states
+    const int64_t hw0 = static_cast<int64_t>(H) * W;
+    const T* xp = static_cast<const T*>(a.x) + p * hw0;
+    switch (threadIdx.x >> 6) {
+        case 0: plane::plane_direction<T, false, false, true>(f, 0, p, xs, nullptr, ld, xp, hw0); break;
+        case 1: plane::plane_direction<T, false, true, true>(f, 1, p, xs, nullptr, ld, xp, hw0); break;
+        case 2: plane::plane_direction<T, true, false, true>(f, 2, p, xs, nullptr, ld, xp, hw0); break;
+        default: plane::plane_direction<T, true, true, true>(f, 3, p, xs, nullptr, ld, xp, hw0); break;
+    }
+    // the lanes that wrote the states read them back; the barrier orders
+    // those writes before the reads, as for any access of the workgroup
+    __syncthreads();
     switch (threadIdx.x >> 6) {
         case 0: adj_direction<T, false, false, MERGE>(a, 0, p, xs, gs, pv, ld); break;
         case 1: adj_direction<T, false, true, MERGE>(a, 1, p, xs, gs, pv, ld); break;
@@ -325,15 +317,30 @@ hipError_t launch_adjplane(const AdjPlaneParams& p, hipStream_t stream) {
     k.H = static_cast<int>(p.h);
     k.W = static_cast<int>(p.w);
     k.shared = p.shared;
+    // the forward the kernel recomputes: unweighted states into hs
+    plane::Plane4K f;
+    f.x = p.x;
+    f.y = nullptr;
+    f.merge = nullptr;
+    for (int d = 0; d < 4; ++d) {
+        f.logits[d] = p.z[d];
+        f.lam[d] = p.lam[d];
+        f.K[d] = static_cast<int>(p.chunk[d]);
+        f.states[d] = p.hs[d];
+    }
+    f.c = p.c;
+    f.cw = p.cw;
+    f.H = k.H;
+    f.W = k.W;
     const size_t lds = 4 * sizeof(float) * static_cast<size_t>(p.h) * static_cast<size_t>(p.w + 1);
     const dim3 grid(static_cast<unsigned>(p.n * p.c));
     const bool merge = p.merge || p.dmerge;
     if (p.dtype == kF32) {
-        if (merge) hipLaunchKernelGGL((adjplane_kernel<float, true>), grid, dim3(256), lds, stream, k);
-        else hipLaunchKernelGGL((adjplane_kernel<float, false>), grid, dim3(256), lds, stream, k);
+        if (merge) hipLaunchKernelGGL((adjplane_kernel<float, true>), grid, dim3(256), lds, stream, k, f);
+        else hipLaunchKernelGGL((adjplane_kernel<float, false>), grid, dim3(256), lds, stream, k, f);
     } else {
-        if (merge) hipLaunchKernelGGL((adjplane_kernel<bf16_t, true>), grid, dim3(256), lds, stream, k);
-        else hipLaunchKernelGGL((adjplane_kernel<bf16_t, false>), grid, dim3(256), lds, stream, k);
+        if (merge) hipLaunchKernelGGL((adjplane_kernel<bf16_t, true>), grid, dim3(256), lds, stream, k, f);
+        else hipLaunchKernelGGL((adjplane_kernel<bf16_t, false>), grid, dim3(256), lds, stream, k, f);
     }
     return hipGetLastError();
 }

@@ -702,10 +702,10 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     const int H = static_cast<int>(h);
     const int W = static_cast<int>(w);
 
-    // Planes of at most 64 x 64 (recomputed states only): the four
-    // directions' states in one pass over LDS-resident planes, then their
-    // adjoints likewise, x, gy and dx in the array frame: no transposes and
-    // no per-direction dx terms.
+    // Planes of at most 64 x 64 (recomputed states only): one launch over
+    // LDS-resident planes recomputes the four directions' states into the
+    // workspace and runs their adjoints on them, x, gy and dx in the array
+    // frame: no transposes and no per-direction dx terms.
     if (gspn::plane4_supported(h, w) && !states) {
         if (shared &&
             timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(sums, 4 * zsum, st); }) != hipSuccess)
@@ -715,11 +715,7 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
             return GSPN_ERR_HIP;
         float* hf[4];
         for (int d = 0; d < 4; ++d) hf[d] = reinterpret_cast<float*>(hs[d]);
-        if (timed(tm, GSPN_STAGE_SCAN, [&] {
-                return gspn::launch_plane4_states(x, logits, lam, hf, n, c, cw, h, w, chunks, dtype, st);
-            }) != hipSuccess)
-            return GSPN_ERR_HIP;
-        if (tm) tm->scan_kernel = GSPN_SCAN_PLANE;
+        if (tm) tm->scan_kernel = GSPN_SCAN_PLANE;  // the plane-resident forward, inside the adjoint launch
         gspn::AdjPlaneParams ap;
         ap.x = x;
         ap.g = gy;

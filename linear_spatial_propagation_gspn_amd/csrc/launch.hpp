@@ -63,12 +63,6 @@ hipError_t launch_plane4(const void* x, const void* const logits[4], const void*
                          void* y, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w, const int64_t chunk[4],
                          int dtype, hipStream_t stream);
 
-// The four directions' unweighted scans of planes of at most 64 x 64 as fp32
-// maps, states[d] in direction d's scan frame ([n][c][S_d][L_d]); no merge.
-hipError_t launch_plane4_states(const void* x, const void* const logits[4], const void* const lam[4],
-                                float* const states[4], int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w,
-                                const int64_t chunk[4], int dtype, hipStream_t stream);
-
 // dst[p][c][r] = src[p][r][c] for `planes` planes of R x Cc elements.
 hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, int Cc, int dtype,
                             hipStream_t stream);
@@ -128,16 +122,17 @@ struct AdjointParams {
 hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream);
 
 // All four directions' adjoint for planes of at most 64 x 64, one workgroup
-// per plane (x, gy and dx in the array frame; the per-direction tensors and
-// the fp32 states hs in each direction's scan frame; dz as in AdjointParams:
-// the storage type, or fp32 sums over channels when shared).  dx is written,
-// dmerge (if given) added into.
+// per plane (x, gy and dx in the array frame; the per-direction tensors in
+// each direction's scan frame; dz as in AdjointParams: the storage type, or
+// fp32 sums over channels when shared).  The launch first recomputes the
+// forward's fp32 states into hs (workspace, each direction's scan frame),
+// then runs the adjoint on them.  dx is written, dmerge (if given) added into.
 struct AdjPlaneParams {
     const void* x;
     const void* g;
     const void* z[4];
     const void* lam[4];
-    const float* hs[4];
+    float* hs[4];
     void* dlam[4];
     void* dz[4];
     void* dx;

@@ -146,7 +146,11 @@ def test_backward_full_tstage_sampled_planes():
     t = G.StageTimes()
     dx, dz, dl = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, times=t)
     torch.cuda.synchronize()
-    assert t.as_dict()["scan_kernel"] == "plane4_kernel"
+    st = t.as_dict()
+    assert st["scan_kernel"] == "plane4_kernel"
+    # one launch: the adjoint recomputes the forward states itself
+    assert st["scan"]["launches"] == 0 and st["adjoint"]["launches"] == 1
+    assert st["transpose"]["launches"] == 0 and st["combine"]["launches"] == 0
     assert torch.isfinite(dx).all()
     for n, c in [(0, 0), (63, 95), (17, 40)]:
         sl = (slice(n, n + 1), slice(c, c + 1))
