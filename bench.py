@@ -121,12 +121,12 @@ def backward_algorithmic_bytes(wl) -> int:
 def adjoint_launch_bytes(wl) -> int:
     """Algorithmic bytes of the adjoint launch: x and dL/dy in both frames,
     four lambdas and logits, four fp32 state maps read; four dlambda and dx
-    terms written; the logit gradients written (per-channel) or added into fp32
-    sums (shared)."""
+    terms written; the logit gradients written (per-channel) or, for shared
+    logits, two fp32 sums a position (weight-gradient differences) added into."""
     u = unit_bytes(wl)
     z = 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
     states = 4 * wl.n * wl.c_scan * wl.h * wl.w * 4
-    dz = 4 * wl.n * 3 * wl.h * wl.w * 4 if prenormalised(wl) else z
+    dz = 4 * wl.n * 2 * wl.h * wl.w * 4 if prenormalised(wl) else z  # shared: two fp32 sums a position
     return 2 * u + 2 * u + 4 * u + z + states + 4 * u + 4 * u + dz
 
 
@@ -139,7 +139,7 @@ def adjplane_launch_bytes(wl) -> int:
     counters show what they cost)."""
     u = unit_bytes(wl)
     z = 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
-    dz = 4 * wl.n * 3 * wl.h * wl.w * 4 if prenormalised(wl) else z
+    dz = 4 * wl.n * 2 * wl.h * wl.w * 4 if prenormalised(wl) else z  # shared: two fp32 sums a position
     return 2 * u + 4 * u + z + 4 * u + dz + u
 
 

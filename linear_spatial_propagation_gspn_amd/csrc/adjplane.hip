@@ -54,7 +54,7 @@ struct AdjPlaneK {
     const void* lam[4];  // [planes][S_d][L_d]
     float* hs[4];        // forward states, fp32 [planes][S_d][L_d], written by the kernel's forward phase
     void* dlam[4];       // [planes][S_d][L_d]
-    void* dz[4];         // [n][cw][3][S_d][L_d], or for shared logits fp32 sums [n][3][S_d][L_d] (added into)
+    void* dz[4];         // [n][cw][3][S_d][L_d], or for shared logits fp32 sums of dw differences [n][3][S_d][L_d] (added into)
     void* dx;            // [planes][H][W]
     const float* merge;  // [4][c] or null
     float* dmerge;       // [4][c] fp32, added into, or null
@@ -202,8 +202,8 @@ __device__ __forceinline__ void adj_direction(const AdjPlaneK& a, int d, int64_t
         const float hl = from_lower_lane(hp);
         const float hr = from_upper_lane(hp);
         float dz[3] = {0.0f, 0.0f, 0.0f};
-        if (!first) {
-            const float dw0 = am * hl, dw1 = am * hp, dw2 = am * hr;
+        const float dw0 = am * hl, dw1 = am * hp, dw2 = am * hr;
+        if (!first && !a.shared) {
             const float dot = (dw0 * w0 + dw1 * w1) + dw2 * w2;
             dz[0] = w0 * (1.0f - s0) * (dw0 - dot);
             dz[1] = w1 * (1.0f - s1) * (dw1 - dot);
@@ -217,8 +217,12 @@ __device__ __forceinline__ void adj_direction(const AdjPlaneK& a, int d, int64_t
             Store<T>::st(dlp + e, am * xk);
             part[pos] = part[pos] + am * lk;
             if (a.shared) {
-#pragma unroll
-                for (int o = 0; o < 3; ++o) atomicAdd(dzs + o * plane + e, dz[o]);
+                // channel sums of the weight-gradient differences; the
+                // shared Jacobian is applied once to them afterwards
+                if (!first) {
+                    atomicAdd(dzs + e, dw0 - dw1);
+                    atomicAdd(dzs + plane + e, dw2 - dw1);
+                }
             } else {
 #pragma unroll
                 for (int o = 0; o < 3; ++o) Store<T>::st(dzp + o * plane + e, dz[o]);

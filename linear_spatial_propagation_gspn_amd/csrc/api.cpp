@@ -742,7 +742,8 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         if (shared) {
             for (int d = 0; d < 4; ++d)
                 if (timed(tm, GSPN_STAGE_REDUCE, [&] {
-                        return gspn::launch_store_sums(sums + d * zsum, dlogits[d], zsum, dtype, st);
+                        return gspn::launch_finish_shared_dz(sums + d * zsum, logits[d], dlogits[d], n,
+                                                             d < 2 ? h : w, d < 2 ? w : h, dtype, st);
                     }) != hipSuccess)
                     return GSPN_ERR_HIP;
         }
@@ -828,7 +829,8 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (shared) {
         for (int d = 0; d < 4; ++d)
             if (timed(tm, GSPN_STAGE_REDUCE, [&] {
-                    return gspn::launch_store_sums(sums + d * zsum, dlogits[d], zsum, dtype, st);
+                    return gspn::launch_finish_shared_dz(sums + d * zsum, logits[d], dlogits[d], n,
+                                                         d < 2 ? h : w, d < 2 ? w : h, dtype, st);
                 }) != hipSuccess)
                 return GSPN_ERR_HIP;
     }

@@ -63,7 +63,7 @@ struct AdjK {
     int K;
     int nchunks;
     int reverse;
-    int shared;  // dz is an fp32 sum over channels (atomic adds; groups of shared_group<P>() channels)
+    int shared;  // dz holds fp32 channel sums of weight-gradient differences (atomic adds; groups of shared_group<P>() channels)
     const float* mscale;  // learnable merge weight of each channel for this direction ([c]), or null for 1
     float* dmerge;        // its gradient [c] (fp32 atomic adds), or null
 };
@@ -254,24 +254,35 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 qn2[g][j] = first ? 0.0f : w[2][j] * a_t[j];
             }
         }
-        // logit gradient of this line (none on a chunk's first line)
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            float dz[3] = {0.0f, 0.0f, 0.0f};
+        // logit gradient of this line (none on a chunk's first line).  For
+        // shared logits only the channel sums of dw_{-1} - dw_0 and
+        // dw_{+1} - dw_0 leave the workgroup: the normalisation's Jacobian
+        // ignores a common shift of the dw, and it is the same for every
+        // channel, so it is applied once to the sums afterwards.
+        if (a.shared) {
             if (!first) {
-                const float dot = (dw[j][0] * w[0][j] + dw[j][1] * w[1][j]) + dw[j][2] * w[2][j];
+                float* dzs = static_cast<float*>(a.dz) + nidx * 3 * plane;
 #pragma unroll
-                for (int o = 0; o < 3; ++o) dz[o] = w[o][j] * (1.0f - sg[o][j]) * (dw[j][o] - dot);
-                if (k0 + j == 0) dz[0] = 0.0f;
-                if (k0 + j + 1 >= L) dz[2] = 0.0f;
-                if (L == 1) dz[1] = 0.0f;  // a single neighbour: w = [1] whatever its logit
+                for (int j = 0; j < P; ++j) {
+                    if (kin[j]) {
+                        atomicAdd(dzs + lo + k0 + j, dw[j][0] - dw[j][1]);
+                        atomicAdd(dzs + plane + lo + k0 + j, dw[j][2] - dw[j][1]);
+                    }
+                }
             }
-            if (kin[j]) {
-                if (a.shared) {
-                    float* dzs = static_cast<float*>(a.dz) + nidx * 3 * plane;
+        } else {
 #pragma unroll
-                    for (int o = 0; o < 3; ++o) atomicAdd(dzs + o * plane + lo + k0 + j, dz[o]);
-                } else {
+            for (int j = 0; j < P; ++j) {
+                float dz[3] = {0.0f, 0.0f, 0.0f};
+                if (!first) {
+                    const float dot = (dw[j][0] * w[0][j] + dw[j][1] * w[1][j]) + dw[j][2] * w[2][j];
+#pragma unroll
+                    for (int o = 0; o < 3; ++o) dz[o] = w[o][j] * (1.0f - sg[o][j]) * (dw[j][o] - dot);
+                    if (k0 + j == 0) dz[0] = 0.0f;
+                    if (k0 + j + 1 >= L) dz[2] = 0.0f;
+                    if (L == 1) dz[1] = 0.0f;  // a single neighbour: w = [1] whatever its logit
+                }
+                if (kin[j]) {
                     T* dzp = static_cast<T*>(a.dz) + zplane;
 #pragma unroll
                     for (int o = 0; o < 3; ++o) st_once<T, NT>(dzp + o * plane + lo + k0 + j, dz[o]);
@@ -334,12 +345,44 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) p[e] = 0.0f;
 }
 
+// Shared logits: dlogits from the channel sums e_{-1} = sum (dw_{-1} - dw_0)
+// and e_{+1} = sum (dw_{+1} - dw_0) that the adjoints left in planes 0 and 1
+// of src ([n][3][S][L] fp32; plane 2 unused).  With the shared weights w and
+// sigmoids s of the position, dz_q = w_q (1 - s_q) (e_q - sum_o w_o e_o),
+// e_0 = 0: the same value as summing each channel's dz, since that Jacobian
+// is linear, equal for all channels and blind to a common shift of the dw
+// (the w sum to 1).  One thread per position of the n * S * L.
 template <typename T>
-__global__ __launch_bounds__(256) void store_sums_kernel(const float* __restrict__ src, T* __restrict__ dst,
-                                                         int64_t n) {
+__global__ __launch_bounds__(256) void finish_shared_dz_kernel(const float* __restrict__ src,
+                                                               const T* __restrict__ z, T* __restrict__ dz,
+                                                               int64_t n, int S, int L) {
+    const int64_t plane = static_cast<int64_t>(S) * L;
+    const int64_t total = n * plane;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride)
-        Store<T>::st(dst + e, src[e]);
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const int64_t img = e / plane;
+        const int64_t r = e - img * plane;
+        const int k = static_cast<int>(r % L);
+        const int64_t base = img * 3 * plane + r;
+        const bool has_l = k > 0;
+        const bool has_r = k + 1 < L;
+        const float s0 = has_l ? sigmoid(Store<T>::ld(z + base)) : 0.0f;
+        const float s1 = sigmoid(Store<T>::ld(z + base + plane));
+        const float s2 = has_r ? sigmoid(Store<T>::ld(z + base + 2 * plane)) : 0.0f;
+        const float rr = recip((s0 + s1) + s2);
+        const float w0 = s0 * rr, w1 = s1 * rr, w2 = s2 * rr;
+        const float e0 = src[base], e2 = src[base + plane];
+        const float dot = w0 * e0 + w2 * e2;
+        float d0 = w0 * (1.0f - s0) * (e0 - dot);
+        float d1 = w1 * (1.0f - s1) * (0.0f - dot);
+        float d2 = w2 * (1.0f - s2) * (e2 - dot);
+        if (!has_l) d0 = 0.0f;
+        if (!has_r) d2 = 0.0f;
+        if (L == 1) d1 = 0.0f;  // a single neighbour: w = [1] whatever its logit
+        Store<T>::st(dz + base, d0);
+        Store<T>::st(dz + base + plane, d1);
+        Store<T>::st(dz + base + 2 * plane, d2);
+    }
 }
 
 unsigned grid_for(int64_t total) {
@@ -425,13 +468,17 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_store_sums(const float* src, void* dst, int64_t n, int dtype, hipStream_t stream) {
+hipError_t launch_finish_shared_dz(const float* sums, const void* logits, void* dlogits, int64_t n, int64_t S,
+                                   int64_t L, int dtype, hipStream_t stream) {
+    const unsigned grid = grid_for(n * S * L);
     if (dtype == kF32) {
-        hipLaunchKernelGGL(store_sums_kernel<float>, dim3(grid_for(n)), dim3(256), 0, stream, src,
-                           static_cast<float*>(dst), n);
+        hipLaunchKernelGGL(finish_shared_dz_kernel<float>, dim3(grid), dim3(256), 0, stream, sums,
+                           static_cast<const float*>(logits), static_cast<float*>(dlogits), n, static_cast<int>(S),
+                           static_cast<int>(L));
     } else {
-        hipLaunchKernelGGL(store_sums_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, stream, src,
-                           static_cast<bf16_t*>(dst), n);
+        hipLaunchKernelGGL(finish_shared_dz_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream, sums,
+                           static_cast<const bf16_t*>(logits), static_cast<bf16_t*>(dlogits), n,
+                           static_cast<int>(S), static_cast<int>(L));
     }
     return hipGetLastError();
 }

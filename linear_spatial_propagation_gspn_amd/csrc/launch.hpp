@@ -100,7 +100,9 @@ hipError_t launch_merge4(const void* h0, const void* h1, const void* h2, const v
 // One direction of the adjoint scan, in vertical form (horizontal directions
 // on x and dL/dy transposed into their scan frame).  hs: the direction's
 // forward states in fp32; dz: logits gradient in the storage type, or
-// (shared) fp32 sums over channels [n][3][S][L] that the kernel adds into.
+// (shared) fp32 channel sums of the weight-gradient differences
+// dw_{-1} - dw_0 and dw_{+1} - dw_0, planes 0 and 1 of [n][3][S][L], that the
+// kernel adds into (launch_finish_shared_dz turns them into dlogits).
 struct AdjointParams {
     const void* x;
     const void* g;
@@ -124,7 +126,7 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream);
 // All four directions' adjoint for planes of at most 64 x 64, one workgroup
 // per plane (x, gy and dx in the array frame; the per-direction tensors in
 // each direction's scan frame; dz as in AdjointParams: the storage type, or
-// fp32 sums over channels when shared).  The launch first recomputes the
+// fp32 difference sums when shared).  The launch first recomputes the
 // forward's fp32 states into hs (workspace, each direction's scan frame),
 // then runs the adjoint on them.  dx is written, dmerge (if given) added into.
 struct AdjPlaneParams {
@@ -145,7 +147,11 @@ struct AdjPlaneParams {
 };
 hipError_t launch_adjplane(const AdjPlaneParams& p, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
-hipError_t launch_store_sums(const float* src, void* dst, int64_t n, int dtype, hipStream_t stream);
+// Shared logits: dlogits (storage type, [n][3][S][L]) from the channel sums
+// of the weight-gradient differences that the adjoints added into sums
+// (planes 0 and 1 of [n][3][S][L] fp32) and the logits themselves.
+hipError_t launch_finish_shared_dz(const float* sums, const void* logits, void* dlogits, int64_t n, int64_t S,
+                                   int64_t L, int dtype, hipStream_t stream);
 
 hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const void* in,
                           const void* weight, void* out, int dtype, hipStream_t stream);
