@@ -70,6 +70,8 @@ def _check_all(got, ref, tol, label):
     ((2, 2, 1, 7), False),        # a single line per plane
     ((1, 2, 17, 1), True),        # a single column per plane
     ((1, 3, 1, 1), True),         # one-position planes: no neighbours, centre weight 1
+    ((2, 37, 24, 72), True),      # shared logits summed over ten channel groups, the last one ragged
+    ((1, 37, 20, 30), True),      # the same over 37 plane-resident workgroups
 ])
 def test_backward_small(shape, shared, chunk, dtype):
     n, c, h, w = shape
