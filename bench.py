@@ -16,11 +16,18 @@ Measurements:
     HIP events on that stream around every launch of the step.  The dominant
     kernel is the line scan; its per-launch duration is the scan stage's time
     divided by its launch count.
-  - roofline.achieved: the scan launch's algorithmic bytes (each tensor the
-    launch reads or writes, moved once) / its per-launch duration.
+  - roofline.achieved: the algorithmic bytes of the units the dominant
+    launch processes (the step's compulsory bytes: every distinct input of
+    the four-direction scan read once and its output written once, divided
+    over the launches that share the scan) / its per-launch duration;
+    roofline.frac = achieved / 8 TB/s.  roofline.design_bytes_per_launch and
+    design_achieved give the bytes the launch's design moves (e.g. x and its
+    transpose, four partial maps) for comparison.
   - roofline.traffic: HBM bytes per scan launch measured with the FETCH_SIZE
     and WRITE_SIZE counters, read from the committed counter summary under
-    profiles/ when it was taken on the current kernel sources, else null.
+    profiles/ when it was taken on the current kernel sources, else null;
+    step_traffic: the same counters summed over every kernel of the step
+    (profiles/step_<workload>_traffic.txt), else null.
   - effective bandwidth of the whole step: algorithmic bytes of the forward
     (every distinct input read once, y written once) / ms per step.
   - cpu_baseline: the fp64 oracle on a bounded sample of the same workload,
@@ -83,6 +90,23 @@ def algorithmic_bytes(wl) -> int:
     z = 4 * wl.n * wl.cw * 3 * hw * es
     wts = 2 * wl.c * wl.c_proxy * es if wl.c_proxy else 0
     return x + lam + z + wts + x
+
+
+def scan_algorithmic_bytes(wl) -> int:
+    """Compulsory bytes of the four-direction scan of the scanned tensor (in
+    proxy space for proxy workloads): x read once, the four directions'
+    logits and lambdas read once as stored, y written once: 18U for fp32
+    per-channel logits, 6U + 12 N H W 2 bytes for bf16 shared logits."""
+    u = unit_bytes(wl)
+    z = 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl)
+    return u + 4 * u + z + u
+
+
+def launch_algorithmic_bytes(wl, launches: int) -> int:
+    """The algorithmic bytes of the units one scan launch processes: the
+    scan's compulsory bytes divided over the launches that carry it (one
+    fused launch; a band of steps each; one direction each)."""
+    return scan_algorithmic_bytes(wl) // max(1, launches)
 
 
 def scan_launch_bytes(wl, kernel: str, launches: int = 1) -> int:
@@ -152,23 +176,35 @@ def merge_weights(wl, on: bool):
     return torch.randn((4, wl.c_scan), generator=g, device="cuda", dtype=torch.float32)
 
 
-def run_step(wl, inp, out, ws, timed=False, merge=None):
+def array_layout(inp: dict) -> dict:
+    """The inputs with every direction's logits and lambda in the array frame
+    [.., H, W] (the horizontal directions' transposed; the vertical ones are
+    the same tensors)."""
+    out = dict(inp)
+    for key in ("logits", "lam"):
+        out[key] = [t if d < 2 else t.transpose(-1, -2).contiguous() for d, t in enumerate(inp[key])]
+    return out
+
+
+def run_step(wl, inp, out, ws, timed=False, merge=None, layout="scan"):
     if wl.c_proxy:
         f = G.gspn_proxy_forward4_timed if timed else G.gspn_proxy_forward4
         return f(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"],
-                 chunk_len=wl.chunk, out=out, workspace=ws, merge=merge)
+                 chunk_len=wl.chunk, out=out, workspace=ws, merge=merge, layout=layout)
     f = G.gspn_forward4_timed if timed else G.gspn_forward4
-    return f(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out, workspace=ws, merge=merge)
+    return f(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=out, workspace=ws, merge=merge,
+             layout=layout)
 
 
-def stage_times(wl, inp, out, ws, reps: int, merge=None) -> dict:
+def stage_times(wl, inp, out, ws, reps: int, merge=None, layout="scan") -> dict:
     """Mean per-step duration and launch count of each stage over reps timed
     steps."""
     acc = {name: {"ms": 0.0, "launches": 0} for name in G.STAGES}
     kernel = None
     for _ in range(reps):
-        _, t = run_step(wl, inp, out, ws, timed=True, merge=merge)
+        _, t = run_step(wl, inp, out, ws, timed=True, merge=merge, layout=layout)
         kernel = t.pop("scan_kernel")
+        t.pop("adjoint_plan")
         for name, v in t.items():
             acc[name]["ms"] += v["ms"] / reps
             acc[name]["launches"] = v["launches"]
@@ -206,6 +242,45 @@ def kernel_sources_digest(kernel: str | None = None) -> str:
     with open(os.path.join(os.path.dirname(CSRC), "build.py"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()
+
+
+def step_counter_traffic(wl, tag: str = "") -> tuple:
+    """(bytes per step, file) from profiles/step_<workload><tag>_traffic.txt,
+    the FETCH_SIZE + WRITE_SIZE counters summed over every kernel of one step,
+    when taken on the current library sources; (None, reason) else."""
+    path = os.path.join(PROFILES, "step_%s%s_traffic.txt" % (wl.name, tag))
+    if not os.path.exists(path):
+        return None, "no step counter summary"
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_sources_digest(None):
+        return None, "library sources changed since the counters were taken"
+    try:
+        return int(fields["step_traffic_bytes"]), os.path.relpath(path, ROOT)
+    except (KeyError, ValueError):
+        return None, "malformed step counter summary"
+
+
+def host_cpu() -> dict:
+    """The host CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
 
 
 def counter_traffic(kernel: str, wl) -> tuple:
@@ -276,7 +351,7 @@ def cpu_baseline_planes(wl, inp, oracle, gy=None, merge=None) -> dict:
     what = "forward" if gs is None else "backward"
     threads = min(oracle.max_threads(), sample)  # planes run in parallel (each its own image)
     return {"value": round(per_call * 1e3 * planes / sample, 3), "unit": "ms per %s (extrapolated)" % what,
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", **host_cpu(),
             "sample": "%d of %d planes (%dx%d, every %d-th), each as its own image, all 4 directions, fp64 %s; "
                       "%d runs, %.1f s of oracle time" % (sample, planes, wl.h, wl.w, step, what, reps, spent)}
 
@@ -311,7 +386,7 @@ def cpu_baseline_proxy(wl, inp, oracle, merge=None) -> dict:
         t_up += time.perf_counter() - t
     total = t_down + t_scan + t_up
     return {"value": round(total * 1e3, 3), "unit": "ms per forward", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", **host_cpu(),
             "sample": "the whole workload once, fp64: projection down %.2f s and up %.2f s over %d-row bands "
                       "(all threads), four-direction scan of the %d proxy planes %.2f s (%d threads busy)"
                       % (t_down, t_up, band, cp, t_scan, min(oracle.max_threads(), n * cp))}
@@ -379,30 +454,32 @@ def bench_backward(args, wl):
     torch.cuda.init()
     G.lib()
     print("bench: backward, workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
-    inp = make_inputs(wl, "cuda")
+    lay = args.layout
+    inp = make_inputs(wl, "cuda")            # scan frame (also what the CPU oracle reads)
+    tin = array_layout(inp) if lay == "array" else inp
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.seed + 1000)
     gy = torch.randn(inp["x"].shape, generator=g, device="cuda", dtype=torch.float32).to(wl.torch_dtype)
-    outs = (torch.empty_like(inp["x"]), [torch.empty_like(z) for z in inp["logits"]],
-            [torch.empty_like(l) for l in inp["lam"]])
-    ws = G.backward4_workspace(inp["x"], wl.cw, with_states=train)
+    outs = (torch.empty_like(inp["x"]), [torch.empty_like(z) for z in tin["logits"]],
+            [torch.empty_like(l) for l in tin["lam"]])
+    ws = G.backward4_workspace(inp["x"], wl.cw, with_states=train, layout=lay)
     merge = merge_weights(wl, args.merge)
     dmerge = torch.empty((4, wl.c_scan), dtype=torch.float32, device="cuda") if args.merge else None
-    fws = G.forward4_workspace(inp["x"], wl.cw) if train else None
+    fws = G.forward4_workspace(inp["x"], wl.cw, lay) if train else None
     states = G.states_buffer(inp["x"]) if train else None
     y = torch.empty_like(inp["x"]) if train else None
 
     def step(times=None, ftimes=None):
         if train:
             if ftimes is None:
-                G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=y, workspace=fws,
-                                merge=merge, states=states)
+                G.gspn_forward4(tin["x"], tin["logits"], tin["lam"], chunk_len=wl.chunk, out=y, workspace=fws,
+                                merge=merge, states=states, layout=lay)
             else:
-                _, ft = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk, out=y,
-                                              workspace=fws, merge=merge, states=states)
+                _, ft = G.gspn_forward4_timed(tin["x"], tin["logits"], tin["lam"], chunk_len=wl.chunk, out=y,
+                                              workspace=fws, merge=merge, states=states, layout=lay)
                 ftimes.update(ft)
-        return G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=wl.chunk, workspace=ws,
-                                out=outs, times=times, merge=merge, dmerge=dmerge, states=states)
+        return G.gspn_backward4(tin["x"], tin["logits"], tin["lam"], gy, chunk_len=wl.chunk, workspace=ws,
+                                out=outs, times=times, merge=merge, dmerge=dmerge, states=states, layout=lay)
 
     for _ in range(args.warmup):
         step()
@@ -430,16 +507,18 @@ def bench_backward(args, wl):
         for name, v in t.as_dict().items():
             if name == "scan_kernel":
                 recompute = v
-            else:
+            elif name != "adjoint_plan":
                 acc[name] += v["ms"] / reps
         for name, v in ft.items():
-            if name != "scan_kernel":
+            if name not in ("scan_kernel", "adjoint_plan"):
                 facc[name] += v["ms"] / reps
     kernel_ms = acc["adjoint"]
     # planes of at most 64 x 64 recompute with the plane-resident forward
     # and run the plane-resident adjoint
     adj_kernel = "adjplane_kernel" if recompute == "plane4_kernel" else "adj4_kernel"
-    bpl = adjplane_launch_bytes(wl) if adj_kernel == "adjplane_kernel" else adjoint_launch_bytes(wl)
+    design = adjplane_launch_bytes(wl) if adj_kernel == "adjplane_kernel" else adjoint_launch_bytes(wl)
+    # the adjoint launch processes every unit of the backward: its compulsory bytes
+    bpl = backward_algorithmic_bytes(wl)
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
     alg = backward_algorithmic_bytes(wl) + (algorithmic_bytes(wl) if train else 0)
     eff = alg / (ms * 1e-3) / 1e9
@@ -452,7 +531,9 @@ def bench_backward(args, wl):
         print("bench: timing the CPU oracle's backward on a sample", file=sys.stderr, flush=True)
         import oracle
         cpu = cpu_baseline_planes(wl, inp, oracle, gy=gy, merge=merge)
-    traffic, traffic_src = counter_traffic(adj_kernel, wl)
+    traffic, traffic_src = counter_traffic(adj_kernel, wl) if lay == "scan" else (None, "scan layout only")
+    tag = ("_train" if train else "_backward") + ("" if lay == "scan" else "_array")
+    step_traffic, step_src = step_counter_traffic(wl, tag)
     rec = {
         "metric": ("ms per 4-direction GSPN training step (forward keeping fp32 states, then backward: dx, "
                    "dlambda, dlogits%s); achieved HBM GB/s" if train else
@@ -463,14 +544,16 @@ def bench_backward(args, wl):
         "dtype": "f32", "data": "synthetic (seeded)",
         "config": {"workload": wl.name, "pass": args.pass_, "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
-                   "merge": "learnable" if args.merge else "sum"},
+                   "merge": "learnable" if args.merge else "sum", "layout": lay},
         "ms_median": round(singles[len(singles) // 2], 4), "ms_min": round(singles[0], 4),
         "effective_GBps": round(eff, 1), "effective_frac": round(eff / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
         "stages_ms": stages,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": adj_kernel,
                      "kernel_ms": round(kernel_ms, 4), "launches_per_step": 1, "bytes_per_launch": bpl,
-                     "traffic_source": traffic_src},
+                     "traffic_source": traffic_src, "design_bytes_per_launch": design,
+                     "design_achieved": round(design / (kernel_ms * 1e-3) / 1e9, 1),
+                     "step_traffic": step_traffic, "step_traffic_source": step_src},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))
@@ -490,6 +573,9 @@ def main():
                     help="capture one step in a HIP graph and time its replays (forward only)")
     ap.add_argument("--merge", action="store_true",
                     help="merge the directions with seeded learnable weights per direction and channel")
+    ap.add_argument("--layout", default="scan", choices=("scan", "array"),
+                    help="per-direction logits / lambdas in their scan frames (default) or all in the array "
+                         "frame [.., H, W] (the library then copies the horizontal ones inside the step)")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -508,29 +594,31 @@ def main():
     torch.cuda.init()
     G.lib()
     print("bench: workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
-    inp = make_inputs(wl, "cuda")
+    lay = args.layout
+    inp = make_inputs(wl, "cuda")            # scan frame (also what the CPU oracle reads)
+    tin = array_layout(inp) if lay == "array" else inp
     out = torch.empty_like(inp["x"])
-    ws = (G.proxy_forward4_workspace(inp["x"], wl.c_proxy, wl.cw) if wl.c_proxy
-          else G.forward4_workspace(inp["x"], wl.cw))
+    ws = (G.proxy_forward4_workspace(inp["x"], wl.c_proxy, wl.cw, lay) if wl.c_proxy
+          else G.forward4_workspace(inp["x"], wl.cw, lay))
     merge = merge_weights(wl, args.merge)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        run_step(wl, inp, out, ws, merge=merge)
+        run_step(wl, tin, out, ws, merge=merge, layout=lay)
     torch.cuda.synchronize()
-    step = lambda: run_step(wl, inp, out, ws, merge=merge)
+    step = lambda: run_step(wl, tin, out, ws, merge=merge, layout=lay)
     if args.graph:
         # the library allocates nothing and launches only kernels on the
         # current stream, so one step captures whole; its replays are timed
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            run_step(wl, inp, out, ws, merge=merge)
+            run_step(wl, tin, out, ws, merge=merge, layout=lay)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            run_step(wl, inp, out, ws, merge=merge)
+            run_step(wl, tin, out, ws, merge=merge, layout=lay)
         torch.cuda.synchronize()
         step = graph.replay
         for _ in range(args.warmup):
@@ -553,13 +641,16 @@ def main():
           file=sys.stderr, flush=True)
 
     singles = per_step_ms(step, args.steps)
-    st, kernel = stage_times(wl, inp, out, ws, reps=max(3, min(args.steps, 10)), merge=merge)
+    st, kernel = stage_times(wl, tin, out, ws, reps=max(3, min(args.steps, 10)), merge=merge, layout=lay)
     scan = st["scan"]
     launches = scan["launches"]
     kernel_ms = scan["ms"] / launches
-    bpl = scan_launch_bytes(wl, kernel, launches)
+    bpl = launch_algorithmic_bytes(wl, launches)
+    design = scan_launch_bytes(wl, kernel, launches)
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
-    traffic, traffic_src = counter_traffic(kernel, wl)
+    tag = "" if lay == "scan" else "_array"
+    traffic, traffic_src = counter_traffic(kernel, wl) if lay == "scan" else (None, "scan layout only")
+    step_traffic, step_src = step_counter_traffic(wl, tag)
     alg = algorithmic_bytes(wl)
     eff = alg / (ms * 1e-3) / 1e9
     print("bench: %s %.4f ms per launch (%d per step), %.1f GB/s algorithmic"
@@ -589,7 +680,7 @@ def main():
         "config": {"workload": wl.name, "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
                    "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
                    "c_proxy": wl.c_proxy, "merge": "learnable" if args.merge else "sum",
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": "hip graph replay" if args.graph else "eager", "layout": lay},
         "ms_median": round(singles[len(singles) // 2], 4),
         "ms_min": round(singles[0], 4),
         "effective_GBps": round(eff, 1),
@@ -602,7 +693,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": kernel, "kernel_ms": round(kernel_ms, 4), "launches_per_step": launches,
-                     "bytes_per_launch": bpl, "traffic_source": traffic_src},
+                     "bytes_per_launch": bpl, "traffic_source": traffic_src,
+                     "design_bytes_per_launch": design,
+                     "design_achieved": round(design / (kernel_ms * 1e-3) / 1e9, 1),
+                     "step_traffic": step_traffic, "step_traffic_source": step_src},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

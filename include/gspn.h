@@ -37,6 +37,16 @@
  *    logits/weights of a position are ordered (k-1, k, k+1) in array order
  *    for every direction; the first line of a scan (and of each chunk) does
  *    not use its logits.
+ *    The four-direction calls (gspn_forward4, gspn_proxy_forward4,
+ *    gspn_backward4 and their workspace queries) take a `layout` argument:
+ *    GSPN_LAYOUT_SCAN is the scan-frame layout above; GSPN_LAYOUT_ARRAY
+ *    stores every direction's logits as [N][Cw][3][H][W] and lambda as
+ *    [N][C][H][W] (array frame for all four directions; so are the backward's
+ *    dlogits and dlam).  The library then copies the horizontal directions'
+ *    tensors into their scan frame inside its workspace with an LDS-tiled
+ *    transpose (and the backward's horizontal gradients back out), so this
+ *    layout needs a workspace and moves those tensors' bytes twice more.
+ *    Any other value is GSPN_ERR_BAD_LAYOUT.
  *  - dtype: every tensor of one call has the same storage type, GSPN_F32 or
  *    GSPN_BF16.  Arithmetic is always fp32 (bf16 values are widened exactly;
  *    bf16 results are rounded to nearest even at each store).
@@ -69,7 +79,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 7
+#define GSPN_ABI_VERSION 8
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -84,12 +94,17 @@ typedef enum {
     GSPN_ERR_ALIASING = 8,
     GSPN_ERR_UNSUPPORTED = 9,
     GSPN_ERR_HIP = 10,
-    GSPN_ERR_WORKSPACE = 11
+    GSPN_ERR_WORKSPACE = 11,
+    GSPN_ERR_BAD_LAYOUT = 12
 } gspn_status;
 
 typedef enum { GSPN_T2B = 0, GSPN_B2T = 1, GSPN_L2R = 2, GSPN_R2L = 3 } gspn_dir;
 
 typedef enum { GSPN_F32 = 0, GSPN_BF16 = 1 } gspn_dtype;
+
+/* Where the per-direction logits and lambdas of the four-direction calls
+ * live (see "Layouts" above). */
+typedef enum { GSPN_LAYOUT_SCAN = 0, GSPN_LAYOUT_ARRAY = 1 } gspn_layout;
 
 /*
  * gspn_normalize_weights -- sigmoid + row normalisation of one direction's
@@ -170,7 +185,7 @@ gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
  * overflowing dimensions, cw not in {1, c}, unknown dtype).
  */
 int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
-                                      int dtype);
+                                      int dtype, int layout);
 
 /*
  * gspn_forward4 -- the four-direction propagation with summed or learnable
@@ -233,7 +248,7 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
                           const void* const lam[4], const float* merge, void* y, float* states, void* workspace,
-                          int64_t workspace_bytes, int dtype, void* stream);
+                          int64_t workspace_bytes, int dtype, int layout, void* stream);
 
 /*
  * gspn_proxy_forward4_workspace_bytes -- bytes of the gspn_proxy_forward4
@@ -242,7 +257,7 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
  * w, cw).  Returns -1 for invalid arguments.
  */
 int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
-                                            int64_t cw, int dtype);
+                                            int64_t cw, int dtype, int layout);
 
 /*
  * gspn_proxy_forward4 -- the compressive-proxy propagation (GSPN-2 notes,
@@ -264,7 +279,8 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
 gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                 const void* const logits[4], const void* const lam[4], const float* merge,
-                                void* y, void* workspace, int64_t workspace_bytes, int dtype, void* stream);
+                                void* y, void* workspace, int64_t workspace_bytes, int dtype, int layout,
+                                void* stream);
 
 /*
  * gspn_backward4_workspace_bytes -- bytes of the gspn_backward4 workspace:
@@ -277,7 +293,8 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
  * floats), which a call given the states does not need: it may pass 16 *
  * n*c*h*w bytes less.  Returns -1 for invalid arguments.
  */
-int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype);
+int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype,
+                                       int layout);
 
 /*
  * gspn_backward4 -- gradients of the four-direction propagation of
@@ -316,7 +333,7 @@ gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
                            const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
                            const float* states, const void* gy, void* dx, void* const dlogits[4],
                            void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes, int dtype,
-                           void* stream);
+                           int layout, void* stream);
 
 /*
  * Stage timing of one forward call (measurement only).
@@ -343,7 +360,9 @@ typedef enum {
     GSPN_STAGE_PROJECT_UP = 5,   /* 1x1 projection C_proxy -> C */
     GSPN_STAGE_ADJOINT = 6,      /* backward: the adjoint line-scan launch */
     GSPN_STAGE_REDUCE = 7,       /* backward: clearing / storing the shared-logit sums, clearing dmerge */
-    GSPN_NUM_STAGES = 8
+    GSPN_STAGE_LAYOUT = 8,       /* GSPN_LAYOUT_ARRAY: horizontal logits / lambdas (and their gradients)
+                                    copied between the array and scan frames */
+    GSPN_NUM_STAGES = 9
 } gspn_stage;
 
 /* Which scan kernel a forward call ran (gspn_stage_times.scan_kernel). */
@@ -356,23 +375,37 @@ typedef enum {
     GSPN_SCAN_BANDED = 5        /* very few long lines: lines split across workgroups, one launch per band of steps */
 } gspn_scan_kernel;
 
+/* The adjoint launch of a backward call (gspn_stage_times.adjoint; all 0
+ * when the call ran none): the kernel family (1 = one workgroup per line and
+ * direction, 2 = one workgroup per plane for planes of at most 64 x 64), the
+ * positions each lane owns, the channels one workgroup runs together (more
+ * than 1 only for channel-shared logits, whose gradient it sums over them),
+ * and whether the streams touched once carry the non-temporal hint. */
+typedef struct {
+    int32_t family;
+    int32_t positions_per_lane;
+    int32_t channel_group;
+    int32_t nontemporal;
+} gspn_adjoint_plan;
+
 typedef struct {
     float ms[GSPN_NUM_STAGES];
     int32_t launches[GSPN_NUM_STAGES];
     int32_t scan_kernel; /* a gspn_scan_kernel value */
+    gspn_adjoint_plan adjoint;
 } gspn_stage_times;
 
 gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* const logits[4],
                                 const void* const lam[4], const float* merge, void* y, float* states,
-                                void* workspace, int64_t workspace_bytes, int dtype, void* stream,
+                                void* workspace, int64_t workspace_bytes, int dtype, int layout, void* stream,
                                 gspn_stage_times* times);
 
 gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
                                       int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
                                       const void* w_up, const void* const logits[4],
                                       const void* const lam[4], const float* merge, void* y, void* workspace,
-                                      int64_t workspace_bytes, int dtype, void* stream,
+                                      int64_t workspace_bytes, int dtype, int layout, void* stream,
                                       gspn_stage_times* times);
 
 /* gspn_backward4 with stage timing (same contract as gspn_forward4_timed);
@@ -383,7 +416,8 @@ gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int
                                  const void* x, const void* const logits[4], const void* const lam[4],
                                  const float* merge, const float* states, const void* gy, void* dx,
                                  void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
-                                 int64_t workspace_bytes, int dtype, void* stream, gspn_stage_times* times);
+                                 int64_t workspace_bytes, int dtype, int layout, void* stream,
+                                 gspn_stage_times* times);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);

@@ -182,11 +182,8 @@ __device__ __forceinline__ void adj_direction(const AdjPlaneK& a, int d, int64_t
         const int tk = t % K;
         const bool first = tk == 0;                   // the chunk's first line: no h_{t-1}, logits unused
         const bool last = tk == K - 1 || t == S - 1;  // the chunk's last line: no a_{t+1}
-        const float s0 = has_l ? sigmoid(widen<T>(rz0[s])) : 0.0f;
-        const float s1 = sigmoid(widen<T>(rz1[s]));
-        const float s2 = has_r ? sigmoid(widen<T>(rz2[s])) : 0.0f;
-        const float r = recip((s0 + s1) + s2);
-        const float w0 = s0 * r, w1 = s1 * r, w2 = s2 * r;
+        float s0, s1, s2, w0, w1, w2;
+        normalise_row_s(widen<T>(rz0[s]), widen<T>(rz1[s]), widen<T>(rz2[s]), has_l, has_r, s0, s1, s2, w0, w1, w2);
         const int pos = HORIZ ? k * ld + i : i * ld + k;
         const float from_r = from_upper_lane(qn0);  // w_{t+1}[k+1, -1] a_{t+1}[k+1]
         const float from_l = from_lower_lane(qn2);  // w_{t+1}[k-1, +1] a_{t+1}[k-1]

@@ -20,6 +20,7 @@ constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxElems = int64_t{1} << 58;
 
 bool valid_dtype(int dt) { return dt == GSPN_F32 || dt == GSPN_BF16; }
+bool valid_layout(int l) { return l == GSPN_LAYOUT_SCAN || l == GSPN_LAYOUT_ARRAY; }
 size_t elem_size(int dt) { return dt == GSPN_F32 ? 4 : 2; }
 bool valid_dir(int d) { return d >= GSPN_T2B && d <= GSPN_R2L; }
 bool horizontal(int d) { return d == GSPN_L2R || d == GSPN_R2L; }
@@ -65,6 +66,7 @@ struct Timer {
     hipEvent_t a[kMax] = {};
     hipEvent_t b[kMax] = {};
     int scan_kernel = GSPN_SCAN_NONE;
+    gspn_adjoint_plan adjoint = {0, 0, 0, 0};
 
     ~Timer() {
         for (int i = 0; i < count; ++i) {
@@ -94,6 +96,7 @@ struct Timer {
             t->launches[s] = 0;
         }
         t->scan_kernel = scan_kernel;
+        t->adjoint = adjoint;
         if (count == 0) return hipSuccess;
         hipError_t e = hipEventSynchronize(b[count - 1]);
         if (e != hipSuccess) return e;
@@ -146,6 +149,18 @@ ScanCheck check_scan(int dir, int64_t chunk_len, int64_t n, int64_t c, int64_t h
     return {GSPN_OK, K};
 }
 
+// GSPN_LAYOUT_ARRAY: bytes of the scan-frame copies of the two horizontal
+// directions' logits ([n][cw][3][w][h] each) and lambdas ([n][c][w][h] each)
+// in the storage type, rounded up to 4 bytes; -1 if that overflows.
+int64_t layout_copy_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype) {
+    const int64_t nhw = checked_product({n, h, w});
+    if (nhw < 0) return -1;
+    const int64_t elems = 2 * (3 * cw + c);  // <= 8 c, so elems * nhw < 2^61
+    const int64_t es = static_cast<int64_t>(elem_size(dtype));
+    if (nhw > 0 && elems > (INT64_MAX / 2) / es / nhw) return -1;
+    return (elems * nhw * es + 3) / 4 * 4;
+}
+
 // The four-direction launches run a workgroup per (plane, chunk) of every
 // direction: the total must fit one launch's grid.
 bool fused_grid_ok(int64_t n, int64_t c, int64_t h, int64_t w, const int64_t chunks[4]) {
@@ -177,6 +192,7 @@ const char* gspn_status_string(int status) {
             return "GSPN_ERR_UNSUPPORTED: line longer than GSPN_MAX_LINE or grid too large";
         case GSPN_ERR_HIP: return "GSPN_ERR_HIP: a HIP launch failed";
         case GSPN_ERR_WORKSPACE: return "GSPN_ERR_WORKSPACE: the workspace is smaller than required";
+        case GSPN_ERR_BAD_LAYOUT: return "GSPN_ERR_BAD_LAYOUT: layout is not GSPN_LAYOUT_SCAN or GSPN_LAYOUT_ARRAY";
         default: return "unknown gspn_status";
     }
 }
@@ -316,8 +332,8 @@ gspn_status gspn_scan4_fwd(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
 }
 
 int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
-                                      int dtype) {
-    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
+                                      int dtype, int layout) {
+    if (!valid_dtype(dtype) || !valid_layout(layout) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
     const int64_t elems = checked_product({n, c, h, w});
     const int64_t maps = 4 * elems * static_cast<int64_t>(elem_size(dtype));
     // channel-shared weights over several channels, normalised once per
@@ -326,7 +342,11 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
     const int64_t weights = (cw == 1 && c > 1) ? 4 * per_dir : 0;
     // fp32 states at band boundaries for the banded scan of very few lines
     const int64_t states = gspn::band_state_floats(checked_product({n, c}), h > w ? h : w) * 4;
-    return (maps + weights + 3) / 4 * 4 + states;
+    const int64_t base = (maps + weights + 3) / 4 * 4 + states;
+    if (layout == GSPN_LAYOUT_SCAN) return base;
+    // then the scan-frame copies of the horizontal logits and lambdas
+    const int64_t lc = layout_copy_bytes(n, c, h, w, cw, dtype);
+    return lc < 0 ? -1 : base + lc;
 }
 
 }  // extern "C"
@@ -362,10 +382,45 @@ hipError_t prenormalise(int64_t n, int64_t h, int64_t w, const void* const logit
     return hipSuccess;
 }
 
+// GSPN_LAYOUT_ARRAY: copies the horizontal directions' logits and lambdas
+// (array frame) into their scan frame at dst (layout_copy_bytes bytes) and
+// points zl / ll at the copies (a lambda given for both horizontal
+// directions is copied once).
+hipError_t copy_to_scan_frame(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, const void* const logits[4],
+                              const void* const lam[4], char* dst, int dtype, hipStream_t st, Timer* tm,
+                              const void* (&zl)[4], const void* (&ll)[4]) {
+    const int64_t es = static_cast<int64_t>(elem_size(dtype));
+    const int64_t wb = n * cw * 3 * h * w * es;
+    const int64_t lb = n * c * h * w * es;
+    for (int d = 2; d < 4; ++d) {
+        char* zt = dst + (d - 2) * wb;
+        char* lt = dst + 2 * wb + (d - 2) * lb;
+        hipError_t e = timed(tm, GSPN_STAGE_LAYOUT, [&] {
+            return gspn::launch_transpose(logits[d], zt, n * cw * 3, static_cast<int>(h), static_cast<int>(w), dtype,
+                                          st);
+        });
+        if (e != hipSuccess) return e;
+        zl[d] = zt;
+        if (d == 3 && lam[3] == lam[2]) {
+            ll[d] = ll[2];
+            continue;
+        }
+        e = timed(tm, GSPN_STAGE_LAYOUT, [&] {
+            return gspn::launch_transpose(lam[d], lt, n * c, static_cast<int>(h), static_cast<int>(w), dtype, st);
+        });
+        if (e != hipSuccess) return e;
+        ll[d] = lt;
+    }
+    return hipSuccess;
+}
+
 gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
-                          const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
-                          void* y, float* states, void* workspace, int64_t workspace_bytes, int dtype, void* stream,
-                          Timer* tm) {
+                          const void* x, const void* const logits_in[4], const void* const lam_in[4],
+                          const float* merge, void* y, float* states, void* workspace, int64_t workspace_bytes,
+                          int dtype, int layout, void* stream, Timer* tm) {
+    if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
+    const void* const* logits = logits_in;
+    const void* const* lam = lam_in;
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -376,6 +431,8 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (!x || !y || !logits || !lam) return GSPN_ERR_NULL_POINTER;
     for (int d = 0; d < 4; ++d)
         if (!logits[d] || !lam[d]) return GSPN_ERR_NULL_POINTER;
+    const bool have_ws = workspace != nullptr && workspace_bytes > 0;
+    if (layout == GSPN_LAYOUT_ARRAY && !have_ws) return GSPN_ERR_WORKSPACE;  // the copies live there
     const size_t es = elem_size(dtype);
     if (!aligned(x, es) || !aligned(y, es)) return GSPN_ERR_MISALIGNED;
     for (int d = 0; d < 4; ++d)
@@ -388,7 +445,6 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     const int64_t mgb = 4 * c * 4;  // merge weights, fp32 [4][c]
     if (merge && !aligned(merge, 4)) return GSPN_ERR_MISALIGNED;
     if (merge && overlap(y, xb, merge, mgb)) return GSPN_ERR_ALIASING;
-    const bool have_ws = workspace != nullptr && workspace_bytes > 0;
     const int64_t sb = 4 * n * c * h * w * 4;  // four fp32 state maps
     if (states) {
         // the states come from the four-direction launch, which takes lines
@@ -403,8 +459,9 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
             if (overlap(states, sb, logits[d], wb) || overlap(states, sb, lam[d], xb)) return GSPN_ERR_ALIASING;
         if (merge && overlap(states, sb, merge, mgb)) return GSPN_ERR_ALIASING;
     }
+    int64_t need = 0;
     if (have_ws) {
-        const int64_t need = gspn_forward4_workspace_bytes(n, c, h, w, cw, dtype);
+        need = gspn_forward4_workspace_bytes(n, c, h, w, cw, dtype, layout);
         if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
         if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
         if (overlap(workspace, need, y, xb) || overlap(workspace, need, x, xb)) return GSPN_ERR_ALIASING;
@@ -415,6 +472,17 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                 return GSPN_ERR_ALIASING;
     }
     const hipStream_t st = as_stream(stream);
+
+    // the per-direction tensors in their scan frames
+    const void* zl[4] = {logits[0], logits[1], logits[2], logits[3]};
+    const void* ll[4] = {lam[0], lam[1], lam[2], lam[3]};
+    if (layout == GSPN_LAYOUT_ARRAY) {
+        char* dst = static_cast<char*>(workspace) + need - layout_copy_bytes(n, c, h, w, cw, dtype);
+        if (copy_to_scan_frame(n, c, h, w, cw, logits, lam, dst, dtype, st, tm, zl, ll) != hipSuccess)
+            return GSPN_ERR_HIP;
+    }
+    logits = zl;
+    lam = ll;
 
     gspn::ScanParams p[4];
     for (int d = 0; d < 4; ++d) {
@@ -555,8 +623,9 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
 gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw, int64_t chunk_len,
                        const void* x, const void* w_down, const void* w_up, const void* const logits[4],
                        const void* const lam[4], const float* merge, void* y, void* workspace,
-                       int64_t workspace_bytes, int dtype, void* stream, Timer* tm) {
+                       int64_t workspace_bytes, int dtype, int layout, void* stream, Timer* tm) {
     if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
+    if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
     if (!dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w})) return GSPN_ERR_BAD_SHAPE;
     if (chunk_len < 0) return GSPN_ERR_BAD_CHUNK;
     if (!(cw == 1 || cw == c_proxy)) return GSPN_ERR_BAD_WEIGHT_CHANNELS;
@@ -569,7 +638,7 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
     const size_t es = elem_size(dtype);
     if (!aligned(x, es) || !aligned(y, es) || !aligned(w_down, es) || !aligned(w_up, es))
         return GSPN_ERR_MISALIGNED;
-    const int64_t need = gspn_proxy_forward4_workspace_bytes(n, c, h, w, c_proxy, cw, dtype);
+    const int64_t need = gspn_proxy_forward4_workspace_bytes(n, c, h, w, c_proxy, cw, dtype, layout);
     if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
     if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
     const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
@@ -598,17 +667,22 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
               [&] { return gspn::launch_project(n, c, h * w, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
     const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, nullptr, fws,
-                                         need - 2 * pb, dtype, stream, tm);
+                                         need - 2 * pb, dtype, layout, stream, tm);
     if (s4 != GSPN_OK) return s4;
     return from_hip(timed(tm, GSPN_STAGE_PROJECT_UP,
                           [&] { return gspn::launch_project(n, c_proxy, h * w, c, yp, w_up, y, dtype, st); }));
 }
 
 gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len, const void* x,
-                          const void* const logits[4], const void* const lam[4], const float* merge,
-                          const float* states, const void* gy, void* dx, void* const dlogits[4], void* const dlam[4],
-                          float* dmerge, void* workspace, int64_t workspace_bytes, int dtype, void* stream,
-                          Timer* tm) {
+                          const void* const logits_in[4], const void* const lam_in[4], const float* merge,
+                          const float* states, const void* gy, void* dx, void* const dlogits_in[4],
+                          void* const dlam_in[4], float* dmerge, void* workspace, int64_t workspace_bytes, int dtype,
+                          int layout, void* stream, Timer* tm) {
+    if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
+    const void* const* logits = logits_in;
+    const void* const* lam = lam_in;
+    void* const* dlogits = dlogits_in;
+    void* const* dlam = dlam_in;
     int64_t chunks[4];
     for (int d = 0; d < 4; ++d) {
         bool empty = false;
@@ -623,7 +697,7 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     const size_t es = elem_size(dtype);
     const int64_t hb = n * c * h * w * 4;  // bytes of one fp32 state map
     // given the states, the workspace's last part (room for them) is not needed
-    const int64_t need = gspn_backward4_workspace_bytes(n, c, h, w, cw, dtype) - (states ? 4 * hb : 0);
+    const int64_t need = gspn_backward4_workspace_bytes(n, c, h, w, cw, dtype, layout) - (states ? 4 * hb : 0);
     if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
     if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
     if (!aligned(x, es) || !aligned(gy, es) || !aligned(dx, es)) return GSPN_ERR_MISALIGNED;
@@ -693,14 +767,52 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     dterm[1] = gt + xb;
     dterm[2] = dterm[1] + xb;
     dterm[3] = dterm[2] + xb;
-    // the recomputed states after the five storage-type maps, rounded up to
-    // 4 bytes (the sums and weights before them are whole floats)
+    // after the five storage-type maps, rounded up to 4 bytes (the sums and
+    // weights before them are whole floats): for GSPN_LAYOUT_ARRAY the
+    // scan-frame copies of the horizontal inputs, then room for the
+    // horizontal gradients in their scan frame; last, the recomputed states
     char* hs[4];
-    const int64_t hoff = ((dterm[3] - ws) + xb + 3) / 4 * 4;
+    const int64_t loff = ((dterm[3] - ws) + xb + 3) / 4 * 4;
+    const int64_t lc = layout == GSPN_LAYOUT_ARRAY ? layout_copy_bytes(n, c, h, w, cw, dtype) : 0;
+    const int64_t hoff = loff + 2 * lc;
     hs[0] = states ? reinterpret_cast<char*>(const_cast<float*>(states)) : ws + hoff;
     for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
     const int H = static_cast<int>(h);
     const int W = static_cast<int>(w);
+
+    // GSPN_LAYOUT_ARRAY: inputs copied into their scan frame; the horizontal
+    // gradients are computed in the scan frame and copied out at the end
+    const void* zl[4] = {logits[0], logits[1], logits[2], logits[3]};
+    const void* ll[4] = {lam[0], lam[1], lam[2], lam[3]};
+    void* dzl[4] = {dlogits[0], dlogits[1], dlogits[2], dlogits[3]};
+    void* dll[4] = {dlam[0], dlam[1], dlam[2], dlam[3]};
+    if (layout == GSPN_LAYOUT_ARRAY) {
+        if (copy_to_scan_frame(n, c, h, w, cw, logits, lam, ws + loff, dtype, st, tm, zl, ll) != hipSuccess)
+            return GSPN_ERR_HIP;
+        char* gdst = ws + loff + lc;
+        for (int d = 2; d < 4; ++d) {
+            dzl[d] = gdst + (d - 2) * wb;
+            dll[d] = gdst + 2 * wb + (d - 2) * xb;
+        }
+    }
+    logits = zl;
+    lam = ll;
+    dlogits = dzl;
+    dlam = dll;
+    // copies the horizontal gradients out into the caller's array-frame buffers
+    auto copy_out = [&]() -> gspn_status {
+        if (layout != GSPN_LAYOUT_ARRAY) return GSPN_OK;
+        for (int d = 2; d < 4; ++d) {
+            if (timed(tm, GSPN_STAGE_LAYOUT, [&] {
+                    return gspn::launch_transpose(dzl[d], dlogits_in[d], n * cw * 3, W, H, dtype, st);
+                }) != hipSuccess ||
+                timed(tm, GSPN_STAGE_LAYOUT, [&] {
+                    return gspn::launch_transpose(dll[d], dlam_in[d], n * c, W, H, dtype, st);
+                }) != hipSuccess)
+                return GSPN_ERR_HIP;
+        }
+        return GSPN_OK;
+    };
 
     // Planes of at most 64 x 64 (recomputed states only): one launch over
     // LDS-resident planes recomputes the four directions' states into the
@@ -739,6 +851,7 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         ap.dtype = dtype;
         if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjplane(ap, st); }) != hipSuccess)
             return GSPN_ERR_HIP;
+        if (tm) tm->adjoint = {2, 1, 1, 0};  // one lane per position, one plane per workgroup
         if (shared) {
             for (int d = 0; d < 4; ++d)
                 if (timed(tm, GSPN_STAGE_REDUCE, [&] {
@@ -747,7 +860,7 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                     }) != hipSuccess)
                     return GSPN_ERR_HIP;
         }
-        return GSPN_OK;
+        return copy_out();
     }
 
     if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] { return gspn::launch_transpose(x, xt, n * c, H, W, dtype, st); }) !=
@@ -819,8 +932,10 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         a[d].mscale = merge ? merge + d * c : nullptr;
         a[d].dmerge = dmerge ? dmerge + d * c : nullptr;
     }
-    if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjoint4(a, st); }) != hipSuccess)
+    gspn::AdjointPlan plan{};
+    if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjoint4(a, st, &plan); }) != hipSuccess)
         return GSPN_ERR_HIP;
+    if (tm) tm->adjoint = {1, plan.positions, plan.group, plan.nontemporal};
     // dx = ((D2^T + D3^T) + D0) + D1, D0 written into dx directly
     if (timed(tm, GSPN_STAGE_COMBINE, [&] {
             return gspn::launch_combine(dx, dterm[1], dterm[2], dterm[3], n * c, H, W, 1, dtype, st);
@@ -834,7 +949,7 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                 }) != hipSuccess)
                 return GSPN_ERR_HIP;
     }
-    return GSPN_OK;
+    return copy_out();
 }
 
 }  // namespace
@@ -844,30 +959,30 @@ extern "C" {
 gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                           int64_t chunk_len, const void* x, const void* const logits[4],
                           const void* const lam[4], const float* merge, void* y, float* states, void* workspace,
-                          int64_t workspace_bytes, int dtype, void* stream) {
+                          int64_t workspace_bytes, int dtype, int layout, void* stream) {
     return forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, states, workspace, workspace_bytes,
-                         dtype, stream, nullptr);
+                         dtype, layout, stream, nullptr);
 }
 
 gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* const logits[4],
                                 const void* const lam[4], const float* merge, void* y, float* states,
-                                void* workspace, int64_t workspace_bytes, int dtype, void* stream,
+                                void* workspace, int64_t workspace_bytes, int dtype, int layout, void* stream,
                                 gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
     const gspn_status s = forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, states, workspace,
-                                        workspace_bytes, dtype, stream, &tm);
+                                        workspace_bytes, dtype, layout, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }
 
 int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
-                                            int64_t cw, int dtype) {
+                                            int64_t cw, int dtype, int layout) {
     if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w}) || c_proxy < 1)
         return -1;
-    const int64_t f4 = gspn_forward4_workspace_bytes(n, c_proxy, h, w, cw, dtype);
+    const int64_t f4 = gspn_forward4_workspace_bytes(n, c_proxy, h, w, cw, dtype, layout);
     if (f4 < 0) return -1;
     return 2 * checked_product({n, c_proxy, h, w}) * static_cast<int64_t>(elem_size(dtype)) + f4;
 }
@@ -875,28 +990,30 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
 gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                 const void* const logits[4], const void* const lam[4], const float* merge,
-                                void* y, void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
+                                void* y, void* workspace, int64_t workspace_bytes, int dtype, int layout,
+                                void* stream) {
     return proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, y, workspace,
-                      workspace_bytes, dtype, stream, nullptr);
+                      workspace_bytes, dtype, layout, stream, nullptr);
 }
 
 gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
                                       int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
                                       const void* w_up, const void* const logits[4],
                                       const void* const lam[4], const float* merge, void* y, void* workspace,
-                                      int64_t workspace_bytes, int dtype, void* stream,
+                                      int64_t workspace_bytes, int dtype, int layout, void* stream,
                                       gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
     const gspn_status s = proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, y,
-                                     workspace, workspace_bytes, dtype, stream, &tm);
+                                     workspace, workspace_bytes, dtype, layout, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }
 
-int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype) {
-    if (!valid_dtype(dtype) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
+int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int dtype,
+                                       int layout) {
+    if (!valid_dtype(dtype) || !valid_layout(layout) || !dims_ok({n, c, h, w}) || !(cw == 1 || cw == c)) return -1;
     const int64_t elems = checked_product({n, c, h, w});
     // x^T, gy^T and three dx terms in the storage type, rounded up to 4
     // bytes; four fp32 state maps (last, so that a caller passing the states
@@ -906,28 +1023,33 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
     const int64_t maps = (5 * elems * static_cast<int64_t>(elem_size(dtype)) + 3) / 4 * 4 + 4 * elems * 4;
     const int64_t nhw = checked_product({n, h, w});
     const int64_t shared = (cw == 1 && c > 1) ? 4 * 3 * nhw * 4 + 4 * nhw * (dtype == GSPN_F32 ? 3 * 4 : 4) : 0;
-    return shared + maps;
+    if (layout == GSPN_LAYOUT_SCAN) return shared + maps;
+    // the scan-frame copies of the horizontal inputs and room for their
+    // gradients, before the states
+    const int64_t lc = layout_copy_bytes(n, c, h, w, cw, dtype);
+    return lc < 0 ? -1 : shared + maps + 2 * lc;
 }
 
 gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                            const void* x, const void* const logits[4], const void* const lam[4], const float* merge,
                            const float* states, const void* gy, void* dx, void* const dlogits[4],
                            void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes, int dtype,
-                           void* stream) {
+                           int layout, void* stream) {
     return backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, states, gy, dx, dlogits, dlam, dmerge,
-                         workspace, workspace_bytes, dtype, stream, nullptr);
+                         workspace, workspace_bytes, dtype, layout, stream, nullptr);
 }
 
 gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                                  const void* x, const void* const logits[4], const void* const lam[4],
                                  const float* merge, const float* states, const void* gy, void* dx,
                                  void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
-                                 int64_t workspace_bytes, int dtype, void* stream, gspn_stage_times* times) {
+                                 int64_t workspace_bytes, int dtype, int layout, void* stream,
+                                 gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
     const gspn_status s = backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, states, gy, dx, dlogits,
-                                        dlam, dmerge, workspace, workspace_bytes, dtype, stream, &tm);
+                                        dlam, dmerge, workspace, workspace_bytes, dtype, layout, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }

@@ -203,16 +203,8 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
         for (int j = 0; j < P; ++j) {
             const bool has_l = k0 + j > 0;
             const bool has_r = k0 + j + 1 < L;
-            const float s0 = has_l ? sigmoid(rz[s][0][j]) : 0.0f;
-            const float s1 = sigmoid(rz[s][1][j]);
-            const float s2 = has_r ? sigmoid(rz[s][2][j]) : 0.0f;
-            const float r = recip((s0 + s1) + s2);
-            sg[0][j] = s0;
-            sg[1][j] = s1;
-            sg[2][j] = s2;
-            w[0][j] = s0 * r;
-            w[1][j] = s1 * r;
-            w[2][j] = s2 * r;
+            normalise_row_s(rz[s][0][j], rz[s][1][j], rz[s][2][j], has_l, has_r, sg[0][j], sg[1][j], sg[2][j],
+                            w[0][j], w[1][j], w[2][j]);
         }
         float dw[P][3];  // weight gradient summed over the group
 #pragma unroll
@@ -366,11 +358,9 @@ __global__ __launch_bounds__(256) void finish_shared_dz_kernel(const float* __re
         const int64_t base = img * 3 * plane + r;
         const bool has_l = k > 0;
         const bool has_r = k + 1 < L;
-        const float s0 = has_l ? sigmoid(Store<T>::ld(z + base)) : 0.0f;
-        const float s1 = sigmoid(Store<T>::ld(z + base + plane));
-        const float s2 = has_r ? sigmoid(Store<T>::ld(z + base + 2 * plane)) : 0.0f;
-        const float rr = recip((s0 + s1) + s2);
-        const float w0 = s0 * rr, w1 = s1 * rr, w2 = s2 * rr;
+        float s0, s1, s2, w0, w1, w2;
+        normalise_row_s(Store<T>::ld(z + base), Store<T>::ld(z + base + plane), Store<T>::ld(z + base + 2 * plane),
+                        has_l, has_r, s0, s1, s2, w0, w1, w2);
         const float e0 = src[base], e2 = src[base + plane];
         const float dot = w0 * e0 + w2 * e2;
         float d0 = w0 * (1.0f - s0) * (e0 - dot);
@@ -394,7 +384,7 @@ unsigned grid_for(int64_t total) {
 
 }  // namespace
 
-hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
+hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, AdjointPlan* plan) {
     Adj4K k;
     int maxL = 1;
     int64_t total = 0;
@@ -436,6 +426,7 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream) {
     // non-temporal streams only when every line is a whole number of cache lines
     bool nt = true;
     for (int d = 0; d < 4; ++d) nt = nt && (p[d].L * (f32 ? 4 : 2)) % 128 == 0;
+    if (plan) *plan = {P, G, nt ? 1 : 0};
 #define GSPN_ADJ_LAUNCH(PP, GG, MM)                                                                               \
     do {                                                                                                          \
         if (f32) {                                                                                                \

@@ -91,27 +91,68 @@ __device__ __forceinline__ float recip(float d) {
     return __builtin_fmaf(r, e, r);
 }
 
-// Logistic sigmoid 1 / (1 + e^{-z}).  e^{-z} is evaluated as 2^{-z log2 e}
-// with the hardware exp2; it saturates to +inf for z below about -88, which
-// gives sigmoid = 0, and to 0 for large z, which gives 1.
+// Logistic sigmoid 1 / (1 + e^{-z}), to within about 2 ulp over the range
+// where it is a normal number.  e^{-z} is 2^{-z log2 e}; the product -z log2 e
+// is rounded to fp32, and that rounding alone would cost up to |z| ulp of
+// relative error in e^{-z} (20 ulp at z = -20).  Its exact error is recovered
+// with one fma (the TwoProduct identity of Ogita, Rump and Oishi, "Accurate
+// sum and dot product", 2005), the error of the fp32 constant is added, and
+// both enter as the first-order factor 2^err ~ 1 + err ln 2.  The hardware
+// exp2 and reciprocal (1 ulp each) finish it (a Newton step on the
+// reciprocal measured no more accurate: 3.4 ulp at most on the normalised
+// weights either way, mean 0.57 ulp, over z in [-20, 20]).  The exponent is
+// capped at 126 (before the correction, which must not meet an infinity), so
+// for z below about -87 the result saturates at 2^-126 instead of going
+// subnormal or to 0 (a row whose every sigmoid is that small is normalised by
+// normalise_row_s's exact fallback); NaN propagates.
 __device__ __forceinline__ float sigmoid(float z) {
-    const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+    constexpr float kL2E = 1.44269502162933349609375f;   // log2 e rounded to fp32
+    constexpr float kL2ELo = 1.925963033500011e-08f;     // log2 e - kL2E
+    constexpr float kLn2 = 0.693147182464599609375f;
+    const float t = -z * kL2E;
+    const float tc = t > 126.0f ? 126.0f : t;  // NaN compares false and stays NaN
+    const float err = __builtin_fabsf(t) < 126.0f ? __builtin_fmaf(-z, kL2E, -t) + -z * kL2ELo : 0.0f;
+    float e = __builtin_amdgcn_exp2f(tc);
+    e = __builtin_fmaf(e, err * kLn2, e);
     return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Row normalisation of one tridiagonal row (GSPN summary page, "Approach":
-// sigmoid then division by the row sum, so the row sums to 1).  has_l /
-// has_r say whether the neighbours k-1 / k+1 exist on the line; a missing
-// neighbour gets weight exactly 0 and is left out of the sum.
-__device__ __forceinline__ void normalise_row(float z0, float z1, float z2, bool has_l, bool has_r,
-                                              float& w0, float& w1, float& w2) {
-    const float s0 = has_l ? sigmoid(z0) : 0.0f;
-    const float s1 = sigmoid(z1);
-    const float s2 = has_r ? sigmoid(z2) : 0.0f;
-    const float r = recip((s0 + s1) + s2);
+// sigmoid then division by the row sum, so the row sums to 1), keeping the
+// sigmoids s (the backward's Jacobian needs them).  has_l / has_r say whether
+// the neighbours k-1 / k+1 exist on the line; a missing neighbour gets weight
+// exactly 0 and is left out of the sum.  When every sigmoid of the row is
+// below 2^-100 (every existing logit below about -69) the sum could underflow,
+// so the weights are taken as e^{z_o - max z} / sum instead: there
+// 1 + e^{z} rounds to 1 in fp32, so sigmoid(z) = e^{z} and the two forms agree
+// to fp32 precision.  That branch is not taken for ordinary logits.
+__device__ __forceinline__ void normalise_row_s(float z0, float z1, float z2, bool has_l, bool has_r, float& s0,
+                                                float& s1, float& s2, float& w0, float& w1, float& w2) {
+    s0 = has_l ? sigmoid(z0) : 0.0f;
+    s1 = sigmoid(z1);
+    s2 = has_r ? sigmoid(z2) : 0.0f;
+    const float sum = (s0 + s1) + s2;
+    const float r = recip(sum);
     w0 = s0 * r;
     w1 = s1 * r;
     w2 = s2 * r;
+    if (sum < 0x1p-100f) {
+        constexpr float kL2E = 1.44269502162933349609375f;
+        const float m = __builtin_fmaxf(__builtin_fmaxf(has_l ? z0 : z1, z1), has_r ? z2 : z1);
+        const float e0 = has_l ? __builtin_amdgcn_exp2f((z0 - m) * kL2E) : 0.0f;
+        const float e1 = __builtin_amdgcn_exp2f((z1 - m) * kL2E);
+        const float e2 = has_r ? __builtin_amdgcn_exp2f((z2 - m) * kL2E) : 0.0f;
+        const float re = recip((e0 + e1) + e2);  // the largest term is 1: the sum lies in [1, 3]
+        w0 = e0 * re;
+        w1 = e1 * re;
+        w2 = e2 * re;
+    }
+}
+
+__device__ __forceinline__ void normalise_row(float z0, float z1, float z2, bool has_l, bool has_r, float& w0,
+                                              float& w1, float& w2) {
+    float s0, s1, s2;
+    normalise_row_s(z0, z1, z2, has_l, has_r, s0, s1, s2, w0, w1, w2);
 }
 
 }  // namespace gspn

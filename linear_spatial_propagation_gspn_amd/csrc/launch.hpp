@@ -121,7 +121,15 @@ struct AdjointParams {
     float* dmerge = nullptr;        // its gradient [c], fp32, added into (null: not wanted)
 };
 
-hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream);
+// What launch_adjoint4 ran: positions per lane, channels per workgroup (the
+// shared-logit gradient is summed over them) and whether the streams touched
+// once carry the non-temporal hint.
+struct AdjointPlan {
+    int positions;
+    int group;
+    int nontemporal;
+};
+hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, AdjointPlan* plan = nullptr);
 
 // All four directions' adjoint for planes of at most 64 x 64, one workgroup
 // per plane (x, gy and dx in the array frame; the per-direction tensors in

@@ -30,8 +30,11 @@ STATUS = {
     0: "GSPN_OK", 1: "GSPN_ERR_NULL_POINTER", 2: "GSPN_ERR_BAD_SHAPE", 3: "GSPN_ERR_BAD_DIRECTION",
     4: "GSPN_ERR_BAD_DTYPE", 5: "GSPN_ERR_BAD_CHUNK", 6: "GSPN_ERR_BAD_WEIGHT_CHANNELS",
     7: "GSPN_ERR_MISALIGNED", 8: "GSPN_ERR_ALIASING", 9: "GSPN_ERR_UNSUPPORTED", 10: "GSPN_ERR_HIP",
-    11: "GSPN_ERR_WORKSPACE",
+    11: "GSPN_ERR_WORKSPACE", 12: "GSPN_ERR_BAD_LAYOUT",
 }
+
+# gspn_layout: where the per-direction logits / lambdas live.
+LAYOUTS = {"scan": 0, "array": 1}
 
 # Symbols declared in include/gspn.h.
 EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy_project",
@@ -41,21 +44,33 @@ EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy
            "gspn_status_string", "gspn_abi_version")
 
 # gspn_stage, in order.
-STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up", "adjoint", "reduce")
+STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up", "adjoint", "reduce", "layout")
 
 
 # gspn_scan_kernel, in order.
 SCAN_KERNELS = ("none", "scan_kernel", "scan4v_kernel", "scan4lp_kernel", "plane4_kernel", "scan4band_kernel")
 
 
+class AdjointPlan(ctypes.Structure):
+    _fields_ = [("family", ctypes.c_int32), ("positions_per_lane", ctypes.c_int32),
+                ("channel_group", ctypes.c_int32), ("nontemporal", ctypes.c_int32)]
+
+
+# gspn_adjoint_plan.family, in order.
+ADJOINT_FAMILIES = ("none", "adj4_kernel", "adjplane_kernel")
+
+
 class StageTimes(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_float * len(STAGES)), ("launches", ctypes.c_int32 * len(STAGES)),
-                ("scan_kernel", ctypes.c_int32)]
+                ("scan_kernel", ctypes.c_int32), ("adjoint", AdjointPlan)]
 
     def as_dict(self) -> dict:
         d = {name: {"ms": float(self.ms[i]), "launches": int(self.launches[i])}
              for i, name in enumerate(STAGES)}
         d["scan_kernel"] = SCAN_KERNELS[self.scan_kernel]
+        a = self.adjoint
+        d["adjoint_plan"] = {"kernel": ADJOINT_FAMILIES[a.family], "positions_per_lane": int(a.positions_per_lane),
+                             "channel_group": int(a.channel_group), "nontemporal": bool(a.nontemporal)}
         return d
 
 
@@ -87,15 +102,15 @@ def lib() -> ctypes.CDLL:
             h.gspn_scan4_fwd.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), ctypes.POINTER(vp), ci, vp]
             h.gspn_scan4_fwd.restype = ci
-            h.gspn_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
+            h.gspn_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci, ci]
             h.gspn_forward4_workspace_bytes.restype = i64
-            h.gspn_proxy_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+            h.gspn_proxy_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci]
             h.gspn_proxy_forward4_workspace_bytes.restype = i64
             h.gspn_proxy_forward4.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp,
-                                              ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, i64, ci, vp]
+                                              ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, i64, ci, ci, vp]
             h.gspn_proxy_forward4.restype = ci
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
-                                        ctypes.POINTER(vp), vp, vp, vp, vp, i64, ci, vp]
+                                        ctypes.POINTER(vp), vp, vp, vp, vp, i64, ci, ci, vp]
             h.gspn_forward4_timed.argtypes = h.gspn_forward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_forward4_timed.restype = ci
             h.gspn_proxy_forward4_timed.argtypes = h.gspn_proxy_forward4.argtypes + [ctypes.POINTER(StageTimes)]
@@ -103,10 +118,10 @@ def lib() -> ctypes.CDLL:
             for name in ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4",
                          "gspn_proxy_project", "gspn_forward4"):
                 getattr(h, name).restype = ci
-            h.gspn_backward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci]
+            h.gspn_backward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci, ci]
             h.gspn_backward4_workspace_bytes.restype = i64
             h.gspn_backward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
-                                         vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, i64, ci, vp]
+                                         vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, i64, ci, ci, vp]
             h.gspn_backward4.restype = ci
             h.gspn_backward4_timed.argtypes = h.gspn_backward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_backward4_timed.restype = ci
@@ -155,6 +170,19 @@ def _raise(st: int, call: str) -> None:
 def frame_shape(direction: int, h: int, w: int) -> tuple[int, int]:
     """(S, L): scan steps and line length of a direction."""
     return (w, h) if direction in (L2R, R2L) else (h, w)
+
+
+def _layout_code(layout: str) -> int:
+    if layout not in LAYOUTS:
+        raise ValueError("layout must be one of %s, got %r" % (tuple(LAYOUTS), layout))
+    return LAYOUTS[layout]
+
+
+def tensor_frame(direction: int, h: int, w: int, layout: str = "scan") -> tuple[int, int]:
+    """(rows, cols) of a direction's logit / lambda planes in ``layout``:
+    its scan frame (S, L) for "scan", (H, W) for "array"."""
+    _layout_code(layout)
+    return (h, w) if layout == "array" else frame_shape(direction, h, w)
 
 
 def to_scan_frame(t: torch.Tensor, direction: int) -> torch.Tensor:
@@ -254,16 +282,16 @@ def gspn_scan4_fwd(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
     return list(outs)
 
 
-def gspn_forward4_workspace_bytes(x: torch.Tensor, cw: int) -> int:
+def gspn_forward4_workspace_bytes(x: torch.Tensor, cw: int, layout: str = "scan") -> int:
     """Bytes of the optional gspn_forward4 workspace for inputs shaped like x
     with cw weight channels (1 = channel-shared)."""
     n, c, h, w = x.shape
-    return int(lib().gspn_forward4_workspace_bytes(n, c, h, w, cw, _dtype_code(x)))
+    return int(lib().gspn_forward4_workspace_bytes(n, c, h, w, cw, _dtype_code(x), _layout_code(layout)))
 
 
-def forward4_workspace(x: torch.Tensor, cw: int) -> torch.Tensor:
+def forward4_workspace(x: torch.Tensor, cw: int, layout: str = "scan") -> torch.Tensor:
     """A workspace buffer (uint8 tensor on x's device) for gspn_forward4."""
-    nbytes = gspn_forward4_workspace_bytes(x, cw)
+    nbytes = gspn_forward4_workspace_bytes(x, cw, layout)
     if nbytes < 0:
         raise ValueError("invalid shape for a gspn_forward4 workspace")
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
@@ -299,13 +327,14 @@ def _states_ptr(states, x):
     return _ptr(states)
 
 
-def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None, states=None):
+def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None, states=None, layout="scan"):
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
+    lc = _layout_code(layout)
     _check(x, "x", (n, c, h, w), dt, x.device)
     for d in range(4):
-        S, L = frame_shape(d, h, w)
+        S, L = tensor_frame(d, h, w, layout)
         _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
         _check(lams[d], "lam[%d]" % d, (n, c, S, L), dt, x.device)
     if out is None:
@@ -321,7 +350,7 @@ def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None, sta
     mp = _merge_ptr(merge, c, x.device)
     sp = _states_ptr(states, x)
     args = (n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp, mp, _ptr(out), sp, ws_ptr, ws_bytes, _dtype_code(x),
-            _stream(x.device))
+            lc, _stream(x.device))
     if times is None:
         _raise(lib().gspn_forward4(*args), "gspn_forward4")
     else:
@@ -332,67 +361,70 @@ def _forward4(x, logits, lams, chunk_len, out, workspace, times, merge=None, sta
 def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                   chunk_len: int = 0, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None,
-                  states: torch.Tensor | bool | None = None):
+                  states: torch.Tensor | bool | None = None, layout: str = "scan"):
     """Four-direction propagation; logits[d] / lams[d] in direction d's scan
-    frame.  The directions are summed, or with ``merge`` (fp32 [4][C] on the
-    device) weighted per direction and channel.  ``workspace`` (see
-    forward4_workspace) lets the library run the four directions
-    concurrently when that pays.  ``states`` (True, or a buffer from
-    states_buffer) also keeps the four directions' fp32 scans for
+    frame (layout "scan") or all in the array frame [.., H, W] (layout
+    "array", which needs the workspace).  The directions are summed, or with
+    ``merge`` (fp32 [4][C] on the device) weighted per direction and channel.
+    ``workspace`` (see forward4_workspace) lets the library run the four
+    directions concurrently when that pays.  ``states`` (True, or a buffer
+    from states_buffer) also keeps the four directions' fp32 scans for
     gspn_backward4 (needs the workspace); the call then returns (out,
     states)."""
     if states is True:
         states = states_buffer(x)
     if states is None or states is False:
-        return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge)
-    return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge, states), states
+        return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge, layout=layout)
+    return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge, states, layout), states
 
 
 def gspn_forward4_timed(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                         chunk_len: int = 0, out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None,
                         merge: torch.Tensor | None = None,
-                        states: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+                        states: torch.Tensor | None = None, layout: str = "scan") -> tuple[torch.Tensor, dict]:
     """gspn_forward4 with HIP events around every launch; returns (out,
     {stage: {"ms", "launches"}}).  Waits for the stream to reach its end."""
     times = StageTimes()
-    out = _forward4(x, logits, lams, chunk_len, out, workspace, times, merge, states)
+    out = _forward4(x, logits, lams, chunk_len, out, workspace, times, merge, states, layout)
     return out, times.as_dict()
 
 
-def proxy_forward4_workspace(x: torch.Tensor, c_proxy: int, cw: int) -> torch.Tensor:
+def proxy_forward4_workspace(x: torch.Tensor, c_proxy: int, cw: int, layout: str = "scan") -> torch.Tensor:
     """A workspace buffer (uint8 tensor on x's device) for gspn_proxy_forward4."""
     n, c, h, w = x.shape
-    nbytes = int(lib().gspn_proxy_forward4_workspace_bytes(n, c, h, w, c_proxy, cw, _dtype_code(x)))
+    nbytes = int(lib().gspn_proxy_forward4_workspace_bytes(n, c, h, w, c_proxy, cw, _dtype_code(x),
+                                                           _layout_code(layout)))
     if nbytes < 0:
         raise ValueError("invalid shape for a gspn_proxy_forward4 workspace")
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
-def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge=None):
+def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge=None, layout="scan"):
     n, c, h, w = x.shape
     dt = x.dtype
     cp = w_down.shape[0]
     cw = logits[0].shape[1]
+    lc = _layout_code(layout)
     _check(x, "x", (n, c, h, w), dt, x.device)
     _check(w_down, "w_down", (cp, c), dt, x.device)
     _check(w_up, "w_up", (c, cp), dt, x.device)
     for d in range(4):
-        S, L = frame_shape(d, h, w)
+        S, L = tensor_frame(d, h, w, layout)
         _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
         _check(lams[d], "lam[%d]" % d, (n, cp, S, L), dt, x.device)
     if out is None:
         out = torch.empty_like(x)
     _check(out, "out", (n, c, h, w), dt, x.device)
     if workspace is None:
-        workspace = proxy_forward4_workspace(x, cp, cw)
+        workspace = proxy_forward4_workspace(x, cp, cw, layout)
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
     mp = _merge_ptr(merge, cp, x.device)
     args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up), zp, lp, mp, _ptr(out),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x), _stream(x.device))
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x), lc, _stream(x.device))
     if times is None:
         _raise(lib().gspn_proxy_forward4(*args), "gspn_proxy_forward4")
     else:
@@ -403,31 +435,32 @@ def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, ti
 def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
                         logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                         chunk_len: int = 0, out: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None) -> torch.Tensor:
+                        workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None,
+                        layout: str = "scan") -> torch.Tensor:
     """Compressive-proxy forward: C -> C_proxy 1x1 projection, four-direction
     scan in proxy space (summed, or weighted by ``merge`` fp32 [4][C_proxy]),
     C_proxy -> C projection."""
-    return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None, merge)
+    return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None, merge, layout)
 
 
 def gspn_proxy_forward4_timed(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
                               logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                               chunk_len: int = 0, out: torch.Tensor | None = None,
                               workspace: torch.Tensor | None = None,
-                              merge: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+                              merge: torch.Tensor | None = None, layout: str = "scan") -> tuple[torch.Tensor, dict]:
     """gspn_proxy_forward4 with HIP events around every launch; returns (out,
     {stage: {"ms", "launches"}})."""
     times = StageTimes()
-    out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge)
+    out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge, layout)
     return out, times.as_dict()
 
 
-def backward4_workspace(x: torch.Tensor, cw: int, with_states: bool = False) -> torch.Tensor:
+def backward4_workspace(x: torch.Tensor, cw: int, with_states: bool = False, layout: str = "scan") -> torch.Tensor:
     """A workspace buffer (uint8 tensor on x's device) for gspn_backward4;
     with_states: for calls given the forward states (16 * x.numel() bytes
     smaller)."""
     n, c, h, w = x.shape
-    nbytes = int(lib().gspn_backward4_workspace_bytes(n, c, h, w, cw, _dtype_code(x)))
+    nbytes = int(lib().gspn_backward4_workspace_bytes(n, c, h, w, cw, _dtype_code(x), _layout_code(layout)))
     if nbytes < 0:
         raise ValueError("invalid shape for a gspn_backward4 workspace")
     if with_states:
@@ -439,21 +472,23 @@ def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
                    gy: torch.Tensor, chunk_len: int = 0, workspace: torch.Tensor | None = None,
                    out: tuple | None = None, times: StageTimes | None = None,
                    merge: torch.Tensor | None = None, dmerge: torch.Tensor | bool | None = None,
-                   states: torch.Tensor | None = None) -> tuple:
+                   states: torch.Tensor | None = None, layout: str = "scan") -> tuple:
     """Gradients of gspn_forward4 (with the same ``merge``) for dL/dy = gy:
     returns (dx, [dlogits_d], [dlam_d]) in the inputs' layouts, and also the
     merge weights' gradient (fp32 [4][C]) as a fourth element when ``merge``
     is given or ``dmerge`` is (a tensor to fill, or True).  ``out`` may
     supply the first three; ``times`` (a StageTimes) selects
     gspn_backward4_timed and receives the stage durations; ``states`` (from
-    gspn_forward4) spares the recompute of the forward."""
+    gspn_forward4) spares the recompute of the forward; ``layout`` as in
+    gspn_forward4 (the gradients come in the same layout as the inputs)."""
     n, c, h, w = x.shape
     dt = x.dtype
     cw = logits[0].shape[1]
+    lc = _layout_code(layout)
     _check(x, "x", (n, c, h, w), dt, x.device)
     _check(gy, "gy", (n, c, h, w), dt, x.device)
     for d in range(4):
-        S, L = frame_shape(d, h, w)
+        S, L = tensor_frame(d, h, w, layout)
         _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
         _check(lams[d], "lam[%d]" % d, (n, c, S, L), dt, x.device)
     if out is None:
@@ -473,14 +508,14 @@ def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
     dmp = _merge_ptr(dmerge, c, x.device, "dmerge") if want_dm else None
     sp = _states_ptr(states, x)
     if workspace is None:
-        workspace = backward4_workspace(x, cw, with_states=states is not None)
+        workspace = backward4_workspace(x, cw, with_states=states is not None, layout=layout)
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
     vp4 = ctypes.c_void_p * 4
     args = (n, c, h, w, cw, int(chunk_len), _ptr(x), vp4(*[z.data_ptr() for z in logits]),
             vp4(*[l.data_ptr() for l in lams]), mp, sp, _ptr(gy), _ptr(dx), vp4(*[t.data_ptr() for t in dz]),
             vp4(*[t.data_ptr() for t in dl]), dmp, _ptr(workspace), workspace.numel() * workspace.element_size(),
-            _dtype_code(x), _stream(x.device))
+            _dtype_code(x), lc, _stream(x.device))
     if times is None:
         _raise(lib().gspn_backward4(*args), "gspn_backward4")
     else:

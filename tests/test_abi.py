@@ -13,7 +13,7 @@ from linear_spatial_propagation_gspn_amd import gspn as G
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gspn.h")
 
-OK, NULLP, SHAPE, DIR, DTYPE, CHUNK, WCH, MISAL, ALIAS, UNSUP, HIP, WSPACE = range(12)
+OK, NULLP, SHAPE, DIR, DTYPE, CHUNK, WCH, MISAL, ALIAS, UNSUP, HIP, WSPACE, LAYOUT = range(13)
 
 # Fake, never-dereferenced device addresses (validation only compares them).
 A = 0x10000000
@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 7
-    for code in range(12):
+    assert lib.gspn_abi_version() == 8
+    for code in range(13):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
     assert lib.gspn_status_string(99).decode() == "unknown gspn_status"
@@ -93,23 +93,23 @@ def test_forward4_validation(lib):
     def states(planes, lmax):  # fp32 scan states at band boundaries, two buffers of four directions
         return 2 * 4 * planes * lmax * 4
 
-    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 0)
+    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 0, 0)
     assert wsb == 4 * 2 * 64 * 4 + states(2, 8)
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 1) == 4 * 2 * 64 * 2 + states(2, 8)
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 1, 0) == 4 * 2 * 64 * 2 + states(2, 8)
     # channel-shared weights add the four directions' fp32 weights
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 0) == (4 * 2 * 64 * 4 + 4 * 3 * 64 * 4  # fp32 triples
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 0, 0) == (4 * 2 * 64 * 4 + 4 * 3 * 64 * 4  # fp32 triples
                                                                   + states(2, 8))
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1) == (4 * 2 * 64 * 2 + 4 * 64 * 4      # half pairs
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1, 0) == (4 * 2 * 64 * 2 + 4 * 64 * 4      # half pairs
                                                                   + states(2, 8))
-    assert lib.gspn_forward4_workspace_bytes(1, 1, 8, 8, 1, 0) == 4 * 64 * 4 + states(1, 8)
-    assert lib.gspn_forward4_workspace_bytes(1, 1, 3, 5, 1, 1) == 4 * 15 * 2 + states(1, 5)
-    assert lib.gspn_forward4_workspace_bytes(2, 3, 6, 40, 3, 1) == 4 * 2 * 3 * 240 * 2 + states(6, 40)
-    assert lib.gspn_forward4_workspace_bytes(1, -2, 8, 8, 2, 0) == -1
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
-    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 5) == -1
+    assert lib.gspn_forward4_workspace_bytes(1, 1, 8, 8, 1, 0, 0) == 4 * 64 * 4 + states(1, 8)
+    assert lib.gspn_forward4_workspace_bytes(1, 1, 3, 5, 1, 1, 0) == 4 * 15 * 2 + states(1, 5)
+    assert lib.gspn_forward4_workspace_bytes(2, 3, 6, 40, 3, 1, 0) == 4 * 2 * 3 * 240 * 2 + states(6, 40)
+    assert lib.gspn_forward4_workspace_bytes(1, -2, 8, 8, 2, 0, 0) == -1
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 3, 0, 0) == -1
+    assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 5, 0) == -1
 
-    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, m=None, y=D_, s=None, ws=None, wsb=0, dt=0):
-        return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, m, y, s, ws, wsb, dt, None)
+    def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, z=zs, l=ls, m=None, y=D_, s=None, ws=None, wsb=0, dt=0, lay=0):
+        return lib.gspn_forward4(n, c, h, w, cw, chunk, x, z, l, m, y, s, ws, wsb, dt, lay, None)
 
     assert f(dt=3) == DTYPE
     assert f(cw=3) == WCH
@@ -130,7 +130,7 @@ def test_forward4_validation(lib):
     assert f(m=W + 16, ws=W, wsb=wsb) == ALIAS       # the workspace overlaps them
     S = 0x6a000000                                   # fp32 forward states, 4 maps of n*c*h*w
     assert f(s=S, ws=W, wsb=wsb) == UNSUP            # not for planes of at most 64 x 64
-    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 80, 2, 0)
+    wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 80, 2, 0, 0)
     f0 = f
 
     def f(**kw):
@@ -174,14 +174,14 @@ def test_proxy_forward4_validation(lib):
     zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
     ls = vp4(C_, C_ + 0x1000000, C_ + 0x2000000, C_ + 0x3000000)
     WD, WU, WS = 0x70000000, 0x71000000, 0x72000000
-    need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1)
-    assert need == 2 * 2 * 64 * 2 + lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1)
-    assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 0, 1, 1) == -1
-    assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 3, 1) == -1
+    need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1, 0)
+    assert need == 2 * 2 * 64 * 2 + lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1, 0)
+    assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 0, 1, 1, 0) == -1
+    assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 3, 1, 0) == -1
 
     def f(n=1, c=6, h=8, w=8, cp=2, cw=1, chunk=0, x=A, wd=WD, wu=WU, z=zs, l=ls, m=None, y=D_, ws=WS, wsb=need,
-          dt=1):
-        return lib.gspn_proxy_forward4(n, c, h, w, cp, cw, chunk, x, wd, wu, z, l, m, y, ws, wsb, dt, None)
+          dt=1, lay=0):
+        return lib.gspn_proxy_forward4(n, c, h, w, cp, cw, chunk, x, wd, wu, z, l, m, y, ws, wsb, dt, lay, None)
 
     assert f(dt=2) == DTYPE
     assert f(cp=-1) == SHAPE
@@ -247,7 +247,7 @@ def test_timed_variants_validate_like_untimed(lib):
         t.ms[i], t.launches[i] = 7.0, 7
 
     def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, y=D_, dt=0, times=ctypes.byref(t)):
-        return lib.gspn_forward4_timed(n, c, h, w, cw, chunk, x, zs, ls, None, y, None, None, 0, dt, None, times)
+        return lib.gspn_forward4_timed(n, c, h, w, cw, chunk, x, zs, ls, None, y, None, None, 0, dt, 0, None, times)
 
     assert f(times=None) == NULLP
     assert f(dt=3) == DTYPE
@@ -259,10 +259,10 @@ def test_timed_variants_validate_like_untimed(lib):
     assert t.scan_kernel == 0
 
     WD, WU, WS = 0x70000000, 0x71000000, 0x72000000
-    need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1)
+    need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1, 0)
 
     def g(n=1, cp=2, ws=WS, wsb=need, dt=1, times=ctypes.byref(t)):
-        return lib.gspn_proxy_forward4_timed(n, 6, 8, 8, cp, 1, 0, A, WD, WU, zs, ls, None, D_, ws, wsb, dt, None,
+        return lib.gspn_proxy_forward4_timed(n, 6, 8, 8, cp, 1, 0, A, WD, WU, zs, ls, None, D_, ws, wsb, dt, 0, None,
                                              times)
 
     assert g(times=None) == NULLP
@@ -279,15 +279,15 @@ def test_backward4_validation(lib):
     dzs = vp4(0x60000000, 0x61000000, 0x62000000, 0x63000000)
     dls = vp4(0x64000000, 0x65000000, 0x66000000, 0x67000000)
     GY, DX, WS = 0x70000000, 0x71000000, 0x72000000
-    need = lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 2, 0)
+    need = lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 2, 0, 0)
     assert need == 9 * 2 * 64 * 4
-    assert lib.gspn_backward4_workspace_bytes(1, 3, 8, 8, 1, 1) == (4 * 3 * 64 * 4 + 4 * 64 * 4 + 4 * 3 * 64 * 4 +
+    assert lib.gspn_backward4_workspace_bytes(1, 3, 8, 8, 1, 1, 0) == (4 * 3 * 64 * 4 + 4 * 64 * 4 + 4 * 3 * 64 * 4 +
                                                                    5 * 3 * 64 * 2)
-    assert lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 3, 0) == -1
+    assert lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 3, 0, 0) == -1
 
     def f(n=1, c=2, h=8, w=8, cw=2, chunk=0, x=A, m=None, s=None, gy=GY, dx=DX, dz=dzs, dl=dls, dm=None, ws=WS,
-          wsb=need, dt=0):
-        return lib.gspn_backward4(n, c, h, w, cw, chunk, x, zs, ls, m, s, gy, dx, dz, dl, dm, ws, wsb, dt, None)
+          wsb=need, dt=0, lay=0):
+        return lib.gspn_backward4(n, c, h, w, cw, chunk, x, zs, ls, m, s, gy, dx, dz, dl, dm, ws, wsb, dt, lay, None)
 
     assert f(dt=2) == DTYPE
     assert f(chunk=-1) == CHUNK
@@ -311,7 +311,7 @@ def test_backward4_validation(lib):
     assert f(m=dls[2] + 4) == ALIAS                 # an output on the merge weights
     S = 0x6a000000                                  # fp32 forward states, 4 maps of n*c*h*w
     assert f(s=S) == UNSUP                          # not for planes of at most 64 x 64
-    need80 = lib.gspn_backward4_workspace_bytes(1, 2, 8, 80, 2, 0)
+    need80 = lib.gspn_backward4_workspace_bytes(1, 2, 8, 80, 2, 0, 0)
     smaller = need80 - 16 * 2 * 8 * 80              # the states' room in the workspace is not needed
     assert f(w=80, wsb=smaller) == WSPACE           # without states it is
     assert f(w=80, s=S, wsb=smaller - 1) == WSPACE
@@ -322,8 +322,65 @@ def test_backward4_validation(lib):
     assert f(w=80, s=0x6b000000, dm=0x6b000000 + 8, wsb=smaller) == ALIAS   # dmerge on the states
     assert f(n=0, x=0, gy=0, dx=0, dz=None, dl=None, ws=0) == OK
     t = G.StageTimes()
-    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, None, GY, DX, dzs, dls, None, WS, need, 0, None,
-                                    None) == NULLP
+    assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, None, GY, DX, dzs, dls, None, WS, need, 0, 0,
+                                    None, None) == NULLP
     assert lib.gspn_backward4_timed(1, 2, 8, 8, 2, 0, A, zs, ls, None, None, GY, DX, dzs, dls, None, WS, need - 1, 0,
-                                    None,
-                                    ctypes.byref(t)) == WSPACE
+                                    0, None, ctypes.byref(t)) == WSPACE
+
+
+def test_layout_argument(lib):
+    """GSPN_LAYOUT_ARRAY: the workspace grows by the scan-frame copies of the
+    horizontal logits and lambdas (forward; twice that in the backward, for
+    their gradients); an unknown layout is rejected before anything else,
+    even for empty tensors; the array layout needs a workspace."""
+    def copies(n, c, h, w, cw, es):
+        return (2 * (3 * cw + c) * n * h * w * es + 3) // 4 * 4
+
+    for (n, c, h, w, cw, dt) in [(1, 2, 8, 8, 2, 0), (1, 2, 8, 8, 1, 1), (2, 3, 6, 40, 3, 1), (1, 1, 3, 5, 1, 1)]:
+        es = 4 if dt == 0 else 2
+        base = lib.gspn_forward4_workspace_bytes(n, c, h, w, cw, dt, 0)
+        assert lib.gspn_forward4_workspace_bytes(n, c, h, w, cw, dt, 1) == base + copies(n, c, h, w, cw, es)
+        bb = lib.gspn_backward4_workspace_bytes(n, c, h, w, cw, dt, 0)
+        assert lib.gspn_backward4_workspace_bytes(n, c, h, w, cw, dt, 1) == bb + 2 * copies(n, c, h, w, cw, es)
+    assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1, 1) == \
+        2 * 2 * 64 * 2 + lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 1, 1, 1)
+    for bad in (2, -1):
+        assert lib.gspn_forward4_workspace_bytes(1, 2, 8, 8, 2, 0, bad) == -1
+        assert lib.gspn_backward4_workspace_bytes(1, 2, 8, 8, 2, 0, bad) == -1
+        assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1, bad) == -1
+
+    vp4 = ctypes.c_void_p * 4
+    zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
+    ls = vp4(C_, C_, C_, C_)
+    W = 0x60000000
+    need = lib.gspn_forward4_workspace_bytes(1, 2, 8, 80, 2, 0, 1)
+
+    def f(n=1, lay=1, ws=W, wsb=need, x=A, y=D_):
+        return lib.gspn_forward4(n, 2, 8, 80, 2, 0, x, zs, ls, None, y, None, ws, wsb, 0, lay, None)
+
+    assert f(lay=2) == LAYOUT
+    assert f(n=0, x=0, y=0, ws=0, wsb=0, lay=7) == LAYOUT   # enum checks run before the empty-tensor return
+    assert f(ws=None, wsb=0) == WSPACE                      # the copies live in the workspace
+    assert f(wsb=lib.gspn_forward4_workspace_bytes(1, 2, 8, 80, 2, 0, 0)) == WSPACE  # the scan layout's is too small
+    assert f(ws=A + 16) == ALIAS
+    assert f(n=0, x=0, y=0) == OK
+
+    WD, WU, WS = 0x70000000, 0x71000000, 0x72000000
+    pneed = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1, 1)
+    assert lib.gspn_proxy_forward4(1, 6, 8, 8, 2, 1, 0, A, WD, WU, zs, ls, None, D_, WS, pneed, 1, 3, None) == LAYOUT
+    assert lib.gspn_proxy_forward4(1, 6, 8, 8, 2, 1, 0, A, WD, WU, zs, ls, None, D_, WS, pneed - 1, 1, 1,
+                                   None) == WSPACE
+
+    dzs = vp4(0x40000000, 0x41000000, 0x42000000, 0x43000000)
+    dls = vp4(0x44000000, 0x45000000, 0x46000000, 0x47000000)
+    bneed = lib.gspn_backward4_workspace_bytes(1, 2, 8, 80, 2, 0, 1)
+
+    def g(lay=1, wsb=bneed, s=None):
+        return lib.gspn_backward4(1, 2, 8, 80, 2, 0, A, zs, ls, None, s, 0x50000000, 0x51000000, dzs, dls, None, WS,
+                                  wsb, 0, lay, None)
+
+    assert g(lay=-3) == LAYOUT
+    assert g(wsb=bneed - 1) == WSPACE
+    assert g(wsb=lib.gspn_backward4_workspace_bytes(1, 2, 8, 80, 2, 0, 0)) == WSPACE
+    # with the states passed, the states' room (last) is not needed in either layout
+    assert g(s=0x6a000000, wsb=bneed - 16 * 2 * 8 * 80 - 1) == WSPACE

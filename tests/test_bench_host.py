@@ -60,8 +60,8 @@ def test_weight_bytes_follow_the_library_workspace(name):
     lib = G.lib()
     dt = 0 if wl.dtype == "f32" else 1
     c = wl.c_scan
-    shared = lib.gspn_forward4_workspace_bytes(wl.n, c, wl.h, wl.w, 1, dt)
-    per_channel = lib.gspn_forward4_workspace_bytes(wl.n, c, wl.h, wl.w, c, dt)
+    shared = lib.gspn_forward4_workspace_bytes(wl.n, c, wl.h, wl.w, 1, dt, 0)
+    per_channel = lib.gspn_forward4_workspace_bytes(wl.n, c, wl.h, wl.w, c, dt, 0)
     if bench.prenormalised(wl):
         assert shared - per_channel == 4 * bench.weight_bytes_per_direction(wl)
     else:
@@ -100,3 +100,25 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_scan_algorithmic_bytes_are_the_compulsory_bytes():
+    """roofline.frac is taken on the four-direction scan's compulsory bytes
+    (every distinct input read once as stored, y written once): 18U for fp32
+    per-channel logits (9,663,676,416 bytes on 1024^2, B=16, C=8) and
+    6U + 12 N H W 2 bytes for bf16 channel-shared logits (14,520,680,448 on
+    1024^2, B=1, C=1152), divided over the launches that share the scan."""
+    assert bench.scan_algorithmic_bytes(WORKLOADS["profile"]) == 9663676416
+    assert bench.scan_algorithmic_bytes(WORKLOADS["profile"]) == bench.algorithmic_bytes(WORKLOADS["profile"])
+    assert bench.scan_algorithmic_bytes(WORKLOADS["wide"]) == 14520680448
+    assert bench.scan_algorithmic_bytes(WORKLOADS["tstage"]) == 1387266048
+    up = 8 * 2048 * 2048 * 2  # one proxy-space map
+    assert bench.scan_algorithmic_bytes(WORKLOADS["proxy"]) == 6 * up + 4 * 3 * 2048 * 2048 * 2
+    assert bench.launch_algorithmic_bytes(WORKLOADS["proxy"], 16) == (6 * up + 4 * 3 * 2048 * 2048 * 2) // 16
+    assert bench.launch_algorithmic_bytes(WORKLOADS["profile"], 1) == 9663676416
+
+
+def test_host_cpu_fields():
+    info = bench.host_cpu()
+    assert set(info) == {"cpu_model", "nproc", "cpu_count"}
+    assert info["nproc"] >= 1

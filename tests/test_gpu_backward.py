@@ -160,3 +160,66 @@ def test_backward_full_tstage_sampled_planes():
                                gy[sl])
         got = (dx[sl], [z[sl] for z in dz], [l[sl] for l in dl])
         _check_all(got, ref, TOL["f32"], "plane (%d, %d)" % (n, c))
+
+
+WIDE_PLAN = {"kernel": "adj4_kernel", "positions_per_lane": 1, "channel_group": 4, "nontemporal": True}
+
+
+@pytest.mark.parametrize("chunk", [0, 5])
+@pytest.mark.parametrize("shape", [(1, 9, 64, 128), (1, 9, 64, 1024), (1, 9, 128, 1024)])
+def test_backward_shared_groups_of_four_nontemporal(shape, chunk):
+    """The wide workload's adjoint instance: bf16 storage, channel-shared
+    logits summed over groups of four channels (9 = 4 + 4 + 1: the last group
+    ragged), one position per lane on lines of up to 1024 positions, and the
+    non-temporal streams that every line being a whole number of 128-byte
+    cache lines selects (H and W multiples of 64)."""
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, "bf16", True, chunk, 700 + h + w)
+    _say("backward groups of four %s chunk=%d" % (shape, chunk))
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 31)
+    t = G.StageTimes()
+    got = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=chunk, times=t)
+    torch.cuda.synchronize()
+    assert t.as_dict()["adjoint_plan"] == WIDE_PLAN
+    ref = oracle.backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk=chunk)
+    _check_all(got, ref, TOL["bf16"], "all outputs")
+
+
+def test_backward_full_wide_sampled_channels():
+    """The 1024^2, B=1, C=1152 workload (bf16, channel-shared logits): the
+    call on the whole tensor, in the configuration the bench times.  dx and
+    every dlambda are checked on sampled channels, which the oracle computes
+    on their own (with the shared logits).  The shared dlogits sum over all
+    1152 channels; the gradient is linear in dL/dy, so a second call with
+    dL/dy zero outside the sampled channels must give the oracle's dlogits of
+    those channels alone, summed."""
+    wl = WORKLOADS["wide"]
+    _say("backward full wide")
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 37)
+    t = G.StageTimes()
+    dx, dz, dl = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, times=t)
+    torch.cuda.synchronize()
+    assert t.as_dict()["adjoint_plan"] == WIDE_PLAN
+    assert torch.isfinite(dx).all()
+    chans = [0, 577, 1151]
+    zs = [_np(z) for z in inp["logits"]]
+    for c in chans:
+        sl = (slice(0, 1), slice(c, c + 1))
+        rdx, rdl, _ = oracle.backward4(_np(inp["x"][sl]), zs, [_np(l[sl]) for l in inp["lam"]], _np(gy[sl]))
+        errs = {"dx": oracle.normwise_error(_np(dx[sl]), rdx)}
+        for d in range(4):
+            errs["dlam%d" % d] = oracle.normwise_error(_np(dl[d][sl]), rdl[d])
+        _say("  channel %d: worst normwise error %.3g" % (c, max(errs.values())))
+        assert max(errs.values()) <= TOL["bf16"], errs
+    gz = torch.zeros_like(gy)
+    gz[:, chans] = gy[:, chans]
+    _, dz2, _ = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gz, out=(dx, dz, dl))
+    torch.cuda.synchronize()
+    _, _, rdz = oracle.backward4(_np(inp["x"][:, chans]), zs, [_np(l[:, chans]) for l in inp["lam"]],
+                                 _np(gz[:, chans]))
+    for d in range(4):
+        e = oracle.normwise_error(_np(dz2[d]), rdz[d])
+        _say("  dlogits %d of channels %s: normwise error %.3g" % (d, chans, e))
+        assert e <= TOL["bf16"]
