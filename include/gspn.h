@@ -251,6 +251,35 @@ gspn_status gspn_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                           int64_t workspace_bytes, int dtype, int layout, void* stream);
 
 /*
+ * gspn_forward4_noalloc -- gspn_forward4 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same computation and arguments, except that
+ * the workspace is not passed in.  It is taken from a static device array of
+ * GSPN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on, from the moment its code is loaded on that device until the
+ * process ends; the call itself allocates and frees nothing.
+ *   Size limit: calls whose gspn_forward4_workspace_bytes(n, c, h, w, cw,
+ *   dtype, layout) exceeds GSPN_NOALLOC_SCRATCH_BYTES return
+ *   GSPN_ERR_WORKSPACE before touching the device.
+ *   Device: the array of the current HIP device is used, so `stream` must
+ *   belong to the current device (as for any launch).  Its address is looked
+ *   up on the device's first call (a failure there is GSPN_ERR_HIP).
+ *   Concurrency: every call on one GPU shares that GPU's array, which keeps
+ *   whatever the last call left there (nothing in it needs clearing between
+ *   calls).  Calls that overlap in time on one GPU -- on different streams or
+ *   from different threads -- race on it and give undefined results; order
+ *   them on one stream or with events.
+ * Other arguments, validation and errors as for gspn_forward4 (the workspace
+ * checks aside).
+ */
+#define GSPN_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+
+gspn_status gspn_forward4_noalloc(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw,
+                                  int64_t chunk_len, const void* x, const void* const logits[4],
+                                  const void* const lam[4], const float* merge, void* y, float* states,
+                                  int dtype, int layout, void* stream);
+
+/*
  * gspn_proxy_forward4_workspace_bytes -- bytes of the gspn_proxy_forward4
  * workspace: the projected input and the merged output in proxy space (2 *
  * n*c_proxy*h*w elements) plus gspn_forward4_workspace_bytes(n, c_proxy, h,

@@ -417,7 +417,9 @@ hipError_t copy_to_scan_frame(int64_t n, int64_t c, int64_t h, int64_t w, int64_
 gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                           const void* x, const void* const logits_in[4], const void* const lam_in[4],
                           const float* merge, void* y, float* states, void* workspace, int64_t workspace_bytes,
-                          int dtype, int layout, void* stream, Timer* tm) {
+                          int dtype, int layout, void* stream, Timer* tm, bool noalloc = false) {
+    // noalloc: the workspace is the current device's static scratch array,
+    // looked up only once every argument has passed validation
     if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
     const void* const* logits = logits_in;
     const void* const* lam = lam_in;
@@ -431,7 +433,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (!x || !y || !logits || !lam) return GSPN_ERR_NULL_POINTER;
     for (int d = 0; d < 4; ++d)
         if (!logits[d] || !lam[d]) return GSPN_ERR_NULL_POINTER;
-    const bool have_ws = workspace != nullptr && workspace_bytes > 0;
+    const bool have_ws = noalloc || (workspace != nullptr && workspace_bytes > 0);
     if (layout == GSPN_LAYOUT_ARRAY && !have_ws) return GSPN_ERR_WORKSPACE;  // the copies live there
     const size_t es = elem_size(dtype);
     if (!aligned(x, es) || !aligned(y, es)) return GSPN_ERR_MISALIGNED;
@@ -460,7 +462,10 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         if (merge && overlap(states, sb, merge, mgb)) return GSPN_ERR_ALIASING;
     }
     int64_t need = 0;
-    if (have_ws) {
+    if (noalloc) {
+        need = gspn_forward4_workspace_bytes(n, c, h, w, cw, dtype, layout);
+        if (need > GSPN_NOALLOC_SCRATCH_BYTES) return GSPN_ERR_WORKSPACE;
+    } else if (have_ws) {
         need = gspn_forward4_workspace_bytes(n, c, h, w, cw, dtype, layout);
         if (workspace_bytes < need) return GSPN_ERR_WORKSPACE;
         if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
@@ -470,6 +475,11 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         for (int d = 0; d < 4; ++d)
             if (overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], xb))
                 return GSPN_ERR_ALIASING;
+    }
+    if (noalloc) {
+        // the scratch is a separate device allocation: it overlaps no argument
+        if (gspn::noalloc_scratch(&workspace) != hipSuccess) return GSPN_ERR_HIP;
+        workspace_bytes = need;
     }
     const hipStream_t st = as_stream(stream);
 
@@ -976,6 +986,15 @@ gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int6
                                         workspace_bytes, dtype, layout, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
+}
+
+static_assert(GSPN_NOALLOC_SCRATCH_BYTES == gspn::kNoallocScratchBytes, "scratch size stated in gspn.h");
+
+gspn_status gspn_forward4_noalloc(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
+                                  const void* x, const void* const logits[4], const void* const lam[4],
+                                  const float* merge, void* y, float* states, int dtype, int layout, void* stream) {
+    return forward4_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, y, states, nullptr, 0, dtype, layout,
+                         stream, nullptr, true);
 }
 
 int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,

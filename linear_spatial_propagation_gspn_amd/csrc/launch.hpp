@@ -164,4 +164,10 @@ hipError_t launch_finish_shared_dz(const float* sums, const void* logits, void* 
 hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const void* in,
                           const void* weight, void* out, int dtype, hipStream_t stream);
 
+// The allocation-free forward's scratch (noalloc.hip): a static device array
+// of kNoallocScratchBytes per GPU; *out receives the current device's copy
+// (its address looked up on that device's first call, then cached).
+constexpr int64_t kNoallocScratchBytes = int64_t{64} << 20;
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace gspn

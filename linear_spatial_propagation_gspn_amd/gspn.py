@@ -41,7 +41,10 @@ EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy
            "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4",
            "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_forward4_timed",
            "gspn_proxy_forward4_timed", "gspn_backward4_workspace_bytes", "gspn_backward4", "gspn_backward4_timed",
-           "gspn_status_string", "gspn_abi_version")
+           "gspn_forward4_noalloc", "gspn_status_string", "gspn_abi_version")
+
+# GSPN_NOALLOC_SCRATCH_BYTES: the static scratch gspn_forward4_noalloc works in.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # gspn_stage, in order.
 STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up", "adjoint", "reduce", "layout")
@@ -111,6 +114,9 @@ def lib() -> ctypes.CDLL:
             h.gspn_proxy_forward4.restype = ci
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp, vp, vp, vp, i64, ci, ci, vp]
+            h.gspn_forward4_noalloc.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
+                                                ctypes.POINTER(vp), vp, vp, vp, ci, ci, vp]
+            h.gspn_forward4_noalloc.restype = ci
             h.gspn_forward4_timed.argtypes = h.gspn_forward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_forward4_timed.restype = ci
             h.gspn_proxy_forward4_timed.argtypes = h.gspn_proxy_forward4.argtypes + [ctypes.POINTER(StageTimes)]
@@ -376,6 +382,33 @@ def gspn_forward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequenc
     if states is None or states is False:
         return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge, layout=layout)
     return _forward4(x, logits, lams, chunk_len, out, workspace, None, merge, states, layout), states
+
+
+def gspn_forward4_noalloc(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
+                          chunk_len: int = 0, out: torch.Tensor | None = None, merge: torch.Tensor | None = None,
+                          states: torch.Tensor | None = None, layout: str = "scan") -> torch.Tensor:
+    """gspn_forward4 without a workspace argument: the library works in its
+    static per-GPU scratch array (NOALLOC_SCRATCH_BYTES), so the call
+    allocates nothing on the device (``out`` and ``states``, if given, are the
+    caller's).  Calls that overlap in time on one GPU race on that array."""
+    n, c, h, w = x.shape
+    dt = x.dtype
+    cw = logits[0].shape[1]
+    lc = _layout_code(layout)
+    _check(x, "x", (n, c, h, w), dt, x.device)
+    for d in range(4):
+        S, L = tensor_frame(d, h, w, layout)
+        _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
+        _check(lams[d], "lam[%d]" % d, (n, c, S, L), dt, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (n, c, h, w), dt, x.device)
+    zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
+    lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
+    _raise(lib().gspn_forward4_noalloc(n, c, h, w, cw, int(chunk_len), _ptr(x), zp, lp,
+                                       _merge_ptr(merge, c, x.device), _ptr(out), _states_ptr(states, x),
+                                       _dtype_code(x), lc, _stream(x.device)), "gspn_forward4_noalloc")
+    return out
 
 
 def gspn_forward4_timed(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],

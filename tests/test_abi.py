@@ -384,3 +384,32 @@ def test_layout_argument(lib):
     assert g(wsb=lib.gspn_backward4_workspace_bytes(1, 2, 8, 80, 2, 0, 0)) == WSPACE
     # with the states passed, the states' room (last) is not needed in either layout
     assert g(s=0x6a000000, wsb=bneed - 16 * 2 * 8 * 80 - 1) == WSPACE
+
+
+def test_noalloc_validation(lib):
+    """gspn_forward4_noalloc validates like gspn_forward4 and rejects calls
+    whose workspace would exceed its static scratch before touching any
+    device (nothing here reaches a device: there is none in this suite)."""
+    vp4 = ctypes.c_void_p * 4
+    zs = vp4(B, B + 0x1000000, B + 0x2000000, B + 0x3000000)
+    ls = vp4(C_, C_, C_, C_)
+
+    def f(n=1, c=2, h=8, w=80, cw=2, chunk=0, x=A, m=None, y=D_, s=None, dt=0, lay=0):
+        return lib.gspn_forward4_noalloc(n, c, h, w, cw, chunk, x, zs, ls, m, y, s, dt, lay, None)
+
+    assert f(dt=3) == DTYPE
+    assert f(lay=4) == LAYOUT
+    assert f(chunk=-1) == CHUNK
+    assert f(x=0) == NULLP
+    assert f(y=A) == ALIAS
+    assert f(n=0, x=0, y=0) == OK
+    assert G.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # 32 planes of 1024 x 1024 fp32: four maps alone are 512 MiB
+    big = lib.gspn_forward4_workspace_bytes(32, 1, 1024, 1024, 1, 0, 0)
+    assert big > G.NOALLOC_SCRATCH_BYTES
+    assert f(n=32, c=1, h=1024, w=1024, cw=1) == WSPACE
+    # the array layout's copies count against the scratch too
+    small = (1, 4, 512, 1024, 4, 0)
+    assert lib.gspn_forward4_workspace_bytes(*small, 0) <= G.NOALLOC_SCRATCH_BYTES
+    assert lib.gspn_forward4_workspace_bytes(*small, 1) > G.NOALLOC_SCRATCH_BYTES
+    assert f(n=1, c=4, h=512, w=1024, cw=4, lay=1) == WSPACE
