@@ -401,7 +401,9 @@ typedef enum {
     GSPN_SCAN_FUSED4 = 2,       /* four directions in one launch, one workgroup per line */
     GSPN_SCAN_LONG_LINE = 3,    /* four directions in one launch, 16-byte vectors per lane */
     GSPN_SCAN_PLANE = 4,        /* one workgroup per plane, all four directions, y written once */
-    GSPN_SCAN_BANDED = 5        /* very few long lines: lines split across workgroups, one launch per band of steps */
+    GSPN_SCAN_BANDED = 5,       /* very few long lines: lines split across workgroups, one launch per band of steps */
+    GSPN_SCAN_SEQUENTIAL = 6    /* many big planes: one workgroup per plane runs the four directions in turn,
+                                   building y in place */
 } gspn_scan_kernel;
 
 /* The adjoint launch of a backward call (gspn_stage_times.adjoint; all 0

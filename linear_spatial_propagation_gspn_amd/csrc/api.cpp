@@ -554,6 +554,22 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         // in one launch).
         if (prenormalise(n, h, w, logits, ws, wdir, dtype, st, tm, p) != hipSuccess) return GSPN_ERR_HIP;
     }
+    // Many big planes: one workgroup per plane runs the four directions in
+    // turn and builds y in place; the scratch map of the horizontal
+    // directions' sum takes the room of x transposed.
+    if (!states && gspn::seq4_supported(h, w) && n * c >= gspn::kSeq4MinPlanes) {
+        bool vec = aligned(x, 16) && aligned(y, 16);
+        for (int d = 0; d < 4; ++d) vec = vec && aligned(p[d].wts, 16) && aligned(p[d].lam, 16);
+        if (vec) {
+            if (tm) tm->scan_kernel = GSPN_SCAN_SEQUENTIAL;
+            const void* wts[4] = {p[0].wts, p[1].wts, p[2].wts, p[3].wts};
+            return from_hip(timed(tm, GSPN_STAGE_SCAN, [&] {
+                return gspn::launch_seq4(x, wts, lam, merge, y, xt, n, c, cw, h, w, chunks, dtype, p[0].wdtype,
+                                         p[0].wts_are_logits, st);
+            }));
+        }
+    }
+
     // The horizontal directions become vertical-form scans of x transposed
     // (their scan frame): line k of step i is x[.., k, i].
     if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] {

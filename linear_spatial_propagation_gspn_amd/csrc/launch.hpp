@@ -63,6 +63,23 @@ hipError_t launch_plane4(const void* x, const void* const logits[4], const void*
                          void* y, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w, const int64_t chunk[4],
                          int dtype, hipStream_t stream);
 
+// Many big planes: one workgroup per (n, c) plane runs L2R, R2L, T2B, B2T
+// one after another, building y in place (seq4.hip).  Planes with both sides
+// multiples of 64 in [64, 1024]; 16-byte aligned tensors.  wts[d]: logits
+// (wdtype == dtype) or, for bf16, channel-shared half pairs (kPairF16);
+// chunk[d] clamped to [1, S_d]; z: scratch of n*c*h*w elements of the
+// storage type ([n][c][w][h], the horizontal directions' sum).
+bool seq4_supported(int64_t h, int64_t w);
+constexpr int64_t kSeq4MinPlanes =
+#ifdef GSPN_SEQ4_MIN_PLANES
+    GSPN_SEQ4_MIN_PLANES;
+#else
+    256;  // one workgroup per CU: fewer planes would leave CUs idle
+#endif
+hipError_t launch_seq4(const void* x, const void* const wts[4], const void* const lam[4], const float* merge,
+                       void* y, void* z, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w,
+                       const int64_t chunk[4], int dtype, int wdtype, int wts_are_logits, hipStream_t stream);
+
 // dst[p][c][r] = src[p][r][c] for `planes` planes of R x Cc elements.
 hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, int Cc, int dtype,
                             hipStream_t stream);

@@ -51,7 +51,8 @@ STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_
 
 
 # gspn_scan_kernel, in order.
-SCAN_KERNELS = ("none", "scan_kernel", "scan4v_kernel", "scan4lp_kernel", "plane4_kernel", "scan4band_kernel")
+SCAN_KERNELS = ("none", "scan_kernel", "scan4v_kernel", "scan4lp_kernel", "plane4_kernel", "scan4band_kernel",
+                "seq4_kernel")
 
 
 class AdjointPlan(ctypes.Structure):
