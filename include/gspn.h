@@ -63,9 +63,13 @@
  *    queues nothing, without looking at its pointers.
  *  - Aliasing: an output may not overlap any input, except that with
  *    accumulate = 1 the output is read and written in place.
- *  - Domain: the fp32 sigmoid saturates, so for each position at least one
- *    existing neighbour's logit must exceed about -87 (otherwise every weight
- *    of that row is 0/0 = NaN).  NaN/Inf inputs propagate by IEEE rules.
+ *  - Domain: every finite logit and +-Inf is accepted.  The fp32 sigmoid
+ *    clamps its argument to [-87, 87]; a row whose every existing logit is
+ *    below about -69 (where the sigmoids could underflow the row sum) is
+ *    normalised as exp(z - max z) / sum, equal to the normalised sigmoids to
+ *    fp32 precision there.  A row whose every existing logit is -Inf has
+ *    weights 0/0 = NaN, as in exact arithmetic.  NaN inputs propagate by IEEE
+ *    rules.
  *  - Limits: a line may hold at most GSPN_MAX_LINE positions (else
  *    GSPN_ERR_UNSUPPORTED); dimensions must be in [0, 2^31) and N*C*H*W < 2^58.
  */

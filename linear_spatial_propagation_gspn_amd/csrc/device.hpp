@@ -100,21 +100,22 @@ __device__ __forceinline__ float recip(float d) {
 // both enter as the first-order factor 2^err ~ 1 + err ln 2.  The hardware
 // exp2 and reciprocal (1 ulp each) finish it (a Newton step on the
 // reciprocal measured no more accurate: 3.4 ulp at most on the normalised
-// weights either way, mean 0.57 ulp, over z in [-20, 20]).  The exponent is
-// capped at 126 (before the correction, which must not meet an infinity), so
-// for z below about -87 the result saturates at 2^-126 instead of going
-// subnormal or to 0 (a row whose every sigmoid is that small is normalised by
-// normalise_row_s's exact fallback); NaN propagates.
+// weights either way, mean 0.57 ulp, over z in [-20, 20]).  z is first
+// clamped to [-87, 87] (keeping its sign; NaN compares false and passes
+// through), which keeps the exponent and its correction finite: the result
+// saturates at about 2^-125.5 and 1 - 2^-126 there (a row whose every
+// sigmoid is that small is normalised by normalise_row_s's exact fallback);
+// NaN propagates.
 __device__ __forceinline__ float sigmoid(float z) {
     constexpr float kL2E = 1.44269502162933349609375f;   // log2 e rounded to fp32
-    constexpr float kL2ELo = 1.925963033500011e-08f;     // log2 e - kL2E
+    constexpr float kL2ELoLn2 = 1.33497577e-08f;          // (log2 e - kL2E) ln 2
     constexpr float kLn2 = 0.693147182464599609375f;
-    const float t = -z * kL2E;
-    const float tc = t > 126.0f ? 126.0f : t;  // NaN compares false and stays NaN
-    const float err = __builtin_fabsf(t) < 126.0f ? __builtin_fmaf(-z, kL2E, -t) + -z * kL2ELo : 0.0f;
-    float e = __builtin_amdgcn_exp2f(tc);
-    e = __builtin_fmaf(e, err * kLn2, e);
-    return __builtin_amdgcn_rcpf(1.0f + e);
+    const float zc = __builtin_fabsf(z) > 87.0f ? __builtin_copysignf(87.0f, z) : z;
+    const float t = -zc * kL2E;
+    // (exact remainder of the rounded product + the constant's error) ln 2
+    const float c = __builtin_fmaf(__builtin_fmaf(-zc, kL2E, -t), kLn2, -zc * kL2ELoLn2);
+    const float e = __builtin_amdgcn_exp2f(t);
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_fmaf(e, c, e));
 }
 
 // Row normalisation of one tridiagonal row (GSPN summary page, "Approach":
