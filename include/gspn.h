@@ -215,9 +215,10 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              gspn_backward4, which then skips its own recompute.  Map d
  *              starts at states + d*n*c*h*w and lies in direction d's scan
  *              frame: [n][c][h][w] for T2B and B2T, [n][c][w][h] for L2R and
- *              R2L.  It needs the workspace, lines of at most 2048
- *              positions and planes larger than 64 x 64 in at least one
- *              dimension (else GSPN_ERR_WORKSPACE / GSPN_ERR_UNSUPPORTED); y
+ *              R2L.  It needs the workspace and lines of at most 2048
+ *              positions (else GSPN_ERR_WORKSPACE / GSPN_ERR_UNSUPPORTED).
+ *              Planes of at most 64 x 64 then leave their one-pass path
+ *              (which keeps no states) for the four-direction launch; y
  *              is then merged from these fp32 maps, so for bf16 storage it
  *              can differ from the y of a call without states in the last
  *              bf16 place.
@@ -351,8 +352,7 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
  *                  recurrence), accumulated in fp32 in an order that may vary
  *                  between calls.
  * states: NULL, or the fp32 states that gspn_forward4 wrote for the same
- * inputs (layout there; planes larger than 64 x 64, else
- * GSPN_ERR_UNSUPPORTED), 4-byte aligned, overlapping no output and not the
+ * inputs (layout there), 4-byte aligned, overlapping no output and not the
  * workspace: the adjoint reads them instead of recomputing the forward.
  * Without them the forward states are recomputed inside, in fp32 and with
  * the same kernel, so both ways give the same gradients bit for bit.

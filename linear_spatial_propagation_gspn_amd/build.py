@@ -67,6 +67,41 @@ def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
     return out
 
 
+CHECK_LIB = os.path.join(PKG, "libgspn_check.so")
+CHECK_BUILD = os.path.join(BUILD, "check")
+
+
+def build_check(verbose: bool = False, out: str = CHECK_LIB) -> str:
+    """Compile the host-only checking library libgspn_check.so (always
+    rebuilds): every source's host code with GSPN_CHECK_LAUNCHES, so that the
+    C ABI runs as usual while each launch replays its kernel's accesses on the
+    host instead of queueing it (csrc/check.hpp), plus the checker's registry
+    (csrc/check.cpp).  No device code is compiled."""
+    os.makedirs(CHECK_BUILD, exist_ok=True)
+
+    def one(src: str) -> str:
+        obj = os.path.join(CHECK_BUILD, src + ".o")
+        cmd = [HIPCC] + COMMON + ["-DGSPN_CHECK_LAUNCHES", "-x", "hip", "--offload-host-only", "-c",
+                                  os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc (host only) failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(one, SOURCES + ["check.cpp"]))
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    os.replace(tmp, out)
+    if verbose:
+        print("built", out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_check(verbose=True)
     sys.exit(0)

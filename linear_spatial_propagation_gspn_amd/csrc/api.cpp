@@ -450,10 +450,9 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     const int64_t sb = 4 * n * c * h * w * 4;  // four fp32 state maps
     if (states) {
         // the states come from the four-direction launch, which takes lines
-        // of at most 2048 positions and a workspace; planes of at most
-        // 64 x 64 (the plane-resident path's) are not supported
-        if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c, h, w, chunks) || gspn::plane4_supported(h, w))
-            return GSPN_ERR_UNSUPPORTED;
+        // of at most 2048 positions and a workspace (also for planes of at
+        // most 64 x 64, whose plane-resident path keeps no states)
+        if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c, h, w, chunks)) return GSPN_ERR_UNSUPPORTED;
         if (!have_ws) return GSPN_ERR_WORKSPACE;
         if (!aligned(states, 4)) return GSPN_ERR_MISALIGNED;
         if (overlap(states, sb, y, xb) || overlap(states, sb, x, xb)) return GSPN_ERR_ALIASING;
@@ -750,7 +749,6 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     }
     if (overlap(workspace, need, x, xb) || overlap(workspace, need, gy, xb)) return GSPN_ERR_ALIASING;
     if (states) {
-        if (gspn::plane4_supported(h, w)) return GSPN_ERR_UNSUPPORTED;  // as in gspn_forward4
         if (!aligned(states, 4)) return GSPN_ERR_MISALIGNED;
         if (overlap(workspace, need, states, 4 * hb)) return GSPN_ERR_ALIASING;
         for (int i = 0; i < 9; ++i)

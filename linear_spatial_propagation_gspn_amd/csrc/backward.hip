@@ -73,6 +73,62 @@ struct Adj4K {
     int64_t blocks[4];
 };
 
+// Index code of adj_line and adj4_kernel, shared with the host replay.
+
+// Direction and index within it of block b (consecutive ranges).
+GSPN_HD void adj4_block(const Adj4K& a, int64_t b, int& dir, int64_t& idx) {
+    dir = 0;
+    idx = b;
+    while (dir < 3 && idx >= a.blocks[dir]) {
+        idx -= a.blocks[dir];
+        ++dir;
+    }
+}
+
+// Channel group pg of a direction: its image, first channel and plane, and
+// the offset of its logits ([n][cw][3][S][L]) in elements.
+struct AdjGroup {
+    int64_t nidx, c0, p0, zplane;
+};
+
+GSPN_HD AdjGroup adj_group(const AdjK& a, int64_t pg, int G, int64_t plane) {
+    const int64_t groups = (a.c + G - 1) / G;
+    AdjGroup r;
+    r.nidx = pg / groups;
+    r.c0 = (pg - r.nidx * groups) * G;
+    r.p0 = r.nidx * a.c + r.c0;
+    r.zplane = (r.nidx * a.cw + (a.cw == 1 ? 0 : r.c0)) * 3 * plane;
+    return r;
+}
+
+// Member g of the group exists; its channel offset (0 when it does not).
+GSPN_HD bool adj_member_ok(const AdjK& a, int64_t c0, int g) { return c0 + g < a.c; }
+GSPN_HD int adj_member(const AdjK& a, int64_t c0, int g) { return adj_member_ok(a, c0, g) ? g : 0; }
+
+// Position k clamped into the line (addresses of lanes past its end), and
+// the clamped left / right neighbours of a lane's positions k0 .. k0 + P - 1.
+// Both ends clamp: a lane past the line's end would otherwise read its left
+// neighbour beyond the row, and beyond the buffer on the last row of the
+// last plane.
+GSPN_HD int adj_clamp(int k, int L) { return k < L - 1 ? k : L - 1; }
+GSPN_HD int adj_left(int k0, int L) { return adj_clamp(k0 - 1 > 0 ? k0 - 1 : 0, L); }
+GSPN_HD int adj_right(int k0, int P, int L) { return adj_clamp(k0 + P, L); }
+
+// Index of one LDS edge value: buffer b, side (0: left, 1: right), member g, lane.
+GSPN_HD int adj_edge(int b, int side, int G, int g, int nt, int lane) { return ((b * 2 + side) * G + g) * nt + lane; }
+
+// Row of step t, and the rows a fill for step t reads: step t clamped to the
+// chunk's first step t0, and the step before that (h_{t-1}, clamped too).
+GSPN_HD int adj_row(int t, int S, bool rev) { return rev ? S - 1 - t : t; }
+struct AdjFill {
+    int64_t lo, hlo;  // element offsets of the two rows
+};
+GSPN_HD AdjFill adj_fill(int t, int t0, int S, int L, bool rev) {
+    const int tc = t > t0 ? t : t0;
+    const int tp = tc - 1 > t0 ? tc - 1 : t0;
+    return {static_cast<int64_t>(adj_row(tc, S, rev)) * L, static_cast<int64_t>(adj_row(tp, S, rev)) * L};
+}
+
 // One (plane group, chunk) line of one direction.  G channels of the same
 // image run together (G > 1 only for channel-shared logits): the logits of a
 // position are normalised once for all of them, and the logit gradient, which
@@ -107,18 +163,18 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     const int S = a.S;
     const int L = a.L;
     const int64_t plane = static_cast<int64_t>(S) * L;
-    const int64_t groups = (a.c + G - 1) / G;
-    const int64_t nidx = pg / groups;
-    const int64_t c0 = (pg - nidx * groups) * G;  // first channel of the group
-    const int64_t p0 = nidx * a.c + c0;           // its plane
-    int gc[G];                                    // channel offset of each member, clamped
+    const AdjGroup grp = adj_group(a, pg, G, plane);
+    const int64_t nidx = grp.nidx;
+    const int64_t c0 = grp.c0;  // first channel of the group
+    const int64_t p0 = grp.p0;  // its plane
+    int gc[G];                  // channel offset of each member, clamped
     bool gok[G];
-    float msc[G];                                 // merge weight of each member (MERGE)
-    float dm[G];                                  // this lane's share of dL/dm (MERGE)
+    float msc[G];               // merge weight of each member (MERGE)
+    float dm[G];                // this lane's share of dL/dm (MERGE)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        gok[g] = c0 + g < a.c;
-        gc[g] = gok[g] ? g : 0;
+        gok[g] = adj_member_ok(a, c0, g);
+        gc[g] = adj_member(a, c0, g);
         msc[g] = (MERGE && a.mscale) ? a.mscale[c0 + gc[g]] : 1.0f;
         dm[g] = 0.0f;
     }
@@ -126,13 +182,13 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     const T* gp = static_cast<const T*>(a.g) + p0 * plane;
     const T* lp = static_cast<const T*>(a.lam) + p0 * plane;
     const float* hp = a.hs + p0 * plane;
-    const int64_t zplane = (nidx * a.cw + (a.cw == 1 ? 0 : c0)) * 3 * plane;
+    const int64_t zplane = grp.zplane;
     const T* zp = static_cast<const T*>(a.z) + zplane;
     T* dlp = static_cast<T*>(a.dlam) + p0 * plane;
     T* dxp = static_cast<T*>(a.dx) + p0 * plane;
 
     auto edge = [&](int b, int side, int g, int lane) -> float& {
-        return edge_raw[((b * 2 + side) * G + g) * nt + lane];
+        return edge_raw[adj_edge(b, side, G, g, nt, lane)];
     };
 
     const int k0 = tid * P;
@@ -140,25 +196,25 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     bool kin[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-        kk[j] = min(k0 + j, L - 1);
+        kk[j] = adj_clamp(k0 + j, L);
         kin[j] = k0 + j < L;
     }
-    const int kl = max(k0 - 1, 0);      // left neighbour of the first position (clamped)
-    const int kr = min(k0 + P, L - 1);  // right neighbour of the last position (clamped)
+    const int kl = adj_left(k0, L);         // left neighbour of the first position (clamped)
+    const int kr = adj_right(k0, P, L);  // right neighbour of the last position (clamped)
 
     const int t0 = q * a.K;
     const int t1 = min(t0 + a.K, S);
     const bool rev = a.reverse != 0;
-    auto line_of = [&](int t) { return rev ? S - 1 - t : t; };
+    auto line_of = [&](int t) { return adj_row(t, S, rev); };
 
     // ring: per step and channel g, x, lambda and h_{t-1} at the positions
     // and their two outer neighbours; the three logits (shared by the group)
     float rg[D][G][P], rx[D][G][P], rl[D][G][P], rh[D][G][P + 2], rz[D][3][P];
     auto fill = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
-        const int tc = max(t, t0);
-        const int64_t lo = static_cast<int64_t>(line_of(tc)) * L;
-        const int64_t hlo = static_cast<int64_t>(line_of(max(tc - 1, t0))) * L;  // h_{t-1} (clamped)
+        const AdjFill f = adj_fill(t, t0, S, L, rev);
+        const int64_t lo = f.lo;
+        const int64_t hlo = f.hlo;  // h_{t-1} (clamped)
 #pragma unroll
         for (int j = 0; j < P; ++j) {
 #pragma unroll
@@ -320,12 +376,9 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
 template <typename T, int P, int G, bool MERGE, bool NT>
 __global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
     extern __shared__ float s_edge_raw[];
-    int dir = 0;
-    int64_t idx = blockIdx.x;
-    while (dir < 3 && idx >= a.blocks[dir]) {
-        idx -= a.blocks[dir];
-        ++dir;
-    }
+    int dir;
+    int64_t idx;
+    adj4_block(a, blockIdx.x, dir, idx);
     const AdjK& k = a.d[dir];
     const int64_t pg = idx / k.nchunks;
     const int q = static_cast<int>(idx - pg * k.nchunks);
@@ -384,6 +437,125 @@ unsigned grid_for(int64_t total) {
 
 }  // namespace
 
+#ifdef GSPN_CHECK_LAUNCHES
+// Host replay of adj4_kernel: for every block and thread, each access of
+// every step at the offsets adj_line computes with the functions above
+// (fills for steps t0 - D .. t1 - 1, clamped as the kernel clamps them;
+// stores, atomics and merge accesses for the chunk's steps), and every LDS
+// edge index against the launch's dynamic LDS.
+static void replay_adjoint4(const Adj4K& k, int64_t nblocks, int nt, size_t lds, int es, int P, int G, int D, bool merge) {
+    const char* kn = "adj4_kernel";
+    int64_t bad = 0, n = 0;
+    auto fail = [&](const char* what, int64_t b, int tid, int t) {
+        if (bad++ < 4) check::violation(kn, what, "block %lld thread %d step %d", static_cast<long long>(b), tid, t);
+    };
+    check::Region rx[4], rg[4], rl[4], rz[4], rh[4], rdl[4], rdz[4], rdx[4], rms[4], rdm[4];
+    for (int d = 0; d < 4; ++d) {
+        const AdjK& a = k.d[d];
+        rx[d] = check::region_of(a.x, kn, "x");
+        rg[d] = check::region_of(a.g, kn, "dL/dy");
+        rl[d] = check::region_of(a.lam, kn, "lambda");
+        rz[d] = check::region_of(a.z, kn, "logits");
+        rh[d] = check::region_of(a.hs, kn, "states");
+        rdl[d] = check::region_of(a.dlam, kn, "dlambda");
+        rdz[d] = check::region_of(a.dz, kn, "dlogits");
+        rdx[d] = check::region_of(a.dx, kn, "dx");
+        if (merge && a.mscale) rms[d] = check::region_of(a.mscale, kn, "merge");
+        if (merge && a.dmerge) rdm[d] = check::region_of(a.dmerge, kn, "dmerge");
+    }
+    for (int b = 0; b < 2; ++b)
+        for (int side = 0; side < 2; ++side)
+            for (int g = 0; g < G; ++g)
+                for (int lane = 0; lane < nt; ++lane)
+                    if (static_cast<size_t>(adj_edge(b, side, G, g, nt, lane) + 1) * 4 > lds) fail("edge LDS", -1, lane, -1);
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int dir;
+        int64_t idx;
+        adj4_block(k, b, dir, idx);
+        const AdjK& a = k.d[dir];
+        const int64_t pg = idx / a.nchunks;
+        const int q = static_cast<int>(idx - pg * a.nchunks);
+        const int S = a.S, L = a.L;
+        const int64_t plane = static_cast<int64_t>(S) * L;
+        const AdjGroup grp = adj_group(a, pg, G, plane);
+        const int t0 = q * a.K;
+        const int t1 = (t0 + a.K < S) ? t0 + a.K : S;
+        const bool rev = a.reverse != 0;
+        const int64_t pe = grp.p0 * plane * es;  // bytes to the group's first plane
+        const char* zb = static_cast<const char*>(a.z) + grp.zplane * es;
+        const float* hb = a.hs + grp.p0 * plane;
+        for (int g = 0; g < G; ++g) {
+            const bool ok = adj_member_ok(a, grp.c0, g);
+            const int64_t c = grp.c0 + adj_member(a, grp.c0, g);
+            if (merge && a.mscale && !check::in_region(rms[dir], a.mscale, c * 4, 4)) fail("merge weight", b, -1, -1);
+            if (merge && a.dmerge && ok && !check::in_region(rdm[dir], a.dmerge, (grp.c0 + g) * 4, 4))
+                fail("dmerge", b, -1, -1);
+        }
+        for (int tid = 0; tid < nt; ++tid) {
+            const int k0 = tid * P;
+            const int kl = adj_left(k0, L), kr = adj_right(k0, P, L);
+            for (int t = t0 - D; t < t1; ++t) {
+                const AdjFill f = adj_fill(t, t0, S, L, rev);
+                for (int j = 0; j < P; ++j) {
+                    const int kk = adj_clamp(k0 + j, L);
+                    for (int o = 0; o < 3; ++o)
+                        if (!check::in_region(rz[dir], zb, (o * plane + f.lo + kk) * es, es)) fail("logit load", b, tid, t);
+                    for (int g = 0; g < G; ++g) {
+                        const int64_t go = adj_member(a, grp.c0, g) * plane;
+                        const int64_t e = (go + f.lo + kk) * es;
+                        if (!check::in_region(rg[dir], a.g, pe + e, es)) fail("dL/dy load", b, tid, t);
+                        if (!check::in_region(rx[dir], a.x, pe + e, es)) fail("x load", b, tid, t);
+                        if (!check::in_region(rl[dir], a.lam, pe + e, es)) fail("lambda load", b, tid, t);
+                        if (!check::in_region(rh[dir], hb, (go + f.hlo + kk) * 4, 4)) fail("state load", b, tid, t);
+                    }
+                }
+                for (int g = 0; g < G; ++g) {
+                    const int64_t go = adj_member(a, grp.c0, g) * plane;
+                    if (!check::in_region(rh[dir], hb, (go + f.hlo + kl) * 4, 4)) fail("left state", b, tid, t);
+                    if (!check::in_region(rh[dir], hb, (go + f.hlo + kr) * 4, 4)) fail("right state", b, tid, t);
+                }
+                n += P * (3 + 4 * G) + 2 * G;
+                if (t < t0) continue;
+                // the step's stores
+                const int64_t lo = static_cast<int64_t>(adj_row(t, S, rev)) * L;
+                for (int j = 0; j < P; ++j) {
+                    if (k0 + j >= L) continue;
+                    for (int g = 0; g < G; ++g) {
+                        if (!adj_member_ok(a, grp.c0, g)) continue;
+                        const int64_t e = (adj_member(a, grp.c0, g) * plane + lo + k0 + j) * es;
+                        if (!check::in_region(rdl[dir], a.dlam, pe + e, es)) fail("dlambda store", b, tid, t);
+                        if (!check::in_region(rdx[dir], a.dx, pe + e, es)) fail("dx store", b, tid, t);
+                    }
+                    if (a.shared) {
+                        if (t != t0) {
+                            const int64_t e = (grp.nidx * 3 * plane + lo + k0 + j) * 4;
+                            if (!check::in_region(rdz[dir], a.dz, e, 4) || !check::in_region(rdz[dir], a.dz, e + plane * 4, 4))
+                                fail("dlogit sum atomic", b, tid, t);
+                        }
+                    } else {
+                        for (int o = 0; o < 3; ++o)
+                            if (!check::in_region(rdz[dir], a.dz, (grp.zplane + o * plane + lo + k0 + j) * es, es))
+                                fail("dlogit store", b, tid, t);
+                    }
+                    n += 2 * G + 3;
+                }
+            }
+        }
+    }
+    if (bad) check::violation(kn, "accesses", "%lld bad", static_cast<long long>(bad));
+    check::count_accesses(n);
+    check::replayed(kn, 1024, 0);
+}
+
+static void replay_elementwise(const char* kn, const char* what, const void* base, int64_t first, int64_t end, int es) {
+    const check::Region r = check::region_of(base, kn, what);
+    if (end > first && (!check::in_region(r, base, first * es, es) || !check::in_region(r, base, (end - 1) * es, es)))
+        check::violation(kn, what, "elements [%lld, %lld) outside the buffer", static_cast<long long>(first),
+                         static_cast<long long>(end));
+    check::count_accesses(end - first);
+}
+#endif
+
 hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, AdjointPlan* plan) {
     Adj4K k;
     int maxL = 1;
@@ -427,6 +599,12 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, Adjo
     bool nt = true;
     for (int d = 0; d < 4; ++d) nt = nt && (p[d].L * (f32 ? 4 : 2)) % 128 == 0;
     if (plan) *plan = {P, G, nt ? 1 : 0};
+#ifdef GSPN_CHECK_LAUNCHES
+    {
+        const int depth = (P == 1 && G == 1) ? adj_depth<1, 1>() : adj_depth<2, 2>();
+        replay_adjoint4(k, total, lanes, lds, f32 ? 4 : 2, P, G, depth, merge);
+    }
+#endif
 #define GSPN_ADJ_LAUNCH(PP, GG, MM)                                                                               \
     do {                                                                                                          \
         if (f32) {                                                                                                \
@@ -455,6 +633,11 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, Adjo
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+#ifdef GSPN_CHECK_LAUNCHES
+    // grid-stride loop over [0, n)
+    replay_elementwise("fill_zero_kernel", "p", p, 0, n, 4);
+    check::replayed("fill_zero_kernel", 256, 0);
+#endif
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
@@ -462,6 +645,17 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
 hipError_t launch_finish_shared_dz(const float* sums, const void* logits, void* dlogits, int64_t n, int64_t S,
                                    int64_t L, int dtype, hipStream_t stream) {
     const unsigned grid = grid_for(n * S * L);
+#ifdef GSPN_CHECK_LAUNCHES
+    // grid-stride loop over the n * S * L positions: planes 0..2 of [n][3][S][L]
+    {
+        const char* kn = "finish_shared_dz_kernel";
+        const int es = dtype == kF32 ? 4 : 2;
+        replay_elementwise(kn, "sums", sums, 0, n * 3 * S * L - S * L, 4);
+        replay_elementwise(kn, "logits", logits, 0, n * 3 * S * L, es);
+        replay_elementwise(kn, "dlogits", dlogits, 0, n * 3 * S * L, es);
+        check::replayed(kn, 256, 0);
+    }
+#endif
     if (dtype == kF32) {
         hipLaunchKernelGGL(finish_shared_dz_kernel<float>, dim3(grid), dim3(256), 0, stream, sums,
                            static_cast<const float*>(logits), static_cast<float*>(dlogits), n, static_cast<int>(S),

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "check.hpp"
+
 namespace gspn {
 
 using bf16_t = uint16_t;  // bf16 storage as raw bits

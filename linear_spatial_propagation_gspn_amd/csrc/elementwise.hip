@@ -7,6 +7,20 @@
 namespace gspn {
 namespace {
 
+// Element e of [planes][S][L] positions (per_plane = S * L): the offset of
+// its first logit in [planes][3][S][L] and its position k on the line.
+// Shared by the kernels and their host replay.
+struct NormPos {
+    int64_t base;
+    int64_t k;
+};
+
+GSPN_HD NormPos norm_pos(int64_t e, int64_t per_plane, int64_t L) {
+    const int64_t pl = e / per_plane;
+    const int64_t r = e - pl * per_plane;
+    return {pl * 3 * per_plane + r, r % L};
+}
+
 // w = sigmoid row normalisation of the logit triple at every (plane, i, k)
 // (GSPN summary page, "Approach"; rows sum to 1, border rows renormalised
 // over the neighbours that exist).  Layout [planes][3][S][L].
@@ -18,10 +32,9 @@ __global__ __launch_bounds__(256) void normalize_kernel(const T* __restrict__ z,
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
          e += stride) {
-        const int64_t pl = e / per_plane;
-        const int64_t r = e - pl * per_plane;
-        const int64_t k = r % L;
-        const int64_t base = pl * 3 * per_plane + r;
+        const NormPos np = norm_pos(e, per_plane, L);
+        const int64_t k = np.k;
+        const int64_t base = np.base;
         float w0, w1, w2;
         normalise_row(Store<T>::ld(z + base), Store<T>::ld(z + base + per_plane),
                       Store<T>::ld(z + base + 2 * per_plane), k > 0, k + 1 < L, w0, w1, w2);
@@ -66,10 +79,9 @@ __global__ __launch_bounds__(256) void normalize_pair4_kernel(const Pair4K a) {
         };
         for (int64_t v = first; v < total / VW; v += stride) {
             const int64_t e = v * VW;
-            const int64_t pl = e / per_plane;
-            const int64_t r = e - pl * per_plane;
-            const int64_t k0 = r % L;
-            const T* zb = z + pl * 3 * per_plane + r;
+            const NormPos np = norm_pos(e, per_plane, L);
+            const int64_t k0 = np.k;
+            const T* zb = z + np.base;
             const V z0 = *reinterpret_cast<const V*>(zb);
             const V z1 = *reinterpret_cast<const V*>(zb + per_plane);
             const V z2 = *reinterpret_cast<const V*>(zb + 2 * per_plane);
@@ -87,10 +99,9 @@ __global__ __launch_bounds__(256) void normalize_pair4_kernel(const Pair4K a) {
         }
     } else {
         for (int64_t e = first; e < total; e += stride) {
-            const int64_t pl = e / per_plane;
-            const int64_t r = e - pl * per_plane;
-            const int64_t k = r % L;
-            const int64_t base = pl * 3 * per_plane + r;
+            const NormPos np = norm_pos(e, per_plane, L);
+            const int64_t k = np.k;
+            const int64_t base = np.base;
             float w0, w1, w2;
             normalise_row(Store<T>::ld(z + base), Store<T>::ld(z + base + per_plane),
                           Store<T>::ld(z + base + 2 * per_plane), k > 0, k + 1 < L, w0, w1, w2);
@@ -123,6 +134,36 @@ unsigned grid_for(int64_t total, int threads) {
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+#ifdef GSPN_CHECK_LAUNCHES
+// Host replay of the normalisation kernels: for every element (or vector of
+// VW elements) the grid-stride loops visit, the three logits read and the
+// outputs written, at the offsets norm_pos gives.
+void replay_normalize(const char* kn, const void* z, const void* w, int64_t planes, int64_t S, int64_t L, int es,
+                      int eo, int vw, bool pair, bool vec) {
+    const check::Region rz = check::region_of(z, kn, "logits");
+    const check::Region rw = check::region_of(w, kn, "weights");
+    const int64_t per_plane = S * L;
+    const int64_t total = planes * per_plane;
+    const int64_t step = vec ? vw : 1;
+    int64_t bad = 0;
+    for (int64_t e = 0; e + step <= total; e += step) {
+        const NormPos np = norm_pos(e, per_plane, L);
+        for (int o = 0; o < 3; ++o)
+            if (!check::in_region(rz, z, (np.base + o * per_plane) * es, step * es) ||
+                (vec && (reinterpret_cast<uint64_t>(z) + (np.base + o * per_plane) * es) % 16 != 0))
+                ++bad;
+        if (pair) {
+            if (!check::in_region(rw, w, e * 4, step * 4)) ++bad;
+        } else {
+            for (int o = 0; o < 3; ++o)
+                if (!check::in_region(rw, w, (np.base + o * per_plane) * eo, eo)) ++bad;
+        }
+    }
+    if (bad) check::violation(kn, "accesses", "%lld bad", static_cast<long long>(bad));
+    check::count_accesses(total * 6);
+}
+#endif
+
 }  // namespace
 
 hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w,
@@ -134,6 +175,11 @@ hipError_t launch_normalize(int dir, int64_t n, int64_t cw, int64_t h, int64_t w
     const int64_t planes = n * cw;
     const unsigned grid = grid_for(planes * S * L, 256);
     if (out_dtype < 0) out_dtype = dtype;
+#ifdef GSPN_CHECK_LAUNCHES
+    replay_normalize("normalize_kernel", logits, w_out, planes, S, L, dtype == kF32 ? 4 : 2,
+                     out_dtype == kF32 ? 4 : 2, 1, false, false);
+    check::replayed("normalize_kernel", 256, 0);
+#endif
     if (dtype == kF32) {
         hipLaunchKernelGGL((normalize_kernel<float, float>), dim3(grid), dim3(256), 0, stream,
                            static_cast<const float*>(logits), static_cast<float*>(w_out), planes, S, L);
@@ -164,6 +210,12 @@ hipError_t launch_normalize_pair4(int64_t n, int64_t h, int64_t w, const void* c
     }
     const int64_t total = n * h * w;
     const dim3 grid(grid_for(k.vec ? total / vw : total, 256), 4);
+#ifdef GSPN_CHECK_LAUNCHES
+    for (int d = 0; d < 4; ++d)
+        replay_normalize("normalize_pair4_kernel", k.z[d], k.w[d], n, k.S[d], k.L[d], dtype == kF32 ? 4 : 2, 4, vw,
+                         true, k.vec != 0);
+    check::replayed("normalize_pair4_kernel", 256, 0);
+#endif
     if (dtype == kF32) hipLaunchKernelGGL(normalize_pair4_kernel<float>, grid, dim3(256), 0, stream, k);
     else hipLaunchKernelGGL(normalize_pair4_kernel<bf16_t>, grid, dim3(256), 0, stream, k);
     return hipGetLastError();

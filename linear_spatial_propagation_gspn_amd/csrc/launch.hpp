@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "check.hpp"
+
 namespace gspn {
 
 enum Dtype { kF32 = 0, kBF16 = 1 };

@@ -19,7 +19,9 @@ namespace gspn {
 
 namespace {
 
+#ifndef GSPN_CHECK_LAUNCHES
 static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+#endif
 
 constexpr int kMaxDevices = 64;
 std::mutex scratch_mu;
@@ -29,11 +31,18 @@ void* scratch_ptr[kMaxDevices] = {};
 
 hipError_t noalloc_scratch(void** out) {
     *out = nullptr;
+#ifdef GSPN_CHECK_LAUNCHES
+    // the host-only checking build has no device array: a fixed address
+    // range stands for it, which the caller registers as a buffer
+    *out = reinterpret_cast<void*>(check::kScratchStandIn);
+    return hipSuccess;
+#endif
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(scratch_mu);
+#ifndef GSPN_CHECK_LAUNCHES
     if (!scratch_ptr[dev]) {
         void* p = nullptr;
         e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with dev current
@@ -41,6 +50,7 @@ hipError_t noalloc_scratch(void** out) {
         if (!p) return hipErrorInvalidSymbol;
         scratch_ptr[dev] = p;
     }
+#endif
     *out = scratch_ptr[dev];
     return hipSuccess;
 }

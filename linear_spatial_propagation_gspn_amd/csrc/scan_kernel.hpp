@@ -56,6 +56,23 @@ struct ScanK {
     const float* mscale;  // merge weight of each channel for this direction ([c]), or null for 1
 };
 
+// Index code of scan_line and the long-line kernel, shared with the host
+// replay: a position clamped into the line (addresses of lanes past its end),
+// the row of scan step t, the step whose row a prefetch for step t reads
+// (steps past the chunk read its last row), and the offset of plane p's
+// weight rows from a.wts in weight elements (packed pairs: one a position).
+GSPN_HD int scan_pos(int k, int L) { return k < L - 1 ? k : L - 1; }
+GSPN_HD int scan_row(int t, int S, bool rev) { return rev ? S - 1 - t : t; }
+GSPN_HD int scan_fetch_step(int t, int t1) { return t < t1 - 1 ? t : t1 - 1; }
+GSPN_HD int64_t scan_weight_offset(const ScanK& a, int64_t p, int64_t plane, bool pair) {
+    const int64_t nidx = p / a.c;
+    const int64_t ci = p - nidx * a.c;
+    return pair ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane;
+}
+// LDS edge value `which` (0: the lane's first position, 1: its last) of lane
+// `lane` in buffer b, for nt lanes.
+GSPN_HD int scan_edge(int b, int which, int nt, int lane) { return (b * 2 + which) * nt + lane; }
+
 template <typename T, int N>
 struct alignas(sizeof(T) * N) VecT {
     T e[N];
@@ -84,7 +101,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
     static_assert(!HORIZ || UT % VW == 0, "tile width must be whole vectors");
 
     auto edge = [&](int b, int which, int lane) -> float& {
-        return edge_raw[(b * 2 + which) * blockDim.x + lane];
+        return edge_raw[scan_edge(b, which, blockDim.x, lane)];
     };
 
     const int tid = threadIdx.x;
@@ -100,8 +117,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
     const float msc = a.mscale ? a.mscale[ci] : 1.0f;  // learnable merge: this direction's weight
     constexpr bool PAIR = std::is_same_v<TW, WPair>;
     using ZT = std::conditional_t<PAIR, uint32_t, TW>;
-    const ZT* __restrict__ zp =
-        static_cast<const ZT*>(a.wts) + (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane);
+    const ZT* __restrict__ zp = static_cast<const ZT*>(a.wts) + scan_weight_offset(a, p, plane, PAIR);
     T* __restrict__ op = static_cast<T*>(a.out) + p * plane;
     TO* __restrict__ oq = static_cast<TO*>(a.out) + p * plane;
 
@@ -116,7 +132,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
     bool kin[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-        kk[j] = min(k0 + j, L - 1);
+        kk[j] = scan_pos(k0 + j, L);
         kin[j] = k0 + j < L;
     }
 
@@ -129,7 +145,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
     float xt[HORIZ ? 2 : 1][P][HORIZ ? UT : 1];
     float yt[HORIZ ? 2 : 1][P][HORIZ ? UT : 1];
 
-    auto line_of = [&](int t) { return rev ? S - 1 - t : t; };
+    auto line_of = [&](int t) { return scan_row(t, S, rev); };
 
     // Inputs of the U steps from tb into ring buffer R; steps past the chunk
     // read the chunk's last line (loaded, never used).
@@ -137,7 +153,7 @@ __device__ __forceinline__ void scan_line(const ScanK& a, int64_t p, int q, floa
         constexpr int R = decltype(rc)::value;
 #pragma unroll
         for (int s = 0; s < U; ++s) {
-            const int64_t lo = static_cast<int64_t>(line_of(min(tb + s, t1 - 1))) * L;
+            const int64_t lo = static_cast<int64_t>(line_of(scan_fetch_step(tb + s, t1))) * L;
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 if constexpr (PAIR) {
@@ -381,7 +397,7 @@ constexpr int waves_per_eu() {
 
 // Single-direction launch: one workgroup per (plane, chunk).
 template <typename T, typename TW, int P, int U, int UT, bool HORIZ, bool REV, bool ACC>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(waves_per_eu<HORIZ, P>())))
+__global__ __launch_bounds__(1024) GSPN_WAVES_PER_EU((waves_per_eu<HORIZ, P>()))
 void scan_kernel(const ScanK a) {
     extern __shared__ float s_edge_raw[];
     const int64_t blk = blockIdx.x;
@@ -477,14 +493,11 @@ struct Scan4K {
     int64_t planes;  // long-line kernel: planes per direction (n * c)
 };
 
-template <typename T, typename TW, int PV, int PH>
-__global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
-    extern __shared__ float s_edge_raw[];
-    using BV = Blocking<T, PV, false>;
-    using BH = Blocking<T, PH, true>;
-    const int64_t b = blockIdx.x;
-    int dir = 0;
-    int64_t idx = b;
+// Direction and index within it of block b of a four-direction launch:
+// direction b % 4 when interleaved, else consecutive ranges.
+GSPN_HD void scan4_block(const Scan4K& a, int64_t b, int& dir, int64_t& idx) {
+    dir = 0;
+    idx = b;
     if (a.interleave) {
         dir = static_cast<int>(b & 3);
         idx = b >> 2;
@@ -494,6 +507,16 @@ __global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
             ++dir;
         }
     }
+}
+
+template <typename T, typename TW, int PV, int PH>
+__global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
+    extern __shared__ float s_edge_raw[];
+    using BV = Blocking<T, PV, false>;
+    using BH = Blocking<T, PH, true>;
+    int dir;
+    int64_t idx;
+    scan4_block(a, blockIdx.x, dir, idx);
     const ScanK& k = a.d[dir];
     const int64_t p = idx / k.nchunks;
     const int q = static_cast<int>(idx - p * k.nchunks);
@@ -511,23 +534,14 @@ __global__ __launch_bounds__(1024) void scan4_kernel(const Scan4K a) {
 // lane of the first two / last two scans.
 template <typename T, typename TW, int PV, int PH, typename TO = T>
 __global__ __launch_bounds__(1024)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<false, (PV > PH ? PV : PH)>())))
+GSPN_WAVES_PER_EU((waves_per_eu<false, (PV > PH ? PV : PH)>()))
 void scan4v_kernel(const Scan4K a) {
     extern __shared__ float s_edge_raw[];
     using BV = Blocking<T, PV, false>;
     using BH = Blocking<T, PH, false>;
-    const int64_t b = blockIdx.x;
-    int dir = 0;
-    int64_t idx = b;
-    if (a.interleave) {
-        dir = static_cast<int>(b & 3);
-        idx = b >> 2;
-    } else {
-        while (dir < 3 && idx >= a.blocks[dir]) {
-            idx -= a.blocks[dir];
-            ++dir;
-        }
-    }
+    int dir;
+    int64_t idx;
+    scan4_block(a, blockIdx.x, dir, idx);
     const ScanK& k = a.d[dir];
     const int64_t p = idx / k.nchunks;
     const int q = static_cast<int>(idx - p * k.nchunks);
@@ -538,11 +552,85 @@ void scan4v_kernel(const Scan4K a) {
     }
 }
 
+#ifdef GSPN_CHECK_LAUNCHES
+// Host replay of scan4v_kernel (vertical-form scan_line, no accumulate): for
+// every block and thread, each element access of every step at the offsets
+// scan_line computes with the functions above (prefetches for steps t0 ..
+// t1, clamped to the chunk's last row; stores by lanes on the line), and
+// every LDS edge index against the launch's dynamic LDS.
+template <typename T, typename TW, typename TO>
+void replay_fused4v(const Scan4K& k, int pv, int ph, int nthreads, size_t lds) {
+    const char* kn = "scan4v_kernel";
+    constexpr bool PAIR = std::is_same_v<TW, WPair>;
+    constexpr int ZE = PAIR ? 4 : static_cast<int>(sizeof(TW));
+    constexpr int NZ = PAIR ? 1 : 3;
+    constexpr int ES = static_cast<int>(sizeof(T));
+    constexpr int EO = static_cast<int>(sizeof(TO));
+    const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
+    int64_t bad = 0, n = 0;
+    auto fail = [&](const char* what, int64_t b, int tid, int t) {
+        if (bad++ < 4) check::violation(kn, what, "block %lld thread %d step %d", static_cast<long long>(b), tid, t);
+    };
+    for (int lane = 0; lane < nthreads; ++lane)
+        if (static_cast<size_t>(scan_edge(1, 1, nthreads, lane) + 1) * 4 > lds) fail("edge LDS", -1, lane, -1);
+    check::Region rx[4], rl[4], ro[4], rz[4];
+    for (int d = 0; d < 4; ++d) {
+        rx[d] = check::region_of(k.d[d].x, kn, "x");
+        rl[d] = check::region_of(k.d[d].lam, kn, "lambda");
+        ro[d] = check::region_of(k.d[d].out, kn, "out");
+        rz[d] = check::region_of(k.d[d].wts, kn, "weights");
+    }
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int dir;
+        int64_t idx;
+        scan4_block(k, b, dir, idx);
+        const ScanK& a = k.d[dir];
+        const int P = dir < 2 ? pv : ph;
+        const int64_t p = idx / a.nchunks;
+        const int q = static_cast<int>(idx - p * a.nchunks);
+        const int S = a.S, L = a.L;
+        const int64_t plane = static_cast<int64_t>(S) * L;
+        const int t0 = q * a.K;
+        const int t1 = (t0 + a.K < S) ? t0 + a.K : S;
+        const bool rev = a.reverse != 0;
+        const char* xb = static_cast<const char*>(a.x) + p * plane * ES;
+        const char* lb = static_cast<const char*>(a.lam) + p * plane * ES;
+        const char* ob = static_cast<const char*>(a.out) + p * plane * EO;
+        const char* zb = static_cast<const char*>(a.wts) + scan_weight_offset(a, p, plane, PAIR) * ZE;
+        for (int tid = 0; tid < nthreads; ++tid) {
+            const int k0 = tid * P;
+            for (int t = t0; t <= t1; ++t) {
+                const int64_t lo = static_cast<int64_t>(scan_row(scan_fetch_step(t, t1), S, rev)) * L;
+                for (int j = 0; j < P; ++j) {
+                    const int64_t e = lo + scan_pos(k0 + j, L);
+                    for (int o = 0; o < NZ; ++o)
+                        if (!check::in_region(rz[dir], zb, (o * plane + e) * ZE, ZE)) fail("weight load", b, tid, t);
+                    if (!check::in_region(rl[dir], lb, e * ES, ES)) fail("lambda load", b, tid, t);
+                    if (!check::in_region(rx[dir], xb, e * ES, ES)) fail("x load", b, tid, t);
+                    n += NZ + 2;
+                    if (t < t1 && k0 + j < L) {
+                        const int64_t so = static_cast<int64_t>(scan_row(t, S, rev)) * L + k0 + j;
+                        if (!check::in_region(ro[dir], ob, so * EO, EO)) fail("store", b, tid, t);
+                        ++n;
+                    }
+                }
+            }
+        }
+    }
+    if (bad) check::violation(kn, "accesses", "%lld bad", static_cast<long long>(bad));
+    check::count_accesses(n);
+    check::replayed(kn, 1024, 0);
+}
+#endif
+
 template <typename T, typename TW, typename TO = T>
 hipError_t launch_fused4v(const Scan4K& k, int pv, int ph, int nthreads, hipStream_t stream) {
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
     const size_t lds = 4 * sizeof(float) * static_cast<size_t>(nthreads);
     const dim3 grid(static_cast<unsigned>(nblocks));
+#ifdef GSPN_CHECK_LAUNCHES
+    replay_fused4v<T, TW, TO>(k, pv, ph, nthreads, lds);
+#endif
     if (pv == 1 && ph == 1) {
         hipLaunchKernelGGL((scan4v_kernel<T, TW, 1, 1, TO>), grid, dim3(nthreads), lds, stream, k);
     } else if (pv == 1) {

@@ -94,6 +94,50 @@ __device__ __forceinline__ float shift_from_upper_lane(float v) {  // lane i get
 
 }  // namespace lp
 
+// Index code of lp_line and scan4lp_kernel, shared with the host replay.
+
+// Byte offsets of a lane's vector in a row of x and lambda (vt), of one
+// weight row (vw) and of the output (vo): the lane's first position, or for
+// a lane past the line (or of an invalid plane) the line's last vector.
+struct LpLane {
+    uint32_t vt, vw, vo;
+    bool active;  // the lane holds positions of a line
+};
+
+GSPN_HD LpLane lp_lane(int tid, bool valid, int L, int P, int es, int zb, int eo) {
+    const int k0 = tid * P;
+    const bool active = valid && k0 < L;
+    const uint32_t k0c = static_cast<uint32_t>(active ? k0 : L - P);
+    return {k0c * static_cast<uint32_t>(es), k0c * static_cast<uint32_t>(zb), k0c * static_cast<uint32_t>(eo),
+            active};
+}
+
+// Bytes from a.wts to the weight rows of plane p (zb bytes a position and row).
+GSPN_HD int64_t lp_weight_offset(const ScanK& a, int64_t p, int64_t plane, bool pair, int zb) {
+    return scan_weight_offset(a, p, plane, pair) * zb;
+}
+
+// Row of scan step t; the step whose row a fill for step t reads (steps past
+// the chunk read its last row).
+GSPN_HD uint32_t lp_row(int t, int S, bool rev) { return static_cast<uint32_t>(scan_row(t, S, rev)); }
+GSPN_HD int lp_fill_step(int t, int t1) { return scan_fetch_step(t, t1); }
+
+// The plane and waves of member g of a long-line workgroup: a.group planes
+// share it, per threads each.
+struct LpMember {
+    int64_t p;    // plane (clamped to an existing one when invalid)
+    bool valid;
+    int tid;      // thread index within the member
+    int wave0;    // the member's first wave
+    int nwaves;
+};
+
+GSPN_HD LpMember lp_member(const Scan4K& a, int64_t pg, int g, int per, int tid) {
+    const int64_t p = pg * a.group + g;
+    const bool valid = p < a.planes;
+    return {valid ? p : a.planes - 1, valid, tid - g * per, g * (per >> 6), per >> 6};
+}
+
 // One (plane, chunk) line of a vertical-form scan, run by `nwaves` waves of
 // the workgroup starting at wave `wave0`; tid is the thread's index among
 // them.  valid = false: the waves only keep step with the workgroup's
@@ -118,23 +162,21 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
     const int S = a.S;
     const int L = a.L;
     const int64_t plane = static_cast<int64_t>(S) * L;
-    const int64_t nidx = p / a.c;
-    const int64_t ci = p - nidx * a.c;
 
     const auto rx = lp::rsrc(static_cast<const T*>(a.x) + p * plane, plane * sizeof(T));
     const auto rl = lp::rsrc(static_cast<const T*>(a.lam) + p * plane, plane * sizeof(T));
     const auto ro = lp::rsrc(static_cast<TO*>(a.out) + p * plane, plane * sizeof(TO));
-    const auto rz = lp::rsrc(static_cast<const char*>(a.wts) +
-                                 (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane) * ZB,
+    const auto rz = lp::rsrc(static_cast<const char*>(a.wts) + lp_weight_offset(a, p, plane, PAIR, ZB),
                              NZ * plane * ZB);
 
     const int k0 = tid * P;
-    const bool active = valid && k0 < L;
-    const int k0c = active ? k0 : L - P;  // lanes past the line read its last vector (unused)
-    const uint32_t vt = static_cast<uint32_t>(k0c) * sizeof(T);
-    const uint32_t vw = static_cast<uint32_t>(k0c) * ZB;
+    // lanes past the line read its last vector (unused)
+    const LpLane ln = lp_lane(tid, valid, L, P, sizeof(T), ZB, sizeof(TO));
+    const bool active = ln.active;
+    const uint32_t vt = ln.vt;
+    const uint32_t vw = ln.vw;
     const uint32_t rowT = static_cast<uint32_t>(L) * sizeof(T);
-    const uint32_t vo = static_cast<uint32_t>(k0c) * sizeof(TO);
+    const uint32_t vo = ln.vo;
     const uint32_t rowO = static_cast<uint32_t>(L) * sizeof(TO);
     const uint32_t rowW = static_cast<uint32_t>(L) * ZB;
     const uint32_t planeW = static_cast<uint32_t>(plane) * ZB;
@@ -144,12 +186,12 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
     const int t0 = q * a.K;
     const int t1 = min(t0 + a.K, S);
     const bool rev = a.reverse != 0;
-    auto line_of = [&](int t) { return static_cast<uint32_t>(rev ? S - 1 - t : t); };
+    auto line_of = [&](int t) { return lp_row(t, S, rev); };
 
     uint32_t sx[D][WT], sl[D][WT], sz[D][NZ][WW];
     auto fill = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
-        const uint32_t i = line_of(min(t, t1 - 1));
+        const uint32_t i = line_of(lp_fill_step(t, t1));
         lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, i * rowT);
         lp::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, i * rowT);
         // logits are per channel here unless a single channel shares them;
@@ -284,18 +326,9 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
 // ranges, as in scan4v_kernel.
 template <typename T, typename TW, bool LOGITS, typename TO = T>
 __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) {
-    const int64_t b = blockIdx.x;
-    int dir = 0;
-    int64_t idx = b;
-    if (a.interleave) {
-        dir = static_cast<int>(b & 3);
-        idx = b >> 2;
-    } else {
-        while (dir < 3 && idx >= a.blocks[dir]) {
-            idx -= a.blocks[dir];
-            ++dir;
-        }
-    }
+    int dir;
+    int64_t idx;
+    scan4_block(a, blockIdx.x, dir, idx);
     const ScanK& k = a.d[dir];
     const int64_t pg = idx / k.nchunks;
     const int q = static_cast<int>(idx - pg * k.nchunks);
@@ -306,15 +339,118 @@ __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) 
     // per is a whole number of waves, so g is uniform in the wave: say so, to
     // keep the plane's buffer resources in scalar registers
     const int g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / per);
-    const int64_t p = pg * a.group + g;
-    const bool valid = p < a.planes;
-    lp_line<T, TW, LOGITS, TO>(k, valid ? p : a.planes - 1, q, valid, static_cast<int>(threadIdx.x) - g * per,
-                               g * (per >> 6), per >> 6);
+    const LpMember m = lp_member(a, pg, g, per, static_cast<int>(threadIdx.x));
+    lp_line<T, TW, LOGITS, TO>(k, m.p, q, m.valid, m.tid, m.wave0, m.nwaves);
 }
+
+#ifdef GSPN_CHECK_LAUNCHES
+// Host replay of scan4lp_kernel: for every block, member and thread, the
+// buffer resources of its plane and each 16-byte access of every step, at
+// the offsets lp_line computes with the functions above (fills for steps t0
+// .. t1 + D - 1, the last D of them clamped to the chunk's last row; stores
+// for the chunk's steps by active lanes).  An access must lie in its
+// tensor's buffer and inside its resource (the hardware would drop it
+// silently otherwise).
+template <typename T, typename TW, bool LOGITS, typename TO>
+void replay_fused4lp(const Scan4K& k, int nthreads) {
+    const char* kn = "scan4lp_kernel";
+    constexpr int P = 16 / static_cast<int>(sizeof(T));
+    constexpr int WT = P * static_cast<int>(sizeof(T)) / 4;
+    constexpr bool PAIR = std::is_same_v<TW, WPair>;
+    constexpr int ZB = PAIR ? 4 : static_cast<int>(sizeof(TW));
+    constexpr int NZ = PAIR ? 1 : 3;
+    constexpr int WW = P * ZB / 4;
+    constexpr int WO = P * static_cast<int>(sizeof(TO)) / 4;
+    constexpr int D = GSPN_LP_DEPTH;
+    const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
+    if (k.group < 1 || nthreads % k.group != 0 || (nthreads / k.group) % 64 != 0)
+        check::violation(kn, "block", "%d threads do not split into %d whole-wave members", nthreads, k.group);
+    const int per = nthreads / k.group;
+    check::Region rx[4], rl[4], ro[4], rz[4];
+    for (int d = 0; d < 4; ++d) {
+        rx[d] = check::region_of(k.d[d].x, kn, "x");
+        rl[d] = check::region_of(k.d[d].lam, kn, "lambda");
+        ro[d] = check::region_of(k.d[d].out, kn, "out");
+        rz[d] = check::region_of(k.d[d].wts, kn, "weights");
+    }
+    int64_t bad = 0, n = 0;
+    auto fail = [&](const char* what, int64_t b, int tid, int t) {
+        if (bad++ < 4) check::violation(kn, what, "block %lld thread %d step %d", static_cast<long long>(b), tid, t);
+    };
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int dir;
+        int64_t idx;
+        scan4_block(k, b, dir, idx);
+        const ScanK& a = k.d[dir];
+        const int64_t pg = idx / a.nchunks;
+        const int q = static_cast<int>(idx - pg * a.nchunks);
+        const int S = a.S, L = a.L;
+        const int64_t plane = static_cast<int64_t>(S) * L;
+        const int t0 = q * a.K;
+        const int t1 = (t0 + a.K < S) ? t0 + a.K : S;
+        const bool rev = a.reverse != 0;
+        if (L % P != 0 || L < P) fail("line not whole vectors", b, -1, -1);
+        for (int g = 0; g < k.group; ++g) {
+            const LpMember m = lp_member(k, pg, g, per, g * per);
+            if (m.wave0 + m.nwaves > lp::kMaxWaves) fail("edge LDS", b, g * per, -1);
+            // the resources: the plane of x, lambda and out, the weight rows
+            const char* xb = static_cast<const char*>(a.x) + m.p * plane * static_cast<int64_t>(sizeof(T));
+            const char* lb = static_cast<const char*>(a.lam) + m.p * plane * static_cast<int64_t>(sizeof(T));
+            const char* ob = static_cast<const char*>(a.out) + m.p * plane * static_cast<int64_t>(sizeof(TO));
+            const char* zb = static_cast<const char*>(a.wts) + lp_weight_offset(a, m.p, plane, PAIR, ZB);
+            const int64_t nt = plane * static_cast<int64_t>(sizeof(T));
+            const int64_t no = plane * static_cast<int64_t>(sizeof(TO));
+            const int64_t nz = NZ * plane * ZB;
+            if (nt > 0x7fffffff || no > 0x7fffffff || nz > 0x7fffffff) fail("resource past 2^31 bytes", b, -1, -1);
+            if (!check::in_region(rx[dir], xb, 0, nt)) fail("x resource", b, -1, -1);
+            if (!check::in_region(rl[dir], lb, 0, nt)) fail("lambda resource", b, -1, -1);
+            if (!check::in_region(ro[dir], ob, 0, no)) fail("out resource", b, -1, -1);
+            if (!check::in_region(rz[dir], zb, 0, nz)) fail("weight resource", b, -1, -1);
+            const uint32_t rowT = static_cast<uint32_t>(L) * sizeof(T);
+            const uint32_t rowO = static_cast<uint32_t>(L) * sizeof(TO);
+            const uint32_t rowW = static_cast<uint32_t>(L) * ZB;
+            const uint32_t planeW = static_cast<uint32_t>(plane) * ZB;
+            for (int tid = g * per; tid < (g + 1) * per; ++tid) {
+                const LpMember mt = lp_member(k, pg, g, per, tid);
+                const LpLane ln = lp_lane(mt.tid, mt.valid, L, P, sizeof(T), ZB, sizeof(TO));
+                for (int t = t0; t < t1 + D; ++t) {
+                    const uint32_t i = lp_row(lp_fill_step(t, t1), S, rev);
+                    for (int v = 0; v < WT / 4; ++v) {
+                        const int64_t off = static_cast<int64_t>(ln.vt) + 16 * v + static_cast<int64_t>(i) * rowT;
+                        if (off + 16 > nt || !check::in_region(rx[dir], xb, off, 16)) fail("x load", b, tid, t);
+                        if (off + 16 > nt || !check::in_region(rl[dir], lb, off, 16)) fail("lambda load", b, tid, t);
+                    }
+                    for (int o = 0; o < NZ; ++o)
+                        for (int v = 0; v < WW / 4; ++v) {
+                            const int64_t off = static_cast<int64_t>(ln.vw) + 16 * v +
+                                                static_cast<int64_t>(o) * planeW + static_cast<int64_t>(i) * rowW;
+                            if (off + 16 > nz || !check::in_region(rz[dir], zb, off, 16)) fail("weight load", b, tid, t);
+                        }
+                    n += 2 * (WT / 4) + NZ * (WW / 4);
+                    if (ln.active && t < t1) {
+                        const uint32_t io = lp_row(t, S, rev);
+                        for (int v = 0; v < WO / 4; ++v) {
+                            const int64_t off = static_cast<int64_t>(ln.vo) + 16 * v + static_cast<int64_t>(io) * rowO;
+                            if (off + 16 > no || !check::in_region(ro[dir], ob, off, 16)) fail("store", b, tid, t);
+                        }
+                        n += WO / 4;
+                    }
+                }
+            }
+        }
+    }
+    if (bad) check::violation(kn, "accesses", "%lld bad", static_cast<long long>(bad));
+    check::count_accesses(n);
+    check::replayed(kn, lp::kMaxLanes, sizeof(float) * 2 * lp::kMaxWaves * 2);
+}
+#endif
 
 template <typename T, typename TW, bool LOGITS, typename TO = T>
 hipError_t launch_fused4lp(const Scan4K& k, int nthreads, hipStream_t stream) {
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
+#ifdef GSPN_CHECK_LAUNCHES
+    replay_fused4lp<T, TW, LOGITS, TO>(k, nthreads);
+#endif
     hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS, TO>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads), 0,
                        stream, k);
     return hipGetLastError();

@@ -25,7 +25,7 @@ struct TileIndex {
     int c0;  // first column of the tile in the source frame
 };
 
-__device__ __forceinline__ TileIndex tile_of(int64_t blk, int R, int Cc) {
+GSPN_HD TileIndex tile_of(int64_t blk, int R, int Cc) {
     const int tr = (R + kTile - 1) / kTile;
     const int tc = (Cc + kTile - 1) / kTile;
     const int64_t per_plane = static_cast<int64_t>(tr) * tc;
@@ -35,6 +35,38 @@ __device__ __forceinline__ TileIndex tile_of(int64_t blk, int R, int Cc) {
     t.r0 = static_cast<int>(r / tc) * kTile;
     t.c0 = static_cast<int>(r % tc) * kTile;
     return t;
+}
+
+// The global accesses of thread tid to one 64 x 64 tile of a (rows x cols)
+// plane: row r, column c of the tile is element (r0 + r, c0 + c) of the
+// plane.  For each tile row of the thread, 16 bytes along the row:
+//   fv(r, c, off)  one 16-byte vector, tile cells (r, c .. c + VW - 1), plane
+//                  elements off .. off + VW - 1 (vec: the plane's rows allow
+//                  16-byte accesses);
+//   fe(r, c, off)  otherwise each element inside the plane on its own;
+//   fn(r, c)       and each tile cell outside it.
+template <int VW, typename FV, typename FE, typename FN>
+GSPN_HD void tile_accesses(int tid, int rows, int cols, int r0, int c0, bool vec, FV&& fv, FE&& fe, FN&& fn) {
+    constexpr int LPR = kTile / VW;      // lanes per tile row
+    constexpr int RPP = kThreads / LPR;  // rows per pass
+    const int lr = tid / LPR;
+    const int lc = (tid % LPR) * VW;
+#pragma unroll
+    for (int i = 0; i < kTile / RPP; ++i) {
+        const int r = lr + i * RPP;
+        const int gr = r0 + r;
+        const int gc = c0 + lc;
+        const int64_t off = static_cast<int64_t>(gr) * cols + gc;
+        if (vec && gr < rows && gc + VW <= cols) {
+            fv(r, lc, off);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                if (gr < rows && gc + e < cols) fe(r, lc + e, off + e);
+                else fn(r, lc + e);
+            }
+        }
+    }
 }
 
 template <typename T>
@@ -80,54 +112,33 @@ __device__ __forceinline__ void vst(V* p, const V& v) {
 template <typename T>
 struct TileIO {
     static constexpr int VW = 16 / static_cast<int>(sizeof(T));  // elements per vector
-    static constexpr int LPR = kTile / VW;                        // lanes per tile row
-    static constexpr int RPP = kThreads / LPR;                    // rows per pass
 
     template <bool NT = false, typename F>
     static __device__ __forceinline__ void read(const T* plane, int rows, int cols, int r0, int c0, bool vec,
                                                 F&& put) {
-        const int lr = threadIdx.x / LPR;
-        const int lc = (threadIdx.x % LPR) * VW;
+        tile_accesses<VW>(
+            threadIdx.x, rows, cols, r0, c0, vec,
+            [&](int r, int c, int64_t off) {
+                const Vec16<T> v = vld<NT>(reinterpret_cast<const Vec16<T>*>(plane + off));
 #pragma unroll
-        for (int i = 0; i < kTile / RPP; ++i) {
-            const int r = lr + i * RPP;
-            const int gr = r0 + r;
-            const int gc = c0 + lc;
-            const T* src = plane + static_cast<int64_t>(gr) * cols + gc;
-            if (vec && gr < rows && gc + VW <= cols) {
-                const Vec16<T> v = vld<NT>(reinterpret_cast<const Vec16<T>*>(src));
-#pragma unroll
-                for (int e = 0; e < VW; ++e) put(r, lc + e, Store<T>::ld(&v.e[e]));
-            } else {
-#pragma unroll
-                for (int e = 0; e < VW; ++e)
-                    put(r, lc + e, (gr < rows && gc + e < cols) ? Store<T>::ld(src + e) : 0.0f);
-            }
-        }
+                for (int e = 0; e < VW; ++e) put(r, c + e, Store<T>::ld(&v.e[e]));
+            },
+            [&](int r, int c, int64_t off) { put(r, c, Store<T>::ld(plane + off)); },
+            [&](int r, int c) { put(r, c, 0.0f); });
     }
 
     template <bool NT = false, typename F>
     static __device__ __forceinline__ void write(T* plane, int rows, int cols, int r0, int c0, bool vec, F&& get) {
-        const int lr = threadIdx.x / LPR;
-        const int lc = (threadIdx.x % LPR) * VW;
-#pragma unroll
-        for (int i = 0; i < kTile / RPP; ++i) {
-            const int r = lr + i * RPP;
-            const int gr = r0 + r;
-            const int gc = c0 + lc;
-            if (gr >= rows) continue;
-            T* dst = plane + static_cast<int64_t>(gr) * cols + gc;
-            if (vec && gc + VW <= cols) {
+        tile_accesses<VW>(
+            threadIdx.x, rows, cols, r0, c0, vec,
+            [&](int r, int c, int64_t off) {
                 Vec16<T> v;
 #pragma unroll
-                for (int e = 0; e < VW; ++e) Store<T>::st(&v.e[e], get(r, lc + e, dst + e));
-                vst<NT>(reinterpret_cast<Vec16<T>*>(dst), v);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VW; ++e)
-                    if (gc + e < cols) Store<T>::st(dst + e, get(r, lc + e, dst + e));
-            }
-        }
+                for (int e = 0; e < VW; ++e) Store<T>::st(&v.e[e], get(r, c + e, plane + off + e));
+                vst<NT>(reinterpret_cast<Vec16<T>*>(plane + off), v);
+            },
+            [&](int r, int c, int64_t off) { Store<T>::st(plane + off, get(r, c, plane + off)); },
+            [&](int, int) {});
     }
 };
 
@@ -196,6 +207,86 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const TS* __res
                                                     [&](int r, int c, const T*) { return any ? tile[r][c] : 0.0f; });
 }
 
+#ifdef GSPN_CHECK_LAUNCHES
+// Host replay of one tile pass of every block over the planes at `base`
+// (R x Cc planes, or Cc x R when frame_t), as the kernels below call TileIO:
+// each access must lie in base's buffer, vectors on 16 bytes, and the LDS
+// cell inside the 64 x 64 tile.
+template <typename T>
+void replay_tiles(const char* kernel, const char* what, const void* base, int64_t nblocks, int R, int Cc,
+                  bool frame_t, bool vec) {
+    if (!base) return;
+    const check::Region reg = check::region_of(base, kernel, what);
+    constexpr int VW = TileIO<T>::VW;
+    const int64_t plane = static_cast<int64_t>(R) * Cc;
+    const int rows = frame_t ? Cc : R;
+    const int cols = frame_t ? R : Cc;
+    int64_t bad = 0, n = 0;
+    auto cell = [&](int r, int c) {
+        if (r < 0 || r >= kTile || c < 0 || c >= kTile) ++bad;
+    };
+    auto acc = [&](const T* pl, int64_t off, int64_t nb, bool vector) {
+        ++n;
+        const uint64_t a = reinterpret_cast<uint64_t>(pl + off);
+        if (!check::in_region(reg, pl, off * static_cast<int64_t>(sizeof(T)), nb) || (vector && a % 16 != 0)) {
+            if (bad++ == 0)
+                check::violation(kernel, what, "access of %lld bytes at %p outside [%p, %p) or misaligned",
+                                 static_cast<long long>(nb), reinterpret_cast<void*>(a),
+                                 reinterpret_cast<void*>(reg.lo), reinterpret_cast<void*>(reg.hi));
+        }
+    };
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const TileIndex ti = tile_of(b, R, Cc);
+        const T* pl = static_cast<const T*>(base) + ti.plane * plane;
+        for (int tid = 0; tid < kThreads; ++tid) {
+            tile_accesses<VW>(
+                tid, rows, cols, frame_t ? ti.c0 : ti.r0, frame_t ? ti.r0 : ti.c0, vec,
+                [&](int r, int c, int64_t off) {
+                    cell(r, c);
+                    cell(r, c + VW - 1);
+                    acc(pl, off, 16, true);
+                },
+                [&](int r, int c, int64_t off) {
+                    cell(r, c);
+                    acc(pl, off, sizeof(T), false);
+                },
+                [&](int r, int c) { cell(r, c); });
+        }
+    }
+    if (bad) check::violation(kernel, what, "%lld bad accesses", static_cast<long long>(bad));
+    check::count_accesses(n);
+}
+
+// The merge weights a combine block reads: merge[k * nch + plane % nch], k < 4.
+void replay_merge(const char* kernel, const float* merge, int64_t nch, int64_t nblocks, int R, int Cc) {
+    if (!merge) return;
+    const check::Region reg = check::region_of(merge, kernel, "merge");
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const int64_t ch = tile_of(b, R, Cc).plane % nch;
+        for (int k = 0; k < 4; ++k)
+            if (!check::in_region(reg, merge, (k * nch + ch) * 4, 4)) {
+                check::violation(kernel, "merge", "weight (%d, %lld) outside the buffer", k,
+                                 static_cast<long long>(ch));
+                return;
+            }
+    }
+}
+
+template <typename T, typename TS>
+void replay_combine(int64_t nblocks, const T* y, const TS* y0, const TS* a, const TS* z2, const TS* z3, int R,
+                    int Cc, int accumulate, int vec_y, int vec_s, int vec_z, const float* merge, int64_t nch) {
+    const char* k = "combine_kernel";
+    replay_merge(k, merge, nch, nblocks, R, Cc);
+    replay_tiles<TS>(k, "z2", z2, nblocks, R, Cc, true, vec_z);
+    replay_tiles<TS>(k, "z3", z3, nblocks, R, Cc, true, vec_z);
+    if (y0) replay_tiles<TS>(k, "y0", y0, nblocks, R, Cc, false, vec_s);
+    else if (accumulate) replay_tiles<T>(k, "y (read)", y, nblocks, R, Cc, false, vec_y);
+    replay_tiles<TS>(k, "a", a, nblocks, R, Cc, false, vec_s);
+    replay_tiles<T>(k, "y", y, nblocks, R, Cc, false, vec_y);
+    check::replayed(k, kThreads, sizeof(float) * kTile * (kTile + 1));
+}
+#endif
+
 int64_t tiles_for(int64_t planes, int R, int Cc) {
     return planes * ((R + kTile - 1) / kTile) * ((Cc + kTile - 1) / kTile);
 }
@@ -210,6 +301,16 @@ hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, i
     const int vw = dtype == kF32 ? 4 : 8;
     const int vs = (Cc % vw == 0) && aligned16(src);
     const int vd = (R % vw == 0) && aligned16(dst);
+#ifdef GSPN_CHECK_LAUNCHES
+    if (dtype == kF32) {
+        replay_tiles<float>("transpose_kernel", "src", src, grid.x, R, Cc, false, vs);
+        replay_tiles<float>("transpose_kernel", "dst", dst, grid.x, R, Cc, true, vd);
+    } else {
+        replay_tiles<bf16_t>("transpose_kernel", "src", src, grid.x, R, Cc, false, vs);
+        replay_tiles<bf16_t>("transpose_kernel", "dst", dst, grid.x, R, Cc, true, vd);
+    }
+    check::replayed("transpose_kernel", kThreads, sizeof(float) * kTile * (kTile + 1));
+#endif
     if (dtype == kF32) {
         hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kThreads), 0, stream,
                            static_cast<const float*>(src), static_cast<float*>(dst), R, Cc, vs, vd);
@@ -227,6 +328,17 @@ hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3
     const int vy = (Cc % vw == 0) && aligned16(y);
     const int vs = vy && (!a || aligned16(a));
     const int vz = (R % vw == 0) && (!z2 || aligned16(z2)) && (!z3 || aligned16(z3));
+#ifdef GSPN_CHECK_LAUNCHES
+    if (dtype == kF32) {
+        replay_combine<float, float>(grid.x, static_cast<const float*>(y), nullptr, static_cast<const float*>(a),
+                                     static_cast<const float*>(z2), static_cast<const float*>(z3), R, Cc, accumulate,
+                                     vs, vs, vz, merge, nch);
+    } else {
+        replay_combine<bf16_t, bf16_t>(grid.x, static_cast<const bf16_t*>(y), nullptr, static_cast<const bf16_t*>(a),
+                                       static_cast<const bf16_t*>(z2), static_cast<const bf16_t*>(z3), R, Cc,
+                                       accumulate, vs, vs, vz, merge, nch);
+    }
+#endif
     if (dtype == kF32) {
         hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
                            static_cast<const float*>(nullptr), static_cast<const float*>(a),
@@ -248,6 +360,15 @@ hipError_t launch_combine_states(void* y, const float* s0, const float* s1, cons
     const int vy = (Cc % (dtype == kF32 ? 4 : 8) == 0) && aligned16(y);
     const int vs = (Cc % 4 == 0) && aligned16(s0) && aligned16(s1);
     const int vz = (R % 4 == 0) && aligned16(s2) && aligned16(s3);
+#ifdef GSPN_CHECK_LAUNCHES
+    if (dtype == kF32) {
+        replay_combine<float, float>(grid.x, static_cast<const float*>(y), s0, s1, s2, s3, R, Cc, 0, vy, vs, vz,
+                                     merge, nch);
+    } else {
+        replay_combine<bf16_t, float>(grid.x, static_cast<const bf16_t*>(y), s0, s1, s2, s3, R, Cc, 0, vy, vs, vz,
+                                      merge, nch);
+    }
+#endif
     if (dtype == kF32) {
         hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
                            s0, s1, s2, s3, R, Cc, 0, vy, vs, vz, merge, nch);

@@ -594,7 +594,9 @@ def gspn4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.
     and (if given) the merge weights.  keep_states: the forward keeps its
     fp32 scans (16 bytes per element of x, held until the backward) so the
     backward need not recompute them; only for planes larger than 64 x 64
-    (smaller ones recompute them either way)."""
+    (for smaller ones the one-pass forward and the plane-resident backward,
+    which recomputes the states inside its launch, are faster than keeping
+    them)."""
     has_merge = merge is not None
     m = merge if has_merge else torch.empty(0, device=x.device)
     h, w = x.shape[-2:]

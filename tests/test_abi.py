@@ -129,7 +129,7 @@ def test_forward4_validation(lib):
     assert f(m=D_ + 8) == ALIAS                      # y overlaps the merge weights
     assert f(m=W + 16, ws=W, wsb=wsb) == ALIAS       # the workspace overlaps them
     S = 0x6a000000                                   # fp32 forward states, 4 maps of n*c*h*w
-    assert f(s=S, ws=W, wsb=wsb) == UNSUP            # not for planes of at most 64 x 64
+    assert f(s=S + 2, ws=W, wsb=wsb) == MISAL        # planes of at most 64 x 64 keep states too
     wsb = lib.gspn_forward4_workspace_bytes(1, 2, 8, 80, 2, 0, 0)
     f0 = f
 
@@ -310,7 +310,7 @@ def test_backward4_validation(lib):
     assert f(dm=WS + 8) == ALIAS                    # dmerge in the workspace
     assert f(m=dls[2] + 4) == ALIAS                 # an output on the merge weights
     S = 0x6a000000                                  # fp32 forward states, 4 maps of n*c*h*w
-    assert f(s=S) == UNSUP                          # not for planes of at most 64 x 64
+    assert f(s=S + 2) == MISAL                      # planes of at most 64 x 64 take states too
     need80 = lib.gspn_backward4_workspace_bytes(1, 2, 8, 80, 2, 0, 0)
     smaller = need80 - 16 * 2 * 8 * 80              # the states' room in the workspace is not needed
     assert f(w=80, wsb=smaller) == WSPACE           # without states it is

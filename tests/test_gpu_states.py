@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from linear_spatial_propagation_gspn_amd import gspn as G
-from linear_spatial_propagation_gspn_amd.workloads import Workload, make_inputs
+from linear_spatial_propagation_gspn_amd.workloads import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -109,15 +109,67 @@ def test_backward_from_states(dtype, shape, shared, chunk, merge):
         assert oracle.normwise_error(_np(a[1][d]), o[2][d]) <= TOL[dtype]
 
 
-def test_states_refused_for_plane_resident_sizes():
-    wl = Workload("case", 1, 2, 16, 24, "f32", False, 0, 91)
+SMALL = [
+    # planes of at most 64 x 64 leave their one-pass path when the states are kept
+    ("f32", (2, 3, 23, 41), False, 5),     # ragged lines: lanes past the end of every line
+    ("bf16", (1, 5, 40, 72), True, 0),     # channel groups of four in the adjoint, the last ragged
+    ("f32", (1, 2, 64, 64), False, 7),
+]
+
+
+@pytest.mark.parametrize("dtype,shape,shared,chunk", SMALL)
+def test_kept_states_on_small_planes(dtype, shape, shared, chunk):
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, dtype, shared, chunk, 501 + h + w)
+    _say("kept states, small planes %s %s shared=%s chunk=%d" % (shape, dtype, shared, chunk))
     inp = make_inputs(wl, DEV)
-    with pytest.raises(G.GspnError, match="UNSUPPORTED"):
-        G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], workspace=G.forward4_workspace(inp["x"], 2),
-                        states=True)
-    with pytest.raises(G.GspnError, match="UNSUPPORTED"):
-        G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], torch.randn_like(inp["x"]),
-                         states=G.states_buffer(inp["x"]))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(wl.seed + 3)
+    gy = torch.randn((n, c, h, w), generator=g, device=DEV, dtype=torch.float32).to(wl.torch_dtype)
+    y, st = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk,
+                            workspace=G.forward4_workspace(inp["x"], wl.cw), states=True)
+    dx, dz, dl = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=chunk, states=st)
+    torch.cuda.synchronize()
+    assert oracle.normwise_error(_np(y), oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk)) \
+        <= TOL[dtype]
+    o = oracle.backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk=chunk)
+    assert oracle.normwise_error(_np(dx), o[0]) <= TOL[dtype]
+    for d in range(4):
+        assert oracle.normwise_error(_np(dl[d]), o[1][d]) <= TOL[dtype]
+        assert oracle.normwise_error(_np(dz[d]), o[2][d]) <= TOL[dtype]
+
+
+def test_tstage_training_step_keeping_states():
+    """The 64 x 96 x 56 x 56 stage map, fp32: forward keeping its states, then
+    the backward from them with the binding's smaller workspace.  Lanes past
+    the end of a 56-position line once read their left neighbour's state
+    past the end of the states buffer here; the gradients are checked on
+    sampled planes that the oracle computes on their own."""
+    wl = WORKLOADS["tstage"]
+    _say("tstage training step keeping states")
+    inp = make_inputs(wl, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(41)
+    gy = torch.randn((wl.n, wl.c, wl.h, wl.w), generator=g, device=DEV, dtype=torch.float32)
+    y, st = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], workspace=G.forward4_workspace(inp["x"], wl.cw),
+                            states=True)
+    t = G.StageTimes()
+    dx, dz, dl = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, states=st, times=t)
+    torch.cuda.synchronize()
+    stages = t.as_dict()
+    assert stages["scan"]["launches"] == 0 and stages["adjoint"]["launches"] == 1
+    assert torch.isfinite(dx).all() and torch.isfinite(y).all()
+    for pn, pc in [(0, 0), (63, 95), (17, 40)]:
+        sl = (slice(pn, pn + 1), slice(pc, pc + 1))
+        zs = [z[sl] for z in inp["logits"]]
+        ls = [l[sl] for l in inp["lam"]]
+        assert oracle.normwise_error(_np(y[sl]), oracle.forward4(inp["x"][sl], zs, ls)) <= TOL["f32"]
+        o = oracle.backward4(inp["x"][sl], zs, ls, gy[sl])
+        errs = [oracle.normwise_error(_np(dx[sl]), o[0])]
+        for d in range(4):
+            errs += [oracle.normwise_error(_np(dl[d][sl]), o[1][d]), oracle.normwise_error(_np(dz[d][sl]), o[2][d])]
+        _say("  plane (%d, %d): worst normwise error %.3g" % (pn, pc, max(errs)))
+        assert max(errs) <= TOL["f32"]
 
 
 def test_backward_from_states_takes_the_smaller_workspace():

@@ -1,0 +1,215 @@
+"""Host-side replay of the library's launches (no GPU): libgspn_check.so is
+the library's host code built with GSPN_CHECK_LAUNCHES, in which each
+launcher replays its kernel's accesses block by block and thread by thread,
+with the index functions the kernel itself calls, and checks every access
+against the buffer that holds the pointer it goes through; the launch itself
+only records the kernel, grid, block and LDS size.
+
+The buffers are address ranges registered with the checker (nothing is
+allocated or touched), sized as the Python binding sizes them: its
+forward4_workspace, states_buffer and backward4_workspace(with_states=True)
+on meta tensors.
+
+The central case is the training step on the 64 x 96 x 56 x 56 stage map that
+keeps the forward's fp32 states for the backward, a configuration that once
+ended in a GPU memory fault.  Its replay showed the cause: lanes past the end
+of a line computed their left neighbour's state offset without clamping it
+into the line, and on the last row of the last plane of the last direction's
+map that read up to 7 floats past the states buffer (whose size there, 147 x
+2 MiB, leaves the allocator no slack).  The clamp is now in adj_left."""
+import ctypes
+import os
+
+import pytest
+import torch
+
+from linear_spatial_propagation_gspn_amd import build as hipbuild
+from linear_spatial_propagation_gspn_amd import gspn as G
+
+
+_vp4 = ctypes.c_void_p * 4
+_i64 = ctypes.c_int64
+
+
+@pytest.fixture(scope="module")
+def chk():
+    src = os.path.join(hipbuild.CSRC)
+    newest = max(os.path.getmtime(os.path.join(src, f)) for f in os.listdir(src))
+    if not os.path.exists(hipbuild.CHECK_LIB) or os.path.getmtime(hipbuild.CHECK_LIB) < newest:
+        hipbuild.build_check()
+    lib = ctypes.CDLL(hipbuild.CHECK_LIB)
+    lib.gspn_check_add_buffer.argtypes = [ctypes.c_char_p, ctypes.c_uint64, ctypes.c_uint64]
+    lib.gspn_check_violations.restype = _i64
+    lib.gspn_check_accesses.restype = _i64
+    lib.gspn_check_launches.restype = _i64
+    lib.gspn_check_report.restype = _i64
+    lib.gspn_check_report.argtypes = [ctypes.c_char_p, _i64]
+    for f in ("gspn_forward4", "gspn_backward4", "gspn_forward4_noalloc"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+def report(lib) -> str:
+    n = lib.gspn_check_report(None, 0)
+    buf = ctypes.create_string_buffer(int(n) + 1)
+    lib.gspn_check_report(buf, n + 1)
+    return buf.value.decode()
+
+
+class Space:
+    """Disjoint address ranges registered as buffers, 2^36 bytes apart (so an
+    overrun lands in no buffer) and 256-byte aligned."""
+
+    def __init__(self, lib):
+        self.lib = lib
+        self.next = 1 << 44
+        lib.gspn_check_reset()
+
+    def buf(self, name: str, nbytes: int) -> int:
+        assert 0 < nbytes < (1 << 36)
+        base = self.next
+        self.next += 1 << 36
+        assert self.lib.gspn_check_add_buffer(name.encode(), base, nbytes) == 0
+        return base
+
+
+def _meta(n, c, h, w, dtype):
+    return torch.empty((n, c, h, w), dtype=dtype, device="meta")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def training_step(lib, n, c, h, w, dtype=torch.float32, shared=False, chunk=0, merge=False, layout="scan",
+                  keep_states=True, short_states=0):
+    """Forward keeping the states, then the backward from them, through the
+    check library's C ABI; returns the two status codes."""
+    sp = Space(lib)
+    x = _meta(n, c, h, w, dtype)
+    es = x.element_size()
+    cw = 1 if shared else c
+    dt = G._dtype_code(x)
+    lc = G._layout_code(layout)
+    xb = n * c * h * w * es
+    zb = n * cw * 3 * h * w * es
+    px = sp.buf("x", xb)
+    pz = [sp.buf("logits%d" % d, zb) for d in range(4)]
+    pl = [sp.buf("lambda%d" % d, xb) for d in range(4)]
+    py = sp.buf("y", xb)
+    pm = sp.buf("merge", 4 * c * 4) if merge else None
+    ps = sp.buf("states", _nbytes(G.states_buffer(x)) - short_states) if keep_states else None
+    fws = G.forward4_workspace(x, cw, layout=layout)
+    pw = sp.buf("forward workspace", _nbytes(fws))
+    rf = lib.gspn_forward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(cw), _i64(chunk), ctypes.c_void_p(px),
+                           _vp4(*pz), _vp4(*pl), ctypes.c_void_p(pm), ctypes.c_void_p(py), ctypes.c_void_p(ps),
+                           ctypes.c_void_p(pw), _i64(_nbytes(fws)), dt, lc, None)
+    pg = sp.buf("dL/dy", xb)
+    pdx = sp.buf("dx", xb)
+    pdz = [sp.buf("dlogits%d" % d, zb) for d in range(4)]
+    pdl = [sp.buf("dlambda%d" % d, xb) for d in range(4)]
+    pdm = sp.buf("dmerge", 4 * c * 4) if merge else None
+    bws = G.backward4_workspace(x, cw, with_states=keep_states, layout=layout)
+    pb = sp.buf("backward workspace", _nbytes(bws))
+    rb = lib.gspn_backward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(cw), _i64(chunk), ctypes.c_void_p(px),
+                            _vp4(*pz), _vp4(*pl), ctypes.c_void_p(pm), ctypes.c_void_p(ps), ctypes.c_void_p(pg),
+                            ctypes.c_void_p(pdx), _vp4(*pdz), _vp4(*pdl), ctypes.c_void_p(pdm), ctypes.c_void_p(pb),
+                            _i64(_nbytes(bws)), dt, lc, None)
+    return rf, rb
+
+
+def _kernels(text: str) -> list:
+    return [line.split()[1] for line in text.splitlines() if line.startswith("launch ")]
+
+
+def test_tstage_training_step_with_kept_states(chk):
+    """The step that faulted: 64 x 96 x 56 x 56, fp32, per-channel logits,
+    forward keeping its states, backward from them with the binding's
+    shrunken workspace.  Every access of every launch stays in its buffer."""
+    rf, rb = training_step(chk, 64, 96, 56, 56)
+    text = report(chk)
+    print(text)
+    assert (rf, rb) == (0, 0), text
+    assert _kernels(text) == [
+        "transpose_kernel<float>", "(scan4lp_kernel<T,", "(combine_kernel<float,",      # forward
+        "transpose_kernel<float>", "transpose_kernel<float>", "(adj4_kernel<float,", "(combine_kernel<float,",
+    ], text
+    assert chk.gspn_check_violations() == 0, text
+    # every position of the four directions, every step: far more than 10^9 accesses
+    assert chk.gspn_check_accesses() > 10 ** 9
+
+
+@pytest.mark.parametrize("case", [
+    dict(n=2, c=3, h=23, w=41, chunk=5),                          # ragged lines, element tiles
+    dict(n=1, c=5, h=40, w=72, dtype=torch.bfloat16, shared=True),  # channel groups of four, the last ragged
+    dict(n=1, c=2, h=64, w=64, merge=True, chunk=7),
+    dict(n=1, c=3, h=56, w=56, layout="array"),
+])
+def test_small_plane_steps_with_kept_states(chk, case):
+    case = dict(case)
+    rf, rb = training_step(chk, case.pop("n"), case.pop("c"), case.pop("h"), case.pop("w"), **case)
+    text = report(chk)
+    assert (rf, rb) == (0, 0), text
+    assert chk.gspn_check_violations() == 0, text
+
+
+@pytest.mark.parametrize("case", [
+    dict(n=1, c=2, h=200, w=130, chunk=9),
+    dict(n=1, c=9, h=64, w=128, dtype=torch.bfloat16, shared=True),
+    dict(n=1, c=2, h=72, w=1500),                                 # two positions per lane in the adjoint
+])
+def test_long_line_steps(chk, case):
+    """Steps of planes above 64 x 64 (kept states are supported there)."""
+    case = dict(case)
+    rf, rb = training_step(chk, case.pop("n"), case.pop("c"), case.pop("h"), case.pop("w"), **case)
+    text = report(chk)
+    assert (rf, rb) == (0, 0), text
+    assert chk.gspn_check_violations() == 0, text
+
+
+def test_checker_sees_an_overrun(chk):
+    """A states buffer one float short: the replay of the forward's scan (its
+    last plane's store) and of the backward's adjoint must report it."""
+    rf, rb = training_step(chk, 2, 3, 40, 48, short_states=4)
+    text = report(chk)
+    assert (rf, rb) == (0, 0)
+    assert chk.gspn_check_violations() > 0
+    assert "scan4lp_kernel" in text and "adj4_kernel" in text
+
+
+def test_unreplayed_launch_is_reported(chk):
+    """The plane-resident forward has no host replay: its launch is reported
+    rather than passed over."""
+    sp = Space(chk)
+    n, c, h, w = 1, 2, 16, 16
+    xb = n * c * h * w * 4
+    px = sp.buf("x", xb)
+    pz = [sp.buf("logits%d" % d, 3 * xb) for d in range(4)]
+    pl = [sp.buf("lambda%d" % d, xb) for d in range(4)]
+    py = sp.buf("y", xb)
+    r = chk.gspn_forward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(c), _i64(0), ctypes.c_void_p(px), _vp4(*pz),
+                          _vp4(*pl), None, ctypes.c_void_p(py), None, None, _i64(0), 0, 0, None)
+    assert r == 0
+    assert chk.gspn_check_violations() == 1
+    assert "plane4_kernel" in report(chk) and "without a host replay" in report(chk)
+
+
+def test_allocation_free_forward_stays_in_its_scratch(chk):
+    """gspn_forward4_noalloc works in the library's static scratch array; the
+    checking build stands an address range in for it, registered here at the
+    array's size: the transposes, scans and merge stay inside it."""
+    sp = Space(chk)
+    assert chk.gspn_check_add_buffer(b"scratch", 0x7E << 40, 64 << 20) == 0
+    n, c, h, w = 1, 3, 200, 130
+    xb = n * c * h * w * 4
+    px = sp.buf("x", xb)
+    pz = [sp.buf("logits%d" % d, 3 * xb) for d in range(4)]
+    pl = [sp.buf("lambda%d" % d, xb) for d in range(4)]
+    py = sp.buf("y", xb)
+    for layout in (0, 1):
+        r = chk.gspn_forward4_noalloc(_i64(n), _i64(c), _i64(h), _i64(w), _i64(c), _i64(9), ctypes.c_void_p(px),
+                                      _vp4(*pz), _vp4(*pl), None, ctypes.c_void_p(py), None, 0, layout, None)
+        assert r == 0
+    text = report(chk)
+    assert chk.gspn_check_violations() == 0, text
+    assert "scan4v_kernel" in text and "combine_kernel" in text
