@@ -115,7 +115,7 @@ struct PixVec<8> {
     }
 };
 
-template <int PX>
+template <int PX, int NS>
 __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(const bf16_t* __restrict__ in,
                                                                               const bf16_t* __restrict__ wt,
                                                                               bf16_t* __restrict__ out, int64_t waves,
@@ -170,16 +170,33 @@ __global__ __launch_bounds__(GSPN_PROJ_THREADS) void project_narrow_out_mfma(con
         }
     };
 
-    Block b0, b1;
-    fetch(0, b0);
-    int k0 = 0;
-    for (; k0 + 32 < cin; k0 += 64) {
-        fetch(k0 + 32, b1);
-        consume(b0);
-        fetch(k0 + 64, b0);  // past c_in it reads clamped channels and yields zeros
-        consume(b1);
+    if constexpr (NS > 0) {
+        // cin <= 32 NS, the block count known here: the loop unrolls into one
+        // straight sequence, in which every MFMA waits only for its own block
+        // (a loop's back edge makes the compiler wait for every load in
+        // flight at its head)
+        Block b[2];
+        fetch(0, b[0]);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (i + 1 < NS) fetch(32 * (i + 1), b[(i + 1) & 1]);
+            // keep the next block's loads ahead of this block's wait (the
+            // scheduler would otherwise sink them below it)
+            __builtin_amdgcn_sched_barrier(0);
+            consume(b[i & 1]);
+        }
+    } else {
+        Block b0, b1;
+        fetch(0, b0);
+        int k0 = 0;
+        for (; k0 + 32 < cin; k0 += 64) {
+            fetch(k0 + 32, b1);
+            consume(b0);
+            fetch(k0 + 64, b0);  // past c_in it reads clamped channels and yields zeros
+            consume(b1);
+        }
+        if (k0 < cin) consume(b0);
     }
-    if (k0 < cin) consume(b0);
 
     // lane holds output rows (l/16)*4 + i for pixels px0 + PX q + j
     bf16_t* dst = out + ni * cout * hw + px0 + PX * q;
@@ -323,15 +340,27 @@ hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, co
             constexpr int per = GSPN_PROJ_THREADS / 64;
             const int64_t w2 = n * (hw / (16 * PX));
             const dim3 g2(static_cast<unsigned>((w2 + per - 1) / per));
-            hipLaunchKernelGGL(project_narrow_out_mfma<PX>, g2, dim3(GSPN_PROJ_THREADS), 0, stream,
-                               static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
-                               static_cast<bf16_t*>(out), w2, hw, static_cast<int>(c_in), static_cast<int>(c_out));
+            const auto* src = static_cast<const bf16_t*>(in);
+            const auto* wts = static_cast<const bf16_t*>(weight);
+            auto* dst = static_cast<bf16_t*>(out);
+            const int ci = static_cast<int>(c_in), co = static_cast<int>(c_out);
+            switch ((c_in + 31) / 32) {  // unrolled instances for up to 512 input channels
+#define GSPN_PROJ_NS(k) \
+    case k: hipLaunchKernelGGL((project_narrow_out_mfma<PX, k>), g2, dim3(GSPN_PROJ_THREADS), 0, stream, src, wts, dst, w2, hw, ci, co); break;
+                GSPN_PROJ_NS(1) GSPN_PROJ_NS(2) GSPN_PROJ_NS(3) GSPN_PROJ_NS(4) GSPN_PROJ_NS(5) GSPN_PROJ_NS(6)
+                GSPN_PROJ_NS(7) GSPN_PROJ_NS(8) GSPN_PROJ_NS(9) GSPN_PROJ_NS(10) GSPN_PROJ_NS(11) GSPN_PROJ_NS(12)
+                GSPN_PROJ_NS(13) GSPN_PROJ_NS(14) GSPN_PROJ_NS(15) GSPN_PROJ_NS(16)
+#undef GSPN_PROJ_NS
+                default:
+                    hipLaunchKernelGGL((project_narrow_out_mfma<PX, 0>), g2, dim3(GSPN_PROJ_THREADS), 0, stream, src,
+                                       wts, dst, w2, hw, ci, co);
+            }
             return hipGetLastError();
         }
         if (c_out <= 16 && c_in % 8 == 0 && aligned_to(in, 8) && aligned_to(out, 8) && aligned_to(weight, 16)) {
             constexpr int per = GSPN_PROJ_THREADS / 64;
             const dim3 g2(static_cast<unsigned>((waves + per - 1) / per));
-            hipLaunchKernelGGL(project_narrow_out_mfma<4>, g2, dim3(GSPN_PROJ_THREADS), 0, stream,
+            hipLaunchKernelGGL((project_narrow_out_mfma<4, 0>), g2, dim3(GSPN_PROJ_THREADS), 0, stream,
                                static_cast<const bf16_t*>(in), static_cast<const bf16_t*>(weight),
                                static_cast<bf16_t*>(out), waves, hw, static_cast<int>(c_in),
                                static_cast<int>(c_out));

@@ -194,7 +194,7 @@ def test_merge4():
 
 @pytest.mark.parametrize("hw", [(13, 29), (16, 32), (8, 24)])   # ragged (VALU) / 128 or 64 pixels per wave (MFMA, bf16)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("cin,cout", [(320, 8), (8, 320), (37, 5), (3, 11), (40, 16), (64, 17), (5, 33)])
+@pytest.mark.parametrize("cin,cout", [(320, 8), (8, 320), (37, 5), (3, 11), (40, 16), (64, 17), (5, 33), (520, 8)])
 def test_project(cin, cout, dtype, hw):
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     g = torch.Generator(device=DEV).manual_seed(cin * 1000 + cout)
