@@ -102,6 +102,14 @@ def scan_algorithmic_bytes(wl) -> int:
     return u + 4 * u + z + u
 
 
+def seq4_launch_planes(wl, cus: int, tail_ran: bool) -> int:
+    """The planes the plane-sequential launch processes: all n * c, or,
+    when the library ran the last, at most half-full round of one plane per
+    CU on the concurrent path (the "tail" stage), all but those."""
+    planes = wl.n * wl.c_scan
+    return planes - planes % cus if tail_ran and cus > 0 else planes
+
+
 def launch_algorithmic_bytes(wl, launches: int) -> int:
     """The algorithmic bytes of the units one scan launch processes: the
     scan's compulsory bytes divided over the launches that carry it (one
@@ -119,6 +127,8 @@ def scan_launch_bytes(wl, kernel: str, launches: int = 1) -> int:
       scan4band_kernel (one launch per band of steps): the long-line
         kernel's bytes spread over the bands (the band-boundary states, a few
         MB, are not counted);
+      seq4_kernel (one launch, the planes in turn): x four times, the
+        lambdas and weights once, the scratch map z 4U, y 3U;
       scan_kernel (one launch per direction): x (or its transpose), the
         direction's weights and lambda, the output written, and read as well
         by the two launches that add into a map (average over the four)."""
@@ -126,6 +136,11 @@ def scan_launch_bytes(wl, kernel: str, launches: int = 1) -> int:
     if kernel == "plane4_kernel":
         return u + 4 * wl.n * wl.cw * 3 * wl.h * wl.w * esize(wl) + 4 * u + u
     wd = weight_bytes_per_direction(wl)
+    if kernel == "seq4_kernel":
+        # x read in each of the four phases, each lambda and weight stream
+        # once, the transposed scratch z written, read and written, read
+        # (4U), y written, read and written (3U)
+        return 4 * u + 4 * u + 4 * wd + 4 * u + 3 * u
     if kernel in ("scan4v_kernel", "scan4lp_kernel"):
         return 2 * u + 4 * wd + 4 * u + 4 * u
     if kernel == "scan4band_kernel":
@@ -222,8 +237,9 @@ KERNEL_SOURCES = {
     "plane4_kernel": ["plane4.hip", "plane_common.hpp"],
     "adj4_kernel": ["backward.hip"],
     "adjplane_kernel": ["adjplane.hip", "plane_common.hpp"],
+    "seq4_kernel": ["seq4.hip"],
 }
-_COMMON = ["device.hpp"]
+_COMMON = ["device.hpp", "check.hpp"]
 
 
 def kernel_sources_digest(kernel: str | None = None) -> str:
@@ -647,6 +663,12 @@ def main():
     kernel_ms = scan["ms"] / launches
     bpl = launch_algorithmic_bytes(wl, launches)
     design = scan_launch_bytes(wl, kernel, launches)
+    if kernel == "seq4_kernel" and st["tail"]["launches"]:
+        # the launch covers all but the tail's planes
+        planes = wl.n * wl.c_scan
+        run = seq4_launch_planes(wl, torch.cuda.get_device_properties(0).multi_processor_count, True)
+        bpl = bpl * run // planes
+        design = design * run // planes
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
     tag = "" if lay == "scan" else "_array"
     traffic, traffic_src = counter_traffic(kernel, wl) if lay == "scan" else (None, "scan layout only")

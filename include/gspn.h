@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 8
+#define GSPN_ABI_VERSION 9
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -395,7 +395,10 @@ typedef enum {
     GSPN_STAGE_REDUCE = 7,       /* backward: clearing / storing the shared-logit sums, clearing dmerge */
     GSPN_STAGE_LAYOUT = 8,       /* GSPN_LAYOUT_ARRAY: horizontal logits / lambdas (and their gradients)
                                     copied between the array and scan frames */
-    GSPN_NUM_STAGES = 9
+    GSPN_STAGE_TAIL = 9,         /* GSPN_SCAN_SEQUENTIAL: the planes of a last, at most half-full round
+                                    of one plane per CU, run on the concurrent four-direction path
+                                    (every launch of that forward, timed as one) */
+    GSPN_NUM_STAGES = 10
 } gspn_stage;
 
 /* Which scan kernel a forward call ran (gspn_stage_times.scan_kernel). */

@@ -560,12 +560,50 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         bool vec = aligned(x, 16) && aligned(y, 16);
         for (int d = 0; d < 4; ++d) vec = vec && aligned(p[d].wts, 16) && aligned(p[d].lam, 16);
         if (vec) {
-            if (tm) tm->scan_kernel = GSPN_SCAN_SEQUENTIAL;
+            // With one workgroup per CU, planes run in rounds of one per CU,
+            // each a chain of four whole scans.  A last round at most half
+            // full would cost a whole round's time for half its work, so
+            // those planes (when they lie in one image and no merge weights
+            // are in play) go to the concurrent four-direction path instead,
+            // which spreads each plane over four workgroups.
+            const int64_t planes = n * c;
+            const int64_t cus = gspn::device_compute_units();
+            const int64_t tail = cus > 0 ? planes % cus : 0;
+            const bool split = planes > cus && tail > 0 && 2 * tail <= cus && !merge &&
+                               (planes - tail) / c == (planes - 1) / c;
+            const int64_t run = split ? planes - tail : planes;
             const void* wts[4] = {p[0].wts, p[1].wts, p[2].wts, p[3].wts};
-            return from_hip(timed(tm, GSPN_STAGE_SCAN, [&] {
-                return gspn::launch_seq4(x, wts, lam, merge, y, xt, n, c, cw, h, w, chunks, dtype, p[0].wdtype,
-                                         p[0].wts_are_logits, st);
-            }));
+            if (timed(tm, GSPN_STAGE_SCAN, [&] {
+                    return gspn::launch_seq4(x, wts, lam, merge, y, xt, n, c, cw, h, w, chunks, dtype, p[0].wdtype,
+                                             p[0].wts_are_logits, run, st);
+                }) != hipSuccess)
+                return GSPN_ERR_HIP;
+            if (split) {
+                // the tail: channels c0 .. c - 1 of image n0, a forward of
+                // its own in the scan frame (the logits and lambdas there
+                // already), in the workspace after the launch above is done
+                // with it (same stream)
+                const int64_t n0 = run / c, c0 = run % c;
+                const int64_t plane_b = h * w * static_cast<int64_t>(es);
+                const void* tz[4];
+                const void* tl[4];
+                for (int d = 0; d < 4; ++d) {
+                    tz[d] = static_cast<const char*>(logits[d]) + (n0 * cw + (cw == 1 ? 0 : c0)) * 3 * plane_b;
+                    tl[d] = static_cast<const char*>(lam[d]) + run * plane_b;
+                }
+                gspn_status sub = GSPN_OK;
+                const hipError_t e = timed(tm, GSPN_STAGE_TAIL, [&] {
+                    sub = forward4_impl(1, tail, h, w, cw == 1 ? 1 : tail, chunk_len,
+                                        static_cast<const char*>(x) + run * plane_b, tz, tl, nullptr,
+                                        static_cast<char*>(y) + run * plane_b, nullptr, workspace, workspace_bytes,
+                                        dtype, GSPN_LAYOUT_SCAN, stream, nullptr, false);
+                    return sub == GSPN_OK ? hipSuccess : hipErrorLaunchFailure;
+                });
+                if (sub != GSPN_OK) return sub;
+                if (e != hipSuccess) return GSPN_ERR_HIP;
+            }
+            if (tm) tm->scan_kernel = GSPN_SCAN_SEQUENTIAL;
+            return GSPN_OK;
         }
     }
 

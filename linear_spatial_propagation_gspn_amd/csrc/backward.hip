@@ -44,8 +44,17 @@ constexpr int adj_depth() { return (P == 1 && G == 1) ? 4 : 2; }
 // per lane: register budget; with the learnable merge's extra state the
 // four-channel groups spill a few registers, and still measured faster than
 // groups of two)
+#ifndef GSPN_ADJ_G1
+#define GSPN_ADJ_G1 4
+#endif
+#ifndef GSPN_ADJ_G2
+#define GSPN_ADJ_G2 2
+#endif
+#ifndef GSPN_ADJ_P
+#define GSPN_ADJ_P 1
+#endif
 template <int P>
-constexpr int shared_group() { return P == 1 ? 4 : 2; }
+constexpr int shared_group() { return P == 1 ? GSPN_ADJ_G1 : GSPN_ADJ_G2; }
 
 struct AdjK {
     const void* x;    // [planes][S][L] (x, or x transposed for horizontal)
@@ -566,7 +575,7 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, Adjo
         maxL = p[d].L > maxL ? static_cast<int>(p[d].L) : maxL;
         merge = merge || p[d].mscale || p[d].dmerge;
     }
-    const int P = maxL <= 1024 ? 1 : 2;  // lines of at most 2048 positions
+    const int P = maxL <= 1024 ? (shared ? GSPN_ADJ_P : 1) : 2;  // lines of at most 2048 positions
     const int G = !shared ? 1 : (P == 1 ? shared_group<1>() : shared_group<2>());
     for (int d = 0; d < 4; ++d) {
         AdjK& a = k.d[d];

@@ -33,6 +33,8 @@
 #include <type_traits>
 #include <utility>
 
+#include <atomic>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -522,13 +524,31 @@ hipError_t launch_seq4_t(const Seq4K& k, int64_t planes, hipStream_t stream) {
 
 }  // namespace
 
+int device_compute_units() {
+#ifdef GSPN_CHECK_LAUNCHES
+    return 256;
+#else
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cus[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 0) v = 0;
+        cus[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+#endif
+}
+
 bool seq4_supported(int64_t h, int64_t w) {
     return h >= 64 && w >= 64 && h <= kLanes * kP && w <= kLanes * kP && h % 64 == 0 && w % 64 == 0;
 }
 
 hipError_t launch_seq4(const void* x, const void* const wts[4], const void* const lam[4], const float* merge,
                        void* y, void* z, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w,
-                       const int64_t chunk[4], int dtype, int wdtype, int wts_are_logits, hipStream_t stream) {
+                       const int64_t chunk[4], int dtype, int wdtype, int wts_are_logits, int64_t run,
+                       hipStream_t stream) {
     Seq4K k;
     k.planes = n * c;
     k.x = x;
@@ -544,7 +564,7 @@ hipError_t launch_seq4(const void* x, const void* const wts[4], const void* cons
     k.cw = cw;
     k.H = static_cast<int>(h);
     k.W = static_cast<int>(w);
-    const int64_t planes = n * c;
+    const int64_t planes = run < n * c ? run : n * c;
     if (dtype == kF32) {
         if (wts_are_logits) return launch_seq4_t<float, float, true, 4>(k, planes, stream);
         return launch_seq4_t<float, float, false, 4>(k, planes, stream);  // channel-shared, normalised once

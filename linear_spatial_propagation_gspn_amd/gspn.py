@@ -47,7 +47,8 @@ EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # gspn_stage, in order.
-STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up", "adjoint", "reduce", "layout")
+STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up", "adjoint", "reduce", "layout",
+          "tail")
 
 
 # gspn_scan_kernel, in order.

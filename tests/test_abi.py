@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 8
+    assert lib.gspn_abi_version() == 9
     for code in range(13):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])

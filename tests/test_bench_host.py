@@ -45,6 +45,12 @@ def test_scan_launch_bytes():
     # channel-shared bf16 weights reach the scan as packed half pairs, 4 bytes a position
     uw = 1152 * 1024 * 1024 * 2
     assert bench.scan_launch_bytes(WORKLOADS["wide"], "scan4lp_kernel") == 10 * uw + 4 * 1024 * 1024 * 4
+    # plane-sequential kernel on the wide workload: x four times, lambdas and
+    # half-pair weights once, z 4U, y 3U
+    assert bench.scan_launch_bytes(WORKLOADS["wide"], "seq4_kernel") == 15 * uw + 4 * 1024 * 1024 * 4
+    # 1152 planes on 256 CUs: the last 128 go to the concurrent path
+    assert bench.seq4_launch_planes(WORKLOADS["wide"], 256, True) == 1024
+    assert bench.seq4_launch_planes(WORKLOADS["wide"], 256, False) == 1152
     # banded scan of the 8 proxy planes: the same launch's bytes over its 16 bands
     up = 8 * 2048 * 2048 * 2
     assert bench.scan_launch_bytes(WORKLOADS["proxy"], "scan4band_kernel", 16) == \

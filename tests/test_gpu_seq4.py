@@ -2,8 +2,10 @@
 for many big planes (at least 256 (n, c) planes, sides multiples of 64 up to
 1024) one workgroup per plane runs L2R, R2L, T2B and B2T in turn and builds
 y in place, the horizontal directions reading x through LDS column tiles.
-Every element is compared with the fp64 oracle (normwise, 1e-5 for fp32
-storage, 2e-2 for bf16), and the call must report that kernel."""
+A last round of planes at most half full (one plane per CU) goes to the
+concurrent four-direction path instead.  Every element is compared with the
+fp64 oracle (normwise, 1e-5 for fp32 storage, 2e-2 for bf16), and the call
+must report that kernel."""
 import sys
 
 import pytest
@@ -39,7 +41,17 @@ CASES = [
     ((1, 256, 128, 192), "bf16", False),  # per-channel bf16 logits normalised in the scan
     ((2, 128, 128, 64), "f32", False),    # per-channel fp32 logits
     ((1, 256, 192, 128), "f32", True),    # shared fp32 logits over 256 channels (fp32 weight triples)
+    ((1, 300, 64, 128), "bf16", True),    # 256 + 44 planes: the last 44 on the concurrent path (no merge)
+    ((2, 150, 64, 128), "f32", False),    # the same for per-channel logits, the 44 in the second image
 ]
+
+CUS = 256  # compute units of the MI355X
+
+
+def _tail_split(n, c, merge):
+    planes = n * c
+    tail = planes % CUS
+    return planes > CUS and 0 < tail and 2 * tail <= CUS and not merge and (planes - tail) // c == (planes - 1) // c
 
 
 @pytest.mark.parametrize("merge", [False, True])
@@ -60,7 +72,11 @@ def test_seq4_matches_oracle(shape, dtype, shared, chunk, merge):
                                      workspace=G.forward4_workspace(inp["x"], wl.cw), merge=m)
     torch.cuda.synchronize()
     assert times["scan_kernel"] == "seq4_kernel", times["scan_kernel"]
-    assert times["transpose"]["launches"] == 0 and times["combine"]["launches"] == 0
+    # a last round of planes at most half full runs on the concurrent path,
+    # timed as one stage
+    assert times["transpose"]["launches"] == 0 and times["combine"]["launches"] == 0, times
+    assert times["scan"]["launches"] == 1
+    assert times["tail"]["launches"] == (1 if _tail_split(n, c, merge) else 0), times
     ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk, merge=None if m is None else _np(m))
     assert oracle.normwise_error(_np(y), ref) <= TOL[dtype]
 
