@@ -91,11 +91,12 @@ def test_seq4_deterministic():
     assert torch.equal(a, b)
 
 
-def test_seq4_array_layout_and_noalloc():
+@pytest.mark.parametrize("c", [256, 300])   # 300: the last 44 planes on the concurrent path
+def test_seq4_array_layout_and_noalloc(c):
     """The array layout (horizontal tensors copied into their scan frame
     first) and the allocation-free entry point reach the same kernel and the
     same bits."""
-    wl = Workload("case", 1, 256, 64, 128, "bf16", True, 0, 6)
+    wl = Workload("case", 1, c, 64, 128, "bf16", True, 0, 6)
     inp = make_inputs(wl, DEV)
     ys = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], workspace=G.forward4_workspace(inp["x"], wl.cw))
     za = [z if d < 2 else z.transpose(-1, -2).contiguous() for d, z in enumerate(inp["logits"])]
@@ -105,4 +106,5 @@ def test_seq4_array_layout_and_noalloc():
     yn = G.gspn_forward4_noalloc(inp["x"], inp["logits"], inp["lam"])
     torch.cuda.synchronize()
     assert times["scan_kernel"] == "seq4_kernel"
+    assert times["tail"]["launches"] == (1 if _tail_split(1, c, False) else 0)
     assert torch.equal(ya, ys) and torch.equal(yn, ys)
