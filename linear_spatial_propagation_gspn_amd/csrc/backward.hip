@@ -238,7 +238,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 rg[s][g][j] = ld_once<T, NT>(gp + go + lo + kk[j]);
-                rx[s][g][j] = Store<T>::ld(xp + go + lo + kk[j]);
+                rx[s][g][j] = ld_once<T, NT>(xp + go + lo + kk[j]);
                 rl[s][g][j] = ld_once<T, NT>(lp + go + lo + kk[j]);
                 rh[s][g][j + 1] = hp[go + hlo + kk[j]];
             }
