@@ -213,3 +213,39 @@ def test_allocation_free_forward_stays_in_its_scratch(chk):
     text = report(chk)
     assert chk.gspn_check_violations() == 0, text
     assert "scan4v_kernel" in text and "combine_kernel" in text
+
+
+def _random_cases(seed: int, count: int):
+    """Random shapes for the replayed paths: planes above 64 x 64 in one
+    dimension, lines up to 2048 (so the four-direction kernels run), mixed
+    dtypes, chunk lengths, shared logits, merge weights and layouts."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    while len(out) < count:
+        h = rng.choice([1, 2, 3, 7, 17, 33, 64, 65, 96, 130, 257, 520, 1025, 2048])
+        w = rng.choice([1, 5, 31, 63, 65, 100, 128, 333, 1000, 1023, 1536, 2048])
+        if h <= 64 and w <= 64:
+            continue
+        n = rng.choice([1, 2])
+        c = rng.choice([1, 2, 3, 5, 9])
+        if n * c * h * w > 3_000_000:
+            continue
+        out.append(dict(n=n, c=c, h=h, w=w, dtype=rng.choice([torch.float32, torch.bfloat16]),
+                        shared=rng.random() < 0.4, chunk=rng.choice([0, 0, 1, 3, 8, 100]),
+                        merge=rng.random() < 0.3, layout=rng.choice(["scan", "scan", "array"]),
+                        keep_states=rng.random() < 0.7))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(2026, 24), ids=lambda c: "%dx%dx%dx%d" % (c["n"], c["c"], c["h"], c["w"]))
+def test_random_shapes_stay_in_bounds(chk, case):
+    """Random shapes: forward (keeping the states or not) and backward,
+    every replayed launch in bounds.  Launches without a replay (the banded
+    scan of very few long lines) are allowed here and reported, not failed."""
+    case = dict(case)
+    rf, rb = training_step(chk, case.pop("n"), case.pop("c"), case.pop("h"), case.pop("w"), **case)
+    text = report(chk)
+    assert (rf, rb) == (0, 0), text
+    bad = [l for l in text.splitlines() if l.startswith("violation") and "without a host replay" not in l]
+    assert not bad, text
