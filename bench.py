@@ -110,6 +110,19 @@ def seq4_launch_planes(wl, cus: int, tail_ran: bool) -> int:
     return planes - planes % cus if tail_ran and cus > 0 else planes
 
 
+def projection_bytes(wl, down: bool) -> int:
+    """Compulsory bytes of one 1x1 projection of the proxy pipeline: the
+    input read once, the output written once, the weights read once (down:
+    C -> C_proxy, up: C_proxy -> C)."""
+    es = esize(wl)
+    hw = wl.h * wl.w
+    return wl.n * (wl.c + wl.c_proxy) * hw * es + wl.c * wl.c_proxy * es
+
+
+# The projection kernels the proxy workload runs (bf16 MFMA paths).
+PROJECTION_KERNELS = {"project_down": "project_narrow_out_mfma", "project_up": "project_narrow_in_mfma"}
+
+
 def launch_algorithmic_bytes(wl, launches: int) -> int:
     """The algorithmic bytes of the units one scan launch processes: the
     scan's compulsory bytes divided over the launches that carry it (one
@@ -238,6 +251,8 @@ KERNEL_SOURCES = {
     "adj4_kernel": ["backward.hip"],
     "adjplane_kernel": ["adjplane.hip", "plane_common.hpp"],
     "seq4_kernel": ["seq4.hip"],
+    "project_narrow_out_mfma": ["project.hip"],
+    "project_narrow_in_mfma": ["project.hip"],
 }
 _COMMON = ["device.hpp", "check.hpp"]
 
@@ -669,6 +684,21 @@ def main():
         run = seq4_launch_planes(wl, torch.cuda.get_device_properties(0).multi_processor_count, True)
         bpl = bpl * run // planes
         design = design * run // planes
+    scan_roofline = None
+    if wl.c_proxy:
+        # the dominant kernel is the stage that takes longest: in the proxy
+        # pipeline a projection (one launch each); the scan's figures are
+        # kept beside it
+        scan_achieved = bpl / (kernel_ms * 1e-3) / 1e9
+        scan_roofline = {"kernel": kernel, "kernel_ms": round(kernel_ms, 4), "launches_per_step": launches,
+                         "bytes_per_launch": bpl, "achieved": round(scan_achieved, 1),
+                         "frac": round(scan_achieved / HBM_PEAK_GBPS, 4), "design_bytes_per_launch": design}
+        stage = max(("project_down", "project_up", "scan"), key=lambda k: st[k]["ms"])
+        if stage != "scan":
+            kernel = PROJECTION_KERNELS[stage]
+            launches = st[stage]["launches"]
+            kernel_ms = st[stage]["ms"] / launches
+            bpl = design = projection_bytes(wl, stage == "project_down")
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
     tag = "" if lay == "scan" else "_array"
     traffic, traffic_src = counter_traffic(kernel, wl) if lay == "scan" else (None, "scan layout only")
@@ -721,6 +751,8 @@ def main():
                      "step_traffic": step_traffic, "step_traffic_source": step_src},
         "cpu_baseline": cpu,
     }
+    if scan_roofline is not None:
+        rec["scan_roofline"] = scan_roofline
     print(json.dumps(rec))
 
 

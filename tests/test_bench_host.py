@@ -124,6 +124,14 @@ def test_scan_algorithmic_bytes_are_the_compulsory_bytes():
     assert bench.launch_algorithmic_bytes(WORKLOADS["profile"], 1) == 9663676416
 
 
+def test_projection_bytes():
+    # proxy: 320 -> 8 channels over 2048^2 bf16 pixels, and the weights
+    px = 2048 * 2048
+    assert bench.projection_bytes(WORKLOADS["proxy"], True) == (320 + 8) * px * 2 + 320 * 8 * 2
+    assert bench.projection_bytes(WORKLOADS["proxy"], False) == bench.projection_bytes(WORKLOADS["proxy"], True)
+    assert set(bench.PROJECTION_KERNELS.values()) <= set(bench.KERNEL_SOURCES)
+
+
 def test_host_cpu_fields():
     info = bench.host_cpu()
     assert set(info) == {"cpu_model", "nproc", "cpu_count"}
