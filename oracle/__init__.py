@@ -282,6 +282,36 @@ def backward4(x, logits: Sequence, lams: Sequence, gy, chunk: int = 0, merge=Non
     return dx, dls, dzs
 
 
+def proxy_backward4(x, w_down, w_up, logits: Sequence, lams: Sequence, gy, chunk: int = 0, merge=None):
+    """Gradient of proxy_forward4 for dL/dy = gy, by the chain rule through
+    its three stages (GSPN-2 notes, "Optimisation 2": x_p = W_down x,
+    y_p = forward4(x_p), y = W_up y_p, all 1x1 projections without bias):
+      dL/dy_p  = W_up^T gy                  (a projection with W_up^T)
+      dx_p, dlam_d, dlogits_d (, dmerge) = backward4 in proxy space for dL/dy_p
+      dx       = W_down^T dx_p               (a projection with W_down^T)
+      dW_up[c][k]   = sum over images and pixels of gy[c] * y_p[k]
+      dW_down[k][c] = sum over images and pixels of dx_p[k] * x[c]
+    Returns (dx, dW_down [C_proxy][C], dW_up [C][C_proxy], [dlam_d],
+    [dlogits_d]) and, with ``merge``, dmerge [4][C_proxy] last."""
+    xx = _f64(x)
+    wd = _f64(w_down)
+    wu = _f64(w_up)
+    gg = _f64(gy)
+    if gg.shape != xx.shape:
+        raise ValueError("gy does not fit x")
+    xp = project(xx, wd)
+    yp = forward4(xp, logits, lams, chunk, merge=merge)
+    gp = project(gg, wu.T)
+    res = backward4(xp, logits, lams, gp, chunk, merge=merge)
+    dxp = res[0]
+    dx = project(dxp, wd.T)
+    dwu = np.einsum("ncp,nkp->ck", gg.reshape(gg.shape[0], gg.shape[1], -1), yp.reshape(yp.shape[0], yp.shape[1], -1))
+    dwd = np.einsum("nkp,ncp->kc", dxp.reshape(dxp.shape[0], dxp.shape[1], -1),
+                    xx.reshape(xx.shape[0], xx.shape[1], -1))
+    out = (dx, dwd, dwu, res[1], res[2])
+    return out + (res[3],) if merge is not None else out
+
+
 def max_threads() -> int:
     """Threads the oracle's OpenMP loops may use (OMP_NUM_THREADS, else all
     cores)."""
