@@ -7,7 +7,8 @@ L->R, R->L, merge by summation, or with --merge by seeded learnable weights
 per direction and channel) over one batch of seeded synthetic inputs already
 resident in HBM; for the proxy workload a step is the compressive proxy
 pipeline (1x1 projection down, forward4 in proxy space, 1x1 projection up).
---pass backward times gspn_backward4 instead.  Prints one JSON line.
+--pass backward times gspn_backward4 instead (gspn_proxy_backward4 for the
+proxy workload).  Prints one JSON line.
 
 Measurements:
   - ms per step: HIP events on the stream the library launches on, bracketing
@@ -170,6 +171,29 @@ def backward_algorithmic_bytes(wl) -> int:
     return 2 * u + z + 4 * u + u + 4 * u + z
 
 
+def proxy_backward_bytes(wl) -> int:
+    """Compulsory bytes of the compressive-proxy backward: x and dL/dy read
+    and dx written (C channels); in proxy space the logits and lambdas read
+    and their gradients written; both projection weights read and their fp32
+    gradients written."""
+    es = esize(wl)
+    hw = wl.h * wl.w
+    big = wl.n * wl.c * hw * es
+    lam = 4 * wl.n * wl.c_proxy * hw * es
+    z = 4 * wl.n * wl.cw * 3 * hw * es
+    return 3 * big + 2 * lam + 2 * z + 2 * wl.c * wl.c_proxy * es + 2 * wl.c * wl.c_proxy * 4
+
+
+def wgrad_pass_bytes(wl) -> int:
+    """Compulsory bytes of one weight-gradient pass of the proxy backward,
+    the average of the two: over dL/dy (C channels) and y_p read, dL/dy_p
+    written; over x (C channels) and dx_p read."""
+    hw = wl.h * wl.w
+    big = wl.n * wl.c * hw * esize(wl)
+    small = wl.n * wl.c_proxy * hw * esize(wl)
+    return (2 * big + 3 * small) // 2
+
+
 def adjoint_launch_bytes(wl) -> int:
     """Algorithmic bytes of the adjoint launch: x and dL/dy in both frames,
     four lambdas and logits, four fp32 state maps read; four dlambda and dx
@@ -253,6 +277,7 @@ KERNEL_SOURCES = {
     "seq4_kernel": ["seq4.hip"],
     "project_narrow_out_mfma": ["project.hip"],
     "project_narrow_in_mfma": ["project.hip"],
+    "wgrad_mfma": ["wgrad.hip"],
 }
 _COMMON = ["device.hpp", "check.hpp"]
 
@@ -470,6 +495,120 @@ def per_step_ms(step, n: int) -> list:
     return sorted(a.elapsed_time(b) for a, b in ev)
 
 
+def cpu_baseline_proxy_backward(wl, inp, gy, oracle, merge=None) -> dict:
+    """The oracle's compressive-proxy backward on the workload's top-left
+    crop of 1/16 of its pixels (every channel; the cost of each stage is
+    linear in the pixel count), repeated until CPU_TARGET_S, scaled to the
+    whole plane."""
+    hs, ws_ = max(1, wl.h // 4), max(1, wl.w // 4)
+    x = _np64(inp["x"][:, :, :hs, :ws_])
+    g = _np64(gy[:, :, :hs, :ws_])
+    zs = [_np64(z[..., :hs, :ws_] if d < 2 else z[..., :ws_, :hs]) for d, z in enumerate(inp["logits"])]
+    ls = [_np64(l[..., :hs, :ws_] if d < 2 else l[..., :ws_, :hs]) for d, l in enumerate(inp["lam"])]
+    wd, wu = _np64(inp["w_down"]), _np64(inp["w_up"])
+    m = None if merge is None else _np64(merge)
+    reps, spent = 0, 0.0
+    while reps < CPU_MAX_REPEATS and (reps == 0 or spent < CPU_TARGET_S):
+        t = time.perf_counter()
+        oracle.proxy_backward4(x, wd, wu, zs, ls, g, chunk=wl.chunk, merge=m)
+        spent += time.perf_counter() - t
+        reps += 1
+    scale = (wl.h * wl.w) / (hs * ws_)
+    return {"value": round(spent / reps * 1e3 * scale, 3), "unit": "ms per proxy backward (extrapolated)",
+            "cores": oracle.max_threads(), "kind": "oracle", **host_cpu(),
+            "sample": "the %dx%d top-left crop (all %d channels, %d proxy channels), fp64 chain-rule backward "
+                      "(projections, four-direction forward and backward in proxy space, weight gradients), "
+                      "scaled by the pixel ratio %.0f; %d runs, %.1f s of oracle time"
+                      % (hs, ws_, wl.c, wl.c_proxy, scale, reps, spent)}
+
+
+def bench_proxy_backward(args, wl):
+    """The backward leg of the compressive-proxy workload:
+    gspn_proxy_backward4 for a seeded dL/dy ~ N(0, 1).  The dominant kernel
+    is the stage that takes longest (the weight-gradient passes, two
+    launches, at full size)."""
+    torch.cuda.init()
+    G.lib()
+    print("bench: proxy backward, workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
+    lay = args.layout
+    inp = make_inputs(wl, "cuda")
+    tin = array_layout(inp) if lay == "array" else inp
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 1000)
+    gy = torch.randn(inp["x"].shape, generator=g, device="cuda", dtype=torch.float32).to(wl.torch_dtype)
+    ws = G.proxy_backward4_workspace(inp["x"], wl.c_proxy, wl.cw, lay)
+    merge = merge_weights(wl, args.merge)
+
+    def step(times=None):
+        return G.gspn_proxy_backward4(tin["x"], tin["w_down"], tin["w_up"], tin["logits"], tin["lam"], gy,
+                                      chunk_len=wl.chunk, workspace=ws, times=times, merge=merge, layout=lay)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    print("bench: proxy backward %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    singles = per_step_ms(step, args.steps)
+    reps = max(3, min(args.steps, 10))
+    acc = {name: [0.0, 0] for name in G.STAGES}
+    for _ in range(reps):
+        t = G.StageTimes()
+        step(times=t)
+        for name, v in t.as_dict().items():
+            if name in acc:
+                acc[name][0] += v["ms"] / reps
+                acc[name][1] = v["launches"]
+    stage = max(("weight_grad", "project_down", "project_up"), key=lambda k: acc[k][0])
+    launches = acc[stage][1]
+    kernel_ms = acc[stage][0] / launches
+    if stage == "weight_grad":
+        kernel, bpl = "wgrad_mfma", wgrad_pass_bytes(wl)
+        slots = min(2048, wl.n * wl.h * wl.w // 128)
+        design = bpl + slots * wl.c * wl.c_proxy * 4      # plus each pass's fp32 partial sums
+    else:
+        kernel = PROJECTION_KERNELS[stage]
+        bpl = design = projection_bytes(wl, stage == "project_down")
+    achieved = bpl / (kernel_ms * 1e-3) / 1e9
+    alg = proxy_backward_bytes(wl)
+    eff = alg / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle's proxy backward on a sample", file=sys.stderr, flush=True)
+        import oracle
+        cpu = cpu_baseline_proxy_backward(wl, inp, gy, oracle, merge)
+    traffic, traffic_src = counter_traffic(kernel, wl) if lay == "scan" else (None, "scan layout only")
+    step_traffic, step_src = step_counter_traffic(wl, "_backward" + ("" if lay == "scan" else "_array"))
+    rec = {
+        "metric": "ms per compressive-proxy GSPN backward (dx, dw_down, dw_up, dlambda, dlogits%s); achieved "
+                  "HBM GB/s" % (", dmerge" if args.merge else ""),
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded)",
+        "config": {"workload": wl.name, "pass": "backward", "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
+                   "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk, "c_proxy": wl.c_proxy,
+                   "merge": "learnable" if args.merge else "sum", "layout": lay},
+        "ms_median": round(singles[len(singles) // 2], 4), "ms_min": round(singles[0], 4),
+        "effective_GBps": round(eff, 1), "effective_frac": round(eff / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
+        "stages_ms": {k: round(v[0], 4) for k, v in acc.items() if v[1]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
+                     "kernel_ms": round(kernel_ms, 4), "launches_per_step": launches, "bytes_per_launch": bpl,
+                     "traffic_source": traffic_src, "design_bytes_per_launch": design,
+                     "design_achieved": round(design / (kernel_ms * 1e-3) / 1e9, 1),
+                     "step_traffic": step_traffic, "step_traffic_source": step_src},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+
+
 def bench_backward(args, wl):
     """The backward leg: gspn_backward4 over the same inputs and a seeded
     dL/dy ~ N(0, 1); the dominant kernel is the adjoint launch.  With
@@ -477,8 +616,11 @@ def bench_backward(args, wl):
     its fp32 states, then gspn_backward4 from those states (no recompute)."""
     train = args.pass_ == "train"
     if wl.c_proxy:
-        print("bench.py: the backward pass covers gspn_forward4 (no proxy projections)", file=sys.stderr)
-        sys.exit(2)
+        if train:
+            print("bench.py: --pass train covers gspn_forward4 (the proxy has --pass backward)", file=sys.stderr)
+            sys.exit(2)
+        bench_proxy_backward(args, wl)
+        return
     if train and wl.h <= 64 and wl.w <= 64:
         print("bench.py: the forward keeps its states only for planes larger than 64 x 64", file=sys.stderr)
         sys.exit(2)

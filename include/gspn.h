@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 9
+#define GSPN_ABI_VERSION 10
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -369,6 +369,49 @@ gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
                            int layout, void* stream);
 
 /*
+ * gspn_proxy_backward4_workspace_bytes -- bytes of the gspn_proxy_backward4
+ * workspace: four proxy-space maps (n*c_proxy*h*w elements of the storage
+ * type each), both projection weights transposed, the weight-gradient
+ * partial sums (at most 2048 * c * c_proxy floats), and the larger of
+ * gspn_forward4_workspace_bytes and gspn_backward4_workspace_bytes for
+ * (n, c_proxy, h, w, cw), each part rounded up to 256 bytes.  Returns -1 for
+ * invalid arguments (c < 1 or c_proxy < 1 among them).
+ */
+int64_t gspn_proxy_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
+                                             int64_t cw, int dtype, int layout);
+
+/*
+ * gspn_proxy_backward4 -- gradients of gspn_proxy_forward4 (same x, w_down,
+ * w_up, logits, lam, merge, cw, chunk_len, layout) for dL/dy = gy, by the
+ * chain rule through its three stages (GSPN-2 notes, "Optimisation 2"):
+ *   dL/dy_p   = w_up^T gy                          (a 1x1 projection C -> C_proxy)
+ *   dx_p, dlogits, dlam, dmerge = gspn_backward4 in proxy space for dL/dy_p,
+ *               at x_p = w_down x
+ *   dx        = w_down^T dx_p                       [n][c][h][w]   (written)
+ *   dw_up     [c][c_proxy] fp32   = sum over images and pixels of gy[c] y_p[k]
+ *   dw_down   [c_proxy][c] fp32   = sum over images and pixels of dx_p[k] x[c]
+ *   dlogits[d], dlam[d], dmerge   as gspn_backward4 gives them in proxy space
+ *               (dmerge optional: NULL skips it)
+ * x_p and y_p = forward4(x_p) are recomputed inside (stored in the storage
+ * type, as the forward stores them; every intermediate rounds once at its
+ * store).  The weight gradients are summed in fp32 over at most 2048 runs
+ * of pixels, then the runs in a fixed order: they do not vary between calls.
+ * With no pixels (n*h*w == 0) dw_down, dw_up and dmerge are written as
+ * zeros and nothing else is touched (the other pointers may then be NULL).
+ * c < 1 or c_proxy < 1 is GSPN_ERR_BAD_SHAPE.  Pointers, alignment (the storage type's size; 4 bytes
+ * for the fp32 arrays and the workspace) and aliasing as in gspn_backward4:
+ * outputs may overlap neither an input, the workspace nor each other.  The
+ * proxy-space propagation must meet gspn_backward4's limits (else
+ * GSPN_ERR_UNSUPPORTED, before anything is queued).
+ */
+gspn_status gspn_proxy_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                 const void* const logits[4], const void* const lam[4], const float* merge,
+                                 const void* gy, void* dx, float* dw_down, float* dw_up, void* const dlogits[4],
+                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
+                                 int dtype, int layout, void* stream);
+
+/*
  * Stage timing of one forward call (measurement only).
  *
  * gspn_forward4_timed / gspn_proxy_forward4_timed take the arguments of
@@ -392,13 +435,17 @@ typedef enum {
     GSPN_STAGE_COMBINE = 4,      /* transposing merge of the partial maps into y */
     GSPN_STAGE_PROJECT_UP = 5,   /* 1x1 projection C_proxy -> C */
     GSPN_STAGE_ADJOINT = 6,      /* backward: the adjoint line-scan launch */
-    GSPN_STAGE_REDUCE = 7,       /* backward: clearing / storing the shared-logit sums, clearing dmerge */
+    GSPN_STAGE_REDUCE = 7,       /* backward: clearing / storing the shared-logit sums, clearing dmerge;
+                                    proxy backward also: the projection weights transposed, the weight-
+                                    gradient partial sums reduced */
     GSPN_STAGE_LAYOUT = 8,       /* GSPN_LAYOUT_ARRAY: horizontal logits / lambdas (and their gradients)
                                     copied between the array and scan frames */
     GSPN_STAGE_TAIL = 9,         /* GSPN_SCAN_SEQUENTIAL: the planes of a last, at most half-full round
                                     of one plane per CU, run on the concurrent four-direction path
                                     (every launch of that forward, timed as one) */
-    GSPN_NUM_STAGES = 10
+    GSPN_STAGE_WEIGHT_GRAD = 10, /* proxy backward: the two passes that sum the weight gradients' partials,
+                                    over gy (with dL/dy_p = w_up^T gy folded in) and over x */
+    GSPN_NUM_STAGES = 11
 } gspn_stage;
 
 /* Which scan kernel a forward call ran (gspn_stage_times.scan_kernel). */
@@ -456,6 +503,19 @@ gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int
                                  void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
                                  int64_t workspace_bytes, int dtype, int layout, void* stream,
                                  gspn_stage_times* times);
+
+/* gspn_proxy_backward4 with stage timing (same contract as gspn_forward4_timed);
+ * the stages of the proxy-space forward and backward it runs are reported as
+ * theirs, x's projection as GSPN_STAGE_PROJECT_DOWN, dx's as
+ * GSPN_STAGE_PROJECT_UP, the passes over gy and x that sum the weight
+ * gradients' partials as GSPN_STAGE_WEIGHT_GRAD. */
+gspn_status gspn_proxy_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                       int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                       const void* const logits[4], const void* const lam[4], const float* merge,
+                                       const void* gy, void* dx, float* dw_down, float* dw_up,
+                                       void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                                       int64_t workspace_bytes, int dtype, int layout, void* stream,
+                                       gspn_stage_times* times);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* gspn_status_string(int status);

@@ -59,7 +59,7 @@ gspn_status from_hip(hipError_t e) { return e == hipSuccess ? GSPN_OK : GSPN_ERR
 // Optional event timing of the launches of one forward call: a pair of HIP
 // events around each launch, read back by finish().
 struct Timer {
-    static constexpr int kMax = 64;
+    static constexpr int kMax = 128;
     hipStream_t st = nullptr;
     int count = 0;
     int stage[kMax] = {};
@@ -1014,6 +1014,172 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     return copy_out();
 }
 
+// Workspace of the proxy backward: x_p, y_p, dL/dy_p and dx_p in the storage
+// type, the two weights transposed, the weight-gradient partial sums, then
+// the larger of the proxy-space forward and backward workspaces (used one
+// after the other); every part starts on a 256-byte boundary.
+struct ProxyBwdLayout {
+    int64_t xp, yp, gp, dxp, wtu, wtd, part, inner, inner_bytes, total;
+};
+
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+bool proxy_bwd_layout(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw, int dtype,
+                      int layout, ProxyBwdLayout* L) {
+    if (!valid_dtype(dtype) || !valid_layout(layout) || !dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w}) ||
+        c < 1 || c_proxy < 1 || !(cw == 1 || cw == c_proxy))
+        return false;
+    const int64_t es = static_cast<int64_t>(elem_size(dtype));
+    const int64_t pb = round256(checked_product({n, c_proxy, h, w}) * es);
+    const int64_t mb = round256(checked_product({c, c_proxy}) * es);
+    const int64_t f4 = gspn_forward4_workspace_bytes(n, c_proxy, h, w, cw, dtype, layout);
+    const int64_t b4 = gspn_backward4_workspace_bytes(n, c_proxy, h, w, cw, dtype, layout);
+    if (pb < 0 || mb < 0 || f4 < 0 || b4 < 0) return false;
+    L->xp = 0;
+    L->yp = pb;
+    L->gp = 2 * pb;
+    L->dxp = 3 * pb;
+    L->wtu = 4 * pb;
+    L->wtd = L->wtu + mb;
+    L->part = L->wtd + mb;
+    L->inner = L->part + round256(gspn::wgrad_slots(n, h * w) * c * c_proxy * 4);
+    L->inner_bytes = f4 > b4 ? f4 : b4;
+    L->total = L->inner + L->inner_bytes;
+    return true;
+}
+
+gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                const void* const logits[4], const void* const lam[4], const float* merge,
+                                const void* gy, void* dx, float* dw_down, float* dw_up, void* const dlogits[4],
+                                void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
+                                int dtype, int layout, void* stream, Timer* tm) {
+    if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
+    if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
+    if (!dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w}) || c < 1 || c_proxy < 1) return GSPN_ERR_BAD_SHAPE;
+    if (chunk_len < 0) return GSPN_ERR_BAD_CHUNK;
+    if (!(cw == 1 || cw == c_proxy)) return GSPN_ERR_BAD_WEIGHT_CHANNELS;
+    if (h > GSPN_MAX_LINE || w > GSPN_MAX_LINE) return GSPN_ERR_UNSUPPORTED;
+    const hipStream_t st = as_stream(stream);
+    if (!dw_down || !dw_up) return GSPN_ERR_NULL_POINTER;
+    if (checked_product({n, h, w}) == 0) {
+        // no pixels: the sums over them are zero, every other output is empty
+        const int64_t gb = c * c_proxy * 4;
+        if (!aligned(dw_down, 4) || !aligned(dw_up, 4) || (dmerge && !aligned(dmerge, 4)))
+            return GSPN_ERR_MISALIGNED;
+        if (overlap(dw_down, gb, dw_up, gb) || (dmerge && (overlap(dmerge, 4 * c_proxy * 4, dw_down, gb) ||
+                                                            overlap(dmerge, 4 * c_proxy * 4, dw_up, gb))))
+            return GSPN_ERR_ALIASING;
+        if (timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(dw_down, c * c_proxy, st); }) !=
+                hipSuccess ||
+            timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(dw_up, c * c_proxy, st); }) !=
+                hipSuccess)
+            return GSPN_ERR_HIP;
+        if (dmerge && timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(dmerge, 4 * c_proxy, st); }) !=
+                          hipSuccess)
+            return GSPN_ERR_HIP;
+        return GSPN_OK;
+    }
+    if (!x || !w_down || !w_up || !gy || !dx || !logits || !lam || !dlogits || !dlam || !workspace)
+        return GSPN_ERR_NULL_POINTER;
+    for (int d = 0; d < 4; ++d)
+        if (!logits[d] || !lam[d] || !dlogits[d] || !dlam[d]) return GSPN_ERR_NULL_POINTER;
+    ProxyBwdLayout L;
+    if (!proxy_bwd_layout(n, c, h, w, c_proxy, cw, dtype, layout, &L)) return GSPN_ERR_BAD_SHAPE;
+    if (workspace_bytes < L.total) return GSPN_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return GSPN_ERR_MISALIGNED;
+    const size_t es = elem_size(dtype);
+    const int64_t xb = n * c * h * w * static_cast<int64_t>(es);
+    const int64_t pb = n * c_proxy * h * w * static_cast<int64_t>(es);
+    const int64_t wb = n * cw * 3 * h * w * static_cast<int64_t>(es);
+    const int64_t mb = c * c_proxy * static_cast<int64_t>(es);
+    const int64_t gb = c * c_proxy * 4;  // a weight gradient, fp32
+    const int64_t mgb = 4 * c_proxy * 4;
+    const int64_t need = L.total;
+    // inputs and outputs: alignment, then no output may overlap an input,
+    // the workspace or another output, and the workspace no input
+    const void* outs[12] = {dx, dw_down, dw_up, dlogits[0], dlogits[1], dlogits[2], dlogits[3],
+                            dlam[0], dlam[1], dlam[2], dlam[3], dmerge};
+    const int64_t ob[12] = {xb, gb, gb, wb, wb, wb, wb, pb, pb, pb, pb, mgb};
+    const size_t oa[12] = {es, 4, 4, es, es, es, es, es, es, es, es, 4};
+    const void* all_in[13] = {x, w_down, w_up, gy, logits[0], logits[1], logits[2], logits[3],
+                              lam[0], lam[1], lam[2], lam[3], merge};
+    const int64_t ib[13] = {xb, mb, mb, xb, wb, wb, wb, wb, pb, pb, pb, pb, mgb};
+    const size_t ia[13] = {es, es, es, es, es, es, es, es, es, es, es, es, 4};
+    for (int i = 0; i < 12; ++i)
+        if (outs[i] && !aligned(outs[i], oa[i])) return GSPN_ERR_MISALIGNED;
+    for (int j = 0; j < 13; ++j)
+        if (all_in[j] && !aligned(all_in[j], ia[j])) return GSPN_ERR_MISALIGNED;
+    for (int i = 0; i < 12; ++i) {
+        if (!outs[i]) continue;
+        if (overlap(outs[i], ob[i], workspace, need)) return GSPN_ERR_ALIASING;
+        for (int j = 0; j < 13; ++j)
+            if (all_in[j] && overlap(outs[i], ob[i], all_in[j], ib[j])) return GSPN_ERR_ALIASING;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] && overlap(outs[i], ob[i], outs[j], ob[j])) return GSPN_ERR_ALIASING;
+    }
+    for (int j = 0; j < 13; ++j)
+        if (all_in[j] && overlap(workspace, need, all_in[j], ib[j])) return GSPN_ERR_ALIASING;
+    const int64_t hw = h * w;
+    // the proxy-space backward's limits, checked before anything is queued
+    int64_t chunks[4];
+    for (int d = 0; d < 4; ++d) {
+        bool empty = false;
+        const ScanCheck ck = check_scan(d, chunk_len, n, c_proxy, h, w, cw, dtype, &empty);
+        if (ck.st != GSPN_OK) return ck.st;
+        chunks[d] = ck.chunk;
+    }
+    if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c_proxy, h, w, chunks)) return GSPN_ERR_UNSUPPORTED;
+    char* ws = static_cast<char*>(workspace);
+    void* xp = ws + L.xp;
+    void* yp = ws + L.yp;
+    void* gp = ws + L.gp;
+    void* dxp = ws + L.dxp;
+    void* wtu = ws + L.wtu;  // w_up^T [c_proxy][c]
+    void* wtd = ws + L.wtd;  // w_down^T [c][c_proxy]
+    float* part = reinterpret_cast<float*>(ws + L.part);
+    void* inner = ws + L.inner;
+    // the weights transposed, for the projections the chain rule needs
+    if (timed(tm, GSPN_STAGE_REDUCE, [&] {
+            return gspn::launch_transpose(w_up, wtu, 1, static_cast<int>(c), static_cast<int>(c_proxy), dtype, st);
+        }) != hipSuccess ||
+        timed(tm, GSPN_STAGE_REDUCE, [&] {
+            return gspn::launch_transpose(w_down, wtd, 1, static_cast<int>(c_proxy), static_cast<int>(c), dtype, st);
+        }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    // the forward's proxy-space input and output, recomputed
+    if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
+              [&] { return gspn::launch_project(n, c, hw, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    gspn_status s = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, nullptr, inner,
+                                  L.inner_bytes, dtype, layout, stream, tm);
+    if (s != GSPN_OK) return s;
+    // dL/dy_p = w_up^T gy, and in the same pass over gy the partial sums of
+    // dL/dw_up[c][k] = sum gy[c] y_p[k]
+    int64_t slots = 0;
+    if (timed(tm, GSPN_STAGE_WEIGHT_GRAD, [&] {
+            return gspn::launch_project_wgrad(n, c, hw, c_proxy, gy, yp, wtu, gp, part, dtype, st, &slots);
+        }) != hipSuccess ||
+        timed(tm, GSPN_STAGE_REDUCE,
+              [&] { return gspn::launch_wgrad_reduce(part, slots, c, c_proxy, dw_up, c_proxy, 1, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    // the propagation's gradients in proxy space
+    s = backward_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, nullptr, gp, dxp, dlogits, dlam,
+                      dmerge, inner, L.inner_bytes, dtype, layout, stream, tm);
+    if (s != GSPN_OK) return s;
+    // dx = w_down^T dx_p; dL/dw_down[k][c] = sum dx_p[k] x[c]
+    if (timed(tm, GSPN_STAGE_PROJECT_UP,
+              [&] { return gspn::launch_project(n, c_proxy, hw, c, dxp, wtd, dx, dtype, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    if (timed(tm, GSPN_STAGE_WEIGHT_GRAD, [&] {
+            return gspn::launch_project_wgrad(n, c, hw, c_proxy, x, dxp, nullptr, nullptr, part, dtype, st, &slots);
+        }) != hipSuccess ||
+        timed(tm, GSPN_STAGE_REDUCE,
+              [&] { return gspn::launch_wgrad_reduce(part, slots, c, c_proxy, dw_down, 1, c, st); }) != hipSuccess)
+        return GSPN_ERR_HIP;
+    return GSPN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1121,6 +1287,40 @@ gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int
     tm.st = as_stream(stream);
     const gspn_status s = backward_impl(n, c, h, w, cw, chunk_len, x, logits, lam, merge, states, gy, dx, dlogits,
                                         dlam, dmerge, workspace, workspace_bytes, dtype, layout, stream, &tm);
+    const hipError_t e = tm.finish(times);
+    return s != GSPN_OK ? s : from_hip(e);
+}
+
+int64_t gspn_proxy_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
+                                             int64_t cw, int dtype, int layout) {
+    ProxyBwdLayout L;
+    return proxy_bwd_layout(n, c, h, w, c_proxy, cw, dtype, layout, &L) ? L.total : -1;
+}
+
+gspn_status gspn_proxy_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                 const void* const logits[4], const void* const lam[4], const float* merge,
+                                 const void* gy, void* dx, float* dw_down, float* dw_up, void* const dlogits[4],
+                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
+                                 int dtype, int layout, void* stream) {
+    return proxy_backward_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, gy, dx,
+                               dw_down, dw_up, dlogits, dlam, dmerge, workspace, workspace_bytes, dtype, layout,
+                               stream, nullptr);
+}
+
+gspn_status gspn_proxy_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
+                                       int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
+                                       const void* const logits[4], const void* const lam[4], const float* merge,
+                                       const void* gy, void* dx, float* dw_down, float* dw_up,
+                                       void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                                       int64_t workspace_bytes, int dtype, int layout, void* stream,
+                                       gspn_stage_times* times) {
+    if (!times) return GSPN_ERR_NULL_POINTER;
+    Timer tm;
+    tm.st = as_stream(stream);
+    const gspn_status s = proxy_backward_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam,
+                                              merge, gy, dx, dw_down, dw_up, dlogits, dlam, dmerge, workspace,
+                                              workspace_bytes, dtype, layout, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }

@@ -188,6 +188,26 @@ hipError_t launch_finish_shared_dz(const float* sums, const void* logits, void* 
 hipError_t launch_project(int64_t n, int64_t c_in, int64_t hw, int64_t c_out, const void* in,
                           const void* weight, void* out, int dtype, hipStream_t stream);
 
+// Weight gradients of the projections, in two launches.  First
+// launch_project_wgrad: with wt (weights [k][c]) given, pout = wt . big as
+// launch_project computes it; in every case the partial sums of
+// G[c][j] = sum over images and pixels of big[n][c][p] * small[n][j][p]
+// (big [n][c][hw], small [n][k][hw]) over at most wgrad_slots(n, hw) runs of
+// pixels into part ([slots][c][k] fp32), *slots_used receiving the count.
+// Then launch_wgrad_reduce: out[c * sc + j * sk] = sum over the slots, in a
+// fixed order.  bf16 with hw % 128 == 0, c % 8 == 0, k <= 16 and 16-byte
+// aligned tensors runs on the matrix cores, in groups of at most
+// 32 kWgradMaxBlocks channels (for c up to that, with the projection folded
+// into the same pass over big); everything else on the VALU.
+constexpr int64_t kWgradMaxSlots = 2048;
+constexpr int kWgradMaxBlocks = 10;
+int64_t wgrad_slots(int64_t n, int64_t hw);
+hipError_t launch_project_wgrad(int64_t n, int64_t c, int64_t hw, int64_t k, const void* big, const void* small,
+                                const void* wt, void* pout, float* part, int dtype, hipStream_t stream,
+                                int64_t* slots_used);
+hipError_t launch_wgrad_reduce(const float* part, int64_t slots, int64_t c, int64_t k, float* out, int64_t sc,
+                               int64_t sk, hipStream_t stream);
+
 // The allocation-free forward's scratch (noalloc.hip): a static device array
 // of kNoallocScratchBytes per GPU; *out receives the current device's copy
 // (its address looked up on that device's first call, then cached).

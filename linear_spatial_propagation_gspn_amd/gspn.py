@@ -41,14 +41,15 @@ EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy
            "gspn_scan4_fwd", "gspn_forward4_workspace_bytes", "gspn_forward4",
            "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_forward4_timed",
            "gspn_proxy_forward4_timed", "gspn_backward4_workspace_bytes", "gspn_backward4", "gspn_backward4_timed",
-           "gspn_forward4_noalloc", "gspn_status_string", "gspn_abi_version")
+           "gspn_forward4_noalloc", "gspn_proxy_backward4_workspace_bytes", "gspn_proxy_backward4",
+           "gspn_proxy_backward4_timed", "gspn_status_string", "gspn_abi_version")
 
 # GSPN_NOALLOC_SCRATCH_BYTES: the static scratch gspn_forward4_noalloc works in.
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # gspn_stage, in order.
 STAGES = ("project_down", "normalize", "transpose", "scan", "combine", "project_up", "adjoint", "reduce", "layout",
-          "tail")
+          "tail", "weight_grad")
 
 
 # gspn_scan_kernel, in order.
@@ -133,6 +134,14 @@ def lib() -> ctypes.CDLL:
             h.gspn_backward4.restype = ci
             h.gspn_backward4_timed.argtypes = h.gspn_backward4.argtypes + [ctypes.POINTER(StageTimes)]
             h.gspn_backward4_timed.restype = ci
+            h.gspn_proxy_backward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci]
+            h.gspn_proxy_backward4_workspace_bytes.restype = i64
+            h.gspn_proxy_backward4.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp, ctypes.POINTER(vp),
+                                               ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.POINTER(vp),
+                                               ctypes.POINTER(vp), vp, vp, i64, ci, ci, vp]
+            h.gspn_proxy_backward4.restype = ci
+            h.gspn_proxy_backward4_timed.argtypes = h.gspn_proxy_backward4.argtypes + [ctypes.POINTER(StageTimes)]
+            h.gspn_proxy_backward4_timed.restype = ci
             h.gspn_status_string.argtypes = [ci]
             h.gspn_status_string.restype = ctypes.c_char_p
             h.gspn_abi_version.argtypes = []
@@ -558,6 +567,67 @@ def gspn_backward4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequen
     return (dx, dz, dl, dmerge) if want_dm else (dx, dz, dl)
 
 
+def proxy_backward4_workspace(x: torch.Tensor, c_proxy: int, cw: int, layout: str = "scan") -> torch.Tensor:
+    """A workspace buffer (uint8 tensor on x's device) for gspn_proxy_backward4."""
+    n, c, h, w = x.shape
+    nbytes = int(lib().gspn_proxy_backward4_workspace_bytes(n, c, h, w, c_proxy, cw, _dtype_code(x),
+                                                            _layout_code(layout)))
+    if nbytes < 0:
+        raise ValueError("invalid shape for a gspn_proxy_backward4 workspace")
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+
+
+def gspn_proxy_backward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
+                         logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor], gy: torch.Tensor,
+                         chunk_len: int = 0, workspace: torch.Tensor | None = None,
+                         times: StageTimes | None = None, merge: torch.Tensor | None = None,
+                         dmerge: torch.Tensor | bool | None = None, layout: str = "scan") -> tuple:
+    """Gradients of gspn_proxy_forward4 (with the same ``merge``) for dL/dy =
+    gy: returns (dx, dw_down fp32 [C_proxy][C], dw_up fp32 [C][C_proxy],
+    [dlogits_d], [dlam_d]) and, when ``merge`` is given or ``dmerge`` is (a
+    tensor to fill, or True), the merge weights' gradient (fp32
+    [4][C_proxy]) last.  ``times`` (a StageTimes) selects
+    gspn_proxy_backward4_timed; ``layout`` as in gspn_proxy_forward4."""
+    n, c, h, w = x.shape
+    dt = x.dtype
+    cp = w_down.shape[0]
+    cw = logits[0].shape[1]
+    lc = _layout_code(layout)
+    _check(x, "x", (n, c, h, w), dt, x.device)
+    _check(gy, "gy", (n, c, h, w), dt, x.device)
+    _check(w_down, "w_down", (cp, c), dt, x.device)
+    _check(w_up, "w_up", (c, cp), dt, x.device)
+    for d in range(4):
+        S, L = tensor_frame(d, h, w, layout)
+        _check(logits[d], "logits[%d]" % d, (n, cw, 3, S, L), dt, x.device)
+        _check(lams[d], "lam[%d]" % d, (n, cp, S, L), dt, x.device)
+    dx = torch.empty_like(x)
+    dwd = torch.empty((cp, c), dtype=torch.float32, device=x.device)
+    dwu = torch.empty((c, cp), dtype=torch.float32, device=x.device)
+    dz = [torch.empty_like(z) for z in logits]
+    dl = [torch.empty_like(l) for l in lams]
+    want_dm = merge is not None or (dmerge is not None and dmerge is not False)
+    if want_dm and not isinstance(dmerge, torch.Tensor):
+        dmerge = torch.empty((4, cp), dtype=torch.float32, device=x.device)
+    mp = _merge_ptr(merge, cp, x.device)
+    dmp = _merge_ptr(dmerge, cp, x.device, "dmerge") if want_dm else None
+    if workspace is None:
+        workspace = proxy_backward4_workspace(x, cp, cw, layout)
+    if workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
+    vp4 = ctypes.c_void_p * 4
+    args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up),
+            vp4(*[z.data_ptr() for z in logits]), vp4(*[l.data_ptr() for l in lams]), mp, _ptr(gy), _ptr(dx),
+            _ptr(dwd), _ptr(dwu), vp4(*[t.data_ptr() for t in dz]), vp4(*[t.data_ptr() for t in dl]), dmp,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x), lc, _stream(x.device))
+    if times is None:
+        _raise(lib().gspn_proxy_backward4(*args), "gspn_proxy_backward4")
+    else:
+        _raise(lib().gspn_proxy_backward4_timed(*args, ctypes.byref(times)), "gspn_proxy_backward4_timed")
+    res = (dx, dwd, dwu, dz, dl)
+    return res + (dmerge,) if want_dm else res
+
+
 class _Forward4(torch.autograd.Function):
     """gspn_forward4 as an autograd node whose backward is gspn_backward4."""
 
@@ -603,3 +673,39 @@ def gspn4(x: torch.Tensor, logits: Sequence[torch.Tensor], lams: Sequence[torch.
     h, w = x.shape[-2:]
     keep = bool(keep_states) and (h > 64 or w > 64)
     return _Forward4.apply(int(chunk_len), has_merge, keep, x, m, *logits, *lams)
+
+
+class _ProxyForward4(torch.autograd.Function):
+    """gspn_proxy_forward4 as an autograd node whose backward is
+    gspn_proxy_backward4 (weight gradients cast to the weights' dtype)."""
+
+    @staticmethod
+    def forward(ctx, chunk_len, has_merge, x, w_down, w_up, merge, *tensors):
+        logits, lams = list(tensors[:4]), list(tensors[4:])
+        y = gspn_proxy_forward4(x, w_down, w_up, logits, lams, chunk_len=chunk_len,
+                                merge=merge if has_merge else None)
+        ctx.chunk_len = chunk_len
+        ctx.has_merge = has_merge
+        ctx.save_for_backward(x, w_down, w_up, merge, *tensors)
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, w_down, w_up, merge, *tensors = ctx.saved_tensors
+        logits, lams = tensors[:4], tensors[4:]
+        res = gspn_proxy_backward4(x, w_down, w_up, logits, lams, gy.to(x.dtype).contiguous(),
+                                   chunk_len=ctx.chunk_len, merge=merge if ctx.has_merge else None)
+        dx, dwd, dwu, dz, dl = res[:5]
+        dm = res[5] if ctx.has_merge else None
+        return (None, None, dx, dwd.to(w_down.dtype), dwu.to(w_up.dtype), dm, *dz, *dl)
+
+
+def gspn_proxy4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor, logits: Sequence[torch.Tensor],
+                lams: Sequence[torch.Tensor], chunk_len: int = 0, merge: torch.Tensor | None = None) -> torch.Tensor:
+    """The compressive-proxy propagation as a differentiable op:
+    gspn_proxy_forward4 forward, gspn_proxy_backward4 for the gradients of
+    x, both projection weights, the logits, the lambdas and (if given) the
+    merge weights."""
+    has_merge = merge is not None
+    m = merge if has_merge else torch.empty(0, device=x.device)
+    return _ProxyForward4.apply(int(chunk_len), has_merge, x, w_down, w_up, m, *logits, *lams)

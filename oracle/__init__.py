@@ -12,11 +12,12 @@ it.  Each wrapper cites the passage of the GSPN pages it follows; the C file
 holds the full list of readings taken where the pages are silent.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_oracle_backward_pins.py`` and ``tests/test_oracle_merge_pins.py``
-(closed forms, brute-force dense matrices, exact rational arithmetic,
-symmetry invariants, library routines, and for the gradients central finite
-differences of the pinned forward and adjoint dot-product identities); none
-is "parity unpinned".
+``tests/test_oracle_backward_pins.py``, ``tests/test_oracle_merge_pins.py``
+and ``tests/test_oracle_proxy_backward_pins.py`` (closed forms, brute-force
+dense matrices, exact rational arithmetic, symmetry invariants, library
+routines, and for the gradients central finite differences of the pinned
+forward and adjoint dot-product and homogeneity identities); none is "parity
+unpinned".
 
 Layouts (contiguous, row-major):
   x, y, h           [N][C][H][W]
@@ -305,9 +306,9 @@ def proxy_backward4(x, w_down, w_up, logits: Sequence, lams: Sequence, gy, chunk
     res = backward4(xp, logits, lams, gp, chunk, merge=merge)
     dxp = res[0]
     dx = project(dxp, wd.T)
-    dwu = np.einsum("ncp,nkp->ck", gg.reshape(gg.shape[0], gg.shape[1], -1), yp.reshape(yp.shape[0], yp.shape[1], -1))
-    dwd = np.einsum("nkp,ncp->kc", dxp.reshape(dxp.shape[0], dxp.shape[1], -1),
-                    xx.reshape(xx.shape[0], xx.shape[1], -1))
+    n = xx.shape[0]
+    dwu = sum(gg[i].reshape(gg.shape[1], -1) @ yp[i].reshape(yp.shape[1], -1).T for i in range(n))
+    dwd = sum(dxp[i].reshape(dxp.shape[1], -1) @ xx[i].reshape(xx.shape[1], -1).T for i in range(n))
     out = (dx, dwd, dwu, res[1], res[2])
     return out + (res[3],) if merge is not None else out
 

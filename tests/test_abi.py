@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 9
+    assert lib.gspn_abi_version() == 10
     for code in range(13):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -413,3 +413,56 @@ def test_noalloc_validation(lib):
     assert lib.gspn_forward4_workspace_bytes(*small, 0) <= G.NOALLOC_SCRATCH_BYTES
     assert lib.gspn_forward4_workspace_bytes(*small, 1) > G.NOALLOC_SCRATCH_BYTES
     assert f(n=1, c=4, h=512, w=1024, cw=4, lay=1) == WSPACE
+
+
+def test_proxy_backward4_validation(lib):
+    """gspn_proxy_backward4 rejects bad arguments before queueing anything
+    (every call here fails validation)."""
+    vp4 = ctypes.c_void_p * 4
+    n, c, h, w, cp = 1, 6, 8, 8, 2
+    es = 2
+    zs = vp4(*[0x10000000 + d * 0x100000 for d in range(4)])
+    ls = vp4(*[0x20000000 + d * 0x100000 for d in range(4)])
+    dzs = vp4(*[0x30000000 + d * 0x100000 for d in range(4)])
+    dls = vp4(*[0x40000000 + d * 0x100000 for d in range(4)])
+    X, WD, WU, GY, DX, DWD, DWU, WS = (0x50000000, 0x51000000, 0x52000000, 0x53000000, 0x54000000, 0x55000000,
+                                       0x56000000, 0x60000000)
+    need = lib.gspn_proxy_backward4_workspace_bytes(n, c, h, w, cp, 1, 1, 0)
+    assert need > 0 and need % 256 == 0
+    assert lib.gspn_proxy_backward4_workspace_bytes(n, c, h, w, cp, 3, 1, 0) == -1     # cw neither 1 nor c_proxy
+    assert lib.gspn_proxy_backward4_workspace_bytes(n, 0, h, w, cp, 1, 1, 0) == -1
+    assert lib.gspn_proxy_backward4_workspace_bytes(n, c, h, w, 0, 1, 1, 0) == -1
+    # at least the proxy-space backward's workspace
+    assert need >= lib.gspn_backward4_workspace_bytes(n, cp, h, w, 1, 1, 0) + 4 * n * cp * h * w * es
+
+    def f(n=n, c=c, h=h, w=w, cp=cp, cw=1, chunk=0, x=X, gy=GY, dx=DX, dwd=DWD, dwu=DWU, dz=dzs, dl=dls, m=None,
+          dm=None, ws=WS, wsb=need, dt=1, lay=0):
+        return lib.gspn_proxy_backward4(n, c, h, w, cp, cw, chunk, x, WD, WU, zs, ls, m, gy, dx, dwd, dwu, dz, dl,
+                                        dm, ws, wsb, dt, lay, None)
+
+    assert f(dt=2) == DTYPE
+    assert f(lay=5) == LAYOUT
+    assert f(c=0) == SHAPE
+    assert f(cp=0) == SHAPE
+    assert f(chunk=-1) == CHUNK
+    assert f(cw=3) == WCH
+    assert f(h=5000) == UNSUP
+    assert f(x=0) == NULLP
+    assert f(dwu=0) == NULLP
+    assert f(dl=vp4(0x40000000, 0, 0x40200000, 0x40300000)) == NULLP
+    assert f(ws=0) == NULLP
+    assert f(wsb=need - 1) == WSPACE
+    assert f(ws=WS + 2) == MISAL
+    assert f(dx=DX + 1) == MISAL
+    assert f(dwd=DWD + 2) == MISAL
+    assert f(dx=X) == ALIAS                                   # dx over x
+    assert f(dwu=DWD + 4) == ALIAS                            # the two weight gradients overlap
+    assert f(dm=WS + 64, m=None) == ALIAS                     # dmerge inside the workspace
+    assert f(dwd=WD) == ALIAS                                 # a gradient over its weights
+    assert f(ws=GY - 64) == ALIAS                             # the workspace over gy
+    assert f(h=3000, wsb=1 << 40) == UNSUP                    # longer lines than the proxy-space backward takes
+    t = G.StageTimes()
+    assert lib.gspn_proxy_backward4_timed(n, c, h, w, cp, 1, 0, X, WD, WU, zs, ls, None, GY, DX, DWD, DWU, dzs, dls,
+                                          None, WS, need, 1, 0, None, None) == NULLP
+    assert lib.gspn_proxy_backward4_timed(n, c, h, w, cp, 1, 0, X, WD, WU, zs, ls, None, GY, DX, DWD, DWU, dzs, dls,
+                                          None, WS, need, 2, 0, None, ctypes.byref(t)) == DTYPE

@@ -44,7 +44,7 @@ def chk():
     lib.gspn_check_launches.restype = _i64
     lib.gspn_check_report.restype = _i64
     lib.gspn_check_report.argtypes = [ctypes.c_char_p, _i64]
-    for f in ("gspn_forward4", "gspn_backward4", "gspn_forward4_noalloc"):
+    for f in ("gspn_forward4", "gspn_backward4", "gspn_forward4_noalloc", "gspn_proxy_forward4", "gspn_proxy_backward4"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -249,3 +249,68 @@ def test_random_shapes_stay_in_bounds(chk, case):
     assert (rf, rb) == (0, 0), text
     bad = [l for l in text.splitlines() if l.startswith("violation") and "without a host replay" not in l]
     assert not bad, text
+
+
+def proxy_training_step(lib, n, c, h, w, cp, dtype=torch.bfloat16, shared=True, chunk=0, merge=False):
+    """The compressive-proxy forward, then its backward, through the check
+    library's C ABI (buffers sized as the binding sizes them); returns the
+    two status codes."""
+    sp = Space(lib)
+    x = _meta(n, c, h, w, dtype)
+    es = x.element_size()
+    cw = 1 if shared else cp
+    dt = G._dtype_code(x)
+    xb = n * c * h * w * es
+    pb = n * cp * h * w * es
+    zb = n * cw * 3 * h * w * es
+    px = sp.buf("x", xb)
+    pwd = sp.buf("w_down", cp * c * es)
+    pwu = sp.buf("w_up", c * cp * es)
+    pz = [sp.buf("logits%d" % d, zb) for d in range(4)]
+    pl = [sp.buf("lambda%d" % d, pb) for d in range(4)]
+    pm = sp.buf("merge", 4 * cp * 4) if merge else None
+    py = sp.buf("y", xb)
+    fws = G.proxy_forward4_workspace(x, cp, cw)
+    pfw = sp.buf("forward workspace", _nbytes(fws))
+    rf = lib.gspn_proxy_forward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(cp), _i64(cw), _i64(chunk),
+                                 ctypes.c_void_p(px), ctypes.c_void_p(pwd), ctypes.c_void_p(pwu), _vp4(*pz), _vp4(*pl),
+                                 ctypes.c_void_p(pm), ctypes.c_void_p(py), ctypes.c_void_p(pfw), _i64(_nbytes(fws)),
+                                 dt, 0, None)
+    pg = sp.buf("dL/dy", xb)
+    pdx = sp.buf("dx", xb)
+    pdwd = sp.buf("dw_down", cp * c * 4)
+    pdwu = sp.buf("dw_up", c * cp * 4)
+    pdz = [sp.buf("dlogits%d" % d, zb) for d in range(4)]
+    pdl = [sp.buf("dlambda%d" % d, pb) for d in range(4)]
+    pdm = sp.buf("dmerge", 4 * cp * 4) if merge else None
+    bws = G.proxy_backward4_workspace(x, cp, cw)
+    pbw = sp.buf("backward workspace", _nbytes(bws))
+    rb = lib.gspn_proxy_backward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(cp), _i64(cw), _i64(chunk),
+                                  ctypes.c_void_p(px), ctypes.c_void_p(pwd), ctypes.c_void_p(pwu), _vp4(*pz),
+                                  _vp4(*pl), ctypes.c_void_p(pm), ctypes.c_void_p(pg), ctypes.c_void_p(pdx),
+                                  ctypes.c_void_p(pdwd), ctypes.c_void_p(pdwu), _vp4(*pdz), _vp4(*pdl),
+                                  ctypes.c_void_p(pdm), ctypes.c_void_p(pbw), _i64(_nbytes(bws)), dt, 0, None)
+    return rf, rb
+
+
+@pytest.mark.parametrize("case", [
+    dict(n=1, c=320, h=64, w=256, cp=8),                                  # folded projection, ten channel blocks
+    dict(n=2, c=328, h=32, w=128, cp=5, merge=True),                      # two channel groups, projection apart
+    dict(n=1, c=24, h=70, w=100, cp=3, chunk=9),                          # bf16, ragged pixel count: VALU sums
+    dict(n=2, c=7, h=65, w=66, cp=2, dtype=torch.float32, shared=False),  # fp32
+], ids=["fold", "groups", "ragged", "f32"])
+def test_proxy_backward_stays_in_bounds(chk, case):
+    """The compressive-proxy backward: the weight transposes, the fused
+    projection with the weight-gradient partial sums, the VALU partial sums
+    and the fixed-order reduction stay inside their buffers.  The
+    projections and the banded scan have no host replay; their launches are
+    reported, not failed."""
+    case = dict(case)
+    rf, rb = proxy_training_step(chk, case.pop("n"), case.pop("c"), case.pop("h"), case.pop("w"), case.pop("cp"),
+                                 **case)
+    text = report(chk)
+    assert (rf, rb) == (0, 0), text
+    bad = [l for l in text.splitlines() if l.startswith("violation") and "without a host replay" not in l]
+    assert not bad, text
+    kernels = set(_kernels(text))
+    assert "wgrad_reduce_kernel" in " ".join(kernels), text
