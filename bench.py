@@ -273,6 +273,7 @@ KERNEL_SOURCES = {
     "scan4v_kernel": _SCAN4,
     "plane4_kernel": ["plane4.hip", "plane_common.hpp"],
     "adj4_kernel": ["backward.hip"],
+    "adj4band_kernel": ["backward.hip"],
     "adjplane_kernel": ["adjplane.hip", "plane_common.hpp"],
     "seq4_kernel": ["seq4.hip"],
     "project_narrow_out_mfma": ["project.hip"],
@@ -673,6 +674,7 @@ def bench_backward(args, wl):
     acc = {name: 0.0 for name in G.STAGES}
     facc = {name: 0.0 for name in G.STAGES}
     recompute = None
+    adj_plan, adj_launches = None, 1
     for _ in range(reps):
         t = G.StageTimes()
         ft = {}
@@ -680,18 +682,26 @@ def bench_backward(args, wl):
         for name, v in t.as_dict().items():
             if name == "scan_kernel":
                 recompute = v
-            elif name != "adjoint_plan":
+            elif name == "adjoint_plan":
+                adj_plan = v
+            else:
                 acc[name] += v["ms"] / reps
+                if name == "adjoint":
+                    adj_launches = max(1, v["launches"])
         for name, v in ft.items():
             if name not in ("scan_kernel", "adjoint_plan"):
                 facc[name] += v["ms"] / reps
-    kernel_ms = acc["adjoint"]
+    kernel_ms = acc["adjoint"] / adj_launches
     # planes of at most 64 x 64 recompute with the plane-resident forward
-    # and run the plane-resident adjoint
+    # and run the plane-resident adjoint; very few long lines run the banded
+    # adjoint, one launch per band
     adj_kernel = "adjplane_kernel" if recompute == "plane4_kernel" else "adj4_kernel"
+    if adj_plan is not None and adj_plan["kernel"] == "adj4band_kernel":
+        adj_kernel = "adj4band_kernel"
     design = adjplane_launch_bytes(wl) if adj_kernel == "adjplane_kernel" else adjoint_launch_bytes(wl)
-    # the adjoint launch processes every unit of the backward: its compulsory bytes
-    bpl = backward_algorithmic_bytes(wl)
+    design //= adj_launches
+    # the adjoint launches process every unit of the backward: its compulsory bytes
+    bpl = backward_algorithmic_bytes(wl) // adj_launches
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
     alg = backward_algorithmic_bytes(wl) + (algorithmic_bytes(wl) if train else 0)
     eff = alg / (ms * 1e-3) / 1e9
@@ -723,7 +733,7 @@ def bench_backward(args, wl):
         "stages_ms": stages,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": adj_kernel,
-                     "kernel_ms": round(kernel_ms, 4), "launches_per_step": 1, "bytes_per_launch": bpl,
+                     "kernel_ms": round(kernel_ms, 4), "launches_per_step": adj_launches, "bytes_per_launch": bpl,
                      "traffic_source": traffic_src, "design_bytes_per_launch": design,
                      "design_achieved": round(design / (kernel_ms * 1e-3) / 1e9, 1),
                      "step_traffic": step_traffic, "step_traffic_source": step_src},

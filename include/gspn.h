@@ -323,7 +323,9 @@ gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int6
  * weights as in gspn_forward4_workspace_bytes; five maps of n*c*h*w
  * elements of the storage type (x and dL/dy transposed into the horizontal
  * scan frame, three per-direction dx terms), rounded up to a multiple of 4
- * bytes; last, the four directions' forward states in fp32 (4 * n*c*h*w
+ * bytes; for at most 16 planes (n*c <= 16) with h and w both at least 512,
+ * 2 * 4 * 3 * n*c * max(h, w) floats for the banded adjoint (family 3
+ * below); last, the four directions' forward states in fp32 (4 * n*c*h*w
  * floats), which a call given the states does not need: it may pass 16 *
  * n*c*h*w bytes less.  Returns -1 for invalid arguments.
  */
@@ -372,10 +374,12 @@ gspn_status gspn_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c
  * gspn_proxy_backward4_workspace_bytes -- bytes of the gspn_proxy_backward4
  * workspace: four proxy-space maps (n*c_proxy*h*w elements of the storage
  * type each), both projection weights transposed, the weight-gradient
- * partial sums (at most 2048 * c * c_proxy floats), and the larger of
- * gspn_forward4_workspace_bytes and gspn_backward4_workspace_bytes for
- * (n, c_proxy, h, w, cw), each part rounded up to 256 bytes.  Returns -1 for
- * invalid arguments (c < 1 or c_proxy < 1 among them).
+ * partial sums (at most 2048 * c * c_proxy floats), for planes larger than
+ * 64 x 64 the proxy-space forward's fp32 states (16 * n*c_proxy*h*w bytes),
+ * and the larger of gspn_forward4_workspace_bytes and
+ * gspn_backward4_workspace_bytes (less the states) for (n, c_proxy, h, w,
+ * cw), each part rounded up to 256 bytes.  Returns -1 for invalid arguments
+ * (c < 1 or c_proxy < 1 among them).
  */
 int64_t gspn_proxy_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
                                              int64_t cw, int dtype, int layout);
@@ -394,7 +398,9 @@ int64_t gspn_proxy_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, in
  *               (dmerge optional: NULL skips it)
  * x_p and y_p = forward4(x_p) are recomputed inside (stored in the storage
  * type, as the forward stores them; every intermediate rounds once at its
- * store).  The weight gradients are summed in fp32 over at most 2048 runs
+ * store); for planes larger than 64 x 64 that forward keeps its fp32 states
+ * for the proxy-space backward, as gspn_forward4 / gspn_backward4 do with
+ * states.  The weight gradients are summed in fp32 over at most 2048 runs
  * of pixels, then the runs in a fixed order: they do not vary between calls.
  * With no pixels (n*h*w == 0) dw_down, dw_up and dmerge are written as
  * zeros and nothing else is touched (the other pointers may then be NULL).
@@ -462,7 +468,12 @@ typedef enum {
 
 /* The adjoint launch of a backward call (gspn_stage_times.adjoint; all 0
  * when the call ran none): the kernel family (1 = one workgroup per line and
- * direction, 2 = one workgroup per plane for planes of at most 64 x 64), the
+ * direction, 2 = one workgroup per plane for planes of at most 64 x 64,
+ * 3 = very few long unchunked lines, at most 16 planes with both sides at
+ * least 512: each line split into segments of 256 positions, one workgroup
+ * per segment with a halo of 128 positions on each side, one launch per
+ * band of 128 steps, the products crossing a band's border kept in the
+ * workspace), the
  * positions each lane owns, the channels one workgroup runs together (more
  * than 1 only for channel-shared logits, whose gradient it sums over them),
  * and whether the streams touched once carry the non-temporal hint. */

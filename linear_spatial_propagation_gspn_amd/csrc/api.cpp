@@ -163,6 +163,18 @@ int64_t layout_copy_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
 
 // The four-direction launches run a workgroup per (plane, chunk) of every
 // direction: the total must fit one launch's grid.
+// Bands of the fp32-state forward for very few long lines (0: the
+// four-direction launch instead).  A forward keeping its states and a
+// backward recomputing them take the same condition, so both run the same
+// kernel and the states agree bit for bit.
+int state_bands(const gspn::ScanParams (&p)[4], int64_t n, int64_t c, int64_t h, int64_t w) {
+    return gspn::adjoint_band_shape(n * c, h, w) ? gspn::band_launches(p) : 0;
+}
+
+int64_t adjoint_band_bytes(int64_t n, int64_t c, int64_t h, int64_t w) {
+    return gspn::adjoint_band_shape(n * c, h, w) ? gspn::adjoint_band_floats(n * c, h > w ? h : w) * 4 : 0;
+}
+
 bool fused_grid_ok(int64_t n, int64_t c, int64_t h, int64_t w, const int64_t chunks[4]) {
     int64_t total = 0;
     for (int d = 0; d < 4; ++d) {
@@ -629,10 +641,20 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
             p[d].odtype = GSPN_F32;
             p[d].mscale = nullptr;  // the merge below applies the merge weights
         }
-        int kind = GSPN_SCAN_FUSED4;
-        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
-            return GSPN_ERR_HIP;
-        if (tm) tm->scan_kernel = kind;
+        const int nbands = state_bands(p, n, c, h, w);
+        if (nbands > 0) {
+            float* state = reinterpret_cast<float*>(ws + ((prenorm ? 4 * wdir : 0) + 4 * xb + 3) / 4 * 4);
+            for (int b = 0; b < nbands; ++b)
+                if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4_band(p, state, b, st); }) !=
+                    hipSuccess)
+                    return GSPN_ERR_HIP;
+            if (tm) tm->scan_kernel = GSPN_SCAN_BANDED;
+        } else {
+            int kind = GSPN_SCAN_FUSED4;
+            if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
+                return GSPN_ERR_HIP;
+            if (tm) tm->scan_kernel = kind;
+        }
         return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
             return gspn::launch_combine_states(y, states, states + elems, states + 2 * elems, states + 3 * elems,
                                                n * c, static_cast<int>(h), static_cast<int>(w), dtype, st, merge,
@@ -836,7 +858,8 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     char* hs[4];
     const int64_t loff = ((dterm[3] - ws) + xb + 3) / 4 * 4;
     const int64_t lc = layout == GSPN_LAYOUT_ARRAY ? layout_copy_bytes(n, c, h, w, cw, dtype) : 0;
-    const int64_t hoff = loff + 2 * lc;
+    float* qband = reinterpret_cast<float*>(ws + loff + 2 * lc);  // the banded adjoint's products
+    const int64_t hoff = loff + 2 * lc + adjoint_band_bytes(n, c, h, w);
     hs[0] = states ? reinterpret_cast<char*>(const_cast<float*>(states)) : ws + hoff;
     for (int d = 1; d < 4; ++d) hs[d] = hs[d - 1] + hb;
     const int H = static_cast<int>(h);
@@ -957,10 +980,21 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         // channel-shared logits: normalised once, as in the forward
         if (shared && prenormalise(n, h, w, logits, wnorm, wdir, dtype, st, tm, p) != hipSuccess)
             return GSPN_ERR_HIP;
-        int kind = GSPN_SCAN_FUSED4;
-        if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
-            return GSPN_ERR_HIP;
-        if (tm) tm->scan_kernel = kind;
+        // very few long lines: the banded forward, its band-border states in
+        // the banded adjoint's scratch (free until the adjoint runs)
+        const int nbands = state_bands(p, n, c, h, w);
+        if (nbands > 0) {
+            for (int b = 0; b < nbands; ++b)
+                if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4_band(p, qband, b, st); }) !=
+                    hipSuccess)
+                    return GSPN_ERR_HIP;
+            if (tm) tm->scan_kernel = GSPN_SCAN_BANDED;
+        } else {
+            int kind = GSPN_SCAN_FUSED4;
+            if (timed(tm, GSPN_STAGE_SCAN, [&] { return gspn::launch_scan4v(p, st, &kind); }) != hipSuccess)
+                return GSPN_ERR_HIP;
+            if (tm) tm->scan_kernel = kind;
+        }
     }
     if (shared &&
         timed(tm, GSPN_STAGE_REDUCE, [&] { return gspn::launch_fill_zero(sums, 4 * zsum, st); }) != hipSuccess)
@@ -994,10 +1028,20 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         a[d].mscale = merge ? merge + d * c : nullptr;
         a[d].dmerge = dmerge ? dmerge + d * c : nullptr;
     }
-    gspn::AdjointPlan plan{};
-    if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjoint4(a, st, &plan); }) != hipSuccess)
-        return GSPN_ERR_HIP;
-    if (tm) tm->adjoint = {1, plan.positions, plan.group, plan.nontemporal};
+    const int bands = adjoint_band_bytes(n, c, h, w) > 0 ? gspn::adjoint_band_launches(a) : 0;
+    if (bands > 0) {
+        for (int b = 0; b < bands; ++b)
+            if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjoint4_band(a, qband, b, st); }) !=
+                hipSuccess)
+                return GSPN_ERR_HIP;
+        const bool nt = (h * static_cast<int64_t>(es)) % 128 == 0 && (w * static_cast<int64_t>(es)) % 128 == 0;
+        if (tm) tm->adjoint = {3, 2, 1, nt ? 1 : 0};
+    } else {
+        gspn::AdjointPlan plan{};
+        if (timed(tm, GSPN_STAGE_ADJOINT, [&] { return gspn::launch_adjoint4(a, st, &plan); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        if (tm) tm->adjoint = {1, plan.positions, plan.group, plan.nontemporal};
+    }
     // dx = ((D2^T + D3^T) + D0) + D1, D0 written into dx directly
     if (timed(tm, GSPN_STAGE_COMBINE, [&] {
             return gspn::launch_combine(dx, dterm[1], dterm[2], dterm[3], n * c, H, W, 1, dtype, st);
@@ -1015,11 +1059,14 @@ gspn_status backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
 }
 
 // Workspace of the proxy backward: x_p, y_p, dL/dy_p and dx_p in the storage
-// type, the two weights transposed, the weight-gradient partial sums, then
-// the larger of the proxy-space forward and backward workspaces (used one
-// after the other); every part starts on a 256-byte boundary.
+// type, the two weights transposed, the weight-gradient partial sums, for
+// planes larger than 64 x 64 the proxy-space forward's fp32 states (kept by
+// the forward, read by the backward), then the larger of the proxy-space
+// forward and backward workspaces (used one after the other); every part
+// starts on a 256-byte boundary.
 struct ProxyBwdLayout {
-    int64_t xp, yp, gp, dxp, wtu, wtd, part, inner, inner_bytes, total;
+    int64_t xp, yp, gp, dxp, wtu, wtd, part, states, inner, inner_bytes, total;
+    bool keep;  // the states are kept
 };
 
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
@@ -1042,8 +1089,13 @@ bool proxy_bwd_layout(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_prox
     L->wtu = 4 * pb;
     L->wtd = L->wtu + mb;
     L->part = L->wtd + mb;
-    L->inner = L->part + round256(gspn::wgrad_slots(n, h * w) * c * c_proxy * 4);
-    L->inner_bytes = f4 > b4 ? f4 : b4;
+    L->states = L->part + round256(gspn::wgrad_slots(n, h * w) * c * c_proxy * 4);
+    // planes of at most 64 x 64 recompute their states inside the adjoint
+    L->keep = !gspn::plane4_supported(h, w);
+    const int64_t sb = L->keep ? 16 * checked_product({n, c_proxy, h, w}) : 0;
+    L->inner = L->states + round256(sb);
+    const int64_t b4s = b4 - sb;  // the backward given the states
+    L->inner_bytes = f4 > b4s ? f4 : b4s;
     L->total = L->inner + L->inner_bytes;
     return true;
 }
@@ -1138,6 +1190,7 @@ gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int6
     void* wtu = ws + L.wtu;  // w_up^T [c_proxy][c]
     void* wtd = ws + L.wtd;  // w_down^T [c][c_proxy]
     float* part = reinterpret_cast<float*>(ws + L.part);
+    float* states = L.keep ? reinterpret_cast<float*>(ws + L.states) : nullptr;
     void* inner = ws + L.inner;
     // the weights transposed, for the projections the chain rule needs
     if (timed(tm, GSPN_STAGE_REDUCE, [&] {
@@ -1151,7 +1204,7 @@ gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int6
     if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
               [&] { return gspn::launch_project(n, c, hw, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
-    gspn_status s = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, nullptr, inner,
+    gspn_status s = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, states, inner,
                                   L.inner_bytes, dtype, layout, stream, tm);
     if (s != GSPN_OK) return s;
     // dL/dy_p = w_up^T gy, and in the same pass over gy the partial sums of
@@ -1164,7 +1217,7 @@ gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int6
               [&] { return gspn::launch_wgrad_reduce(part, slots, c, c_proxy, dw_up, c_proxy, 1, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
     // the propagation's gradients in proxy space
-    s = backward_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, nullptr, gp, dxp, dlogits, dlam,
+    s = backward_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, states, gp, dxp, dlogits, dlam,
                       dmerge, inner, L.inner_bytes, dtype, layout, stream, tm);
     if (s != GSPN_OK) return s;
     // dx = w_down^T dx_p; dL/dw_down[k][c] = sum dx_p[k] x[c]
@@ -1257,7 +1310,10 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
     // may give that much less); for channel-shared logits over several
     // channels the gradient sums and the normalised weights of the recomputed
     // forward (first)
-    const int64_t maps = (5 * elems * static_cast<int64_t>(elem_size(dtype)) + 3) / 4 * 4 + 4 * elems * 4;
+    // the banded adjoint's products at band boundaries, for launches of very
+    // few long lines (before the states)
+    const int64_t maps = (5 * elems * static_cast<int64_t>(elem_size(dtype)) + 3) / 4 * 4 + 4 * elems * 4 +
+                         adjoint_band_bytes(n, c, h, w);
     const int64_t nhw = checked_product({n, h, w});
     const int64_t shared = (cw == 1 && c > 1) ? 4 * 3 * nhw * 4 + 4 * nhw * (dtype == GSPN_F32 ? 3 * 4 : 4) : 0;
     if (layout == GSPN_LAYOUT_SCAN) return shared + maps;

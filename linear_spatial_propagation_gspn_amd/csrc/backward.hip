@@ -40,6 +40,12 @@ using IC = std::integral_constant<int, V>;
 template <int P, int G>
 constexpr int adj_depth() { return (P == 1 && G == 1) ? 4 : 2; }
 
+// steps in flight in the banded adjoint: its workgroups of four waves run
+// one a CU, so the registers a deeper ring takes cost no occupancy
+#ifndef GSPN_ADJ_BAND_DEPTH
+#define GSPN_ADJ_BAND_DEPTH 8
+#endif
+
 // channels per workgroup for channel-shared logits (fewer for two positions
 // per lane: register budget; with the learnable merge's extra state the
 // four-channel groups spill a few registers, and still measured faster than
@@ -138,6 +144,24 @@ GSPN_HD AdjFill adj_fill(int t, int t0, int S, int L, bool rev) {
     return {static_cast<int64_t>(adj_row(tc, S, rev)) * L, static_cast<int64_t>(adj_row(tp, S, rev)) * L};
 }
 
+// A band of the banded adjoint (few, long lines): the workgroup's lanes
+// cover positions r0 .. r0 + nt P - 1 of the line (its segment
+// [o_lo, o_hi) plus a halo on each side) for the steps tb_lo .. tb_hi - 1.
+// The products w a of the step above the band come from qin (rows o of
+// qstride floats; null: the band holds the chunk's last step), those of its
+// bottom step go to qout (null: none wanted).  Only the segment's own
+// positions store anything.
+struct AdjBand {
+    int r0, o_lo, o_hi, tb_lo, tb_hi;
+    int64_t qstride;
+    const float* qin;
+    float* qout;
+};
+
+// Position k clamped into the line at both ends (band lanes may start
+// before position 0).
+GSPN_HD int adj_clamp2(int k, int L) { return k < 0 ? 0 : (k < L - 1 ? k : L - 1); }
+
 // One (plane group, chunk) line of one direction.  G channels of the same
 // image run together (G > 1 only for channel-shared logits): the logits of a
 // position are normalised once for all of them, and the logit gradient, which
@@ -164,9 +188,11 @@ __device__ __forceinline__ void st_once(T* p, float v) {
     else Store<T>::st(p, v);
 }
 
-template <typename T, int P, int G, bool MERGE, bool NT>
-__device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float* edge_raw) {
-    constexpr int D = adj_depth<P, G>();
+template <typename T, int P, int G, bool MERGE, bool NT, bool BAND = false>
+__device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float* edge_raw,
+                                         const AdjBand& bd = AdjBand{}) {
+    static_assert(!BAND || G == 1, "bands run one channel per workgroup");
+    constexpr int D = BAND ? GSPN_ADJ_BAND_DEPTH : adj_depth<P, G>();
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
     const int S = a.S;
@@ -200,19 +226,24 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
         return edge_raw[adj_edge(b, side, G, g, nt, lane)];
     };
 
-    const int k0 = tid * P;
+    const int k0 = (BAND ? bd.r0 : 0) + tid * P;
     int kk[P];
-    bool kin[P];
+    bool kin[P];  // in the line
+    bool own[P];  // stored by this workgroup (BAND: in its segment)
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-        kk[j] = adj_clamp(k0 + j, L);
-        kin[j] = k0 + j < L;
+        kk[j] = BAND ? adj_clamp2(k0 + j, L) : adj_clamp(k0 + j, L);
+        kin[j] = (!BAND || k0 + j >= 0) && k0 + j < L;
+        own[j] = BAND ? (kin[j] && k0 + j >= bd.o_lo && k0 + j < bd.o_hi) : kin[j];
     }
-    const int kl = adj_left(k0, L);         // left neighbour of the first position (clamped)
-    const int kr = adj_right(k0, P, L);  // right neighbour of the last position (clamped)
+    // left neighbour of the first position, right one of the last (clamped)
+    const int kl = BAND ? adj_clamp2(k0 - 1, L) : adj_left(k0, L);
+    const int kr = BAND ? adj_clamp2(k0 + P, L) : adj_right(k0, P, L);
 
     const int t0 = q * a.K;
     const int t1 = min(t0 + a.K, S);
+    const int ttop = BAND ? bd.tb_hi : t1;  // one past this launch's first (highest) step
+    const int tbot = BAND ? bd.tb_lo : t0;  // its last step
     const bool rev = a.reverse != 0;
     auto line_of = [&](int t) { return adj_row(t, S, rev); };
 
@@ -298,9 +329,9 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 float am = a_t[j];
                 if constexpr (MERGE) {
                     am = a_t[j] * msc[g];  // the adjoint of the merged output
-                    dm[g] = __builtin_fmaf(a_t[j], rl[s][g][j] * rx[s][g][j], dm[g]);
+                    if (!BAND || own[j]) dm[g] = __builtin_fmaf(a_t[j], rl[s][g][j] * rx[s][g][j], dm[g]);
                 }
-                if (kin[j] && gok[g]) {
+                if (own[j] && gok[g]) {
                     st_once<T, NT>(dlp + go + lo + k0 + j, am * rx[s][g][j]);
                     st_once<T, NT>(dxp + go + lo + k0 + j, am * rl[s][g][j]);
                 }
@@ -321,7 +352,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 float* dzs = static_cast<float*>(a.dz) + nidx * 3 * plane;
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
-                    if (kin[j]) {
+                    if (own[j]) {
                         atomicAdd(dzs + lo + k0 + j, dw[j][0] - dw[j][1]);
                         atomicAdd(dzs + plane + lo + k0 + j, dw[j][2] - dw[j][1]);
                     }
@@ -339,7 +370,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                     if (k0 + j + 1 >= L) dz[2] = 0.0f;
                     if (L == 1) dz[1] = 0.0f;  // a single neighbour: w = [1] whatever its logit
                 }
-                if (kin[j]) {
+                if (own[j]) {
                     T* dzp = static_cast<T*>(a.dz) + zplane;
 #pragma unroll
                     for (int o = 0; o < 3; ++o) st_once<T, NT>(dzp + o * plane + lo + k0 + j, dz[o]);
@@ -357,18 +388,47 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     };
 
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
-        (fill(IC<Ss>{}, t1 - 1 - Ss), ...);
+        (fill(IC<Ss>{}, ttop - 1 - Ss), ...);
     }(std::make_integer_sequence<int, D>{});
-    step(IC<0>{}, IC<1>{}, t1 - 1);
-    int t = t1 - 2;
-    for (; t - (D - 1) >= t0; t -= D) {
+    if constexpr (BAND) {
+        // the products of the step above the band (none above the chunk's
+        // last step), published to the neighbours like a step's own
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const bool have = bd.qin != nullptr && kin[j];
+            qn0[0][j] = have ? bd.qin[kk[j]] : 0.0f;
+            qn1[0][j] = have ? bd.qin[bd.qstride + kk[j]] : 0.0f;
+            qn2[0][j] = have ? bd.qin[2 * bd.qstride + kk[j]] : 0.0f;
+        }
+        edge(buf, 0, 0, tid) = qn0[0][0];
+        edge(buf, 1, 0, tid) = qn2[0][P - 1];
+        __syncthreads();
+        step(IC<0>{}, IC<0>{}, ttop - 1);
+    } else {
+        step(IC<0>{}, IC<1>{}, t1 - 1);
+    }
+    int t = ttop - 2;
+    for (; t - (D - 1) >= tbot; t -= D) {
         [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
             (step(IC<(Ss + 1) % D>{}, IC<0>{}, t - Ss), ...);
         }(std::make_integer_sequence<int, D>{});
     }
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
-        ((t - Ss >= t0 ? step(IC<(Ss + 1) % D>{}, IC<0>{}, t - Ss) : void()), ...);
+        ((t - Ss >= tbot ? step(IC<(Ss + 1) % D>{}, IC<0>{}, t - Ss) : void()), ...);
     }(std::make_integer_sequence<int, D - 1>{});
+    if constexpr (BAND) {
+        // the products of the band's bottom step, for the band below
+        if (bd.qout) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                if (own[j]) {
+                    bd.qout[k0 + j] = qn0[0][j];
+                    bd.qout[bd.qstride + k0 + j] = qn1[0][j];
+                    bd.qout[2 * bd.qstride + k0 + j] = qn2[0][j];
+                }
+            }
+        }
+    }
 
     if (MERGE && a.dmerge) {
         // sum over the wave, one atomic add per wave and member
@@ -392,6 +452,56 @@ __global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
     const int64_t pg = idx / k.nchunks;
     const int q = static_cast<int>(idx - pg * k.nchunks);
     adj_line<T, P, G, MERGE, NT>(k, pg, q, s_edge_raw);
+}
+
+// The banded adjoint: a launch per band of kAdjBandHalo steps (counted down
+// from each direction's last step), one workgroup of kAdjBandThreads lanes,
+// two positions each, per (direction, plane, segment); a segment is
+// kAdjBandSeg positions, with a halo of kAdjBandHalo on each side.  The
+// coupling M^T moves information one position per step, so what the halo's
+// outer edge gets wrong (its outer neighbours taken as 0) reaches at most
+// kAdjBandHalo positions inwards by the band's end: the segment stays exact.
+constexpr int kAdjBandThreads = 256;
+constexpr int kAdjBandSeg = 256;
+constexpr int kAdjBandHalo = 128;
+static_assert(kAdjBandSeg + 2 * kAdjBandHalo == 2 * kAdjBandThreads, "lanes cover the segment and its halos");
+
+struct Adj4BandK {
+    Adj4K base;           // blocks[d]: planes * nseg[d], or 0 once the direction's scan has ended
+    int nseg[4];          // segments per line of each direction
+    int band;             // steps S_d - (band + 1) halo .. S_d - band halo - 1 of direction d
+    int64_t planes;       // planes per direction
+    int64_t lmax;         // floats per row of the product buffers
+    const float* qin;     // products above the band: direction d, plane p, row o at ((d planes + p) 3 + o) lmax
+    float* qout;          // those of its bottom step, same layout
+};
+
+// Band of workgroup (dir, plane p, segment sg) (shared with the host replay).
+GSPN_HD AdjBand adj_band(const Adj4BandK& k, int dir, int64_t p, int sg) {
+    const AdjK& a = k.base.d[dir];
+    AdjBand bd;
+    bd.o_lo = sg * kAdjBandSeg;
+    bd.o_hi = bd.o_lo + kAdjBandSeg < a.L ? bd.o_lo + kAdjBandSeg : a.L;
+    bd.r0 = bd.o_lo - kAdjBandHalo;
+    bd.tb_hi = a.S - k.band * kAdjBandHalo;
+    bd.tb_lo = bd.tb_hi - kAdjBandHalo > 0 ? bd.tb_hi - kAdjBandHalo : 0;
+    bd.qstride = k.lmax;
+    const int64_t off = (static_cast<int64_t>(dir) * k.planes + p) * 3 * k.lmax;
+    bd.qin = k.band == 0 ? nullptr : k.qin + off;
+    bd.qout = bd.tb_lo > 0 ? k.qout + off : nullptr;
+    return bd;
+}
+
+template <typename T, bool MERGE, bool NT>
+__global__ __launch_bounds__(kAdjBandThreads) void adj4band_kernel(const Adj4BandK k) {
+    extern __shared__ float s_edge_raw[];
+    int dir;
+    int64_t idx;
+    adj4_block(k.base, blockIdx.x, dir, idx);
+    const AdjK& a = k.base.d[dir];
+    const int64_t p = idx / k.nseg[dir];
+    const int sg = static_cast<int>(idx - p * k.nseg[dir]);
+    adj_line<T, 2, 1, MERGE, NT, true>(a, p, 0, s_edge_raw, adj_band(k, dir, p, sg));
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -556,6 +666,107 @@ static void replay_adjoint4(const Adj4K& k, int64_t nblocks, int nt, size_t lds,
     check::replayed(kn, 1024, 0);
 }
 
+static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bool merge) {
+    const char* kn = "adj4band_kernel";
+    constexpr int P = 2, D = GSPN_ADJ_BAND_DEPTH;
+    const int nt = kAdjBandThreads;
+    int64_t bad = 0, n = 0;
+    auto fail = [&](const char* what, int64_t b, int tid, int t) {
+        if (bad++ < 4) check::violation(kn, what, "block %lld thread %d step %d", static_cast<long long>(b), tid, t);
+    };
+    check::Region rx[4], rg[4], rl[4], rz[4], rh[4], rdl[4], rdz[4], rdx[4], rms[4], rdm[4];
+    for (int d = 0; d < 4; ++d) {
+        const AdjK& a = k.base.d[d];
+        rx[d] = check::region_of(a.x, kn, "x");
+        rg[d] = check::region_of(a.g, kn, "dL/dy");
+        rl[d] = check::region_of(a.lam, kn, "lambda");
+        rz[d] = check::region_of(a.z, kn, "logits");
+        rh[d] = check::region_of(a.hs, kn, "states");
+        rdl[d] = check::region_of(a.dlam, kn, "dlambda");
+        rdz[d] = check::region_of(a.dz, kn, "dlogits");
+        rdx[d] = check::region_of(a.dx, kn, "dx");
+        if (merge && a.mscale) rms[d] = check::region_of(a.mscale, kn, "merge");
+        if (merge && a.dmerge) rdm[d] = check::region_of(a.dmerge, kn, "dmerge");
+    }
+    const check::Region rqi = check::region_of(k.qin, kn, "band products in");
+    const check::Region rqo = check::region_of(k.qout, kn, "band products out");
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int dir;
+        int64_t idx;
+        adj4_block(k.base, b, dir, idx);
+        const AdjK& a = k.base.d[dir];
+        const int64_t pp = idx / k.nseg[dir];
+        const int sg = static_cast<int>(idx - pp * k.nseg[dir]);
+        const AdjBand bd = adj_band(k, dir, pp, sg);
+        const int S = a.S, L = a.L;
+        const int64_t plane = static_cast<int64_t>(S) * L;
+        const AdjGroup grp = adj_group(a, pp, 1, plane);
+        const bool rev = a.reverse != 0;
+        const int64_t pe = grp.p0 * plane * es;
+        const char* zb = static_cast<const char*>(a.z) + grp.zplane * es;
+        const float* hb = a.hs + grp.p0 * plane;
+        if (a.nchunks != 1 || bd.tb_lo >= bd.tb_hi) fail("band steps", b, -1, -1);
+        if (merge && a.mscale && !check::in_region(rms[dir], a.mscale, grp.c0 * 4, 4)) fail("merge weight", b, -1, -1);
+        if (merge && a.dmerge && !check::in_region(rdm[dir], a.dmerge, grp.c0 * 4, 4)) fail("dmerge", b, -1, -1);
+        for (int tid = 0; tid < nt; ++tid) {
+            const int k0 = bd.r0 + tid * P;
+            const int kl = adj_clamp2(k0 - 1, L), kr = adj_clamp2(k0 + P, L);
+            for (int j = 0; j < P; ++j) {
+                const int kk = adj_clamp2(k0 + j, L);
+                const bool kin = k0 + j >= 0 && k0 + j < L;
+                const bool own = kin && k0 + j >= bd.o_lo && k0 + j < bd.o_hi;
+                for (int o = 0; o < 3; ++o) {
+                    if (bd.qin && kin && !check::in_region(rqi, bd.qin, (o * bd.qstride + kk) * 4, 4))
+                        fail("band products load", b, tid, -1);
+                    if (bd.qout && own && !check::in_region(rqo, bd.qout, (o * bd.qstride + k0 + j) * 4, 4))
+                        fail("band products store", b, tid, -1);
+                }
+            }
+            for (int t = bd.tb_lo - D; t < bd.tb_hi; ++t) {
+                const AdjFill f = adj_fill(t, 0, S, L, rev);
+                for (int j = 0; j < P; ++j) {
+                    const int kk = adj_clamp2(k0 + j, L);
+                    for (int o = 0; o < 3; ++o)
+                        if (!check::in_region(rz[dir], zb, (o * plane + f.lo + kk) * es, es)) fail("logit load", b, tid, t);
+                    const int64_t e = (f.lo + kk) * es;
+                    if (!check::in_region(rg[dir], a.g, pe + e, es)) fail("dL/dy load", b, tid, t);
+                    if (!check::in_region(rx[dir], a.x, pe + e, es)) fail("x load", b, tid, t);
+                    if (!check::in_region(rl[dir], a.lam, pe + e, es)) fail("lambda load", b, tid, t);
+                    if (!check::in_region(rh[dir], hb, (f.hlo + kk) * 4, 4)) fail("state load", b, tid, t);
+                }
+                if (!check::in_region(rh[dir], hb, (f.hlo + kl) * 4, 4)) fail("left state", b, tid, t);
+                if (!check::in_region(rh[dir], hb, (f.hlo + kr) * 4, 4)) fail("right state", b, tid, t);
+                n += P * 7 + 2;
+                if (t < bd.tb_lo) continue;
+                const int64_t lo = static_cast<int64_t>(adj_row(t, S, rev)) * L;
+                for (int j = 0; j < P; ++j) {
+                    const bool own = k0 + j >= 0 && k0 + j < L && k0 + j >= bd.o_lo && k0 + j < bd.o_hi;
+                    if (!own) continue;
+                    const int64_t e = (lo + k0 + j) * es;
+                    if (!check::in_region(rdl[dir], a.dlam, pe + e, es)) fail("dlambda store", b, tid, t);
+                    if (!check::in_region(rdx[dir], a.dx, pe + e, es)) fail("dx store", b, tid, t);
+                    if (a.shared) {
+                        if (t != 0) {
+                            const int64_t ez = (grp.nidx * 3 * plane + lo + k0 + j) * 4;
+                            if (!check::in_region(rdz[dir], a.dz, ez, 4) ||
+                                !check::in_region(rdz[dir], a.dz, ez + plane * 4, 4))
+                                fail("dlogit sum atomic", b, tid, t);
+                        }
+                    } else {
+                        for (int o = 0; o < 3; ++o)
+                            if (!check::in_region(rdz[dir], a.dz, (grp.zplane + o * plane + lo + k0 + j) * es, es))
+                                fail("dlogit store", b, tid, t);
+                    }
+                    n += 5;
+                }
+            }
+        }
+    }
+    if (bad) check::violation(kn, "accesses", "%lld bad", static_cast<long long>(bad));
+    check::count_accesses(n);
+    check::replayed(kn, kAdjBandThreads, 0);
+}
+
 static void replay_elementwise(const char* kn, const char* what, const void* base, int64_t first, int64_t end, int es) {
     const check::Region r = check::region_of(base, kn, what);
     if (end > first && (!check::in_region(r, base, first * es, es) || !check::in_region(r, base, (end - 1) * es, es)))
@@ -564,6 +775,96 @@ static void replay_elementwise(const char* kn, const char* what, const void* bas
     check::count_accesses(end - first);
 }
 #endif
+
+namespace {
+
+AdjK adj_args(const AdjointParams& p) {
+    AdjK a;
+    a.x = p.x;
+    a.g = p.g;
+    a.lam = p.lam;
+    a.z = p.logits;
+    a.hs = static_cast<const float*>(p.hs);
+    a.dlam = p.dlam;
+    a.dz = p.dz;
+    a.dx = p.dx;
+    a.c = p.c;
+    a.cw = p.cw;
+    a.S = static_cast<int>(p.S);
+    a.L = static_cast<int>(p.L);
+    a.K = static_cast<int>(p.chunk);
+    a.nchunks = static_cast<int>((p.S + p.chunk - 1) / p.chunk);
+    a.reverse = p.reverse;
+    a.shared = p.shared;
+    a.mscale = p.mscale;
+    a.dmerge = p.dmerge;
+    return a;
+}
+
+constexpr int64_t kAdjBandMaxLines = 64;  // lines (planes x 4 directions) below which bands pay
+
+}  // namespace
+
+bool adjoint_band_shape(int64_t planes, int64_t h, int64_t w) {
+    return planes * 4 <= kAdjBandMaxLines && h >= 2 * kAdjBandThreads && w >= 2 * kAdjBandThreads;
+}
+
+int64_t adjoint_band_floats(int64_t planes, int64_t lmax) { return 2 * 4 * 3 * planes * lmax; }
+
+int adjoint_band_launches(const AdjointParams (&p)[4]) {
+    int64_t smax = 0;
+    for (int d = 0; d < 4; ++d) {
+        if (p[d].chunk < p[d].S) return 0;  // chunked lines run in parallel already
+        smax = p[d].S > smax ? p[d].S : smax;
+    }
+    // p[0] is vertical (S = h, L = w), p[2] horizontal (S = w, L = h)
+    if (!adjoint_band_shape(p[0].n * p[0].c, p[0].S, p[0].L)) return 0;
+    return static_cast<int>((smax + kAdjBandHalo - 1) / kAdjBandHalo);
+}
+
+hipError_t launch_adjoint4_band(const AdjointParams (&p)[4], float* qbuf, int band, hipStream_t stream) {
+    Adj4BandK k;
+    const int64_t planes = p[0].n * p[0].c;
+    int64_t lmax = 1, total = 0;
+    bool merge = false;
+    for (int d = 0; d < 4; ++d) {
+        lmax = p[d].L > lmax ? p[d].L : lmax;
+        merge = merge || p[d].mscale || p[d].dmerge;
+    }
+    for (int d = 0; d < 4; ++d) {
+        k.base.d[d] = adj_args(p[d]);
+        k.nseg[d] = static_cast<int>((p[d].L + kAdjBandSeg - 1) / kAdjBandSeg);
+        k.base.blocks[d] = p[d].S - static_cast<int64_t>(band) * kAdjBandHalo > 0 ? planes * k.nseg[d] : 0;
+        total += k.base.blocks[d];
+    }
+    k.band = band;
+    k.planes = planes;
+    k.lmax = lmax;
+    k.qin = qbuf + (band & 1) * 4 * planes * 3 * lmax;
+    k.qout = qbuf + ((band + 1) & 1) * 4 * planes * 3 * lmax;
+    const bool f32 = p[0].dtype == kF32;
+    bool nt = true;
+    for (int d = 0; d < 4; ++d) nt = nt && (p[d].L * (f32 ? 4 : 2)) % 128 == 0;
+    const size_t lds = 4 * sizeof(float) * kAdjBandThreads;
+    const dim3 grid(static_cast<unsigned>(total));
+#ifdef GSPN_CHECK_LAUNCHES
+    replay_adjoint4_band(k, total, f32 ? 4 : 2, merge);
+#endif
+#define GSPN_ADJB_LAUNCH(TT, MM)                                                                                    \
+    do {                                                                                                            \
+        if (nt) hipLaunchKernelGGL((adj4band_kernel<TT, MM, true>), grid, dim3(kAdjBandThreads), lds, stream, k);  \
+        else hipLaunchKernelGGL((adj4band_kernel<TT, MM, false>), grid, dim3(kAdjBandThreads), lds, stream, k);    \
+    } while (0)
+    if (f32) {
+        if (merge) GSPN_ADJB_LAUNCH(float, true);
+        else GSPN_ADJB_LAUNCH(float, false);
+    } else {
+        if (merge) GSPN_ADJB_LAUNCH(bf16_t, true);
+        else GSPN_ADJB_LAUNCH(bf16_t, false);
+    }
+#undef GSPN_ADJB_LAUNCH
+    return hipGetLastError();
+}
 
 hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, AdjointPlan* plan) {
     Adj4K k;

@@ -155,6 +155,18 @@ struct AdjointPlan {
 };
 hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, AdjointPlan* plan = nullptr);
 
+// The same adjoint for launches of very few long, unchunked lines: each line
+// is split across workgroups (segments with halos) and the adjoint advances
+// in bands of steps, one launch per band, bands 0 .. adjoint_band_launches
+// - 1 in order.  adjoint_band_launches: the number of bands, or 0 when this
+// path does not apply (chunked lines, more than 16 planes, sides under 512).
+// qbuf: adjoint_band_floats(n * c, max(h, w)) floats of scratch, which the
+// workspace holds whenever adjoint_band_shape(n * c, h, w).
+bool adjoint_band_shape(int64_t planes, int64_t h, int64_t w);
+int64_t adjoint_band_floats(int64_t planes, int64_t lmax);
+int adjoint_band_launches(const AdjointParams (&p)[4]);
+hipError_t launch_adjoint4_band(const AdjointParams (&p)[4], float* qbuf, int band, hipStream_t stream);
+
 // All four directions' adjoint for planes of at most 64 x 64, one workgroup
 // per plane (x, gy and dx in the array frame; the per-direction tensors in
 // each direction's scan frame; dz as in AdjointParams: the storage type, or

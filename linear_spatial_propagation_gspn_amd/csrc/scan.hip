@@ -38,6 +38,8 @@ extern template hipError_t launch_band4<float, float, true>(const BandK&, hipStr
 extern template hipError_t launch_band4<float, float, false>(const BandK&, hipStream_t);
 extern template hipError_t launch_band4<bf16_t, bf16_t, true>(const BandK&, hipStream_t);
 extern template hipError_t launch_band4<bf16_t, WPair, false>(const BandK&, hipStream_t);
+extern template hipError_t launch_band4<bf16_t, WPair, false, float>(const BandK&, hipStream_t);
+extern template hipError_t launch_band4<bf16_t, bf16_t, true, float>(const BandK&, hipStream_t);
 
 namespace {
 
@@ -188,7 +190,8 @@ int band_launches(const ScanParams (&p)[4]) {
     if (!lp_eligible(p)) return 0;
     for (int d = 0; d < 4; ++d)
         if (p[d].mscale) return 0;  // merge weights are applied after the scan (launch_combine)
-    if (p[0].odtype != -1 && p[0].odtype != p[0].dtype) return 0;
+    // outputs in the storage type, or fp32 states
+    if (p[0].odtype != -1 && p[0].odtype != p[0].dtype && p[0].odtype != kF32) return 0;
     const int span = band_positions(p[0].dtype);
     const int64_t planes = p[0].n * p[0].c;
     if (planes * 4 > kBandMaxLines) return 0;
@@ -229,6 +232,10 @@ hipError_t launch_scan4_band(const ScanParams (&p)[4], float* state, int index, 
     if (p[0].dtype == kF32) {
         return p[0].wts_are_logits ? launch_band4<float, float, true>(b, stream)
                                    : launch_band4<float, float, false>(b, stream);
+    }
+    if (p[0].odtype == kF32) {
+        if (p[0].wdtype == kPairF16) return launch_band4<bf16_t, WPair, false, float>(b, stream);
+        return launch_band4<bf16_t, bf16_t, true, float>(b, stream);
     }
     if (p[0].wdtype == kPairF16) return launch_band4<bf16_t, WPair, false>(b, stream);
     return launch_band4<bf16_t, bf16_t, true>(b, stream);

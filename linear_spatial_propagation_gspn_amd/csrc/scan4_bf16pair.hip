@@ -14,5 +14,6 @@ template hipError_t launch_fused4lp<bf16_t, WPair, false, float>(const Scan4K&, 
 
 // the banded kernel for very few long lines
 template hipError_t launch_band4<bf16_t, WPair, false>(const BandK&, hipStream_t);
+template hipError_t launch_band4<bf16_t, WPair, false, float>(const BandK&, hipStream_t);
 
 }  // namespace gspn

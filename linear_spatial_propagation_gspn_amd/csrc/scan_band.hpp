@@ -53,7 +53,9 @@ struct BandK {
 // CH: chunks restart inside the band (chunk_len below the scan length), so
 // every step checks for a chunk's first line; otherwise only step 0 of the
 // scan can be one.
-template <typename T, typename TW, bool LOGITS, bool CH>
+// TO: the stored states' type (T, or fp32 for the fp32 states a backward
+// pass reads).
+template <typename T, typename TW, bool LOGITS, bool CH, typename TO = T>
 __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p, int g) {
     const ScanK& a = b.d[dir];
     constexpr int P = 16 / static_cast<int>(sizeof(T));  // positions per lane
@@ -73,7 +75,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 
     const auto rx = lp::rsrc(static_cast<const T*>(a.x) + p * plane, plane * sizeof(T));
     const auto rl = lp::rsrc(static_cast<const T*>(a.lam) + p * plane, plane * sizeof(T));
-    const auto ro = lp::rsrc(static_cast<T*>(a.out) + p * plane, plane * sizeof(T));
+    const auto ro = lp::rsrc(static_cast<TO*>(a.out) + p * plane, plane * sizeof(TO));
     const auto rz = lp::rsrc(static_cast<const char*>(a.wts) +
                                  (PAIR ? nidx * plane : (nidx * a.cw + (a.cw == 1 ? 0 : ci)) * 3 * plane) * ZB,
                              NZ * plane * ZB);
@@ -87,6 +89,8 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
     const uint32_t vt = static_cast<uint32_t>(k0c) * sizeof(T);
     const uint32_t vw = static_cast<uint32_t>(k0c) * ZB;
     const uint32_t rowT = static_cast<uint32_t>(L) * sizeof(T);
+    const uint32_t vo = static_cast<uint32_t>(k0c) * sizeof(TO);
+    const uint32_t rowO = static_cast<uint32_t>(L) * sizeof(TO);
     const uint32_t rowW = static_cast<uint32_t>(L) * ZB;
     const uint32_t planeW = static_cast<uint32_t>(plane) * ZB;
     const bool has_l0 = k0 > 0;
@@ -106,6 +110,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
     // no clamping is needed, and the store's offset (sT) likewise.
     const uint32_t dT = rev ? 0u - rowT : rowT;
     const uint32_t dW = rev ? 0u - rowW : rowW;
+    const uint32_t dO = rev ? 0u - rowO : rowO;
     uint32_t fT = 0, fW = 0;
     auto load_slot = [&](auto slot, uint32_t oT, uint32_t oW) {
         constexpr int s = decltype(slot)::value;
@@ -133,7 +138,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 #pragma unroll
     for (int j = 0; j < P; ++j) h[j] = (t0 > 0 && active) ? hin[k0c + j] : 0.0f;
 
-    uint32_t sT = line_of(t0) * rowT;
+    uint32_t sO = line_of(t0) * rowO;
     // lambda_j x_j + c for the bf16 pair (j, j + 1) in word e: one bf16 dot
     // product with the other half of x masked to 0.  Its fp32 result can
     // differ from fmaf's by one unit in the last place (measured on gfx950:
@@ -219,20 +224,24 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
         // positions are 0 anyway
 #pragma unroll
         for (int j = 0; j < P; ++j) h[j] = (j == 0 || j == P - 1) && !active ? 0.0f : hn[j];
-        const uint32_t oT = sT;
-        sT += dT;
+        const uint32_t oO = sO;
+        sO += dO;
         if (owned) {
-            uint32_t ow[WT];
-            if constexpr (sizeof(T) == 4) {
+            constexpr int WO = P * static_cast<int>(sizeof(TO)) / 4;  // output words per lane
+            uint32_t ow[WO];
+            if constexpr (sizeof(TO) == 4) {
 #pragma unroll
-                for (int e = 0; e < WT; ++e) ow[e] = __float_as_uint(h[e]);
+                for (int e = 0; e < WO; ++e) ow[e] = __float_as_uint(h[e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < WT; ++e) ow[e] = pack_bf16x2(h[2 * e], h[2 * e + 1]);
+                for (int e = 0; e < WO; ++e) ow[e] = pack_bf16x2(h[2 * e], h[2 * e + 1]);
             }
-            const lp::int4v o = {static_cast<int>(ow[0]), static_cast<int>(ow[1]), static_cast<int>(ow[2]),
-                                 static_cast<int>(ow[3])};
-            __builtin_amdgcn_raw_buffer_store_b128(o, ro, vt, oT, GSPN_LP_STREAM_AUX);
+#pragma unroll
+            for (int v = 0; v < WO / 4; ++v) {
+                const lp::int4v o = {static_cast<int>(ow[4 * v]), static_cast<int>(ow[4 * v + 1]),
+                                     static_cast<int>(ow[4 * v + 2]), static_cast<int>(ow[4 * v + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(o, ro, vo + 16 * v, oO, GSPN_LP_STREAM_AUX);
+            }
         }
     };
 
@@ -270,7 +279,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 // segments of one line all go to the same XCD, so a segment's halo rows,
 // which its neighbours read in the same steps, come from that XCD's L2
 // (every direction active, equal segment counts, lines a multiple of 8).
-template <typename T, typename TW, bool LOGITS, bool CH>
+template <typename T, typename TW, bool LOGITS, bool CH, typename TO = T>
 __global__ __launch_bounds__(64) void scan4band_kernel(const BandK b) {
     int dir = 0;
     int64_t p;
@@ -292,22 +301,22 @@ __global__ __launch_bounds__(64) void scan4band_kernel(const BandK b) {
         p = idx / b.nseg[dir];
         g = static_cast<int>(idx - p * b.nseg[dir]);
     }
-    band_segment<T, TW, LOGITS, CH>(b, dir, p, g);
+    band_segment<T, TW, LOGITS, CH, TO>(b, dir, p, g);
 }
 
 // One band: every direction whose scan has not ended by step b.t0.
-template <typename T, typename TW, bool LOGITS>
+template <typename T, typename TW, bool LOGITS, typename TO = T>
 hipError_t launch_band4(const BandK& b, hipStream_t stream) {
     const int64_t nblocks = b.blocks[0] + b.blocks[1] + b.blocks[2] + b.blocks[3];
     if (nblocks == 0) return hipSuccess;
     bool chunked = false;
     for (int d = 0; d < 4; ++d) chunked = chunked || (b.blocks[d] > 0 && b.d[d].K < b.d[d].S);
     if (chunked) {
-        hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, true>), dim3(static_cast<unsigned>(nblocks)), dim3(64),
-                           0, stream, b);
+        hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, true, TO>), dim3(static_cast<unsigned>(nblocks)),
+                           dim3(64), 0, stream, b);
     } else {
-        hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, false>), dim3(static_cast<unsigned>(nblocks)), dim3(64),
-                           0, stream, b);
+        hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, false, TO>), dim3(static_cast<unsigned>(nblocks)),
+                           dim3(64), 0, stream, b);
     }
     return hipGetLastError();
 }

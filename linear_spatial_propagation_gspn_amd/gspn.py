@@ -63,7 +63,7 @@ class AdjointPlan(ctypes.Structure):
 
 
 # gspn_adjoint_plan.family, in order.
-ADJOINT_FAMILIES = ("none", "adj4_kernel", "adjplane_kernel")
+ADJOINT_FAMILIES = ("none", "adj4_kernel", "adjplane_kernel", "adj4band_kernel")
 
 
 class StageTimes(ctypes.Structure):

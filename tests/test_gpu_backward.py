@@ -223,3 +223,41 @@ def test_backward_full_wide_sampled_channels():
         e = oracle.normwise_error(_np(dz2[d]), rdz[d])
         _say("  dlogits %d of channels %s: normwise error %.3g" % (d, chans, e))
         assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape,shared,dtype,merge,keep", [
+    ((1, 2, 512, 640), False, "f32", False, False),
+    ((1, 3, 600, 520), True, "bf16", True, False),
+    ((2, 2, 1030, 513), True, "f32", False, True),     # states kept by the forward
+    ((1, 1, 2048, 512), False, "bf16", False, False),  # sixteen bands of the vertical scans, four of the horizontal
+])
+def test_backward_banded(shape, shared, dtype, merge, keep):
+    """Very few long unchunked lines: the adjoint runs in bands of 128 steps
+    over segments of 256 positions with 128-position halos (adj4band_kernel),
+    one launch per band, and matches the oracle's gradient."""
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, dtype, shared, 0, 700 + h + w)
+    _say("banded backward %s shared=%s %s merge=%s states=%s" % (shape, shared, dtype, merge, keep))
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 23)
+    m = None
+    if merge:
+        g = torch.Generator(device=DEV)
+        g.manual_seed(5)
+        m = torch.randn((4, c), generator=g, device=DEV, dtype=torch.float32)
+    st = None
+    if keep:
+        _, st = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], workspace=G.forward4_workspace(inp["x"], wl.cw),
+                                merge=m, states=True)
+    t = G.StageTimes()
+    got = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, merge=m, states=st, times=t)
+    torch.cuda.synchronize()
+    td = t.as_dict()
+    assert td["adjoint_plan"]["kernel"] == "adj4band_kernel", td["adjoint_plan"]
+    assert td["adjoint"]["launches"] == (max(h, w) + 127) // 128
+    ref = oracle.backward4(inp["x"], inp["logits"], inp["lam"], gy, merge=None if m is None else _np(m))
+    _check_all(got[:3], ref[:3], TOL[dtype], "all outputs")
+    if merge:
+        e = oracle.normwise_error(_np(got[3]), ref[3])
+        _say("  dmerge normwise error %.3g" % e)
+        assert e <= TOL[dtype]

@@ -45,6 +45,11 @@ CASES = [
     ("f32", (2, 3, 70, 90), False, 9),
     ("bf16", (1, 4, 100, 130), True, 0),   # shared weights as half pairs
     ("bf16", (2, 2, 72, 40), False, 7),
+    # very few long lines: the banded forward writes the states, the banded
+    # adjoint reads them (unchunked) or the one-line adjoint does (chunked)
+    ("f32", (1, 3, 512, 600), False, 0),
+    ("bf16", (1, 2, 520, 512), True, 0),
+    ("bf16", (2, 2, 512, 544), False, 100),
 ]
 
 

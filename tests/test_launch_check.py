@@ -314,3 +314,22 @@ def test_proxy_backward_stays_in_bounds(chk, case):
     assert not bad, text
     kernels = set(_kernels(text))
     assert "wgrad_reduce_kernel" in " ".join(kernels), text
+
+
+@pytest.mark.parametrize("case", [
+    dict(n=1, c=2, h=520, w=512, dtype=torch.bfloat16, shared=True, merge=True, keep_states=False),
+    dict(n=2, c=1, h=512, w=600, dtype=torch.float32, keep_states=True),
+    dict(n=1, c=3, h=700, w=530, dtype=torch.bfloat16, layout="array", keep_states=False),
+], ids=["bf16-shared-merge", "f32-states", "bf16-array"])
+def test_banded_adjoint_stays_in_bounds(chk, case):
+    """Very few long lines: the backward runs the banded adjoint (segments
+    with halos, one launch per band of steps); every band's loads, the
+    products it reads from the band above and writes for the band below,
+    and the segment's own stores stay inside their buffers."""
+    case = dict(case)
+    rf, rb = training_step(chk, case.pop("n"), case.pop("c"), case.pop("h"), case.pop("w"), **case)
+    text = report(chk)
+    assert (rf, rb) == (0, 0), text
+    bad = [l for l in text.splitlines() if l.startswith("violation") and "without a host replay" not in l]
+    assert not bad, text
+    assert "adj4band_kernel" in text and "adj4_kernel<" not in text, text
