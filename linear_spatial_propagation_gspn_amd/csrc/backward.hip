@@ -45,6 +45,8 @@ constexpr int adj_depth() { return (P == 1 && G == 1) ? 4 : 2; }
 #ifndef GSPN_ADJ_BAND_DEPTH
 #define GSPN_ADJ_BAND_DEPTH 8
 #endif
+template <int P>
+constexpr int adj_band_depth() { return P == 2 ? GSPN_ADJ_BAND_DEPTH : GSPN_ADJ_BAND_DEPTH / 2; }
 
 // channels per workgroup for channel-shared logits (fewer for two positions
 // per lane: register budget; with the learnable merge's extra state the
@@ -161,6 +163,9 @@ struct AdjBand {
 // Position k clamped into the line at both ends (band lanes may start
 // before position 0).
 GSPN_HD int adj_clamp2(int k, int L) { return k < 0 ? 0 : (k < L - 1 ? k : L - 1); }
+// First position of an aligned group of P (k and L multiples of P, L >= P)
+// clamped to the line's last group.
+GSPN_HD int adj_group_start(int k, int P, int L) { return k < 0 ? 0 : (k < L - P ? k : L - P); }
 
 // One (plane group, chunk) line of one direction.  G channels of the same
 // image run together (G > 1 only for channel-shared logits): the logits of a
@@ -188,11 +193,50 @@ __device__ __forceinline__ void st_once(T* p, float v) {
     else Store<T>::st(p, v);
 }
 
-template <typename T, int P, int G, bool MERGE, bool NT, bool BAND = false>
+// P (2 or 4) neighbouring positions in one load or store (VEC: the group
+// starts at a multiple of P in a line whose length is one, so its address
+// is aligned to the group's size).
+template <typename T, int P, bool NT>
+__device__ __forceinline__ void ld_vec(const T* p, float (&v)[P]) {
+    static_assert(P == 2 || P == 4, "pairs or quads");
+    if constexpr (sizeof(T) == 4) {
+        typedef float fv __attribute__((ext_vector_type(P)));
+        const fv q = NT ? __builtin_nontemporal_load(reinterpret_cast<const fv*>(p)) : *reinterpret_cast<const fv*>(p);
+#pragma unroll
+        for (int j = 0; j < P; ++j) v[j] = q[j];
+    } else {
+        typedef uint32_t uv __attribute__((ext_vector_type(P / 2)));
+        const uv q = NT ? __builtin_nontemporal_load(reinterpret_cast<const uv*>(p)) : *reinterpret_cast<const uv*>(p);
+#pragma unroll
+        for (int j = 0; j < P; ++j) v[j] = __uint_as_float((j & 1) ? (q[j >> 1] & 0xffff0000u) : (q[j >> 1] << 16));
+    }
+}
+template <typename T, int P, bool NT>
+__device__ __forceinline__ void st_vec(T* p, const float (&v)[P]) {
+    static_assert(P == 2 || P == 4, "pairs or quads");
+    if constexpr (sizeof(T) == 4) {
+        typedef float fv __attribute__((ext_vector_type(P)));
+        fv q;
+#pragma unroll
+        for (int j = 0; j < P; ++j) q[j] = v[j];
+        if constexpr (NT) __builtin_nontemporal_store(q, reinterpret_cast<fv*>(p));
+        else *reinterpret_cast<fv*>(p) = q;
+    } else {
+        typedef uint32_t uv __attribute__((ext_vector_type(P / 2)));
+        uv q;
+#pragma unroll
+        for (int j = 0; j < P / 2; ++j) q[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        if constexpr (NT) __builtin_nontemporal_store(q, reinterpret_cast<uv*>(p));
+        else *reinterpret_cast<uv*>(p) = q;
+    }
+}
+
+template <typename T, int P, int G, bool MERGE, bool NT, bool BAND = false, bool VEC = false>
 __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float* edge_raw,
                                          const AdjBand& bd = AdjBand{}) {
     static_assert(!BAND || G == 1, "bands run one channel per workgroup");
-    constexpr int D = BAND ? GSPN_ADJ_BAND_DEPTH : adj_depth<P, G>();
+    static_assert(!VEC || (BAND && (P == 2 || P == 4)), "pairs or quads of positions in the banded adjoint");
+    constexpr int D = BAND ? adj_band_depth<P>() : adj_depth<P, G>();
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
     const int S = a.S;
@@ -239,6 +283,8 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
     // left neighbour of the first position, right one of the last (clamped)
     const int kl = BAND ? adj_clamp2(k0 - 1, L) : adj_left(k0, L);
     const int kr = BAND ? adj_clamp2(k0 + P, L) : adj_right(k0, P, L);
+    // VEC: the group's first position, clamped to the line's last group
+    const int kp = adj_group_start(k0, P, L);
 
     const int t0 = q * a.K;
     const int t1 = min(t0 + a.K, S);
@@ -255,6 +301,20 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
         const AdjFill f = adj_fill(t, t0, S, L, rev);
         const int64_t lo = f.lo;
         const int64_t hlo = f.hlo;  // h_{t-1} (clamped)
+        if constexpr (VEC) {
+#pragma unroll
+            for (int o = 0; o < 3; ++o) ld_vec<T, P, NT>(zp + o * plane + lo + kp, rz[s][o]);
+            ld_vec<T, P, NT>(gp + lo + kp, rg[s][0]);
+            ld_vec<T, P, NT>(xp + lo + kp, rx[s][0]);
+            ld_vec<T, P, NT>(lp + lo + kp, rl[s][0]);
+            float hv[P];
+            ld_vec<float, P, false>(hp + hlo + kp, hv);
+#pragma unroll
+            for (int j = 0; j < P; ++j) rh[s][0][j + 1] = hv[j];
+            rh[s][0][0] = hp[hlo + kl];
+            rh[s][0][P + 1] = hp[hlo + kr];
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < P; ++j) {
 #pragma unroll
@@ -324,6 +384,20 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 a_t[j] = (kin[j] && gok[g]) ? v : 0.0f;
             }
             const int64_t go = gc[g] * plane;
+            if constexpr (VEC) {
+                // the group's positions are all the segment's, or none
+                float vl[P], vd[P];
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const float m = MERGE ? a_t[j] * msc[0] : a_t[j];
+                    vl[j] = m * rx[s][0][j];
+                    vd[j] = m * rl[s][0][j];
+                }
+                if (own[0]) {
+                    st_vec<T, P, NT>(dlp + lo + k0, vl);
+                    st_vec<T, P, NT>(dxp + lo + k0, vd);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 float am = a_t[j];
@@ -331,7 +405,7 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                     am = a_t[j] * msc[g];  // the adjoint of the merged output
                     if (!BAND || own[j]) dm[g] = __builtin_fmaf(a_t[j], rl[s][g][j] * rx[s][g][j], dm[g]);
                 }
-                if (own[j] && gok[g]) {
+                if (!VEC && own[j] && gok[g]) {
                     st_once<T, NT>(dlp + go + lo + k0 + j, am * rx[s][g][j]);
                     st_once<T, NT>(dxp + go + lo + k0 + j, am * rl[s][g][j]);
                 }
@@ -359,9 +433,11 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 }
             }
         } else {
+            float dzv[P][3];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                float dz[3] = {0.0f, 0.0f, 0.0f};
+                float* dz = dzv[j];
+                dz[0] = dz[1] = dz[2] = 0.0f;
                 if (!first) {
                     const float dot = (dw[j][0] * w[0][j] + dw[j][1] * w[1][j]) + dw[j][2] * w[2][j];
 #pragma unroll
@@ -370,10 +446,22 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                     if (k0 + j + 1 >= L) dz[2] = 0.0f;
                     if (L == 1) dz[1] = 0.0f;  // a single neighbour: w = [1] whatever its logit
                 }
-                if (own[j]) {
+                if (!VEC && own[j]) {
                     T* dzp = static_cast<T*>(a.dz) + zplane;
 #pragma unroll
                     for (int o = 0; o < 3; ++o) st_once<T, NT>(dzp + o * plane + lo + k0 + j, dz[o]);
+                }
+            }
+            if constexpr (VEC) {
+                if (own[0]) {
+                    T* dzp = static_cast<T*>(a.dz) + zplane;
+#pragma unroll
+                    for (int o = 0; o < 3; ++o) {
+                        float v[P];
+#pragma unroll
+                        for (int j = 0; j < P; ++j) v[j] = dzv[j][o];
+                        st_vec<T, P, NT>(dzp + o * plane + lo + k0, v);
+                    }
                 }
             }
         }
@@ -461,10 +549,10 @@ __global__ __launch_bounds__(1024) void adj4_kernel(const Adj4K a) {
 // coupling M^T moves information one position per step, so what the halo's
 // outer edge gets wrong (its outer neighbours taken as 0) reaches at most
 // kAdjBandHalo positions inwards by the band's end: the segment stays exact.
-constexpr int kAdjBandThreads = 256;
 constexpr int kAdjBandSeg = 256;
 constexpr int kAdjBandHalo = 128;
-static_assert(kAdjBandSeg + 2 * kAdjBandHalo == 2 * kAdjBandThreads, "lanes cover the segment and its halos");
+constexpr int kAdjBandSpan = kAdjBandSeg + 2 * kAdjBandHalo;  // positions of a workgroup
+constexpr int kAdjBandThreads = kAdjBandSpan / 2;            // lanes with two positions each (four: half)
 
 struct Adj4BandK {
     Adj4K base;           // blocks[d]: planes * nseg[d], or 0 once the direction's scan has ended
@@ -492,7 +580,9 @@ GSPN_HD AdjBand adj_band(const Adj4BandK& k, int dir, int64_t p, int sg) {
     return bd;
 }
 
-template <typename T, bool MERGE, bool NT>
+// VEC: every line's length a multiple of P and every tensor aligned to P
+// elements: each lane loads and stores its P positions as one vector.
+template <typename T, bool MERGE, bool NT, bool VEC, int P>
 __global__ __launch_bounds__(kAdjBandThreads) void adj4band_kernel(const Adj4BandK k) {
     extern __shared__ float s_edge_raw[];
     int dir;
@@ -501,7 +591,7 @@ __global__ __launch_bounds__(kAdjBandThreads) void adj4band_kernel(const Adj4Ban
     const AdjK& a = k.base.d[dir];
     const int64_t p = idx / k.nseg[dir];
     const int sg = static_cast<int>(idx - p * k.nseg[dir]);
-    adj_line<T, 2, 1, MERGE, NT, true>(a, p, 0, s_edge_raw, adj_band(k, dir, p, sg));
+    adj_line<T, P, 1, MERGE, NT, true, VEC>(a, p, 0, s_edge_raw, adj_band(k, dir, p, sg));
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -666,10 +756,10 @@ static void replay_adjoint4(const Adj4K& k, int64_t nblocks, int nt, size_t lds,
     check::replayed(kn, 1024, 0);
 }
 
-static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bool merge) {
+static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bool merge, bool vec, int P) {
     const char* kn = "adj4band_kernel";
-    constexpr int P = 2, D = GSPN_ADJ_BAND_DEPTH;
-    const int nt = kAdjBandThreads;
+    const int D = P == 2 ? adj_band_depth<2>() : adj_band_depth<4>();
+    const int nt = kAdjBandSpan / P;
     int64_t bad = 0, n = 0;
     auto fail = [&](const char* what, int64_t b, int tid, int t) {
         if (bad++ < 4) check::violation(kn, what, "block %lld thread %d step %d", static_cast<long long>(b), tid, t);
@@ -722,10 +812,12 @@ static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bo
                         fail("band products store", b, tid, -1);
                 }
             }
+            const int kp = adj_group_start(k0, P, L);
+            if (vec && (k0 % P != 0 || L % P != 0)) fail("group alignment", b, tid, -1);
             for (int t = bd.tb_lo - D; t < bd.tb_hi; ++t) {
                 const AdjFill f = adj_fill(t, 0, S, L, rev);
                 for (int j = 0; j < P; ++j) {
-                    const int kk = adj_clamp2(k0 + j, L);
+                    const int kk = vec ? kp + j : adj_clamp2(k0 + j, L);
                     for (int o = 0; o < 3; ++o)
                         if (!check::in_region(rz[dir], zb, (o * plane + f.lo + kk) * es, es)) fail("logit load", b, tid, t);
                     const int64_t e = (f.lo + kk) * es;
@@ -764,7 +856,7 @@ static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bo
     }
     if (bad) check::violation(kn, "accesses", "%lld bad", static_cast<long long>(bad));
     check::count_accesses(n);
-    check::replayed(kn, kAdjBandThreads, 0);
+    check::replayed(kn, nt, 0);
 }
 
 static void replay_elementwise(const char* kn, const char* what, const void* base, int64_t first, int64_t end, int es) {
@@ -845,15 +937,41 @@ hipError_t launch_adjoint4_band(const AdjointParams (&p)[4], float* qbuf, int ba
     const bool f32 = p[0].dtype == kF32;
     bool nt = true;
     for (int d = 0; d < 4; ++d) nt = nt && (p[d].L * (f32 ? 4 : 2)) % 128 == 0;
-    const size_t lds = 4 * sizeof(float) * kAdjBandThreads;
     const dim3 grid(static_cast<unsigned>(total));
+    // groups of P positions a lane: lines whose lengths are multiples of P,
+    // every tensor aligned to P elements (quads, else pairs, else one
+    // position at a time, two a lane)
+    auto vec_ok = [&](int P) {
+        const size_t al = static_cast<size_t>(P) * (f32 ? 4 : 2);
+        bool ok = true;
+        for (int d = 0; d < 4; ++d) {
+            const AdjointParams& q = p[d];
+            ok = ok && q.L % P == 0 && q.L >= P && reinterpret_cast<uintptr_t>(q.x) % al == 0 &&
+                 reinterpret_cast<uintptr_t>(q.g) % al == 0 && reinterpret_cast<uintptr_t>(q.lam) % al == 0 &&
+                 reinterpret_cast<uintptr_t>(q.logits) % al == 0 && reinterpret_cast<uintptr_t>(q.dlam) % al == 0 &&
+                 reinterpret_cast<uintptr_t>(q.dx) % al == 0 && reinterpret_cast<uintptr_t>(q.hs) % (4 * P) == 0 &&
+                 (q.shared || reinterpret_cast<uintptr_t>(q.dz) % al == 0);
+        }
+        return ok;
+    };
+    // (quads on workgroups of half the lanes measured slower: the proxy
+    // backward's adjoint 3.9 against 1.9 ms)
+    const int P = 2;
+    const bool vec = vec_ok(2);
+    const int threads = kAdjBandSpan / P;
+    const size_t lds = 4 * sizeof(float) * threads;
 #ifdef GSPN_CHECK_LAUNCHES
-    replay_adjoint4_band(k, total, f32 ? 4 : 2, merge);
+    replay_adjoint4_band(k, total, f32 ? 4 : 2, merge, vec, P);
 #endif
-#define GSPN_ADJB_LAUNCH(TT, MM)                                                                                    \
-    do {                                                                                                            \
-        if (nt) hipLaunchKernelGGL((adj4band_kernel<TT, MM, true>), grid, dim3(kAdjBandThreads), lds, stream, k);  \
-        else hipLaunchKernelGGL((adj4band_kernel<TT, MM, false>), grid, dim3(kAdjBandThreads), lds, stream, k);    \
+#define GSPN_ADJB_LAUNCH2(TT, MM, VV, PP)                                                                         \
+    do {                                                                                                          \
+        if (nt) hipLaunchKernelGGL((adj4band_kernel<TT, MM, true, VV, PP>), grid, dim3(threads), lds, stream, k);  \
+        else hipLaunchKernelGGL((adj4band_kernel<TT, MM, false, VV, PP>), grid, dim3(threads), lds, stream, k);    \
+    } while (0)
+#define GSPN_ADJB_LAUNCH(TT, MM)                          \
+    do {                                                  \
+        if (vec) GSPN_ADJB_LAUNCH2(TT, MM, true, 2);         \
+        else GSPN_ADJB_LAUNCH2(TT, MM, false, 2);            \
     } while (0)
     if (f32) {
         if (merge) GSPN_ADJB_LAUNCH(float, true);
@@ -863,6 +981,7 @@ hipError_t launch_adjoint4_band(const AdjointParams (&p)[4], float* qbuf, int ba
         else GSPN_ADJB_LAUNCH(bf16_t, false);
     }
 #undef GSPN_ADJB_LAUNCH
+#undef GSPN_ADJB_LAUNCH2
     return hipGetLastError();
 }
 

@@ -182,7 +182,7 @@ namespace {
 constexpr int64_t kBandMaxLines = 64;  // lines (planes x 4 directions) below which it pays
 constexpr int kBandMaxLaunches = 32;
 
-int band_positions(int dtype) { return 64 * (dtype == kF32 ? 4 : 8); }
+int band_positions(int dtype) { return 64 * GSPN_BAND_BYTES / (dtype == kF32 ? 4 : 2); }
 
 }  // namespace
 
@@ -208,7 +208,7 @@ int band_launches(const ScanParams (&p)[4]) {
 int64_t band_state_floats(int64_t planes, int64_t lmax) { return 2 * 4 * planes * lmax; }
 
 hipError_t launch_scan4_band(const ScanParams (&p)[4], float* state, int index, hipStream_t stream) {
-    const int P = p[0].dtype == kF32 ? 4 : 8;
+    const int P = GSPN_BAND_BYTES / (p[0].dtype == kF32 ? 4 : 2);
     const int span = band_positions(p[0].dtype);
     const int64_t planes = p[0].n * p[0].c;
     BandK b;

@@ -10,10 +10,11 @@
 // inputs.  Here a line is cut into segments of `seg` positions, one
 // single-wave workgroup per segment, and the scan advances in bands of
 // `halo` steps, one launch per band:
-//  - a workgroup is one wave of 16-byte vectors (8 bf16 or 4 fp32 positions
-//    per lane): its segment of half those positions plus `halo`, a quarter,
-//    on each side (the line borders clip this), starting from the exact
-//    states at the band's first step, which the previous band stored;
+//  - a workgroup is one wave of GSPN_BAND_BYTES-byte vectors (8 bf16 or 4
+//    fp32 positions per lane at 16 bytes): its segment of half those
+//    positions plus `halo`, a quarter, on each side (the line borders clip
+//    this), starting from the exact states at the band's first step, which
+//    the previous band stored;
 //  - the tridiagonal coupling moves information one position per step, so
 //    the values that the halo's outer edge gets wrong (its outer neighbours
 //    are taken as 0) reach at most `halo` positions inwards by the band's
@@ -33,6 +34,53 @@ namespace gspn {
 #ifndef GSPN_BAND_DEPTH
 #define GSPN_BAND_DEPTH 12
 #endif
+// bytes of each row a lane loads per step (its positions: this over the
+// element size)
+#ifndef GSPN_BAND_BYTES
+#define GSPN_BAND_BYTES 16
+#endif
+
+namespace band {
+
+// W 32-bit words from the buffer at voff + soff, in the widest loads W allows.
+template <int W, int AUX = 0>
+__device__ __forceinline__ void load_words(uint32_t (&d)[W], __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                           uint32_t soff) {
+    if constexpr (W % 4 == 0) {
+        lp::load_words<W, AUX>(d, r, voff, soff);
+    } else if constexpr (W == 2) {
+        typedef int int2v __attribute__((ext_vector_type(2)));
+        const int2v q = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
+        d[0] = static_cast<uint32_t>(q[0]);
+        d[1] = static_cast<uint32_t>(q[1]);
+    } else {
+        static_assert(W == 1, "1, 2 or a multiple of 4 words");
+        d[0] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+    }
+}
+
+// W 32-bit words to the buffer at voff + soff.
+template <int W, int AUX = 0>
+__device__ __forceinline__ void store_words(const uint32_t (&w)[W], __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                            uint32_t soff) {
+    if constexpr (W % 4 == 0) {
+#pragma unroll
+        for (int v = 0; v < W / 4; ++v) {
+            const lp::int4v o = {static_cast<int>(w[4 * v]), static_cast<int>(w[4 * v + 1]),
+                                 static_cast<int>(w[4 * v + 2]), static_cast<int>(w[4 * v + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(o, r, voff + 16 * v, soff, AUX);
+        }
+    } else if constexpr (W == 2) {
+        typedef int int2v __attribute__((ext_vector_type(2)));
+        const int2v o = {static_cast<int>(w[0]), static_cast<int>(w[1])};
+        __builtin_amdgcn_raw_buffer_store_b64(o, r, voff, soff, AUX);
+    } else {
+        static_assert(W == 1, "1, 2 or a multiple of 4 words");
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(w[0]), r, voff, soff, AUX);
+    }
+}
+
+}  // namespace band
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -58,7 +106,7 @@ struct BandK {
 template <typename T, typename TW, bool LOGITS, bool CH, typename TO = T>
 __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p, int g) {
     const ScanK& a = b.d[dir];
-    constexpr int P = 16 / static_cast<int>(sizeof(T));  // positions per lane
+    constexpr int P = GSPN_BAND_BYTES / static_cast<int>(sizeof(T));  // positions per lane
     constexpr int WT = P * static_cast<int>(sizeof(T)) / 4;
     constexpr bool PAIR = std::is_same_v<TW, WPair>;
     constexpr int ZB = PAIR ? 4 : static_cast<int>(sizeof(TW));
@@ -114,11 +162,11 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
     uint32_t fT = 0, fW = 0;
     auto load_slot = [&](auto slot, uint32_t oT, uint32_t oW) {
         constexpr int s = decltype(slot)::value;
-        lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, oT);
-        lp::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, oT);
+        band::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, oT);
+        band::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, oT);
         constexpr int ZAUX = LOGITS ? GSPN_LP_STREAM_AUX : 0;
 #pragma unroll
-        for (int o = 0; o < NZ; ++o) lp::load_words<WW, ZAUX>(sz[s][o], rz, vw, o * planeW + oW);
+        for (int o = 0; o < NZ; ++o) band::load_words<WW, ZAUX>(sz[s][o], rz, vw, o * planeW + oW);
     };
     // step t's inputs, the row clamped to the band (rows past it are never used)
     auto fill = [&](auto slot, int t) {
@@ -236,12 +284,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 #pragma unroll
                 for (int e = 0; e < WO; ++e) ow[e] = pack_bf16x2(h[2 * e], h[2 * e + 1]);
             }
-#pragma unroll
-            for (int v = 0; v < WO / 4; ++v) {
-                const lp::int4v o = {static_cast<int>(ow[4 * v]), static_cast<int>(ow[4 * v + 1]),
-                                     static_cast<int>(ow[4 * v + 2]), static_cast<int>(ow[4 * v + 3])};
-                __builtin_amdgcn_raw_buffer_store_b128(o, ro, vo + 16 * v, oO, GSPN_LP_STREAM_AUX);
-            }
+            band::store_words<WO, GSPN_LP_STREAM_AUX>(ow, ro, vo, oO);
         }
     };
 
