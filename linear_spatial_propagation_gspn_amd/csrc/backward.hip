@@ -45,8 +45,17 @@ constexpr int adj_depth() { return (P == 1 && G == 1) ? 4 : 2; }
 #ifndef GSPN_ADJ_BAND_DEPTH
 #define GSPN_ADJ_BAND_DEPTH 8
 #endif
-template <int P>
-constexpr int adj_band_depth() { return P == 2 ? GSPN_ADJ_BAND_DEPTH : GSPN_ADJ_BAND_DEPTH / 2; }
+template <int P, int G>
+constexpr int adj_band_depth() { return GSPN_ADJ_BAND_DEPTH * 2 / (P * G) > 1 ? GSPN_ADJ_BAND_DEPTH * 2 / (P * G) : 2; }
+
+// channels one banded workgroup runs together for channel-shared logits
+// (their logit gradient summed in registers before its atomic adds).  One:
+// groups of 2 and 4 halve and quarter the workgroups and the steps in
+// flight, and measured slower (proxy-space adjoint 2.18 and 3.16 ms against
+// 1.85) for all the atomics they save.
+#ifndef GSPN_ADJ_BAND_G
+#define GSPN_ADJ_BAND_G 1
+#endif
 
 // channels per workgroup for channel-shared logits (fewer for two positions
 // per lane: register budget; with the learnable merge's extra state the
@@ -155,7 +164,8 @@ GSPN_HD AdjFill adj_fill(int t, int t0, int S, int L, bool rev) {
 // positions store anything.
 struct AdjBand {
     int r0, o_lo, o_hi, tb_lo, tb_hi;
-    int64_t qstride;
+    int64_t qstride;  // floats between the rows o of one channel's products
+    int64_t mstride;  // floats between the products of consecutive channels
     const float* qin;
     float* qout;
 };
@@ -234,9 +244,8 @@ __device__ __forceinline__ void st_vec(T* p, const float (&v)[P]) {
 template <typename T, int P, int G, bool MERGE, bool NT, bool BAND = false, bool VEC = false>
 __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float* edge_raw,
                                          const AdjBand& bd = AdjBand{}) {
-    static_assert(!BAND || G == 1, "bands run one channel per workgroup");
     static_assert(!VEC || (BAND && (P == 2 || P == 4)), "pairs or quads of positions in the banded adjoint");
-    constexpr int D = BAND ? adj_band_depth<P>() : adj_depth<P, G>();
+    constexpr int D = BAND ? adj_band_depth<P, G>() : adj_depth<P, G>();
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
     const int S = a.S;
@@ -304,15 +313,19 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
         if constexpr (VEC) {
 #pragma unroll
             for (int o = 0; o < 3; ++o) ld_vec<T, P, NT>(zp + o * plane + lo + kp, rz[s][o]);
-            ld_vec<T, P, NT>(gp + lo + kp, rg[s][0]);
-            ld_vec<T, P, NT>(xp + lo + kp, rx[s][0]);
-            ld_vec<T, P, NT>(lp + lo + kp, rl[s][0]);
-            float hv[P];
-            ld_vec<float, P, false>(hp + hlo + kp, hv);
 #pragma unroll
-            for (int j = 0; j < P; ++j) rh[s][0][j + 1] = hv[j];
-            rh[s][0][0] = hp[hlo + kl];
-            rh[s][0][P + 1] = hp[hlo + kr];
+            for (int g = 0; g < G; ++g) {
+                const int64_t go = gc[g] * plane;
+                ld_vec<T, P, NT>(gp + go + lo + kp, rg[s][g]);
+                ld_vec<T, P, NT>(xp + go + lo + kp, rx[s][g]);
+                ld_vec<T, P, NT>(lp + go + lo + kp, rl[s][g]);
+                float hv[P];
+                ld_vec<float, P, false>(hp + go + hlo + kp, hv);
+#pragma unroll
+                for (int j = 0; j < P; ++j) rh[s][g][j + 1] = hv[j];
+                rh[s][g][0] = hp[go + hlo + kl];
+                rh[s][g][P + 1] = hp[go + hlo + kr];
+            }
             return;
         }
 #pragma unroll
@@ -389,13 +402,13 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
                 float vl[P], vd[P];
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
-                    const float m = MERGE ? a_t[j] * msc[0] : a_t[j];
-                    vl[j] = m * rx[s][0][j];
-                    vd[j] = m * rl[s][0][j];
+                    const float m = MERGE ? a_t[j] * msc[g] : a_t[j];
+                    vl[j] = m * rx[s][g][j];
+                    vd[j] = m * rl[s][g][j];
                 }
-                if (own[0]) {
-                    st_vec<T, P, NT>(dlp + lo + k0, vl);
-                    st_vec<T, P, NT>(dxp + lo + k0, vd);
+                if (own[0] && gok[g]) {
+                    st_vec<T, P, NT>(dlp + go + lo + k0, vl);
+                    st_vec<T, P, NT>(dxp + go + lo + k0, vd);
                 }
             }
 #pragma unroll
@@ -482,14 +495,18 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
         // the products of the step above the band (none above the chunk's
         // last step), published to the neighbours like a step's own
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const bool have = bd.qin != nullptr && kin[j];
-            qn0[0][j] = have ? bd.qin[kk[j]] : 0.0f;
-            qn1[0][j] = have ? bd.qin[bd.qstride + kk[j]] : 0.0f;
-            qn2[0][j] = have ? bd.qin[2 * bd.qstride + kk[j]] : 0.0f;
+        for (int g = 0; g < G; ++g) {
+            const float* qi = bd.qin + g * bd.mstride;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const bool have = bd.qin != nullptr && kin[j] && gok[g];
+                qn0[g][j] = have ? qi[kk[j]] : 0.0f;
+                qn1[g][j] = have ? qi[bd.qstride + kk[j]] : 0.0f;
+                qn2[g][j] = have ? qi[2 * bd.qstride + kk[j]] : 0.0f;
+            }
+            edge(buf, 0, g, tid) = qn0[g][0];
+            edge(buf, 1, g, tid) = qn2[g][P - 1];
         }
-        edge(buf, 0, 0, tid) = qn0[0][0];
-        edge(buf, 1, 0, tid) = qn2[0][P - 1];
         __syncthreads();
         step(IC<0>{}, IC<0>{}, ttop - 1);
     } else {
@@ -508,11 +525,15 @@ __device__ __forceinline__ void adj_line(const AdjK& a, int64_t pg, int q, float
         // the products of the band's bottom step, for the band below
         if (bd.qout) {
 #pragma unroll
-            for (int j = 0; j < P; ++j) {
-                if (own[j]) {
-                    bd.qout[k0 + j] = qn0[0][j];
-                    bd.qout[bd.qstride + k0 + j] = qn1[0][j];
-                    bd.qout[2 * bd.qstride + k0 + j] = qn2[0][j];
+            for (int g = 0; g < G; ++g) {
+                float* qo = bd.qout + g * bd.mstride;
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    if (own[j] && gok[g]) {
+                        qo[k0 + j] = qn0[g][j];
+                        qo[bd.qstride + k0 + j] = qn1[g][j];
+                        qo[2 * bd.qstride + k0 + j] = qn2[g][j];
+                    }
                 }
             }
         }
@@ -564,7 +585,8 @@ struct Adj4BandK {
     float* qout;          // those of its bottom step, same layout
 };
 
-// Band of workgroup (dir, plane p, segment sg) (shared with the host replay).
+// Band of workgroup (dir, first plane p of its channel group, segment sg)
+// (shared with the host replay).
 GSPN_HD AdjBand adj_band(const Adj4BandK& k, int dir, int64_t p, int sg) {
     const AdjK& a = k.base.d[dir];
     AdjBand bd;
@@ -574,6 +596,7 @@ GSPN_HD AdjBand adj_band(const Adj4BandK& k, int dir, int64_t p, int sg) {
     bd.tb_hi = a.S - k.band * kAdjBandHalo;
     bd.tb_lo = bd.tb_hi - kAdjBandHalo > 0 ? bd.tb_hi - kAdjBandHalo : 0;
     bd.qstride = k.lmax;
+    bd.mstride = 3 * k.lmax;
     const int64_t off = (static_cast<int64_t>(dir) * k.planes + p) * 3 * k.lmax;
     bd.qin = k.band == 0 ? nullptr : k.qin + off;
     bd.qout = bd.tb_lo > 0 ? k.qout + off : nullptr;
@@ -582,16 +605,17 @@ GSPN_HD AdjBand adj_band(const Adj4BandK& k, int dir, int64_t p, int sg) {
 
 // VEC: every line's length a multiple of P and every tensor aligned to P
 // elements: each lane loads and stores its P positions as one vector.
-template <typename T, bool MERGE, bool NT, bool VEC, int P>
+template <typename T, bool MERGE, bool NT, bool VEC, int P, int G>
 __global__ __launch_bounds__(kAdjBandThreads) void adj4band_kernel(const Adj4BandK k) {
     extern __shared__ float s_edge_raw[];
     int dir;
     int64_t idx;
     adj4_block(k.base, blockIdx.x, dir, idx);
     const AdjK& a = k.base.d[dir];
-    const int64_t p = idx / k.nseg[dir];
-    const int sg = static_cast<int>(idx - p * k.nseg[dir]);
-    adj_line<T, P, 1, MERGE, NT, true, VEC>(a, p, 0, s_edge_raw, adj_band(k, dir, p, sg));
+    const int64_t pg = idx / k.nseg[dir];  // channel group
+    const int sg = static_cast<int>(idx - pg * k.nseg[dir]);
+    const int64_t plane = static_cast<int64_t>(a.S) * a.L;
+    adj_line<T, P, G, MERGE, NT, true, VEC>(a, pg, 0, s_edge_raw, adj_band(k, dir, adj_group(a, pg, G, plane).p0, sg));
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -756,9 +780,9 @@ static void replay_adjoint4(const Adj4K& k, int64_t nblocks, int nt, size_t lds,
     check::replayed(kn, 1024, 0);
 }
 
-static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bool merge, bool vec, int P) {
+static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bool merge, bool vec, int P, int G) {
     const char* kn = "adj4band_kernel";
-    const int D = P == 2 ? adj_band_depth<2>() : adj_band_depth<4>();
+    const int D = G == 1 ? adj_band_depth<2, 1>() : adj_band_depth<2, GSPN_ADJ_BAND_G>();
     const int nt = kAdjBandSpan / P;
     int64_t bad = 0, n = 0;
     auto fail = [&](const char* what, int64_t b, int tid, int t) {
@@ -785,31 +809,41 @@ static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bo
         int64_t idx;
         adj4_block(k.base, b, dir, idx);
         const AdjK& a = k.base.d[dir];
-        const int64_t pp = idx / k.nseg[dir];
-        const int sg = static_cast<int>(idx - pp * k.nseg[dir]);
-        const AdjBand bd = adj_band(k, dir, pp, sg);
+        const int64_t pg = idx / k.nseg[dir];
+        const int sg = static_cast<int>(idx - pg * k.nseg[dir]);
         const int S = a.S, L = a.L;
         const int64_t plane = static_cast<int64_t>(S) * L;
-        const AdjGroup grp = adj_group(a, pp, 1, plane);
+        const AdjGroup grp = adj_group(a, pg, G, plane);
+        const AdjBand bd = adj_band(k, dir, grp.p0, sg);
         const bool rev = a.reverse != 0;
         const int64_t pe = grp.p0 * plane * es;
         const char* zb = static_cast<const char*>(a.z) + grp.zplane * es;
         const float* hb = a.hs + grp.p0 * plane;
         if (a.nchunks != 1 || bd.tb_lo >= bd.tb_hi) fail("band steps", b, -1, -1);
-        if (merge && a.mscale && !check::in_region(rms[dir], a.mscale, grp.c0 * 4, 4)) fail("merge weight", b, -1, -1);
-        if (merge && a.dmerge && !check::in_region(rdm[dir], a.dmerge, grp.c0 * 4, 4)) fail("dmerge", b, -1, -1);
+        for (int g = 0; g < G; ++g) {
+            const bool ok = adj_member_ok(a, grp.c0, g);
+            const int64_t c = grp.c0 + adj_member(a, grp.c0, g);
+            if (merge && a.mscale && !check::in_region(rms[dir], a.mscale, c * 4, 4)) fail("merge weight", b, -1, -1);
+            if (merge && a.dmerge && ok && !check::in_region(rdm[dir], a.dmerge, (grp.c0 + g) * 4, 4))
+                fail("dmerge", b, -1, -1);
+        }
         for (int tid = 0; tid < nt; ++tid) {
             const int k0 = bd.r0 + tid * P;
             const int kl = adj_clamp2(k0 - 1, L), kr = adj_clamp2(k0 + P, L);
-            for (int j = 0; j < P; ++j) {
-                const int kk = adj_clamp2(k0 + j, L);
-                const bool kin = k0 + j >= 0 && k0 + j < L;
-                const bool own = kin && k0 + j >= bd.o_lo && k0 + j < bd.o_hi;
-                for (int o = 0; o < 3; ++o) {
-                    if (bd.qin && kin && !check::in_region(rqi, bd.qin, (o * bd.qstride + kk) * 4, 4))
-                        fail("band products load", b, tid, -1);
-                    if (bd.qout && own && !check::in_region(rqo, bd.qout, (o * bd.qstride + k0 + j) * 4, 4))
-                        fail("band products store", b, tid, -1);
+            for (int g = 0; g < G; ++g) {
+                if (!adj_member_ok(a, grp.c0, g)) continue;
+                for (int j = 0; j < P; ++j) {
+                    const int kk = adj_clamp2(k0 + j, L);
+                    const bool kin = k0 + j >= 0 && k0 + j < L;
+                    const bool own = kin && k0 + j >= bd.o_lo && k0 + j < bd.o_hi;
+                    for (int o = 0; o < 3; ++o) {
+                        if (bd.qin && kin &&
+                            !check::in_region(rqi, bd.qin, (g * bd.mstride + o * bd.qstride + kk) * 4, 4))
+                            fail("band products load", b, tid, -1);
+                        if (bd.qout && own &&
+                            !check::in_region(rqo, bd.qout, (g * bd.mstride + o * bd.qstride + k0 + j) * 4, 4))
+                            fail("band products store", b, tid, -1);
+                    }
                 }
             }
             const int kp = adj_group_start(k0, P, L);
@@ -820,23 +854,32 @@ static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bo
                     const int kk = vec ? kp + j : adj_clamp2(k0 + j, L);
                     for (int o = 0; o < 3; ++o)
                         if (!check::in_region(rz[dir], zb, (o * plane + f.lo + kk) * es, es)) fail("logit load", b, tid, t);
-                    const int64_t e = (f.lo + kk) * es;
-                    if (!check::in_region(rg[dir], a.g, pe + e, es)) fail("dL/dy load", b, tid, t);
-                    if (!check::in_region(rx[dir], a.x, pe + e, es)) fail("x load", b, tid, t);
-                    if (!check::in_region(rl[dir], a.lam, pe + e, es)) fail("lambda load", b, tid, t);
-                    if (!check::in_region(rh[dir], hb, (f.hlo + kk) * 4, 4)) fail("state load", b, tid, t);
+                    for (int g = 0; g < G; ++g) {
+                        const int64_t go = adj_member(a, grp.c0, g) * plane;
+                        const int64_t e = (go + f.lo + kk) * es;
+                        if (!check::in_region(rg[dir], a.g, pe + e, es)) fail("dL/dy load", b, tid, t);
+                        if (!check::in_region(rx[dir], a.x, pe + e, es)) fail("x load", b, tid, t);
+                        if (!check::in_region(rl[dir], a.lam, pe + e, es)) fail("lambda load", b, tid, t);
+                        if (!check::in_region(rh[dir], hb, (go + f.hlo + kk) * 4, 4)) fail("state load", b, tid, t);
+                    }
                 }
-                if (!check::in_region(rh[dir], hb, (f.hlo + kl) * 4, 4)) fail("left state", b, tid, t);
-                if (!check::in_region(rh[dir], hb, (f.hlo + kr) * 4, 4)) fail("right state", b, tid, t);
-                n += P * 7 + 2;
+                for (int g = 0; g < G; ++g) {
+                    const int64_t go = adj_member(a, grp.c0, g) * plane;
+                    if (!check::in_region(rh[dir], hb, (go + f.hlo + kl) * 4, 4)) fail("left state", b, tid, t);
+                    if (!check::in_region(rh[dir], hb, (go + f.hlo + kr) * 4, 4)) fail("right state", b, tid, t);
+                }
+                n += P * (3 + 4 * G) + 2 * G;
                 if (t < bd.tb_lo) continue;
                 const int64_t lo = static_cast<int64_t>(adj_row(t, S, rev)) * L;
                 for (int j = 0; j < P; ++j) {
                     const bool own = k0 + j >= 0 && k0 + j < L && k0 + j >= bd.o_lo && k0 + j < bd.o_hi;
                     if (!own) continue;
-                    const int64_t e = (lo + k0 + j) * es;
-                    if (!check::in_region(rdl[dir], a.dlam, pe + e, es)) fail("dlambda store", b, tid, t);
-                    if (!check::in_region(rdx[dir], a.dx, pe + e, es)) fail("dx store", b, tid, t);
+                    for (int g = 0; g < G; ++g) {
+                        if (!adj_member_ok(a, grp.c0, g)) continue;
+                        const int64_t e = (adj_member(a, grp.c0, g) * plane + lo + k0 + j) * es;
+                        if (!check::in_region(rdl[dir], a.dlam, pe + e, es)) fail("dlambda store", b, tid, t);
+                        if (!check::in_region(rdx[dir], a.dx, pe + e, es)) fail("dx store", b, tid, t);
+                    }
                     if (a.shared) {
                         if (t != 0) {
                             const int64_t ez = (grp.nidx * 3 * plane + lo + k0 + j) * 4;
@@ -849,7 +892,7 @@ static void replay_adjoint4_band(const Adj4BandK& k, int64_t nblocks, int es, bo
                             if (!check::in_region(rdz[dir], a.dz, (grp.zplane + o * plane + lo + k0 + j) * es, es))
                                 fail("dlogit store", b, tid, t);
                     }
-                    n += 5;
+                    n += 2 * G + 3;
                 }
             }
         }
@@ -923,10 +966,12 @@ hipError_t launch_adjoint4_band(const AdjointParams (&p)[4], float* qbuf, int ba
         lmax = p[d].L > lmax ? p[d].L : lmax;
         merge = merge || p[d].mscale || p[d].dmerge;
     }
+    const int G = p[0].shared ? GSPN_ADJ_BAND_G : 1;
+    const int64_t groups = p[0].n * ((p[0].c + G - 1) / G);
     for (int d = 0; d < 4; ++d) {
         k.base.d[d] = adj_args(p[d]);
         k.nseg[d] = static_cast<int>((p[d].L + kAdjBandSeg - 1) / kAdjBandSeg);
-        k.base.blocks[d] = p[d].S - static_cast<int64_t>(band) * kAdjBandHalo > 0 ? planes * k.nseg[d] : 0;
+        k.base.blocks[d] = p[d].S - static_cast<int64_t>(band) * kAdjBandHalo > 0 ? groups * k.nseg[d] : 0;
         total += k.base.blocks[d];
     }
     k.band = band;
@@ -959,19 +1004,24 @@ hipError_t launch_adjoint4_band(const AdjointParams (&p)[4], float* qbuf, int ba
     const int P = 2;
     const bool vec = vec_ok(2);
     const int threads = kAdjBandSpan / P;
-    const size_t lds = 4 * sizeof(float) * threads;
+    const size_t lds = 4 * sizeof(float) * threads * G;
 #ifdef GSPN_CHECK_LAUNCHES
-    replay_adjoint4_band(k, total, f32 ? 4 : 2, merge, vec, P);
+    replay_adjoint4_band(k, total, f32 ? 4 : 2, merge, vec, P, G);
 #endif
-#define GSPN_ADJB_LAUNCH2(TT, MM, VV, PP)                                                                         \
-    do {                                                                                                          \
-        if (nt) hipLaunchKernelGGL((adj4band_kernel<TT, MM, true, VV, PP>), grid, dim3(threads), lds, stream, k);  \
-        else hipLaunchKernelGGL((adj4band_kernel<TT, MM, false, VV, PP>), grid, dim3(threads), lds, stream, k);    \
+#define GSPN_ADJB_LAUNCH3(TT, MM, VV, GG)                                                                           \
+    do {                                                                                                            \
+        if (nt) hipLaunchKernelGGL((adj4band_kernel<TT, MM, true, VV, 2, GG>), grid, dim3(threads), lds, stream, k); \
+        else hipLaunchKernelGGL((adj4band_kernel<TT, MM, false, VV, 2, GG>), grid, dim3(threads), lds, stream, k);   \
     } while (0)
-#define GSPN_ADJB_LAUNCH(TT, MM)                          \
-    do {                                                  \
-        if (vec) GSPN_ADJB_LAUNCH2(TT, MM, true, 2);         \
-        else GSPN_ADJB_LAUNCH2(TT, MM, false, 2);            \
+#define GSPN_ADJB_LAUNCH2(TT, MM, VV)                         \
+    do {                                                      \
+        if (G > 1) GSPN_ADJB_LAUNCH3(TT, MM, VV, GSPN_ADJ_BAND_G); \
+        else GSPN_ADJB_LAUNCH3(TT, MM, VV, 1);                    \
+    } while (0)
+#define GSPN_ADJB_LAUNCH(TT, MM)                  \
+    do {                                          \
+        if (vec) GSPN_ADJB_LAUNCH2(TT, MM, true);    \
+        else GSPN_ADJB_LAUNCH2(TT, MM, false);       \
     } while (0)
     if (f32) {
         if (merge) GSPN_ADJB_LAUNCH(float, true);
@@ -982,6 +1032,7 @@ hipError_t launch_adjoint4_band(const AdjointParams (&p)[4], float* qbuf, int ba
     }
 #undef GSPN_ADJB_LAUNCH
 #undef GSPN_ADJB_LAUNCH2
+#undef GSPN_ADJB_LAUNCH3
     return hipGetLastError();
 }
 
