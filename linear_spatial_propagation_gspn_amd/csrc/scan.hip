@@ -182,7 +182,7 @@ namespace {
 constexpr int64_t kBandMaxLines = 64;  // lines (planes x 4 directions) below which it pays
 constexpr int kBandMaxLaunches = 32;
 
-int band_positions(int dtype) { return 64 * GSPN_BAND_BYTES / (dtype == kF32 ? 4 : 2); }
+int band_positions(int dtype) { return 64 * GSPN_BAND_WAVES * GSPN_BAND_BYTES / (dtype == kF32 ? 4 : 2); }
 
 }  // namespace
 

@@ -35,9 +35,13 @@ namespace gspn {
 #define GSPN_BAND_DEPTH 12
 #endif
 // bytes of each row a lane loads per step (its positions: this over the
-// element size)
+// element size), and waves a workgroup: a workgroup spans 64 waves bytes
+// lanes' worth of positions
 #ifndef GSPN_BAND_BYTES
 #define GSPN_BAND_BYTES 16
+#endif
+#ifndef GSPN_BAND_WAVES
+#define GSPN_BAND_WAVES 1
 #endif
 
 namespace band {
@@ -114,7 +118,13 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
     constexpr int WW = P * ZB / 4;
     constexpr int D = GSPN_BAND_DEPTH;
 
-    const int lane = threadIdx.x;
+    constexpr int BW = GSPN_BAND_WAVES;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // several waves: the outer neighbours of a wave's edge lanes cross
+    // through LDS (double-buffered, one barrier a step)
+    __shared__ float edges[2][BW][2];
+    int ebuf = 0;
     const int S = a.S;
     const int L = a.L;
     const int64_t plane = static_cast<int64_t>(S) * L;
@@ -130,7 +140,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 
     const int s0 = g * b.seg;
     const int s1 = min(s0 + b.seg, L);
-    const int k0 = s0 - b.halo + lane * P;   // the lane's first position (may lie outside the line)
+    const int k0 = s0 - b.halo + (wave * 64 + lane) * P;   // the lane's first position (may lie outside the line)
     const bool active = k0 >= 0 && k0 < L && k0 < s1 + b.halo;
     const bool owned = k0 >= s0 && k0 < s1;  // positions this workgroup stores
     const int k0c = min(max(k0, 0), L - P);  // addresses of lanes outside the line stay inside it
@@ -185,6 +195,12 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
     const float* hin = b.hin + dir * b.sstride + p * L;
 #pragma unroll
     for (int j = 0; j < P; ++j) h[j] = (t0 > 0 && active) ? hin[k0c + j] : 0.0f;
+    if constexpr (BW > 1) {
+        // lanes outside the line publish exact zeros (see the step's end)
+        if (lane == 0) edges[0][wave][0] = active ? h[0] : 0.0f;
+        if (lane == 63) edges[0][wave][1] = active ? h[P - 1] : 0.0f;
+        __syncthreads();
+    }
 
     uint32_t sO = line_of(t0) * rowO;
     // lambda_j x_j + c for the bf16 pair (j, j + 1) in word e: one bf16 dot
@@ -222,8 +238,12 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
                 }
             }
         } else {
-            const float left = lp::shift_from_lower_lane(h[P - 1]);   // 0 beyond the wave
-            const float right = lp::shift_from_upper_lane(h[0]);
+            float left = lp::shift_from_lower_lane(h[P - 1]);   // 0 beyond the wave
+            float right = lp::shift_from_upper_lane(h[0]);
+            if constexpr (BW > 1) {
+                if (lane == 0) left = wave > 0 ? edges[ebuf][wave - 1][1] : 0.0f;
+                if (lane == 63) right = wave + 1 < BW ? edges[ebuf][wave + 1][0] : 0.0f;
+            }
             if constexpr (PAIR) {
                 // centre weight eliminated, as in the long-line kernel
                 float dd[P + 1];
@@ -272,6 +292,12 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
         // positions are 0 anyway
 #pragma unroll
         for (int j = 0; j < P; ++j) h[j] = (j == 0 || j == P - 1) && !active ? 0.0f : hn[j];
+        if constexpr (BW > 1) {
+            ebuf ^= 1;
+            if (lane == 0) edges[ebuf][wave][0] = h[0];
+            if (lane == 63) edges[ebuf][wave][1] = h[P - 1];
+            __syncthreads();
+        }
         const uint32_t oO = sO;
         sO += dO;
         if (owned) {
@@ -323,7 +349,7 @@ __device__ __forceinline__ void band_segment(const BandK& b, int dir, int64_t p,
 // which its neighbours read in the same steps, come from that XCD's L2
 // (every direction active, equal segment counts, lines a multiple of 8).
 template <typename T, typename TW, bool LOGITS, bool CH, typename TO = T>
-__global__ __launch_bounds__(64) void scan4band_kernel(const BandK b) {
+__global__ __launch_bounds__(64 * GSPN_BAND_WAVES) void scan4band_kernel(const BandK b) {
     int dir = 0;
     int64_t p;
     int g;
@@ -356,10 +382,10 @@ hipError_t launch_band4(const BandK& b, hipStream_t stream) {
     for (int d = 0; d < 4; ++d) chunked = chunked || (b.blocks[d] > 0 && b.d[d].K < b.d[d].S);
     if (chunked) {
         hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, true, TO>), dim3(static_cast<unsigned>(nblocks)),
-                           dim3(64), 0, stream, b);
+                           dim3(64 * GSPN_BAND_WAVES), 0, stream, b);
     } else {
         hipLaunchKernelGGL((scan4band_kernel<T, TW, LOGITS, false, TO>), dim3(static_cast<unsigned>(nblocks)),
-                           dim3(64), 0, stream, b);
+                           dim3(64 * GSPN_BAND_WAVES), 0, stream, b);
     }
     return hipGetLastError();
 }
