@@ -73,6 +73,8 @@ def _errors(got, ref):
     ((2, 64, 33, 47, 4), "bf16", True, 5, True),       # ragged pixel count: VALU sums
     ((1, 24, 20, 30, 3), "f32", False, 0, False),      # plane-resident proxy-space backward
     ((2, 40, 72, 40, 5), "f32", True, 9, True),        # fp32, shared logits, chunks, merge
+    ((1, 20, 16, 128, 4), "bf16", True, 0, False),     # channels not a multiple of 8: VALU sums
+    ((1, 48, 24, 64, 24), "bf16", False, 0, False),    # more than 16 proxy channels: VALU sums
 ])
 def test_proxy_backward_small(shape, dtype, shared, chunk, merge):
     n, c, h, w, cp = shape
@@ -90,6 +92,28 @@ def test_proxy_backward_small(shape, dtype, shared, chunk, merge):
     errs = _errors(got, ref)
     _say("  worst normwise error %.3g (%s)" % (max(errs.values()), max(errs, key=errs.get)))
     assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_proxy_backward_array_layout(dtype):
+    """The per-direction logits and lambdas in the array frame ([.., H, W]
+    for every direction): the same gradients as the scan layout, the
+    horizontal ones returned in the array frame."""
+    wl = Workload("case", 1, 64, 40, 128, dtype, True, 0, 55, c_proxy=8)
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 9)
+    za = [z if d < 2 else z.transpose(-1, -2).contiguous() for d, z in enumerate(inp["logits"])]
+    la = [l if d < 2 else l.transpose(-1, -2).contiguous() for d, l in enumerate(inp["lam"])]
+    a = G.gspn_proxy_backward4(inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"], gy)
+    b = G.gspn_proxy_backward4(inp["x"], inp["w_down"], inp["w_up"], za, la, gy, layout="array")
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.allclose(a[i].float(), b[i].float(), rtol=1e-5, atol=1e-6), i
+    for d in range(4):
+        back = (lambda t: t) if d < 2 else (lambda t: t.transpose(-1, -2))
+        assert torch.equal(a[4][d], back(b[4][d]))
+        # shared-logit sums are fp32 atomics: equal up to their order
+        assert torch.allclose(a[3][d].float(), back(b[3][d]).float(), rtol=2e-2, atol=1e-3)
 
 
 def test_proxy_backward_timed_stages():
