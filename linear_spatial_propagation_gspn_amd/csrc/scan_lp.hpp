@@ -445,14 +445,48 @@ void replay_fused4lp(const Scan4K& k, int nthreads) {
 }
 #endif
 
+// Waves of the long-line scan resident on one CU (a build parameter; 0: as
+// many as registers allow).  Each step of a line streams a whole row of
+// every input, so the CU's share of bandwidth, not its wave count, bounds the
+// step; fewer resident lines each step faster.  On the 1024^2, B=16, C=8 fp32
+// forward (512 workgroups of four waves) one workgroup per CU ran the scan in
+// 2.33 ms, two rounds, against 2.47 ms with two workgroups per CU in one
+// round; the wide backward's recompute (2304 workgroups) gained 1.8 ms.  The
+// launch reserves LDS it does not use so that no more workgroups fit, and
+// only when the grid is whole rounds of them (or many rounds), since a last
+// round that is mostly empty would cost more than the gain.
+#ifndef GSPN_LP_WAVES_PER_CU
+#define GSPN_LP_WAVES_PER_CU 4
+#endif
+// Only workgroups of at least this many waves (lines of at least 1024
+// positions at four waves): short lines are bound by the latency of their
+// steps, which more resident workgroups hide.
+#ifndef GSPN_LP_RESERVE_MIN_WAVES
+#define GSPN_LP_RESERVE_MIN_WAVES 4
+#endif
+constexpr int64_t kCuLdsBytes = 160 * 1024;
+
+// Dynamic LDS to reserve for nblocks workgroups of nthreads on cus CUs.
+GSPN_HD size_t lp_lds_reserve(int64_t nblocks, int nthreads, int64_t cus) {
+    const int waves = (nthreads + 63) / 64;
+    if (GSPN_LP_WAVES_PER_CU <= 0 || cus <= 0 || waves < GSPN_LP_RESERVE_MIN_WAVES || waves <= 0) return 0;
+    const int64_t per_cu = GSPN_LP_WAVES_PER_CU / waves > 1 ? GSPN_LP_WAVES_PER_CU / waves : 1;
+    const int64_t round = per_cu * cus;
+    if (nblocks < round || (nblocks % round != 0 && nblocks < 4 * round)) return 0;
+    // per_cu workgroups fit, one more does not (the edge buffers' few static
+    // bytes aside)
+    return static_cast<size_t>(kCuLdsBytes / (per_cu + 1) + 1024);
+}
+
 template <typename T, typename TW, bool LOGITS, typename TO = T>
 hipError_t launch_fused4lp(const Scan4K& k, int nthreads, hipStream_t stream) {
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
 #ifdef GSPN_CHECK_LAUNCHES
     replay_fused4lp<T, TW, LOGITS, TO>(k, nthreads);
 #endif
-    hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS, TO>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads), 0,
-                       stream, k);
+    const size_t reserve = lp_lds_reserve(nblocks, nthreads, device_compute_units());
+    hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS, TO>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads),
+                       reserve, stream, k);
     return hipGetLastError();
 }
 

@@ -333,3 +333,46 @@ def test_banded_adjoint_stays_in_bounds(chk, case):
     bad = [l for l in text.splitlines() if l.startswith("violation") and "without a host replay" not in l]
     assert not bad, text
     assert "adj4band_kernel" in text and "adj4_kernel<" not in text, text
+
+
+def forward_only(lib, n, c, h, w, dtype=torch.float32):
+    """The four-direction forward with the binding's workspace, no states."""
+    sp = Space(lib)
+    x = _meta(n, c, h, w, dtype)
+    es = x.element_size()
+    xb = n * c * h * w * es
+    px = sp.buf("x", xb)
+    pz = [sp.buf("logits%d" % d, 3 * xb) for d in range(4)]
+    pl = [sp.buf("lambda%d" % d, xb) for d in range(4)]
+    py = sp.buf("y", xb)
+    fws = G.forward4_workspace(x, c)
+    pw = sp.buf("forward workspace", _nbytes(fws))
+    return lib.gspn_forward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(c), _i64(0), ctypes.c_void_p(px), _vp4(*pz),
+                             _vp4(*pl), None, ctypes.c_void_p(py), None, ctypes.c_void_p(pw), _i64(_nbytes(fws)),
+                             G._dtype_code(x), 0, None)
+
+
+def _lp_dynamic_lds(text: str) -> int:
+    lines = [l for l in text.splitlines() if l.startswith("launch ") and "scan4lp_kernel" in l]
+    assert len(lines) == 1, text
+    return int(lines[0].split("lds=")[1].split("+")[0])
+
+
+@pytest.mark.parametrize("c, h, w, reserved", [
+    (64, 8, 1024, True),    # four-wave workgroups, 256 of them: one whole round of one a CU
+    (65, 8, 1024, False),   # 260: a second round nearly empty, so none reserved
+    (64, 8, 256, False),    # one-wave workgroups (short lines): as many a CU as fit
+])
+def test_long_line_scan_lds_reservation(chk, c, h, w, reserved):
+    """The long-line scan reserves LDS it does not use, so that one four-wave
+    workgroup runs a CU (on the checking build's 256 CUs), only where the grid
+    is whole rounds of them; the reservation leaves room for one workgroup,
+    not two."""
+    assert forward_only(chk, 1, c, h, w) == 0
+    text = report(chk)
+    assert chk.gspn_check_violations() == 0, text
+    lds = _lp_dynamic_lds(text)
+    if reserved:
+        assert 80 * 1024 < lds <= 160 * 1024 - 1024, text
+    else:
+        assert lds == 0, text
