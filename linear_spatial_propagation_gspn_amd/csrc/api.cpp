@@ -429,9 +429,14 @@ hipError_t copy_to_scan_frame(int64_t n, int64_t c, int64_t h, int64_t w, int64_
 gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw, int64_t chunk_len,
                           const void* x, const void* const logits_in[4], const void* const lam_in[4],
                           const float* merge, void* y, float* states, void* workspace, int64_t workspace_bytes,
-                          int dtype, int layout, void* stream, Timer* tm, bool noalloc = false) {
+                          int dtype, int layout, void* stream, Timer* tm, bool noalloc = false,
+                          int64_t merge_ld = 0) {
     // noalloc: the workspace is the current device's static scratch array,
-    // looked up only once every argument has passed validation
+    // looked up only once every argument has passed validation.
+    // merge_ld: floats between the merge weights' direction rows (0: c); more
+    // than c only for the plane-sequential path's tail, a channel range of a
+    // wider call, which takes the concurrent path and its transposing merge.
+    const int64_t mld = merge_ld > 0 ? merge_ld : c;
     if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
     const void* const* logits = logits_in;
     const void* const* lam = lam_in;
@@ -456,7 +461,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     if (overlap(y, xb, x, xb)) return GSPN_ERR_ALIASING;
     for (int d = 0; d < 4; ++d)
         if (overlap(y, xb, logits[d], wb) || overlap(y, xb, lam[d], xb)) return GSPN_ERR_ALIASING;
-    const int64_t mgb = 4 * c * 4;  // merge weights, fp32 [4][c]
+    const int64_t mgb = (3 * mld + c) * 4;  // merge weights, fp32 [4][c], rows mld floats apart
     if (merge && !aligned(merge, 4)) return GSPN_ERR_MISALIGNED;
     if (merge && overlap(y, xb, merge, mgb)) return GSPN_ERR_ALIASING;
     const int64_t sb = 4 * n * c * h * w * 4;  // four fp32 state maps
@@ -522,12 +527,12 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         p[d].accumulate = 0;
         p[d].dtype = dtype;
         p[d].wdtype = dtype;
-        p[d].mscale = merge ? merge + d * c : nullptr;
+        p[d].mscale = merge ? merge + d * mld : nullptr;
     }
 
     // Planes of at most 64 x 64: one pass over LDS-resident planes, whether
     // or not a workspace is given (unless the states are wanted).
-    if (gspn::plane4_supported(h, w) && !states) {
+    if (gspn::plane4_supported(h, w) && !states && (!merge || mld == c)) {
         if (tm) tm->scan_kernel = GSPN_SCAN_PLANE;
         return from_hip(timed(tm, GSPN_STAGE_SCAN, [&] {
             return gspn::launch_plane4(x, logits, lam, merge, y, n, c, cw, h, w, chunks, dtype, st);
@@ -568,20 +573,20 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     // Many big planes: one workgroup per plane runs the four directions in
     // turn and builds y in place; the scratch map of the horizontal
     // directions' sum takes the room of x transposed.
-    if (!states && gspn::seq4_supported(h, w) && n * c >= gspn::kSeq4MinPlanes) {
+    if (!states && gspn::seq4_supported(h, w) && n * c >= gspn::kSeq4MinPlanes && (!merge || mld == c)) {
         bool vec = aligned(x, 16) && aligned(y, 16);
         for (int d = 0; d < 4; ++d) vec = vec && aligned(p[d].wts, 16) && aligned(p[d].lam, 16);
         if (vec) {
             // With one workgroup per CU, planes run in rounds of one per CU,
             // each a chain of four whole scans.  A last round at most half
             // full would cost a whole round's time for half its work, so
-            // those planes (when they lie in one image and no merge weights
-            // are in play) go to the concurrent four-direction path instead,
-            // which spreads each plane over four workgroups.
+            // those planes (when they lie in one image) go to the concurrent
+            // four-direction path instead, which spreads each plane over four
+            // workgroups; its merge weights are those of the tail's channels.
             const int64_t planes = n * c;
             const int64_t cus = gspn::device_compute_units();
             const int64_t tail = cus > 0 ? planes % cus : 0;
-            const bool split = planes > cus && tail > 0 && 2 * tail <= cus && !merge &&
+            const bool split = planes > cus && tail > 0 && 2 * tail <= cus && mld == c &&
                                (planes - tail) / c == (planes - 1) / c;
             const int64_t run = split ? planes - tail : planes;
             const void* wts[4] = {p[0].wts, p[1].wts, p[2].wts, p[3].wts};
@@ -606,9 +611,10 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                 gspn_status sub = GSPN_OK;
                 const hipError_t e = timed(tm, GSPN_STAGE_TAIL, [&] {
                     sub = forward4_impl(1, tail, h, w, cw == 1 ? 1 : tail, chunk_len,
-                                        static_cast<const char*>(x) + run * plane_b, tz, tl, nullptr,
-                                        static_cast<char*>(y) + run * plane_b, nullptr, workspace, workspace_bytes,
-                                        dtype, GSPN_LAYOUT_SCAN, stream, nullptr, false);
+                                        static_cast<const char*>(x) + run * plane_b, tz, tl,
+                                        merge ? merge + c0 : nullptr, static_cast<char*>(y) + run * plane_b,
+                                        nullptr, workspace, workspace_bytes, dtype, GSPN_LAYOUT_SCAN, stream,
+                                        nullptr, false, c);
                     return sub == GSPN_OK ? hipSuccess : hipErrorLaunchFailure;
                 });
                 if (sub != GSPN_OK) return sub;
@@ -658,7 +664,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
             return gspn::launch_combine_states(y, states, states + elems, states + 2 * elems, states + 3 * elems,
                                                n * c, static_cast<int>(h), static_cast<int>(w), dtype, st, merge,
-                                               c);
+                                               c, mld);
         }));
     }
 
@@ -686,7 +692,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         }
         return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
             return gspn::launch_combine(y, m1, m2, m3, n * c, static_cast<int>(h), static_cast<int>(w), 1, dtype,
-                                        st, merge, c);
+                                        st, merge, c, mld);
         }));
     }
     // Longer lines, sequential path: T2B writes y, B2T adds to it; L2R writes

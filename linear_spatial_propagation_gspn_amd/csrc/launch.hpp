@@ -93,17 +93,18 @@ hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, i
 
 // y[p][r][c] = ((m2 z2[p][c][r] + m3 z3[p][c][r]) + m0 y[p][r][c] (if accumulate)) + m1 a[p][r][c]
 // over planes of R x Cc; a, z2, z3 may be NULL; z2, z3 are Cc x R planes;
-// m0..m3: merge[k][p % nch] (learnable merge weights [4][nch]), or 1 if merge is null.
+// m0..m3: merge[k][p % nch] (learnable merge weights [4][nch], rows mld floats
+// apart; mld = 0 means nch), or 1 if merge is null.
 hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3, int64_t planes, int R,
                           int Cc, int accumulate, int dtype, hipStream_t stream, const float* merge = nullptr,
-                          int64_t nch = 1);
+                          int64_t nch = 1, int64_t mld = 0);
 
 // y[p][r][c] = ((m2 s2[p][c][r] + m3 s3[p][c][r]) + m0 s0[p][r][c]) + m1 s1[p][r][c]:
 // the same merge from four fp32 state maps (s2, s3 in the transposed frame),
 // y in the storage type.
 hipError_t launch_combine_states(void* y, const float* s0, const float* s1, const float* s2, const float* s3,
                                  int64_t planes, int R, int Cc, int dtype, hipStream_t stream,
-                                 const float* merge = nullptr, int64_t nch = 1);
+                                 const float* merge = nullptr, int64_t nch = 1, int64_t mld = 0);
 
 // out_dtype: storage type of w_out (-1: the same as dtype; kF32 is allowed
 // for bf16 logits).

@@ -157,12 +157,18 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict
                      [&](int c, int r, const T*) { return tile[r][c]; });
 }
 
+// Offset of the merge weight of direction row k and channel ch in a [4][..]
+// array whose rows lie mld floats apart (mld = the channel count, or more for
+// a channel range of a wider tensor).
+GSPN_HD int64_t merge_index(int k, int64_t ch, int64_t mld) { return k * mld + ch; }
+
 // For planes of R x Cc in the array frame:
 //   y[p][r][c] = ((m2 z2[p][c][r] + m3 z3[p][c][r]) + m0 b[p][r][c]) + m1 a[p][r][c]
 // where b is y itself (accumulate), a separate source y0, or absent; a, z2,
 // z3 may each be absent (NULL) and z2, z3 are in the transposed frame
 // (Cc x R planes); m0..m3 are the learnable merge weights merge[k][ch] of
-// the plane's channel ch = p % nch, or 1 without merge weights.  The sources
+// the plane's channel ch = p % nch (row k at merge + k * mld), or 1 without
+// merge weights.  The sources
 // other than y are of type TS (the storage type, or fp32 states).  Every
 // source is read into the LDS tile with row-vector accesses of its own
 // frame; y is read completely before it is written, so it may be updated in
@@ -171,7 +177,8 @@ template <typename T, typename TS>
 __global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const TS* __restrict__ y0, const TS* __restrict__ a,
                                                            const TS* __restrict__ z2, const TS* __restrict__ z3,
                                                            int R, int Cc, int accumulate, int vec_y, int vec_s,
-                                                           int vec_z, const float* __restrict__ merge, int64_t nch) {
+                                                           int vec_z, const float* __restrict__ merge, int64_t nch,
+                                                           int64_t mld) {
     __shared__ float tile[kTile][kTile + 1];
     const TileIndex ti = tile_of(blockIdx.x, R, Cc);
     const int64_t plane = static_cast<int64_t>(R) * Cc;
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(T* y, const TS* __res
     if (merge) {
         const int64_t ch = ti.plane % nch;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m[k] = merge[k * nch + ch];
+        for (int k = 0; k < 4; ++k) m[k] = merge[merge_index(k, ch, mld)];
     }
     bool any = false;
     auto add_t = [&](const TS* z, float wt) {  // transposed source: its row c is column c of the tile
@@ -257,14 +264,16 @@ void replay_tiles(const char* kernel, const char* what, const void* base, int64_
     check::count_accesses(n);
 }
 
-// The merge weights a combine block reads: merge[k * nch + plane % nch], k < 4.
-void replay_merge(const char* kernel, const float* merge, int64_t nch, int64_t nblocks, int R, int Cc) {
+// The merge weights a combine block reads: those of channel plane % nch in
+// each of the four rows, k < 4.
+void replay_merge(const char* kernel, const float* merge, int64_t nch, int64_t mld, int64_t nblocks, int R,
+                  int Cc) {
     if (!merge) return;
     const check::Region reg = check::region_of(merge, kernel, "merge");
     for (int64_t b = 0; b < nblocks; ++b) {
         const int64_t ch = tile_of(b, R, Cc).plane % nch;
         for (int k = 0; k < 4; ++k)
-            if (!check::in_region(reg, merge, (k * nch + ch) * 4, 4)) {
+            if (!check::in_region(reg, merge, merge_index(k, ch, mld) * 4, 4)) {
                 check::violation(kernel, "merge", "weight (%d, %lld) outside the buffer", k,
                                  static_cast<long long>(ch));
                 return;
@@ -274,9 +283,10 @@ void replay_merge(const char* kernel, const float* merge, int64_t nch, int64_t n
 
 template <typename T, typename TS>
 void replay_combine(int64_t nblocks, const T* y, const TS* y0, const TS* a, const TS* z2, const TS* z3, int R,
-                    int Cc, int accumulate, int vec_y, int vec_s, int vec_z, const float* merge, int64_t nch) {
+                    int Cc, int accumulate, int vec_y, int vec_s, int vec_z, const float* merge, int64_t nch,
+                    int64_t mld) {
     const char* k = "combine_kernel";
-    replay_merge(k, merge, nch, nblocks, R, Cc);
+    replay_merge(k, merge, nch, mld, nblocks, R, Cc);
     replay_tiles<TS>(k, "z2", z2, nblocks, R, Cc, true, vec_z);
     replay_tiles<TS>(k, "z3", z3, nblocks, R, Cc, true, vec_z);
     if (y0) replay_tiles<TS>(k, "y0", y0, nblocks, R, Cc, false, vec_s);
@@ -322,7 +332,9 @@ hipError_t launch_transpose(const void* src, void* dst, int64_t planes, int R, i
 }
 
 hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3, int64_t planes, int R,
-                          int Cc, int accumulate, int dtype, hipStream_t stream, const float* merge, int64_t nch) {
+                          int Cc, int accumulate, int dtype, hipStream_t stream, const float* merge, int64_t nch,
+                          int64_t mld) {
+    if (mld <= 0) mld = nch;
     const dim3 grid(static_cast<unsigned>(tiles_for(planes, R, Cc)));
     const int vw = dtype == kF32 ? 4 : 8;
     const int vy = (Cc % vw == 0) && aligned16(y);
@@ -332,30 +344,31 @@ hipError_t launch_combine(void* y, const void* a, const void* z2, const void* z3
     if (dtype == kF32) {
         replay_combine<float, float>(grid.x, static_cast<const float*>(y), nullptr, static_cast<const float*>(a),
                                      static_cast<const float*>(z2), static_cast<const float*>(z3), R, Cc, accumulate,
-                                     vs, vs, vz, merge, nch);
+                                     vs, vs, vz, merge, nch, mld);
     } else {
         replay_combine<bf16_t, bf16_t>(grid.x, static_cast<const bf16_t*>(y), nullptr, static_cast<const bf16_t*>(a),
                                        static_cast<const bf16_t*>(z2), static_cast<const bf16_t*>(z3), R, Cc,
-                                       accumulate, vs, vs, vz, merge, nch);
+                                       accumulate, vs, vs, vz, merge, nch, mld);
     }
 #endif
     if (dtype == kF32) {
         hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
                            static_cast<const float*>(nullptr), static_cast<const float*>(a),
                            static_cast<const float*>(z2), static_cast<const float*>(z3), R, Cc, accumulate, vs, vs,
-                           vz, merge, nch);
+                           vz, merge, nch, mld);
     } else {
         hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), grid, dim3(kThreads), 0, stream,
                            static_cast<bf16_t*>(y), static_cast<const bf16_t*>(nullptr),
                            static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(z2),
-                           static_cast<const bf16_t*>(z3), R, Cc, accumulate, vs, vs, vz, merge, nch);
+                           static_cast<const bf16_t*>(z3), R, Cc, accumulate, vs, vs, vz, merge, nch, mld);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_combine_states(void* y, const float* s0, const float* s1, const float* s2, const float* s3,
                                  int64_t planes, int R, int Cc, int dtype, hipStream_t stream, const float* merge,
-                                 int64_t nch) {
+                                 int64_t nch, int64_t mld) {
+    if (mld <= 0) mld = nch;
     const dim3 grid(static_cast<unsigned>(tiles_for(planes, R, Cc)));
     const int vy = (Cc % (dtype == kF32 ? 4 : 8) == 0) && aligned16(y);
     const int vs = (Cc % 4 == 0) && aligned16(s0) && aligned16(s1);
@@ -363,18 +376,18 @@ hipError_t launch_combine_states(void* y, const float* s0, const float* s1, cons
 #ifdef GSPN_CHECK_LAUNCHES
     if (dtype == kF32) {
         replay_combine<float, float>(grid.x, static_cast<const float*>(y), s0, s1, s2, s3, R, Cc, 0, vy, vs, vz,
-                                     merge, nch);
+                                     merge, nch, mld);
     } else {
         replay_combine<bf16_t, float>(grid.x, static_cast<const bf16_t*>(y), s0, s1, s2, s3, R, Cc, 0, vy, vs, vz,
-                                      merge, nch);
+                                      merge, nch, mld);
     }
 #endif
     if (dtype == kF32) {
         hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(kThreads), 0, stream, static_cast<float*>(y),
-                           s0, s1, s2, s3, R, Cc, 0, vy, vs, vz, merge, nch);
+                           s0, s1, s2, s3, R, Cc, 0, vy, vs, vz, merge, nch, mld);
     } else {
         hipLaunchKernelGGL((combine_kernel<bf16_t, float>), grid, dim3(kThreads), 0, stream,
-                           static_cast<bf16_t*>(y), s0, s1, s2, s3, R, Cc, 0, vy, vs, vz, merge, nch);
+                           static_cast<bf16_t*>(y), s0, s1, s2, s3, R, Cc, 0, vy, vs, vz, merge, nch, mld);
     }
     return hipGetLastError();
 }

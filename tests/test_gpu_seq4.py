@@ -41,7 +41,7 @@ CASES = [
     ((1, 256, 128, 192), "bf16", False),  # per-channel bf16 logits normalised in the scan
     ((2, 128, 128, 64), "f32", False),    # per-channel fp32 logits
     ((1, 256, 192, 128), "f32", True),    # shared fp32 logits over 256 channels (fp32 weight triples)
-    ((1, 300, 64, 128), "bf16", True),    # 256 + 44 planes: the last 44 on the concurrent path (no merge)
+    ((1, 300, 64, 128), "bf16", True),    # 256 + 44 planes: the last 44 on the concurrent path
     ((2, 150, 64, 128), "f32", False),    # the same for per-channel logits, the 44 in the second image
 ]
 
@@ -51,7 +51,7 @@ CUS = 256  # compute units of the MI355X
 def _tail_split(n, c, merge):
     planes = n * c
     tail = planes % CUS
-    return planes > CUS and 0 < tail and 2 * tail <= CUS and not merge and (planes - tail) // c == (planes - 1) // c
+    return planes > CUS and 0 < tail and 2 * tail <= CUS and (planes - tail) // c == (planes - 1) // c
 
 
 @pytest.mark.parametrize("merge", [False, True])
