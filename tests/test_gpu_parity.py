@@ -477,6 +477,30 @@ def test_full_size_sampled_planes(name, planes):
         assert e <= TOL[wl.dtype]
 
 
+def test_full_size_wide_merge_sampled_planes():
+    """The 1152-channel workload with learnable merge weights: the first 1024
+    planes on the plane-sequential kernel, the last 128 (the tail) on the
+    concurrent path, whose transposing merge reads the tail channels' merge
+    weights in place; sampled planes from both against the oracle."""
+    wl = WORKLOADS["wide"]
+    _say("full wide, learnable merge")
+    inp = make_inputs(wl, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(wl.seed + 2000)
+    m = torch.randn((4, wl.c), generator=g, device=DEV, dtype=torch.float32)
+    got, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=wl.chunk,
+                                       workspace=G.forward4_workspace(inp["x"], wl.cw), merge=m)
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "seq4_kernel" and times["tail"]["launches"] == 1, times
+    mm = m.double().cpu().numpy()
+    for c in (0, 1023, 1024, 1100, 1151):
+        x, zs, ls = _plane_inputs(inp, wl, 0, c)
+        ref = oracle.forward4(x, zs, ls, chunk=wl.chunk, merge=mm[:, c:c + 1])
+        e = _err(got[0:1, c:c + 1], ref)
+        _say("  channel %d: normwise error %.3g" % (c, e))
+        assert e <= TOL[wl.dtype]
+
+
 def test_full_size_no_workspace_sampled_planes():
     """The 1024^2, B=16, C=8 workload without a workspace: one launch per
     direction, horizontal lines as per-lane row tiles."""
