@@ -8,7 +8,8 @@ per direction and channel) over one batch of seeded synthetic inputs already
 resident in HBM; for the proxy workload a step is the compressive proxy
 pipeline (1x1 projection down, forward4 in proxy space, 1x1 projection up).
 --pass backward times gspn_backward4 instead (gspn_proxy_backward4 for the
-proxy workload).  Prints one JSON line.
+proxy workload); --pass train a training step, the forward keeping its states
+and the backward reading them.  Prints one JSON line.
 
 Measurements:
   - ms per step: HIP events on the stream the library launches on, bracketing
@@ -527,10 +528,14 @@ def bench_proxy_backward(args, wl):
     """The backward leg of the compressive-proxy workload:
     gspn_proxy_backward4 for a seeded dL/dy ~ N(0, 1).  The dominant kernel
     is the stage that takes longest (the weight-gradient passes, two
-    launches, at full size)."""
+    launches, at full size).  With --pass train a step is a training step:
+    gspn_proxy_forward4 keeping its proxy-space state, then
+    gspn_proxy_backward4 from it (no recompute)."""
+    train = args.pass_ == "train"
     torch.cuda.init()
     G.lib()
-    print("bench: proxy backward, workload %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
+    print("bench: proxy %s, workload %s, generating inputs" % ("train" if train else "backward", wl.name),
+          file=sys.stderr, flush=True)
     lay = args.layout
     inp = make_inputs(wl, "cuda")
     tin = array_layout(inp) if lay == "array" else inp
@@ -539,10 +544,22 @@ def bench_proxy_backward(args, wl):
     gy = torch.randn(inp["x"].shape, generator=g, device="cuda", dtype=torch.float32).to(wl.torch_dtype)
     ws = G.proxy_backward4_workspace(inp["x"], wl.c_proxy, wl.cw, lay)
     merge = merge_weights(wl, args.merge)
+    fws = G.proxy_forward4_workspace(inp["x"], wl.c_proxy, wl.cw, lay) if train else None
+    kept = G.proxy_states_buffer(inp["x"], wl.c_proxy) if train else None
+    y = torch.empty_like(inp["x"]) if train else None
+    ftimes = {}
 
     def step(times=None):
-        return G.gspn_proxy_backward4(tin["x"], tin["w_down"], tin["w_up"], tin["logits"], tin["lam"], gy,
-                                      chunk_len=wl.chunk, workspace=ws, times=times, merge=merge, layout=lay)
+        args_ = (tin["x"], tin["w_down"], tin["w_up"], tin["logits"], tin["lam"])
+        if train:
+            if times is not None:
+                _, ftimes["t"] = G.gspn_proxy_forward4_timed(*args_, chunk_len=wl.chunk, out=y, workspace=fws,
+                                                             merge=merge, layout=lay, states=kept)
+            else:
+                G.gspn_proxy_forward4(*args_, chunk_len=wl.chunk, out=y, workspace=fws, merge=merge, layout=lay,
+                                      states=kept)
+        return G.gspn_proxy_backward4(*args_, gy, chunk_len=wl.chunk, workspace=ws, times=times, merge=merge,
+                                      layout=lay, states=kept)
 
     for _ in range(args.warmup):
         step()
@@ -556,10 +573,11 @@ def bench_proxy_backward(args, wl):
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
-    print("bench: proxy backward %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    print("bench: proxy %s %.3f ms/step" % ("train" if train else "backward", ms), file=sys.stderr, flush=True)
     singles = per_step_ms(step, args.steps)
     reps = max(3, min(args.steps, 10))
     acc = {name: [0.0, 0] for name in G.STAGES}
+    facc = {name: [0.0, 0] for name in G.STAGES}
     for _ in range(reps):
         t = G.StageTimes()
         step(times=t)
@@ -567,6 +585,10 @@ def bench_proxy_backward(args, wl):
             if name in acc:
                 acc[name][0] += v["ms"] / reps
                 acc[name][1] = v["launches"]
+        for name, v in ftimes.get("t", {}).items():
+            if name in facc:
+                facc[name][0] += v["ms"] / reps
+                facc[name][1] = v["launches"]
     stage = max(("weight_grad", "project_down", "project_up"), key=lambda k: acc[k][0])
     launches = acc[stage][1]
     kernel_ms = acc[stage][0] / launches
@@ -578,7 +600,7 @@ def bench_proxy_backward(args, wl):
         kernel = PROJECTION_KERNELS[stage]
         bpl = design = projection_bytes(wl, stage == "project_down")
     achieved = bpl / (kernel_ms * 1e-3) / 1e9
-    alg = proxy_backward_bytes(wl)
+    alg = proxy_backward_bytes(wl) + (algorithmic_bytes(wl) if train else 0)
     eff = alg / (ms * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
@@ -586,19 +608,27 @@ def bench_proxy_backward(args, wl):
         import oracle
         cpu = cpu_baseline_proxy_backward(wl, inp, gy, oracle, merge)
     traffic, traffic_src = counter_traffic(kernel, wl) if lay == "scan" else (None, "scan layout only")
-    step_traffic, step_src = step_counter_traffic(wl, "_backward" + ("" if lay == "scan" else "_array"))
+    tag = ("_train" if train else "_backward") + ("" if lay == "scan" else "_array")
+    step_traffic, step_src = step_counter_traffic(wl, tag)
+    grads = "dx, dw_down, dw_up, dlambda, dlogits%s" % (", dmerge" if args.merge else "")
+    if train:
+        stages = {"forward_" + k: round(v[0], 4) for k, v in facc.items() if v[1]}
+        stages.update({"backward_" + k: round(v[0], 4) for k, v in acc.items() if v[1]})
+    else:
+        stages = {k: round(v[0], 4) for k, v in acc.items() if v[1]}
     rec = {
-        "metric": "ms per compressive-proxy GSPN backward (dx, dw_down, dw_up, dlambda, dlogits%s); achieved "
-                  "HBM GB/s" % (", dmerge" if args.merge else ""),
+        "metric": ("ms per compressive-proxy GSPN training step (forward keeping its proxy-space state, then "
+                   "backward: %s); achieved HBM GB/s" % grads) if train else
+                  ("ms per compressive-proxy GSPN backward (%s); achieved HBM GB/s" % grads),
         "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded)",
-        "config": {"workload": wl.name, "pass": "backward", "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w,
-                   "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk, "c_proxy": wl.c_proxy,
-                   "merge": "learnable" if args.merge else "sum", "layout": lay},
+        "config": {"workload": wl.name, "pass": "train" if train else "backward", "n": wl.n, "c": wl.c,
+                   "h": wl.h, "w": wl.w, "storage": wl.dtype, "shared_w": wl.shared_w, "chunk_len": wl.chunk,
+                   "c_proxy": wl.c_proxy, "merge": "learnable" if args.merge else "sum", "layout": lay},
         "ms_median": round(singles[len(singles) // 2], 4), "ms_min": round(singles[0], 4),
         "effective_GBps": round(eff, 1), "effective_frac": round(eff / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
-        "stages_ms": {k: round(v[0], 4) for k, v in acc.items() if v[1]},
+        "stages_ms": stages,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
                      "kernel_ms": round(kernel_ms, 4), "launches_per_step": launches, "bytes_per_launch": bpl,
@@ -617,9 +647,6 @@ def bench_backward(args, wl):
     its fp32 states, then gspn_backward4 from those states (no recompute)."""
     train = args.pass_ == "train"
     if wl.c_proxy:
-        if train:
-            print("bench.py: --pass train covers gspn_forward4 (the proxy has --pass backward)", file=sys.stderr)
-            sys.exit(2)
         bench_proxy_backward(args, wl)
         return
     if train and wl.h <= 64 and wl.w <= 64:

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define GSPN_ABI_VERSION 10
+#define GSPN_ABI_VERSION 11
 #define GSPN_MAX_LINE 4096
 
 typedef enum {
@@ -294,6 +294,17 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
                                             int64_t cw, int dtype, int layout);
 
 /*
+ * gspn_proxy_states_bytes -- bytes of the proxy-space state that
+ * gspn_proxy_forward4 can keep for gspn_proxy_backward4 (its `states`
+ * argument): the projected input x_p and the merged proxy-space output y_p
+ * (n*c_proxy*h*w elements of the storage type each, each part rounded up to
+ * 256 bytes) and, for planes larger than 64 x 64, the four directions' fp32
+ * proxy-space scans as gspn_forward4 keeps them (16 * n*c_proxy*h*w bytes).
+ * Returns -1 for invalid arguments.
+ */
+int64_t gspn_proxy_states_bytes(int64_t n, int64_t c_proxy, int64_t h, int64_t w, int dtype);
+
+/*
  * gspn_proxy_forward4 -- the compressive-proxy propagation (GSPN-2 notes,
  * "Optimisation 2"): project C -> C_proxy, run the four-direction
  * propagation in proxy space, project back C_proxy -> C:
@@ -307,14 +318,23 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
  *            aligned, overlapping nothing else (else GSPN_ERR_WORKSPACE /
  *            GSPN_ERR_MISALIGNED / GSPN_ERR_ALIASING; NULL is
  *            GSPN_ERR_NULL_POINTER).
+ *   states   NULL, or gspn_proxy_states_bytes() bytes, 256-byte aligned, that
+ *            overlap no input, y or the workspace (else GSPN_ERR_MISALIGNED /
+ *            GSPN_ERR_ALIASING): the call keeps x_p, y_p and (planes larger
+ *            than 64 x 64) the fp32 proxy-space scans there for
+ *            gspn_proxy_backward4, which then recomputes none of them.  For
+ *            planes larger than 64 x 64 y_p is then merged from those fp32
+ *            scans, as gspn_forward4 does with states, so for bf16 storage y
+ *            can differ from that of a call without it in the last bf16
+ *            place (it is the y_p the backward's own recompute forms).
  * Intermediates are stored in the storage type (bf16 intermediates round
  * once at each store).
  */
 gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                 const void* const logits[4], const void* const lam[4], const float* merge,
-                                void* y, void* workspace, int64_t workspace_bytes, int dtype, int layout,
-                                void* stream);
+                                void* y, void* states, void* workspace, int64_t workspace_bytes, int dtype,
+                                int layout, void* stream);
 
 /*
  * gspn_backward4_workspace_bytes -- bytes of the gspn_backward4 workspace:
@@ -396,11 +416,15 @@ int64_t gspn_proxy_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, in
  *   dw_down   [c_proxy][c] fp32   = sum over images and pixels of dx_p[k] x[c]
  *   dlogits[d], dlam[d], dmerge   as gspn_backward4 gives them in proxy space
  *               (dmerge optional: NULL skips it)
- * x_p and y_p = forward4(x_p) are recomputed inside (stored in the storage
- * type, as the forward stores them; every intermediate rounds once at its
- * store); for planes larger than 64 x 64 that forward keeps its fp32 states
- * for the proxy-space backward, as gspn_forward4 / gspn_backward4 do with
- * states.  The weight gradients are summed in fp32 over at most 2048 runs
+ * states: NULL, or what gspn_proxy_forward4 kept for the same inputs
+ * (gspn_proxy_states_bytes() bytes, 256-byte aligned, overlapping no output
+ * and not the workspace).  Without it x_p and y_p = forward4(x_p) are
+ * recomputed inside (stored in the storage type, as the forward stores them;
+ * every intermediate rounds once at its store), and for planes larger than
+ * 64 x 64 that forward keeps its fp32 states for the proxy-space backward, as
+ * gspn_forward4 / gspn_backward4 do with states; both ways give the same
+ * gradients (those summed with fp32 atomics up to their summation order).
+ * The workspace is the same size either way.  The weight gradients are summed in fp32 over at most 2048 runs
  * of pixels, then the runs in a fixed order: they do not vary between calls.
  * With no pixels (n*h*w == 0) dw_down, dw_up and dmerge are written as
  * zeros and nothing else is touched (the other pointers may then be NULL).
@@ -413,9 +437,9 @@ int64_t gspn_proxy_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, in
 gspn_status gspn_proxy_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                  int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                  const void* const logits[4], const void* const lam[4], const float* merge,
-                                 const void* gy, void* dx, float* dw_down, float* dw_up, void* const dlogits[4],
-                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
-                                 int dtype, int layout, void* stream);
+                                 const void* states, const void* gy, void* dx, float* dw_down, float* dw_up,
+                                 void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                                 int64_t workspace_bytes, int dtype, int layout, void* stream);
 
 /*
  * Stage timing of one forward call (measurement only).
@@ -500,9 +524,9 @@ gspn_status gspn_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int6
 gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
                                       int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
                                       const void* w_up, const void* const logits[4],
-                                      const void* const lam[4], const float* merge, void* y, void* workspace,
-                                      int64_t workspace_bytes, int dtype, int layout, void* stream,
-                                      gspn_stage_times* times);
+                                      const void* const lam[4], const float* merge, void* y, void* states,
+                                      void* workspace, int64_t workspace_bytes, int dtype, int layout,
+                                      void* stream, gspn_stage_times* times);
 
 /* gspn_backward4 with stage timing (same contract as gspn_forward4_timed);
  * the forward recompute is reported as GSPN_STAGE_SCAN, except for planes of
@@ -523,7 +547,7 @@ gspn_status gspn_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int
 gspn_status gspn_proxy_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                        int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                        const void* const logits[4], const void* const lam[4], const float* merge,
-                                       const void* gy, void* dx, float* dw_down, float* dw_up,
+                                       const void* states, const void* gy, void* dx, float* dw_down, float* dw_up,
                                        void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
                                        int64_t workspace_bytes, int dtype, int layout, void* stream,
                                        gspn_stage_times* times);

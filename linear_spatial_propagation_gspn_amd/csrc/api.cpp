@@ -711,9 +711,30 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     }));
 }
 
+// The proxy-space state a compressive-proxy forward keeps for its backward:
+// x_p, y_p (storage type) and, for planes larger than 64 x 64, the four
+// directions' fp32 scans; offsets in bytes, parts rounded up to 256 bytes.
+struct ProxyStates {
+    int64_t xp, yp, scans, total;
+    bool has_scans;
+};
+
+bool proxy_states_layout(int64_t n, int64_t c_proxy, int64_t h, int64_t w, int dtype, ProxyStates* K) {
+    if (!valid_dtype(dtype) || !dims_ok({n, c_proxy, h, w}) || c_proxy < 1) return false;
+    const int64_t e = checked_product({n, c_proxy, h, w});
+    if (e < 0 || e > (INT64_MAX / 64)) return false;
+    const int64_t pb = (e * static_cast<int64_t>(elem_size(dtype)) + 255) / 256 * 256;
+    K->xp = 0;
+    K->yp = pb;
+    K->scans = 2 * pb;
+    K->has_scans = !gspn::plane4_supported(h, w);
+    K->total = K->scans + (K->has_scans ? 16 * e : 0);
+    return true;
+}
+
 gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw, int64_t chunk_len,
                        const void* x, const void* w_down, const void* w_up, const void* const logits[4],
-                       const void* const lam[4], const float* merge, void* y, void* workspace,
+                       const void* const lam[4], const float* merge, void* y, void* keep, void* workspace,
                        int64_t workspace_bytes, int dtype, int layout, void* stream, Timer* tm) {
     if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
     if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
@@ -749,15 +770,30 @@ gspn_status proxy_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_pro
             overlap(workspace, need, logits[d], wb) || overlap(workspace, need, lam[d], pb))
             return GSPN_ERR_ALIASING;
     }
+    ProxyStates K;
+    if (keep) {
+        if (!proxy_states_layout(n, c_proxy, h, w, dtype, &K)) return GSPN_ERR_BAD_SHAPE;
+        if (!aligned(keep, 256)) return GSPN_ERR_MISALIGNED;
+        const int64_t kb = K.total;
+        if (overlap(keep, kb, x, xb) || overlap(keep, kb, y, xb) || overlap(keep, kb, w_down, mb) ||
+            overlap(keep, kb, w_up, mb) || overlap(keep, kb, workspace, need) ||
+            (merge && overlap(keep, kb, merge, mgb)))
+            return GSPN_ERR_ALIASING;
+        for (int d = 0; d < 4; ++d)
+            if (overlap(keep, kb, logits[d], wb) || overlap(keep, kb, lam[d], pb)) return GSPN_ERR_ALIASING;
+    }
     char* ws = static_cast<char*>(workspace);
-    void* xp = ws;
-    void* yp = ws + pb;
+    // x_p and y_p in the workspace, or where the caller keeps them
+    char* kp = static_cast<char*>(keep);
+    void* xp = keep ? kp + K.xp : ws;
+    void* yp = keep ? kp + K.yp : ws + pb;
+    float* scans = keep && K.has_scans ? reinterpret_cast<float*>(kp + K.scans) : nullptr;
     char* fws = ws + 2 * pb;
     const hipStream_t st = as_stream(stream);
     if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
               [&] { return gspn::launch_project(n, c, h * w, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
         return GSPN_ERR_HIP;
-    const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, nullptr, fws,
+    const gspn_status s4 = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, scans, fws,
                                          need - 2 * pb, dtype, layout, stream, tm);
     if (s4 != GSPN_OK) return s4;
     return from_hip(timed(tm, GSPN_STAGE_PROJECT_UP,
@@ -1109,9 +1145,9 @@ bool proxy_bwd_layout(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_prox
 gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                 const void* const logits[4], const void* const lam[4], const float* merge,
-                                const void* gy, void* dx, float* dw_down, float* dw_up, void* const dlogits[4],
-                                void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
-                                int dtype, int layout, void* stream, Timer* tm) {
+                                const void* kept, const void* gy, void* dx, float* dw_down, float* dw_up,
+                                void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                                int64_t workspace_bytes, int dtype, int layout, void* stream, Timer* tm) {
     if (!valid_dtype(dtype)) return GSPN_ERR_BAD_DTYPE;
     if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
     if (!dims_ok({n, c, h, w}) || !dims_ok({n, c_proxy, h, w}) || c < 1 || c_proxy < 1) return GSPN_ERR_BAD_SHAPE;
@@ -1178,6 +1214,15 @@ gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int6
     }
     for (int j = 0; j < 13; ++j)
         if (all_in[j] && overlap(workspace, need, all_in[j], ib[j])) return GSPN_ERR_ALIASING;
+    ProxyStates K;
+    if (kept) {
+        // read only: it may overlap inputs, but no output nor the workspace
+        if (!proxy_states_layout(n, c_proxy, h, w, dtype, &K)) return GSPN_ERR_BAD_SHAPE;
+        if (!aligned(kept, 256)) return GSPN_ERR_MISALIGNED;
+        if (overlap(kept, K.total, workspace, need)) return GSPN_ERR_ALIASING;
+        for (int i = 0; i < 12; ++i)
+            if (outs[i] && overlap(kept, K.total, outs[i], ob[i])) return GSPN_ERR_ALIASING;
+    }
     const int64_t hw = h * w;
     // the proxy-space backward's limits, checked before anything is queued
     int64_t chunks[4];
@@ -1189,14 +1234,17 @@ gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int6
     }
     if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c_proxy, h, w, chunks)) return GSPN_ERR_UNSUPPORTED;
     char* ws = static_cast<char*>(workspace);
-    void* xp = ws + L.xp;
-    void* yp = ws + L.yp;
+    const char* kp = static_cast<const char*>(kept);
+    void* xp = kept ? const_cast<char*>(kp + K.xp) : ws + L.xp;
+    void* yp = kept ? const_cast<char*>(kp + K.yp) : ws + L.yp;
     void* gp = ws + L.gp;
     void* dxp = ws + L.dxp;
     void* wtu = ws + L.wtu;  // w_up^T [c_proxy][c]
     void* wtd = ws + L.wtd;  // w_down^T [c][c_proxy]
     float* part = reinterpret_cast<float*>(ws + L.part);
-    float* states = L.keep ? reinterpret_cast<float*>(ws + L.states) : nullptr;
+    float* states = !L.keep ? nullptr
+                    : kept  ? reinterpret_cast<float*>(const_cast<char*>(kp + K.scans))
+                            : reinterpret_cast<float*>(ws + L.states);
     void* inner = ws + L.inner;
     // the weights transposed, for the projections the chain rule needs
     if (timed(tm, GSPN_STAGE_REDUCE, [&] {
@@ -1206,13 +1254,17 @@ gspn_status proxy_backward_impl(int64_t n, int64_t c, int64_t h, int64_t w, int6
             return gspn::launch_transpose(w_down, wtd, 1, static_cast<int>(c_proxy), static_cast<int>(c), dtype, st);
         }) != hipSuccess)
         return GSPN_ERR_HIP;
-    // the forward's proxy-space input and output, recomputed
-    if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
-              [&] { return gspn::launch_project(n, c, hw, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
-        return GSPN_ERR_HIP;
-    gspn_status s = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, states, inner,
-                                  L.inner_bytes, dtype, layout, stream, tm);
-    if (s != GSPN_OK) return s;
+    // the forward's proxy-space input and output (and scans), recomputed
+    // unless kept
+    gspn_status s = GSPN_OK;
+    if (!kept) {
+        if (timed(tm, GSPN_STAGE_PROJECT_DOWN,
+                  [&] { return gspn::launch_project(n, c, hw, c_proxy, x, w_down, xp, dtype, st); }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        s = forward4_impl(n, c_proxy, h, w, cw, chunk_len, xp, logits, lam, merge, yp, states, inner, L.inner_bytes,
+                          dtype, layout, stream, tm);
+        if (s != GSPN_OK) return s;
+    }
     // dL/dy_p = w_up^T gy, and in the same pass over gy the partial sums of
     // dL/dw_up[c][k] = sum gy[c] y_p[k]
     int64_t slots = 0;
@@ -1283,26 +1335,31 @@ int64_t gspn_proxy_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int
     return 2 * checked_product({n, c_proxy, h, w}) * static_cast<int64_t>(elem_size(dtype)) + f4;
 }
 
+int64_t gspn_proxy_states_bytes(int64_t n, int64_t c_proxy, int64_t h, int64_t w, int dtype) {
+    ProxyStates K;
+    return proxy_states_layout(n, c_proxy, h, w, dtype, &K) ? K.total : -1;
+}
+
 gspn_status gspn_proxy_forward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                 int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                 const void* const logits[4], const void* const lam[4], const float* merge,
-                                void* y, void* workspace, int64_t workspace_bytes, int dtype, int layout,
-                                void* stream) {
-    return proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, y, workspace,
+                                void* y, void* states, void* workspace, int64_t workspace_bytes, int dtype,
+                                int layout, void* stream) {
+    return proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, y, states, workspace,
                       workspace_bytes, dtype, layout, stream, nullptr);
 }
 
 gspn_status gspn_proxy_forward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy,
                                       int64_t cw, int64_t chunk_len, const void* x, const void* w_down,
                                       const void* w_up, const void* const logits[4],
-                                      const void* const lam[4], const float* merge, void* y, void* workspace,
-                                      int64_t workspace_bytes, int dtype, int layout, void* stream,
-                                      gspn_stage_times* times) {
+                                      const void* const lam[4], const float* merge, void* y, void* states,
+                                      void* workspace, int64_t workspace_bytes, int dtype, int layout,
+                                      void* stream, gspn_stage_times* times) {
     if (!times) return GSPN_ERR_NULL_POINTER;
     Timer tm;
     tm.st = as_stream(stream);
     const gspn_status s = proxy_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, y,
-                                     workspace, workspace_bytes, dtype, layout, stream, &tm);
+                                     states, workspace, workspace_bytes, dtype, layout, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }
@@ -1362,18 +1419,18 @@ int64_t gspn_proxy_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, in
 gspn_status gspn_proxy_backward4(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                  int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                  const void* const logits[4], const void* const lam[4], const float* merge,
-                                 const void* gy, void* dx, float* dw_down, float* dw_up, void* const dlogits[4],
-                                 void* const dlam[4], float* dmerge, void* workspace, int64_t workspace_bytes,
-                                 int dtype, int layout, void* stream) {
-    return proxy_backward_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, gy, dx,
-                               dw_down, dw_up, dlogits, dlam, dmerge, workspace, workspace_bytes, dtype, layout,
+                                 const void* states, const void* gy, void* dx, float* dw_down, float* dw_up,
+                                 void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
+                                 int64_t workspace_bytes, int dtype, int layout, void* stream) {
+    return proxy_backward_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam, merge, states, gy,
+                               dx, dw_down, dw_up, dlogits, dlam, dmerge, workspace, workspace_bytes, dtype, layout,
                                stream, nullptr);
 }
 
 gspn_status gspn_proxy_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t w, int64_t c_proxy, int64_t cw,
                                        int64_t chunk_len, const void* x, const void* w_down, const void* w_up,
                                        const void* const logits[4], const void* const lam[4], const float* merge,
-                                       const void* gy, void* dx, float* dw_down, float* dw_up,
+                                       const void* states, const void* gy, void* dx, float* dw_down, float* dw_up,
                                        void* const dlogits[4], void* const dlam[4], float* dmerge, void* workspace,
                                        int64_t workspace_bytes, int dtype, int layout, void* stream,
                                        gspn_stage_times* times) {
@@ -1381,8 +1438,8 @@ gspn_status gspn_proxy_backward4_timed(int64_t n, int64_t c, int64_t h, int64_t 
     Timer tm;
     tm.st = as_stream(stream);
     const gspn_status s = proxy_backward_impl(n, c, h, w, c_proxy, cw, chunk_len, x, w_down, w_up, logits, lam,
-                                              merge, gy, dx, dw_down, dw_up, dlogits, dlam, dmerge, workspace,
-                                              workspace_bytes, dtype, layout, stream, &tm);
+                                              merge, states, gy, dx, dw_down, dw_up, dlogits, dlam, dmerge,
+                                              workspace, workspace_bytes, dtype, layout, stream, &tm);
     const hipError_t e = tm.finish(times);
     return s != GSPN_OK ? s : from_hip(e);
 }

@@ -42,7 +42,7 @@ EXPORTS = ("gspn_normalize_weights", "gspn_scan_fwd", "gspn_merge4", "gspn_proxy
            "gspn_proxy_forward4_workspace_bytes", "gspn_proxy_forward4", "gspn_forward4_timed",
            "gspn_proxy_forward4_timed", "gspn_backward4_workspace_bytes", "gspn_backward4", "gspn_backward4_timed",
            "gspn_forward4_noalloc", "gspn_proxy_backward4_workspace_bytes", "gspn_proxy_backward4",
-           "gspn_proxy_backward4_timed", "gspn_status_string", "gspn_abi_version")
+           "gspn_proxy_backward4_timed", "gspn_proxy_states_bytes", "gspn_status_string", "gspn_abi_version")
 
 # GSPN_NOALLOC_SCRATCH_BYTES: the static scratch gspn_forward4_noalloc works in.
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -113,7 +113,10 @@ def lib() -> ctypes.CDLL:
             h.gspn_proxy_forward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci]
             h.gspn_proxy_forward4_workspace_bytes.restype = i64
             h.gspn_proxy_forward4.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp,
-                                              ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, i64, ci, ci, vp]
+                                              ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, i64, ci, ci,
+                                              vp]
+            h.gspn_proxy_states_bytes.argtypes = [i64, i64, i64, i64, ci]
+            h.gspn_proxy_states_bytes.restype = i64
             h.gspn_proxy_forward4.restype = ci
             h.gspn_forward4.argtypes = [i64, i64, i64, i64, i64, i64, vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp, vp, vp, vp, i64, ci, ci, vp]
@@ -137,7 +140,7 @@ def lib() -> ctypes.CDLL:
             h.gspn_proxy_backward4_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci]
             h.gspn_proxy_backward4_workspace_bytes.restype = i64
             h.gspn_proxy_backward4.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp, ctypes.POINTER(vp),
-                                               ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.POINTER(vp),
+                                               ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, ctypes.POINTER(vp),
                                                ctypes.POINTER(vp), vp, vp, i64, ci, ci, vp]
             h.gspn_proxy_backward4.restype = ci
             h.gspn_proxy_backward4_timed.argtypes = h.gspn_proxy_backward4.argtypes + [ctypes.POINTER(StageTimes)]
@@ -444,7 +447,20 @@ def proxy_forward4_workspace(x: torch.Tensor, c_proxy: int, cw: int, layout: str
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
-def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge=None, layout="scan"):
+def proxy_states_buffer(x: torch.Tensor, c_proxy: int) -> torch.Tensor:
+    """A buffer (uint8 tensor on x's device, 256-byte aligned) for the
+    proxy-space state gspn_proxy_forward4 keeps for gspn_proxy_backward4."""
+    n, c, h, w = x.shape
+    nbytes = int(lib().gspn_proxy_states_bytes(n, c_proxy, h, w, _dtype_code(x)))
+    if nbytes < 0:
+        raise ValueError("invalid shape for a proxy states buffer")
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=x.device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge=None, layout="scan",
+                    states=None):
     n, c, h, w = x.shape
     dt = x.dtype
     cp = w_down.shape[0]
@@ -467,7 +483,14 @@ def _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, ti
     zp = (ctypes.c_void_p * 4)(*[z.data_ptr() for z in logits])
     lp = (ctypes.c_void_p * 4)(*[l.data_ptr() for l in lams])
     mp = _merge_ptr(merge, cp, x.device)
-    args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up), zp, lp, mp, _ptr(out),
+    sp = None
+    if states is not None:
+        if states.device != x.device or not states.is_contiguous():
+            raise ValueError("states must be a contiguous buffer on %s" % x.device)
+        if states.numel() * states.element_size() < lib().gspn_proxy_states_bytes(n, cp, h, w, _dtype_code(x)):
+            raise ValueError("states buffer too small (see proxy_states_buffer)")
+        sp = _ptr(states)
+    args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up), zp, lp, mp, _ptr(out), sp,
             _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x), lc, _stream(x.device))
     if times is None:
         _raise(lib().gspn_proxy_forward4(*args), "gspn_proxy_forward4")
@@ -480,22 +503,31 @@ def gspn_proxy_forward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tenso
                         logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                         chunk_len: int = 0, out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, merge: torch.Tensor | None = None,
-                        layout: str = "scan") -> torch.Tensor:
+                        layout: str = "scan", states: torch.Tensor | bool | None = None):
     """Compressive-proxy forward: C -> C_proxy 1x1 projection, four-direction
     scan in proxy space (summed, or weighted by ``merge`` fp32 [4][C_proxy]),
-    C_proxy -> C projection."""
-    return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None, merge, layout)
+    C_proxy -> C projection.  ``states`` (True, or a buffer from
+    proxy_states_buffer) also keeps x_p, y_p and the proxy-space fp32 scans
+    for gspn_proxy_backward4; the call then returns (out, states)."""
+    if states is True:
+        states = proxy_states_buffer(x, w_down.shape[0])
+    if states is None or states is False:
+        return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None, merge, layout)
+    return _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, None, merge, layout,
+                           states), states
 
 
 def gspn_proxy_forward4_timed(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor,
                               logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor],
                               chunk_len: int = 0, out: torch.Tensor | None = None,
                               workspace: torch.Tensor | None = None,
-                              merge: torch.Tensor | None = None, layout: str = "scan") -> tuple[torch.Tensor, dict]:
+                              merge: torch.Tensor | None = None, layout: str = "scan",
+                              states: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
     """gspn_proxy_forward4 with HIP events around every launch; returns (out,
-    {stage: {"ms", "launches"}})."""
+    {stage: {"ms", "launches"}}); ``states``: a buffer to keep the proxy-space
+    state in, as for gspn_proxy_forward4."""
     times = StageTimes()
-    out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge, layout)
+    out = _proxy_forward4(x, w_down, w_up, logits, lams, chunk_len, out, workspace, times, merge, layout, states)
     return out, times.as_dict()
 
 
@@ -581,13 +613,16 @@ def gspn_proxy_backward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tens
                          logits: Sequence[torch.Tensor], lams: Sequence[torch.Tensor], gy: torch.Tensor,
                          chunk_len: int = 0, workspace: torch.Tensor | None = None,
                          times: StageTimes | None = None, merge: torch.Tensor | None = None,
-                         dmerge: torch.Tensor | bool | None = None, layout: str = "scan") -> tuple:
+                         dmerge: torch.Tensor | bool | None = None, layout: str = "scan",
+                         states: torch.Tensor | None = None) -> tuple:
     """Gradients of gspn_proxy_forward4 (with the same ``merge``) for dL/dy =
     gy: returns (dx, dw_down fp32 [C_proxy][C], dw_up fp32 [C][C_proxy],
     [dlogits_d], [dlam_d]) and, when ``merge`` is given or ``dmerge`` is (a
     tensor to fill, or True), the merge weights' gradient (fp32
     [4][C_proxy]) last.  ``times`` (a StageTimes) selects
-    gspn_proxy_backward4_timed; ``layout`` as in gspn_proxy_forward4."""
+    gspn_proxy_backward4_timed; ``layout`` as in gspn_proxy_forward4;
+    ``states`` (what gspn_proxy_forward4 kept for the same inputs) spares the
+    recompute of x_p and of the proxy-space forward."""
     n, c, h, w = x.shape
     dt = x.dtype
     cp = w_down.shape[0]
@@ -615,9 +650,16 @@ def gspn_proxy_backward4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tens
         workspace = proxy_backward4_workspace(x, cp, cw, layout)
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
+    sp = None
+    if states is not None:
+        if states.device != x.device or not states.is_contiguous():
+            raise ValueError("states must be a contiguous buffer on %s" % x.device)
+        if states.numel() * states.element_size() < lib().gspn_proxy_states_bytes(n, cp, h, w, _dtype_code(x)):
+            raise ValueError("states buffer too small (see proxy_states_buffer)")
+        sp = _ptr(states)
     vp4 = ctypes.c_void_p * 4
     args = (n, c, h, w, cp, cw, int(chunk_len), _ptr(x), _ptr(w_down), _ptr(w_up),
-            vp4(*[z.data_ptr() for z in logits]), vp4(*[l.data_ptr() for l in lams]), mp, _ptr(gy), _ptr(dx),
+            vp4(*[z.data_ptr() for z in logits]), vp4(*[l.data_ptr() for l in lams]), mp, sp, _ptr(gy), _ptr(dx),
             _ptr(dwd), _ptr(dwu), vp4(*[t.data_ptr() for t in dz]), vp4(*[t.data_ptr() for t in dl]), dmp,
             _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(x), lc, _stream(x.device))
     if times is None:
@@ -680,32 +722,40 @@ class _ProxyForward4(torch.autograd.Function):
     gspn_proxy_backward4 (weight gradients cast to the weights' dtype)."""
 
     @staticmethod
-    def forward(ctx, chunk_len, has_merge, x, w_down, w_up, merge, *tensors):
+    def forward(ctx, chunk_len, has_merge, keep, x, w_down, w_up, merge, *tensors):
         logits, lams = list(tensors[:4]), list(tensors[4:])
+        states = proxy_states_buffer(x, w_down.shape[0]) if keep else torch.empty(0, device=x.device)
         y = gspn_proxy_forward4(x, w_down, w_up, logits, lams, chunk_len=chunk_len,
-                                merge=merge if has_merge else None)
+                                merge=merge if has_merge else None, states=states if keep else None)
+        if keep:
+            y = y[0]
         ctx.chunk_len = chunk_len
         ctx.has_merge = has_merge
-        ctx.save_for_backward(x, w_down, w_up, merge, *tensors)
+        ctx.keep = keep
+        ctx.save_for_backward(x, w_down, w_up, merge, states, *tensors)
         return y
 
     @staticmethod
     def backward(ctx, gy):
-        x, w_down, w_up, merge, *tensors = ctx.saved_tensors
+        x, w_down, w_up, merge, states, *tensors = ctx.saved_tensors
         logits, lams = tensors[:4], tensors[4:]
         res = gspn_proxy_backward4(x, w_down, w_up, logits, lams, gy.to(x.dtype).contiguous(),
-                                   chunk_len=ctx.chunk_len, merge=merge if ctx.has_merge else None)
+                                   chunk_len=ctx.chunk_len, merge=merge if ctx.has_merge else None,
+                                   states=states if ctx.keep else None)
         dx, dwd, dwu, dz, dl = res[:5]
         dm = res[5] if ctx.has_merge else None
-        return (None, None, dx, dwd.to(w_down.dtype), dwu.to(w_up.dtype), dm, *dz, *dl)
+        return (None, None, None, dx, dwd.to(w_down.dtype), dwu.to(w_up.dtype), dm, *dz, *dl)
 
 
 def gspn_proxy4(x: torch.Tensor, w_down: torch.Tensor, w_up: torch.Tensor, logits: Sequence[torch.Tensor],
-                lams: Sequence[torch.Tensor], chunk_len: int = 0, merge: torch.Tensor | None = None) -> torch.Tensor:
+                lams: Sequence[torch.Tensor], chunk_len: int = 0, merge: torch.Tensor | None = None,
+                keep_states: bool = False) -> torch.Tensor:
     """The compressive-proxy propagation as a differentiable op:
     gspn_proxy_forward4 forward, gspn_proxy_backward4 for the gradients of
     x, both projection weights, the logits, the lambdas and (if given) the
-    merge weights."""
+    merge weights.  keep_states: the forward keeps x_p, y_p and the
+    proxy-space fp32 scans (gspn_proxy_states_bytes, held until the
+    backward) so the backward recomputes none of them."""
     has_merge = merge is not None
     m = merge if has_merge else torch.empty(0, device=x.device)
-    return _ProxyForward4.apply(int(chunk_len), has_merge, x, w_down, w_up, m, *logits, *lams)
+    return _ProxyForward4.apply(int(chunk_len), has_merge, bool(keep_states), x, w_down, w_up, m, *logits, *lams)

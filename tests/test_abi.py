@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gspn_abi_version() == 10
+    assert lib.gspn_abi_version() == 11
     for code in range(13):
         s = lib.gspn_status_string(code).decode()
         assert s.startswith(G.STATUS[code])
@@ -180,8 +180,8 @@ def test_proxy_forward4_validation(lib):
     assert lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 3, 1, 0) == -1
 
     def f(n=1, c=6, h=8, w=8, cp=2, cw=1, chunk=0, x=A, wd=WD, wu=WU, z=zs, l=ls, m=None, y=D_, ws=WS, wsb=need,
-          dt=1, lay=0):
-        return lib.gspn_proxy_forward4(n, c, h, w, cp, cw, chunk, x, wd, wu, z, l, m, y, ws, wsb, dt, lay, None)
+          dt=1, lay=0, st=None):
+        return lib.gspn_proxy_forward4(n, c, h, w, cp, cw, chunk, x, wd, wu, z, l, m, y, st, ws, wsb, dt, lay, None)
 
     assert f(dt=2) == DTYPE
     assert f(cp=-1) == SHAPE
@@ -196,6 +196,9 @@ def test_proxy_forward4_validation(lib):
     assert f(ws=A - 16) == ALIAS
     assert f(m=0x73000001) == MISAL
     assert f(m=WS + 64) == ALIAS                     # merge weights inside the workspace
+    assert f(st=0x7E000010) == MISAL                 # kept state: 256-byte alignment
+    assert f(st=WS + 256) == ALIAS                   # kept state inside the workspace
+    assert f(st=A - 256) == ALIAS                    # kept state over x
     assert f(n=0, x=0, wd=0, wu=0, z=None, l=None, y=0, ws=0) == OK
 
 
@@ -262,8 +265,8 @@ def test_timed_variants_validate_like_untimed(lib):
     need = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1, 0)
 
     def g(n=1, cp=2, ws=WS, wsb=need, dt=1, times=ctypes.byref(t)):
-        return lib.gspn_proxy_forward4_timed(n, 6, 8, 8, cp, 1, 0, A, WD, WU, zs, ls, None, D_, ws, wsb, dt, 0, None,
-                                             times)
+        return lib.gspn_proxy_forward4_timed(n, 6, 8, 8, cp, 1, 0, A, WD, WU, zs, ls, None, D_, None, ws, wsb, dt, 0,
+                                             None, times)
 
     assert g(times=None) == NULLP
     assert g(dt=2) == DTYPE
@@ -367,8 +370,9 @@ def test_layout_argument(lib):
 
     WD, WU, WS = 0x70000000, 0x71000000, 0x72000000
     pneed = lib.gspn_proxy_forward4_workspace_bytes(1, 6, 8, 8, 2, 1, 1, 1)
-    assert lib.gspn_proxy_forward4(1, 6, 8, 8, 2, 1, 0, A, WD, WU, zs, ls, None, D_, WS, pneed, 1, 3, None) == LAYOUT
-    assert lib.gspn_proxy_forward4(1, 6, 8, 8, 2, 1, 0, A, WD, WU, zs, ls, None, D_, WS, pneed - 1, 1, 1,
+    assert lib.gspn_proxy_forward4(1, 6, 8, 8, 2, 1, 0, A, WD, WU, zs, ls, None, D_, None, WS, pneed, 1, 3,
+                                   None) == LAYOUT
+    assert lib.gspn_proxy_forward4(1, 6, 8, 8, 2, 1, 0, A, WD, WU, zs, ls, None, D_, None, WS, pneed - 1, 1, 1,
                                    None) == WSPACE
 
     dzs = vp4(0x40000000, 0x41000000, 0x42000000, 0x43000000)
@@ -436,9 +440,9 @@ def test_proxy_backward4_validation(lib):
     assert need >= lib.gspn_backward4_workspace_bytes(n, cp, h, w, 1, 1, 0) + 4 * n * cp * h * w * es
 
     def f(n=n, c=c, h=h, w=w, cp=cp, cw=1, chunk=0, x=X, gy=GY, dx=DX, dwd=DWD, dwu=DWU, dz=dzs, dl=dls, m=None,
-          dm=None, ws=WS, wsb=need, dt=1, lay=0):
-        return lib.gspn_proxy_backward4(n, c, h, w, cp, cw, chunk, x, WD, WU, zs, ls, m, gy, dx, dwd, dwu, dz, dl,
-                                        dm, ws, wsb, dt, lay, None)
+          dm=None, ws=WS, wsb=need, dt=1, lay=0, st=None):
+        return lib.gspn_proxy_backward4(n, c, h, w, cp, cw, chunk, x, WD, WU, zs, ls, m, st, gy, dx, dwd, dwu, dz,
+                                        dl, dm, ws, wsb, dt, lay, None)
 
     assert f(dt=2) == DTYPE
     assert f(lay=5) == LAYOUT
@@ -462,7 +466,18 @@ def test_proxy_backward4_validation(lib):
     assert f(ws=GY - 64) == ALIAS                             # the workspace over gy
     assert f(h=3000, wsb=1 << 40) == UNSUP                    # longer lines than the proxy-space backward takes
     t = G.StageTimes()
-    assert lib.gspn_proxy_backward4_timed(n, c, h, w, cp, 1, 0, X, WD, WU, zs, ls, None, GY, DX, DWD, DWU, dzs, dls,
-                                          None, WS, need, 1, 0, None, None) == NULLP
-    assert lib.gspn_proxy_backward4_timed(n, c, h, w, cp, 1, 0, X, WD, WU, zs, ls, None, GY, DX, DWD, DWU, dzs, dls,
-                                          None, WS, need, 2, 0, None, ctypes.byref(t)) == DTYPE
+    assert lib.gspn_proxy_backward4_timed(n, c, h, w, cp, 1, 0, X, WD, WU, zs, ls, None, None, GY, DX, DWD, DWU,
+                                          dzs, dls, None, WS, need, 1, 0, None, None) == NULLP
+    assert lib.gspn_proxy_backward4_timed(n, c, h, w, cp, 1, 0, X, WD, WU, zs, ls, None, None, GY, DX, DWD, DWU,
+                                          dzs, dls, None, WS, need, 2, 0, None, ctypes.byref(t)) == DTYPE
+    # kept proxy-space state: its size, alignment and aliasing
+    kb = lib.gspn_proxy_states_bytes(n, cp, h, w, 1)
+    pe = n * cp * h * w
+    small = (h <= 64 and w <= 64)
+    assert kb == 2 * ((pe * es + 255) // 256 * 256) + (0 if small else 16 * pe)
+    assert lib.gspn_proxy_states_bytes(n, 0, h, w, 1) == -1 and lib.gspn_proxy_states_bytes(n, cp, h, w, 2) == -1
+    ST = 0x7E000000
+    assert f(st=ST + 16) == MISAL                             # 256-byte alignment
+    assert f(st=WS + 256) == ALIAS                            # inside the workspace
+    assert f(st=DX - 256) == ALIAS                            # over an output
+

@@ -245,3 +245,67 @@ def test_full_size_proxy_backward():
         e = oracle.normwise_error(_np(dx[:, c:c + 1]), rdx[:, j:j + 1])
         _say("  dx channel %d: normwise error %.3g" % (c, e))
         assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape,dtype,shared,chunk,merge", [
+    ((1, 40, 96, 128, 8), "bf16", True, 0, True),     # planes above 64 x 64: the fp32 scans kept too
+    ((2, 64, 64, 200, 4), "bf16", False, 9, False),   # per-channel logits, chunks
+    ((1, 24, 40, 48, 3), "f32", True, 0, False),      # planes of at most 64 x 64: x_p and y_p only
+])
+def test_proxy_backward_from_kept_states(shape, dtype, shared, chunk, merge):
+    """gspn_proxy_forward4 keeping its proxy-space state (x_p, y_p, the fp32
+    scans), then gspn_proxy_backward4 reading it: the forward agrees with the
+    oracle, and the gradients are those of the recomputing backward (bit for
+    bit, but the fp32-atomic sums of shared logits and of dmerge, up to their
+    order), so also the oracle's."""
+    n, c, h, w, cp = shape
+    wl = Workload("case", n, c, h, w, dtype, shared, chunk, 77 + h + c, c_proxy=cp)
+    _say("proxy backward from kept states %s %s shared=%s chunk=%d merge=%s" % (shape, dtype, shared, chunk, merge))
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 201 + w)
+    m = _merge(cp, 8) if merge else None
+    args = (inp["x"], inp["w_down"], inp["w_up"], inp["logits"], inp["lam"])
+    y, st = G.gspn_proxy_forward4(*args, chunk_len=chunk, merge=m, states=True)
+    kept = G.gspn_proxy_backward4(*args, gy, chunk_len=chunk, merge=m, states=st)
+    full = G.gspn_proxy_backward4(*args, gy, chunk_len=chunk, merge=m)
+    torch.cuda.synchronize()
+    ref_y = oracle.proxy_forward4(_np(inp["x"]), _np(inp["w_down"]), _np(inp["w_up"]),
+                                  [_np(z) for z in inp["logits"]], [_np(l) for l in inp["lam"]], chunk=chunk,
+                                  merge=None if m is None else _np(m))
+    assert oracle.normwise_error(_np(y), ref_y) <= TOL[dtype]
+    for i in range(3):   # dx, dw_down, dw_up
+        assert torch.equal(kept[i], full[i]), i
+    for d in range(4):
+        assert torch.equal(kept[4][d], full[4][d]), d   # dlambda
+        if shared:
+            assert oracle.normwise_error(_np(kept[3][d]), _np(full[3][d])) <= 1e-2, d
+        else:
+            assert torch.equal(kept[3][d], full[3][d]), d
+    if merge:
+        assert oracle.normwise_error(_np(kept[5]), _np(full[5])) <= 1e-5
+    ref = oracle.proxy_backward4(_np(inp["x"]), _np(inp["w_down"]), _np(inp["w_up"]),
+                                 [_np(z) for z in inp["logits"]], [_np(l) for l in inp["lam"]], _np(gy),
+                                 chunk=chunk, merge=None if m is None else _np(m))
+    errs = _errors(kept, ref)
+    _say("  worst normwise error %.3g (%s)" % (max(errs.values()), max(errs, key=errs.get)))
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+def test_proxy_autograd_keeping_states():
+    """gspn_proxy4(keep_states=True) as a training step: the same gradients
+    as without kept states."""
+    wl = Workload("case", 1, 32, 96, 128, "bf16", True, 0, 91, c_proxy=8)
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 17)
+    grads = []
+    for keep in (False, True):
+        x = inp["x"].clone().requires_grad_(True)
+        wd = inp["w_down"].clone().requires_grad_(True)
+        wu = inp["w_up"].clone().requires_grad_(True)
+        lams = [l.clone().requires_grad_(True) for l in inp["lam"]]
+        y = G.gspn_proxy4(x, wd, wu, inp["logits"], lams, keep_states=keep)
+        y.backward(gy)
+        grads.append([x.grad, wd.grad, wu.grad] + [l.grad for l in lams])
+    torch.cuda.synchronize()
+    for a, b in zip(*grads):
+        assert torch.equal(a, b)

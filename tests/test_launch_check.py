@@ -251,10 +251,11 @@ def test_random_shapes_stay_in_bounds(chk, case):
     assert not bad, text
 
 
-def proxy_training_step(lib, n, c, h, w, cp, dtype=torch.bfloat16, shared=True, chunk=0, merge=False):
+def proxy_training_step(lib, n, c, h, w, cp, dtype=torch.bfloat16, shared=True, chunk=0, merge=False, keep=False):
     """The compressive-proxy forward, then its backward, through the check
-    library's C ABI (buffers sized as the binding sizes them); returns the
-    two status codes."""
+    library's C ABI (buffers sized as the binding sizes them); keep: the
+    forward keeps the proxy-space state for the backward; returns the two
+    status codes."""
     sp = Space(lib)
     x = _meta(n, c, h, w, dtype)
     es = x.element_size()
@@ -272,10 +273,12 @@ def proxy_training_step(lib, n, c, h, w, cp, dtype=torch.bfloat16, shared=True, 
     py = sp.buf("y", xb)
     fws = G.proxy_forward4_workspace(x, cp, cw)
     pfw = sp.buf("forward workspace", _nbytes(fws))
+    lib.gspn_proxy_states_bytes.restype = _i64
+    pk = sp.buf("proxy states", lib.gspn_proxy_states_bytes(_i64(n), _i64(cp), _i64(h), _i64(w), dt)) if keep else None
     rf = lib.gspn_proxy_forward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(cp), _i64(cw), _i64(chunk),
                                  ctypes.c_void_p(px), ctypes.c_void_p(pwd), ctypes.c_void_p(pwu), _vp4(*pz), _vp4(*pl),
-                                 ctypes.c_void_p(pm), ctypes.c_void_p(py), ctypes.c_void_p(pfw), _i64(_nbytes(fws)),
-                                 dt, 0, None)
+                                 ctypes.c_void_p(pm), ctypes.c_void_p(py), ctypes.c_void_p(pk), ctypes.c_void_p(pfw),
+                                 _i64(_nbytes(fws)), dt, 0, None)
     pg = sp.buf("dL/dy", xb)
     pdx = sp.buf("dx", xb)
     pdwd = sp.buf("dw_down", cp * c * 4)
@@ -287,7 +290,8 @@ def proxy_training_step(lib, n, c, h, w, cp, dtype=torch.bfloat16, shared=True, 
     pbw = sp.buf("backward workspace", _nbytes(bws))
     rb = lib.gspn_proxy_backward4(_i64(n), _i64(c), _i64(h), _i64(w), _i64(cp), _i64(cw), _i64(chunk),
                                   ctypes.c_void_p(px), ctypes.c_void_p(pwd), ctypes.c_void_p(pwu), _vp4(*pz),
-                                  _vp4(*pl), ctypes.c_void_p(pm), ctypes.c_void_p(pg), ctypes.c_void_p(pdx),
+                                  _vp4(*pl), ctypes.c_void_p(pm), ctypes.c_void_p(pk), ctypes.c_void_p(pg),
+                                  ctypes.c_void_p(pdx),
                                   ctypes.c_void_p(pdwd), ctypes.c_void_p(pdwu), _vp4(*pdz), _vp4(*pdl),
                                   ctypes.c_void_p(pdm), ctypes.c_void_p(pbw), _i64(_nbytes(bws)), dt, 0, None)
     return rf, rb
@@ -314,6 +318,35 @@ def test_proxy_backward_stays_in_bounds(chk, case):
     assert not bad, text
     kernels = set(_kernels(text))
     assert "wgrad_reduce_kernel" in " ".join(kernels), text
+
+
+@pytest.mark.parametrize("case", [
+    dict(n=1, c=320, h=64, w=256, cp=8),                                  # planes > 64 x 64: the scans kept too
+    dict(n=2, c=7, h=40, w=48, cp=2, dtype=torch.float32, shared=False),  # small planes: x_p and y_p only
+], ids=["scans", "small"])
+def test_proxy_training_step_with_kept_states_stays_in_bounds(chk, case):
+    """The compressive-proxy forward keeping its proxy-space state in a
+    buffer of gspn_proxy_states_bytes, the backward reading it instead of
+    recomputing: every replayed launch stays inside its buffers, and the
+    backward launches neither the down projection nor a forward scan."""
+    base = dict(case)
+    case = dict(case)
+    rf, rb = proxy_training_step(chk, case.pop("n"), case.pop("c"), case.pop("h"), case.pop("w"), case.pop("cp"),
+                                 keep=True, **case)
+    text = report(chk)
+    assert (rf, rb) == (0, 0), text
+    bad = [l for l in text.splitlines() if l.startswith("violation") and "without a host replay" not in l]
+    assert not bad, text
+    kept = _kernels(text)
+    rf, rb = proxy_training_step(chk, base.pop("n"), base.pop("c"), base.pop("h"), base.pop("w"), base.pop("cp"),
+                                 **base)
+    assert (rf, rb) == (0, 0)
+    full = _kernels(report(chk))
+    # the same launches but the backward's recompute: one projection (x down)
+    # and the proxy-space forward fewer
+    proj = lambda ks: sum(1 for k in ks if "project" in k and "wgrad" not in k)
+    assert proj(kept) == proj(full) - 1, (kept, full)
+    assert len(kept) < len(full) - 1, (kept, full)
 
 
 @pytest.mark.parametrize("case", [
