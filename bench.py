@@ -267,7 +267,8 @@ def stage_times(wl, inp, out, ws, reps: int, merge=None, layout="scan") -> dict:
 # The sources each measured kernel is built from: its own file, the headers
 # its device code includes, the launch code that configures it (in the same
 # files) and the build flags.  launch.hpp only declares host launchers.
-_SCAN4 = ["scan_kernel.hpp", "scan_lp.hpp", "scan.hip", "scan4_f32.hip", "scan4_bf16.hip", "scan4_bf16pair.hip"]
+_SCAN4 = ["scan_kernel.hpp", "scan_lp.hpp", "coltile.hpp", "scan.hip", "scan4_f32.hip", "scan4_f32x.hip",
+          "scan4_bf16.hip", "scan4_bf16pair.hip"]
 KERNEL_SOURCES = {
     "scan4lp_kernel": _SCAN4,
     "scan4band_kernel": _SCAN4 + ["scan_band.hpp"],
@@ -276,7 +277,7 @@ KERNEL_SOURCES = {
     "adj4_kernel": ["backward.hip"],
     "adj4band_kernel": ["backward.hip"],
     "adjplane_kernel": ["adjplane.hip", "plane_common.hpp"],
-    "seq4_kernel": ["seq4.hip"],
+    "seq4_kernel": ["seq4.hip", "coltile.hpp"],
     "project_narrow_out_mfma": ["project.hip"],
     "project_narrow_in_mfma": ["project.hip"],
     "wgrad_mfma": ["wgrad.hip"],

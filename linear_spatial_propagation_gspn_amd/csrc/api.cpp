@@ -44,6 +44,14 @@ bool dims_ok(std::initializer_list<int64_t> dims) {
     return checked_product(dims) >= 0;
 }
 
+// The long-line scan reading the horizontal directions' x through LDS
+// column tiles instead of a transposed copy (a build parameter, so that the
+// two can be measured against each other).
+#ifndef GSPN_XTILE
+#define GSPN_XTILE 1
+#endif
+constexpr bool xtile_enabled() { return GSPN_XTILE != 0; }
+
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -625,23 +633,48 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         }
     }
 
-    // The horizontal directions become vertical-form scans of x transposed
-    // (their scan frame): line k of step i is x[.., k, i].
-    if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] {
-            return gspn::launch_transpose(x, xt, n * c, static_cast<int>(h), static_cast<int>(w), dtype, st);
-        }) != hipSuccess)
-        return GSPN_ERR_HIP;
+    // The horizontal directions become vertical-form scans in their scan
+    // frame, where line k of step i is x[.., k, i]: of x transposed, or,
+    // where the long-line kernel takes them (lp_xtile_supported), of x itself
+    // read through LDS column tiles, so that no transposed copy is made.
+    const int64_t elems = n * c * h * w;
     for (int d = 2; d < 4; ++d) {
-        p[d].x = xt;
         p[d].h = w;
         p[d].w = h;
         p[d].dir = d - 2;  // L2R runs like T2B, R2L like B2T, in the transposed frame
+    }
+    bool xtile = false;
+    if (xtile_enabled() && gspn::fused4_supported(h, w) && fused_grid_ok(n, c, h, w, chunks)) {
+        gspn::ScanParams q[4] = {p[0], p[1], p[2], p[3]};
+        // the outputs and merge handling of the paths below
+        for (int d = 0; d < 4; ++d) {
+            q[d].mscale = nullptr;
+            if (states) {
+                q[d].out = states + d * elems;
+                q[d].odtype = GSPN_F32;
+            }
+        }
+        if (!states) {
+            q[1].out = m1;
+            q[2].out = m2;
+            q[3].out = m3;
+        }
+        q[2].xtile = q[3].xtile = 1;
+        xtile = gspn::lp_xtile_supported(q);
+    }
+    if (xtile) {
+        p[2].xtile = p[3].xtile = 1;
+    } else {
+        if (timed(tm, GSPN_STAGE_TRANSPOSE, [&] {
+                return gspn::launch_transpose(x, xt, n * c, static_cast<int>(h), static_cast<int>(w), dtype, st);
+            }) != hipSuccess)
+            return GSPN_ERR_HIP;
+        p[2].x = p[3].x = xt;
     }
 
     // With the states wanted: the four directions in one launch, each into
     // its fp32 state map, then y merged from those maps.
     if (states) {
-        const int64_t elems = n * c * h * w;
         for (int d = 0; d < 4; ++d) {
             p[d].out = states + d * elems;
             p[d].odtype = GSPN_F32;

@@ -30,9 +30,20 @@ struct ScanParams {
     int wdtype;  // format of wts: dtype, or for weights normalised beforehand kF32 / kPairF16
     int odtype = -1;  // storage type of out: -1 = dtype; kF32 for fp32 states of bf16 scans
     const float* mscale = nullptr;  // learnable merge: weight of each channel ([c]) for this direction
+    int xtile = 0;  // a vertical-form horizontal scan whose x is the array-frame plane, read through
+                    // LDS column tiles by the long-line kernel (lp_xtile_supported) instead of rows of
+                    // x transposed
 };
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
+
+// Whether the four-direction long-line launch can read the horizontal
+// directions' x through LDS column tiles (ScanParams::xtile) for these
+// vertical-form directions: fp32 storage, one 256-lane workgroup a line,
+// unchunked horizontal scans of a multiple of 32 steps, 16-byte aligned
+// tensors, more lines than the banded kernel takes.  p[2], p[3] describe the
+// horizontal directions in vertical form with x the array-frame plane.
+bool lp_xtile_supported(const ScanParams (&p)[4]);
 
 // The four directions of one forward in one launch; p[d] describes direction d
 // (each with its own output buffer, accumulate = 0).

@@ -28,6 +28,8 @@ extern template hipError_t launch_fused4v<bf16_t, bf16_t>(const Scan4K&, int, in
 extern template hipError_t launch_fused4v<bf16_t, WPair>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4lp<float, float, true>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<float, float, false>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4lp<float, float, true, float, true>(const Scan4K&, int, hipStream_t);
+extern template hipError_t launch_fused4lp<float, float, false, float, true>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true>(const Scan4K&, int, hipStream_t);
 extern template hipError_t launch_fused4v<bf16_t, bf16_t, float>(const Scan4K&, int, int, int, hipStream_t);
 extern template hipError_t launch_fused4lp<bf16_t, bf16_t, true, float>(const Scan4K&, int, hipStream_t);
@@ -93,6 +95,7 @@ ScanK make_args(const ScanParams& p, int P) {
     k.reverse = (p.dir == 1 || p.dir == 3) ? 1 : 0;
     k.logits = p.wts_are_logits ? 1 : 0;
     k.mscale = p.mscale;
+    k.xtile = p.xtile;
     // Row tiles take 16-byte accesses when every tile of every chunk starts
     // on a 16-byte column: rows and chunk starts are whole vectors apart.
     const int ut = horiz_tile_width(esz, P);
@@ -241,6 +244,21 @@ hipError_t launch_scan4_band(const ScanParams (&p)[4], float* state, int index, 
     return launch_band4<bf16_t, bf16_t, true>(b, stream);
 }
 
+bool lp_xtile_supported(const ScanParams (&p)[4]) {
+    if (p[0].dtype != kF32 || !lp_eligible(p)) return false;
+    for (int d = 0; d < 4; ++d)
+        if (p[d].mscale || (p[d].odtype != -1 && p[d].odtype != kF32)) return false;
+    // one 256-lane workgroup a line (the tile's loaders); the horizontal
+    // scans unchunked, their steps whole tiles
+    const int64_t L01 = p[0].w, L23 = p[2].w;
+    const int lanes = lanes_for(static_cast<int>(L01 > L23 ? L01 : L23), 4);
+    if (lanes != lp::kMaxLanes) return false;
+    for (int d = 2; d < 4; ++d)
+        if (p[d].chunk < p[d].h || p[d].h % LpXTile::TS != 0) return false;
+    // more lines than the banded kernel takes
+    return band_launches(p) == 0 && p[0].n * p[0].c * 4 > kBandMaxLines;
+}
+
 hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind) {
     // the separate output maps are merged afterwards (launch_combine), which
     // applies any merge weights
@@ -271,6 +289,10 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
                    (planes + group * 2 - 1) / (group * 2) * 4 >= kLpGroupMinBlocks)
                 group *= 2;
         }
+        const bool xt = p[2].xtile || p[3].xtile;
+        if (xt && (!lp_xtile_supported(p) || !p[2].xtile || !p[3].xtile || p[0].xtile || p[1].xtile))
+            return hipErrorInvalidValue;
+        if (xt) group = 1;
         Scan4K k;
         for (int d = 0; d < 4; ++d) {
             k.d[d] = make_args(p[d], P);
@@ -282,6 +304,10 @@ hipError_t launch_scan4v(const ScanParams (&p)[4], hipStream_t stream, int* kind
         k.planes = planes;
         const int nthreads = lanes * group;
         if (kind) *kind = 3;
+        if (xt) {
+            return logits ? launch_fused4lp<float, float, true, float, true>(k, nthreads, stream)
+                          : launch_fused4lp<float, float, false, float, true>(k, nthreads, stream);
+        }
         if (p[0].dtype == kF32) {
             return logits ? launch_fused4lp<float, float, true>(k, nthreads, stream)
                           : launch_fused4lp<float, float, false>(k, nthreads, stream);

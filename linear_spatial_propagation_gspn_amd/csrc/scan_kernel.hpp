@@ -54,6 +54,7 @@ struct ScanK {
     int logits;    // wts holds logits (1) or normalised weights (0)
     int vec_tile;  // horizontal: every full tile of every chunk allows 16-byte row access
     const float* mscale;  // merge weight of each channel for this direction ([c]), or null for 1
+    int xtile;     // long-line kernel: x is the array-frame plane [L][S], read through LDS column tiles
 };
 
 // Index code of scan_line and the long-line kernel, shared with the host

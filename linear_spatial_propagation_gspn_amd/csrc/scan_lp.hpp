@@ -28,6 +28,7 @@
 
 #include <utility>
 
+#include "coltile.hpp"
 #include "scan_kernel.hpp"
 
 namespace gspn {
@@ -138,14 +139,27 @@ GSPN_HD LpMember lp_member(const Scan4K& a, int64_t pg, int g, int per, int tid)
     return {valid ? p : a.planes - 1, valid, tid - g * per, g * (per >> 6), per >> 6};
 }
 
+// Column tiles for the horizontal directions' x (XT): whole 128-byte runs of
+// every row of the array-frame plane, 128 KB of LDS for lines of 1024
+// positions, the next tile in flight in registers (fp32 only: one 256-lane
+// workgroup a line).
+using LpXTile = coltile::Tile<float, lp::kMaxLanes, 128>;
+#ifndef GSPN_LP_XT_DEPTH
+#define GSPN_LP_XT_DEPTH 8
+#endif
+
 // One (plane, chunk) line of a vertical-form scan, run by `nwaves` waves of
 // the workgroup starting at wave `wave0`; tid is the thread's index among
 // them.  valid = false: the waves only keep step with the workgroup's
 // barriers (p is then any existing plane).  T: storage of x, lambda and the
 // output; TW: storage of the weights (WPair: packed half pairs of
 // channel-shared weights); LOGITS: the weights are logits normalised here
-// (else normalised weights, zero outside the line).
-template <typename T, typename TW, bool LOGITS, typename TO = T>
+// (else normalised weights, zero outside the line).  XT: a horizontal
+// direction whose x is the array-frame plane [L][S] (a.xtile), its column
+// i read from an LDS column tile instead of row i of x transposed; one
+// unchunked line a workgroup of lp::kMaxLanes threads (tid = threadIdx.x),
+// S a multiple of the tile's 32 steps.
+template <typename T, typename TW, bool LOGITS, typename TO = T, bool XT = false>
 __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool valid, int tid, int wave0,
                                         int nwaves) {
     constexpr int P = 16 / static_cast<int>(sizeof(T));              // positions per lane
@@ -154,8 +168,10 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
     constexpr int ZB = PAIR ? 4 : static_cast<int>(sizeof(TW));      // weight bytes per position and row
     constexpr int NZ = PAIR ? 1 : 3;                                  // weight rows
     constexpr int WW = P * ZB / 4;                                    // words per lane: one weight row
-    constexpr int D = GSPN_LP_DEPTH;                                  // steps in flight
+    constexpr int D = XT ? GSPN_LP_XT_DEPTH : GSPN_LP_DEPTH;          // steps in flight
+    static_assert(!XT || sizeof(T) == 4, "column tiles of fp32 x only");
     __shared__ float edges[2][lp::kMaxWaves][2];
+    __shared__ uint32_t xtl[XT ? coltile::tile_dwords<128>() : 1];
 
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -188,11 +204,11 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
     const bool rev = a.reverse != 0;
     auto line_of = [&](int t) { return lp_row(t, S, rev); };
 
-    uint32_t sx[D][WT], sl[D][WT], sz[D][NZ][WW];
+    uint32_t sx[XT ? 1 : D][WT], sl[D][WT], sz[D][NZ][WW];
     auto fill = [&](auto slot, int t) {
         constexpr int s = decltype(slot)::value;
         const uint32_t i = line_of(lp_fill_step(t, t1));
-        lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, i * rowT);
+        if constexpr (!XT) lp::load_words<WT, GSPN_LP_X_AUX>(sx[s], rx, vt, i * rowT);
         lp::load_words<WT, GSPN_LP_STREAM_AUX>(sl[s], rl, vt, i * rowT);
         // logits are per channel here unless a single channel shares them;
         // normalised weights are always shared
@@ -208,13 +224,31 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
 
     // Step t from slot s; FIRST: the first line of the chunk (h_prev = 0 and
     // its weights unused).  The slot is refilled with step t + D.
+    // the x words of step t: the ring slot, or (XT) the lane's positions of
+    // the tile row of x's column line_of(t)
+    const int k0c = active ? k0 : L - P;
+    auto x_words = [&](auto slot, int t, uint32_t (&xw)[WT]) {
+        constexpr int s = decltype(slot)::value;
+        if constexpr (XT) {
+            const int tt = static_cast<int>(line_of(t)) % LpXTile::TS;
+            const lp::int4v v = *reinterpret_cast<const lp::int4v*>(xtl + tt * LpXTile::row_stride(L) + k0c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xw[e] = static_cast<uint32_t>(v[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < WT; ++e) xw[e] = sx[s][e];
+        }
+    };
+
     auto step = [&](auto slot, auto firstc, int t) {
         constexpr int s = decltype(slot)::value;
         constexpr bool FIRST = decltype(firstc)::value != 0;
+        uint32_t xw[WT];
+        x_words(slot, t, xw);
         float hn[P];
         if constexpr (FIRST) {
 #pragma unroll
-            for (int j = 0; j < P; ++j) hn[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+            for (int j = 0; j < P; ++j) hn[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(xw, j);
         } else if constexpr (PAIR) {
             // h + w_{k-1} (h_{k-1} - h) + w_{k+1} (h_{k+1} - h) + lambda x: the
             // same row-stochastic combination with the centre weight
@@ -234,13 +268,13 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
             dd[P] = right - h[P - 1];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                const float base = __builtin_fmaf(lp::elem<T, WT>(sl[s], j), lp::elem<T, WT>(sx[s], j), h[j]);
+                const float base = __builtin_fmaf(lp::elem<T, WT>(sl[s], j), lp::elem<T, WT>(xw, j), h[j]);
                 hn[j] = __builtin_fmaf(pair_hi(sz[s][0][j]), dd[j + 1], __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base));
             }
         } else {
             float u[P];
 #pragma unroll
-            for (int j = 0; j < P; ++j) u[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(sx[s], j);
+            for (int j = 0; j < P; ++j) u[j] = lp::elem<T, WT>(sl[s], j) * lp::elem<T, WT>(xw, j);
             float w[3][P];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
@@ -302,6 +336,40 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
         __syncthreads();
     };
 
+    if constexpr (XT) {
+        // One loop iteration per column tile of TS steps, its steps unrolled
+        // (TS a multiple of D, so the ring slots are compile-time): the next
+        // tile's loads are issued at the top, a whole tile ahead, and the
+        // first tile's first step is peeled (h_prev = 0).  Lanes past the
+        // line read the line's last positions (k0c) and store nothing.
+        constexpr int TS = LpXTile::TS;
+        static_assert(TS % D == 0, "ring slots align with tiles");
+        LpXTile tl;
+        const int R = L, C = S;  // x [L][S]: the line's positions are its rows, the steps its columns
+        auto block_of = [&](int t) { return static_cast<int>(line_of(t)) / TS * TS; };
+        tl.template load<GSPN_LP_X_AUX>(rx, R, C, block_of(0), tid);
+        [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+            (fill(IC<Ss>{}, Ss), ...);
+        }(std::make_integer_sequence<int, D>{});
+        // every lane is past the previous tile (the last step's barrier)
+        tl.store(xtl, R, tid);
+        __syncthreads();
+        tl.template load<GSPN_LP_X_AUX>(rx, R, C, block_of(TS < S ? TS : S - 1), tid);
+        step(IC<0>{}, IC<1>{}, 0);
+        [&]<int... Js>(std::integer_sequence<int, Js...>) {
+            (step(IC<(Js + 1) % D>{}, IC<0>{}, Js + 1), ...);
+        }(std::make_integer_sequence<int, TS - 1>{});
+        for (int tb = TS; tb < S; tb += TS) {
+            tl.store(xtl, R, tid);
+            __syncthreads();
+            tl.template load<GSPN_LP_X_AUX>(rx, R, C, block_of(tb + TS < S ? tb + TS : S - 1), tid);
+            [&]<int... Js>(std::integer_sequence<int, Js...>) {
+                (step(IC<Js % D>{}, IC<0>{}, tb + Js), ...);
+            }(std::make_integer_sequence<int, TS>{});
+        }
+        return;
+    }
+
     // prologue: D steps in flight, then the chunk's first line
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         (fill(IC<Ss>{}, t0 + Ss), ...);
@@ -324,7 +392,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
 // Four vertical-form scans in one launch; block b is direction b % 4 when the
 // directions have equal block counts (Scan4K::interleave), else consecutive
 // ranges, as in scan4v_kernel.
-template <typename T, typename TW, bool LOGITS, typename TO = T>
+template <typename T, typename TW, bool LOGITS, typename TO = T, bool XT = false>
 __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) {
     int dir;
     int64_t idx;
@@ -340,7 +408,13 @@ __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) 
     // keep the plane's buffer resources in scalar registers
     const int g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / per);
     const LpMember m = lp_member(a, pg, g, per, static_cast<int>(threadIdx.x));
-    lp_line<T, TW, LOGITS, TO>(k, m.p, q, m.valid, m.tid, m.wave0, m.nwaves);
+    if constexpr (XT) {
+        // the horizontal directions through column tiles, the vertical ones as usual
+        if (k.xtile) lp_line<T, TW, LOGITS, TO, true>(k, m.p, q, m.valid, m.tid, m.wave0, m.nwaves);
+        else lp_line<T, TW, LOGITS, TO, false>(k, m.p, q, m.valid, m.tid, m.wave0, m.nwaves);
+    } else {
+        lp_line<T, TW, LOGITS, TO>(k, m.p, q, m.valid, m.tid, m.wave0, m.nwaves);
+    }
 }
 
 #ifdef GSPN_CHECK_LAUNCHES
@@ -351,7 +425,7 @@ __global__ __launch_bounds__(lp::kMaxLanes) void scan4lp_kernel(const Scan4K a) 
 // for the chunk's steps by active lanes).  An access must lie in its
 // tensor's buffer and inside its resource (the hardware would drop it
 // silently otherwise).
-template <typename T, typename TW, bool LOGITS, typename TO>
+template <typename T, typename TW, bool LOGITS, typename TO, bool XT>
 void replay_fused4lp(const Scan4K& k, int nthreads) {
     const char* kn = "scan4lp_kernel";
     constexpr int P = 16 / static_cast<int>(sizeof(T));
@@ -361,7 +435,7 @@ void replay_fused4lp(const Scan4K& k, int nthreads) {
     constexpr int NZ = PAIR ? 1 : 3;
     constexpr int WW = P * ZB / 4;
     constexpr int WO = P * static_cast<int>(sizeof(TO)) / 4;
-    constexpr int D = GSPN_LP_DEPTH;
+    constexpr int D = XT ? GSPN_LP_XT_DEPTH : GSPN_LP_DEPTH;
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
     if (k.group < 1 || nthreads % k.group != 0 || (nthreads / k.group) % 64 != 0)
         check::violation(kn, "block", "%d threads do not split into %d whole-wave members", nthreads, k.group);
@@ -413,11 +487,32 @@ void replay_fused4lp(const Scan4K& k, int nthreads) {
             for (int tid = g * per; tid < (g + 1) * per; ++tid) {
                 const LpMember mt = lp_member(k, pg, g, per, tid);
                 const LpLane ln = lp_lane(mt.tid, mt.valid, L, P, sizeof(T), ZB, sizeof(TO));
+                const bool xt = XT && a.xtile;
+                if (xt) {
+                    // column tiles of x [L][S]: every tile's loads (the next
+                    // tile's at the top of each, the last reloading its own)
+                    // and the lane's tile-row reads
+                    constexpr int TS = LpXTile::TS;
+                    if (S % TS != 0 || k.group != 1 || nthreads != lp::kMaxLanes || a.nchunks != 1)
+                        fail("column tiles", b, tid, -1);
+                    for (int tb = 0; tb <= S; tb += TS) {
+                        const int c0 = lp_row(tb < S ? tb : S - 1, S, rev) / TS * TS;
+                        for (int qd = 0; qd < LpXTile::NQ; ++qd) {
+                            const int64_t off = coltile::chunk_offset(qd * lp::kMaxLanes + tid, L, S, c0, 4,
+                                                                      LpXTile::CPR);
+                            if (off + 16 > nt || !check::in_region(rx[dir], xb, off, 16)) fail("x tile load", b, tid, tb);
+                        }
+                        n += LpXTile::NQ;
+                    }
+                    const int k0c = ln.active ? mt.tid * P : L - P;
+                    if ((TS - 1) * LpXTile::row_stride(L) + k0c + 4 > coltile::tile_dwords<128>())
+                        fail("x tile LDS read", b, tid, -1);
+                }
                 for (int t = t0; t < t1 + D; ++t) {
                     const uint32_t i = lp_row(lp_fill_step(t, t1), S, rev);
                     for (int v = 0; v < WT / 4; ++v) {
                         const int64_t off = static_cast<int64_t>(ln.vt) + 16 * v + static_cast<int64_t>(i) * rowT;
-                        if (off + 16 > nt || !check::in_region(rx[dir], xb, off, 16)) fail("x load", b, tid, t);
+                        if (!xt && (off + 16 > nt || !check::in_region(rx[dir], xb, off, 16))) fail("x load", b, tid, t);
                         if (off + 16 > nt || !check::in_region(rl[dir], lb, off, 16)) fail("lambda load", b, tid, t);
                     }
                     for (int o = 0; o < NZ; ++o)
@@ -441,7 +536,8 @@ void replay_fused4lp(const Scan4K& k, int nthreads) {
     }
     if (bad) check::violation(kn, "accesses", "%lld bad", static_cast<long long>(bad));
     check::count_accesses(n);
-    check::replayed(kn, lp::kMaxLanes, sizeof(float) * 2 * lp::kMaxWaves * 2);
+    check::replayed(kn, lp::kMaxLanes,
+                    sizeof(float) * 2 * lp::kMaxWaves * 2 + (XT ? 4 * coltile::tile_dwords<128>() : 0));
 }
 #endif
 
@@ -478,14 +574,17 @@ GSPN_HD size_t lp_lds_reserve(int64_t nblocks, int nthreads, int64_t cus) {
     return static_cast<size_t>(kCuLdsBytes / (per_cu + 1) + 1024);
 }
 
-template <typename T, typename TW, bool LOGITS, typename TO = T>
+// XT: the horizontal directions marked xtile read x through column tiles;
+// their 128 KB of static LDS already leave one workgroup a CU, so no LDS is
+// reserved.
+template <typename T, typename TW, bool LOGITS, typename TO = T, bool XT = false>
 hipError_t launch_fused4lp(const Scan4K& k, int nthreads, hipStream_t stream) {
     const int64_t nblocks = k.blocks[0] + k.blocks[1] + k.blocks[2] + k.blocks[3];
 #ifdef GSPN_CHECK_LAUNCHES
-    replay_fused4lp<T, TW, LOGITS, TO>(k, nthreads);
+    replay_fused4lp<T, TW, LOGITS, TO, XT>(k, nthreads);
 #endif
-    const size_t reserve = lp_lds_reserve(nblocks, nthreads, device_compute_units());
-    hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS, TO>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads),
+    const size_t reserve = XT ? 0 : lp_lds_reserve(nblocks, nthreads, device_compute_units());
+    hipLaunchKernelGGL((scan4lp_kernel<T, TW, LOGITS, TO, XT>), dim3(static_cast<unsigned>(nblocks)), dim3(nthreads),
                        reserve, stream, k);
     return hipGetLastError();
 }

@@ -36,6 +36,7 @@
 #include <atomic>
 
 #include "device.hpp"
+#include "coltile.hpp"
 #include "launch.hpp"
 
 namespace gspn {
@@ -55,7 +56,7 @@ constexpr int kP = 4;                      // positions per lane
 #define GSPN_SEQ4_TILE_ROW_BYTES 128
 #endif
 constexpr int kTileRowBytes = GSPN_SEQ4_TILE_ROW_BYTES;
-constexpr int kTileDwords = (kTileRowBytes / 2) * 514;  // LDS tile: TS rows of RS dwords (both storage types)
+constexpr int kTileDwords = coltile::tile_dwords<kTileRowBytes>();  // LDS tile: TS rows of RS dwords
 // planes per workgroup, each on its own four waves: with channel-shared
 // weights the planes' weight loads then coincide in time and all but the
 // first are served by the cache
@@ -160,90 +161,9 @@ struct Seq4K {
 
 namespace {
 
-// Column tiles: the column block [c0, c0 + TS) of every row of an R x C
-// source matrix (row-major, element type T; R and C multiples of 64) lands
-// in LDS step-major: tile row tt (column c0 + tt) holds the R values of that
-// column, RS dwords apart.  TS = kTileRowBytes / sizeof(T) columns.  fp32:
-// RS = R + 4 dwords (16-byte aligned rows); bf16: rows of R/2 dwords each
-// holding two consecutive source rows' values (low half the even row),
-// RS = R/2 + 2.
-// A row's run of kTileRowBytes is CPR chunks of 16 bytes.  Lane tid loads
-// chunk g = q * kLanes + tid of round q: 16 bytes of row g / CPR (fp32) or
-// of rows 2 (g / CPR) and 2 (g / CPR) + 1 (bf16), from column
-// 16/sizeof(T) * (g % CPR) of the block, so CPR consecutive lanes read one
-// whole run of a row.
+// Column tiles of x (and of z): 128-byte runs of every row (coltile.hpp).
 template <typename T>
-struct Tile {
-    static constexpr bool F32 = sizeof(T) == 4;
-    static constexpr int TS = kTileRowBytes / static_cast<int>(sizeof(T));
-    static constexpr int CPR = kTileRowBytes / 16;          // 16-byte chunks per row
-    static constexpr int CSH = CPR == 8 ? 3 : 2;            // log2 CPR
-    static constexpr int NQ = 1024 * CPR / kLanes;          // chunks per lane for R = 1024
-    uint32_t q[NQ][4];
-
-    __device__ static int row_stride(int R) { return F32 ? R + 4 : R / 2 + 2; }
-
-    // Issue the loads of column block c0 (rounds beyond R rows clamp their
-    // addresses into the matrix and are not stored).
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int R, int C, int c0, int tid) {
-        const uint32_t rowb = static_cast<uint32_t>(C) * sizeof(T);
-        if constexpr (F32) {
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int g = i * kLanes + tid;
-                const int r = min(g >> CSH, R - 1);
-                const uint32_t off = static_cast<uint32_t>(r) * rowb + (c0 + 4 * (g & (CPR - 1))) * 4u;
-                uint32_t (&d)[4] = q[i];
-                ldw<4, kNT>(d, src, off, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NQ / 2; ++i) {
-                const int g = i * kLanes + tid;
-                const int r = min(2 * (g >> CSH), R - 2);
-                const uint32_t off = static_cast<uint32_t>(r) * rowb + (c0 + 8 * (g & (CPR - 1))) * 2u;
-                uint32_t (&d0)[4] = q[2 * i];
-                uint32_t (&d1)[4] = q[2 * i + 1];
-                ldw<4, kNT>(d0, src, off, 0);
-                ldw<4, kNT>(d1, src, off + rowb, 0);
-            }
-        }
-    }
-
-    // Write the loaded block into LDS (the caller makes sure no lane still
-    // reads the previous block, and synchronises before the new one is read).
-    __device__ __forceinline__ void store(uint32_t* lds, int R, int tid) const {
-        const int RS = row_stride(R);
-        if constexpr (F32) {
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int g = i * kLanes + tid;
-                const int r = g >> CSH;
-                if (r < R) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) lds[(4 * (g & (CPR - 1)) + e) * RS + r] = q[i][e];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NQ / 2; ++i) {
-                const int g = i * kLanes + tid;
-                const int rp = g >> CSH;
-                if (2 * rp < R) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t a = q[2 * i][e >> 1];
-                        const uint32_t b = q[2 * i + 1][e >> 1];
-                        // low half: the even row's value, high half: the odd row's
-                        const uint32_t v = (e & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                                                   : __builtin_amdgcn_perm(b, a, 0x05040100u);
-                        lds[(8 * (g & (CPR - 1)) + e) * RS + rp] = v;
-                    }
-                }
-            }
-        }
-    }
-};
+using Tile = coltile::Tile<T, kLanes, kTileRowBytes>;
 
 // One direction's scan over a whole plane.  MODE: 0 L2R (x tiles, z = h),
 // 1 R2L (x tiles, z += h), 2 T2B (x rows, y = h + z^T tiles), 3 B2T (x rows,
@@ -428,7 +348,7 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
 
     // the tile block holding array column (horizontal) / z column (T2B) i
     auto block_of = [&](int t) { return (line_of(t) / TS) * TS; };
-    if constexpr (TILE) tl.load(rsrc_tile, tR, tC, block_of(0), tid);
+    if constexpr (TILE) tl.template load<kNT>(rsrc_tile, tR, tC, block_of(0), tid);
     [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         (fill(IC<Ss>{}, Ss), ...);
     }(std::make_integer_sequence<int, D>{});
@@ -444,7 +364,7 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
             // every lane is past the previous block (the last step's barrier)
             tl.store(tile, tR, tid);
             __syncthreads();
-            tl.load(rsrc_tile, tR, tC, block_of(min(t0 + TS, S - 1)), tid);
+            tl.template load<kNT>(rsrc_tile, tR, tC, block_of(min(t0 + TS, S - 1)), tid);
         }
         [&]<int... Js>(std::integer_sequence<int, Js...>) {
             (step(IC<Js % D>{}, t0 + Js), ...);

@@ -561,3 +561,40 @@ def test_full_size_proxy_sampled_channels():
         e = _err(got[:, c:c + 1], ref[:, j:j + 1])
         _say("  channel %d: normwise error %.3g" % (c, e))
         assert e <= 2e-2
+
+
+@pytest.mark.parametrize("shape,shared,merge,keep", [
+    ((1, 17, 1024, 64), False, False, False),   # 1024-row horizontal lines, two column tiles
+    ((2, 9, 1024, 96), False, True, False),     # three tiles, learnable merge, two images
+    ((1, 20, 1024, 128), True, False, False),   # channel-shared fp32 weight triples
+    ((1, 17, 1024, 64), False, False, True),    # the forward keeping its fp32 states
+    ((1, 17, 960, 64), False, False, False),    # lines of 960 rows: the tile's last rounds unused
+])
+def test_long_line_column_tiles(shape, shared, merge, keep):
+    """fp32 planes whose lines take one 256-lane workgroup: the long-line
+    scan's horizontal directions read x through LDS column tiles (no
+    transposed copy, no transpose launch) and match the oracle."""
+    n, c, h, w = shape
+    wl = _wl(n=n, c=c, h=h, w=w, dtype="f32", shared=shared, seed=61 + w + c)
+    _say("column tiles %s shared=%s merge=%s keep=%s" % (shape, shared, merge, keep))
+    inp = make_inputs(wl, DEV)
+    m = None
+    if merge:
+        g = torch.Generator(device=DEV)
+        g.manual_seed(3)
+        m = torch.randn((4, c), generator=g, device=DEV)
+    st = G.states_buffer(inp["x"]) if keep else None
+    got, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"],
+                                       workspace=G.forward4_workspace(inp["x"], wl.cw), merge=m, states=st)
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "scan4lp_kernel", times["scan_kernel"]
+    assert times["transpose"]["launches"] == 0, times
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], merge=None if m is None else _np(m))
+    assert _err(got, ref) <= TOL["f32"]
+    if keep:
+        # the kept states are the four unweighted scans in their scan frames
+        for d in range(4):
+            hd = G.state_map(st, d, tuple(inp["x"].shape))
+            rd = oracle.scan(d, _np(inp["x"]), _np(inp["logits"][d]), _np(inp["lam"][d]), 0)
+            rd = rd if d < 2 else rd.transpose(0, 1, 3, 2)   # the oracle's map is in the array frame
+            assert oracle.normwise_error(_np(hd), rd) <= TOL["f32"], d

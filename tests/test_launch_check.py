@@ -392,16 +392,17 @@ def _lp_dynamic_lds(text: str) -> int:
 
 
 @pytest.mark.parametrize("c, h, w, reserved", [
-    (64, 8, 1024, True),    # four-wave workgroups, 256 of them: one whole round of one a CU
-    (65, 8, 1024, False),   # 260: a second round nearly empty, so none reserved
-    (64, 8, 256, False),    # one-wave workgroups (short lines): as many a CU as fit
+    (64, 8, 2048, True),    # four-wave workgroups, 256 of them: one whole round of one a CU
+    (65, 8, 2048, False),   # 260: a second round nearly empty, so none reserved
+    (64, 8, 512, False),    # one-wave workgroups (short lines): as many a CU as fit
 ])
 def test_long_line_scan_lds_reservation(chk, c, h, w, reserved):
     """The long-line scan reserves LDS it does not use, so that one four-wave
     workgroup runs a CU (on the checking build's 256 CUs), only where the grid
     is whole rounds of them; the reservation leaves room for one workgroup,
-    not two."""
-    assert forward_only(chk, 1, c, h, w) == 0
+    not two.  (bf16: fp32 planes of such lines read x through column tiles,
+    whose static LDS leaves one workgroup a CU anyway.)"""
+    assert forward_only(chk, 1, c, h, w, torch.bfloat16) == 0
     text = report(chk)
     assert chk.gspn_check_violations() == 0, text
     lds = _lp_dynamic_lds(text)
@@ -409,3 +410,28 @@ def test_long_line_scan_lds_reservation(chk, c, h, w, reserved):
         assert 80 * 1024 < lds <= 160 * 1024 - 1024, text
     else:
         assert lds == 0, text
+
+
+@pytest.mark.parametrize("n, c, h, w, keep", [
+    (1, 17, 1024, 64, False),    # 1024-row horizontal lines of 64 steps: two column tiles
+    (1, 17, 1024, 96, True),     # three tiles, the states kept (fp32 maps written by the scan)
+])
+def test_long_line_scan_column_tiles(chk, n, c, h, w, keep):
+    """fp32 planes whose lines take one 256-lane workgroup: the long-line
+    scan's horizontal directions read x through LDS column tiles instead of a
+    transposed copy (no transpose launch in the forward); every tile load
+    and tile-row read stays in bounds, and the tile is the kernel's static
+    LDS."""
+    if keep:
+        rf, rb = training_step(chk, n, c, h, w)
+        assert (rf, rb) == (0, 0)
+    else:
+        assert forward_only(chk, n, c, h, w) == 0
+    text = report(chk)
+    assert chk.gspn_check_violations() == 0, text
+    ks = _kernels(text)
+    fwd = ks[:ks.index("(combine_kernel<float,") + 1]
+    assert "transpose_kernel<float>" not in fwd, text
+    lines = [l for l in text.splitlines() if l.startswith("launch ") and "scan4lp_kernel" in l]
+    dyn, static = (int(v) for v in lines[0].split("lds=")[1].split("+"))
+    assert dyn == 0 and static > 128 * 1024, text   # the column tile is static LDS; nothing reserved
