@@ -144,8 +144,16 @@ GSPN_HD LpMember lp_member(const Scan4K& a, int64_t pg, int g, int per, int tid)
 // positions, the next tile in flight in registers (fp32 only: one 256-lane
 // workgroup a line).
 using LpXTile = coltile::Tile<float, lp::kMaxLanes, 128>;
+// steps in flight (a divisor of the tile's 32 steps): 4 and 8 measured the
+// same, 2 and 16 slower (profile step 3.08 and 4.35 ms against 2.70)
 #ifndef GSPN_LP_XT_DEPTH
-#define GSPN_LP_XT_DEPTH 8
+#define GSPN_LP_XT_DEPTH 4
+#endif
+// cache policy of the column tiles' loads: non-temporal (the opposite
+// direction reads x again only a whole scan later); with the default policy
+// the profile scan took 2.44 ms against 2.26
+#ifndef GSPN_LP_XTILE_AUX
+#define GSPN_LP_XTILE_AUX 2
 #endif
 
 // One (plane, chunk) line of a vertical-form scan, run by `nwaves` waves of
@@ -347,14 +355,14 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
         LpXTile tl;
         const int R = L, C = S;  // x [L][S]: the line's positions are its rows, the steps its columns
         auto block_of = [&](int t) { return static_cast<int>(line_of(t)) / TS * TS; };
-        tl.template load<GSPN_LP_X_AUX>(rx, R, C, block_of(0), tid);
+        tl.template load<GSPN_LP_XTILE_AUX>(rx, R, C, block_of(0), tid);
         [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
             (fill(IC<Ss>{}, Ss), ...);
         }(std::make_integer_sequence<int, D>{});
         // every lane is past the previous tile (the last step's barrier)
         tl.store(xtl, R, tid);
         __syncthreads();
-        tl.template load<GSPN_LP_X_AUX>(rx, R, C, block_of(TS < S ? TS : S - 1), tid);
+        tl.template load<GSPN_LP_XTILE_AUX>(rx, R, C, block_of(TS < S ? TS : S - 1), tid);
         step(IC<0>{}, IC<1>{}, 0);
         [&]<int... Js>(std::integer_sequence<int, Js...>) {
             (step(IC<(Js + 1) % D>{}, IC<0>{}, Js + 1), ...);
@@ -362,7 +370,7 @@ __device__ __forceinline__ void lp_line(const ScanK& a, int64_t p, int q, bool v
         for (int tb = TS; tb < S; tb += TS) {
             tl.store(xtl, R, tid);
             __syncthreads();
-            tl.template load<GSPN_LP_X_AUX>(rx, R, C, block_of(tb + TS < S ? tb + TS : S - 1), tid);
+            tl.template load<GSPN_LP_XTILE_AUX>(rx, R, C, block_of(tb + TS < S ? tb + TS : S - 1), tid);
             [&]<int... Js>(std::integer_sequence<int, Js...>) {
                 (step(IC<Js % D>{}, IC<0>{}, tb + Js), ...);
             }(std::make_integer_sequence<int, TS>{});
