@@ -106,7 +106,9 @@ def test_backward_from_states(dtype, shape, shared, chunk, merge):
             assert torch.allclose(a[1][d].float(), b[1][d].float(), rtol=1e-5, atol=1e-6)
         else:
             assert torch.equal(a[1][d], b[1][d])
-    assert torch.allclose(a[3], b[3], rtol=1e-5, atol=1e-5)   # dmerge: fp32 atomics
+    # dmerge: fp32 atomic sums in an order that varies between calls, each
+    # entry a sum with cancellation, so compared normwise
+    assert (a[3] - b[3]).abs().max() <= 1e-5 * b[3].abs().max()
     o = oracle.backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk=chunk, merge=None if m is None else _np(m))
     assert oracle.normwise_error(_np(a[0]), o[0]) <= TOL[dtype]
     for d in range(4):
