@@ -218,10 +218,13 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              R2L.  It needs the workspace and lines of at most 2048
  *              positions (else GSPN_ERR_WORKSPACE / GSPN_ERR_UNSUPPORTED).
  *              Planes of at most 64 x 64 then leave their one-pass path
- *              (which keeps no states) for the four-direction launch; y
- *              is then merged from these fp32 maps, so for bf16 storage it
- *              can differ from the y of a call without states in the last
- *              bf16 place.
+ *              (which keeps no states) for the four-direction launch, and
+ *              so do many big planes given merge weights; y is then merged
+ *              from these fp32 maps, so for bf16 storage it can differ from
+ *              the y of a call without states in the last bf16 place.
+ *              Without merge weights many big planes keep the
+ *              plane-sequential kernel, which writes the same maps bit for
+ *              bit, and the same y as without states.
  *   workspace  optional device buffer of workspace_bytes bytes, 4-byte
  *              aligned.  NULL (or 0 bytes): the directions run one after
  *              another, the first writing y and the others adding to it, and
@@ -377,7 +380,8 @@ int64_t gspn_backward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t 
  * inputs (layout there), 4-byte aligned, overlapping no output and not the
  * workspace: the adjoint reads them instead of recomputing the forward.
  * Without them the forward states are recomputed inside, in fp32 and with
- * the same kernel, so both ways give the same gradients bit for bit.
+ * the same per-position arithmetic, so both ways give the same gradients bit
+ * for bit.
  * workspace: required, gspn_backward4_workspace_bytes() bytes (16 * n*c*h*w
  * fewer with states), 4-byte aligned.  Outputs may overlap neither an input,
  * the workspace nor each other.  Lines may hold at most 2048 positions, and

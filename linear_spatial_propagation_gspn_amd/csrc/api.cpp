@@ -438,13 +438,16 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                           const void* x, const void* const logits_in[4], const void* const lam_in[4],
                           const float* merge, void* y, float* states, void* workspace, int64_t workspace_bytes,
                           int dtype, int layout, void* stream, Timer* tm, bool noalloc = false,
-                          int64_t merge_ld = 0) {
+                          int64_t merge_ld = 0, int64_t states_ld = 0) {
     // noalloc: the workspace is the current device's static scratch array,
     // looked up only once every argument has passed validation.
     // merge_ld: floats between the merge weights' direction rows (0: c); more
     // than c only for the plane-sequential path's tail, a channel range of a
     // wider call, which takes the concurrent path and its transposing merge.
+    // states_ld: floats between the four state maps (0: n c h w); more only
+    // for that tail, whose maps are plane ranges of the wider call's.
     const int64_t mld = merge_ld > 0 ? merge_ld : c;
+    const int64_t sel = states_ld > 0 ? states_ld : n * c * h * w;
     if (!valid_layout(layout)) return GSPN_ERR_BAD_LAYOUT;
     const void* const* logits = logits_in;
     const void* const* lam = lam_in;
@@ -472,11 +475,12 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     const int64_t mgb = (3 * mld + c) * 4;  // merge weights, fp32 [4][c], rows mld floats apart
     if (merge && !aligned(merge, 4)) return GSPN_ERR_MISALIGNED;
     if (merge && overlap(y, xb, merge, mgb)) return GSPN_ERR_ALIASING;
-    const int64_t sb = 4 * n * c * h * w * 4;  // four fp32 state maps
+    const int64_t sb = (3 * sel + n * c * h * w) * 4;  // four fp32 state maps, sel floats apart
     if (states) {
         // the states come from the four-direction launch, which takes lines
         // of at most 2048 positions and a workspace (also for planes of at
-        // most 64 x 64, whose plane-resident path keeps no states)
+        // most 64 x 64, whose plane-resident path keeps no states), or from
+        // the plane-sequential kernel, which the same shapes allow
         if (!gspn::fused4_supported(h, w) || !fused_grid_ok(n, c, h, w, chunks)) return GSPN_ERR_UNSUPPORTED;
         if (!have_ws) return GSPN_ERR_WORKSPACE;
         if (!aligned(states, 4)) return GSPN_ERR_MISALIGNED;
@@ -580,8 +584,11 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     }
     // Many big planes: one workgroup per plane runs the four directions in
     // turn and builds y in place; the scratch map of the horizontal
-    // directions' sum takes the room of x transposed.
-    if (!states && gspn::seq4_supported(h, w) && n * c >= gspn::kSeq4MinPlanes && (!merge || mld == c)) {
+    // directions' sum takes the room of x transposed.  It also writes the
+    // states (the fp32 h of every direction, unweighted, so not with merge
+    // weights), bit for bit those of the four-direction launch.
+    if (!(states && merge) && gspn::seq4_supported(h, w) && n * c >= gspn::kSeq4MinPlanes &&
+        (!merge || mld == c)) {
         bool vec = aligned(x, 16) && aligned(y, 16);
         for (int d = 0; d < 4; ++d) vec = vec && aligned(p[d].wts, 16) && aligned(p[d].lam, 16);
         if (vec) {
@@ -600,7 +607,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
             const void* wts[4] = {p[0].wts, p[1].wts, p[2].wts, p[3].wts};
             if (timed(tm, GSPN_STAGE_SCAN, [&] {
                     return gspn::launch_seq4(x, wts, lam, merge, y, xt, n, c, cw, h, w, chunks, dtype, p[0].wdtype,
-                                             p[0].wts_are_logits, run, st);
+                                             p[0].wts_are_logits, run, states, sel, st);
                 }) != hipSuccess)
                 return GSPN_ERR_HIP;
             if (split) {
@@ -621,8 +628,8 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
                     sub = forward4_impl(1, tail, h, w, cw == 1 ? 1 : tail, chunk_len,
                                         static_cast<const char*>(x) + run * plane_b, tz, tl,
                                         merge ? merge + c0 : nullptr, static_cast<char*>(y) + run * plane_b,
-                                        nullptr, workspace, workspace_bytes, dtype, GSPN_LAYOUT_SCAN, stream,
-                                        nullptr, false, c);
+                                        states ? states + run * h * w : nullptr, workspace, workspace_bytes,
+                                        dtype, GSPN_LAYOUT_SCAN, stream, nullptr, false, c, sel);
                     return sub == GSPN_OK ? hipSuccess : hipErrorLaunchFailure;
                 });
                 if (sub != GSPN_OK) return sub;
@@ -637,7 +644,6 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     // frame, where line k of step i is x[.., k, i]: of x transposed, or,
     // where the long-line kernel takes them (lp_xtile_supported), of x itself
     // read through LDS column tiles, so that no transposed copy is made.
-    const int64_t elems = n * c * h * w;
     for (int d = 2; d < 4; ++d) {
         p[d].h = w;
         p[d].w = h;
@@ -650,7 +656,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
         for (int d = 0; d < 4; ++d) {
             q[d].mscale = nullptr;
             if (states) {
-                q[d].out = states + d * elems;
+                q[d].out = states + d * sel;
                 q[d].odtype = GSPN_F32;
             }
         }
@@ -676,7 +682,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     // its fp32 state map, then y merged from those maps.
     if (states) {
         for (int d = 0; d < 4; ++d) {
-            p[d].out = states + d * elems;
+            p[d].out = states + d * sel;
             p[d].odtype = GSPN_F32;
             p[d].mscale = nullptr;  // the merge below applies the merge weights
         }
@@ -695,7 +701,7 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
             if (tm) tm->scan_kernel = kind;
         }
         return from_hip(timed(tm, GSPN_STAGE_COMBINE, [&] {
-            return gspn::launch_combine_states(y, states, states + elems, states + 2 * elems, states + 3 * elems,
+            return gspn::launch_combine_states(y, states, states + sel, states + 2 * sel, states + 3 * sel,
                                                n * c, static_cast<int>(h), static_cast<int>(w), dtype, st, merge,
                                                c, mld);
         }));

@@ -153,6 +153,8 @@ struct Seq4K {
     void* y;               // [planes][H][W]
     void* z;               // workspace [planes][W][H]: the horizontal directions' sum, transposed
     const float* merge;    // [4][c] learnable merge weights, or null
+    float* st;             // fp32 state maps (map d: st + d * st_ld, its scan frame), or null
+    int64_t st_ld;         // floats between the state maps
     int64_t c;
     int64_t cw;
     int H, W;
@@ -169,10 +171,12 @@ using Tile = coltile::Tile<T, kLanes, kTileRowBytes>;
 // 1 R2L (x tiles, z += h), 2 T2B (x rows, y = h + z^T tiles), 3 B2T (x rows,
 // y += h).  T: storage type; TW: WPair (channel-shared weights normalised
 // beforehand) or T (logits, normalised here); D: steps of per-step inputs in
-// flight; LOGITS: TW holds logits (else fp32 weights normalised beforehand).
+// flight; LOGITS: TW holds logits (else fp32 weights normalised beforehand);
+// STATES: h of every line is also stored, in fp32, as a row of the
+// direction's state map (the rows of z and y are already in the maps' frames).
 // tid: the thread's index among the plane's kLanes; valid = false: the
 // waves only keep step with the workgroup's barriers (p is then any plane).
-template <typename T, typename TW, bool LOGITS, int MODE, int D, bool MERGE>
+template <typename T, typename TW, bool LOGITS, int MODE, int D, bool MERGE, bool STATES>
 __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid, int tid, uint32_t* tile,
                                           float (*edges)[kWaves][2], Tile<T>& tl) {
     constexpr bool PAIR = std::is_same_v<TW, WPair>;
@@ -187,6 +191,7 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
     constexpr bool TILE = MODE <= 2;                 // a column tile feeds this phase
     constexpr bool EXTRA_ROW = MODE == 1 || MODE == 3;  // a row of z / y is added
     static_assert(64 % D == 0 && TS % D == 0, "ring groups align with tiles and lines");
+    static_assert(!(STATES && MERGE), "the states are the unweighted scans");
 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,6 +213,8 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
     const auto rx = rsrc(static_cast<const T*>(a.x) + p * plane, plane * ES);
     const auto rzt = rsrc(static_cast<T*>(a.z) + p * plane, plane * ES);  // z, [W][H]
     const auto ry = rsrc(static_cast<T*>(a.y) + p * plane, plane * ES);
+    // this plane's state map of the direction, [S][L] (one plane's bytes)
+    const auto rst = rsrc(STATES ? a.st + DIR * a.st_ld + p * plane : a.st, STATES ? plane * 4 : 0);
     // the tile's source: x ([H][W]) in the horizontal phases, z ([W][H]) in T2B
     const auto rsrc_tile = MODE == 2 ? rzt : rx;
     const int tR = MODE == 2 ? W : H;  // rows of the tile source = the line length
@@ -312,9 +319,13 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
             for (int j = 1; j < kP; ++j) dd[j] = h[j] - h[j - 1];
             dd[kP] = right - h[kP - 1];
 #pragma unroll
-            for (int j = 0; j < kP; ++j)
+            for (int j = 0; j < kP; ++j) {
+                // lambda x + h fused as the long-line scan fuses it, so that
+                // the unweighted scans of the two kernels agree bit for bit
+                const float base = MERGE ? h[j] + u[j] : __builtin_fmaf(elem<T, NW>(sl[s], j), xin[j], h[j]);
                 hn[j] = __builtin_fmaf(pair_hi(sz[s][0][j]), dd[j + 1],
-                                       __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], h[j] + u[j]));
+                                       __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base));
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < kP; ++j) {
@@ -339,6 +350,13 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
             if constexpr (MODE <= 1) stw<NW, GSPN_SEQ4_RMW_AUX>(ow, rzt, vt, soff);      // read back a phase later
             else if constexpr (MODE == 2) stw<NW, GSPN_SEQ4_RMW_AUX>(ow, ry, vt, soff);  // read back by B2T
             else stw<NW, kNT>(ow, ry, vt, soff);
+            if constexpr (STATES) {
+                // read only by a backward, after this launch
+                uint32_t hw[kP];
+#pragma unroll
+                for (int j = 0; j < kP; ++j) hw[j] = __float_as_uint(h[j]);
+                stw<kP, kNT>(hw, rst, static_cast<uint32_t>(k0c) * 4, static_cast<uint32_t>(i) * L * 4);
+            }
         }
         buf ^= 1;
         if (lane == 0) edges[buf][wave][0] = h[0];
@@ -373,7 +391,7 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
 }
 
 // The phases of PH (bit m: phase m) for one plane per group of four waves.
-template <typename T, typename TW, bool LOGITS, int D, bool MERGE, int PH>
+template <typename T, typename TW, bool LOGITS, int D, bool MERGE, bool STATES, int PH>
 __global__ __launch_bounds__(kLanes * kGroups, (PH & 7) ? kBlocksPerCU : 4) void seq4_kernel(const Seq4K a) {
     constexpr bool TILES = (PH & 7) != 0;  // a phase reads column tiles
     __shared__ uint32_t tiles[kGroups][TILES ? kTileDwords : 1];
@@ -397,13 +415,13 @@ __global__ __launch_bounds__(kLanes * kGroups, (PH & 7) ? kBlocksPerCU : 4) void
         __syncthreads();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
-    if constexpr ((PH & 1) != 0) seq_phase<T, TW, LOGITS, 0, D, MERGE>(a, p, valid, tid, tile, edges, tl);
+    if constexpr ((PH & 1) != 0) seq_phase<T, TW, LOGITS, 0, D, MERGE, STATES>(a, p, valid, tid, tile, edges, tl);
     if constexpr ((PH & 1) != 0 && (PH & 2) != 0) handoff();
-    if constexpr ((PH & 2) != 0) seq_phase<T, TW, LOGITS, 1, D, MERGE>(a, p, valid, tid, tile, edges, tl);
+    if constexpr ((PH & 2) != 0) seq_phase<T, TW, LOGITS, 1, D, MERGE, STATES>(a, p, valid, tid, tile, edges, tl);
     if constexpr ((PH & 3) != 0 && (PH & 4) != 0) handoff();
-    if constexpr ((PH & 4) != 0) seq_phase<T, TW, LOGITS, 2, D, MERGE>(a, p, valid, tid, tile, edges, tl);
+    if constexpr ((PH & 4) != 0) seq_phase<T, TW, LOGITS, 2, D, MERGE, STATES>(a, p, valid, tid, tile, edges, tl);
     if constexpr ((PH & 7) != 0 && (PH & 8) != 0) handoff();
-    if constexpr ((PH & 8) != 0) seq_phase<T, TW, LOGITS, 3, D, MERGE>(a, p, valid, tid, tile, edges, tl);
+    if constexpr ((PH & 8) != 0) seq_phase<T, TW, LOGITS, 3, D, MERGE, STATES>(a, p, valid, tid, tile, edges, tl);
 }
 
 // How the four phases are split over launches: one launch of all four, two
@@ -412,34 +430,35 @@ __global__ __launch_bounds__(kLanes * kGroups, (PH & 7) ? kBlocksPerCU : 4) void
 #define GSPN_SEQ4_SPLIT 0
 #endif
 
-template <typename T, typename TW, bool LOGITS, int D, bool MERGE, int PH>
+template <typename T, typename TW, bool LOGITS, int D, bool MERGE, bool STATES, int PH>
 hipError_t launch_phases(const Seq4K& k, int64_t planes, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((planes + kGroups - 1) / kGroups));
-    hipLaunchKernelGGL((seq4_kernel<T, TW, LOGITS, D, MERGE, PH>), grid, dim3(kLanes * kGroups), 0, stream, k);
+    hipLaunchKernelGGL((seq4_kernel<T, TW, LOGITS, D, MERGE, STATES, PH>), grid, dim3(kLanes * kGroups), 0, stream, k);
     return hipGetLastError();
 }
 
-template <typename T, typename TW, bool LOGITS, int D, bool MERGE>
+template <typename T, typename TW, bool LOGITS, int D, bool MERGE, bool STATES>
 hipError_t launch_seq4_m(const Seq4K& k, int64_t planes, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if constexpr (GSPN_SEQ4_SPLIT == 0) {
-        e = launch_phases<T, TW, LOGITS, D, MERGE, 15>(k, planes, stream);
+        e = launch_phases<T, TW, LOGITS, D, MERGE, STATES, 15>(k, planes, stream);
     } else if constexpr (GSPN_SEQ4_SPLIT == 1) {
-        e = launch_phases<T, TW, LOGITS, D, MERGE, 3>(k, planes, stream);
-        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, 12>(k, planes, stream);
+        e = launch_phases<T, TW, LOGITS, D, MERGE, STATES, 3>(k, planes, stream);
+        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, STATES, 12>(k, planes, stream);
     } else {
-        e = launch_phases<T, TW, LOGITS, D, MERGE, 1>(k, planes, stream);
-        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, 2>(k, planes, stream);
-        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, 4>(k, planes, stream);
-        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, 8>(k, planes, stream);
+        e = launch_phases<T, TW, LOGITS, D, MERGE, STATES, 1>(k, planes, stream);
+        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, STATES, 2>(k, planes, stream);
+        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, STATES, 4>(k, planes, stream);
+        if (e == hipSuccess) e = launch_phases<T, TW, LOGITS, D, MERGE, STATES, 8>(k, planes, stream);
     }
     return e;
 }
 
 template <typename T, typename TW, bool LOGITS, int D>
 hipError_t launch_seq4_t(const Seq4K& k, int64_t planes, hipStream_t stream) {
-    if (k.merge) return launch_seq4_m<T, TW, LOGITS, D, true>(k, planes, stream);
-    return launch_seq4_m<T, TW, LOGITS, D, false>(k, planes, stream);
+    if (k.merge) return launch_seq4_m<T, TW, LOGITS, D, true, false>(k, planes, stream);
+    if (k.st) return launch_seq4_m<T, TW, LOGITS, D, false, true>(k, planes, stream);
+    return launch_seq4_m<T, TW, LOGITS, D, false, false>(k, planes, stream);
 }
 
 }  // namespace
@@ -468,7 +487,7 @@ bool seq4_supported(int64_t h, int64_t w) {
 hipError_t launch_seq4(const void* x, const void* const wts[4], const void* const lam[4], const float* merge,
                        void* y, void* z, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w,
                        const int64_t chunk[4], int dtype, int wdtype, int wts_are_logits, int64_t run,
-                       hipStream_t stream) {
+                       float* states, int64_t states_ld, hipStream_t stream) {
     Seq4K k;
     k.planes = n * c;
     k.x = x;
@@ -480,6 +499,8 @@ hipError_t launch_seq4(const void* x, const void* const wts[4], const void* cons
     k.y = y;
     k.z = z;
     k.merge = merge;
+    k.st = merge ? nullptr : states;  // with merge weights the caller keeps no states here
+    k.st_ld = states_ld;
     k.c = c;
     k.cw = cw;
     k.H = static_cast<int>(h);

@@ -5,7 +5,9 @@ y in place, the horizontal directions reading x through LDS column tiles.
 A last round of planes at most half full (one plane per CU) goes to the
 concurrent four-direction path instead.  Every element is compared with the
 fp64 oracle (normwise, 1e-5 for fp32 storage, 2e-2 for bf16), and the call
-must report that kernel."""
+must report that kernel.  Without merge weights a forward keeping its states
+takes the same kernel, which writes the fp32 scans bit for bit as the
+four-direction launch does."""
 import sys
 
 import pytest
@@ -108,3 +110,58 @@ def test_seq4_array_layout_and_noalloc(c):
     assert times["scan_kernel"] == "seq4_kernel"
     assert times["tail"]["launches"] == (1 if _tail_split(1, c, False) else 0)
     assert torch.equal(ya, ys) and torch.equal(yn, ys)
+
+
+# without merge weights the kernel also writes the four unweighted fp32 scans
+STATE_CASES = [CASES[0], CASES[2], CASES[3], CASES[5], CASES[6]]
+
+
+@pytest.mark.parametrize("chunk", [0, 7])
+@pytest.mark.parametrize("shape,dtype,shared", STATE_CASES)
+def test_seq4_keeps_states(shape, dtype, shared, chunk):
+    """A forward keeping its states runs the plane-sequential kernel too (the
+    tail's planes, if any, on the concurrent path into the same maps): y is
+    that of the forward without states, each map matches the oracle's scan,
+    and the maps equal bit for bit those of the four-direction launch (taken
+    by a forward keeping states with merge weights, whose states are the same
+    unweighted scans), so a backward from them returns the recomputing
+    backward's gradients."""
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, dtype, shared, chunk, 1700 + h + w + c)
+    print("seq4 states %s %s shared=%s chunk=%d" % (shape, dtype, shared, chunk), flush=True)
+    sys.stdout.flush()
+    inp = make_inputs(wl, DEV)
+    ws = G.forward4_workspace(inp["x"], wl.cw)
+    st = G.states_buffer(inp["x"])
+    y, times = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk, workspace=ws, states=st)
+    plain = G.gspn_forward4(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk, workspace=ws)
+    st2 = G.states_buffer(inp["x"])
+    _, times2 = G.gspn_forward4_timed(inp["x"], inp["logits"], inp["lam"], chunk_len=chunk, workspace=ws,
+                                      merge=torch.ones((4, c), device=DEV), states=st2)
+    torch.cuda.synchronize()
+    assert times["scan_kernel"] == "seq4_kernel", times["scan_kernel"]
+    assert times["tail"]["launches"] == (1 if _tail_split(n, c, False) else 0), times
+    assert times2["scan_kernel"] != "seq4_kernel", times2["scan_kernel"]
+    # y of the planes the kernel ran (a tail's y is merged from its maps, in
+    # another order with and without states)
+    run = n * c - ((n * c) % CUS if _tail_split(n, c, False) else 0)
+    assert torch.equal(y.reshape(n * c, h, w)[:run], plain.reshape(n * c, h, w)[:run])
+    assert torch.equal(st, st2)
+    ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk)
+    assert oracle.normwise_error(_np(y), ref) <= TOL[dtype]
+    for d in range(4):
+        got = _np(G.state_map(st, d, shape))
+        want = oracle.scan(d, inp["x"], inp["logits"][d], inp["lam"][d], chunk)
+        if d >= 2:
+            want = want.transpose(0, 1, 3, 2)  # the horizontal directions' scan frame
+        assert oracle.normwise_error(got, want) <= TOL[dtype], d
+    if not shared:  # (shared logits' gradients are fp32 atomic sums, in an order that varies)
+        g = torch.Generator(device=DEV)
+        g.manual_seed(wl.seed + 7)
+        gy = torch.randn((n, c, h, w), generator=g, device=DEV, dtype=torch.float32).to(wl.torch_dtype)
+        a = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=chunk, states=st)
+        b = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0])
+        for d in range(4):
+            assert torch.equal(a[1][d], b[1][d]) and torch.equal(a[2][d], b[2][d]), d
