@@ -224,7 +224,8 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              the y of a call without states in the last bf16 place.
  *              Without merge weights many big planes keep the
  *              plane-sequential kernel, which writes the same maps bit for
- *              bit, and the same y as without states.
+ *              bit; its y may differ from the y of a call without states in
+ *              the last bf16 place.
  *   workspace  optional device buffer of workspace_bytes bytes, 4-byte
  *              aligned.  NULL (or 0 bytes): the directions run one after
  *              another, the first writing y and the others adding to it, and

@@ -320,9 +320,10 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
             dd[kP] = right - h[kP - 1];
 #pragma unroll
             for (int j = 0; j < kP; ++j) {
-                // lambda x + h fused as the long-line scan fuses it, so that
-                // the unweighted scans of the two kernels agree bit for bit
-                const float base = MERGE ? h[j] + u[j] : __builtin_fmaf(elem<T, NW>(sl[s], j), xin[j], h[j]);
+                // with states, lambda x + h fused as the long-line scan fuses
+                // it, so that the kept scans of the two kernels agree bit for
+                // bit (without, a product and an add measured faster)
+                const float base = STATES ? __builtin_fmaf(elem<T, NW>(sl[s], j), xin[j], h[j]) : h[j] + u[j];
                 hn[j] = __builtin_fmaf(pair_hi(sz[s][0][j]), dd[j + 1],
                                        __builtin_fmaf(pair_lo(sz[s][0][j]), -dd[j], base));
             }

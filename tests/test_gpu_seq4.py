@@ -120,8 +120,9 @@ STATE_CASES = [CASES[0], CASES[2], CASES[3], CASES[5], CASES[6]]
 @pytest.mark.parametrize("shape,dtype,shared", STATE_CASES)
 def test_seq4_keeps_states(shape, dtype, shared, chunk):
     """A forward keeping its states runs the plane-sequential kernel too (the
-    tail's planes, if any, on the concurrent path into the same maps): y is
-    that of the forward without states, each map matches the oracle's scan,
+    tail's planes, if any, on the concurrent path into the same maps): y
+    agrees with that of the forward without states, each map matches the
+    oracle's scan,
     and the maps equal bit for bit those of the four-direction launch (taken
     by a forward keeping states with merge weights, whose states are the same
     unweighted scans), so a backward from them returns the recomputing
@@ -142,10 +143,10 @@ def test_seq4_keeps_states(shape, dtype, shared, chunk):
     assert times["scan_kernel"] == "seq4_kernel", times["scan_kernel"]
     assert times["tail"]["launches"] == (1 if _tail_split(n, c, False) else 0), times
     assert times2["scan_kernel"] != "seq4_kernel", times2["scan_kernel"]
-    # y of the planes the kernel ran (a tail's y is merged from its maps, in
-    # another order with and without states)
-    run = n * c - ((n * c) % CUS if _tail_split(n, c, False) else 0)
-    assert torch.equal(y.reshape(n * c, h, w)[:run], plain.reshape(n * c, h, w)[:run])
+    # with states the kernel fuses lambda x + h into one multiply-add (as the
+    # four-direction launch does), without it rounds the product first: y
+    # agrees to rounding
+    assert oracle.normwise_error(_np(y), _np(plain)) <= TOL[dtype]
     assert torch.equal(st, st2)
     ref = oracle.forward4(inp["x"], inp["logits"], inp["lam"], chunk=chunk)
     assert oracle.normwise_error(_np(y), ref) <= TOL[dtype]
