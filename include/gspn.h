@@ -218,14 +218,13 @@ int64_t gspn_forward4_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w
  *              R2L.  It needs the workspace and lines of at most 2048
  *              positions (else GSPN_ERR_WORKSPACE / GSPN_ERR_UNSUPPORTED).
  *              Planes of at most 64 x 64 then leave their one-pass path
- *              (which keeps no states) for the four-direction launch, and
- *              so do many big planes given merge weights; y is then merged
- *              from these fp32 maps, so for bf16 storage it can differ from
- *              the y of a call without states in the last bf16 place.
- *              Without merge weights many big planes keep the
- *              plane-sequential kernel, which writes the same maps bit for
- *              bit; its y may differ from the y of a call without states in
- *              the last bf16 place.
+ *              (which keeps no states) for the four-direction launch; y is
+ *              then merged from these fp32 maps, so for bf16 storage it can
+ *              differ from the y of a call without states in the last bf16
+ *              place.  Many big planes keep the plane-sequential kernel,
+ *              which writes the same maps bit for bit; its y, too, may
+ *              differ from the y of a call without states in the last bf16
+ *              place.
  *   workspace  optional device buffer of workspace_bytes bytes, 4-byte
  *              aligned.  NULL (or 0 bytes): the directions run one after
  *              another, the first writing y and the others adding to it, and

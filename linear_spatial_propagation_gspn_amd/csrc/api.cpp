@@ -585,10 +585,9 @@ gspn_status forward4_impl(int64_t n, int64_t c, int64_t h, int64_t w, int64_t cw
     // Many big planes: one workgroup per plane runs the four directions in
     // turn and builds y in place; the scratch map of the horizontal
     // directions' sum takes the room of x transposed.  It also writes the
-    // states (the fp32 h of every direction, unweighted, so not with merge
-    // weights), bit for bit those of the four-direction launch.
-    if (!(states && merge) && gspn::seq4_supported(h, w) && n * c >= gspn::kSeq4MinPlanes &&
-        (!merge || mld == c)) {
+    // states (the fp32 h of every direction, unweighted), bit for bit those
+    // of the four-direction launch.
+    if (gspn::seq4_supported(h, w) && n * c >= gspn::kSeq4MinPlanes && (!merge || mld == c)) {
         bool vec = aligned(x, 16) && aligned(y, 16);
         for (int d = 0; d < 4; ++d) vec = vec && aligned(p[d].wts, 16) && aligned(p[d].lam, 16);
         if (vec) {

@@ -89,10 +89,9 @@ constexpr int64_t kSeq4MinPlanes =
 #else
     256;  // one workgroup per CU: fewer planes would leave CUs idle
 #endif
-// Runs the first `run` of the n * c planes (run <= n * c).  states (without
-// merge weights only; else ignored): fp32 maps of the four unweighted scans,
-// map d at states + d * states_ld, each in its direction's scan frame, or
-// null.
+// Runs the first `run` of the n * c planes (run <= n * c).  states: fp32
+// maps of the four unweighted scans, map d at states + d * states_ld, each in
+// its direction's scan frame, or null.
 hipError_t launch_seq4(const void* x, const void* const wts[4], const void* const lam[4], const float* merge,
                        void* y, void* z, int64_t n, int64_t c, int64_t cw, int64_t h, int64_t w,
                        const int64_t chunk[4], int dtype, int wdtype, int wts_are_logits, int64_t run,

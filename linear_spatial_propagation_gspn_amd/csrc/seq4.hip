@@ -173,7 +173,9 @@ using Tile = coltile::Tile<T, kLanes, kTileRowBytes>;
 // beforehand) or T (logits, normalised here); D: steps of per-step inputs in
 // flight; LOGITS: TW holds logits (else fp32 weights normalised beforehand);
 // STATES: h of every line is also stored, in fp32, as a row of the
-// direction's state map (the rows of z and y are already in the maps' frames).
+// direction's state map (the rows of z and y are already in the maps' frames);
+// the scan then runs unweighted and a merge weight scales h where it enters
+// z or y (else the weight scales lambda x, the scan being linear in it).
 // tid: the thread's index among the plane's kLanes; valid = false: the
 // waves only keep step with the workgroup's barriers (p is then any plane).
 template <typename T, typename TW, bool LOGITS, int MODE, int D, bool MERGE, bool STATES>
@@ -191,7 +193,6 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
     constexpr bool TILE = MODE <= 2;                 // a column tile feeds this phase
     constexpr bool EXTRA_ROW = MODE == 1 || MODE == 3;  // a row of z / y is added
     static_assert(64 % D == 0 && TS % D == 0, "ring groups align with tiles and lines");
-    static_assert(!(STATES && MERGE), "the states are the unweighted scans");
 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -296,7 +297,7 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
 #pragma unroll
         for (int j = 0; j < kP; ++j) {
             const float lx = elem<T, NW>(sl[s], j) * xin[j];
-            u[j] = MERGE ? lx * msc : lx;
+            u[j] = MERGE && !STATES ? lx * msc : lx;
         }
         // neighbours from the previous step: inside the wave by DPP, across
         // wave edges from LDS (0 beyond the line; lanes past it hold h = 0)
@@ -344,7 +345,10 @@ __device__ __forceinline__ void seq_phase(const Seq4K& a, int64_t p, bool valid,
         if (active) {
             float ov[kP];
 #pragma unroll
-            for (int j = 0; j < kP; ++j) ov[j] = MODE == 0 ? h[j] : h[j] + extra[j];
+            for (int j = 0; j < kP; ++j) {
+                if constexpr (MERGE && STATES) ov[j] = MODE == 0 ? msc * h[j] : __builtin_fmaf(msc, h[j], extra[j]);
+                else ov[j] = MODE == 0 ? h[j] : h[j] + extra[j];
+            }
             uint32_t ow[NW];
             pack<T, NW>(ow, ov);
             const uint32_t soff = static_cast<uint32_t>(i) * rowT;
@@ -457,8 +461,11 @@ hipError_t launch_seq4_m(const Seq4K& k, int64_t planes, hipStream_t stream) {
 
 template <typename T, typename TW, bool LOGITS, int D>
 hipError_t launch_seq4_t(const Seq4K& k, int64_t planes, hipStream_t stream) {
+    if (k.st) {
+        if (k.merge) return launch_seq4_m<T, TW, LOGITS, D, true, true>(k, planes, stream);
+        return launch_seq4_m<T, TW, LOGITS, D, false, true>(k, planes, stream);
+    }
     if (k.merge) return launch_seq4_m<T, TW, LOGITS, D, true, false>(k, planes, stream);
-    if (k.st) return launch_seq4_m<T, TW, LOGITS, D, false, true>(k, planes, stream);
     return launch_seq4_m<T, TW, LOGITS, D, false, false>(k, planes, stream);
 }
 
@@ -500,7 +507,7 @@ hipError_t launch_seq4(const void* x, const void* const wts[4], const void* cons
     k.y = y;
     k.z = z;
     k.merge = merge;
-    k.st = merge ? nullptr : states;  // with merge weights the caller keeps no states here
+    k.st = states;
     k.st_ld = states_ld;
     k.c = c;
     k.cw = cw;
