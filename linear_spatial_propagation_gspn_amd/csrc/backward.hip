@@ -58,11 +58,16 @@ constexpr int adj_band_depth() { return GSPN_ADJ_BAND_DEPTH * 2 / (P * G) > 1 ? 
 #endif
 
 // channels per workgroup for channel-shared logits (fewer for two positions
-// per lane: register budget; with the learnable merge's extra state the
-// four-channel groups spill a few registers, and still measured faster than
-// groups of two)
+// per lane: register budget).  With the learnable merge's extra state a
+// four-channel group of 1024-lane workgroups (128 registers a lane) spills
+// 68 bytes a lane, and groups of two measured faster there (wide backward:
+// adjoint 21.2-21.5 -> 16.1-16.3 ms); without merge weights four stay
+// faster (14.9-15.5 against 15.9-16.0 ms).
 #ifndef GSPN_ADJ_G1
 #define GSPN_ADJ_G1 4
+#endif
+#ifndef GSPN_ADJ_G1_MERGE
+#define GSPN_ADJ_G1_MERGE 2
 #endif
 #ifndef GSPN_ADJ_G2
 #define GSPN_ADJ_G2 2
@@ -70,8 +75,8 @@ constexpr int adj_band_depth() { return GSPN_ADJ_BAND_DEPTH * 2 / (P * G) > 1 ? 
 #ifndef GSPN_ADJ_P
 #define GSPN_ADJ_P 1
 #endif
-template <int P>
-constexpr int shared_group() { return P == 1 ? GSPN_ADJ_G1 : GSPN_ADJ_G2; }
+template <int P, bool MERGE>
+constexpr int shared_group() { return P == 1 ? (MERGE ? GSPN_ADJ_G1_MERGE : GSPN_ADJ_G1) : GSPN_ADJ_G2; }
 
 struct AdjK {
     const void* x;    // [planes][S][L] (x, or x transposed for horizontal)
@@ -89,7 +94,7 @@ struct AdjK {
     int K;
     int nchunks;
     int reverse;
-    int shared;  // dz holds fp32 channel sums of weight-gradient differences (atomic adds; groups of shared_group<P>() channels)
+    int shared;  // dz holds fp32 channel sums of weight-gradient differences (atomic adds; groups of shared_group<P, MERGE>() channels)
     const float* mscale;  // learnable merge weight of each channel for this direction ([c]), or null for 1
     float* dmerge;        // its gradient [c] (fp32 atomic adds), or null
 };
@@ -1047,7 +1052,9 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, Adjo
         merge = merge || p[d].mscale || p[d].dmerge;
     }
     const int P = maxL <= 1024 ? (shared ? GSPN_ADJ_P : 1) : 2;  // lines of at most 2048 positions
-    const int G = !shared ? 1 : (P == 1 ? shared_group<1>() : shared_group<2>());
+    const int G = !shared ? 1
+                  : P == 1   ? (merge ? shared_group<1, true>() : shared_group<1, false>())
+                             : (merge ? shared_group<2, true>() : shared_group<2, false>());
     for (int d = 0; d < 4; ++d) {
         AdjK& a = k.d[d];
         a.x = p[d].x;
@@ -1097,7 +1104,7 @@ hipError_t launch_adjoint4(const AdjointParams (&p)[4], hipStream_t stream, Adjo
     } while (0)
 #define GSPN_ADJ_LAUNCH_P(PP, MM)                                                                                 \
     do {                                                                                                          \
-        if (shared) GSPN_ADJ_LAUNCH(PP, shared_group<PP>(), MM);                                                  \
+        if (shared) GSPN_ADJ_LAUNCH(PP, (shared_group<PP, MM>()), MM);                                            \
         else GSPN_ADJ_LAUNCH(PP, 1, MM);                                                                          \
     } while (0)
     if (P == 1) {

@@ -261,3 +261,30 @@ def test_backward_banded(shape, shared, dtype, merge, keep):
         e = oracle.normwise_error(_np(got[3]), ref[3])
         _say("  dmerge normwise error %.3g" % e)
         assert e <= TOL[dtype]
+
+
+WIDE_MERGE_PLAN = dict(WIDE_PLAN, channel_group=2)
+
+
+@pytest.mark.parametrize("chunk", [0, 5])
+@pytest.mark.parametrize("shape", [(1, 9, 64, 128), (1, 9, 128, 1024)])
+def test_backward_shared_merge_groups_of_two(shape, chunk):
+    """The wide workload's adjoint with learnable merge weights: the same
+    instance but for channel groups of two (9 = 2 + 2 + 2 + 2 + 1), which
+    keep the merge's extra state in registers.  dx, every dlambda, every
+    dlogits and dmerge against the oracle."""
+    n, c, h, w = shape
+    wl = Workload("case", n, c, h, w, "bf16", True, chunk, 750 + h + w)
+    _say("backward merge groups of two %s chunk=%d" % (shape, chunk))
+    inp = make_inputs(wl, DEV)
+    gy = _gy(wl, 33)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(wl.seed + 3)
+    m = torch.randn((4, c), generator=g, device=DEV)
+    t = G.StageTimes()
+    got = G.gspn_backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk_len=chunk, merge=m, dmerge=True, times=t)
+    torch.cuda.synchronize()
+    assert t.as_dict()["adjoint_plan"] == WIDE_MERGE_PLAN
+    ref = oracle.backward4(inp["x"], inp["logits"], inp["lam"], gy, chunk=chunk, merge=_np(m))
+    _check_all(got[:3], ref[:3], TOL["bf16"], "all outputs")
+    assert oracle.normwise_error(_np(got[3]), ref[3]) <= TOL["bf16"]
