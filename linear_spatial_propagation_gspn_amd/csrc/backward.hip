@@ -58,13 +58,14 @@ constexpr int adj_band_depth() { return GSPN_ADJ_BAND_DEPTH * 2 / (P * G) > 1 ? 
 #endif
 
 // channels per workgroup for channel-shared logits (fewer for two positions
-// per lane: register budget).  With the learnable merge's extra state a
-// four-channel group of 1024-lane workgroups (128 registers a lane) spills
-// 68 bytes a lane, and groups of two measured faster there (wide backward:
-// adjoint 21.2-21.5 -> 16.1-16.3 ms); without merge weights four stay
-// faster (14.9-15.5 against 15.9-16.0 ms).
+// per lane: register budget).  A 1024-lane workgroup leaves 128 registers a
+// lane.  Without merge weights groups of three fit them (four spill 8 bytes
+// a lane): wide adjoint 13.7-13.8 ms against 14.8-15.4 for four and 15.9-16.0
+// for two.  With the learnable merge's extra state three spill 20 bytes and
+// four 68, so groups of two (16.1-16.2 ms, against 16.9-17.0 for three and
+// 21.2-21.5 for four).
 #ifndef GSPN_ADJ_G1
-#define GSPN_ADJ_G1 4
+#define GSPN_ADJ_G1 3
 #endif
 #ifndef GSPN_ADJ_G1_MERGE
 #define GSPN_ADJ_G1_MERGE 2

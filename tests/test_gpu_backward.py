@@ -162,20 +162,20 @@ def test_backward_full_tstage_sampled_planes():
         _check_all(got, ref, TOL["f32"], "plane (%d, %d)" % (n, c))
 
 
-WIDE_PLAN = {"kernel": "adj4_kernel", "positions_per_lane": 1, "channel_group": 4, "nontemporal": True}
+WIDE_PLAN = {"kernel": "adj4_kernel", "positions_per_lane": 1, "channel_group": 3, "nontemporal": True}
 
 
 @pytest.mark.parametrize("chunk", [0, 5])
-@pytest.mark.parametrize("shape", [(1, 9, 64, 128), (1, 9, 64, 1024), (1, 9, 128, 1024)])
-def test_backward_shared_groups_of_four_nontemporal(shape, chunk):
+@pytest.mark.parametrize("shape", [(1, 10, 64, 128), (1, 10, 64, 1024), (1, 10, 128, 1024)])
+def test_backward_shared_groups_of_three_nontemporal(shape, chunk):
     """The wide workload's adjoint instance: bf16 storage, channel-shared
-    logits summed over groups of four channels (9 = 4 + 4 + 1: the last group
-    ragged), one position per lane on lines of up to 1024 positions, and the
+    logits summed over groups of three channels (10 = 3 + 3 + 3 + 1: the last
+    group ragged), one position per lane on lines of up to 1024 positions, and the
     non-temporal streams that every line being a whole number of 128-byte
     cache lines selects (H and W multiples of 64)."""
     n, c, h, w = shape
     wl = Workload("case", n, c, h, w, "bf16", True, chunk, 700 + h + w)
-    _say("backward groups of four %s chunk=%d" % (shape, chunk))
+    _say("backward groups of three %s chunk=%d" % (shape, chunk))
     inp = make_inputs(wl, DEV)
     gy = _gy(wl, 31)
     t = G.StageTimes()

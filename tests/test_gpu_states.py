@@ -119,7 +119,7 @@ def test_backward_from_states(dtype, shape, shared, chunk, merge):
 SMALL = [
     # planes of at most 64 x 64 leave their one-pass path when the states are kept
     ("f32", (2, 3, 23, 41), False, 5),     # ragged lines: lanes past the end of every line
-    ("bf16", (1, 5, 40, 72), True, 0),     # channel groups of four in the adjoint, the last ragged
+    ("bf16", (1, 5, 40, 72), True, 0),     # channel groups of three in the adjoint, the last ragged
     ("f32", (1, 2, 64, 64), False, 7),
 ]
 

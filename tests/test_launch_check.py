@@ -141,7 +141,7 @@ def test_tstage_training_step_with_kept_states(chk):
 
 @pytest.mark.parametrize("case", [
     dict(n=2, c=3, h=23, w=41, chunk=5),                          # ragged lines, element tiles
-    dict(n=1, c=5, h=40, w=72, dtype=torch.bfloat16, shared=True),  # channel groups of four, the last ragged
+    dict(n=1, c=5, h=40, w=72, dtype=torch.bfloat16, shared=True),  # channel groups of three, the last ragged
     dict(n=1, c=2, h=64, w=64, merge=True, chunk=7),
     dict(n=1, c=3, h=56, w=56, layout="array"),
 ])
